@@ -1,0 +1,532 @@
+// libamc host side: argument validation, workspace planning, launch sequencing
+// and the kernel timer.  Nothing here touches the GPU before validation has
+// passed, so every argument error returns with nothing enqueued.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "amc.h"
+#include "amc_internal.h"
+
+namespace amc {
+
+// ---------------------------------------------------------------------------
+// timer
+// ---------------------------------------------------------------------------
+struct Timer {
+  std::vector<hipEvent_t> start, stop;
+  std::vector<int> cls;
+  size_t used = 0;
+  bool failed = false;
+};
+
+void timer_begin(Timer *t, int c, hipStream_t s) {
+  if (!t || t->failed) return;
+  if (t->used == t->start.size()) {
+    hipEvent_t a, b;
+    if (hipEventCreate(&a) != hipSuccess || hipEventCreate(&b) != hipSuccess) {
+      t->failed = true;
+      return;
+    }
+    t->start.push_back(a);
+    t->stop.push_back(b);
+    t->cls.push_back(c);
+  }
+  t->cls[t->used] = c;
+  if (hipEventRecord(t->start[t->used], s) != hipSuccess) t->failed = true;
+}
+
+void timer_end(Timer *t, int c, hipStream_t s) {
+  (void)c;
+  if (!t || t->failed) return;
+  if (hipEventRecord(t->stop[t->used], s) != hipSuccess) t->failed = true;
+  t->used++;
+}
+
+// ---------------------------------------------------------------------------
+// planning
+// ---------------------------------------------------------------------------
+static inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+struct Plan {
+  Dims dm{};
+  std::vector<HeadDesc> desc;
+  int kR = 1;
+  int64_t max_cycles = 0, sum_t = 0, sum_cycles = 0, sum_n = 0, sum_T = 0;
+  bool store_phi = true;
+  // byte offsets in the workspace
+  uint64_t o_desc = 0, o_shift_part = 0, o_shift = 0, o_phi = 0, o_m = 0, o_r = 0, o_mhat = 0,
+           o_Y = 0, o_sel_slot = 0, o_sel_list = 0, o_panel = 0, o_G = 0, o_bvec = 0, o_w = 0,
+           o_rhs = 0, o_cvsel = 0, o_pos = 0, o_cand_val = 0, o_cand_idx = 0, o_flist = 0, o_fcount = 0,
+           o_dn = 0, o_L = 0, total = 0;
+};
+
+static amc_status check_problem(const amc_problem *p) {
+  if (!p || p->num_heads < 1 || !p->cu_q || !p->cu_k || !p->budgets) return AMC_ERR_INVALID_ARG;
+  if (p->in_dtype != AMC_F32 && p->in_dtype != AMC_BF16) return AMC_ERR_INVALID_ARG;
+  if (!(std::isfinite(p->scale)) || p->scale < 0.0f) return AMC_ERR_INVALID_ARG;
+  if (p->head_dim != 64 && p->head_dim != 128) {
+    return p->head_dim > 0 ? AMC_ERR_UNSUPPORTED : AMC_ERR_INVALID_ARG;
+  }
+  if (p->cu_q[0] != 0 || p->cu_k[0] != 0) return AMC_ERR_INVALID_ARG;
+  for (int h = 0; h < p->num_heads; ++h) {
+    const int64_t n = p->cu_q[h + 1] - p->cu_q[h];
+    const int64_t T = p->cu_k[h + 1] - p->cu_k[h];
+    const int64_t t = p->budgets[h];
+    if (n < 1 || T < 1 || t < 1 || t > T) return AMC_ERR_INVALID_ARG;
+    if (T > (int64_t(1) << 30) || n > (int64_t(1) << 30)) return AMC_ERR_UNSUPPORTED;
+  }
+  return AMC_OK;
+}
+
+static amc_status check_options(const amc_options *o) {
+  if (!o) return AMC_ERR_INVALID_ARG;
+  if (o->select != AMC_SEL_OMP && o->select != AMC_SEL_OMP_BATCHED) return AMC_ERR_INVALID_ARG;
+  if (o->topk < 1 || o->refit_every < 1) return AMC_ERR_INVALID_ARG;
+  if (o->select == AMC_SEL_OMP && (o->topk != 1 || o->refit_every != 1)) return AMC_ERR_INVALID_ARG;
+  if (int64_t(o->topk) * o->refit_every > kMaxCycle) return AMC_ERR_UNSUPPORTED;
+  if (o->nnls_pg_iters < 0 || o->nnls_max_iters < 0) return AMC_ERR_INVALID_ARG;
+  if (!(o->nnls_tol >= 0.0) || !std::isfinite(o->nnls_tol)) return AMC_ERR_INVALID_ARG;
+  if (o->cv_dtype != AMC_F32 && o->cv_dtype != AMC_BF16) return AMC_ERR_INVALID_ARG;
+  if (o->flags & ~uint32_t(AMC_FLAG_TRACE)) return AMC_ERR_INVALID_ARG;
+  return AMC_OK;
+}
+
+// Builds the plan.  features_only: the amc_mass_features stage (no selection state).
+static amc_status make_plan(const amc_problem *p, const amc_options *o, bool features_only, Plan &pl) {
+  amc_status st = check_problem(p);
+  if (st != AMC_OK) return st;
+  if (!features_only) {
+    st = check_options(o);
+    if (st != AMC_OK) return st;
+  }
+  const int H = p->num_heads;
+  const int d = p->head_dim;
+  pl.kR = features_only ? 1 : o->topk * o->refit_every;
+  Dims &dm = pl.dm;
+  dm.H = H;
+  dm.d = d;
+  dm.in_bf16 = p->in_dtype == AMC_BF16;
+  dm.scale = p->scale > 0.0f ? double(p->scale) : 1.0 / std::sqrt(double(d));
+  pl.desc.assign(H, HeadDesc{});
+  int64_t phi = 0, nn = 0, tt = 0, t2 = 0, panel = 0, cblk = 0, sblk = 0, cyc = 0, TT = 0, tri = 0;
+  for (int h = 0; h < H; ++h) {
+    HeadDesc &D = pl.desc[h];
+    D.n = p->cu_q[h + 1] - p->cu_q[h];
+    D.T = p->cu_k[h + 1] - p->cu_k[h];
+    D.t = features_only ? 1 : p->budgets[h];
+    D.q_off = p->cu_q[h];
+    D.k_off = p->cu_k[h];
+    D.ldT = (D.T + 3) / 4 * 4;
+    D.phi_off = phi;
+    D.n_off = nn;
+    D.t_off = tt;
+    D.tt_off = t2;
+    D.panel_off = panel;
+    D.cblk_off = cblk;
+    D.n_cblk = ceil_div(D.T, kSweepCols);
+    D.sblk_off = sblk;
+    D.n_sblk = ceil_div(D.n, kShiftRows);
+    D.cyc_off = cyc;
+    D.tri_off = tri;
+    if (!features_only) {
+      if (D.t > kLdsMaxT) return AMC_ERR_UNSUPPORTED;  // large-budget solver not in this build
+      if (D.n_cblk > kMaxSweepBlocks) return AMC_ERR_UNSUPPORTED;
+    }
+    const int64_t cycles = ceil_div(D.t, pl.kR);
+    phi += D.n * D.ldT;
+    nn += D.n;
+    tt += D.t;
+    t2 += D.t * D.t;
+    tri += D.t * (D.t + 1) / 2;
+    panel += D.t * D.n;
+    cblk += D.n_cblk;
+    sblk += D.n_sblk;
+    cyc += cycles;
+    TT += D.T;
+    dm.max_n = std::max(dm.max_n, D.n);
+    dm.max_T = std::max(dm.max_T, D.T);
+    dm.max_t = std::max(dm.max_t, D.t);
+    dm.max_sblk = std::max(dm.max_sblk, D.n_sblk);
+    dm.max_cblk = std::max(dm.max_cblk, D.n_cblk);
+    pl.max_cycles = std::max(pl.max_cycles, cycles);
+  }
+  dm.total_sblk = sblk;
+  pl.sum_t = tt;
+  pl.sum_cycles = cyc;
+  pl.sum_n = nn;
+  pl.sum_T = TT;
+  const uint64_t phi_bytes = uint64_t(phi) * 4;
+  if (!features_only) {
+    pl.store_phi = phi_bytes <= o->phi_budget_bytes;
+    if (!pl.store_phi) return AMC_ERR_UNSUPPORTED;  // recompute-mode sweep not in this build
+  }
+
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  pl.o_desc = take(sizeof(HeadDesc) * H);
+  pl.o_shift_part = take(4ull * sblk);
+  pl.o_shift = take(8ull * H);
+  if (features_only) {
+    pl.total = off;
+    return AMC_OK;
+  }
+  pl.o_phi = take(phi_bytes);
+  pl.o_m = take(8ull * nn);
+  pl.o_r = take(8ull * nn);
+  pl.o_mhat = take(8ull * nn);
+  pl.o_Y = take(4ull * nn * d);
+  pl.o_sel_slot = take(4ull * TT);
+  pl.o_sel_list = take(4ull * tt);
+  pl.o_panel = take(8ull * panel);
+  pl.o_G = take(8ull * t2);
+  pl.o_bvec = take(8ull * tt);
+  pl.o_w = take(8ull * tt);
+  pl.o_rhs = take(8ull * tt * d);
+  pl.o_cvsel = take(4ull * tt * d);
+  pl.o_pos = take(4ull * tt);
+  pl.o_cand_val = take(8ull * cblk * (kMaxCycle + 1));
+  pl.o_cand_idx = take(4ull * cblk * (kMaxCycle + 1));
+  pl.o_flist = take(4ull * tt);
+  pl.o_fcount = take(4ull * H);
+  pl.o_dn = take(8ull * tt);
+  pl.o_L = take(8ull * tri);
+  pl.total = off;
+  return AMC_OK;
+}
+
+static void trace_layout(const Plan &pl, amc_trace_layout *L) {
+  uint64_t off = 0;
+  auto take = [&](uint64_t bytes) {
+    const uint64_t at = off;
+    off = align256(off + bytes);
+    return at;
+  };
+  L->shift = take(8ull * pl.dm.H);
+  L->pick = take(4ull * pl.sum_t);
+  L->pick_score = take(8ull * pl.sum_t);
+  L->weight = take(8ull * pl.sum_t);
+  L->runner_up = take(8ull * pl.sum_cycles);
+  L->nnls_iters = take(4ull * pl.sum_cycles);
+  L->total_bytes = off;
+}
+
+// Copies the head descriptors to the device through kernel arguments, so the
+// host vector may die as soon as the call returns (no pageable async copy).
+static amc_status upload_desc(const Plan &pl, HeadDesc *d_desc, hipStream_t s) {
+  const uint64_t *words = reinterpret_cast<const uint64_t *>(pl.desc.data());
+  const int64_t n = int64_t(pl.desc.size()) * int64_t(sizeof(HeadDesc) / 8);
+  if (launch_copy_words(reinterpret_cast<uint64_t *>(d_desc), words, n, s) != hipSuccess) return AMC_ERR_HIP;
+  return AMC_OK;
+}
+
+static bool sync_check_enabled() {
+  const char *e = std::getenv("AMC_SYNC_CHECK");
+  return e && e[0] == '1';
+}
+
+}  // namespace amc
+
+using namespace amc;
+
+// ---------------------------------------------------------------------------
+// C ABI
+// ---------------------------------------------------------------------------
+extern "C" {
+
+void amc_default_options(amc_options *o) {
+  if (!o) return;
+  std::memset(o, 0, sizeof(*o));
+  o->select = AMC_SEL_OMP;
+  o->topk = 1;
+  o->refit_every = 1;
+  o->nnls_pg_iters = 8;
+  o->nnls_max_iters = 0;
+  o->nnls_tol = 0.0;
+  o->phi_budget_bytes = 64ull << 30;
+  o->cv_dtype = AMC_F32;
+  o->flags = 0;
+  o->timer = nullptr;
+}
+
+amc_status amc_workspace_size(const amc_problem *p, const amc_options *o, uint64_t *bytes) {
+  if (!bytes) return AMC_ERR_INVALID_ARG;
+  Plan pl;
+  amc_status st = make_plan(p, o, false, pl);
+  if (st != AMC_OK) return st;
+  *bytes = pl.total;
+  return AMC_OK;
+}
+
+amc_status amc_mass_features_workspace(const amc_problem *p, uint64_t *bytes) {
+  if (!bytes) return AMC_ERR_INVALID_ARG;
+  Plan pl;
+  amc_status st = make_plan(p, nullptr, true, pl);
+  if (st != AMC_OK) return st;
+  *bytes = pl.total;
+  return AMC_OK;
+}
+
+amc_status amc_output_offsets(const amc_problem *p, int64_t *cu_budgets) {
+  if (!cu_budgets) return AMC_ERR_INVALID_ARG;
+  amc_status st = check_problem(p);
+  if (st != AMC_OK) return st;
+  cu_budgets[0] = 0;
+  for (int h = 0; h < p->num_heads; ++h) cu_budgets[h + 1] = cu_budgets[h] + p->budgets[h];
+  return AMC_OK;
+}
+
+amc_status amc_cycle_offsets(const amc_problem *p, const amc_options *o, int64_t *cu_cycles) {
+  if (!cu_cycles) return AMC_ERR_INVALID_ARG;
+  amc_status st = check_problem(p);
+  if (st != AMC_OK) return st;
+  st = check_options(o);
+  if (st != AMC_OK) return st;
+  const int64_t kR = int64_t(o->topk) * o->refit_every;
+  cu_cycles[0] = 0;
+  for (int h = 0; h < p->num_heads; ++h) cu_cycles[h + 1] = cu_cycles[h] + ceil_div(p->budgets[h], kR);
+  return AMC_OK;
+}
+
+amc_status amc_trace_layout_for(const amc_problem *p, const amc_options *o, amc_trace_layout *layout) {
+  if (!layout) return AMC_ERR_INVALID_ARG;
+  Plan pl;
+  amc_status st = make_plan(p, o, false, pl);
+  if (st != AMC_OK) return st;
+  trace_layout(pl, layout);
+  return AMC_OK;
+}
+
+#define AMC_LAUNCH(cls, expr)                                                     \
+  do {                                                                            \
+    if (timer) timer_begin(timer, (cls), stream);                                 \
+    hipError_t e_ = (expr);                                                       \
+    if (timer) timer_end(timer, (cls), stream);                                   \
+    if (e_ != hipSuccess) return AMC_ERR_HIP;                                     \
+    if (sync_check) {                                                             \
+      if (hipStreamSynchronize(stream) != hipSuccess || hipGetLastError() != hipSuccess) \
+        return AMC_ERR_HIP;                                                       \
+    }                                                                             \
+  } while (0)
+
+amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q, const void *K,
+                       const void *V, const float *beta_in, void *Ck, float *beta, void *Cv,
+                       int32_t *sel_idx, int32_t *head_status, void *trace, uint64_t trace_bytes,
+                       void *workspace, uint64_t workspace_bytes, void *stream_ptr) {
+  Plan pl;
+  amc_status st = make_plan(p, o, false, pl);
+  if (st != AMC_OK) return st;
+  if (!Q || !K || !V || !Ck || !beta || !Cv) return AMC_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < pl.total) return AMC_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return AMC_ERR_WORKSPACE;
+  amc_trace_layout tl{};
+  const bool tracing = (o->flags & AMC_FLAG_TRACE) != 0;
+  if (tracing) {
+    trace_layout(pl, &tl);
+    if (!trace || trace_bytes < tl.total_bytes) return AMC_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(trace) & 255) return AMC_ERR_WORKSPACE;
+  }
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  Timer *timer = reinterpret_cast<Timer *>(o->timer);
+  const bool sync_check = sync_check_enabled();
+
+  char *ws = static_cast<char *>(workspace);
+  Buffers b{};
+  b.desc = reinterpret_cast<const HeadDesc *>(ws + pl.o_desc);
+  b.Q = Q;
+  b.K = K;
+  b.V = V;
+  b.beta_in = beta_in;
+  b.shift_part = reinterpret_cast<float *>(ws + pl.o_shift_part);
+  b.shift = reinterpret_cast<double *>(ws + pl.o_shift);
+  b.phi = reinterpret_cast<float *>(ws + pl.o_phi);
+  b.m = reinterpret_cast<double *>(ws + pl.o_m);
+  b.r = reinterpret_cast<double *>(ws + pl.o_r);
+  b.mhat = reinterpret_cast<double *>(ws + pl.o_mhat);
+  b.Y = reinterpret_cast<float *>(ws + pl.o_Y);
+  b.sel_slot = reinterpret_cast<int32_t *>(ws + pl.o_sel_slot);
+  b.sel_list = reinterpret_cast<int32_t *>(ws + pl.o_sel_list);
+  b.panel = reinterpret_cast<double *>(ws + pl.o_panel);
+  b.G = reinterpret_cast<double *>(ws + pl.o_G);
+  b.bvec = reinterpret_cast<double *>(ws + pl.o_bvec);
+  b.w = reinterpret_cast<double *>(ws + pl.o_w);
+  b.rhs = reinterpret_cast<double *>(ws + pl.o_rhs);
+  b.cv_sel = reinterpret_cast<float *>(ws + pl.o_cvsel);
+  b.pos_of_slot = reinterpret_cast<int32_t *>(ws + pl.o_pos);
+  b.cand_val = reinterpret_cast<double *>(ws + pl.o_cand_val);
+  b.cand_idx = reinterpret_cast<int32_t *>(ws + pl.o_cand_idx);
+  b.ols_flist = reinterpret_cast<int32_t *>(ws + pl.o_flist);
+  b.ols_fcount = reinterpret_cast<int32_t *>(ws + pl.o_fcount);
+  b.ols_dn = reinterpret_cast<double *>(ws + pl.o_dn);
+  b.ols_L = reinterpret_cast<double *>(ws + pl.o_L);
+  b.head_status = head_status;
+  if (tracing) {
+    char *tr = static_cast<char *>(trace);
+    b.tr_shift = reinterpret_cast<double *>(tr + tl.shift);
+    b.tr_pick = reinterpret_cast<int32_t *>(tr + tl.pick);
+    b.tr_pick_score = reinterpret_cast<double *>(tr + tl.pick_score);
+    b.tr_weight = reinterpret_cast<double *>(tr + tl.weight);
+    b.tr_runner = reinterpret_cast<double *>(tr + tl.runner_up);
+    b.tr_iters = reinterpret_cast<int32_t *>(tr + tl.nnls_iters);
+  }
+  NnlsParams np{o->nnls_pg_iters, o->nnls_max_iters, o->nnls_tol};
+  const Dims &dm = pl.dm;
+
+  AMC_LAUNCH(AMC_K_INIT, (upload_desc(pl, const_cast<HeadDesc *>(b.desc), stream) == AMC_OK
+                              ? hipSuccess
+                              : hipErrorLaunchFailure));
+  AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.sel_slot, pl.sum_T, 0, stream));
+  if (head_status) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(head_status, dm.H, 0, stream));
+  AMC_LAUNCH(AMC_K_SHIFT, launch_shift(dm, b, stream));
+  AMC_LAUNCH(AMC_K_PHI, launch_phi(dm, b, 1, stream));
+  for (int c = 0; c < pl.max_cycles; ++c) {
+    AMC_LAUNCH(AMC_K_SWEEP, launch_sweep(dm, b, c, pl.kR, stream));
+    AMC_LAUNCH(AMC_K_MERGE, launch_merge(dm, b, c, pl.kR, stream));
+    AMC_LAUNCH(AMC_K_PANEL, launch_panel(dm, b, c, pl.kR, stream));
+    AMC_LAUNCH(AMC_K_GRAM, launch_gram(dm, b, c, pl.kR, stream));
+    AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dm, b, c, pl.kR, np, stream));
+    AMC_LAUNCH(AMC_K_RESID, launch_resid(dm, b, c, pl.kR, stream));
+  }
+  AMC_LAUNCH(AMC_K_OLS_NORMAL, launch_ols_normal(dm, b, stream));
+  AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_factor(dm, b, stream));
+  AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_trsm(dm, b, stream));
+  AMC_LAUNCH(AMC_K_PACK, launch_pack(dm, b, Ck, beta, Cv, o->cv_dtype == AMC_BF16, sel_idx, stream));
+  return AMC_OK;
+}
+
+amc_status amc_mass_features(const amc_problem *p, const void *Q, const void *K, const void *V,
+                             const float *beta_in, double *shift, float *phi, double *m, float *Y,
+                             int32_t *head_status, void *workspace, uint64_t workspace_bytes,
+                             void *stream_ptr) {
+  Plan pl;
+  amc_status st = make_plan(p, nullptr, true, pl);
+  if (st != AMC_OK) return st;
+  if (!Q || !K || !V || !shift || !m || !Y) return AMC_ERR_INVALID_ARG;
+  if (!workspace || workspace_bytes < pl.total) return AMC_ERR_WORKSPACE;
+  if (reinterpret_cast<uintptr_t>(workspace) & 255) return AMC_ERR_WORKSPACE;
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  Timer *timer = nullptr;
+  const bool sync_check = sync_check_enabled();
+  // The caller's Phi is packed densely ([n][T] per head); the kernel writes rows
+  // of stride ldT, so a caller Phi is only accepted when every T is a multiple of 4.
+  if (phi) {
+    for (const HeadDesc &D : pl.desc)
+      if (D.ldT != D.T) return AMC_ERR_UNSUPPORTED;
+  }
+  char *ws = static_cast<char *>(workspace);
+  Buffers b{};
+  b.desc = reinterpret_cast<const HeadDesc *>(ws + pl.o_desc);
+  b.Q = Q;
+  b.K = K;
+  b.V = V;
+  b.beta_in = beta_in;
+  b.shift_part = reinterpret_cast<float *>(ws + pl.o_shift_part);
+  b.shift = shift;
+  b.phi = phi;
+  b.m = m;
+  b.r = nullptr;
+  b.Y = Y;
+  b.head_status = head_status;
+  AMC_LAUNCH(AMC_K_INIT, (upload_desc(pl, const_cast<HeadDesc *>(b.desc), stream) == AMC_OK
+                              ? hipSuccess
+                              : hipErrorLaunchFailure));
+  if (head_status) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(head_status, pl.dm.H, 0, stream));
+  AMC_LAUNCH(AMC_K_SHIFT, launch_shift(pl.dm, b, stream));
+  AMC_LAUNCH(AMC_K_PHI, launch_phi(pl.dm, b, phi != nullptr, stream));
+  return AMC_OK;
+}
+
+amc_status amc_nnls(int32_t num, const int64_t *cu_t, const double *G, const double *g, double *w,
+                    int32_t warm, int32_t pg_iters, int32_t max_iters, double tol, int32_t *iters,
+                    int32_t *status, void *stream_ptr) {
+  if (num < 1 || !cu_t || !G || !g || !w) return AMC_ERR_INVALID_ARG;
+  if (pg_iters < 0 || max_iters < 0 || !(tol >= 0.0) || !std::isfinite(tol)) return AMC_ERR_INVALID_ARG;
+  if (cu_t[0] != 0) return AMC_ERR_INVALID_ARG;
+  int64_t max_t = 0;
+  std::vector<int64_t> cu2(num + 1, 0);
+  for (int i = 0; i < num; ++i) {
+    const int64_t t = cu_t[i + 1] - cu_t[i];
+    if (t < 1) return AMC_ERR_INVALID_ARG;
+    if (t > kLdsMaxT) return AMC_ERR_UNSUPPORTED;
+    max_t = std::max(max_t, t);
+    cu2[i + 1] = cu2[i] + t * t;
+  }
+  hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
+  NnlsParams np{pg_iters, max_iters, tol};
+  // The size tables travel as kernel arguments in chunks; see launch_nnls_batched.
+  hipError_t e = launch_nnls_batched(num, cu_t, cu2.data(), max_t, G, g, w, warm, np, iters, status, stream);
+  if (e != hipSuccess) return AMC_ERR_HIP;
+  if (sync_check_enabled()) {
+    if (hipStreamSynchronize(stream) != hipSuccess || hipGetLastError() != hipSuccess) return AMC_ERR_HIP;
+  }
+  return AMC_OK;
+}
+
+amc_status amc_timer_create(void **timer) {
+  if (!timer) return AMC_ERR_INVALID_ARG;
+  Timer *t = new (std::nothrow) Timer();
+  if (!t) return AMC_ERR_INVALID_ARG;
+  *timer = t;
+  return AMC_OK;
+}
+
+amc_status amc_timer_reset(void *timer) {
+  if (!timer) return AMC_ERR_INVALID_ARG;
+  Timer *t = static_cast<Timer *>(timer);
+  t->used = 0;
+  t->failed = false;
+  return AMC_OK;
+}
+
+amc_status amc_timer_read(void *timer, int32_t kernel_class, int64_t *launches, double *total_ms) {
+  if (!timer || !launches || !total_ms) return AMC_ERR_INVALID_ARG;
+  if (kernel_class < 0 || kernel_class >= AMC_NUM_KERNEL_CLASSES) return AMC_ERR_INVALID_ARG;
+  Timer *t = static_cast<Timer *>(timer);
+  if (t->failed) return AMC_ERR_HIP;
+  int64_t cnt = 0;
+  double tot = 0.0;
+  for (size_t i = 0; i < t->used; ++i) {
+    if (t->cls[i] != kernel_class) continue;
+    if (hipEventSynchronize(t->stop[i]) != hipSuccess) return AMC_ERR_HIP;
+    float ms = 0.0f;
+    if (hipEventElapsedTime(&ms, t->start[i], t->stop[i]) != hipSuccess) return AMC_ERR_HIP;
+    ++cnt;
+    tot += ms;
+  }
+  *launches = cnt;
+  *total_ms = tot;
+  return AMC_OK;
+}
+
+void amc_timer_destroy(void *timer) {
+  if (!timer) return;
+  Timer *t = static_cast<Timer *>(timer);
+  for (hipEvent_t e : t->start) (void)hipEventDestroy(e);
+  for (hipEvent_t e : t->stop) (void)hipEventDestroy(e);
+  delete t;
+}
+
+const char *amc_status_string(amc_status s) {
+  switch (s) {
+    case AMC_OK: return "ok";
+    case AMC_ERR_INVALID_ARG: return "invalid argument";
+    case AMC_ERR_UNSUPPORTED: return "unsupported by this build";
+    case AMC_ERR_WORKSPACE: return "workspace or trace buffer too small or misaligned";
+    case AMC_ERR_HIP: return "HIP runtime error";
+  }
+  return "unknown status";
+}
+
+int amc_version(void) { return AMC_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,116 @@
+// Internal declarations shared by the libamc host planner and its HIP kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "amc.h"
+
+namespace amc {
+
+// Tile sizes fixed by the kernels.
+constexpr int kShiftRows = 128;  // queries per block of the logit-maximum kernel
+constexpr int kPhiRows = 64;     // queries per block of the mass-feature kernel
+constexpr int kPhiKeys = 64;     // keys per tile of the mass-feature kernel
+constexpr int kSweepCols = 256;  // columns per block of the correlation sweep
+constexpr int kMaxCycle = 255;   // largest k * R (keys per refit cycle)
+constexpr int kLdsMaxT = 192;    // largest budget of the LDS-resident NNLS / value fit
+constexpr int kMaxSweepBlocks = 1024;  // sweep column blocks per head the merge handles
+
+// Per-head descriptor, computed on the host and copied to the device once per call.
+// All offsets are in elements of the array they index.
+struct HeadDesc {
+  int64_t n, T, t;        // queries, keys, budget
+  int64_t q_off;          // first row of the head in Q
+  int64_t k_off;          // first row of the head in K, V, beta_in; first entry in sel_slot
+  int64_t ldT;            // row stride of the head's Phi (T rounded up to 4)
+  int64_t phi_off;        // first element of the head's Phi
+  int64_t n_off;          // first entry in the per-query arrays (m, r, mhat, rows of Y)
+  int64_t t_off;          // first entry in the per-slot arrays (= cu_budgets[h])
+  int64_t tt_off;         // first element of the head's t x t matrices (G, normal matrix)
+  int64_t panel_off;      // first element of the head's float64 panel [t][n]
+  int64_t cblk_off;       // first sweep column block of the head in the candidate arrays
+  int64_t n_cblk;         // sweep column blocks of the head
+  int64_t sblk_off;       // first logit-maximum block of the head
+  int64_t n_sblk;         // logit-maximum blocks of the head
+  int64_t cyc_off;        // first cycle of the head in the per-cycle trace arrays
+  int64_t tri_off;        // first element of the head's packed triangle (value-fit factor)
+  int64_t pad;
+};
+static_assert(sizeof(HeadDesc) == 18 * 8, "HeadDesc layout");
+
+// Device pointers of the workspace carve-up and of the caller's buffers.
+struct Buffers {
+  const HeadDesc *desc;
+  const void *Q, *K, *V;
+  const float *beta_in;
+  float *shift_part;   // [sum n_sblk]
+  double *shift;       // [H]
+  float *phi;          // [sum n*ldT]
+  double *m, *r, *mhat;  // [sum n]
+  float *Y;            // [sum n][d]
+  int32_t *sel_slot;   // [sum T]  0 = unselected, else 1 + slot
+  int32_t *sel_list;   // [sum t]  key index of each slot
+  double *panel;       // [sum t*n] row a = float64 column of slot a over the queries
+  double *G;           // [sum t*t]
+  double *bvec;        // [sum t]
+  double *w;           // [sum t]
+  double *rhs;         // [sum t][d]
+  float *cv_sel;       // [sum t][d]
+  int32_t *pos_of_slot;  // [sum t]
+  int32_t *ols_flist;  // [sum t]  slots with w > 0, ascending
+  int32_t *ols_fcount; // [H]
+  double *ols_dn;      // [sum t]  diagonal scaling of the normal matrix
+  double *ols_L;       // [sum t*(t+1)/2] packed Cholesky factor of the scaled normal matrix
+  double *cand_val;    // [sum n_cblk][kMaxCycle + 1]
+  int32_t *cand_idx;   // [sum n_cblk][kMaxCycle + 1]
+  int32_t *head_status;  // [H] or null
+  // trace (all null when tracing is off)
+  double *tr_shift, *tr_pick_score, *tr_weight, *tr_runner;
+  int32_t *tr_pick, *tr_iters;
+};
+
+struct Dims {
+  int H, d;
+  int in_bf16;         // 1: Q/K/V are bfloat16, 0: float32
+  double scale;
+  int64_t max_n, max_T, max_t;
+  int64_t max_sblk, max_cblk;
+  int64_t total_sblk;
+};
+
+struct NnlsParams {
+  int pg_iters;
+  int max_iters;  // 0: automatic
+  double tol;     // 0: automatic
+};
+
+// Event-pair recorder used by the launch wrappers when a timer is attached.
+struct Timer;
+void timer_begin(Timer *t, int cls, hipStream_t s);
+void timer_end(Timer *t, int cls, hipStream_t s);
+
+// Kernel launchers (each returns hipSuccess or the launch error).
+hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
+hipError_t launch_shift(const Dims &dm, const Buffers &b, hipStream_t s);
+hipError_t launch_phi(const Dims &dm, const Buffers &b, int store_phi, hipStream_t s);
+hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_merge(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int cyc_keys,
+                       const NnlsParams &np, hipStream_t s);
+hipError_t launch_resid(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s);
+hipError_t launch_pack(const Dims &dm, const Buffers &b, void *Ck, float *beta, void *Cv,
+                       int cv_bf16, int32_t *sel_idx, hipStream_t s);
+// Stand-alone batched NNLS on caller-provided Gram systems.
+// h_cu_t / h_cu_t2 are HOST prefix sums of t_b and t_b^2; they travel as kernel arguments.
+hipError_t launch_nnls_batched(int num, const int64_t *h_cu_t, const int64_t *h_cu_t2, int64_t max_t,
+                               const double *G, const double *g, double *w, int warm,
+                               const NnlsParams &np, int32_t *iters, int32_t *status, hipStream_t s);
+hipError_t launch_copy_words(uint64_t *dst, const uint64_t *src, int64_t count, hipStream_t s);
+hipError_t launch_ols_factor(const Dims &dm, const Buffers &b, hipStream_t s);
+hipError_t launch_ols_trsm(const Dims &dm, const Buffers &b, hipStream_t s);
+
+}  // namespace amc

@@ -1,0 +1,359 @@
+// Value fit and packing (xinfinite.net article, section 2, step 3: with C_k
+// and beta fixed, C_v is an ordinary least-squares solution).
+//
+// The compacted block's attention output for query i is sum_j A_ij C_v[j]
+// with A_ij = Phi_ij w_j / mhat_i over the keys with w_j > 0 (a key with
+// w_j = 0 has beta = -inf and contributes nothing).  C_v solves the normal
+// equations (A^T A) C_v = A^T Y; A^T A is formed in float64 from the float64
+// panel and factored by Cholesky in unit-diagonal form (condition numbers
+// reach ~1e9 here), with a small diagonal shift as the fallback when a pivot
+// vanishes (then AMC_HS_CHOL_JITTER is reported).
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <cmath>
+#include <type_traits>
+
+#include "amc_internal.h"
+
+namespace amc {
+namespace {
+
+constexpr int NT = 256;
+
+__device__ __forceinline__ int tri(int r) { return r * (r + 1) / 2; }
+
+__device__ __forceinline__ void decode_tri(int e, int *r, int *c) {
+  int rr = int((sqrtf(8.0f * float(e) + 1.0f) - 1.0f) * 0.5f);
+  while (tri(rr + 1) <= e) ++rr;
+  while (tri(rr) > e) --rr;
+  *r = rr;
+  *c = e - tri(rr);
+}
+
+// ---------------------------------------------------------------------------
+// normal equations: N = At At^T and rhs = At Y with At[a][i] = P[a][i] w_a / mhat_i.
+// Block tile: 64 rows a x 64 columns b, b < t -> N, b >= t -> rhs column b - t.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
+                                                   const double *__restrict__ w, const double *__restrict__ mhat,
+                                                   const float *__restrict__ Y, double *__restrict__ N,
+                                                   double *__restrict__ rhs) {
+  constexpr int CH = 32;
+  __shared__ double xs[64][CH + 1];
+  __shared__ double zs[64][CH + 1];
+  __shared__ double sw[128];
+  const int h = blockIdx.z;
+  const HeadDesc Dh = desc[h];
+  const int64_t t = Dh.t, n = Dh.n;
+  const int64_t a0 = int64_t(blockIdx.x) * 64, b0 = int64_t(blockIdx.y) * 64;
+  if (a0 >= t || b0 >= t + D) return;
+  const int tid = threadIdx.x;
+  const int ta = (tid >> 4) * 4, tb = (tid & 15) * 4;
+  const double *P = Dh.panel_off + panel;
+  if (tid < 64) sw[tid] = (a0 + tid < t) ? w[Dh.t_off + a0 + tid] : 0.0;
+  if (tid >= 64 && tid < 128) sw[tid] = (b0 + tid - 64 < t) ? w[Dh.t_off + b0 + tid - 64] : 0.0;
+  __syncthreads();
+  double acc[4][4] = {};
+  for (int64_t i0 = 0; i0 < n; i0 += CH) {
+    for (int e = tid; e < 64 * CH; e += NT) {
+      const int r = e / CH, c = e % CH;
+      const int64_t i = i0 + c;
+      double x = 0.0, z = 0.0;
+      if (i < n) {
+        const double inv = 1.0 / mhat[Dh.n_off + i];
+        if (a0 + r < t) x = P[(a0 + r) * n + i] * sw[r] * inv;
+        const int64_t b = b0 + r;
+        if (b < t) z = P[b * n + i] * sw[64 + r] * inv;
+        else if (b - t < D) z = double(Y[(Dh.n_off + i) * D + (b - t)]);
+      }
+      xs[r][c] = x;
+      zs[r][c] = z;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = 0; c < CH; ++c) {
+      double xa[4], zb[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        xa[q] = xs[ta + q][c];
+        zb[q] = zs[tb + q][c];
+      }
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+#pragma unroll
+        for (int u = 0; u < 4; ++u) acc[q][u] = fma(xa[q], zb[u], acc[q][u]);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int64_t a = a0 + ta + q;
+    if (a >= t) continue;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int64_t b = b0 + tb + u;
+      if (b < t) N[Dh.tt_off + a * t + b] = acc[q][u];
+      else if (b - t < D) rhs[(Dh.t_off + a) * D + (b - t)] = acc[q][u];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// factor: unit-diagonal Cholesky of N restricted to F = {a : w_a > 0}.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(NT) void k_ols_factor(const HeadDesc *__restrict__ desc, const double *__restrict__ N,
+                                                   const double *__restrict__ w, int32_t *__restrict__ flist,
+                                                   int32_t *__restrict__ fcount, double *__restrict__ dn,
+                                                   double *__restrict__ Lout, int32_t *__restrict__ head_status) {
+  extern __shared__ __attribute__((aligned(16))) double Ls[];
+  __shared__ int sf[kLdsMaxT];
+  __shared__ double sdn[kLdsMaxT];
+  __shared__ int sh_f, sh_fail;
+  const int h = blockIdx.x;
+  const HeadDesc Dh = desc[h];
+  const int t = int(Dh.t);
+  const int tid = threadIdx.x;
+  if (tid == 0) {
+    int k = 0;
+    for (int a = 0; a < t; ++a)
+      if (w[Dh.t_off + a] > 0.0) sf[k++] = a;
+    sh_f = k;
+  }
+  __syncthreads();
+  const int f = sh_f;
+  for (int k = tid; k < f; k += NT) {
+    const double v = N[Dh.tt_off + int64_t(sf[k]) * t + sf[k]];
+    sdn[k] = (v > 0.0 && isfinite(v)) ? sqrt(v) : 1.0;
+  }
+  __syncthreads();
+  double jitter = 0.0;
+  for (int attempt = 0; attempt < 6; ++attempt) {
+    const int ne = tri(f);
+    for (int e = tid; e < ne; e += NT) {
+      int r, c;
+      decode_tri(e, &r, &c);
+      double v = N[Dh.tt_off + int64_t(sf[r]) * t + sf[c]] / (sdn[r] * sdn[c]);
+      if (r == c) v += jitter;
+      Ls[e] = v;
+    }
+    if (tid == 0) sh_fail = -1;
+    __syncthreads();
+    for (int k = 0; k < f; ++k) {
+      if (tid == 0) {
+        const double piv = Ls[tri(k) + k];
+        if (!(piv > 1e-15)) sh_fail = k;
+        else Ls[tri(k) + k] = sqrt(piv);
+      }
+      __syncthreads();
+      if (sh_fail >= 0) break;
+      const double dkk = Ls[tri(k) + k];
+      for (int r = k + 1 + tid; r < f; r += NT) Ls[tri(r) + k] /= dkk;
+      __syncthreads();
+      const int mm = f - k - 1;
+      const int nt = tri(mm);
+      for (int e = tid; e < nt; e += NT) {
+        int r, c;
+        decode_tri(e, &r, &c);
+        r += k + 1;
+        c += k + 1;
+        Ls[tri(r) + c] -= Ls[tri(r) + k] * Ls[tri(c) + k];
+      }
+      __syncthreads();
+    }
+    if (sh_fail < 0) break;
+    jitter = jitter == 0.0 ? 1e-13 : jitter * 100.0;
+    if (tid == 0 && head_status) atomicOr(head_status + h, int32_t(AMC_HS_CHOL_JITTER));
+    __syncthreads();
+  }
+  for (int e = tid; e < tri(f); e += NT) Lout[Dh.tri_off + e] = Ls[e];
+  for (int k = tid; k < f; k += NT) {
+    flist[Dh.t_off + k] = sf[k];
+    dn[Dh.t_off + k] = sdn[k];
+  }
+  if (tid == 0) fcount[h] = f;
+}
+
+// ---------------------------------------------------------------------------
+// triangular solves for 8 right-hand-side columns per block; C_v[F] = D^-1 X.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(NT) void k_ols_trsm(const HeadDesc *__restrict__ desc, const double *__restrict__ rhs,
+                                                 const int32_t *__restrict__ flist,
+                                                 const int32_t *__restrict__ fcount, const double *__restrict__ dn,
+                                                 const double *__restrict__ Lg, const double *__restrict__ w,
+                                                 float *__restrict__ cv_sel) {
+  constexpr int NC = 8;
+  extern __shared__ __attribute__((aligned(16))) double sm[];
+  const int h = blockIdx.y;
+  const HeadDesc Dh = desc[h];
+  const int t = int(Dh.t);
+  const int c0 = blockIdx.x * NC;
+  const int f = fcount[h];
+  const int tid = threadIdx.x;
+  double *Ls = sm;
+  double *X = sm + tri(f);  // [f][NC]
+  for (int e = tid; e < tri(f); e += NT) Ls[e] = Lg[Dh.tri_off + e];
+  for (int e = tid; e < f * NC; e += NT) {
+    const int k = e / NC, c = e % NC;
+    X[e] = rhs[(Dh.t_off + flist[Dh.t_off + k]) * D + c0 + c] / dn[Dh.t_off + k];
+  }
+  // keys with w = 0 get a zero value row
+  for (int e = tid; e < t * NC; e += NT) {
+    const int a = e / NC, c = e % NC;
+    if (!(w[Dh.t_off + a] > 0.0)) cv_sel[(Dh.t_off + a) * D + c0 + c] = 0.0f;
+  }
+  __syncthreads();
+  for (int k = 0; k < f; ++k) {
+    if (tid < NC) X[k * NC + tid] /= Ls[tri(k) + k];
+    __syncthreads();
+    const int cnt = (f - k - 1) * NC;
+    for (int e = tid; e < cnt; e += NT) {
+      const int r = k + 1 + e / NC, c = e % NC;
+      X[r * NC + c] -= Ls[tri(r) + k] * X[k * NC + c];
+    }
+    __syncthreads();
+  }
+  for (int k = f - 1; k >= 0; --k) {
+    if (tid < NC) X[k * NC + tid] /= Ls[tri(k) + k];
+    __syncthreads();
+    const int cnt = k * NC;
+    for (int e = tid; e < cnt; e += NT) {
+      const int r = e / NC, c = e % NC;
+      X[r * NC + c] -= Ls[tri(k) + r] * X[k * NC + c];
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < f * NC; e += NT) {
+    const int k = e / NC, c = e % NC;
+    cv_sel[(Dh.t_off + flist[Dh.t_off + k]) * D + c0 + c] = float(X[e] / dn[Dh.t_off + k]);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// pack: ascending original index; C_k copy, beta = beta_in + log w, C_v, sel_idx
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return uint16_t(u >> 16);
+}
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(NT) void k_pack(const HeadDesc *__restrict__ desc, const int32_t *__restrict__ sel_slot,
+                                             const int32_t *__restrict__ sel_list, const double *__restrict__ w,
+                                             const float *__restrict__ beta_in, const void *__restrict__ Kv,
+                                             const float *__restrict__ cv_sel, void *__restrict__ Ckv,
+                                             float *__restrict__ beta, void *__restrict__ Cvv, int cv_bf16,
+                                             int32_t *__restrict__ sel_idx) {
+  using E = typename std::conditional<BF16, uint16_t, float>::type;
+  __shared__ int cnt[NT];
+  __shared__ int spos[kLdsMaxT];
+  const int h = blockIdx.x;
+  const HeadDesc Dh = desc[h];
+  const int tid = threadIdx.x;
+  const int64_t T = Dh.T;
+  const int64_t chunk = (T + NT - 1) / NT;
+  const int64_t j0 = tid * chunk, j1 = (j0 + chunk < T) ? j0 + chunk : T;
+  for (int a = tid; a < kLdsMaxT; a += NT) spos[a] = -1;
+  int c = 0;
+  for (int64_t j = j0; j < j1; ++j) c += sel_slot[Dh.k_off + j] != 0;
+  cnt[tid] = c;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < NT; ++i) {
+      const int v = cnt[i];
+      cnt[i] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int pos = cnt[tid];
+  const int64_t out = Dh.t_off;
+  for (int64_t j = j0; j < j1; ++j) {
+    const int s = sel_slot[Dh.k_off + j];
+    if (s <= 0 || s > Dh.t || pos >= Dh.t) continue;
+    const int slot = s - 1;
+    spos[slot] = pos;
+    if (sel_idx) sel_idx[out + pos] = int32_t(j);
+    const double wv = w[Dh.t_off + slot];
+    const double bi = beta_in ? double(beta_in[Dh.k_off + j]) : 0.0;
+    beta[out + pos] = wv > 0.0 ? float(bi + log(wv)) : -INFINITY;
+    ++pos;
+  }
+  __syncthreads();
+  const E *K = static_cast<const E *>(Kv);
+  E *Ck = static_cast<E *>(Ckv);
+  const int64_t t = Dh.t;
+  for (int64_t e = tid; e < t * D; e += NT) {
+    const int64_t a = e / D, col = e % D;
+    const int sp = spos[a];
+    const int j = sel_list[Dh.t_off + a];
+    if (sp < 0 || j < 0 || j >= Dh.T) continue;
+    const int64_t row = out + sp;
+    Ck[row * D + col] = K[(Dh.k_off + j) * D + col];
+    const float v = cv_sel[(Dh.t_off + a) * D + col];
+    if (cv_bf16) static_cast<uint16_t *>(Cvv)[row * D + col] = f32_to_bf16_rne(v);
+    else static_cast<float *>(Cvv)[row * D + col] = v;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s) {
+  dim3 grid(unsigned((dm.max_t + 63) / 64), unsigned((dm.max_t + dm.d + 63) / 64), unsigned(dm.H));
+  if (dm.d == 128)
+    hipLaunchKernelGGL((k_ols_normal<128>), grid, dim3(NT), 0, s, b.desc, b.panel, b.w, b.mhat, b.Y, b.G, b.rhs);
+  else
+    hipLaunchKernelGGL((k_ols_normal<64>), grid, dim3(NT), 0, s, b.desc, b.panel, b.w, b.mhat, b.Y, b.G, b.rhs);
+  return hipGetLastError();
+}
+
+hipError_t launch_ols_factor(const Dims &dm, const Buffers &b, hipStream_t s) {
+  const size_t bytes = size_t(8) * size_t(dm.max_t) * size_t(dm.max_t + 1) / 2 + 16;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ols_factor),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(k_ols_factor, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.w, b.ols_flist,
+                     b.ols_fcount, b.ols_dn, b.ols_L, b.head_status);
+  return hipGetLastError();
+}
+
+hipError_t launch_ols_trsm(const Dims &dm, const Buffers &b, hipStream_t s) {
+  const size_t bytes = size_t(8) * (size_t(dm.max_t) * size_t(dm.max_t + 1) / 2 + size_t(dm.max_t) * 8) + 16;
+  dim3 grid(unsigned(dm.d / 8), unsigned(dm.H));
+  hipError_t e;
+  if (dm.d == 128) {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ols_trsm<128>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_ols_trsm<128>), grid, dim3(NT), bytes, s, b.desc, b.rhs, b.ols_flist, b.ols_fcount,
+                       b.ols_dn, b.ols_L, b.w, b.cv_sel);
+  } else {
+    e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ols_trsm<64>),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_ols_trsm<64>), grid, dim3(NT), bytes, s, b.desc, b.rhs, b.ols_flist, b.ols_fcount,
+                       b.ols_dn, b.ols_L, b.w, b.cv_sel);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_pack(const Dims &dm, const Buffers &b, void *Ck, float *beta, void *Cv, int cv_bf16,
+                       int32_t *sel_idx, hipStream_t s) {
+#define AMC_PACK_ARGS b.desc, b.sel_slot, b.sel_list, b.w, b.beta_in, b.K, b.cv_sel, Ck, beta, Cv, cv_bf16, sel_idx
+  if (dm.d == 128) {
+    if (dm.in_bf16) hipLaunchKernelGGL((k_pack<128, true>), dim3(unsigned(dm.H)), dim3(NT), 0, s, AMC_PACK_ARGS);
+    else hipLaunchKernelGGL((k_pack<128, false>), dim3(unsigned(dm.H)), dim3(NT), 0, s, AMC_PACK_ARGS);
+  } else {
+    if (dm.in_bf16) hipLaunchKernelGGL((k_pack<64, true>), dim3(unsigned(dm.H)), dim3(NT), 0, s, AMC_PACK_ARGS);
+    else hipLaunchKernelGGL((k_pack<64, false>), dim3(unsigned(dm.H)), dim3(NT), 0, s, AMC_PACK_ARGS);
+  }
+#undef AMC_PACK_ARGS
+  return hipGetLastError();
+}
+
+}  // namespace amc

@@ -1,0 +1,347 @@
+// Stage 1 kernels: the per-head logit shift, and the mass features
+// Phi = exp(l - s), the target mass m = Phi 1 and the attention output
+// Y = Phi V / m (zhichai.net deep-dive, section 1.6; xinfinite.net article,
+// section 2, step 3).
+//
+// The fit side of the method (m, and later the Gram system and residual) is
+// conditioned like cond(Phi_S^T Phi_S) ~ 1e9, so the logits that feed m are
+// computed in float64 on the MFMA units (v_mfma_f64_16x16x4f64) from the
+// exact bf16/fp32 inputs; Phi is rounded to float32 only for storage, where
+// the memory-bound correlation sweeps read it.  The shift only needs to keep
+// exp() in range, so it comes from a cheap bf16 MFMA pass.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <type_traits>
+
+#include "amc_internal.h"
+
+namespace amc {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t u16) { return __uint_as_float(u16 << 16); }
+
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+
+// 8 consecutive elements of an input row as 8 bf16 bit patterns.
+template <bool BF16>
+__device__ __forceinline__ uint4 load8_bf16(const void *base, int64_t off) {
+  if constexpr (BF16) {
+    return *reinterpret_cast<const uint4 *>(static_cast<const uint16_t *>(base) + off);
+  } else {
+    const float4 a = *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off);
+    const float4 b = *reinterpret_cast<const float4 *>(static_cast<const float *>(base) + off + 4);
+    uint4 r;
+    r.x = f32_to_bf16_bits(a.x) | (f32_to_bf16_bits(a.y) << 16);
+    r.y = f32_to_bf16_bits(a.z) | (f32_to_bf16_bits(a.w) << 16);
+    r.z = f32_to_bf16_bits(b.x) | (f32_to_bf16_bits(b.y) << 16);
+    r.w = f32_to_bf16_bits(b.z) | (f32_to_bf16_bits(b.w) << 16);
+    return r;
+  }
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+
+struct WordChunk {
+  uint64_t w[384];
+};
+
+__global__ void k_put_words(uint64_t *dst, int count, WordChunk c) {
+  const int i = threadIdx.x + blockIdx.x * blockDim.x;
+  if (i < count) dst[i] = c.w[i];
+}
+
+__global__ void k_fill_i32(int32_t *p, int64_t count, int32_t v) {
+  for (int64_t i = blockIdx.x * int64_t(blockDim.x) + threadIdx.x; i < count; i += int64_t(gridDim.x) * blockDim.x)
+    p[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// logit maximum: one partial per (head, 128 queries), bf16 MFMA 16x16x32
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_shift(const HeadDesc *__restrict__ desc, const void *__restrict__ Q,
+                                               const void *__restrict__ K, const float *__restrict__ beta_in,
+                                               float scale, float *__restrict__ shift_part) {
+  constexpr int KC = D / 32;
+  constexpr int KSTR = D + 8;  // bf16 elements per LDS row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) uint16_t ks[64 * KSTR];
+  __shared__ float red[4];
+  const HeadDesc Dh = desc[blockIdx.y];
+  const int blk = blockIdx.x;
+  if (blk >= Dh.n_sblk) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int64_t qb = int64_t(blk) * kShiftRows + wave * 32;
+
+  uint4 qf[2][KC];
+#pragma unroll
+  for (int rb = 0; rb < 2; ++rb) {
+    const int64_t row = qb + rb * 16 + c16;
+#pragma unroll
+    for (int c = 0; c < KC; ++c)
+      qf[rb][c] = row < Dh.n ? load8_bf16<BF16>(Q, (Dh.q_off + row) * D + 32 * c + 8 * g) : make_uint4(0, 0, 0, 0);
+  }
+  float mx = -INFINITY;
+  for (int64_t k0 = 0; k0 < Dh.T; k0 += 64) {
+    __syncthreads();
+    for (int gi = tid; gi < 64 * D / 8; gi += 256) {
+      const int key = gi / (D / 8), c8 = gi % (D / 8);
+      const uint4 v = (k0 + key < Dh.T) ? load8_bf16<BF16>(K, (Dh.k_off + k0 + key) * D + 8 * c8) : make_uint4(0, 0, 0, 0);
+      *reinterpret_cast<uint4 *>(&ks[key * KSTR + 8 * c8]) = v;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      uint4 kf[KC];
+#pragma unroll
+      for (int c = 0; c < KC; ++c) kf[c] = *reinterpret_cast<const uint4 *>(&ks[(kb * 16 + c16) * KSTR + 32 * c + 8 * g]);
+      const int64_t key = k0 + kb * 16 + c16;
+      const float bias = (key < Dh.T && beta_in) ? beta_in[Dh.k_off + key] : 0.0f;
+#pragma unroll
+      for (int rb = 0; rb < 2; ++rb) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < KC; ++c)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qf[rb][c]), as_bf16x8(kf[c]), acc, 0, 0, 0);
+        if (key < Dh.T) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t q = qb + rb * 16 + 4 * g + e;
+            if (q < Dh.n) mx = fmaxf(mx, fmaf(scale, acc[e], bias));
+          }
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if (lane == 0) red[wave] = mx;
+  __syncthreads();
+  if (tid == 0) shift_part[Dh.sblk_off + blk] = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+}
+
+// ---------------------------------------------------------------------------
+// mass features: float64 MFMA logits (S^T = K Q^T), fused exp / row sum /
+// float32 store and float32 MFMA Phi V.  One block = 64 queries, 4 waves of 16.
+// ---------------------------------------------------------------------------
+template <typename T>
+struct In;
+template <>
+struct In<uint16_t> {
+  __device__ static float f(uint16_t v) { return bf16_bits_to_f32(v); }
+};
+template <>
+struct In<float> {
+  __device__ static float f(float v) { return v; }
+};
+
+// v_mfma_f64_16x16x4f64 leaves output row i in lane group i % 4, element
+// i / 4 (rows interleaved across the lane groups).  With S^T = K Q^T the rows
+// are keys, so lane group g, element e of key block kb holds this key:
+__device__ __forceinline__ int phi_key(int kb, int g, int e) { return kb * 16 + g + 4 * e; }
+// The Phi V product consumes those values as its A operand at k-step (kb, e),
+// so V is stored transposed with each 16-key block permuted to make the four
+// keys a lane needs (phi_key(kb, g, 0..3)) contiguous.
+__device__ __forceinline__ int vt_pos(int key) { return (key & ~15) | ((key & 3) << 2) | ((key >> 2) & 3); }
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, const void *__restrict__ Qv,
+                                             const void *__restrict__ Kv, const void *__restrict__ Vv,
+                                             const float *__restrict__ beta_in, double scale,
+                                             const float *__restrict__ shift_part, double *__restrict__ shift_out,
+                                             double *__restrict__ tr_shift, float *__restrict__ phi,
+                                             double *__restrict__ m_out, double *__restrict__ r_out,
+                                             float *__restrict__ Y_out, int32_t *__restrict__ head_status) {
+  using E = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int KSTR = D + 4;   // elements per K row in LDS
+  constexpr int VSTR = 64 + 4;  // elements per transposed V row in LDS
+  constexpr int NU = D / 16;
+  __shared__ __attribute__((aligned(16))) E ks[64 * KSTR];
+  __shared__ __attribute__((aligned(16))) E vt[D * VSTR];
+  __shared__ float sbias[64];
+  __shared__ double s_shift;
+  const E *Q = static_cast<const E *>(Qv);
+  const E *K = static_cast<const E *>(Kv);
+  const E *V = static_cast<const E *>(Vv);
+
+  const int h = blockIdx.y;
+  const HeadDesc Dh = desc[h];
+  const int blk = blockIdx.x;
+  if (int64_t(blk) * kPhiRows >= Dh.n) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+
+  if (tid < 64) {
+    float v = -INFINITY;
+    for (int64_t i = tid; i < Dh.n_sblk; i += 64) v = fmaxf(v, shift_part[Dh.sblk_off + i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (tid == 0) s_shift = double(v);
+  }
+  __syncthreads();
+  const double s = s_shift;
+  if (blk == 0 && tid == 0) {
+    shift_out[h] = s;
+    if (tr_shift) tr_shift[h] = s;
+  }
+
+  const int64_t q0 = int64_t(blk) * kPhiRows + wave * 16;
+  const int64_t q = q0 + c16;  // this lane's query in the logit tile
+  const bool qvalid = q < Dh.n;
+  float qf[D / 4];
+#pragma unroll
+  for (int u = 0; u < NU; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      qf[4 * u + v] = qvalid ? In<E>::f(Q[(Dh.q_off + q) * D + 16 * u + 4 * g + v]) : 0.0f;
+
+  f32x4 uacc[NU];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  double msum = 0.0;
+  float *prow = (phi && qvalid) ? phi + Dh.phi_off + q * Dh.ldT : nullptr;
+
+  for (int64_t k0 = 0; k0 < Dh.T; k0 += kPhiKeys) {
+    __syncthreads();
+    // K tile [64][D] and V tile transposed [D][64], zero beyond T
+    for (int gi = tid; gi < 64 * D / 4; gi += 256) {
+      const int key = gi / (D / 4), c4 = gi % (D / 4);
+      const bool ok = k0 + key < Dh.T;
+      const int64_t src = (Dh.k_off + k0 + key) * D + 4 * c4;
+      const int vkey = vt_pos(key);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        ks[key * KSTR + 4 * c4 + e] = ok ? K[src + e] : E(0);
+        vt[(4 * c4 + e) * VSTR + vkey] = ok ? V[src + e] : E(0);
+      }
+    }
+    if (tid < 64) sbias[tid] = (k0 + tid < Dh.T && beta_in) ? beta_in[Dh.k_off + k0 + tid] : 0.0f;
+    __syncthreads();
+
+    float pf[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+      for (int u = 0; u < NU; ++u) {
+        const E *kp = &ks[(kb * 16 + c16) * KSTR + 16 * u + 4 * g];
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+          acc = __builtin_amdgcn_mfma_f64_16x16x4f64(double(In<E>::f(kp[v])), double(qf[4 * u + v]), acc, 0, 0, 0);
+      }
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kl = phi_key(kb, g, e);
+        double p = 0.0;
+        if (k0 + kl < Dh.T) p = exp(scale * acc[e] + double(sbias[kl]) - s);
+        msum += p;
+        pf[kb][e] = float(p);
+        if (prow && k0 + kl < Dh.T) prow[k0 + kl] = pf[kb][e];
+      }
+    }
+#pragma unroll
+    for (int db = 0; db < NU; ++db) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const E *vp = &vt[(db * 16 + c16) * VSTR + kb * 16 + 4 * g];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+          uacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(pf[kb][e], In<E>::f(vp[e]), uacc[db], 0, 0, 0);
+      }
+    }
+  }
+
+  // m for query q0 + c16: partial sums sit in the four lanes c16, c16+16, c16+32, c16+48
+  msum += __shfl_xor(msum, 16);
+  msum += __shfl_xor(msum, 32);
+  bool bad = false;
+  if (g == 0 && qvalid) {
+    m_out[Dh.n_off + q] = msum;
+    if (r_out) r_out[Dh.n_off + q] = msum;
+    bad |= !isfinite(msum);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double mq = __shfl(msum, 4 * g + e);
+    const int64_t qy = q0 + 4 * g + e;
+    if (qy < Dh.n) {
+#pragma unroll
+      for (int db = 0; db < NU; ++db) {
+        const float y = float(double(uacc[db][e]) / mq);
+        bad |= !isfinite(y);
+        Y_out[(Dh.n_off + qy) * D + db * 16 + c16] = y;
+      }
+    }
+  }
+  if (bad && head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
+}
+
+}  // namespace
+
+hipError_t launch_copy_words(uint64_t *dst, const uint64_t *src, int64_t count, hipStream_t s) {
+  for (int64_t base = 0; base < count; base += 384) {
+    WordChunk c;
+    const int n = int(count - base < 384 ? count - base : 384);
+    for (int i = 0; i < n; ++i) c.w[i] = src[base + i];
+    hipLaunchKernelGGL(k_put_words, dim3(2), dim3(256), 0, s, dst + base, n, c);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s) {
+  if (count <= 0) return hipSuccess;
+  int64_t blocks = (count + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_fill_i32, dim3(unsigned(blocks)), dim3(256), 0, s, p, count, value);
+  return hipGetLastError();
+}
+
+hipError_t launch_shift(const Dims &dm, const Buffers &b, hipStream_t s) {
+  dim3 grid(unsigned(dm.max_sblk), unsigned(dm.H));
+  const float sc = float(dm.scale);
+  if (dm.d == 128) {
+    if (dm.in_bf16)
+      hipLaunchKernelGGL((k_shift<128, true>), grid, dim3(256), 0, s, b.desc, b.Q, b.K, b.beta_in, sc, b.shift_part);
+    else
+      hipLaunchKernelGGL((k_shift<128, false>), grid, dim3(256), 0, s, b.desc, b.Q, b.K, b.beta_in, sc, b.shift_part);
+  } else {
+    if (dm.in_bf16)
+      hipLaunchKernelGGL((k_shift<64, true>), grid, dim3(256), 0, s, b.desc, b.Q, b.K, b.beta_in, sc, b.shift_part);
+    else
+      hipLaunchKernelGGL((k_shift<64, false>), grid, dim3(256), 0, s, b.desc, b.Q, b.K, b.beta_in, sc, b.shift_part);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_phi(const Dims &dm, const Buffers &b, int store_phi, hipStream_t s) {
+  dim3 grid(unsigned((dm.max_n + kPhiRows - 1) / kPhiRows), unsigned(dm.H));
+  float *phi = store_phi ? b.phi : nullptr;
+#define AMC_PHI_ARGS b.desc, b.Q, b.K, b.V, b.beta_in, dm.scale, b.shift_part, b.shift, b.tr_shift, phi, b.m, b.r, b.Y, b.head_status
+  if (dm.d == 128) {
+    if (dm.in_bf16)
+      hipLaunchKernelGGL((k_phi<128, true>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
+    else
+      hipLaunchKernelGGL((k_phi<128, false>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
+  } else {
+    if (dm.in_bf16)
+      hipLaunchKernelGGL((k_phi<64, true>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
+    else
+      hipLaunchKernelGGL((k_phi<64, false>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
+  }
+#undef AMC_PHI_ARGS
+  return hipGetLastError();
+}
+
+}  // namespace amc

@@ -1,0 +1,406 @@
+// Greedy key selection kernels (zhichai.net deep-dive, section 1.6; batched
+// top-k selection with delayed refit, xinfinite.net article, section 3):
+//
+//   sweep  : c_j = r^T Phi[:, j] over the unselected keys, block-local top-(K+1)
+//   merge  : per-head top-(K+1) of the block candidates; appends the K picks
+//   panel  : float64 columns Phi[:, j] of the new picks, recomputed from Q, K
+//   gram   : new columns of G = Phi_S^T Phi_S and of b = Phi_S^T m
+//   resid  : mhat = Phi_S w and r = m - mhat
+//
+// A "cycle" is the R iterations between two refits.  Within a cycle the
+// residual does not change, so the R top-k picks of the cycle are the top
+// k*R keys of a single sweep; the sweep runs once per cycle.
+#include <hip/hip_runtime.h>
+
+#include <cfloat>
+#include <climits>
+#include <cmath>
+#include <type_traits>
+
+#include "amc_internal.h"
+
+namespace amc {
+namespace {
+
+constexpr int KP_STRIDE = kMaxCycle + 1;  // candidate slots per sweep block
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// Sorts 256 (value, index) pairs in LDS, best first (value descending, index ascending).
+__device__ void block_sort256(double *v, int *ix) {
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= 256; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int p = tid ^ j;
+      if (p > tid) {
+        const double va = v[tid], vb = v[p];
+        const int ia = ix[tid], ib = ix[p];
+        const bool first_better = better(va, ia, vb, ib);
+        const bool want_first_better = (tid & k) == 0;
+        if (first_better != want_first_better) {
+          v[tid] = vb;
+          v[p] = va;
+          ix[tid] = ib;
+          ix[p] = ia;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__device__ __forceinline__ int cycle_keys(const HeadDesc &D, int cycle, int kR, int64_t *S0) {
+  const int64_t s0 = int64_t(cycle) * kR;
+  *S0 = s0;
+  if (s0 >= D.t) return 0;
+  const int64_t left = D.t - s0;
+  return int(left < kR ? left : kR);
+}
+
+// ---------------------------------------------------------------------------
+// sweep: one block = 256 columns of one head, 4 waves split the rows
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc, const float *__restrict__ phi,
+                                               const double *__restrict__ r, const int32_t *__restrict__ sel_slot,
+                                               int cycle, int kR, double *__restrict__ cand_val,
+                                               int32_t *__restrict__ cand_idx, int32_t *__restrict__ head_status) {
+  __shared__ double red[4][256];
+  __shared__ double sv[256];
+  __shared__ int si[256];
+  const int h = blockIdx.y;
+  const HeadDesc D = desc[h];
+  const int blk = blockIdx.x;
+  if (blk >= D.n_cblk) return;
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int64_t j0 = int64_t(blk) * kSweepCols + 4 * lane;
+  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
+  if (j0 < D.T) {
+    const float *p = phi + D.phi_off + j0;
+    const double *rr = r + D.n_off;
+    const int64_t ld = D.ldT;
+    int64_t i = wave;
+    for (; i + 28 < D.n; i += 32) {
+      f32x4 x[8];
+      double rv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + (i + 4 * u) * ld));
+        rv[u] = rr[i + 4 * u];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        a0 = fma(rv[u], double(x[u].x), a0);
+        a1 = fma(rv[u], double(x[u].y), a1);
+        a2 = fma(rv[u], double(x[u].z), a2);
+        a3 = fma(rv[u], double(x[u].w), a3);
+      }
+    }
+    for (; i < D.n; i += 4) {
+      const f32x4 x = *reinterpret_cast<const f32x4 *>(p + i * ld);
+      const double rv = rr[i];
+      a0 = fma(rv, double(x.x), a0);
+      a1 = fma(rv, double(x.y), a1);
+      a2 = fma(rv, double(x.z), a2);
+      a3 = fma(rv, double(x.w), a3);
+    }
+  }
+  red[wave][4 * lane + 0] = a0;
+  red[wave][4 * lane + 1] = a1;
+  red[wave][4 * lane + 2] = a2;
+  red[wave][4 * lane + 3] = a3;
+  __syncthreads();
+  const int64_t col = int64_t(blk) * kSweepCols + tid;
+  double c = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  int idx = int(col);
+  if (col >= D.T || sel_slot[D.k_off + col] != 0) {
+    c = -INFINITY;
+    idx = INT_MAX;
+  } else if (!isfinite(c)) {
+    if (head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
+    c = -DBL_MAX;  // still a valid, selectable key
+  }
+  sv[tid] = c;
+  si[tid] = idx;
+  __syncthreads();
+  block_sort256(sv, si);
+  if (tid <= Kc) {
+    const int64_t o = (D.cblk_off + blk) * KP_STRIDE + tid;
+    cand_val[o] = sv[tid];
+    cand_idx[o] = si[tid];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge: one block per head; tournament over the sorted block candidate lists
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_merge(const HeadDesc *__restrict__ desc, int cycle, int kR,
+                                               const double *__restrict__ cand_val,
+                                               const int32_t *__restrict__ cand_idx, int32_t *__restrict__ sel_slot,
+                                               int32_t *__restrict__ sel_list, int32_t *__restrict__ tr_pick,
+                                               double *__restrict__ tr_pick_score, double *__restrict__ tr_runner) {
+  __shared__ double wv[4];
+  __shared__ int wi[4], wl[4];
+  __shared__ int win_list;
+  const int h = blockIdx.x;
+  const HeadDesc D = desc[h];
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = int(D.n_cblk);
+  // each thread owns lists tid, tid+256, tid+512, tid+768
+  int pos[4] = {0, 0, 0, 0};
+  for (int rank = 0; rank <= Kc; ++rank) {
+    double bv = -INFINITY;
+    int bi = INT_MAX, bl = -1;
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int l = tid + 256 * q;
+      if (l < nl && pos[q] <= Kc) {
+        const int64_t o = (D.cblk_off + l) * KP_STRIDE + pos[q];
+        const double v = cand_val[o];
+        const int ix = cand_idx[o];
+        if (bl < 0 || better(v, ix, bv, bi)) {
+          bv = v;
+          bi = ix;
+          bl = l;
+        }
+      }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const double ov = __shfl_xor(bv, off);
+      const int oi = __shfl_xor(bi, off);
+      const int ol = __shfl_xor(bl, off);
+      if (ol >= 0 && (bl < 0 || better(ov, oi, bv, bi))) {
+        bv = ov;
+        bi = oi;
+        bl = ol;
+      }
+    }
+    if (lane == 0) {
+      wv[wave] = bv;
+      wi[wave] = bi;
+      wl[wave] = bl;
+    }
+    __syncthreads();
+    if (tid == 0) {
+      double v = wv[0];
+      int ix = wi[0], l = wl[0];
+      for (int w = 1; w < 4; ++w)
+        if (wl[w] >= 0 && (l < 0 || better(wv[w], wi[w], v, ix))) {
+          v = wv[w];
+          ix = wi[w];
+          l = wl[w];
+        }
+      win_list = l;
+      if (rank < Kc) {
+        const int64_t slot = S0 + rank;
+        if (ix >= 0 && ix < D.T) {
+          sel_list[D.t_off + slot] = ix;
+          sel_slot[D.k_off + ix] = int32_t(slot + 1);
+        }
+        if (tr_pick) {
+          tr_pick[D.t_off + slot] = ix;
+          tr_pick_score[D.t_off + slot] = v;
+        }
+      } else if (tr_runner) {
+        tr_runner[D.cyc_off + cycle] = (ix >= 0 && ix < D.T) ? v : -INFINITY;
+      }
+    }
+    __syncthreads();
+    const int l = win_list;
+    if (l >= 0 && (l & 255) == tid) pos[l >> 8]++;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// panel: float64 Phi columns of the new picks; one block = 64 queries
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_panel(const HeadDesc *__restrict__ desc, const void *__restrict__ Qv,
+                                               const void *__restrict__ Kv, const float *__restrict__ beta_in,
+                                               double scale, const double *__restrict__ shift,
+                                               const int32_t *__restrict__ sel_list, int cycle, int kR,
+                                               double *__restrict__ panel) {
+  using E = typename std::conditional<BF16, uint16_t, float>::type;
+  __shared__ float qs[64][D + 1];
+  __shared__ float kbuf[4][D];
+  const E *Q = static_cast<const E *>(Qv);
+  const E *K = static_cast<const E *>(Kv);
+  const int h = blockIdx.y;
+  const HeadDesc Dh = desc[h];
+  int64_t S0;
+  const int Kc = cycle_keys(Dh, cycle, kR, &S0);
+  if (Kc == 0) return;
+  const int64_t q0 = int64_t(blockIdx.x) * 64;
+  if (q0 >= Dh.n) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  auto cvt = [](E v) -> float {
+    if constexpr (BF16) return __uint_as_float(uint32_t(v) << 16);
+    else return v;
+  };
+  for (int e = tid; e < 64 * D; e += 256) {
+    const int r = e / D, c = e % D;
+    qs[r][c] = (q0 + r < Dh.n) ? cvt(Q[(Dh.q_off + q0 + r) * D + c]) : 0.0f;
+  }
+  __syncthreads();
+  const double s = shift[h];
+  const int64_t q = q0 + lane;
+  for (int kk = wave; kk < Kc; kk += 4) {
+    const int j = sel_list[Dh.t_off + S0 + kk];
+    const bool jok = j >= 0 && j < Dh.T;
+    for (int c = lane; c < D; c += 64) kbuf[wave][c] = jok ? cvt(K[(Dh.k_off + j) * D + c]) : 0.0f;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    double dot = 0.0;
+#pragma unroll 8
+    for (int c = 0; c < D; ++c) dot = fma(double(qs[lane][c]), double(kbuf[wave][c]), dot);
+    const double bias = (beta_in && jok) ? double(beta_in[Dh.k_off + j]) : 0.0;
+    if (q < Dh.n) panel[Dh.panel_off + (S0 + kk) * Dh.n + q] = jok ? exp(scale * dot + bias - s) : 0.0;
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// gram: G[a][b] and G[b][a] for a < S0 + Kc, b in the new slots; b_b = Phi_b^T m.
+// One block = 64 rows a (the row index a == S0 + Kc stands for m) x 16 new columns.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_gram(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
+                                              const double *__restrict__ m, int cycle, int kR,
+                                              double *__restrict__ G, double *__restrict__ bvec) {
+  constexpr int CH = 64;
+  __shared__ double xs[64][CH + 1];
+  __shared__ double zs[16][CH + 1];
+  const int h = blockIdx.z;
+  const HeadDesc D = desc[h];
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0) return;
+  const int64_t Snew = S0 + Kc;
+  const int64_t a0 = int64_t(blockIdx.x) * 64;
+  const int b0 = blockIdx.y * 16;
+  if (a0 > Snew || b0 >= Kc) return;
+  const int tid = threadIdx.x;
+  const int ta = tid >> 2, tb = (tid & 3) * 4;
+  const double *P = panel + D.panel_off;
+  const int64_t n = D.n;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int64_t i0 = 0; i0 < n; i0 += CH) {
+    for (int e = tid; e < 64 * CH; e += 256) {
+      const int r = e / CH, c = e % CH;
+      const int64_t a = a0 + r, i = i0 + c;
+      double v = 0.0;
+      if (i < n) {
+        if (a < Snew) v = P[a * n + i];
+        else if (a == Snew) v = m[D.n_off + i];
+      }
+      xs[r][c] = v;
+    }
+    for (int e = tid; e < 16 * CH; e += 256) {
+      const int r = e / CH, c = e % CH;
+      const int64_t b = S0 + b0 + r, i = i0 + c;
+      zs[r][c] = (b0 + r < Kc && i < n) ? P[b * n + i] : 0.0;
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = 0; c < CH; ++c) {
+      const double x = xs[ta][c];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] = fma(x, zs[tb + q][c], acc[q]);
+    }
+    __syncthreads();
+  }
+  const int64_t a = a0 + ta;
+  const int64_t ld = D.t;
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int bl = b0 + tb + q;
+    if (bl >= Kc) continue;
+    const int64_t b = S0 + bl;
+    if (a < Snew) {
+      G[D.tt_off + a * ld + b] = acc[q];
+      G[D.tt_off + b * ld + a] = acc[q];
+    } else if (a == Snew) {
+      bvec[D.t_off + b] = acc[q];
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// residual: mhat = Phi_S w, r = m - mhat (float64)
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_resid(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
+                                               const double *__restrict__ w, const double *__restrict__ m, int cycle,
+                                               int kR, double *__restrict__ r, double *__restrict__ mhat) {
+  __shared__ double ws[kLdsMaxT];
+  const int h = blockIdx.y;
+  const HeadDesc D = desc[h];
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0) return;
+  const int64_t p = S0 + Kc;
+  for (int a = threadIdx.x; a < p; a += 256) ws[a] = w[D.t_off + a];
+  __syncthreads();
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= D.n) return;
+  const double *P = panel + D.panel_off;
+  double acc = 0.0;
+  for (int64_t a = 0; a < p; ++a) acc = fma(P[a * D.n + i], ws[a], acc);
+  mhat[D.n_off + i] = acc;
+  r[D.n_off + i] = m[D.n_off + i] - acc;
+}
+
+}  // namespace
+
+hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  hipLaunchKernelGGL(k_sweep, dim3(unsigned(dm.max_cblk), unsigned(dm.H)), dim3(256), 0, s, b.desc, b.phi, b.r,
+                     b.sel_slot, cycle, kR, b.cand_val, b.cand_idx, b.head_status);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  hipLaunchKernelGGL(k_merge, dim3(unsigned(dm.H)), dim3(256), 0, s, b.desc, cycle, kR, b.cand_val, b.cand_idx,
+                     b.sel_slot, b.sel_list, b.tr_pick, b.tr_pick_score, b.tr_runner);
+  return hipGetLastError();
+}
+
+hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  dim3 grid(unsigned((dm.max_n + 63) / 64), unsigned(dm.H));
+#define AMC_PANEL_ARGS b.desc, b.Q, b.K, b.beta_in, dm.scale, b.shift, b.sel_list, cycle, kR, b.panel
+  if (dm.d == 128) {
+    if (dm.in_bf16) hipLaunchKernelGGL((k_panel<128, true>), grid, dim3(256), 0, s, AMC_PANEL_ARGS);
+    else hipLaunchKernelGGL((k_panel<128, false>), grid, dim3(256), 0, s, AMC_PANEL_ARGS);
+  } else {
+    if (dm.in_bf16) hipLaunchKernelGGL((k_panel<64, true>), grid, dim3(256), 0, s, AMC_PANEL_ARGS);
+    else hipLaunchKernelGGL((k_panel<64, false>), grid, dim3(256), 0, s, AMC_PANEL_ARGS);
+  }
+#undef AMC_PANEL_ARGS
+  return hipGetLastError();
+}
+
+hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  // rows a in [0, S0 + Kc], so up to max_t + 1 rows; new columns up to kR
+  const int64_t rows = dm.max_t + 1;
+  dim3 grid(unsigned((rows + 63) / 64), unsigned((kR + 15) / 16), unsigned(dm.H));
+  hipLaunchKernelGGL(k_gram, grid, dim3(256), 0, s, b.desc, b.panel, b.m, cycle, kR, b.G, b.bvec);
+  return hipGetLastError();
+}
+
+hipError_t launch_resid(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  dim3 grid(unsigned((dm.max_n + 255) / 256), unsigned(dm.H));
+  hipLaunchKernelGGL(k_resid, grid, dim3(256), 0, s, b.desc, b.panel, b.w, b.m, cycle, kR, b.r, b.mhat);
+  return hipGetLastError();
+}
+
+}  // namespace amc

@@ -1,0 +1,221 @@
+/*
+ * amc.h - attention-matching KV compaction on one MI355X (gfx950).
+ *
+ * C ABI of libamc.  The method is "Fast KV Compaction via Attention
+ * Matching" (arXiv 2602.16284) as described on the pages that summarise it:
+ *
+ *   - problem statement: compact a block of keys/values (K, V) of length T to
+ *     t << T entries (C_k, beta, C_v) so that, on reference queries, the
+ *     compacted block reproduces the local attention output and the attention
+ *     mass (xinfinite.net article, section 1; youleyou.com rewrite, "the
+ *     math", formulas 1 and 2; zhichai.net deep-dive, section 1.3);
+ *   - C_k is a subset of the original keys, chosen by greedy orthogonal
+ *     matching pursuit on the mass features Phi_ij = exp(q_i . k_j), with an
+ *     NNLS refit of non-negative weights w after each pick and beta = log w
+ *     (zhichai.net deep-dive, section 1.6; xinfinite.net article, section 2,
+ *     step 2 and Fig. 1);
+ *   - the batched variant takes the top k keys per iteration and refits only
+ *     every R iterations (xinfinite.net article, section 3, Table 1);
+ *   - C_v is the ordinary least squares fit of the attention output with C_k
+ *     and beta fixed (xinfinite.net article, section 2, step 3);
+ *   - beta is an additive per-token logit bias, one scalar per compacted
+ *     token (zhichai.net deep-dive, sections 1.4 and 4.1);
+ *   - heads with different budgets are packed flat, varlen, without padding
+ *     (zhichai.net deep-dive, section 4.2).
+ *
+ * Conventions used by every entry point:
+ *
+ *   - Heads are independent problems.  Head h owns rows cu_q[h]..cu_q[h+1]-1
+ *     of Q and rows cu_k[h]..cu_k[h+1]-1 of K, V (and of beta_in).  Q, K and V
+ *     are row-major with head_dim contiguous elements per row.
+ *   - The logit of query i and key j is  l_ij = scale * q_i . k_j + beta_in_j
+ *     (scale defaults to 1/sqrt(head_dim), the model's own logit scale).
+ *   - Outputs are packed by cu_budgets (amc_output_offsets): head h owns
+ *     output rows cu_budgets[h]..cu_budgets[h+1]-1, in ascending original key
+ *     index.  A compacted key whose NNLS weight is zero keeps its slot with
+ *     beta = -inf and a zero value row.
+ *   - All device buffers belong to the caller; the library never allocates
+ *     device memory.  Host arrays are read only during the call.
+ *   - Calls that take a stream enqueue work on it and return without
+ *     synchronising.  Argument, shape and workspace errors are detected before
+ *     anything is enqueued (no partial output).  A failed launch returns
+ *     AMC_ERR_HIP.
+ *   - Data-dependent numeric events are reported per head in head_status
+ *     (device int32[H], optional) as AMC_HS_* bits; the call still completes.
+ *   - The library holds no global mutable state; calls are reentrant.  Two
+ *     calls that share a workspace must not overlap in time.
+ */
+#ifndef AMC_H
+#define AMC_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define AMC_VERSION 1
+
+typedef enum {
+  AMC_OK = 0,
+  AMC_ERR_INVALID_ARG = 1, /* a pointer, size, shape or option is invalid */
+  AMC_ERR_UNSUPPORTED = 2, /* valid but outside what this build implements */
+  AMC_ERR_WORKSPACE = 3,   /* workspace or trace buffer too small / misaligned */
+  AMC_ERR_HIP = 4          /* a HIP runtime call or kernel launch failed */
+} amc_status;
+
+typedef enum { AMC_F32 = 0, AMC_BF16 = 1 } amc_dtype;
+
+typedef enum {
+  AMC_SEL_OMP = 0,        /* one key per iteration, NNLS refit after each */
+  AMC_SEL_OMP_BATCHED = 1 /* top-k keys per iteration, refit every R iterations */
+} amc_select;
+
+/* head_status bits */
+#define AMC_HS_CHOL_JITTER 1u    /* the value fit needed a diagonal shift */
+#define AMC_HS_NNLS_CAP 2u       /* an NNLS refit hit its iteration cap */
+#define AMC_HS_NONFINITE 4u      /* Q, K, V or beta_in produced a non-finite logit or output */
+#define AMC_HS_NNLS_SINGULAR 8u  /* a candidate key was linearly dependent on the active set */
+
+/* amc_options.flags */
+#define AMC_FLAG_TRACE 1u /* fill the trace buffer (selection order, scores, weights) */
+
+/* Kernel classes reported by the timer (amc_timer_read). */
+typedef enum {
+  AMC_K_INIT = 0,
+  AMC_K_SHIFT = 1,   /* per-head logit maximum */
+  AMC_K_PHI = 2,     /* mass features, target mass, attention output */
+  AMC_K_SWEEP = 3,   /* r^T Phi correlation sweep with block top-k */
+  AMC_K_MERGE = 4,   /* per-head top-k merge and selection update */
+  AMC_K_PANEL = 5,   /* float64 columns of the selected keys */
+  AMC_K_GRAM = 6,    /* Gram matrix and right-hand side update */
+  AMC_K_NNLS = 7,    /* NNLS refit */
+  AMC_K_RESID = 8,   /* residual r = m - Phi_S w */
+  AMC_K_OLS_NORMAL = 9, /* normal equations of the value fit */
+  AMC_K_OLS_SOLVE = 10, /* Cholesky solve of the value fit */
+  AMC_K_PACK = 11,   /* sorted, packed outputs */
+  AMC_NUM_KERNEL_CLASSES = 12
+} amc_kernel_class;
+
+typedef struct {
+  int32_t num_heads;      /* H >= 1 */
+  int32_t head_dim;       /* d in {64, 128}; else AMC_ERR_UNSUPPORTED */
+  const int64_t *cu_q;    /* HOST int64[H+1], cu_q[0] = 0, strictly increasing */
+  const int64_t *cu_k;    /* HOST int64[H+1], cu_k[0] = 0, strictly increasing */
+  const int64_t *budgets; /* HOST int64[H], 1 <= budgets[h] <= T_h */
+  amc_dtype in_dtype;     /* storage type of Q, K, V (C_k is written in it too) */
+  float scale;            /* logit scale; 0 means 1/sqrt(head_dim) */
+} amc_problem;
+
+typedef struct {
+  amc_select select;
+  int32_t topk;           /* k: keys taken per iteration (1 for AMC_SEL_OMP) */
+  int32_t refit_every;    /* R: refit after every R-th iteration (1 for AMC_SEL_OMP) */
+  int32_t nnls_pg_iters;  /* projected-gradient iterations before the active-set polish */
+  int32_t nnls_max_iters; /* active-set iteration cap per refit (0 = 3 * budget + 30) */
+  double nnls_tol;        /* KKT tolerance relative to max |b| in unit-diagonal form (0 = 10 eps t) */
+  uint64_t phi_budget_bytes; /* Phi is stored when sum_h n_h T_h * 4 <= this */
+  amc_dtype cv_dtype;     /* C_v output type (default AMC_F32) */
+  uint32_t flags;         /* AMC_FLAG_* */
+  void *timer;            /* optional amc_timer_create() handle; NULL = none */
+} amc_options;
+
+/* Offsets, in bytes from the start of the trace buffer, of its sections.
+ * Sections (each 256-byte aligned):
+ *   shift      double [H]          the per-head logit shift s used for Phi
+ *   pick       int32  [sum t_h]    original key index, in selection order, at cu_budgets[h]
+ *   pick_score double [sum t_h]    r^T Phi[:, j] of each pick in the sweep that took it
+ *   weight     double [sum t_h]    final NNLS weight w of each pick (selection order)
+ *   runner_up  double [sum c_h]    best score not taken by each cycle, at cu_cycles[h]
+ *   nnls_iters int32  [sum c_h]    active-set iterations of the refit closing each cycle
+ * where a "cycle" is the R iterations between two refits; head h has
+ * c_h = ceil(t_h / (k R)) cycles (amc_cycle_offsets). */
+typedef struct {
+  uint64_t shift, pick, pick_score, weight, runner_up, nnls_iters;
+  uint64_t total_bytes;
+} amc_trace_layout;
+
+/* Fills *o with the defaults: plain OMP (k = R = 1), 8 projected-gradient
+ * iterations, automatic NNLS cap and tolerance, 64 GiB Phi budget, float32
+ * C_v, no trace, no timer. */
+void amc_default_options(amc_options *o);
+
+/* Workspace bytes amc_compact needs for this problem (device memory,
+ * 256-byte aligned).  Errors: AMC_ERR_INVALID_ARG for an invalid problem or
+ * options, AMC_ERR_UNSUPPORTED for a shape outside this build. */
+amc_status amc_workspace_size(const amc_problem *p, const amc_options *o, uint64_t *bytes);
+
+/* cu_budgets (HOST int64[H+1]): exclusive prefix sum of the budgets; the
+ * output row range of each head.  Selection-batch sizes do not change it. */
+amc_status amc_output_offsets(const amc_problem *p, int64_t *cu_budgets);
+
+/* cu_cycles (HOST int64[H+1]): exclusive prefix sum of the per-head number of
+ * refit cycles ceil(t_h / (k R)); indexes the per-cycle trace sections. */
+amc_status amc_cycle_offsets(const amc_problem *p, const amc_options *o, int64_t *cu_cycles);
+
+/* Trace buffer layout for this problem and these options. */
+amc_status amc_trace_layout_for(const amc_problem *p, const amc_options *o, amc_trace_layout *layout);
+
+/* Compacts every head.  Device pointers:
+ *   Q        [sum n_h][d]  in_dtype
+ *   K, V     [sum T_h][d]  in_dtype
+ *   beta_in  [sum T_h]     float32, nullable (all zero); an existing per-key
+ *                          logit bias, e.g. from an earlier compaction
+ *   Ck       [sum t_h][d]  in_dtype, exact copies of the selected keys
+ *   beta     [sum t_h]     float32, beta_in_j + log w_j (-inf where w_j = 0)
+ *   Cv       [sum t_h][d]  cv_dtype
+ *   sel_idx  [sum t_h]     int32, nullable: selected original index (within the head)
+ *   head_status [H]        int32, nullable: AMC_HS_* bits
+ *   trace    trace_bytes   nullable unless AMC_FLAG_TRACE (layout: amc_trace_layout_for)
+ *   workspace workspace_bytes (>= amc_workspace_size, 256-byte aligned)
+ * stream is a hipStream_t (NULL: the default stream). */
+amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q, const void *K,
+                       const void *V, const float *beta_in, void *Ck, float *beta, void *Cv,
+                       int32_t *sel_idx, int32_t *head_status, void *trace, uint64_t trace_bytes,
+                       void *workspace, uint64_t workspace_bytes, void *stream);
+
+/* Stage 1 alone: the per-head shift s_h (logit maximum, float64[H]), the mass
+ * features Phi = exp(l - s) (float32 [n_h][T_h] per head, packed at
+ * sum_{g<h} n_g T_g; nullable), the target mass m = Phi 1 (float64[sum n_h])
+ * and the attention output Y = Phi V / m (float32 [sum n_h][d])
+ * (zhichai.net deep-dive, section 1.6: Phi and m; xinfinite.net article,
+ * section 2, step 3: the output to match).  workspace as for amc_compact. */
+amc_status amc_mass_features(const amc_problem *p, const void *Q, const void *K, const void *V,
+                             const float *beta_in, double *shift, float *phi, double *m, float *Y,
+                             int32_t *head_status, void *workspace, uint64_t workspace_bytes,
+                             void *stream);
+
+/* Workspace bytes for amc_mass_features. */
+amc_status amc_mass_features_workspace(const amc_problem *p, uint64_t *bytes);
+
+/* Batched NNLS: for each problem b, w_b = argmin_{w >= 0} 0.5 w^T G_b w - g_b^T w
+ * with G_b symmetric positive semi-definite (the Gram form of the bias fit,
+ * zhichai.net deep-dive, section 1.6; projected gradient, xinfinite.net
+ * article, Fig. 2; exact active-set polish).  Device pointers:
+ *   G      float64, problem b at G + cu_t2[b] (dense t_b x t_b, row-major)
+ *   g      float64[sum t_b] at cu_t[b];  w  float64[sum t_b] (in: warm start
+ *          if warm != 0, out: solution)
+ *   iters  int32[num] nullable: active-set iterations used
+ *   status int32[num] nullable: AMC_HS_NNLS_* bits
+ * cu_t (HOST int64[num+1]) gives the sizes; cu_t2 is derived (sum of t_b^2).
+ * t_b <= 192 in this build (else AMC_ERR_UNSUPPORTED). */
+amc_status amc_nnls(int32_t num, const int64_t *cu_t, const double *G, const double *g, double *w,
+                    int32_t warm, int32_t pg_iters, int32_t max_iters, double tol, int32_t *iters,
+                    int32_t *status, void *stream);
+
+/* Kernel timer: HIP events recorded around every launch of an amc_compact
+ * call whose options carry the handle.  Reading synchronises on the events. */
+amc_status amc_timer_create(void **timer);
+amc_status amc_timer_reset(void *timer);
+/* Launch count and summed duration (ms) of one kernel class since the last reset. */
+amc_status amc_timer_read(void *timer, int32_t kernel_class, int64_t *launches, double *total_ms);
+void amc_timer_destroy(void *timer);
+
+const char *amc_status_string(amc_status s);
+int amc_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* AMC_H */

@@ -1,0 +1,91 @@
+"""Helpers shared by the GPU tests, the smoke check and the benchmark:
+moving seeded inputs to the device, and comparing a libamc compaction with
+the float64 oracle under the replay protocol.
+
+Replay protocol: the oracle re-runs the greedy selection, following the
+GPU's picks.  At each iteration where the oracle's own margin (score of the
+last pick minus the best unpicked score, over the top score) exceeds 1e-6,
+the GPU's picks must be the oracle's; below that the GPU's pick is accepted.
+Then: beta within 1e-3 (absolute) on keys active on both sides, a key active
+on one side only carries at most 1e-6 of that side's largest weight, and the
+relative mass and attention-output errors of the GPU's compacted block are
+within 1e-3 (absolute) of the oracle's own.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import oracle
+import synth
+from oracle import amc_oracle as O
+
+MARGIN_TOL = 1e-6
+BETA_TOL = 1e-3
+ERR_TOL = 1e-3
+WEIGHT_REL = 1e-6
+
+
+def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
+    if dtype == "bf16":
+        return torch.from_numpy(synth.bf16_bits(x).view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(np.asarray(x, dtype=np.float32)).to(device)
+
+
+def pack_heads(heads, dtype: str, device="cuda"):
+    """Concatenates per-head (Q, K, V) into packed device tensors and offsets."""
+    cu_q, cu_k = [0], [0]
+    for h in heads:
+        cu_q.append(cu_q[-1] + h.Q.shape[0])
+        cu_k.append(cu_k[-1] + h.K.shape[0])
+    Q = to_device(np.concatenate([h.Q for h in heads]), dtype, device)
+    K = to_device(np.concatenate([h.K for h in heads]), dtype, device)
+    V = to_device(np.concatenate([h.V for h in heads]), dtype, device)
+    return Q, K, V, cu_q, cu_k
+
+
+def head_outputs(res, h: int):
+    Ck, beta, Cv, sel = res.head(h)
+    return (Ck.float().cpu().numpy().astype(np.float64), beta.cpu().numpy().astype(np.float64),
+            Cv.float().cpu().numpy().astype(np.float64), sel.cpu().numpy().astype(np.int64))
+
+
+def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, trace=None):
+    """Compares head h of a libamc result (run with trace=True) with the
+    oracle.  Returns a report dict; ``report['ok']`` is the verdict."""
+    if trace is None:
+        trace = res.trace()
+    picks_order = [int(j) for j in trace["pick"][h]]
+    sizes = O.iteration_sizes(t, k, R)
+    per_it, pos = [], 0
+    for kk, _ in sizes:
+        per_it.append(picks_order[pos: pos + kk])
+        pos += kk
+    ref = oracle.compact(Q, K, V, t, k, R, beta_in=beta_in, replay=per_it, margin_tol=MARGIN_TOL)
+    Ck, beta, Cv, sel = head_outputs(res, h)
+    rep = {"mismatch_iters": [s.it for s in ref.selection.steps if s.mismatch],
+           "forced_iters": [s.it for s in ref.selection.steps if s.forced],
+           "min_margin": float(min(s.margin for s in ref.selection.steps))}
+    rep["same_set"] = bool(np.array_equal(np.asarray(ref.sel_idx), sel))
+    rep["ck_exact"] = bool(np.array_equal(Ck, np.asarray(K, dtype=np.float64)[sel])) if rep["same_set"] else False
+    # weights: the GPU's beta carries beta_in + log w
+    bi = np.zeros(len(sel)) if beta_in is None else np.asarray(beta_in, dtype=np.float64)[sel]
+    with np.errstate(invalid="ignore"):
+        w_gpu = np.where(np.isfinite(beta), np.exp(beta - bi), 0.0)
+    w_ref = ref.w
+    act_g, act_r = w_gpu > 0, w_ref > 0
+    both = act_g & act_r
+    rep["beta_maxdiff"] = float(np.max(np.abs(beta[both] - ref.beta[both]))) if np.any(both) else 0.0
+    only_g = act_g & ~act_r
+    only_r = act_r & ~act_g
+    rep["one_sided_ok"] = bool(np.all(w_gpu[only_g] <= WEIGHT_REL * w_gpu.max(initial=0.0)) and
+                               np.all(w_ref[only_r] <= WEIGHT_REL * w_ref.max(initial=0.0)))
+    e_gpu = oracle.errors(Q, K, V, Ck, beta, Cv, beta_in)
+    e_ref = oracle.errors(Q, K, V, ref.Ck, ref.beta, ref.Cv, beta_in)
+    rep["e_gpu"], rep["e_ref"] = e_gpu, e_ref
+    rep["e_mass_diff"] = abs(e_gpu[0] - e_ref[0])
+    rep["e_out_diff"] = abs(e_gpu[1] - e_ref[1])
+    rep["ok"] = (not rep["mismatch_iters"] and rep["same_set"] and rep["ck_exact"] and
+                 rep["beta_maxdiff"] <= BETA_TOL and rep["one_sided_ok"] and
+                 rep["e_mass_diff"] <= ERR_TOL and rep["e_out_diff"] <= ERR_TOL)
+    return rep

@@ -1,0 +1,245 @@
+"""GPU parity: libamc (through its C ABI) against the float64 oracle."""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from attention_matching_least_amd import amc
+from oracle import amc_oracle as O
+
+from amc_check import head_outputs, pack_heads, replay_check, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+# ----------------------------------------------------------------------------
+# stage 1: shift, Phi, m, Y
+# ----------------------------------------------------------------------------
+@pytest.mark.parametrize("dtype,d,ns,Ts,with_beta", [
+    ("f32", 64, [70, 130, 64], [100, 260, 64], False),
+    ("bf16", 128, [65, 200], [132, 516], True),
+    ("bf16", 64, [1, 127], [4, 200], True),
+])
+def test_mass_features(dtype, d, ns, Ts, with_beta):
+    _say(f"mass_features {dtype} d={d} n={ns} T={Ts}")
+    heads = [synth.make_head([20, i], n, T, d, dtype == "bf16", dtype) for i, (n, T) in enumerate(zip(ns, Ts))]
+    Q, K, V, cu_q, cu_k = pack_heads(heads, dtype)
+    beta = None
+    betas = [None] * len(heads)
+    if with_beta:
+        betas = [synth.random_beta([21, i], T, 2.0) for i, T in enumerate(Ts)]
+        beta = torch.from_numpy(np.concatenate(betas).astype(np.float32)).cuda()
+    shift, phi, m, Y, hs = amc.mass_features(Q, K, V, cu_q=cu_q, cu_k=cu_k, beta_in=beta)
+    shift, phi, m, Y = shift.cpu().numpy(), phi.cpu().numpy(), m.cpu().numpy(), Y.cpu().numpy()
+    assert np.all(hs.cpu().numpy() == 0)
+    po = 0
+    for i, h in enumerate(heads):
+        n, T = h.Q.shape[0], h.K.shape[0]
+        L = oracle.logits(h.Q, h.K, betas[i])
+        smax = L.max()
+        tol_s = 1e-3 * abs(smax) + 1e-3 if dtype == "bf16" else 0.02 * abs(smax) + 0.5
+        assert abs(shift[i] - smax) <= tol_s, (shift[i], smax)
+        f = oracle.mass_features(h.Q, h.K, h.V, betas[i], shift=shift[i])
+        ph = phi[po: po + n * T].reshape(n, T)
+        po += n * T
+        assert np.all(np.abs(ph - f.Phi) <= 2e-7 * f.Phi + 1e-37)
+        mm = m[cu_q[i]: cu_q[i + 1]]
+        assert np.max(np.abs(mm - f.m) / f.m) < 1e-12
+        yy = Y[cu_q[i]: cu_q[i + 1]]
+        assert np.max(np.abs(yy - f.Y)) < 2e-5 * max(1.0, np.max(np.abs(f.Y)))
+
+
+# ----------------------------------------------------------------------------
+# NNLS on given Gram systems
+# ----------------------------------------------------------------------------
+def _phi_like(rng, n, t, spread):
+    d = 8
+    Qm = rng.normal(size=(n, d))
+    Km = rng.normal(size=(t, d)) * spread / math.sqrt(d)
+    return np.exp(Qm @ Km.T - 2.0)
+
+
+@pytest.mark.parametrize("pg_iters", [0, 8])
+def test_nnls_against_oracle(pg_iters):
+    rng = np.random.default_rng(5)
+    Gs, bs, As, ys = [], [], [], []
+    for t in (1, 2, 5, 17, 40, 64, 100, 164, 192):
+        A = _phi_like(rng, 400, t, 5.0)
+        y = A @ (np.abs(rng.normal(size=t)) * (rng.random(t) > 0.3)) + 0.05 * rng.normal(size=400) * A.mean()
+        As.append(A)
+        ys.append(y)
+        Gs.append(A.T @ A)
+        bs.append(A.T @ y)
+    _say(f"nnls {len(Gs)} systems, pg_iters={pg_iters}")
+    ws, iters, status = amc.nnls(Gs, bs, pg_iters=pg_iters)
+    for A, y, G, b, w in zip(As, ys, Gs, bs, ws):
+        ref = oracle.fnnls(G, b)
+        assert O.nnls_kkt_violation(G, b, w) < 1e-8
+        assert np.linalg.norm(A @ (w - ref)) <= 1e-8 * np.linalg.norm(y)
+        big = ref > 1e-6 * ref.max()
+        assert np.allclose(w[big], ref[big], rtol=1e-5)
+    # warm start from a random feasible point reaches the same minimiser
+    w0 = [np.abs(rng.normal(size=len(b))) for b in bs]
+    ws2, _, _ = amc.nnls(Gs, bs, w0=w0, pg_iters=pg_iters)
+    for A, y, w, w2 in zip(As, ys, ws, ws2):
+        assert np.linalg.norm(A @ (w - w2)) <= 1e-8 * np.linalg.norm(y)
+
+
+# ----------------------------------------------------------------------------
+# whole compaction
+# ----------------------------------------------------------------------------
+def _run(heads, budgets, dtype, k=1, R=1, beta_in=None, **kw):
+    Q, K, V, cu_q, cu_k = pack_heads(heads, dtype)
+    bt = None
+    if beta_in is not None:
+        bt = torch.from_numpy(np.concatenate(beta_in).astype(np.float32)).cuda()
+    sel = "omp" if (k == 1 and R == 1) else "batched"
+    res = amc.compact(Q, K, V, budgets, cu_q=cu_q, cu_k=cu_k, beta_in=bt, select=sel, topk=k, refit_every=R,
+                      trace=True, **kw)
+    torch.cuda.synchronize()
+    return res
+
+
+def _assert_ok(rep, tag):
+    _say(f"{tag}: {rep}")
+    assert rep["ok"], (tag, rep)
+
+
+def test_compact_single_head_fp32():
+    w = synth.workload(0)
+    h = w.head(0)
+    _say("workload 0")
+    res = _run([h], [32], "f32")
+    assert int(res.head_status[0]) == 0
+    tr = res.trace()
+    _assert_ok(replay_check(h.Q, h.K, h.V, 32, 1, 1, res, 0, trace=tr), "workload0")
+
+
+@pytest.mark.parametrize("k,R", [(1, 1), (4, 2), (3, 3)])
+def test_compact_varlen_ragged(k, R):
+    shapes = [(300, 700, 40), (129, 257, 23), (200, 1000, 64)]
+    heads = [synth.make_head([30, i], n, T, 128, True, "bf16") for i, (n, T, _) in enumerate(shapes)]
+    budgets = [t for _, _, t in shapes]
+    betas = [synth.random_beta([31, i], T, 1.0) for i, (_, T, _) in enumerate(shapes)]
+    _say(f"varlen k={k} R={R}")
+    res = _run(heads, budgets, "bf16", k, R, beta_in=betas)
+    hs = res.head_status.cpu().numpy()
+    assert np.all(hs == 0), hs
+    tr = res.trace()
+    for i, h in enumerate(heads):
+        _assert_ok(replay_check(h.Q, h.K, h.V, budgets[i], k, R, res, i, beta_in=betas[i], trace=tr), f"head{i}")
+
+
+def test_compact_d64_bf16_batched():
+    heads = [synth.make_head([40, i], 256, 512, 64, True, "bf16") for i in range(2)]
+    res = _run(heads, [32, 31], "bf16", 4, 2)
+    tr = res.trace()
+    for i, h in enumerate(heads):
+        _assert_ok(replay_check(h.Q, h.K, h.V, [32, 31][i], 4, 2, res, i, trace=tr), f"d64 head{i}")
+
+
+def test_determinism():
+    heads = [synth.make_head([50, i], 200, 600, 128, True, "bf16") for i in range(3)]
+    a = _run(heads, [20, 30, 25], "bf16", 4, 2)
+    b = _run(heads, [20, 30, 25], "bf16", 4, 2)
+    for x, y in ((a.Ck, b.Ck), (a.beta, b.beta), (a.Cv, b.Cv), (a.sel_idx, b.sel_idx)):
+        assert torch.equal(x.view(torch.uint8) if x.dtype != torch.int32 else x,
+                           y.view(torch.uint8) if y.dtype != torch.int32 else y)
+
+
+def test_full_budget_identity():
+    h = synth.make_head(np.random.SeedSequence([0, 5]), 256, 64, 64, False, "f32")
+    res = _run([h], [64], "f32")
+    Ck, beta, Cv, sel = head_outputs(res, 0)
+    assert np.array_equal(sel, np.arange(64))
+    assert np.max(np.abs(beta)) < 1e-6
+    assert np.max(np.abs(Cv - h.V)) < 1e-4
+    e = oracle.errors(h.Q, h.K, h.V, Ck, beta, Cv)
+    assert e[0] < 1e-9 and e[1] < 1e-5
+
+
+def test_budget_one_closed_form():
+    h = synth.make_head([60, 1], 300, 400, 128, True, "bf16")
+    res = _run([h], [1], "bf16")
+    Ck, beta, Cv, sel = head_outputs(res, 0)
+    f = oracle.mass_features(h.Q, h.K, h.V)
+    j = int(np.argmax(f.Phi.T @ f.m))
+    assert sel[0] == j
+    phi = f.Phi[:, j]
+    w = max(0.0, phi @ f.m) / (phi @ phi)
+    assert abs(beta[0] - math.log(w)) < 1e-6
+    # one key: the output is that key's value, so the fit is the mean of Y rows weighted
+    assert np.allclose(Cv[0], f.Y.mean(axis=0), atol=1e-4)
+
+
+def test_duplicate_keys():
+    """Exact duplicate keys score identically; the lower index wins on both sides."""
+    base = synth.make_head([70, 2], 300, 400, 128, True, "bf16")
+    K = base.K.copy()
+    V = base.V.copy()
+    K[150:200] = K[0:50]
+    V[150:200] = V[0:50]
+    h = synth.Head(base.Q, K, V, base.centres, True)
+    res = _run([h], [60], "bf16")
+    rep = replay_check(h.Q, h.K, h.V, 60, 1, 1, res, 0)
+    _say(f"duplicates: status {int(res.head_status[0])}")
+    _assert_ok(rep, "duplicates")
+
+
+def test_fewer_queries_than_budget():
+    """n < t: Phi_S loses column rank, the Gram system is singular in float64
+    (cond(G) = cond(Phi_S)^2 > 1e14) and dependent candidates are dropped from
+    the fit (AMC_HS_NNLS_SINGULAR).  The weights are not unique there, so the
+    compacted block is held to the oracle's errors, not to its selection."""
+    base = synth.make_head([70, 1], 40, 300, 128, True, "bf16")
+    res = _run([base], [60], "bf16")
+    rep = replay_check(base.Q, base.K, base.V, 60, 1, 1, res, 0)
+    _say(f"n<t: {rep} status {int(res.head_status[0])}")
+    assert int(res.head_status[0]) & ~amc.HS_NNLS_SINGULAR == 0
+    assert rep["ck_exact"] or not rep["same_set"]
+    assert rep["e_mass_diff"] <= 1e-3 and rep["e_out_diff"] <= 1e-3
+    _, _, _, sel = head_outputs(res, 0)
+    assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < 300
+
+
+def test_nonfinite_input_is_flagged_and_isolated():
+    heads = [synth.make_head([80, i], 100, 300, 128, True, "bf16") for i in range(2)]
+    Qb = heads[1].Q.copy()
+    Qb[5, 3] = np.nan
+    heads[1] = synth.Head(Qb, heads[1].K, heads[1].V, heads[1].centres, True)
+    res = _run(heads, [10, 10], "bf16")
+    hs = res.head_status.cpu().numpy()
+    assert hs[1] & amc.HS_NONFINITE
+    assert hs[0] == 0
+    _assert_ok(replay_check(heads[0].Q, heads[0].K, heads[0].V, 10, 1, 1, res, 0), "clean head next to a NaN head")
+
+
+@pytest.mark.slow
+def test_workload1_full_size_sampled():
+    w = synth.workload(1)
+    heads = w.heads()
+    _say("workload 1: 8 heads T=8192 n=4096 t=164 plain OMP")
+    res = _run(heads, w.budgets, w.dtype)
+    assert np.all(res.head_status.cpu().numpy() == 0)
+    tr = res.trace()
+    for h in (0, 5):
+        _assert_ok(replay_check(heads[h].Q, heads[h].K, heads[h].V, 164, 1, 1, res, h, trace=tr), f"w1 head{h}")
+
+
+@pytest.mark.slow
+def test_workload2_full_size_sampled():
+    w = synth.workload(2)
+    _say("workload 2: generating 288 heads")
+    heads = w.heads()
+    res = _run(heads, w.budgets, w.dtype, w.topk, w.refit_every)
+    assert np.all(res.head_status.cpu().numpy() == 0)
+    tr = res.trace()
+    for h in (0, 201):
+        _assert_ok(replay_check(heads[h].Q, heads[h].K, heads[h].V, 164, 4, 2, res, h, trace=tr), f"w2 head{h}")
