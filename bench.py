@@ -1,0 +1,204 @@
+"""Throughput benchmark of attention-matching KV compaction on one MI355X.
+
+A step is one amc_compact call over the whole batch of heads (every stage:
+shift, mass features, the selection loop with its NNLS refits, the value fit
+and the packing), with inputs already resident in HBM.  The default workload
+is a Qwen3-4B-shaped stack: 36 layers x 8 KV heads = 288 heads, T = 8192 keys,
+n = 4096 reference queries, d = 128, budget 164 (50x), batched selection with
+top-k = 4 and a refit every 2 iterations, bf16 inputs.
+
+Prints one JSON line (rank 0).  The dominant kernel's roofline figure comes
+from the library's HIP-event timer over the timed steps; the CPU baseline is
+the float64 oracle on a small seeded sample of the same heads.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+from concurrent.futures import ProcessPoolExecutor
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import synth  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_traffic.md")
+SWEEP_SOURCE = os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_select.hip")
+
+
+def _head_bits(args):
+    idx, h = args
+    w = synth.workload(idx)
+    head = w.head(h)
+    return (synth.bf16_bits(head.Q), synth.bf16_bits(head.K), synth.bf16_bits(head.V)) if w.dtype == "bf16" else \
+        (head.Q.astype(np.float32), head.K.astype(np.float32), head.V.astype(np.float32))
+
+
+def generate(idx: int, workers: int):
+    w = synth.workload(idx)
+    H = w.num_heads
+    jobs = [(idx, h) for h in range(H)]
+    if workers > 1 and H > 1:
+        with ProcessPoolExecutor(max_workers=workers) as ex:
+            parts = list(ex.map(_head_bits, jobs, chunksize=max(1, H // (4 * workers))))
+    else:
+        parts = [_head_bits(j) for j in jobs]
+    Q = np.concatenate([p[0] for p in parts])
+    K = np.concatenate([p[1] for p in parts])
+    V = np.concatenate([p[2] for p in parts])
+    return w, Q, K, V
+
+
+def sweep_source_hash() -> str:
+    with open(SWEEP_SOURCE, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def read_traffic():
+    """HBM bytes per sweep launch measured by rocprofv3 counters, if they were
+    taken on the current sweep source (else None)."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    vals = {}
+    with open(TRAFFIC_FILE) as f:
+        for line in f:
+            if line.startswith("traffic:"):
+                for kv in line[len("traffic:"):].split():
+                    k, v = kv.split("=")
+                    vals[k] = v
+    if vals.get("source_sha") != sweep_source_hash():
+        return None
+    try:
+        return float(vals["bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(idx: int, sample_heads: int):
+    import oracle
+
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max([int(i.get("num_threads", 1)) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = len(os.sched_getaffinity(0))
+    w = synth.workload(idx)
+    heads = w.heads(list(range(sample_heads)))
+    t0 = time.perf_counter()
+    for h, b in zip(heads, w.budgets[:sample_heads]):
+        oracle.compact(h.Q, h.K, h.V, b, w.topk, w.refit_every)
+    dt = time.perf_counter() - t0
+    return {"value": sample_heads / dt, "unit": "heads/s", "cores": threads, "kind": "oracle",
+            "sample": f"first {sample_heads} heads of the workload, float64 numpy/scipy oracle, {dt:.1f} s"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2],
+                    help="1: one 8-head layer, plain OMP; 2: 288-head stack, batched selection")
+    ap.add_argument("--cpu-sample", type=int, default=3, help="oracle heads timed for the CPU baseline (0: skip)")
+    ap.add_argument("--workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    ap.add_argument("--no-timer", action="store_true", help="do not record per-kernel events")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for {args.gpus}); the heads of a call are independent, "
+              "so a multi-GPU run would shard them by head with no collective on the hot path.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    from attention_matching_least_amd import amc
+
+    dev = torch.device("cuda:0")
+    t_gen = time.perf_counter()
+    w, Qb, Kb, Vb = generate(args.workload, args.workers)
+    gen_s = time.perf_counter() - t_gen
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    def up(a):
+        t = torch.from_numpy(a.view(np.int16) if a.dtype == np.uint16 else a)
+        return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
+
+    Q, K, V = up(Qb), up(Kb), up(Vb)
+    del Qb, Kb, Vb
+    H = w.num_heads
+    cu_q = [w.n * h for h in range(H + 1)]
+    cu_k = [w.T * h for h in range(H + 1)]
+    select = "omp" if (w.topk == 1 and w.refit_every == 1) else "batched"
+    kw = dict(cu_q=cu_q, cu_k=cu_k, select=select, topk=w.topk, refit_every=w.refit_every)
+    ws_bytes = amc.compact_workspace_bytes(cu_q, cu_k, w.budgets, w.d, tdt, select=select, topk=w.topk,
+                                           refit_every=w.refit_every)
+    workspace = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
+    timer = None if args.no_timer else amc.Timer()
+
+    for _ in range(args.warmup):
+        amc.compact(Q, K, V, w.budgets, workspace=workspace, **kw)
+    torch.cuda.synchronize()
+    if timer:
+        timer.reset()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        res = amc.compact(Q, K, V, w.budgets, workspace=workspace, timer=timer, **kw)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    status = res.head_status.cpu().numpy()
+    ms_per_step = 1000.0 * elapsed / args.steps
+    value = H * args.steps / elapsed
+
+    roofline = None
+    kernels = None
+    if timer:
+        kernels = timer.summary()
+        sw = kernels.get("sweep")
+        if sw:
+            # algorithmic bytes of one sweep launch: every head's float32 Phi read once
+            per_launch = float(sum(w.n * w.T * 4 for _ in range(H)))
+            achieved = per_launch / (sw["avg_ms"] * 1e-3) / 1e9
+            traffic = read_traffic()
+            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                        "kernel": "k_sweep", "avg_launch_ms": round(sw["avg_ms"], 4),
+                        "launches": sw["launches"], "algorithmic_bytes_per_launch": per_launch}
+
+    cpu = cpu_baseline(args.workload, args.cpu_sample) if args.cpu_sample > 0 else None
+
+    out = {
+        "metric": "KV heads compacted/sec at T=8192,50x (d=128)",
+        "value": round(value, 2),
+        "unit": "heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f64",
+        "data": "synthetic (seeded clustered Gaussians, bf16)",
+        "config": {"workload": w.name, "heads": H, "T": w.T, "n": w.n, "d": w.d, "budget": w.budgets[0],
+                   "topk": w.topk, "refit_every": w.refit_every, "parallelism": "none (one GPU)"},
+        "roofline": roofline,
+        "cpu_baseline": cpu,
+        "kernels_ms": {k: round(v["total_ms"] / args.steps, 3) for k, v in (kernels or {}).items()},
+        "head_status_nonzero": int(np.count_nonzero(status)),
+        "input_generation_s": round(gen_s, 1),
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
