@@ -58,8 +58,8 @@ class Options(ctypes.Structure):
         ("select", ctypes.c_int32),
         ("topk", ctypes.c_int32),
         ("refit_every", ctypes.c_int32),
-        ("nnls_pg_iters", ctypes.c_int32),
         ("nnls_max_iters", ctypes.c_int32),
+        ("nnls_polish", ctypes.c_int32),
         ("nnls_tol", ctypes.c_double),
         ("phi_budget_bytes", ctypes.c_uint64),
         ("cv_dtype", ctypes.c_int32),
@@ -178,7 +178,7 @@ def make_problem(num_heads: int, head_dim: int, cu_q: Sequence[int], cu_k: Seque
     return p, (aq, ak, ab)
 
 
-def make_options(select: str = "omp", topk: int = 1, refit_every: int = 1, nnls_pg_iters: int = 8,
+def make_options(select: str = "omp", topk: int = 1, refit_every: int = 1, nnls_polish: int = 1,
                  nnls_max_iters: int = 0, nnls_tol: float = 0.0, phi_budget_bytes: Optional[int] = None,
                  cv_dtype: torch.dtype = torch.float32, trace: bool = False, timer: "Timer" = None) -> Options:
     o = Options()
@@ -186,7 +186,7 @@ def make_options(select: str = "omp", topk: int = 1, refit_every: int = 1, nnls_
     o.select = {"omp": AMC_SEL_OMP, "batched": AMC_SEL_OMP_BATCHED}[select]
     o.topk = int(topk)
     o.refit_every = int(refit_every)
-    o.nnls_pg_iters = int(nnls_pg_iters)
+    o.nnls_polish = int(nnls_polish)
     o.nnls_max_iters = int(nnls_max_iters)
     o.nnls_tol = float(nnls_tol)
     if phi_budget_bytes is not None:
@@ -318,7 +318,7 @@ class CompactResult:
 
 def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=None, cu_k=None,
             beta_in: Optional[torch.Tensor] = None, select: str = "omp", topk: int = 1, refit_every: int = 1,
-            nnls_pg_iters: int = 8, nnls_max_iters: int = 0, nnls_tol: float = 0.0,
+            nnls_polish: int = 1, nnls_max_iters: int = 0, nnls_tol: float = 0.0,
             phi_budget_bytes: Optional[int] = None, cv_dtype: torch.dtype = torch.float32, trace: bool = False,
             timer: Optional[Timer] = None, scale: float = 0.0, stream=None,
             workspace: Optional[torch.Tensor] = None) -> CompactResult:
@@ -340,7 +340,7 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
     if len(bud) != H:
         raise ValueError("one budget per head")
     prob, keep = make_problem(H, d, cq, ck, bud, _dtype_code(Qp), scale)
-    opts = make_options(select, topk, refit_every, nnls_pg_iters, nnls_max_iters, nnls_tol, phi_budget_bytes,
+    opts = make_options(select, topk, refit_every, nnls_polish, nnls_max_iters, nnls_tol, phi_budget_bytes,
                         cv_dtype, trace, timer)
     ws_bytes = workspace_size(prob, opts)
     cb = output_offsets(prob)

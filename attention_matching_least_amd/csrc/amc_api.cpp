@@ -64,7 +64,7 @@ struct Plan {
   uint64_t o_desc = 0, o_shift_part = 0, o_shift = 0, o_phi = 0, o_m = 0, o_r = 0, o_mhat = 0,
            o_Y = 0, o_sel_slot = 0, o_sel_list = 0, o_panel = 0, o_G = 0, o_bvec = 0, o_w = 0,
            o_rhs = 0, o_cvsel = 0, o_pos = 0, o_cand_val = 0, o_cand_idx = 0, o_flist = 0, o_fcount = 0,
-           o_dn = 0, o_L = 0, total = 0;
+           o_dn = 0, o_L = 0, o_nnL = 0, o_nnP = 0, o_nnnp = 0, o_gA = 0, total = 0;
 };
 
 static amc_status check_problem(const amc_problem *p) {
@@ -91,7 +91,7 @@ static amc_status check_options(const amc_options *o) {
   if (o->topk < 1 || o->refit_every < 1) return AMC_ERR_INVALID_ARG;
   if (o->select == AMC_SEL_OMP && (o->topk != 1 || o->refit_every != 1)) return AMC_ERR_INVALID_ARG;
   if (int64_t(o->topk) * o->refit_every > kMaxCycle) return AMC_ERR_UNSUPPORTED;
-  if (o->nnls_pg_iters < 0 || o->nnls_max_iters < 0) return AMC_ERR_INVALID_ARG;
+  if (o->nnls_max_iters < 0 || o->nnls_polish < 0 || o->nnls_polish > 8) return AMC_ERR_INVALID_ARG;
   if (!(o->nnls_tol >= 0.0) || !std::isfinite(o->nnls_tol)) return AMC_ERR_INVALID_ARG;
   if (o->cv_dtype != AMC_F32 && o->cv_dtype != AMC_BF16) return AMC_ERR_INVALID_ARG;
   if (o->flags & ~uint32_t(AMC_FLAG_TRACE)) return AMC_ERR_INVALID_ARG;
@@ -201,6 +201,10 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.o_fcount = take(4ull * H);
   pl.o_dn = take(8ull * tt);
   pl.o_L = take(8ull * tri);
+  pl.o_nnL = take(8ull * tri);
+  pl.o_nnP = take(4ull * tt);
+  pl.o_nnnp = take(4ull * H);
+  pl.o_gA = take(8ull * tt);
   pl.total = off;
   return AMC_OK;
 }
@@ -250,8 +254,8 @@ void amc_default_options(amc_options *o) {
   o->select = AMC_SEL_OMP;
   o->topk = 1;
   o->refit_every = 1;
-  o->nnls_pg_iters = 8;
   o->nnls_max_iters = 0;
+  o->nnls_polish = 1;
   o->nnls_tol = 0.0;
   o->phi_budget_bytes = 64ull << 30;
   o->cv_dtype = AMC_F32;
@@ -369,6 +373,10 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   b.ols_fcount = reinterpret_cast<int32_t *>(ws + pl.o_fcount);
   b.ols_dn = reinterpret_cast<double *>(ws + pl.o_dn);
   b.ols_L = reinterpret_cast<double *>(ws + pl.o_L);
+  b.nn_L = reinterpret_cast<double *>(ws + pl.o_nnL);
+  b.nn_P = reinterpret_cast<int32_t *>(ws + pl.o_nnP);
+  b.nn_np = reinterpret_cast<int32_t *>(ws + pl.o_nnnp);
+  b.gA = reinterpret_cast<double *>(ws + pl.o_gA);
   b.head_status = head_status;
   if (tracing) {
     char *tr = static_cast<char *>(trace);
@@ -379,7 +387,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
     b.tr_runner = reinterpret_cast<double *>(tr + tl.runner_up);
     b.tr_iters = reinterpret_cast<int32_t *>(tr + tl.nnls_iters);
   }
-  NnlsParams np{o->nnls_pg_iters, o->nnls_max_iters, o->nnls_tol};
+  NnlsParams np{0, o->nnls_max_iters, o->nnls_tol};
   const Dims &dm = pl.dm;
 
   AMC_LAUNCH(AMC_K_INIT, (upload_desc(pl, const_cast<HeadDesc *>(b.desc), stream) == AMC_OK
@@ -393,9 +401,14 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
     AMC_LAUNCH(AMC_K_SWEEP, launch_sweep(dm, b, c, pl.kR, stream));
     AMC_LAUNCH(AMC_K_MERGE, launch_merge(dm, b, c, pl.kR, stream));
     AMC_LAUNCH(AMC_K_PANEL, launch_panel(dm, b, c, pl.kR, stream));
-    AMC_LAUNCH(AMC_K_GRAM, launch_gram(dm, b, c, pl.kR, stream));
-    AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dm, b, c, pl.kR, np, stream));
-    AMC_LAUNCH(AMC_K_RESID, launch_resid(dm, b, c, pl.kR, stream));
+    AMC_LAUNCH(AMC_K_GRAM, launch_gram(dm, b, c, pl.kR, 0, stream));
+    AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dm, b, c, pl.kR, 0, np, stream));
+    AMC_LAUNCH(AMC_K_RESID, launch_resid(dm, b, c, pl.kR, 0, stream));
+  }
+  for (int r = 0; r < o->nnls_polish; ++r) {
+    AMC_LAUNCH(AMC_K_GRAM, launch_gram(dm, b, 0, pl.kR, 1, stream));
+    AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dm, b, 0, pl.kR, 1, np, stream));
+    AMC_LAUNCH(AMC_K_RESID, launch_resid(dm, b, 0, pl.kR, 1, stream));
   }
   AMC_LAUNCH(AMC_K_OLS_NORMAL, launch_ols_normal(dm, b, stream));
   AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_factor(dm, b, stream));

@@ -54,6 +54,7 @@ struct Buffers {
   double *panel;       // [sum t*n] row a = float64 column of slot a over the queries
   double *G;           // [sum t*t]
   double *bvec;        // [sum t]
+  double *gA;          // [sum t]  Phi_S^T r from the float64 panel and residual
   double *w;           // [sum t]
   double *rhs;         // [sum t][d]
   float *cv_sel;       // [sum t][d]
@@ -62,6 +63,9 @@ struct Buffers {
   int32_t *ols_fcount; // [H]
   double *ols_dn;      // [sum t]  diagonal scaling of the normal matrix
   double *ols_L;       // [sum t*(t+1)/2] packed Cholesky factor of the scaled normal matrix
+  double *nn_L;        // [sum t*(t+1)/2] NNLS factor of the free set, kept between refits
+  int32_t *nn_P;       // [sum t]  NNLS free set in factor order
+  int32_t *nn_np;      // [H]      NNLS free-set size
   double *cand_val;    // [sum n_cblk][kMaxCycle + 1]
   int32_t *cand_idx;   // [sum n_cblk][kMaxCycle + 1]
   int32_t *head_status;  // [H] or null
@@ -80,7 +84,7 @@ struct Dims {
 };
 
 struct NnlsParams {
-  int pg_iters;
+  int pg_iters;   // projected-gradient warm-up (stand-alone solver)
   int max_iters;  // 0: automatic
   double tol;     // 0: automatic
 };
@@ -97,10 +101,10 @@ hipError_t launch_phi(const Dims &dm, const Buffers &b, int store_phi, hipStream
 hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_merge(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
-hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
-hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int cyc_keys,
+hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);
+hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish,
                        const NnlsParams &np, hipStream_t s);
-hipError_t launch_resid(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_resid(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);
 hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s);
 hipError_t launch_pack(const Dims &dm, const Buffers &b, void *Ck, float *beta, void *Cv,
                        int cv_bf16, int32_t *sel_idx, hipStream_t s);

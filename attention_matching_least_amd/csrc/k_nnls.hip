@@ -3,16 +3,31 @@
 // after every pick; xinfinite.net article, section 2, step 2).
 //
 // The pages' GPU solver is projected gradient (xinfinite.net article,
-// Fig. 2).  On these Gram matrices (condition numbers ~1e9) projected
-// gradient alone does not reach the minimiser, so it only warms up the active
-// set here; an exact active-set polish (the Gram-form method of Bro and
-// De Jong, with a Cholesky solve of the free block in LDS) finishes the fit.
-// Everything runs in float64 in unit-diagonal form (w = u / sqrt(diag G)),
-// which leaves the minimiser unchanged and makes the tolerance meaningful for
-// columns of very different norm.
+// Fig. 2).  On these Gram matrices (condition numbers 1e9 and beyond)
+// projected gradient alone does not reach the minimiser, so the exact
+// minimiser is found by an active-set method on the Gram form (Bro and
+// De Jong's fast NNLS): the most violating zero variable enters, the
+// least-squares solution on the free set is computed from a Cholesky factor,
+// and if it leaves the feasible set the iterate steps back and the blocking
+// variables leave.  Projected gradient survives as the warm-up of the
+// stand-alone solver (amc_nnls).
 //
-// One 256-thread block solves one system; the packed Cholesky factor of the
-// free block (p <= 192) lives in LDS.
+// Accuracy.  Everything is float64 in unit-diagonal form (w = u / sqrt(diag
+// G)).  The solver works in correction form: it keeps the gradient
+// g = b - G u explicitly, moves by corrections d = G_PP^-1 g_P solved with the
+// factor, and updates g by -G d.  Inside a compaction each refit starts from
+// g = Phi_S^T r computed from the float64 panel and the float64 residual of
+// the previous refit (the corrected semi-normal equations of Bjorck), so the
+// gradient never suffers the cancellation of b - G u, and a final refit with
+// no new key refines the weights once more.
+//
+// The factor is updated, not recomputed: a variable that enters appends one
+// row (a forward substitution); a variable that leaves is deleted by a row
+// shift plus a rank-one update of the trailing block.  Between the refits of
+// one compaction the factor and the free set persist in the workspace.  The
+// sequential passes run in one wave with vectors spread over the lanes'
+// registers (index i lives in lane i % 64, slot i / 64); the mat-vecs use the
+// whole block.  The packed factor of up to 192 variables lives in LDS.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -25,16 +40,41 @@ namespace amc {
 namespace {
 
 constexpr int NT = 256;
+constexpr int NR = (kLdsMaxT + 63) / 64;  // register slots per lane for a vector of length <= kLdsMaxT
 constexpr unsigned char F_PASSIVE = 1, F_BLOCKED = 2;
+constexpr double PIV_TOL = 1e-14;  // smallest acceptable squared pivot in unit-diagonal form
 
 __device__ __forceinline__ int tri(int r) { return r * (r + 1) / 2; }
 
-__device__ __forceinline__ void decode_tri(int e, int *r, int *c) {
-  int rr = int((sqrtf(8.0f * float(e) + 1.0f) - 1.0f) * 0.5f);
-  while (tri(rr + 1) <= e) ++rr;
-  while (tri(rr) > e) --rr;
-  *r = rr;
-  *c = e - tri(rr);
+__device__ __forceinline__ void wsync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// element k of a lane-distributed vector, broadcast to every lane.  Written
+// as selects over all slots so the vector stays in registers.
+__device__ __forceinline__ double getv(const double (&r)[NR], int k) {
+  const int s = k >> 6;
+  double x = r[0];
+#pragma unroll
+  for (int m = 1; m < NR; ++m) x = (s == m) ? r[m] : x;
+  return __shfl(x, k & 63);
+}
+
+__device__ __forceinline__ void setv(double (&r)[NR], int k, double v) {
+  const bool mine = lane_id() == (k & 63);
+  const int s = k >> 6;
+#pragma unroll
+  for (int m = 0; m < NR; ++m) r[m] = (mine && s == m) ? v : r[m];
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+  return v;
 }
 
 struct Red {
@@ -74,32 +114,29 @@ __device__ int block_argmax(double v, int idx, Red *red, double *out_v) {
   return idx;
 }
 
-__device__ double block_sum(double v, Red *red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  __syncthreads();
-  if (lane == 0) red->v[wave] = v;
-  __syncthreads();
-  double s = 0.0;
-  for (int w = 0; w < NT / 64; ++w) s += red->v[w];
-  return s;
-}
-
-struct Smem {
-  double *L, *u, *y, *g, *dg, *bs, *v;
-  int *plist;
+// LDS state of one solve
+struct St {
+  double *L;      // packed lower factor of Gs_PP, rows in free-set order
+  double *rdiag;  // 1 / L_kk
+  double *u;      // scaled iterate, per variable
+  double *g;      // scaled gradient bs - Gs u, per variable
+  double *dg;     // sqrt(G_aa)
+  double *bs;     // b_a / dg_a
+  double *delta;  // step of the free variables, in factor order
+  int *plist;     // free set in factor order
+  int *np;        // free-set size
+  int *ctl;       // wave-0 decision broadcast to the block
   unsigned char *flag;
 };
 
-__device__ Smem carve(char *base, int maxp) {
-  Smem s;
+__device__ St carve(char *base, int maxp) {
+  St s;
   double *d = reinterpret_cast<double *>(base);
   s.L = d;
   d += tri(maxp);
-  s.u = d;
+  s.rdiag = d;
   d += maxp;
-  s.y = d;
+  s.u = d;
   d += maxp;
   s.g = d;
   d += maxp;
@@ -107,190 +144,326 @@ __device__ Smem carve(char *base, int maxp) {
   d += maxp;
   s.bs = d;
   d += maxp;
-  s.v = d;
+  s.delta = d;
   d += maxp;
   s.plist = reinterpret_cast<int *>(d);
-  s.flag = reinterpret_cast<unsigned char *>(s.plist + maxp);
+  s.np = s.plist + maxp;
+  s.ctl = s.np + 1;
+  s.flag = reinterpret_cast<unsigned char *>(s.ctl + 1);
   return s;
 }
 
-// g = bs - Gs u with Gs = D^-1 G D^-1 (D = diag(dg)), using v = u / dg.
-__device__ void grad(const double *G, int64_t ld, int p, const Smem &S) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int a = tid; a < p; a += NT) S.v[a] = S.u[a] / S.dg[a];
-  __syncthreads();
-  for (int a = wave; a < p; a += NT / 64) {
-    double acc = 0.0;
-    for (int b = lane; b < p; b += 64) acc = fma(G[a * ld + b], S.v[b], acc);
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
-    if (lane == 0) S.g[a] = S.bs[a] - acc / S.dg[a];
-  }
-  __syncthreads();
+__host__ __device__ constexpr size_t nnls_smem_bytes(int maxp) {
+  return size_t(8) * (size_t(maxp) * (maxp + 1) / 2 + 6 * size_t(maxp)) + 4 * (size_t(maxp) + 2) + size_t(maxp) + 16;
 }
 
-// Least squares on the passive set with feasibility back-tracking.  Returns
-// with u optimal on its (possibly reduced) passive set.  just_added: the
-// variable that entered last (or -1); if its own solution component is not
-// positive on the first solve it is blocked for this fit (the safeguard of
-// Lawson and Hanson against cycling on round-off).
-__device__ void solve_passive(const double *G, int64_t ld, int p, const Smem &S, int just_added, int *status,
-                              Red *red) {
-  __shared__ int sh_np, sh_fail, sh_kmin, sh_first;
-  __shared__ double sh_alpha;
-  const int tid = threadIdx.x;
-  if (tid == 0) sh_first = 1;
-  for (int guard = 0; guard < 2 * p + 4; ++guard) {
+// ---- wave-0 routines ------------------------------------------------------
+
+// L x = r (forward), leading n rows
+__device__ __forceinline__ void fwd(const St &S, int n, double (&r)[NR]) {
+  const int lane = lane_id();
+  for (int k = 0; k < n; ++k) {
+    const double xk = getv(r, k) * S.rdiag[k];
+    setv(r, k, xk);
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      const int i = lane + 64 * m;
+      if (i > k && i < n) r[m] = fma(-S.L[tri(i) + k], xk, r[m]);
+    }
+  }
+}
+
+// L^T x = r (backward), leading n rows
+__device__ __forceinline__ void bwd(const St &S, int n, double (&r)[NR]) {
+  const int lane = lane_id();
+  for (int k = n - 1; k >= 0; --k) {
+    const double xk = getv(r, k) * S.rdiag[k];
+    setv(r, k, xk);
+    const int base = tri(k);
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      const int i = lane + 64 * m;
+      if (i < k) r[m] = fma(-S.L[base + i], xk, r[m]);
+    }
+  }
+}
+
+// Appends variable j to the factor.  Returns false (and changes nothing) if
+// its column is numerically dependent on the free set.
+__device__ __forceinline__ bool append(const St &S, const double *G, int64_t ld, int j) {
+  const int lane = lane_id();
+  const int np = *S.np;
+  const double dj = S.dg[j];
+  double c[NR];
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const int k = lane + 64 * m;
+    double v = 0.0;
+    if (k < np) {
+      const int a = S.plist[k];
+      v = G[int64_t(j) * ld + a] / (S.dg[a] * dj);
+    }
+    c[m] = v;
+  }
+  fwd(S, np, c);
+  double ss = 0.0;
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const int k = lane + 64 * m;
+    if (k < np) ss = fma(c[m], c[m], ss);
+  }
+  ss = wave_sum(ss);
+  const double gjj = G[int64_t(j) * ld + j] / (dj * dj);
+  const double d2 = gjj - ss;
+  if (!(d2 > PIV_TOL)) return false;
+  const double djj = sqrt(d2);
+  const int base = tri(np);
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const int k = lane + 64 * m;
+    if (k < np) S.L[base + k] = c[m];
+  }
+  if (lane == 0) {
+    S.L[base + np] = djj;
+    S.rdiag[np] = 1.0 / djj;
+    S.plist[np] = j;
+    S.flag[j] |= F_PASSIVE;
+    *S.np = np + 1;
+  }
+  wsync();
+  return true;
+}
+
+// Deletes factor position q: rows below shift up without column q, then the
+// trailing block absorbs the removed column by a rank-one update.
+__device__ __forceinline__ void remove_at(const St &S, int q) {
+  const int lane = lane_id();
+  const int np = *S.np;
+  double x[NR];
+#pragma unroll
+  for (int m = 0; m < NR; ++m) x[m] = 0.0;
+  for (int i = q + 1; i < np; ++i) {
+    double v[NR];
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      const int c = lane + 64 * m;
+      v[m] = c <= i ? S.L[tri(i) + c] : 0.0;
+    }
+    const double xi = S.L[tri(i) + q];
+    // new row i-1, entry c' = old entry c' (c' < q) or old entry c'+1 (c' >= q)
+    double nv[NR];
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      const double right_same = __shfl(v[m], (lane + 1) & 63);
+      const double right_next = (m + 1 < NR) ? __shfl(v[m + 1 < NR ? m + 1 : m], 0) : 0.0;
+      const double right = lane == 63 ? right_next : right_same;
+      const int cp = lane + 64 * m;
+      nv[m] = cp < q ? v[m] : right;
+    }
+    wsync();
+    const int nb = tri(i - 1);
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      const int cp = lane + 64 * m;
+      if (cp <= i - 1) S.L[nb + cp] = nv[m];
+    }
+    setv(x, i - 1, xi);
+    wsync();
+  }
+  int pv[NR];
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const int k = lane + 64 * m;
+    pv[m] = (k + 1 < np) ? S.plist[k + 1] : 0;
+  }
+  wsync();
+#pragma unroll
+  for (int m = 0; m < NR; ++m) {
+    const int k = lane + 64 * m;
+    if (k >= q && k < np - 1) S.plist[k] = pv[m];
+  }
+  if (lane == 0) *S.np = np - 1;
+  wsync();
+  const int n2 = np - 1;
+  // rank-one update: L33' L33'^T = L33 L33^T + x x^T on positions q..n2-1
+  for (int k = q; k < n2; ++k) {
+    const double lkk = S.L[tri(k) + k];
+    const double xk = getv(x, k);
+    const double r = sqrt(lkk * lkk + xk * xk);
+    const double cc = r / lkk, s = xk / lkk;
+#pragma unroll
+    for (int m = 0; m < NR; ++m) {
+      const int i = lane + 64 * m;
+      if (i > k && i < n2) {
+        const double lik = (S.L[tri(i) + k] + s * x[m]) / cc;
+        S.L[tri(i) + k] = lik;
+        x[m] = cc * x[m] - s * lik;
+      }
+    }
+    if (lane == 0) {
+      S.L[tri(k) + k] = r;
+      S.rdiag[k] = 1.0 / r;
+    }
+    wsync();
+  }
+}
+
+// ---- block routines -------------------------------------------------------
+
+// g_a -= sum_k Gs[a][P_k] delta_k for every variable a < p (G is symmetric, so
+// row P_k of G is read contiguously).
+__device__ void grad_update(const St &S, const double *G, int64_t ld, int p) {
+  const int np = *S.np;
+  for (int a = threadIdx.x; a < p; a += NT) {
+    double acc = 0.0;
+    for (int k = 0; k < np; ++k) {
+      const double dk = S.delta[k];
+      if (dk != 0.0) {
+        const int c = S.plist[k];
+        acc = fma(G[int64_t(c) * ld + a], dk / S.dg[c], acc);
+      }
+    }
+    S.g[a] -= acc / S.dg[a];
+  }
+}
+
+enum { CTL_DONE = 1, CTL_PARTIAL = 2, CTL_DROP = 3 };
+
+// Least squares on the free set in correction form, with feasibility
+// back-tracking, starting from a feasible u whose support is the free set.
+// entering: the variable that just entered (or -1); if on the first solve it
+// alone blocks, it is set aside for the rest of this fit (Lawson and Hanson's
+// guard against cycling on round-off).
+__device__ void settle(const St &S, const double *G, int64_t ld, int p, int entering) {
+  const int tid = threadIdx.x, wave = tid >> 6;
+  bool first = true;
+  for (int guard = 0; guard < kLdsMaxT + 4; ++guard) {
     __syncthreads();
-    if (tid == 0) {
-      int k = 0;
-      for (int a = 0; a < p; ++a)
-        if (S.flag[a] & F_PASSIVE) S.plist[k++] = a;
-      sh_np = k;
-      sh_fail = -1;
+    if (wave == 0) {
+      const int lane = lane_id();
+      const int np = *S.np;
+      double d[NR];
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        const int k = lane + 64 * m;
+        d[m] = k < np ? S.g[S.plist[k]] : 0.0;
+      }
+      fwd(S, np, d);
+      bwd(S, np, d);  // d = Gs_PP^-1 g_P: the step to the free-set optimum
+      double best = INFINITY;
+      int kb = -1;
+#pragma unroll
+      for (int m = 0; m < NR; ++m) {
+        const int k = lane + 64 * m;
+        if (k < np) {
+          const double ua = S.u[S.plist[k]];
+          const double z = ua + d[m];
+          if (z <= 0.0) {
+            const double rt = d[m] < 0.0 ? ua / (-d[m]) : 0.0;
+            if (kb < 0 || rt < best) {
+              best = rt;
+              kb = k;
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const double ob = __shfl_xor(best, off);
+        const int ok = __shfl_xor(kb, off);
+        if (ok >= 0 && (kb < 0 || ob < best || (ob == best && ok < kb))) {
+          best = ob;
+          kb = ok;
+        }
+      }
+      int ctl;
+      if (kb < 0) {
+        ctl = CTL_DONE;
+#pragma unroll
+        for (int m = 0; m < NR; ++m) {
+          const int k = lane + 64 * m;
+          if (k < np) S.delta[k] = d[m];
+        }
+      } else if (first && entering >= 0 && kb == np - 1 && S.plist[kb] == entering && S.u[entering] == 0.0) {
+        ctl = CTL_DROP;
+      } else {
+        ctl = CTL_PARTIAL;
+        const double alpha = best < 1.0 ? best : 1.0;
+#pragma unroll
+        for (int m = 0; m < NR; ++m) {
+          const int k = lane + 64 * m;
+          if (k < np) {
+            const double ua = S.u[S.plist[k]];
+            double un = (k == kb) ? 0.0 : fma(alpha, d[m], ua);
+            if (!(un > 0.0)) un = 0.0;
+            S.delta[k] = un - ua;
+          }
+        }
+      }
+      if (lane == 0) *S.ctl = ctl;
+      wsync();
     }
     __syncthreads();
-    const int np = sh_np;
-    if (np == 0) {
-      for (int a = tid; a < p; a += NT) S.u[a] = 0.0;
+    const int ctl = *S.ctl;
+    if (ctl == CTL_DROP) {
+      if (tid == 0) {
+        *S.np = *S.np - 1;
+        S.flag[entering] = F_BLOCKED;
+      }
       __syncthreads();
       return;
     }
-    const int ne = tri(np);
-    for (int e = tid; e < ne; e += NT) {
-      int r, c;
-      decode_tri(e, &r, &c);
-      const int ar = S.plist[r], ac = S.plist[c];
-      S.L[e] = G[ar * ld + ac] / (S.dg[ar] * S.dg[ac]);
-    }
-    __syncthreads();
-    // right-looking Cholesky of the packed free block
-    for (int k = 0; k < np; ++k) {
-      if (tid == 0) {
-        const double piv = S.L[tri(k) + k];
-        if (!(piv > 1e-14)) sh_fail = k;
-        else S.L[tri(k) + k] = sqrt(piv);
-      }
-      __syncthreads();
-      if (sh_fail >= 0) break;
-      const double dkk = S.L[tri(k) + k];
-      for (int r = k + 1 + tid; r < np; r += NT) S.L[tri(r) + k] /= dkk;
-      __syncthreads();
-      const int mm = np - k - 1;
-      const int nt = tri(mm);
-      for (int e = tid; e < nt; e += NT) {
-        int r, c;
-        decode_tri(e, &r, &c);
-        r += k + 1;
-        c += k + 1;
-        S.L[tri(r) + c] -= S.L[tri(r) + k] * S.L[tri(c) + k];
-      }
-      __syncthreads();
-    }
-    if (sh_fail >= 0) {
-      // the failing variable depends linearly on the ones before it: drop it for this fit
-      if (tid == 0) {
-        const int a = S.plist[sh_fail];
-        S.flag[a] = F_BLOCKED;
-        S.u[a] = 0.0;
-        *status |= int(AMC_HS_NNLS_SINGULAR);
-        sh_first = 0;
-      }
-      continue;
-    }
-    // forward then backward substitution: y = L^-T L^-1 bs_P
-    for (int k = tid; k < np; k += NT) S.y[k] = S.bs[S.plist[k]];
-    __syncthreads();
-    for (int k = 0; k < np; ++k) {
-      if (tid == 0) S.y[k] /= S.L[tri(k) + k];
-      __syncthreads();
-      const double yk = S.y[k];
-      for (int r = k + 1 + tid; r < np; r += NT) S.y[r] -= S.L[tri(r) + k] * yk;
-      __syncthreads();
-    }
-    for (int k = np - 1; k >= 0; --k) {
-      if (tid == 0) S.y[k] /= S.L[tri(k) + k];
-      __syncthreads();
-      const double yk = S.y[k];
-      for (int r = tid; r < k; r += NT) S.y[r] -= S.L[tri(k) + r] * yk;
-      __syncthreads();
-    }
-    // feasibility
-    double ratio = INFINITY;
-    int kk = -1;
+    grad_update(S, G, ld, p);
+    const int np = *S.np;
     for (int k = tid; k < np; k += NT) {
-      if (S.y[k] <= 0.0) {
-        const double ua = S.u[S.plist[k]];
-        const double den = ua - S.y[k];
-        const double rt = den > 0.0 ? ua / den : 0.0;
-        if (kk < 0 || rt < ratio) {
-          ratio = rt;
-          kk = k;
+      const int a = S.plist[k];
+      const double un = S.u[a] + S.delta[k];
+      S.u[a] = un > 0.0 ? un : 0.0;
+    }
+    __syncthreads();
+    if (ctl == CTL_DONE) return;
+    first = false;
+    if (wave == 0) {
+      // every free variable that reached zero leaves (highest position first)
+      for (int k = *S.np - 1; k >= 0; --k) {
+        const int a = S.plist[k];
+        if (!(S.u[a] > 0.0)) {
+          wsync();
+          if (lane_id() == 0) {
+            S.u[a] = 0.0;
+            S.flag[a] &= ~F_PASSIVE;
+          }
+          wsync();
+          remove_at(S, k);
         }
       }
     }
-    double best;
-    const int kmin = block_argmax(kk >= 0 ? -ratio : -INFINITY, kk, red, &best);
-    if (kmin < 0) {
-      for (int a = tid; a < p; a += NT) S.u[a] = 0.0;
-      __syncthreads();
-      for (int k = tid; k < np; k += NT) S.u[S.plist[k]] = S.y[k];
-      __syncthreads();
-      return;
-    }
-    if (tid == 0) {
-      sh_alpha = -best;
-      sh_kmin = kmin;
-    }
-    __syncthreads();
-    if (sh_first && just_added >= 0 && S.plist[sh_kmin] == just_added && S.u[just_added] == 0.0) {
-      // the entering variable does not take a positive value: block it, keep u
-      __syncthreads();
-      if (tid == 0) {
-        S.flag[just_added] = F_BLOCKED;
-        S.u[just_added] = 0.0;
-      }
-      __syncthreads();
-      return;
-    }
-    const double alpha = sh_alpha;
-    for (int k = tid; k < np; k += NT) {
-      const int a = S.plist[k];
-      S.u[a] += alpha * (S.y[k] - S.u[a]);
-    }
-    __syncthreads();
-    if (tid == 0) {
-      S.u[S.plist[sh_kmin]] = 0.0;
-      sh_first = 0;
-    }
-    __syncthreads();
-    for (int k = tid; k < np; k += NT) {
-      const int a = S.plist[k];
-      if (!(S.u[a] > 0.0)) {
-        S.u[a] = 0.0;
-        S.flag[a] &= ~F_PASSIVE;
-      }
-    }
   }
   __syncthreads();
 }
 
-// Solves one system.  nwarm: entries of w used as the warm start (the rest start at 0).
-__device__ void nnls_block(const double *G, int64_t ld, int p, const double *b, double *w, int nwarm,
-                           const NnlsParams np_, char *smem, int maxp, int *iters_out, int *status_out) {
+// One block solves one system.
+//   gA     : accurate unscaled gradient b - G w at the warm start (nullable:
+//            then it is formed from G and b)
+//   np_in, plist_in, L_in : persisted free set and factor (np_in = 0: none)
+//   pg     : projected-gradient warm-up iterations (stand-alone solver only)
+__device__ __forceinline__ void nnls_solve(const double *G, int64_t ld, int p, const double *b, const double *gA,
+                                           double *w, int nwarm, const NnlsParams prm, char *smem, int maxp,
+                                           int np_in, const int32_t *plist_in, const double *L_in, int pg,
+                                           int *iters_out, int *status_out) {
   __shared__ Red red;
-  __shared__ int sh_status, sh_iters;
-  const int tid = threadIdx.x;
-  Smem S = carve(smem, maxp);
+  __shared__ int sh_status;
+  const int tid = threadIdx.x, wave = tid >> 6;
+  St S = carve(smem, maxp);
   if (tid == 0) {
     sh_status = 0;
-    sh_iters = 0;
+    *S.np = np_in;
   }
   double bl = 0.0;
   for (int a = tid; a < p; a += NT) {
-    const double gaa = G[a * ld + a];
-    unsigned char f = 0;
+    const double gaa = G[int64_t(a) * ld + a];
     double dg = sqrt(gaa);
+    unsigned char f = 0;
     if (!(dg > 0.0) || !isfinite(dg)) {
       dg = 1.0;
       f = F_BLOCKED;
@@ -303,48 +476,93 @@ __device__ void nnls_block(const double *G, int64_t ld, int p, const double *b, 
     S.flag[a] = f;
     bl = fmax(bl, fabs(bs));
   }
+  for (int e = tid; e < tri(np_in); e += NT) S.L[e] = L_in[e];
+  __syncthreads();
+  for (int k = tid; k < np_in; k += NT) {
+    const int a = plist_in[k];
+    S.plist[k] = a;
+    S.flag[a] |= F_PASSIVE;
+    S.rdiag[k] = 1.0 / S.L[tri(k) + k];
+  }
+  __syncthreads();
+  // initial gradient
+  if (gA) {
+    for (int a = tid; a < p; a += NT) S.g[a] = (S.flag[a] & F_BLOCKED) ? 0.0 : gA[a] / S.dg[a];
+  } else {
+    for (int a = tid; a < p; a += NT) {
+      double acc = 0.0;
+      for (int c = 0; c < p; ++c) acc = fma(G[int64_t(c) * ld + a], S.u[c] / S.dg[c], acc);
+      S.g[a] = S.bs[a] - acc / S.dg[a];
+    }
+  }
   double bmax;
   (void)block_argmax(bl, 0, &red, &bmax);
-  const double tol = (np_.tol > 0.0 ? np_.tol : 10.0 * DBL_EPSILON * double(p)) * bmax;
-  const int cap = np_.max_iters > 0 ? np_.max_iters : 3 * p + 30;
+  const double tol = (prm.tol > 0.0 ? prm.tol : 10.0 * DBL_EPSILON * double(p)) * bmax;
+  const int cap = prm.max_iters > 0 ? prm.max_iters : 3 * p + 30;
+  int iters = 0;
 
   if (bmax > 0.0 && isfinite(bmax)) {
-    // projected-gradient warm-up, step 1/L with L a Gershgorin bound of Gs
-    if (np_.pg_iters > 0) {
-      double rs = 0.0;
-      const int lane = tid & 63, wave = tid >> 6;
+    if (pg > 0) {
+      // projected-gradient warm-up (step 1/L, L a Gershgorin bound of Gs)
       double rowmax = 0.0;
-      for (int a = wave; a < p; a += NT / 64) {
+      for (int a = tid; a < p; a += NT) {
         double acc = 0.0;
-        for (int c = lane; c < p; c += 64) acc += fabs(G[a * ld + c]) / S.dg[c];
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) acc += __shfl_xor(acc, off);
+        for (int c = 0; c < p; ++c) acc += fabs(G[int64_t(c) * ld + a]) / S.dg[c];
         if (!(S.flag[a] & F_BLOCKED)) rowmax = fmax(rowmax, acc / S.dg[a]);
       }
-      (void)rs;
       double Lmax;
       (void)block_argmax(rowmax, 0, &red, &Lmax);
       const double step = Lmax > 0.0 ? 1.0 / Lmax : 0.0;
-      for (int it = 0; it < np_.pg_iters; ++it) {
-        grad(G, ld, p, S);
-        for (int a = tid; a < p; a += NT)
-          if (!(S.flag[a] & F_BLOCKED)) S.u[a] = fmax(0.0, S.u[a] + step * S.g[a]);
+      for (int it = 0; it < pg; ++it) {
         __syncthreads();
+        for (int a = tid; a < p; a += NT)
+          S.delta[a] = (S.flag[a] & F_BLOCKED) ? 0.0 : fmax(0.0, S.u[a] + step * S.g[a]) - S.u[a];
+        __syncthreads();
+        for (int a = tid; a < p; a += NT) {
+          double acc = 0.0;
+          for (int c = 0; c < p; ++c) acc = fma(G[int64_t(c) * ld + a], S.delta[c] / S.dg[c], acc);
+          S.g[a] -= acc / S.dg[a];
+        }
+        __syncthreads();
+        for (int a = tid; a < p; a += NT) S.u[a] += S.delta[a];
       }
+      __syncthreads();
     }
-    for (int a = tid; a < p; a += NT)
-      if (S.u[a] > 0.0) S.flag[a] |= F_PASSIVE;
-    __syncthreads();
-    int anyp = 0;
-    for (int a = tid; a < p; a += NT) anyp |= (S.flag[a] & F_PASSIVE) ? 1 : 0;
-    if (block_sum(double(anyp), &red) > 0.0) solve_passive(G, ld, p, S, -1, &sh_status, &red);
-    int iters = 0;
+    if (np_in == 0) {
+      // the support of the warm start becomes the free set
+      if (wave == 0) {
+        for (int a = 0; a < p; ++a) {
+          if (S.u[a] > 0.0 && !(S.flag[a] & F_PASSIVE) && !append(S, G, ld, a)) {
+            if (lane_id() == 0) S.flag[a] = F_BLOCKED;
+            wsync();
+          }
+        }
+      }
+      __syncthreads();
+      // a dependent variable dropped here still carries weight: take it out of u and g
+      for (int a = tid; a < p; a += NT) S.delta[a] = ((S.flag[a] & F_BLOCKED) && S.u[a] > 0.0) ? -S.u[a] : 0.0;
+      __syncthreads();
+      for (int a = tid; a < p; a += NT) {
+        double acc = 0.0;
+        for (int c = 0; c < p; ++c)
+          if (S.delta[c] != 0.0) acc = fma(G[int64_t(c) * ld + a], S.delta[c] / S.dg[c], acc);
+        S.g[a] -= acc / S.dg[a];
+      }
+      __syncthreads();
+      for (int a = tid; a < p; a += NT)
+        if (S.flag[a] & F_BLOCKED) S.u[a] = 0.0;
+      __syncthreads();
+      if (*S.np > 0) settle(S, G, ld, p, -1);
+    } else {
+      settle(S, G, ld, p, -1);  // refine the persisted optimum with the accurate gradient
+    }
     for (;;) {
-      grad(G, ld, p, S);
+      __syncthreads();
       double gv = -INFINITY;
       int gi = -1;
       for (int a = tid; a < p; a += NT) {
-        if (!(S.flag[a] & (F_PASSIVE | F_BLOCKED)) && (gi < 0 || S.g[a] > gv)) {
+        if (S.flag[a] & (F_PASSIVE | F_BLOCKED)) continue;
+        if (gi < 0 || S.g[a] > gv) {
           gv = S.g[a];
           gi = a;
         }
@@ -357,44 +575,63 @@ __device__ void nnls_block(const double *G, int64_t ld, int p, const double *b, 
         break;
       }
       ++iters;
+      if (wave == 0) {
+        const bool ok = append(S, G, ld, j);
+        if (lane_id() == 0) {
+          *S.ctl = ok ? 1 : 0;
+          if (!ok) {
+            S.flag[j] = F_BLOCKED;
+            sh_status |= int(AMC_HS_NNLS_SINGULAR);
+          }
+        }
+        wsync();
+      }
       __syncthreads();
-      if (tid == 0) S.flag[j] |= F_PASSIVE;
-      __syncthreads();
-      solve_passive(G, ld, p, S, j, &sh_status, &red);
+      if (*S.ctl) settle(S, G, ld, p, j);
     }
-    if (tid == 0) sh_iters = iters;
-  } else {
-    for (int a = tid; a < p; a += NT) S.u[a] = 0.0;
   }
   __syncthreads();
   for (int a = tid; a < p; a += NT) w[a] = S.u[a] / S.dg[a];
   if (tid == 0) {
-    *iters_out = sh_iters;
+    *iters_out = iters;
     *status_out = sh_status;
   }
 }
 
-__host__ __device__ constexpr size_t nnls_smem_bytes(int maxp) {
-  return size_t(8) * (size_t(maxp) * (maxp + 1) / 2 + 6 * size_t(maxp)) + 4 * size_t(maxp) + size_t(maxp) + 16;
-}
-
+// One refit per head.  polish: no new key; refine the last fit (p = t).
 __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ desc, const double *__restrict__ G,
-                                                   const double *__restrict__ bvec, double *__restrict__ w, int cycle,
-                                                   int kR, NnlsParams np_, int maxp, int32_t *__restrict__ tr_iters,
-                                                   double *__restrict__ tr_weight,
+                                                   const double *__restrict__ bvec, const double *__restrict__ gA,
+                                                   double *__restrict__ w, int cycle, int kR, int polish,
+                                                   NnlsParams prm, int maxp, double *__restrict__ nn_L,
+                                                   int32_t *__restrict__ nn_P, int32_t *__restrict__ nn_np,
+                                                   int32_t *__restrict__ tr_iters, double *__restrict__ tr_weight,
                                                    int32_t *__restrict__ head_status) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int h = blockIdx.x;
   const HeadDesc D = desc[h];
-  const int64_t S0 = int64_t(cycle) * kR;
-  if (S0 >= D.t) return;
-  const int Kc = int(D.t - S0 < kR ? D.t - S0 : kR);
+  int64_t S0;
+  int Kc;
+  if (polish) {
+    S0 = D.t;
+    Kc = 0;
+  } else {
+    S0 = int64_t(cycle) * kR;
+    if (S0 >= D.t) return;
+    Kc = int(D.t - S0 < kR ? D.t - S0 : kR);
+  }
   const int p = int(S0) + Kc;
+  const int np_in = S0 == 0 ? 0 : nn_np[h];
   int iters = 0, status = 0;
-  nnls_block(G + D.tt_off, D.t, p, bvec + D.t_off, w + D.t_off, int(S0), np_, smem, maxp, &iters, &status);
+  nnls_solve(G + D.tt_off, D.t, p, bvec + D.t_off, gA + D.t_off, w + D.t_off, int(S0), prm, smem, maxp, np_in,
+             nn_P + D.t_off, nn_L + D.tri_off, 0, &iters, &status);
+  St S = carve(smem, maxp);
   __syncthreads();
+  const int np = *S.np;
+  for (int e = threadIdx.x; e < tri(np); e += NT) nn_L[D.tri_off + e] = S.L[e];
+  for (int k = threadIdx.x; k < np; k += NT) nn_P[D.t_off + k] = S.plist[k];
   if (threadIdx.x == 0) {
-    if (tr_iters) tr_iters[D.cyc_off + cycle] = iters;
+    nn_np[h] = np;
+    if (tr_iters && !polish) tr_iters[D.cyc_off + cycle] = iters;
     if (status && head_status) atomicOr(head_status + h, status);
   }
   if (tr_weight)
@@ -409,7 +646,7 @@ struct NnlsChunk {
 
 __global__ __launch_bounds__(NT) void k_nnls_batched(NnlsChunk ch, int base, const double *__restrict__ G,
                                                      const double *__restrict__ g, double *__restrict__ w, int warm,
-                                                     NnlsParams np_, int maxp, int32_t *__restrict__ iters,
+                                                     NnlsParams prm, int maxp, int32_t *__restrict__ iters,
                                                      int32_t *__restrict__ status) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   const int i = blockIdx.x;
@@ -417,7 +654,8 @@ __global__ __launch_bounds__(NT) void k_nnls_batched(NnlsChunk ch, int base, con
   const int64_t t0 = ch.cu_t[i];
   const int p = int(ch.cu_t[i + 1] - t0);
   int it = 0, st = 0;
-  nnls_block(G + ch.cu_t2[i], p, p, g + t0, w + t0, warm ? p : 0, np_, smem, maxp, &it, &st);
+  nnls_solve(G + ch.cu_t2[i], p, p, g + t0, nullptr, w + t0, warm ? p : 0, prm, smem, maxp, 0, nullptr, nullptr,
+             prm.pg_iters, &it, &st);
   if (threadIdx.x == 0) {
     if (iters) iters[base + i] = it;
     if (status) status[base + i] = st;
@@ -426,15 +664,15 @@ __global__ __launch_bounds__(NT) void k_nnls_batched(NnlsChunk ch, int base, con
 
 }  // namespace
 
-hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int kR, const NnlsParams &np,
+hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int kR, int polish, const NnlsParams &np,
                        hipStream_t s) {
   const int maxp = int(dm.max_t);
   const size_t bytes = nnls_smem_bytes(maxp);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_nnls_cycle),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_nnls_cycle, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.bvec, b.w, cycle, kR,
-                     np, maxp, b.tr_iters, b.tr_weight, b.head_status);
+  hipLaunchKernelGGL(k_nnls_cycle, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.bvec, b.gA, b.w, cycle,
+                     kR, polish, np, maxp, b.nn_L, b.nn_P, b.nn_np, b.tr_iters, b.tr_weight, b.head_status);
   return hipGetLastError();
 }
 

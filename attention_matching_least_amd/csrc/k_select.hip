@@ -273,44 +273,67 @@ __global__ __launch_bounds__(256) void k_panel(const HeadDesc *__restrict__ desc
 }
 
 // ---------------------------------------------------------------------------
-// gram: G[a][b] and G[b][a] for a < S0 + Kc, b in the new slots; b_b = Phi_b^T m.
-// One block = 64 rows a (the row index a == S0 + Kc stands for m) x 16 new columns.
+// gram: G[a][b] and G[b][a] for a < S0 + Kc, b in the new slots; b_b = Phi_b^T m;
+// and gA[a] = Phi_a^T r for every a < S0 + Kc, the gradient of the NNLS at the
+// previous weights computed from the float64 panel and residual.
+// One block = 64 rows a (the row index a == S0 + Kc stands for m) x 16 new
+// columns; the blocks of the first column tile also carry the r column.
+// polish: no new column, gA over all t slots.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_gram(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
-                                              const double *__restrict__ m, int cycle, int kR,
-                                              double *__restrict__ G, double *__restrict__ bvec) {
+                                              const double *__restrict__ m, const double *__restrict__ r, int cycle,
+                                              int kR, int polish, double *__restrict__ G, double *__restrict__ bvec,
+                                              double *__restrict__ gA) {
   constexpr int CH = 64;
   __shared__ double xs[64][CH + 1];
-  __shared__ double zs[16][CH + 1];
+  __shared__ double zs[17][CH + 1];
   const int h = blockIdx.z;
   const HeadDesc D = desc[h];
   int64_t S0;
-  const int Kc = cycle_keys(D, cycle, kR, &S0);
-  if (Kc == 0) return;
+  int Kc;
+  if (polish) {
+    S0 = D.t;
+    Kc = 0;
+  } else {
+    Kc = cycle_keys(D, cycle, kR, &S0);
+    if (Kc == 0) return;
+  }
   const int64_t Snew = S0 + Kc;
   const int64_t a0 = int64_t(blockIdx.x) * 64;
   const int b0 = blockIdx.y * 16;
-  if (a0 > Snew || b0 >= Kc) return;
+  const bool rcol = blockIdx.y == 0;
+  // rows a <= Snew when there are new columns (a == Snew is m), a < Snew otherwise
+  const int64_t rows = Kc > 0 ? Snew + 1 : Snew;
+  if (a0 >= rows || (b0 >= Kc && !rcol)) return;
   const int tid = threadIdx.x;
   const int ta = tid >> 2, tb = (tid & 3) * 4;
   const double *P = panel + D.panel_off;
   const int64_t n = D.n;
   double acc[4] = {0.0, 0.0, 0.0, 0.0};
+  double accr = 0.0;
   for (int64_t i0 = 0; i0 < n; i0 += CH) {
     for (int e = tid; e < 64 * CH; e += 256) {
-      const int r = e / CH, c = e % CH;
-      const int64_t a = a0 + r, i = i0 + c;
+      const int rr = e / CH, c = e % CH;
+      const int64_t a = a0 + rr, i = i0 + c;
       double v = 0.0;
       if (i < n) {
         if (a < Snew) v = P[a * n + i];
-        else if (a == Snew) v = m[D.n_off + i];
+        else if (a == Snew && Kc > 0) v = m[D.n_off + i];
       }
-      xs[r][c] = v;
+      xs[rr][c] = v;
     }
-    for (int e = tid; e < 16 * CH; e += 256) {
-      const int r = e / CH, c = e % CH;
-      const int64_t b = S0 + b0 + r, i = i0 + c;
-      zs[r][c] = (b0 + r < Kc && i < n) ? P[b * n + i] : 0.0;
+    for (int e = tid; e < 17 * CH; e += 256) {
+      const int rr = e / CH, c = e % CH;
+      const int64_t i = i0 + c;
+      double v = 0.0;
+      if (i < n) {
+        if (rr < 16) {
+          if (b0 + rr < Kc) v = P[(S0 + b0 + rr) * n + i];
+        } else if (rcol) {
+          v = r[D.n_off + i];
+        }
+      }
+      zs[rr][c] = v;
     }
     __syncthreads();
 #pragma unroll 4
@@ -318,6 +341,7 @@ __global__ __launch_bounds__(256) void k_gram(const HeadDesc *__restrict__ desc,
       const double x = xs[ta][c];
 #pragma unroll
       for (int q = 0; q < 4; ++q) acc[q] = fma(x, zs[tb + q][c], acc[q]);
+      accr = fma(x, zs[16][c], accr);
     }
     __syncthreads();
   }
@@ -335,6 +359,7 @@ __global__ __launch_bounds__(256) void k_gram(const HeadDesc *__restrict__ desc,
       bvec[D.t_off + b] = acc[q];
     }
   }
+  if (rcol && (tid & 3) == 0 && a < Snew) gA[D.t_off + a] = accr;
 }
 
 // ---------------------------------------------------------------------------
@@ -342,14 +367,19 @@ __global__ __launch_bounds__(256) void k_gram(const HeadDesc *__restrict__ desc,
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_resid(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
                                                const double *__restrict__ w, const double *__restrict__ m, int cycle,
-                                               int kR, double *__restrict__ r, double *__restrict__ mhat) {
+                                               int kR, int polish, double *__restrict__ r, double *__restrict__ mhat) {
   __shared__ double ws[kLdsMaxT];
   const int h = blockIdx.y;
   const HeadDesc D = desc[h];
-  int64_t S0;
-  const int Kc = cycle_keys(D, cycle, kR, &S0);
-  if (Kc == 0) return;
-  const int64_t p = S0 + Kc;
+  int64_t p;
+  if (polish) {
+    p = D.t;
+  } else {
+    int64_t S0;
+    const int Kc = cycle_keys(D, cycle, kR, &S0);
+    if (Kc == 0) return;
+    p = S0 + Kc;
+  }
   for (int a = threadIdx.x; a < p; a += 256) ws[a] = w[D.t_off + a];
   __syncthreads();
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
@@ -389,17 +419,17 @@ hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int kR, hip
   return hipGetLastError();
 }
 
-hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int kR, int polish, hipStream_t s) {
   // rows a in [0, S0 + Kc], so up to max_t + 1 rows; new columns up to kR
   const int64_t rows = dm.max_t + 1;
-  dim3 grid(unsigned((rows + 63) / 64), unsigned((kR + 15) / 16), unsigned(dm.H));
-  hipLaunchKernelGGL(k_gram, grid, dim3(256), 0, s, b.desc, b.panel, b.m, cycle, kR, b.G, b.bvec);
+  dim3 grid(unsigned((rows + 63) / 64), unsigned(polish ? 1 : (kR + 15) / 16), unsigned(dm.H));
+  hipLaunchKernelGGL(k_gram, grid, dim3(256), 0, s, b.desc, b.panel, b.m, b.r, cycle, kR, polish, b.G, b.bvec, b.gA);
   return hipGetLastError();
 }
 
-hipError_t launch_resid(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+hipError_t launch_resid(const Dims &dm, const Buffers &b, int cycle, int kR, int polish, hipStream_t s) {
   dim3 grid(unsigned((dm.max_n + 255) / 256), unsigned(dm.H));
-  hipLaunchKernelGGL(k_resid, grid, dim3(256), 0, s, b.desc, b.panel, b.w, b.m, cycle, kR, b.r, b.mhat);
+  hipLaunchKernelGGL(k_resid, grid, dim3(256), 0, s, b.desc, b.panel, b.w, b.m, cycle, kR, polish, b.r, b.mhat);
   return hipGetLastError();
 }
 

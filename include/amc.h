@@ -111,8 +111,8 @@ typedef struct {
   amc_select select;
   int32_t topk;           /* k: keys taken per iteration (1 for AMC_SEL_OMP) */
   int32_t refit_every;    /* R: refit after every R-th iteration (1 for AMC_SEL_OMP) */
-  int32_t nnls_pg_iters;  /* projected-gradient iterations before the active-set polish */
   int32_t nnls_max_iters; /* active-set iteration cap per refit (0 = 3 * budget + 30) */
+  int32_t nnls_polish;    /* refinement refits after the last key (default 1) */
   double nnls_tol;        /* KKT tolerance relative to max |b| in unit-diagonal form (0 = 10 eps t) */
   uint64_t phi_budget_bytes; /* Phi is stored when sum_h n_h T_h * 4 <= this */
   amc_dtype cv_dtype;     /* C_v output type (default AMC_F32) */
@@ -135,9 +135,11 @@ typedef struct {
   uint64_t total_bytes;
 } amc_trace_layout;
 
-/* Fills *o with the defaults: plain OMP (k = R = 1), 8 projected-gradient
- * iterations, automatic NNLS cap and tolerance, 64 GiB Phi budget, float32
- * C_v, no trace, no timer. */
+/* Fills *o with the defaults: plain OMP (k = R = 1), automatic NNLS cap and
+ * tolerance, one polish refit, 64 GiB Phi budget, float32 C_v, no trace, no
+ * timer.  Every refit starts from the previous refit's exact minimiser and
+ * from the gradient Phi_S^T r of its float64 residual; a polish refit repeats
+ * that once with no new key. */
 void amc_default_options(amc_options *o);
 
 /* Workspace bytes amc_compact needs for this problem (device memory,

@@ -10,6 +10,15 @@ Then: beta within 1e-3 (absolute) on keys active on both sides, a key active
 on one side only carries at most 1e-6 of that side's largest weight, and the
 relative mass and attention-output errors of the GPU's compacted block are
 within 1e-3 (absolute) of the oracle's own.
+
+The beta rule presumes the NNLS weights are determined to that accuracy in
+float64.  For each head the check first measures the oracle's own envelope:
+the final NNLS solved by two exact methods (Lawson-Hanson on Phi_S and FNNLS
+on its Gram matrix).  Where those disagree by more than the beta tolerance,
+the weights are not identifiable at float64 (nearly collinear columns: the
+fitted mass agrees to ~1e-7 while single weights move by large factors); the
+report says so with the envelope, and the GPU's weights are held to the
+minimum instead: their NNLS residual within 1e-6 (relative) of Lawson-Hanson's.
 """
 from __future__ import annotations
 
@@ -24,6 +33,7 @@ MARGIN_TOL = 1e-6
 BETA_TOL = 1e-3
 ERR_TOL = 1e-3
 WEIGHT_REL = 1e-6
+RESID_REL = 1e-6
 
 
 def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -76,16 +86,39 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
     act_g, act_r = w_gpu > 0, w_ref > 0
     both = act_g & act_r
     rep["beta_maxdiff"] = float(np.max(np.abs(beta[both] - ref.beta[both]))) if np.any(both) else 0.0
-    only_g = act_g & ~act_r
-    only_r = act_r & ~act_g
-    rep["one_sided_ok"] = bool(np.all(w_gpu[only_g] <= WEIGHT_REL * w_gpu.max(initial=0.0)) and
-                               np.all(w_ref[only_r] <= WEIGHT_REL * w_ref.max(initial=0.0)))
+    rep["one_sided_ok"] = _one_sided_ok(w_gpu, w_ref)
+    # the oracle's own envelope for these weights
+    P = ref.features.Phi[:, np.asarray(ref.sel_idx)]
+    m = ref.features.m
+    w_alt = O.fnnls(P.T @ P, P.T @ m) if len(w_ref) <= 256 else O.nnls_lawson_hanson(P, m)
+    lw_r, lw_a = np.log(np.where(w_ref > 0, w_ref, 1.0)), np.log(np.where(w_alt > 0, w_alt, 1.0))
+    both_o = (w_ref > 0) & (w_alt > 0)
+    env = float(np.max(np.abs(lw_r - lw_a)[both_o])) if np.any(both_o) else 0.0
+    rep["beta_envelope"] = env
+    rep["beta_identifiable"] = env <= BETA_TOL and _one_sided_ok(w_alt, w_ref)
+    # the GPU's float64 weights (trace, selection order) in ascending key order
+    order = np.argsort(np.asarray(trace["pick"][h]), kind="stable")
+    w_gpu64 = np.asarray(trace["weight"][h], dtype=np.float64)[order]
+    res_g = float(np.linalg.norm(m - P @ w_gpu64))
+    res_r = float(np.linalg.norm(m - P @ w_ref))
+    rep["resid_excess"] = (res_g - res_r) / max(res_r, 1e-300)
     e_gpu = oracle.errors(Q, K, V, Ck, beta, Cv, beta_in)
     e_ref = oracle.errors(Q, K, V, ref.Ck, ref.beta, ref.Cv, beta_in)
     rep["e_gpu"], rep["e_ref"] = e_gpu, e_ref
     rep["e_mass_diff"] = abs(e_gpu[0] - e_ref[0])
     rep["e_out_diff"] = abs(e_gpu[1] - e_ref[1])
-    rep["ok"] = (not rep["mismatch_iters"] and rep["same_set"] and rep["ck_exact"] and
-                 rep["beta_maxdiff"] <= BETA_TOL and rep["one_sided_ok"] and
+    if rep["beta_identifiable"]:
+        weights_ok = rep["beta_maxdiff"] <= BETA_TOL and rep["one_sided_ok"]
+    else:
+        weights_ok = rep["resid_excess"] <= RESID_REL
+    rep["ok"] = (not rep["mismatch_iters"] and rep["same_set"] and rep["ck_exact"] and weights_ok and
                  rep["e_mass_diff"] <= ERR_TOL and rep["e_out_diff"] <= ERR_TOL)
     return rep
+
+
+def _one_sided_ok(wa, wb):
+    """A key active on one side only carries at most WEIGHT_REL of that side's largest weight."""
+    only_a = (wa > 0) & ~(wb > 0)
+    only_b = (wb > 0) & ~(wa > 0)
+    return bool(np.all(wa[only_a] <= WEIGHT_REL * wa.max(initial=0.0)) and
+                np.all(wb[only_b] <= WEIGHT_REL * wb.max(initial=0.0)))

@@ -50,7 +50,7 @@ def test_default_options():
     o = amc.make_options()
     assert o.select == amc.AMC_SEL_OMP and o.topk == 1 and o.refit_every == 1
     assert o.phi_budget_bytes == 64 << 30
-    assert o.nnls_pg_iters == 8 and o.flags == 0
+    assert o.nnls_polish == 1 and o.flags == 0
 
 
 def test_offsets_and_workspace():
