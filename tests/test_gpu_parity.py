@@ -79,6 +79,11 @@ def test_nnls_against_oracle(pg_iters):
         bs.append(A.T @ y)
     _say(f"nnls {len(Gs)} systems, pg_iters={pg_iters}")
     ws, iters, status = amc.nnls(Gs, bs, pg_iters=pg_iters)
+    for A, y, G, b, w, it, st in zip(As, ys, Gs, bs, ws, iters, status):
+        ref = oracle.fnnls(G, b)
+        _say(f"t={len(b)} kkt={O.nnls_kkt_violation(G, b, w):.2e} iters={it} status={st} "
+             f"active gpu={int((w > 0).sum())} oracle={int((ref > 0).sum())} "
+             f"fit={np.linalg.norm(A @ (w - ref)) / np.linalg.norm(y):.2e}")
     for A, y, G, b, w in zip(As, ys, Gs, bs, ws):
         ref = oracle.fnnls(G, b)
         assert O.nnls_kkt_violation(G, b, w) < 1e-8
