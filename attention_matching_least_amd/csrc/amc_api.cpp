@@ -64,7 +64,7 @@ struct Plan {
   uint64_t o_desc = 0, o_shift_part = 0, o_shift = 0, o_phi = 0, o_m = 0, o_r = 0, o_mhat = 0,
            o_Y = 0, o_sel_slot = 0, o_sel_list = 0, o_panel = 0, o_G = 0, o_bvec = 0, o_w = 0,
            o_rhs = 0, o_cvsel = 0, o_pos = 0, o_cand_val = 0, o_cand_idx = 0, o_flist = 0, o_fcount = 0,
-           o_dn = 0, o_L = 0, o_nnL = 0, o_nnP = 0, o_nnnp = 0, o_gA = 0, total = 0;
+           o_dn = 0, o_L = 0, o_nnL = 0, o_nnP = 0, o_nnnp = 0, o_gA = 0, o_nnvec = 0, total = 0;
 };
 
 static amc_status check_problem(const amc_problem *p) {
@@ -153,6 +153,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     dm.max_n = std::max(dm.max_n, D.n);
     dm.max_T = std::max(dm.max_T, D.T);
     dm.max_t = std::max(dm.max_t, D.t);
+    dm.min_t = h == 0 ? D.t : std::min(dm.min_t, D.t);
     dm.max_sblk = std::max(dm.max_sblk, D.n_sblk);
     dm.max_cblk = std::max(dm.max_cblk, D.n_cblk);
     pl.max_cycles = std::max(pl.max_cycles, cycles);
@@ -205,6 +206,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.o_nnP = take(4ull * tt);
   pl.o_nnnp = take(4ull * H);
   pl.o_gA = take(8ull * tt);
+  pl.o_nnvec = dm.max_t > kNnlsLdsT ? take(8ull * kNnlsVecPerSlot * tt) : 0;
   pl.total = off;
   return AMC_OK;
 }
@@ -376,6 +378,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   b.nn_L = reinterpret_cast<double *>(ws + pl.o_nnL);
   b.nn_P = reinterpret_cast<int32_t *>(ws + pl.o_nnP);
   b.nn_np = reinterpret_cast<int32_t *>(ws + pl.o_nnnp);
+  b.nn_vec = pl.dm.max_t > kNnlsLdsT ? reinterpret_cast<double *>(ws + pl.o_nnvec) : nullptr;
   b.gA = reinterpret_cast<double *>(ws + pl.o_gA);
   b.head_status = head_status;
   if (tracing) {
@@ -470,7 +473,7 @@ amc_status amc_nnls(int32_t num, const int64_t *cu_t, const double *G, const dou
   for (int i = 0; i < num; ++i) {
     const int64_t t = cu_t[i + 1] - cu_t[i];
     if (t < 1) return AMC_ERR_INVALID_ARG;
-    if (t > kLdsMaxT) return AMC_ERR_UNSUPPORTED;
+    if (t > kNnlsLdsT) return AMC_ERR_UNSUPPORTED;
     max_t = std::max(max_t, t);
     cu2[i + 1] = cu2[i] + t * t;
   }

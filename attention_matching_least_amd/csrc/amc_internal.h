@@ -14,7 +14,9 @@ constexpr int kPhiRows = 64;     // queries per block of the mass-feature kernel
 constexpr int kPhiKeys = 64;     // keys per tile of the mass-feature kernel
 constexpr int kSweepCols = 256;  // columns per block of the correlation sweep
 constexpr int kMaxCycle = 255;   // largest k * R (keys per refit cycle)
-constexpr int kLdsMaxT = 192;    // largest budget of the LDS-resident NNLS / value fit
+constexpr int kLdsMaxT = 192;    // largest budget of the LDS-resident value fit
+constexpr int kNnlsLdsT = 176;   // largest budget whose NNLS state fits in LDS (larger: global memory)
+constexpr int kNnlsVecPerSlot = 13;  // float64 words of global NNLS state per budget slot
 constexpr int kMaxSweepBlocks = 1024;  // sweep column blocks per head the merge handles
 
 // Per-head descriptor, computed on the host and copied to the device once per call.
@@ -66,6 +68,7 @@ struct Buffers {
   double *nn_L;        // [sum t*(t+1)/2] NNLS factor of the free set, kept between refits
   int32_t *nn_P;       // [sum t]  NNLS free set in factor order
   int32_t *nn_np;      // [H]      NNLS free-set size
+  double *nn_vec;      // [sum t][kNnlsVecPerSlot] NNLS vectors of heads above kNnlsLdsT (else null)
   double *cand_val;    // [sum n_cblk][kMaxCycle + 1]
   int32_t *cand_idx;   // [sum n_cblk][kMaxCycle + 1]
   int32_t *head_status;  // [H] or null
@@ -78,7 +81,7 @@ struct Dims {
   int H, d;
   int in_bf16;         // 1: Q/K/V are bfloat16, 0: float32
   double scale;
-  int64_t max_n, max_T, max_t;
+  int64_t max_n, max_T, max_t, min_t;
   int64_t max_sblk, max_cblk;
   int64_t total_sblk;
 };

@@ -6,31 +6,35 @@
 // Fig. 2).  On these Gram matrices (condition numbers 1e9 and beyond)
 // projected gradient alone does not reach the minimiser, so the exact
 // minimiser is found by an active-set method on the Gram form (Bro and
-// De Jong's fast NNLS): the most violating zero variable enters, the
+// De Jong's fast NNLS): zero variables with a positive gradient enter, the
 // least-squares solution on the free set is computed from a Cholesky factor,
 // and if it leaves the feasible set the iterate steps back and the blocking
 // variables leave.  Projected gradient survives as the warm-up of the
 // stand-alone solver (amc_nnls).
 //
 // Accuracy.  Everything is float64 in unit-diagonal form (w = u / sqrt(diag
-// G)).  The solver works in correction form: it keeps the gradient
-// g = b - G u explicitly, moves by corrections d = G_PP^-1 g_P solved with the
-// factor, and updates g by -G d.  Inside a compaction each refit starts from
-// g = Phi_S^T r computed from the float64 panel and the float64 residual of
-// the previous refit (the corrected semi-normal equations of Bjorck), so the
-// gradient never suffers the cancellation of b - G u, and a final refit with
-// no new key refines the weights once more.
+// G)).  The solver keeps the gradient g = b - G u explicitly.  Each refit of
+// a compaction starts from g = Phi_S^T r computed from the float64 panel and
+// the float64 residual of the previous refit (the corrected semi-normal
+// equations of Bjorck), and a final refit with no new key refines the weights
+// once more.  Within a refit the rows of zero variables follow every step
+// exactly (g_Z -= G_ZP delta, read from G); the rows of the free set follow
+// the factor's model: the step d solves L L^T d = g_P, so moving a fraction
+// alpha along d scales g_P by (1 - alpha).
 //
-// The factor is updated, not recomputed.  Up to eight zero variables with a
-// positive gradient enter together: one forward substitution with several
-// right-hand sides gives their new factor rows and L^-1 g for the following
-// solve, and a small Cholesky of the block finishes the rows.  A variable
-// that leaves is deleted by a row shift plus a rank-one update of the
-// trailing block.  Between the refits of one compaction the factor and the
-// free set persist in the workspace.  The sequential passes run in one wave
-// with vectors spread over the lanes' registers (index i lives in lane i % 64,
-// slot i / 64, broadcast with v_readlane); the mat-vecs use the whole block.
-// The packed factor of up to 192 variables lives in LDS.
+// The factor is updated, not recomputed.  Up to eight candidates enter
+// together: one blocked forward substitution with several right-hand sides
+// gives their factor rows and L^-1 g for the following solve, and a small
+// Cholesky of the block finishes the rows.  A variable that leaves is deleted
+// by a row shift plus a blocked rank-one update of the trailing rows.  Between
+// the refits of one compaction the factor and the free set persist in the
+// workspace.
+//
+// GPU mapping: one 256-thread block per system.  Triangular work runs in
+// 16-row blocks: one wave solves the 16 x 16 diagonal block in registers
+// (v_readlane broadcasts), then every thread updates one of the rows beyond
+// it.  The state lives in LDS for budgets up to kNnlsLdsT; above that the same
+// code runs on the workspace copy in global memory.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -44,24 +48,20 @@ namespace amc {
 namespace {
 
 constexpr int NT = 256;
-constexpr int NR = (kLdsMaxT + 63) / 64;  // register slots per lane for a vector of length <= kLdsMaxT
-constexpr int NB = 8;  // zero variables that may enter together
-constexpr unsigned char F_PASSIVE = 1, F_BLOCKED = 2, F_NEW = 4;
+constexpr int NW = NT / 64;
+constexpr int TB = 16;             // triangular block
+constexpr int NB = 8;              // candidates that may enter together
+constexpr int NRHS = NB + 1;       // rows of the right-hand-side scratch
+constexpr unsigned char F_PASSIVE = 1, F_BLOCKED = 2, F_NEW = 4, F_DROP = 8, F_CAND = 16;
 constexpr double PIV_TOL = 1e-14;  // smallest acceptable squared pivot in unit-diagonal form
+static_assert(NRHS <= 3 * NW, "diagonal solves take three right-hand sides per wave");
+static_assert(NRHS >= 8, "settle uses rows 1..7 of the right-hand-side scratch");
 
 __device__ __forceinline__ int tri(int r) { return r * (r + 1) / 2; }
 
-__device__ __forceinline__ void wsync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
-
-__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
-
 // Compile-time loop: f(integral_constant<int, I>) for I in [B, E).  Register
-// arrays indexed only through it keep constant indices from the front end
-// on, so they are never demoted to scratch memory.
+// arrays indexed only through it keep constant indices, so they stay in
+// registers.
 template <int B, int E, typename F>
 __device__ __forceinline__ void static_for(F &&f) {
   if constexpr (B < E) {
@@ -77,26 +77,6 @@ __device__ __forceinline__ double rl(double x, int lane) {
   return __hiloint2double(hi, lo);
 }
 
-// element k of a lane-distributed vector, broadcast to every lane
-__device__ __forceinline__ double getv(const double (&r)[NR], int k) {
-  const int s = k >> 6;
-  double x = r[0];
-  static_for<1, NR>([&](auto M) {
-    constexpr int m = M;
-    x = (s == m) ? r[m] : x;
-  });
-  return rl(x, k & 63);
-}
-
-__device__ __forceinline__ void setv(double (&r)[NR], int k, double v) {
-  const bool mine = lane_id() == (k & 63);
-  const int s = k >> 6;
-  static_for<0, NR>([&](auto M) {
-    constexpr int m = M;
-    r[m] = (mine && s == m) ? v : r[m];
-  });
-}
-
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
@@ -104,11 +84,12 @@ __device__ __forceinline__ double wave_sum(double v) {
 }
 
 struct Red {
-  double v[NT / 64];
-  int i[NT / 64];
+  double v[NW];
+  int i[NW];
 };
 
-// Block max of v (ties to the lower index); returns the winning index, -1 if none valid.
+// Block max of v (ties to the lower index); returns the winning index, -1 if
+// no thread passed a valid one.  Every thread gets the result.
 __device__ __forceinline__ int block_argmax(double v, int idx, Red *red, double *out_v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
 #pragma unroll
@@ -128,7 +109,7 @@ __device__ __forceinline__ int block_argmax(double v, int idx, Red *red, double 
   __syncthreads();
   v = red->v[0];
   idx = red->i[0];
-  for (int w = 1; w < NT / 64; ++w) {
+  for (int w = 1; w < NW; ++w) {
     const double ov = red->v[w];
     const int oi = red->i[w];
     if (oi >= 0 && (idx < 0 || ov > v || (ov == v && oi < idx))) {
@@ -140,572 +121,726 @@ __device__ __forceinline__ int block_argmax(double v, int idx, Red *red, double 
   return idx;
 }
 
-// LDS state of one solve
-struct St {
-  double *L;      // packed lower factor of Gs_PP, rows in free-set order
-  double *rdiag;  // 1 / L_kk
-  double *u;      // scaled iterate, per variable
-  double *g;      // scaled gradient bs - Gs u, per variable
-  double *dg;     // sqrt(G_aa)
-  double *bs;     // b_a / dg_a
-  double *delta;  // step of the free variables, in factor order
-  double *blk;    // block-append scratch: dot products and block rows
-  int *plist;     // free set in factor order
-  int *cand;      // entering candidates
-  int *np;        // free-set size
-  int *ctl;       // wave-0 decisions broadcast to the block: [0] settle step, [1] candidates,
-                  // [2] free-set size, [3] enter one at a time from now on
-  unsigned char *flag;
+__device__ __forceinline__ int block_count(int c, Red *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+  __syncthreads();
+  if (lane == 0) red->i[wave] = c;
+  __syncthreads();
+  int s = 0;
+  for (int w = 0; w < NW; ++w) s += red->i[w];
+  return s;
+}
+
+// Small per-block scratch (always LDS).
+struct Blk {
+  double dots[NRHS * NRHS];  // Gram of the forward-solved candidate rows (lower triangle)
+  double Gc[NB * NB];        // scaled G among the candidates
+  double E[NB * NB];         // factor entries among accepted candidates
+  double Dg[NB];             // their diagonal
+  double yb[NB];             // their entries of L^-1 g
+  double cs[2 * TB];         // rotations of one block of the rank-one update
+  int cand[NB];              // entering candidates
+  int accb[NB];              // accepted candidates, in order
+  int ctl[8];                // [1], [4] scan state, [2] accepted count, [3] enter one at a time
+  int np;                    // free-set size
 };
 
-constexpr int BLK_DOUBLES = (NB + 1) * (NB + 1) + NB * NB + 2 * NB;
+// State of one solve.  Vectors are indexed by variable (u, g, dg, flag) or by
+// factor position (plist, rhs rows).
+struct St {
+  double *L;      // packed lower factor of Gs_PP, rows in free-set order
+  double *u;      // scaled iterate
+  double *g;      // scaled gradient bs - Gs u
+  double *dg;     // sqrt(G_aa)
+  double *rhs;    // NRHS rows of mp: right-hand sides; in settle row 0 = solve vector,
+                  // 1 = step, 2 = step / dg, 3..6 = partial sums, 7 = removed column
+  int *plist;     // free set in factor order
+  unsigned char *flag;
+  Blk *bk;
+  int mp;         // row stride of rhs (largest p of the system)
+};
 
-__device__ St carve(char *base, int maxp) {
+// LDS bytes of the state for systems up to maxp variables (LDS variant)
+__host__ __device__ constexpr size_t nnls_smem_bytes(int maxp) {
+  return size_t(8) * (size_t(maxp) * (maxp + 1) / 2 + size_t(3 + NRHS) * maxp) + 4 * size_t(maxp) +
+         ((size_t(maxp) + 15) & ~size_t(15));
+}
+
+__device__ __forceinline__ St carve_lds(char *base, int maxp, Blk *bk) {
   St s;
+  s.mp = maxp;
+  s.bk = bk;
   double *d = reinterpret_cast<double *>(base);
   s.L = d;
   d += tri(maxp);
-  s.rdiag = d;
-  d += maxp;
   s.u = d;
   d += maxp;
   s.g = d;
   d += maxp;
   s.dg = d;
   d += maxp;
-  s.bs = d;
-  d += maxp;
-  s.delta = d;
-  d += maxp;
-  s.blk = d;
-  d += BLK_DOUBLES;
+  s.rhs = d;
+  d += NRHS * maxp;
   s.plist = reinterpret_cast<int *>(d);
-  s.cand = s.plist + maxp;
-  s.np = s.cand + NB;
-  s.ctl = s.np + 1;
-  s.flag = reinterpret_cast<unsigned char *>(s.ctl + 4);
+  s.flag = reinterpret_cast<unsigned char *>(s.plist + maxp);
   return s;
 }
 
-__host__ __device__ constexpr size_t nnls_smem_bytes(int maxp) {
-  return size_t(8) * (size_t(maxp) * (maxp + 1) / 2 + 6 * size_t(maxp) + BLK_DOUBLES) +
-         4 * (size_t(maxp) + NB + 5) + size_t(maxp) + 16;
+// Global-memory state of one head: u, g, dg, the rhs rows, then the flag bytes.
+__device__ __forceinline__ St carve_global(double *vec, double *L, int32_t *plist, int mp, Blk *bk) {
+  St s;
+  s.mp = mp;
+  s.bk = bk;
+  s.L = L;
+  s.u = vec;
+  s.g = vec + mp;
+  s.dg = vec + 2 * mp;
+  s.rhs = vec + 3 * mp;
+  s.flag = reinterpret_cast<unsigned char *>(vec + (3 + NRHS) * mp);
+  s.plist = plist;
+  return s;
 }
+static_assert(kNnlsVecPerSlot == 3 + NRHS + 1, "global NNLS state layout");
 
-// ---- wave-0 routines ------------------------------------------------------
+// ---- triangular solves ----------------------------------------------------
 
-// L x = r (forward) for B right-hand sides at once, leading n rows.  The
-// column of L for the next step is loaded while the current one is applied.
-template <int B>
-__device__ __forceinline__ void fwd_multi(const St &S, int n, double (&r)[B][NR]) {
-  const int lane = lane_id();
-  double nxt[NR];
-  static_for<0, NR>([&](auto I_m) {
-    constexpr int m = decltype(I_m)::value;
-    const int i = lane + 64 * m;
-    nxt[m] = (i > 0 && i < n) ? S.L[tri(i)] : 0.0;
-  });
-  for (int k = 0; k < n; ++k) {
-    double cur[NR];
-    static_for<0, NR>([&](auto I_m) {
-      constexpr int m = decltype(I_m)::value;
-      cur[m] = nxt[m];
-    });
-    if (k + 1 < n) {
-      static_for<0, NR>([&](auto I_m) {
-        constexpr int m = decltype(I_m)::value;
-        const int i = lane + 64 * m;
-        nxt[m] = (i > k + 1 && i < n) ? S.L[tri(i) + k + 1] : 0.0;
+// Solves L X = R in place for the nr right-hand sides rhs[b * mp + k], k < n.
+__device__ __forceinline__ void fwd_blk(const St &S, int n, int nr) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int mp = S.mp;
+  for (int r0 = 0; r0 < n; r0 += TB) {
+    const int e = n - r0 < TB ? n - r0 : TB;
+    // diagonal block: wave w solves right-hand sides w, w + 4, w + 8; lane i holds row r0 + i
+    if (wave < nr && lane < TB) {
+      const int i = lane;
+      const bool act = i < e;
+      const int rb = act ? tri(r0 + i) + r0 : 0;
+      double Lrow[TB];
+      static_for<0, TB>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        Lrow[j] = (act && j < i) ? S.L[rb + j] : 0.0;
       });
-    }
-    const double rk = S.rdiag[k];
-    static_for<0, B>([&](auto I_b) {
-      constexpr int b = decltype(I_b)::value;
-      const double xk = getv(r[b], k) * rk;
-      setv(r[b], k, xk);
-      static_for<0, NR>([&](auto I_m) {
-        constexpr int m = decltype(I_m)::value;
-        r[b][m] = fma(-cur[m], xk, r[b][m]);
+      const double rd = act ? 1.0 / S.L[rb + i] : 0.0;
+      double x[3];
+      static_for<0, 3>([&](auto Qc) {
+        constexpr int q = decltype(Qc)::value;
+        const int b = wave + NW * q;
+        x[q] = (act && b < nr) ? S.rhs[b * mp + r0 + i] : 0.0;
       });
-    });
-  }
-}
-
-// L^T x = r (backward), leading n rows
-__device__ __forceinline__ void bwd(const St &S, int n, double (&r)[NR]) {
-  const int lane = lane_id();
-  double nxt[NR];
-  static_for<0, NR>([&](auto I_m) {
-    constexpr int m = decltype(I_m)::value;
-    const int i = lane + 64 * m;
-    nxt[m] = (n > 0 && i < n - 1) ? S.L[tri(n - 1) + i] : 0.0;
-  });
-  for (int k = n - 1; k >= 0; --k) {
-    double cur[NR];
-    static_for<0, NR>([&](auto I_m) {
-      constexpr int m = decltype(I_m)::value;
-      cur[m] = nxt[m];
-    });
-    if (k > 0) {
-      static_for<0, NR>([&](auto I_m) {
-        constexpr int m = decltype(I_m)::value;
-        const int i = lane + 64 * m;
-        nxt[m] = (i < k - 1) ? S.L[tri(k - 1) + i] : 0.0;
-      });
-    }
-    const double xk = getv(r, k) * S.rdiag[k];
-    setv(r, k, xk);
-    static_for<0, NR>([&](auto I_m) {
-      constexpr int m = decltype(I_m)::value;
-      r[m] = fma(-cur[m], xk, r[m]);
-    });
-  }
-}
-
-__device__ __forceinline__ double gs(const St &S, const double *G, int64_t ld, int a, int c) {
-  return G[int64_t(a) * ld + c] / (S.dg[a] * S.dg[c]);
-}
-
-// Appends the nc <= NB candidates in S.cand (zero, not blocked) to the free
-// set.  One forward pass over the current factor gives each candidate's row
-// l = L^-1 Gs[P, j] and y_P = L^-1 g_P; the rows are finished by a Cholesky
-// of the block (candidates whose pivot vanishes are blocked).  Returns
-// y = L^-1 g_P over the extended free set in registers.
-__device__ __forceinline__ void block_append(const St &S, const double *G, int64_t ld, int nc, double (&y)[NR],
-                                             int *status) {
-  const int lane = lane_id();
-  const int np0 = *S.np;
-  double r[NB + 1][NR];
-  static_for<0, NR>([&](auto I_m) {
-    constexpr int m = decltype(I_m)::value;
-    const int k = lane + 64 * m;
-    const int a = k < np0 ? S.plist[k] : 0;
-    r[0][m] = k < np0 ? S.g[a] : 0.0;
-    static_for<0, NB>([&](auto I_b) {
-      constexpr int b = decltype(I_b)::value;
-      r[b + 1][m] = (k < np0 && b < nc) ? gs(S, G, ld, S.cand[b], a) : 0.0;
-    });
-  });
-  fwd_multi<NB + 1>(S, np0, r);
-  // Gram of the block rows over the old columns: dots[b1][b2] = <r_b1, r_b2>, b = 0 is y
-  double *dots = S.blk;                        // (NB+1) x (NB+1)
-  double *E = S.blk + (NB + 1) * (NB + 1);     // NB x NB: block-row entries by accepted order
-  double *Dg = E + NB * NB;                    // NB: diagonal of accepted rows
-  double *yb = Dg + NB;                        // NB: y of accepted rows
-  static_for<0, NB + 1>([&](auto I_b1) {
-    constexpr int b1 = decltype(I_b1)::value;
-    static_for<0, b1 + 1>([&](auto I_b2) {
-      constexpr int b2 = decltype(I_b2)::value;
-      if (b1 > nc || b2 > nc) return;
-      double v = 0.0;
-      static_for<0, NR>([&](auto I_m) {
-        constexpr int m = decltype(I_m)::value;
-        v = fma(r[b1][m], r[b2][m], v);
-      });
-      v = wave_sum(v);
-      if (lane == 0) dots[b1 * (NB + 1) + b2] = v;
-    });
-  });
-  wsync();
-  // Cholesky of the block, identical in every lane (wave-uniform values);
-  // loops are unrolled so the small arrays stay in registers
-  int rank[NB], idx_of[NB];
-  int nacc = 0;
-  static_for<0, NB>([&](auto I_b) {
-    constexpr int b = decltype(I_b)::value;
-    rank[b] = -1;
-    idx_of[b] = 0;
-  });
-  static_for<0, NB>([&](auto I_b) {
-    constexpr int b = decltype(I_b)::value;
-    if (b < nc) {
-      const int j = S.cand[b];
-      double row[NB];
-      double ss = dots[(b + 1) * (NB + 1) + (b + 1)];
-      double yy = S.g[j] - dots[(b + 1) * (NB + 1)];
-      static_for<0, NB>([&](auto I_a) {
-        constexpr int a = decltype(I_a)::value;
-        row[a] = 0.0;
-        if (a < nacc) {
-          const int bb = idx_of[a];
-          double v = gs(S, G, ld, j, S.cand[bb]) - dots[(b + 1) * (NB + 1) + (bb + 1)];
-          static_for<0, a>([&](auto I_a2) {
-            constexpr int a2 = decltype(I_a2)::value;
-            v -= row[a2] * E[a * NB + a2];
+      static_for<0, TB>([&](auto K) {
+        constexpr int kk = decltype(K)::value;
+        if (kk < e) {
+          static_for<0, 3>([&](auto Qc) {
+            constexpr int q = decltype(Qc)::value;
+            if (wave + NW * q < nr) {
+              const double xk = rl(x[q] * rd, kk);
+              x[q] = i == kk ? xk : (i > kk ? fma(-Lrow[kk], xk, x[q]) : x[q]);
+            }
           });
-          v /= Dg[a];
-          row[a] = v;
-          ss += v * v;
-          yy -= v * yb[a];
         }
       });
-      const double d2 = gs(S, G, ld, j, j) - ss;
-      if (d2 > PIV_TOL) {
-        const double dd = sqrt(d2);
-        rank[b] = nacc;
-        static_for<0, NB>([&](auto I_a) {
-          constexpr int a = decltype(I_a)::value;
-          if (a == nacc) idx_of[a] = b;
+      static_for<0, 3>([&](auto Qc) {
+        constexpr int q = decltype(Qc)::value;
+        const int b = wave + NW * q;
+        if (act && b < nr) S.rhs[b * mp + r0 + i] = x[q];
+      });
+    }
+    __syncthreads();
+    if (r0 + TB < n) {
+      // rows below: r_row -= L[row, block] x_block
+      for (int row = r0 + TB + tid; row < n; row += NT) {
+        const int rb = tri(row) + r0;
+        double Lr[TB];
+        static_for<0, TB>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          Lr[j] = S.L[rb + j];
         });
-        if (lane == 0) {
-          static_for<0, NB>([&](auto I_a) {
-            constexpr int a = decltype(I_a)::value;
-            if (a < nacc) E[nacc * NB + a] = row[a];
+        for (int b = 0; b < nr; ++b) {
+          const double *xb = S.rhs + b * mp + r0;
+          double a0 = 0.0, a1 = 0.0;
+          static_for<0, TB / 2>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            a0 = fma(Lr[2 * j], xb[2 * j], a0);
+            a1 = fma(Lr[2 * j + 1], xb[2 * j + 1], a1);
           });
-          Dg[nacc] = dd;
-          yb[nacc] = yy / dd;
+          S.rhs[b * mp + row] -= a0 + a1;
         }
-        wsync();
-        ++nacc;
-      } else {
-        if (lane == 0) {
+      }
+      __syncthreads();
+    }
+  }
+}
+
+// Solves L^T x = r in place for the vector x (factor order, length n >= 1).
+__device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int r0 = ((n - 1) / TB) * TB; r0 >= 0; r0 -= TB) {
+    const int e = n - r0 < TB ? n - r0 : TB;
+    if (wave == 0 && lane < TB) {
+      const int i = lane;
+      const bool act = i < e;
+      double Lc[TB];  // column i of the diagonal block, rows below i
+      static_for<0, TB>([&](auto K) {
+        constexpr int kk = decltype(K)::value;
+        Lc[kk] = (act && kk > i && kk < e) ? S.L[tri(r0 + kk) + r0 + i] : 0.0;
+      });
+      const double rd = act ? 1.0 / S.L[tri(r0 + i) + r0 + i] : 0.0;
+      double xv = act ? x[r0 + i] : 0.0;
+      static_for<0, TB>([&](auto K) {
+        constexpr int kk = TB - 1 - decltype(K)::value;
+        if (kk < e) {
+          const double xk = rl(xv * rd, kk);
+          xv = i == kk ? xk : (i < kk ? fma(-Lc[kk], xk, xv) : xv);
+        }
+      });
+      if (act) x[r0 + i] = xv;
+    }
+    __syncthreads();
+    // columns before the block: x_c -= sum_k L[r0 + k][c] x_{r0 + k}
+    for (int c = tid; c < r0; c += NT) {
+      double a0 = 0.0, a1 = 0.0;
+      static_for<0, TB / 2>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        if (2 * k < e) a0 = fma(S.L[tri(r0 + 2 * k) + c], x[r0 + 2 * k], a0);
+        if (2 * k + 1 < e) a1 = fma(S.L[tri(r0 + 2 * k + 1) + c], x[r0 + 2 * k + 1], a1);
+      });
+      x[c] -= a0 + a1;
+    }
+    __syncthreads();
+  }
+}
+
+// ---- gradient update -------------------------------------------------------
+
+// After a step: rows of the free set scale by keep (the factor's model: 0 for
+// a full step, 1 - alpha for a partial one); rows of zero variables subtract
+// G_ZP delta, with delta / dg in rhs row 2.  Each wave sums a quarter of the
+// free set, with many loads of G in flight; the quarters are added in a fixed
+// order, so the result does not depend on timing.
+__device__ __forceinline__ void grad_update(const St &S, const double *G, int64_t ld, int p, double keep) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int np = S.bk->np, mp = S.mp;
+  const int k0 = (np * wave) / NW, k1 = (np * (wave + 1)) / NW;
+  const int *pl = S.plist;
+  const double *dsc = S.rhs + 2 * mp;
+  double *zp = S.rhs + (3 + wave) * mp;
+  for (int a0 = 0; a0 < p; a0 += NT) {
+    double acc[4] = {0.0, 0.0, 0.0, 0.0};
+    int ac[4];
+    static_for<0, 4>([&](auto M) {
+      constexpr int m = decltype(M)::value;
+      const int a = a0 + lane + 64 * m;
+      ac[m] = a < p ? a : p - 1;
+    });
+    int k = k0;
+    for (; k + 8 <= k1; k += 8) {
+      int c[8];
+      double s[8];
+      static_for<0, 8>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        c[u] = pl[k + u];
+        s[u] = dsc[k + u];
+      });
+      static_for<0, 4>([&](auto M) {
+        constexpr int m = decltype(M)::value;
+        if (a0 + 64 * m < p) {
+          double v[8];
+          static_for<0, 8>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            v[u] = G[int64_t(c[u]) * ld + ac[m]];
+          });
+          static_for<0, 8>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            acc[m] = fma(v[u], s[u], acc[m]);
+          });
+        }
+      });
+    }
+    for (; k < k1; ++k) {
+      const int c = pl[k];
+      const double s = dsc[k];
+      static_for<0, 4>([&](auto M) {
+        constexpr int m = decltype(M)::value;
+        if (a0 + 64 * m < p) acc[m] = fma(G[int64_t(c) * ld + ac[m]], s, acc[m]);
+      });
+    }
+    static_for<0, 4>([&](auto M) {
+      constexpr int m = decltype(M)::value;
+      const int a = a0 + lane + 64 * m;
+      if (a < p) zp[a] = acc[m];
+    });
+  }
+  __syncthreads();
+  const double *z = S.rhs + 3 * mp;
+  for (int a = tid; a < p; a += NT) {
+    const unsigned char f = S.flag[a];
+    if (f & F_PASSIVE) {
+      S.g[a] *= keep;
+    } else if (!(f & F_BLOCKED)) {
+      S.g[a] -= ((z[a] + z[mp + a]) + (z[2 * mp + a] + z[3 * mp + a])) / S.dg[a];
+    }
+  }
+  __syncthreads();
+}
+
+// ---- factor updates --------------------------------------------------------
+
+// row of packed lower-triangle index s
+__device__ __forceinline__ int row_of(int s) {
+  int i = int((sqrtf(8.0f * float(s) + 1.0f) - 1.0f) * 0.5f);
+  if (tri(i + 1) <= s) ++i;
+  if (tri(i) > s) --i;
+  return i;
+}
+
+// Deletes factor position q: rows below move up one row without column q,
+// then the trailing rows absorb the removed column by a rank-one update
+// (Givens rotations, applied 16 columns at a time).
+__device__ __forceinline__ void remove_at(const St &S, int q) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  Blk *bk = S.bk;
+  const int np = bk->np, n2 = np - 1;
+  double *xc = S.rhs + 7 * S.mp;
+  for (int i = q + 1 + tid; i < np; i += NT) xc[i - 1] = S.L[tri(i) + q];
+  // Every element moves to a lower index, so chunks taken in increasing
+  // source order never overwrite a source that is still to be read.
+  for (int base = q; base < n2; base += NT) {
+    const int k = base + tid;
+    const int pv = k < n2 ? S.plist[k + 1] : 0;
+    __syncthreads();
+    if (k < n2) S.plist[k] = pv;
+  }
+  const int s0 = tri(q + 1), s1 = tri(np);
+  for (int base = s0; base < s1; base += NT * 8) {
+    double v[8];
+    int dst[8];
+    static_for<0, 8>([&](auto U) {
+      constexpr int u = decltype(U)::value;
+      const int s = base + u * NT + tid;
+      dst[u] = -1;
+      v[u] = 0.0;
+      if (s < s1) {
+        const int i = row_of(s);
+        const int c = s - tri(i);
+        if (c != q) {
+          dst[u] = tri(i - 1) + (c < q ? c : c - 1);
+          v[u] = S.L[s];
+        }
+      }
+    });
+    __syncthreads();
+    static_for<0, 8>([&](auto U) {
+      constexpr int u = decltype(U)::value;
+      if (dst[u] >= 0) S.L[dst[u]] = v[u];
+    });
+  }
+  __syncthreads();
+  // rank-one update: L' L'^T = L L^T + x x^T on positions q..n2-1
+  for (int k0 = q; k0 < n2; k0 += TB) {
+    const int e = n2 - k0 < TB ? n2 - k0 : TB;
+    if (wave == 0 && lane < TB) {
+      const int i = lane;
+      const bool act = i < e;
+      const int rb = act ? tri(k0 + i) + k0 : 0;
+      double Lr[TB];
+      static_for<0, TB>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        Lr[j] = (act && j <= i) ? S.L[rb + j] : 0.0;
+      });
+      double xv = act ? xc[k0 + i] : 0.0;
+      static_for<0, TB>([&](auto K) {
+        constexpr int kk = decltype(K)::value;
+        if (kk < e) {
+          const double lkk = rl(Lr[kk], kk), xk = rl(xv, kk);
+          const double t2 = fma(lkk, lkk, xk * xk);
+          const double ri = rsqrt(t2);
+          const double c = lkk * ri, s = xk * ri;
+          if (i == kk) {
+            Lr[kk] = t2 * ri;
+          } else if (i > kk) {
+            const double l = Lr[kk];
+            Lr[kk] = fma(c, l, s * xv);
+            xv = fma(c, xv, -s * l);
+          }
+          if (lane == 0) {
+            bk->cs[2 * kk] = c;
+            bk->cs[2 * kk + 1] = s;
+          }
+        }
+      });
+      if (act) {
+        static_for<0, TB>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          if (j <= i) S.L[rb + j] = Lr[j];
+        });
+      }
+    }
+    __syncthreads();
+    if (k0 + TB < n2) {
+      for (int row = k0 + TB + tid; row < n2; row += NT) {
+        const int rb = tri(row) + k0;
+        double Lr[TB];
+        static_for<0, TB>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          Lr[j] = S.L[rb + j];
+        });
+        double xv = xc[row];
+        static_for<0, TB>([&](auto K) {
+          constexpr int kk = decltype(K)::value;
+          const double c = bk->cs[2 * kk], s = bk->cs[2 * kk + 1];
+          const double l = Lr[kk];
+          Lr[kk] = fma(c, l, s * xv);
+          xv = fma(c, xv, -s * l);
+        });
+        static_for<0, TB>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          S.L[rb + j] = Lr[j];
+        });
+        xc[row] = xv;
+      }
+      __syncthreads();
+    }
+  }
+  if (tid == 0) bk->np = n2;
+  __syncthreads();
+}
+
+// Largest factor position k < np with pred(k) true, -1 if none.
+template <typename P>
+__device__ __forceinline__ int last_position(int np, P pred, Red *red) {
+  int best = -1;
+  for (int k = threadIdx.x; k < np; k += NT)
+    if (pred(k)) best = k;
+  double v;
+  return block_argmax(double(best), best, red, &v);
+}
+
+// Appends the nc <= NB candidates in bk->cand (zero, not blocked) to the free
+// set.  One blocked forward pass over the current factor gives each
+// candidate's row l = L^-1 Gs[P, j] and y = L^-1 g_P; a Cholesky of the block
+// finishes the rows (candidates whose pivot vanishes are blocked).  On return
+// rhs row 0 holds y = L^-1 g_P over the extended free set and bk->ctl[2] the
+// number of accepted candidates.
+__device__ __forceinline__ void block_append(const St &S, const double *G, int64_t ld, int nc, int *status) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  Blk *bk = S.bk;
+  const int np0 = bk->np, mp = S.mp;
+  for (int k = tid; k < np0; k += NT) {
+    const int a = S.plist[k];
+    const double da = S.dg[a];
+    S.rhs[k] = S.g[a];
+    for (int b = 0; b < nc; ++b) {
+      const int j = bk->cand[b];
+      S.rhs[(b + 1) * mp + k] = G[int64_t(j) * ld + a] / (S.dg[j] * da);
+    }
+  }
+  if (tid < nc * nc) {
+    const int j1 = bk->cand[tid / nc], j2 = bk->cand[tid % nc];
+    bk->Gc[(tid / nc) * NB + tid % nc] = G[int64_t(j1) * ld + j2] / (S.dg[j1] * S.dg[j2]);
+  }
+  __syncthreads();
+  if (np0 > 0) fwd_blk(S, np0, nc + 1);
+  // dots[b1][b2] = <rhs_b1, rhs_b2> over the old positions, b2 <= b1 (one wave per pair)
+  const int npair = (nc + 1) * (nc + 2) / 2;
+  for (int pr = wave; pr < npair; pr += NW) {
+    int b1 = 0;
+    while ((b1 + 1) * (b1 + 2) / 2 <= pr) ++b1;
+    const int b2 = pr - b1 * (b1 + 1) / 2;
+    double v = 0.0;
+    for (int k = lane; k < np0; k += 64) v = fma(S.rhs[b1 * mp + k], S.rhs[b2 * mp + k], v);
+    v = wave_sum(v);
+    if (lane == 0) bk->dots[b1 * NRHS + b2] = v;
+  }
+  __syncthreads();
+  // Cholesky of the candidate block in wave 0 (wave-uniform values in registers)
+  if (wave == 0) {
+    double E[NB][NB], Dg[NB], yb[NB];
+    int idx[NB];
+    int nacc = 0;
+    static_for<0, NB>([&](auto A) {
+      constexpr int a = decltype(A)::value;
+      Dg[a] = 1.0;
+      yb[a] = 0.0;
+      idx[a] = 0;
+      static_for<0, NB>([&](auto A2) { E[a][decltype(A2)::value] = 0.0; });
+    });
+    static_for<0, NB>([&](auto Bc) {
+      constexpr int b = decltype(Bc)::value;
+      if (b < nc) {
+        const int j = bk->cand[b];
+        double row[NB];
+        double ss = bk->dots[(b + 1) * NRHS + (b + 1)];
+        double yy = S.g[j] - bk->dots[(b + 1) * NRHS];
+        static_for<0, NB>([&](auto A) {
+          constexpr int a = decltype(A)::value;
+          row[a] = 0.0;
+          if (a < nacc) {
+            const int bb = idx[a];
+            double v = bk->Gc[b * NB + bb] - bk->dots[(b + 1) * NRHS + (bb + 1)];
+            static_for<0, a>([&](auto A2) {
+              constexpr int a2 = decltype(A2)::value;
+              v -= row[a2] * E[a][a2];
+            });
+            v /= Dg[a];
+            row[a] = v;
+            ss += v * v;
+            yy -= v * yb[a];
+          }
+        });
+        const double d2 = bk->Gc[b * NB + b] - ss;
+        if (d2 > PIV_TOL) {
+          const double dd = sqrt(d2);
+          static_for<0, NB>([&](auto A) {
+            constexpr int a = decltype(A)::value;
+            if (a == nacc) {
+              static_for<0, a>([&](auto A2) {
+                constexpr int a2 = decltype(A2)::value;
+                E[a][a2] = row[a2];
+              });
+              Dg[a] = dd;
+              yb[a] = yy / dd;
+              idx[a] = b;
+            }
+          });
+          ++nacc;
+        } else if (lane == 0) {
           S.flag[j] = F_BLOCKED;
           *status |= int(AMC_HS_NNLS_SINGULAR);
         }
-        wsync();
-      }
-    }
-  });
-  // write the accepted rows
-  static_for<0, NB>([&](auto I_b) {
-    constexpr int b = decltype(I_b)::value;
-    if (b >= nc || rank[b] < 0) return;
-    const int pos = np0 + rank[b];
-    const int base = tri(pos);
-    static_for<0, NR>([&](auto I_m) {
-      constexpr int m = decltype(I_m)::value;
-      const int k = lane + 64 * m;
-      if (k < np0) S.L[base + k] = r[b + 1][m];
-    });
-    const int ra = rank[b];
-    for (int a = lane; a < ra; a += 64) S.L[base + np0 + a] = E[ra * NB + a];
-    if (lane == 0) {
-      S.L[base + pos] = Dg[ra];
-      S.rdiag[pos] = 1.0 / Dg[ra];
-      S.plist[pos] = S.cand[b];
-      S.flag[S.cand[b]] |= F_PASSIVE | F_NEW;
-    }
-  });
-  static_for<0, NR>([&](auto I_m) {
-    constexpr int m = decltype(I_m)::value;
-    y[m] = r[0][m];
-  });
-  for (int a = 0; a < nacc; ++a) setv(y, np0 + a, yb[a]);
-  if (lane == 0) *S.np = np0 + nacc;
-  wsync();
-}
-
-// Deletes factor position q: rows below shift up without column q, then the
-// trailing block absorbs the removed column by a rank-one update.
-__device__ __forceinline__ void remove_at(const St &S, int q) {
-  const int lane = lane_id();
-  const int np = *S.np;
-  double x[NR];
-  static_for<0, NR>([&](auto I_m) {
-    constexpr int m = decltype(I_m)::value;
-    x[m] = 0.0;
-  });
-  for (int i = q + 1; i < np; ++i) {
-    double v[NR];
-    static_for<0, NR>([&](auto I_m) {
-      constexpr int m = decltype(I_m)::value;
-      const int c = lane + 64 * m;
-      v[m] = c <= i ? S.L[tri(i) + c] : 0.0;
-    });
-    const double xi = S.L[tri(i) + q];
-    // new row i-1, entry c' = old entry c' (c' < q) or old entry c'+1 (c' >= q)
-    double nv[NR];
-    static_for<0, NR>([&](auto I_m) {
-      constexpr int m = decltype(I_m)::value;
-      const double right_same = __shfl(v[m], (lane + 1) & 63);
-      const double right_next = (m + 1 < NR) ? __shfl(v[m + 1 < NR ? m + 1 : m], 0) : 0.0;
-      const double right = lane == 63 ? right_next : right_same;
-      const int cp = lane + 64 * m;
-      nv[m] = cp < q ? v[m] : right;
-    });
-    wsync();
-    const int nb = tri(i - 1);
-    static_for<0, NR>([&](auto I_m) {
-      constexpr int m = decltype(I_m)::value;
-      const int cp = lane + 64 * m;
-      if (cp <= i - 1) S.L[nb + cp] = nv[m];
-    });
-    setv(x, i - 1, xi);
-    wsync();
-  }
-  int pv[NR];
-  static_for<0, NR>([&](auto I_m) {
-    constexpr int m = decltype(I_m)::value;
-    const int k = lane + 64 * m;
-    pv[m] = (k + 1 < np) ? S.plist[k + 1] : 0;
-  });
-  wsync();
-  static_for<0, NR>([&](auto I_m) {
-    constexpr int m = decltype(I_m)::value;
-    const int k = lane + 64 * m;
-    if (k >= q && k < np - 1) S.plist[k] = pv[m];
-  });
-  if (lane == 0) *S.np = np - 1;
-  wsync();
-  const int n2 = np - 1;
-  // rank-one update: L33' L33'^T = L33 L33^T + x x^T on positions q..n2-1
-  for (int k = q; k < n2; ++k) {
-    const double lkk = S.L[tri(k) + k];
-    const double xk = getv(x, k);
-    const double r = sqrt(lkk * lkk + xk * xk);
-    const double cc = r / lkk, s = xk / lkk;
-    static_for<0, NR>([&](auto I_m) {
-      constexpr int m = decltype(I_m)::value;
-      const int i = lane + 64 * m;
-      if (i > k && i < n2) {
-        const double lik = (S.L[tri(i) + k] + s * x[m]) / cc;
-        S.L[tri(i) + k] = lik;
-        x[m] = cc * x[m] - s * lik;
       }
     });
     if (lane == 0) {
-      S.L[tri(k) + k] = r;
-      S.rdiag[k] = 1.0 / r;
-    }
-    wsync();
-  }
-}
-
-// ---- block routines -------------------------------------------------------
-
-// g_a -= sum_k Gs[a][P_k] delta_k for every variable a < p (G is symmetric, so
-// row P_k of G is read contiguously across the threads).  Eight independent
-// partial sums keep eight loads in flight per thread.
-__device__ __forceinline__ void grad_update(const St &S, const double *G, int64_t ld, int p) {
-  const int np = *S.np;
-  for (int a = threadIdx.x; a < p; a += NT) {
-    double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-    int k = 0;
-    for (; k + 8 <= np; k += 8) {
-      static_for<0, 8>([&](auto I_u) {
-        constexpr int u = decltype(I_u)::value;
-        const int c = S.plist[k + u];
-        acc[u] = fma(G[int64_t(c) * ld + a], S.delta[k + u] / S.dg[c], acc[u]);
+      static_for<0, NB>([&](auto A) {
+        constexpr int a = decltype(A)::value;
+        bk->Dg[a] = Dg[a];
+        bk->yb[a] = yb[a];
+        bk->accb[a] = idx[a];
+        static_for<0, a>([&](auto A2) {
+          constexpr int a2 = decltype(A2)::value;
+          bk->E[a * NB + a2] = E[a][a2];
+        });
       });
+      bk->ctl[2] = nacc;
     }
-    for (; k < np; ++k) {
-      const int c = S.plist[k];
-      acc[0] = fma(G[int64_t(c) * ld + a], S.delta[k] / S.dg[c], acc[0]);
-    }
-    const double s = ((acc[0] + acc[1]) + (acc[2] + acc[3])) + ((acc[4] + acc[5]) + (acc[6] + acc[7]));
-    S.g[a] -= s / S.dg[a];
   }
+  __syncthreads();
+  const int nacc = bk->ctl[2];
+  for (int a = 0; a < nacc; ++a) {
+    const int b = bk->accb[a];
+    const int pos = np0 + a;
+    const int base = tri(pos);
+    for (int k = tid; k < np0; k += NT) S.L[base + k] = S.rhs[(b + 1) * mp + k];
+    if (tid < a) S.L[base + np0 + tid] = bk->E[a * NB + tid];
+    if (tid == 0) {
+      const int j = bk->cand[b];
+      S.L[base + pos] = bk->Dg[a];
+      S.plist[pos] = j;
+      S.flag[j] = F_PASSIVE | F_NEW;
+      S.rhs[pos] = bk->yb[a];
+    }
+  }
+  __syncthreads();
+  if (tid == 0) bk->np = np0 + nacc;
+  __syncthreads();
 }
 
-enum { CTL_DONE = 1, CTL_PARTIAL = 2, CTL_DROP = 3 };
-constexpr unsigned char F_DROP = 8;
-
-// Least squares on the free set in correction form, with feasibility
-// back-tracking, starting from a feasible u whose support is the free set;
-// variables that just entered sit at zero, flagged F_NEW.  have_y: y holds
-// L^-1 g_P already.
+// Least squares on the free set, with feasibility back-tracking, starting
+// from a feasible u whose support is the free set; variables that just
+// entered sit at zero, flagged F_NEW.  have_y: rhs row 0 holds L^-1 g_P.
 //  - An entering variable whose solution is not positive leaves again before
 //    any step is taken.  If it entered alone it is set aside for the rest of
 //    this fit (Lawson and Hanson's guard against cycling on round-off);
 //    otherwise ctl[3] is raised so that later candidates enter one at a time.
 //  - Otherwise the iterate moves toward the solution, as far as feasibility
 //    allows, and the variables that reach zero leave.
-__device__ __forceinline__ void settle(const St &S, const double *G, int64_t ld, int p, double (&y)[NR], bool have_y,
-                                       bool single) {
-  const int tid = threadIdx.x, wave = tid >> 6;
-  for (int guard = 0; guard < 2 * kLdsMaxT + 4; ++guard) {
+__device__ __forceinline__ void settle(const St &S, const double *G, int64_t ld, int p, bool have_y, bool single,
+                                       Red *red) {
+  const int tid = threadIdx.x;
+  Blk *bk = S.bk;
+  const int mp = S.mp;
+  for (int guard = 0; guard < 4 * mp + 8; ++guard) {
     __syncthreads();
-    if (wave == 0) {
-      const int lane = lane_id();
-      const int np = *S.np;
-      double d[1][NR];
-      if (have_y) {
-        static_for<0, NR>([&](auto I_m) {
-          constexpr int m = decltype(I_m)::value;
-          d[0][m] = y[m];
-        });
-      } else {
-        static_for<0, NR>([&](auto I_m) {
-          constexpr int m = decltype(I_m)::value;
-          const int k = lane + 64 * m;
-          d[0][m] = k < np ? S.g[S.plist[k]] : 0.0;
-        });
-        fwd_multi<1>(S, np, d);
-      }
-      bwd(S, np, d[0]);  // d = Gs_PP^-1 g_P: the step to the free-set optimum
-      // entering variables that do not turn positive
-      int ndrop = 0;
-      static_for<0, NR>([&](auto I_m) {
-        constexpr int m = decltype(I_m)::value;
-        const int k = lane + 64 * m;
-        if (k < np) {
-          const int a = S.plist[k];
-          if ((S.flag[a] & F_NEW) && S.u[a] == 0.0 && !(d[0][m] > 0.0)) {
-            S.flag[a] |= F_DROP;
-            ++ndrop;
-          }
-        }
-      });
-      ndrop = int(wave_sum(double(ndrop)));
-      int ctl;
-      if (ndrop > 0) {
-        ctl = CTL_DROP;
-      } else {
-        double best = INFINITY;
-        int kb = -1;
-        static_for<0, NR>([&](auto I_m) {
-          constexpr int m = decltype(I_m)::value;
-          const int k = lane + 64 * m;
-          if (k < np) {
-            const double ua = S.u[S.plist[k]];
-            if (ua + d[0][m] <= 0.0) {
-              const double rt = d[0][m] < 0.0 ? ua / (-d[0][m]) : 0.0;
-              if (kb < 0 || rt < best) {
-                best = rt;
-                kb = k;
-              }
-            }
-          }
-        });
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          const double ob = __shfl_xor(best, off);
-          const int ok = __shfl_xor(kb, off);
-          if (ok >= 0 && (kb < 0 || ob < best || (ob == best && ok < kb))) {
-            best = ob;
-            kb = ok;
-          }
-        }
-        ctl = kb < 0 ? CTL_DONE : CTL_PARTIAL;
-        const double alpha = kb < 0 ? 1.0 : (best < 1.0 ? best : 1.0);
-        static_for<0, NR>([&](auto I_m) {
-          constexpr int m = decltype(I_m)::value;
-          const int k = lane + 64 * m;
-          if (k < np) {
-            const double ua = S.u[S.plist[k]];
-            double un = (k == kb) ? 0.0 : fma(alpha, d[0][m], ua);
-            if (!(un > 0.0)) un = 0.0;
-            S.delta[k] = ctl == CTL_DONE ? d[0][m] : un - ua;
-          }
-        });
-      }
-      if (lane == 0) S.ctl[0] = ctl;
-      wsync();
+    const int np = bk->np;
+    if (np == 0) break;
+    if (!have_y) {
+      for (int k = tid; k < np; k += NT) S.rhs[k] = S.g[S.plist[k]];
+      __syncthreads();
+      fwd_blk(S, np, 1);
     }
     have_y = false;
-    __syncthreads();
-    const int ctl = S.ctl[0];
-    if (ctl == CTL_DROP) {
-      if (wave == 0) {
-        for (int k = *S.np - 1; k >= 0; --k) {
-          const int a = S.plist[k];
-          if (S.flag[a] & F_DROP) {
-            wsync();
-            if (lane_id() == 0) {
-              S.flag[a] = single ? F_BLOCKED : 0;
-              if (!single) S.ctl[3] = 1;
-            }
-            wsync();
-            remove_at(S, k);
-          }
+    bwd_blk(S, np, S.rhs);  // rhs = Gs_PP^-1 g_P: the step to the free-set optimum
+    int ndrop = 0;
+    double best = INFINITY;
+    int kb = -1;
+    for (int k = tid; k < np; k += NT) {
+      const int a = S.plist[k];
+      const double d = S.rhs[k];
+      const double ua = S.u[a];
+      if ((S.flag[a] & F_NEW) && ua == 0.0 && !(d > 0.0)) {
+        S.flag[a] |= F_DROP;
+        ++ndrop;
+      } else if (ua + d <= 0.0) {
+        const double rt = d < 0.0 ? ua / (-d) : 0.0;
+        if (kb < 0 || rt < best) {
+          best = rt;
+          kb = k;
         }
+      }
+    }
+    ndrop = block_count(ndrop, red);
+    if (ndrop > 0) {
+      for (;;) {
+        const int q = last_position(bk->np, [&](int k) { return (S.flag[S.plist[k]] & F_DROP) != 0; }, red);
+        if (q < 0) break;
+        if (tid == 0) {
+          S.flag[S.plist[q]] = single ? F_BLOCKED : 0;
+          if (!single) bk->ctl[3] = 1;
+        }
+        __syncthreads();
+        remove_at(S, q);
       }
       continue;
     }
-    grad_update(S, G, ld, p);
-    const int np = *S.np;
+    double nbest;
+    kb = block_argmax(kb >= 0 ? -best : -INFINITY, kb, red, &nbest);
+    best = -nbest;
+    const bool done = kb < 0;
+    const double alpha = done ? 1.0 : (best < 1.0 ? best : 1.0);
+    double *delta = S.rhs + mp, *dsc = S.rhs + 2 * mp;
     for (int k = tid; k < np; k += NT) {
       const int a = S.plist[k];
-      const double un = S.u[a] + S.delta[k];
-      S.u[a] = un > 0.0 ? un : 0.0;
+      const double ua = S.u[a];
+      const double d = S.rhs[k];
+      double un = (k == kb) ? 0.0 : fma(alpha, d, ua);
+      if (!(un > 0.0)) un = 0.0;
+      const double dl = done ? d : un - ua;
+      delta[k] = dl;
+      dsc[k] = dl / S.dg[a];
     }
     __syncthreads();
-    if (wave == 0) {
-      if (ctl == CTL_PARTIAL) {
-        // every free variable that reached zero leaves (highest position first)
-        for (int k = *S.np - 1; k >= 0; --k) {
-          const int a = S.plist[k];
-          if (!(S.u[a] > 0.0)) {
-            wsync();
-            if (lane_id() == 0) {
-              S.u[a] = 0.0;
-              S.flag[a] &= ~(F_PASSIVE | F_NEW);
-            }
-            wsync();
-            remove_at(S, k);
-          }
-        }
-      }
-      for (int k = lane_id(); k < *S.np; k += 64) S.flag[S.plist[k]] &= ~F_NEW;
-      wsync();
+    grad_update(S, G, ld, p, done ? 0.0 : 1.0 - alpha);
+    for (int k = tid; k < np; k += NT) {
+      const int a = S.plist[k];
+      const double un = S.u[a] + delta[k];
+      S.u[a] = un > 0.0 ? un : 0.0;
+      S.flag[a] &= ~F_NEW;
     }
-    if (ctl == CTL_DONE) break;
+    __syncthreads();
+    if (done) break;
+    // every free variable that reached zero leaves (highest position first)
+    for (;;) {
+      const int q = last_position(bk->np, [&](int k) { return !(S.u[S.plist[k]] > 0.0); }, red);
+      if (q < 0) break;
+      if (tid == 0) {
+        const int a = S.plist[q];
+        S.u[a] = 0.0;
+        S.flag[a] &= ~(F_PASSIVE | F_NEW);
+      }
+      __syncthreads();
+      remove_at(S, q);
+    }
   }
   __syncthreads();
 }
 
-// Top-NB zero variables by gradient above tol (wave 0); returns the count.
-__device__ __forceinline__ int pick_candidates(const St &S, int p, double tol, int maxc) {
-  const int lane = lane_id();
-  double v[NR];
-  static_for<0, NR>([&](auto I_m) {
-    constexpr int m = decltype(I_m)::value;
-    const int a = lane + 64 * m;
-    v[m] = (a < p && !(S.flag[a] & (F_PASSIVE | F_BLOCKED)) && S.g[a] > tol) ? S.g[a] : -INFINITY;
-  });
+// Up to maxc zero variables with the largest gradients above tol (ties to the
+// lower index) go to bk->cand; returns their count.
+__device__ __forceinline__ int pick_candidates(const St &S, int p, double tol, int maxc, Red *red) {
   int nc = 0;
-  for (int b = 0; b < maxc; ++b) {
+  for (; nc < maxc; ++nc) {
     double bv = -INFINITY;
     int bi = -1;
-    static_for<0, NR>([&](auto I_m) {
-      constexpr int m = decltype(I_m)::value;
-      const int a = lane + 64 * m;
-      if (v[m] > bv || (v[m] == bv && bi >= 0 && a < bi && v[m] > -INFINITY)) {
-        if (v[m] > -INFINITY) {
-          bv = v[m];
+    for (int a = threadIdx.x; a < p; a += NT) {
+      if (!(S.flag[a] & (F_PASSIVE | F_BLOCKED | F_CAND))) {
+        const double v = S.g[a];
+        if (v > tol && (bi < 0 || v > bv)) {
+          bv = v;
           bi = a;
         }
       }
-    });
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const double ov = __shfl_xor(bv, off);
-      const int oi = __shfl_xor(bi, off);
-      if (oi >= 0 && (bi < 0 || ov > bv || (ov == bv && oi < bi))) {
-        bv = ov;
-        bi = oi;
-      }
     }
+    double v;
+    bi = block_argmax(bv, bi, red, &v);
     if (bi < 0) break;
-    if (lane == 0) S.cand[nc] = bi;
-    static_for<0, NR>([&](auto I_m) {
-      constexpr int m = decltype(I_m)::value;
-      if (lane + 64 * m == bi) v[m] = -INFINITY;
-    });
-    ++nc;
+    if (threadIdx.x == 0) {
+      S.bk->cand[nc] = bi;
+      S.flag[bi] |= F_CAND;
+    }
+    __syncthreads();
   }
-  wsync();
   return nc;
 }
 
-// One block solves one system.
-//   gA     : accurate unscaled gradient b - G w at the warm start (nullable:
-//            then it is formed from G and b)
-//   np_in, plist_in, L_in : persisted free set and factor (np_in = 0: none)
-//   pg     : projected-gradient warm-up iterations (stand-alone solver only)
-__device__ __forceinline__ void nnls_solve(const double *G, int64_t ld, int p, const double *b, const double *gA,
-                                           double *w, int nwarm, const NnlsParams prm, char *smem, int maxp,
-                                           int np_in, const int32_t *plist_in, const double *L_in, int pg,
-                                           int *iters_out, int *status_out) {
-  __shared__ Red red;
-  __shared__ int sh_status;
-  const int tid = threadIdx.x, wave = tid >> 6;
-  St S = carve(smem, maxp);
-  if (tid == 0) {
-    sh_status = 0;
-    *S.np = np_in;
-    S.ctl[3] = 0;
+// One block solves one system on the state S (u, g, dg, flag set up by
+// nnls_setup for a < p; L, plist and bk->np hold the starting free set).
+//   tol, cap : KKT tolerance on the scaled gradient and outer-iteration cap
+//   support  : the positive entries of u enter the free set first (warm
+//              start of the stand-alone solver)
+__device__ __forceinline__ void nnls_core(const St &S, const double *G, int64_t ld, int p, double tol, int cap,
+                                          bool support, Red *red, int *status, int *iters_out) {
+  const int tid = threadIdx.x;
+  Blk *bk = S.bk;
+  int iters = 0;
+  if (support) {
+    // the support of the warm start becomes the free set, NB variables at a time
+    int a0 = 0;
+    for (;;) {
+      __syncthreads();
+      if (tid == 0) {
+        int nc = 0;
+        for (; a0 < p && nc < NB; ++a0)
+          if (S.u[a0] > 0.0 && !(S.flag[a0] & (F_PASSIVE | F_BLOCKED))) bk->cand[nc++] = a0;
+        bk->ctl[1] = nc;
+        bk->ctl[4] = a0;
+      }
+      __syncthreads();
+      const int nc = bk->ctl[1];
+      a0 = bk->ctl[4];
+      if (nc == 0) break;
+      block_append(S, G, ld, nc, status);
+    }
+    for (int k = tid; k < bk->np; k += NT) S.flag[S.plist[k]] &= ~F_NEW;
+    // a dependent variable dropped here still carries weight: take it out of u and g
+    double *tmp = S.rhs + 2 * S.mp;
+    for (int a = tid; a < p; a += NT) tmp[a] = ((S.flag[a] & F_BLOCKED) && S.u[a] > 0.0) ? -S.u[a] : 0.0;
+    __syncthreads();
+    for (int a = tid; a < p; a += NT) {
+      double acc = 0.0;
+      for (int c = 0; c < p; ++c)
+        if (tmp[c] != 0.0) acc = fma(G[int64_t(c) * ld + a], tmp[c] / S.dg[c], acc);
+      S.g[a] -= acc / S.dg[a];
+    }
+    __syncthreads();
+    for (int a = tid; a < p; a += NT)
+      if (S.flag[a] & F_BLOCKED) S.u[a] = 0.0;
   }
+  // refine the starting free set with the gradient given
+  settle(S, G, ld, p, false, false, red);
+  for (;;) {
+    const int nc = pick_candidates(S, p, tol, bk->ctl[3] ? 1 : NB, red);
+    if (nc == 0) break;
+    if (iters >= cap) {
+      if (tid == 0) *status |= int(AMC_HS_NNLS_CAP);
+      break;
+    }
+    ++iters;
+    block_append(S, G, ld, nc, status);
+    if (bk->ctl[2] > 0) settle(S, G, ld, p, true, nc == 1, red);
+  }
+  __syncthreads();
+  *iters_out = iters;
+}
+
+// Sets up u, g, dg, flag for a < p from G, b, the warm start (first nwarm
+// entries of w) and the accurate gradient gA (nullable: formed from G and
+// b), and marks the starting free set.  Returns the KKT tolerance, 0 when
+// there is nothing to fit.
+__device__ __forceinline__ double nnls_setup(const St &S, const double *G, int64_t ld, int p, const double *b,
+                                             const double *gA, const double *w, int nwarm, const NnlsParams &prm,
+                                             Red *red) {
+  const int tid = threadIdx.x;
   double bl = 0.0;
   for (int a = tid; a < p; a += NT) {
     const double gaa = G[int64_t(a) * ld + a];
@@ -716,149 +851,76 @@ __device__ __forceinline__ void nnls_solve(const double *G, int64_t ld, int p, c
       f = F_BLOCKED;
     }
     S.dg[a] = dg;
-    const double bs = f ? 0.0 : b[a] / dg;
-    S.bs[a] = bs;
     const double u0 = (a < nwarm && !f) ? fmax(w[a], 0.0) * dg : 0.0;
     S.u[a] = u0 > 0.0 ? u0 : 0.0;
     S.flag[a] = f;
-    bl = fmax(bl, fabs(bs));
-  }
-  for (int e = tid; e < tri(np_in); e += NT) S.L[e] = L_in[e];
-  __syncthreads();
-  for (int k = tid; k < np_in; k += NT) {
-    const int a = plist_in[k];
-    S.plist[k] = a;
-    S.flag[a] |= F_PASSIVE;
-    S.rdiag[k] = 1.0 / S.L[tri(k) + k];
+    bl = fmax(bl, f ? 0.0 : fabs(b[a] / dg));
   }
   __syncthreads();
-  // initial gradient
+  for (int k = tid; k < S.bk->np; k += NT) S.flag[S.plist[k]] |= F_PASSIVE;
   if (gA) {
     for (int a = tid; a < p; a += NT) S.g[a] = (S.flag[a] & F_BLOCKED) ? 0.0 : gA[a] / S.dg[a];
   } else {
     for (int a = tid; a < p; a += NT) {
       double acc = 0.0;
       for (int c = 0; c < p; ++c) acc = fma(G[int64_t(c) * ld + a], S.u[c] / S.dg[c], acc);
-      S.g[a] = S.bs[a] - acc / S.dg[a];
+      S.g[a] = (S.flag[a] & F_BLOCKED) ? 0.0 : b[a] / S.dg[a] - acc / S.dg[a];
     }
   }
   double bmax;
-  (void)block_argmax(bl, 0, &red, &bmax);
-  const double tol = (prm.tol > 0.0 ? prm.tol : 10.0 * DBL_EPSILON * double(p)) * bmax;
-  const int cap = prm.max_iters > 0 ? prm.max_iters : 3 * p + 30;
-  int iters = 0;
-  double y[NR];
-  static_for<0, NR>([&](auto I_m) {
-    constexpr int m = decltype(I_m)::value;
-    y[m] = 0.0;
-  });
+  (void)block_argmax(bl, 0, red, &bmax);
+  if (!(bmax > 0.0) || !isfinite(bmax)) return 0.0;
+  return (prm.tol > 0.0 ? prm.tol : 10.0 * DBL_EPSILON * double(p)) * bmax;
+}
 
-  if (bmax > 0.0 && isfinite(bmax)) {
-    if (pg > 0) {
-      // projected-gradient warm-up (step 1/L, L a Gershgorin bound of Gs)
-      double rowmax = 0.0;
-      for (int a = tid; a < p; a += NT) {
-        double acc = 0.0;
-        for (int c = 0; c < p; ++c) acc += fabs(G[int64_t(c) * ld + a]) / S.dg[c];
-        if (!(S.flag[a] & F_BLOCKED)) rowmax = fmax(rowmax, acc / S.dg[a]);
-      }
-      double Lmax;
-      (void)block_argmax(rowmax, 0, &red, &Lmax);
-      const double step = Lmax > 0.0 ? 1.0 / Lmax : 0.0;
-      for (int it = 0; it < pg; ++it) {
-        __syncthreads();
-        for (int a = tid; a < p; a += NT)
-          S.delta[a] = (S.flag[a] & F_BLOCKED) ? 0.0 : fmax(0.0, S.u[a] + step * S.g[a]) - S.u[a];
-        __syncthreads();
-        for (int a = tid; a < p; a += NT) {
-          double acc = 0.0;
-          for (int c = 0; c < p; ++c) acc = fma(G[int64_t(c) * ld + a], S.delta[c] / S.dg[c], acc);
-          S.g[a] -= acc / S.dg[a];
-        }
-        __syncthreads();
-        for (int a = tid; a < p; a += NT) S.u[a] += S.delta[a];
-      }
-      __syncthreads();
+// Projected-gradient warm-up (step 1/L, L a Gershgorin bound of Gs).
+__device__ __forceinline__ void pg_warmup(const St &S, const double *G, int64_t ld, int p, int iters, Red *red) {
+  const int tid = threadIdx.x;
+  double *tmp = S.rhs + 2 * S.mp;
+  double rowmax = 0.0;
+  for (int a = tid; a < p; a += NT) {
+    double acc = 0.0;
+    for (int c = 0; c < p; ++c) acc += fabs(G[int64_t(c) * ld + a]) / S.dg[c];
+    if (!(S.flag[a] & F_BLOCKED)) rowmax = fmax(rowmax, acc / S.dg[a]);
+  }
+  double Lmax;
+  (void)block_argmax(rowmax, 0, red, &Lmax);
+  const double step = Lmax > 0.0 ? 1.0 / Lmax : 0.0;
+  for (int it = 0; it < iters; ++it) {
+    __syncthreads();
+    for (int a = tid; a < p; a += NT)
+      tmp[a] = (S.flag[a] & F_BLOCKED) ? 0.0 : fmax(0.0, S.u[a] + step * S.g[a]) - S.u[a];
+    __syncthreads();
+    for (int a = tid; a < p; a += NT) {
+      double acc = 0.0;
+      for (int c = 0; c < p; ++c) acc = fma(G[int64_t(c) * ld + a], tmp[c] / S.dg[c], acc);
+      S.g[a] -= acc / S.dg[a];
     }
-    if (np_in == 0) {
-      // the support of the warm start becomes the free set, NB variables at a time
-      if (wave == 0) {
-        int a0 = 0;
-        for (;;) {
-          int nc = 0;
-          for (; a0 < p && nc < NB; ++a0)
-            if (S.u[a0] > 0.0 && !(S.flag[a0] & (F_PASSIVE | F_BLOCKED))) {
-              if (lane_id() == 0) S.cand[nc] = a0;
-              ++nc;
-            }
-          wsync();
-          if (nc == 0) break;
-          block_append(S, G, ld, nc, y, &sh_status);
-        }
-        for (int k = lane_id(); k < *S.np; k += 64) S.flag[S.plist[k]] &= ~F_NEW;
-        wsync();
-      }
-      __syncthreads();
-      // a dependent variable dropped here still carries weight: take it out of u and g
-      for (int a = tid; a < p; a += NT) S.delta[a] = ((S.flag[a] & F_BLOCKED) && S.u[a] > 0.0) ? -S.u[a] : 0.0;
-      __syncthreads();
-      for (int a = tid; a < p; a += NT) {
-        double acc = 0.0;
-        for (int c = 0; c < p; ++c)
-          if (S.delta[c] != 0.0) acc = fma(G[int64_t(c) * ld + a], S.delta[c] / S.dg[c], acc);
-        S.g[a] -= acc / S.dg[a];
-      }
-      __syncthreads();
-      for (int a = tid; a < p; a += NT)
-        if (S.flag[a] & F_BLOCKED) S.u[a] = 0.0;
-      __syncthreads();
-      if (*S.np > 0) settle(S, G, ld, p, y, false, false);
-    } else {
-      settle(S, G, ld, p, y, false, false);  // refine the persisted optimum with the accurate gradient
-    }
-    for (;;) {
-      __syncthreads();
-      if (wave == 0) {
-        const int nc = pick_candidates(S, p, tol, S.ctl[3] ? 1 : NB);
-        if (lane_id() == 0) S.ctl[1] = nc;
-        wsync();
-      }
-      __syncthreads();
-      const int nc = S.ctl[1];
-      if (nc == 0) break;
-      if (iters >= cap) {
-        if (tid == 0) sh_status |= int(AMC_HS_NNLS_CAP);
-        break;
-      }
-      ++iters;
-      if (wave == 0) {
-        block_append(S, G, ld, nc, y, &sh_status);
-        if (lane_id() == 0) S.ctl[2] = *S.np;
-        wsync();
-      }
-      __syncthreads();
-      if (S.ctl[2] > 0) settle(S, G, ld, p, y, true, nc == 1);
-    }
+    __syncthreads();
+    for (int a = tid; a < p; a += NT) S.u[a] += tmp[a];
   }
   __syncthreads();
-  for (int a = tid; a < p; a += NT) w[a] = S.u[a] / S.dg[a];
-  if (tid == 0) {
-    *iters_out = iters;
-    *status_out = sh_status;
-  }
 }
 
 // One refit per head.  polish: no new key; refine the last fit (p = t).
+// kGlobal: the state lives in the workspace (budgets above kNnlsLdsT); else
+// in LDS.  Each variant skips the heads of the other.
+template <bool kGlobal>
 __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ desc, const double *__restrict__ G,
                                                    const double *__restrict__ bvec, const double *__restrict__ gA,
                                                    double *__restrict__ w, int cycle, int kR, int polish,
                                                    NnlsParams prm, int maxp, double *__restrict__ nn_L,
                                                    int32_t *__restrict__ nn_P, int32_t *__restrict__ nn_np,
-                                                   int32_t *__restrict__ tr_iters, double *__restrict__ tr_weight,
+                                                   double *__restrict__ nn_vec, int32_t *__restrict__ tr_iters,
+                                                   double *__restrict__ tr_weight,
                                                    int32_t *__restrict__ head_status) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ Blk bk;
+  __shared__ Red red;
+  __shared__ int sh_status;
   const int h = blockIdx.x;
   const HeadDesc D = desc[h];
+  if ((D.t > kNnlsLdsT) != kGlobal) return;
   int64_t S0;
   int Kc;
   if (polish) {
@@ -869,23 +931,58 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
     if (S0 >= D.t) return;
     Kc = int(D.t - S0 < kR ? D.t - S0 : kR);
   }
+  const int tid = threadIdx.x;
   const int p = int(S0) + Kc;
   const int np_in = S0 == 0 ? 0 : nn_np[h];
-  int iters = 0, status = 0;
-  nnls_solve(G + D.tt_off, D.t, p, bvec + D.t_off, gA + D.t_off, w + D.t_off, int(S0), prm, smem, maxp, np_in,
-             nn_P + D.t_off, nn_L + D.tri_off, 0, &iters, &status);
-  St S = carve(smem, maxp);
+  double *Lg = nn_L + D.tri_off;
+  int32_t *Pg = nn_P + D.t_off;
+  const St S = kGlobal ? carve_global(nn_vec + D.t_off * kNnlsVecPerSlot, Lg, Pg, int(D.t), &bk)
+                       : carve_lds(smem, maxp, &bk);
+  if (tid == 0) {
+    sh_status = 0;
+    bk.np = np_in;
+    bk.ctl[3] = 0;
+  }
+  if (!kGlobal) {
+    // bring the persisted factor into LDS, eight loads in flight per thread
+    const int ne = tri(np_in);
+    for (int e0 = 0; e0 < ne; e0 += 8 * NT) {
+      double v[8];
+      static_for<0, 8>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        const int e = e0 + u * NT + tid;
+        v[u] = e < ne ? Lg[e] : 0.0;
+      });
+      static_for<0, 8>([&](auto U) {
+        constexpr int u = decltype(U)::value;
+        const int e = e0 + u * NT + tid;
+        if (e < ne) S.L[e] = v[u];
+      });
+    }
+    for (int k = tid; k < np_in; k += NT) S.plist[k] = Pg[k];
+  }
   __syncthreads();
-  const int np = *S.np;
-  for (int e = threadIdx.x; e < tri(np); e += NT) nn_L[D.tri_off + e] = S.L[e];
-  for (int k = threadIdx.x; k < np; k += NT) nn_P[D.t_off + k] = S.plist[k];
-  if (threadIdx.x == 0) {
+  const double tol = nnls_setup(S, G + D.tt_off, D.t, p, bvec + D.t_off, gA + D.t_off, w + D.t_off, int(S0), prm,
+                                &red);
+  int iters = 0;
+  if (tol > 0.0) {
+    const int cap = prm.max_iters > 0 ? prm.max_iters : 3 * p + 30;
+    nnls_core(S, G + D.tt_off, D.t, p, tol, cap, false, &red, &sh_status, &iters);
+  }
+  __syncthreads();
+  for (int a = tid; a < p; a += NT) w[D.t_off + a] = S.u[a] / S.dg[a];
+  const int np = bk.np;
+  if (!kGlobal) {
+    for (int e = tid; e < tri(np); e += NT) Lg[e] = S.L[e];
+    for (int k = tid; k < np; k += NT) Pg[k] = S.plist[k];
+  }
+  if (tid == 0) {
     nn_np[h] = np;
     if (tr_iters && !polish) tr_iters[D.cyc_off + cycle] = iters;
-    if (status && head_status) atomicOr(head_status + h, status);
+    if (sh_status && head_status) atomicOr(head_status + h, sh_status);
   }
   if (tr_weight)
-    for (int a = threadIdx.x; a < p; a += NT) tr_weight[D.t_off + a] = w[D.t_off + a];
+    for (int a = tid; a < p; a += NT) tr_weight[D.t_off + a] = S.u[a] / S.dg[a];
 }
 
 struct NnlsChunk {
@@ -899,16 +996,33 @@ __global__ __launch_bounds__(NT) void k_nnls_batched(NnlsChunk ch, int base, con
                                                      NnlsParams prm, int maxp, int32_t *__restrict__ iters,
                                                      int32_t *__restrict__ status) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
+  __shared__ Blk bk;
+  __shared__ Red red;
+  __shared__ int sh_status;
   const int i = blockIdx.x;
   if (i >= ch.count) return;
   const int64_t t0 = ch.cu_t[i];
   const int p = int(ch.cu_t[i + 1] - t0);
-  int it = 0, st = 0;
-  nnls_solve(G + ch.cu_t2[i], p, p, g + t0, nullptr, w + t0, warm ? p : 0, prm, smem, maxp, 0, nullptr, nullptr,
-             prm.pg_iters, &it, &st);
+  const double *Gi = G + ch.cu_t2[i];
+  const St S = carve_lds(smem, maxp, &bk);
+  if (threadIdx.x == 0) {
+    sh_status = 0;
+    bk.np = 0;
+    bk.ctl[3] = 0;
+  }
+  __syncthreads();
+  const double tol = nnls_setup(S, Gi, p, p, g + t0, nullptr, w + t0, warm ? p : 0, prm, &red);
+  int it = 0;
+  if (tol > 0.0) {
+    if (prm.pg_iters > 0) pg_warmup(S, Gi, p, p, prm.pg_iters, &red);
+    const int cap = prm.max_iters > 0 ? prm.max_iters : 3 * p + 30;
+    nnls_core(S, Gi, p, p, tol, cap, true, &red, &sh_status, &it);
+  }
+  __syncthreads();
+  for (int a = threadIdx.x; a < p; a += NT) w[t0 + a] = S.u[a] / S.dg[a];
   if (threadIdx.x == 0) {
     if (iters) iters[base + i] = it;
-    if (status) status[base + i] = st;
+    if (status) status[base + i] = sh_status;
   }
 }
 
@@ -916,14 +1030,25 @@ __global__ __launch_bounds__(NT) void k_nnls_batched(NnlsChunk ch, int base, con
 
 hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int kR, int polish, const NnlsParams &np,
                        hipStream_t s) {
-  const int maxp = int(dm.max_t);
-  const size_t bytes = nnls_smem_bytes(maxp);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_nnls_cycle),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_nnls_cycle, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.bvec, b.gA, b.w, cycle,
-                     kR, polish, np, maxp, b.nn_L, b.nn_P, b.nn_np, b.tr_iters, b.tr_weight, b.head_status);
-  return hipGetLastError();
+  if (dm.min_t <= kNnlsLdsT) {
+    const int maxp = int(dm.max_t < kNnlsLdsT ? dm.max_t : kNnlsLdsT);
+    const size_t bytes = nnls_smem_bytes(maxp);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_nnls_cycle<false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_nnls_cycle<false>, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.bvec, b.gA,
+                       b.w, cycle, kR, polish, np, maxp, b.nn_L, b.nn_P, b.nn_np, b.nn_vec, b.tr_iters, b.tr_weight,
+                       b.head_status);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (dm.max_t > kNnlsLdsT) {
+    hipLaunchKernelGGL(k_nnls_cycle<true>, dim3(unsigned(dm.H)), dim3(NT), 0, s, b.desc, b.G, b.bvec, b.gA, b.w,
+                       cycle, kR, polish, np, 0, b.nn_L, b.nn_P, b.nn_np, b.nn_vec, b.tr_iters, b.tr_weight,
+                       b.head_status);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_nnls_batched(int num, const int64_t *h_cu_t, const int64_t *h_cu_t2, int64_t max_t,

@@ -200,7 +200,7 @@ amc_status amc_mass_features_workspace(const amc_problem *p, uint64_t *bytes);
  *   iters  int32[num] nullable: active-set iterations used
  *   status int32[num] nullable: AMC_HS_NNLS_* bits
  * cu_t (HOST int64[num+1]) gives the sizes; cu_t2 is derived (sum of t_b^2).
- * t_b <= 192 in this build (else AMC_ERR_UNSUPPORTED). */
+ * t_b <= 176 in this build (else AMC_ERR_UNSUPPORTED). */
 amc_status amc_nnls(int32_t num, const int64_t *cu_t, const double *G, const double *g, double *w,
                     int32_t warm, int32_t pg_iters, int32_t max_iters, double tol, int32_t *iters,
                     int32_t *status, void *stream);

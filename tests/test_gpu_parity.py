@@ -70,7 +70,7 @@ def _phi_like(rng, n, t, spread):
 def test_nnls_against_oracle(pg_iters):
     rng = np.random.default_rng(5)
     Gs, bs, As, ys = [], [], [], []
-    for t in (1, 2, 5, 17, 40, 64, 100, 164, 192):
+    for t in (1, 2, 5, 17, 40, 64, 100, 164, 176):
         A = _phi_like(rng, 400, t, 5.0)
         y = A @ (np.abs(rng.normal(size=t)) * (rng.random(t) > 0.3)) + 0.05 * rng.normal(size=400) * A.mean()
         As.append(A)
