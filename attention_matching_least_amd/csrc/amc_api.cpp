@@ -136,7 +136,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     D.cyc_off = cyc;
     D.tri_off = tri;
     if (!features_only) {
-      if (D.t > kLdsMaxT) return AMC_ERR_UNSUPPORTED;  // large-budget solver not in this build
+      if (D.t > kMaxBudget) return AMC_ERR_UNSUPPORTED;
       if (D.n_cblk > kMaxSweepBlocks) return AMC_ERR_UNSUPPORTED;
     }
     const int64_t cycles = ceil_div(D.t, pl.kR);

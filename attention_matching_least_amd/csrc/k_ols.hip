@@ -113,6 +113,7 @@ __global__ __launch_bounds__(NT) void k_ols_factor(const HeadDesc *__restrict__ 
   __shared__ int sh_f, sh_fail;
   const int h = blockIdx.x;
   const HeadDesc Dh = desc[h];
+  if (Dh.t > kLdsMaxT) return;  // k_ols_factor_g
   const int t = int(Dh.t);
   const int tid = threadIdx.x;
   if (tid == 0) {
@@ -188,6 +189,7 @@ __global__ __launch_bounds__(NT) void k_ols_trsm(const HeadDesc *__restrict__ de
   extern __shared__ __attribute__((aligned(16))) double sm[];
   const int h = blockIdx.y;
   const HeadDesc Dh = desc[h];
+  if (Dh.t > kLdsMaxT) return;  // k_ols_trsm_g
   const int t = int(Dh.t);
   const int c0 = blockIdx.x * NC;
   const int f = fcount[h];
@@ -247,17 +249,17 @@ __global__ __launch_bounds__(NT) void k_pack(const HeadDesc *__restrict__ desc, 
                                              const float *__restrict__ beta_in, const void *__restrict__ Kv,
                                              const float *__restrict__ cv_sel, void *__restrict__ Ckv,
                                              float *__restrict__ beta, void *__restrict__ Cvv, int cv_bf16,
-                                             int32_t *__restrict__ sel_idx) {
+                                             int32_t *__restrict__ sel_idx, int32_t *__restrict__ pos_of_slot) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   __shared__ int cnt[NT];
-  __shared__ int spos[kLdsMaxT];
   const int h = blockIdx.x;
   const HeadDesc Dh = desc[h];
   const int tid = threadIdx.x;
   const int64_t T = Dh.T;
   const int64_t chunk = (T + NT - 1) / NT;
   const int64_t j0 = tid * chunk, j1 = (j0 + chunk < T) ? j0 + chunk : T;
-  for (int a = tid; a < kLdsMaxT; a += NT) spos[a] = -1;
+  int32_t *spos = pos_of_slot + Dh.t_off;
+  for (int64_t a = tid; a < Dh.t; a += NT) spos[a] = -1;
   int c = 0;
   for (int64_t j = j0; j < j1; ++j) c += sel_slot[Dh.k_off + j] != 0;
   cnt[tid] = c;
@@ -301,6 +303,318 @@ __global__ __launch_bounds__(NT) void k_pack(const HeadDesc *__restrict__ desc, 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Budgets above kLdsMaxT: the same value fit with the factor in global memory.
+// ---------------------------------------------------------------------------
+constexpr int TBO = 16;  // panel width of the blocked factorisation and solves
+
+template <int B, int E, typename F>
+__device__ __forceinline__ void static_for(F &&f) {
+  if constexpr (B < E) {
+    f(std::integral_constant<int, B>{});
+    static_for<B + 1, E>(f);
+  }
+}
+
+__device__ __forceinline__ double rl(double x, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
+  return __hiloint2double(hi, lo);
+}
+
+// F = {a : w_a > 0} ascending, its size, and the diagonal scaling of N_FF.
+__global__ __launch_bounds__(NT) void k_ols_flist_g(const HeadDesc *__restrict__ desc, const double *__restrict__ N,
+                                                    const double *__restrict__ w, int32_t *__restrict__ flist,
+                                                    int32_t *__restrict__ fcount, double *__restrict__ dn) {
+  __shared__ int wcnt[NT / 64];
+  const int h = blockIdx.x;
+  const HeadDesc Dh = desc[h];
+  if (Dh.t <= kLdsMaxT) return;
+  const int t = int(Dh.t);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t *fl = flist + Dh.t_off;
+  int base = 0;
+  for (int a0 = 0; a0 < t; a0 += NT) {
+    const int a = a0 + tid;
+    const bool pred = a < t && w[Dh.t_off + a] > 0.0;
+    const unsigned long long bal = __ballot(pred);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) wcnt[wave] = __popcll(bal);
+    __syncthreads();
+    int off = base;
+    for (int v = 0; v < wave; ++v) off += wcnt[v];
+    if (pred) fl[off + before] = a;
+    for (int v = 0; v < NT / 64; ++v) base += wcnt[v];
+    __syncthreads();
+  }
+  for (int k = tid; k < base; k += NT) {
+    const int a = fl[k];
+    const double v = N[Dh.tt_off + int64_t(a) * t + a];
+    dn[Dh.t_off + k] = (v > 0.0 && isfinite(v)) ? sqrt(v) : 1.0;
+  }
+  if (tid == 0) fcount[h] = base;
+}
+
+// Blocked right-looking Cholesky of the scaled N_FF in the packed factor
+// storage: per panel of 16 columns, wave 0 factors the diagonal block in
+// registers, every thread then solves one row of the panel below it, and the
+// trailing triangle takes the panel's rank-16 update in 4 x 4 tiles.
+__global__ __launch_bounds__(NT) void k_ols_factor_g(const HeadDesc *__restrict__ desc, const double *__restrict__ N,
+                                                     const int32_t *__restrict__ flist,
+                                                     const int32_t *__restrict__ fcount, const double *__restrict__ dn,
+                                                     double *__restrict__ L, int32_t *__restrict__ head_status) {
+  __shared__ double Db[TBO * TBO];
+  __shared__ int sh_fail;
+  const int h = blockIdx.x;
+  const HeadDesc Dh = desc[h];
+  if (Dh.t <= kLdsMaxT) return;
+  const int t = int(Dh.t);
+  const int f = fcount[h];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t *fl = flist + Dh.t_off;
+  const double *dnh = dn + Dh.t_off;
+  const double *Nh = N + Dh.tt_off;
+  double *Lh = L + Dh.tri_off;
+  double jitter = 0.0;
+  for (int attempt = 0; attempt < 6; ++attempt) {
+    for (int e = tid; e < tri(f); e += NT) {
+      int r, c;
+      decode_tri(e, &r, &c);
+      double v = Nh[int64_t(fl[r]) * t + fl[c]] / (dnh[r] * dnh[c]);
+      if (r == c) v += jitter;
+      Lh[e] = v;
+    }
+    if (tid == 0) sh_fail = -1;
+    __syncthreads();
+    for (int k0 = 0; k0 < f; k0 += TBO) {
+      const int e = f - k0 < TBO ? f - k0 : TBO;
+      if (wave == 0 && lane < TBO) {
+        const int i = lane;
+        const bool act = i < e;
+        const int rb = act ? tri(k0 + i) + k0 : 0;
+        double Lr[TBO];
+        static_for<0, TBO>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          Lr[j] = (act && j <= i) ? Lh[rb + j] : 0.0;
+        });
+        bool bad = false;
+        static_for<0, TBO>([&](auto K) {
+          constexpr int kk = decltype(K)::value;
+          if (kk < e) {
+            const double piv = rl(Lr[kk], kk);
+            if (!(piv > 1e-15)) bad = true;
+            const double d = sqrt(piv > 1e-15 ? piv : 1.0);
+            const double rdd = 1.0 / d;
+            if (i == kk) Lr[kk] = d;
+            else if (i > kk) Lr[kk] *= rdd;
+            static_for<kk + 1, TBO>([&](auto J) {
+              constexpr int j = decltype(J)::value;
+              if (j < e) {
+                const double ljk = rl(Lr[kk], j);
+                if (i >= j) Lr[j] = fma(-Lr[kk], ljk, Lr[j]);
+              }
+            });
+          }
+        });
+        if (act) {
+          static_for<0, TBO>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            if (j <= i) {
+              Lh[rb + j] = Lr[j];
+              Db[i * TBO + j] = Lr[j];
+            }
+          });
+        }
+        if (bad && lane == 0) sh_fail = k0;
+      }
+      __syncthreads();
+      if (sh_fail >= 0) break;
+      if (k0 + TBO >= f) continue;
+      // panel rows below the block: L[r, k0:k0+16] = A[r, k0:k0+16] L_blk^-T
+      for (int r = k0 + TBO + tid; r < f; r += NT) {
+        const int rb = tri(r) + k0;
+        double x[TBO];
+        static_for<0, TBO>([&](auto K) {
+          constexpr int kk = decltype(K)::value;
+          x[kk] = Lh[rb + kk];
+        });
+        static_for<0, TBO>([&](auto K) {
+          constexpr int kk = decltype(K)::value;
+          double v = x[kk];
+          static_for<0, kk>([&](auto J) {
+            constexpr int j = decltype(J)::value;
+            v = fma(-x[j], Db[kk * TBO + j], v);
+          });
+          x[kk] = v / Db[kk * TBO + kk];
+        });
+        static_for<0, TBO>([&](auto K) {
+          constexpr int kk = decltype(K)::value;
+          Lh[rb + kk] = x[kk];
+        });
+      }
+      __syncthreads();
+      // trailing update A[r][c] -= sum_j L[r][k0+j] L[c][k0+j], r >= c >= k0 + 16, in 4 x 4 tiles
+      const int s0 = k0 + TBO;
+      const int m = f - s0;
+      const int nb = (m + 3) / 4;
+      const int ntiles = nb * (nb + 1) / 2;
+      for (int ti = tid; ti < ntiles; ti += NT) {
+        int R, C;
+        decode_tri(ti, &R, &C);
+        int rr[4], cc[4];
+        static_for<0, 4>([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          const int r = s0 + 4 * R + q, c = s0 + 4 * C + q;
+          rr[q] = r < f ? r : f - 1;
+          cc[q] = c < f ? c : f - 1;
+        });
+        double acc[4][4];
+        static_for<0, 4>([&](auto Q) {
+          static_for<0, 4>([&](auto U) { acc[decltype(Q)::value][decltype(U)::value] = 0.0; });
+        });
+        for (int j = 0; j < TBO; ++j) {
+          double pr[4], pc[4];
+          static_for<0, 4>([&](auto Q) {
+            constexpr int q = decltype(Q)::value;
+            pr[q] = Lh[tri(rr[q]) + k0 + j];
+            pc[q] = Lh[tri(cc[q]) + k0 + j];
+          });
+          static_for<0, 4>([&](auto Q) {
+            constexpr int q = decltype(Q)::value;
+            static_for<0, 4>([&](auto U) {
+              constexpr int u = decltype(U)::value;
+              acc[q][u] = fma(pr[q], pc[u], acc[q][u]);
+            });
+          });
+        }
+        static_for<0, 4>([&](auto Q) {
+          constexpr int q = decltype(Q)::value;
+          const int r = s0 + 4 * R + q;
+          static_for<0, 4>([&](auto U) {
+            constexpr int u = decltype(U)::value;
+            const int c = s0 + 4 * C + u;
+            if (r < f && c <= r) Lh[tri(r) + c] -= acc[q][u];
+          });
+        });
+      }
+      __syncthreads();
+    }
+    __syncthreads();
+    if (sh_fail < 0) break;
+    jitter = jitter == 0.0 ? 1e-13 : jitter * 100.0;
+    if (tid == 0 && head_status) atomicOr(head_status + h, int32_t(AMC_HS_CHOL_JITTER));
+    __syncthreads();
+  }
+}
+
+// Triangular solves with the global factor, 8 right-hand-side columns per
+// block, in place in the rhs rows of F: L Y = X / dn, L^T Z = Y, C_v = Z / dn.
+template <int D>
+__global__ __launch_bounds__(NT) void k_ols_trsm_g(const HeadDesc *__restrict__ desc, double *__restrict__ rhs,
+                                                   const int32_t *__restrict__ flist,
+                                                   const int32_t *__restrict__ fcount, const double *__restrict__ dn,
+                                                   const double *__restrict__ L, const double *__restrict__ w,
+                                                   float *__restrict__ cv_sel) {
+  constexpr int NC = 8;
+  __shared__ double Db[TBO * TBO];
+  __shared__ double Xb[TBO * NC];
+  const int h = blockIdx.y;
+  const HeadDesc Dh = desc[h];
+  if (Dh.t <= kLdsMaxT) return;
+  const int t = int(Dh.t);
+  const int c0 = blockIdx.x * NC;
+  const int f = fcount[h];
+  const int tid = threadIdx.x;
+  const int32_t *fl = flist + Dh.t_off;
+  const double *dnh = dn + Dh.t_off;
+  const double *Lh = L + Dh.tri_off;
+  auto X = [&](int k) -> double * { return rhs + (Dh.t_off + fl[k]) * D + c0; };
+  for (int e = tid; e < t * NC; e += NT) {
+    const int a = e / NC, c = e % NC;
+    if (!(w[Dh.t_off + a] > 0.0)) cv_sel[(Dh.t_off + a) * D + c0 + c] = 0.0f;
+  }
+  for (int e = tid; e < f * NC; e += NT) X(e / NC)[e % NC] /= dnh[e / NC];
+  __syncthreads();
+  // forward
+  for (int k0 = 0; k0 < f; k0 += TBO) {
+    const int e = f - k0 < TBO ? f - k0 : TBO;
+    for (int q = tid; q < TBO * TBO; q += NT) {
+      const int i = q / TBO, j = q % TBO;
+      Db[q] = (i < e && j <= i) ? Lh[tri(k0 + i) + k0 + j] : 0.0;
+    }
+    for (int q = tid; q < e * NC; q += NT) Xb[q] = X(k0 + q / NC)[q % NC];
+    __syncthreads();
+    if (tid < NC) {
+      for (int i = 0; i < e; ++i) {
+        double v = Xb[i * NC + tid];
+        for (int j = 0; j < i; ++j) v = fma(-Db[i * TBO + j], Xb[j * NC + tid], v);
+        Xb[i * NC + tid] = v / Db[i * TBO + i];
+      }
+    }
+    __syncthreads();
+    for (int q = tid; q < e * NC; q += NT) X(k0 + q / NC)[q % NC] = Xb[q];
+    for (int r = k0 + TBO + tid; r < f; r += NT) {
+      const int rb = tri(r) + k0;
+      double lr[TBO];
+      static_for<0, TBO>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        lr[j] = Lh[rb + j];
+      });
+      double *xr = X(r);
+      static_for<0, NC>([&](auto Cc) {
+        constexpr int c = decltype(Cc)::value;
+        double acc = 0.0;
+        static_for<0, TBO>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          acc = fma(lr[j], Xb[j * NC + c], acc);
+        });
+        xr[c] -= acc;
+      });
+    }
+    __syncthreads();
+  }
+  // backward
+  for (int k0 = ((f - 1) / TBO) * TBO; f > 0 && k0 >= 0; k0 -= TBO) {
+    const int e = f - k0 < TBO ? f - k0 : TBO;
+    for (int q = tid; q < TBO * TBO; q += NT) {
+      const int i = q / TBO, j = q % TBO;
+      Db[q] = (i < e && j <= i) ? Lh[tri(k0 + i) + k0 + j] : 0.0;
+    }
+    for (int q = tid; q < e * NC; q += NT) Xb[q] = X(k0 + q / NC)[q % NC];
+    __syncthreads();
+    if (tid < NC) {
+      for (int i = e - 1; i >= 0; --i) {
+        double v = Xb[i * NC + tid];
+        for (int j = i + 1; j < e; ++j) v = fma(-Db[j * TBO + i], Xb[j * NC + tid], v);
+        Xb[i * NC + tid] = v / Db[i * TBO + i];
+      }
+    }
+    __syncthreads();
+    for (int q = tid; q < e * NC; q += NT) X(k0 + q / NC)[q % NC] = Xb[q];
+    for (int r = tid; r < k0; r += NT) {
+      double *xr = X(r);
+      double acc[NC];
+      static_for<0, NC>([&](auto Cc) { acc[decltype(Cc)::value] = 0.0; });
+      for (int j = 0; j < e; ++j) {
+        const double l = Lh[tri(k0 + j) + r];
+        static_for<0, NC>([&](auto Cc) {
+          constexpr int c = decltype(Cc)::value;
+          acc[c] = fma(l, Xb[j * NC + c], acc[c]);
+        });
+      }
+      static_for<0, NC>([&](auto Cc) {
+        constexpr int c = decltype(Cc)::value;
+        xr[c] -= acc[c];
+      });
+    }
+    __syncthreads();
+  }
+  for (int e = tid; e < f * NC; e += NT) {
+    const int k = e / NC, c = e % NC;
+    cv_sel[(Dh.t_off + fl[k]) * D + c0 + c] = float(X(k)[c] / dnh[k]);
+  }
+}
+
 }  // namespace
 
 hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s) {
@@ -313,18 +627,43 @@ hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s) {
 }
 
 hipError_t launch_ols_factor(const Dims &dm, const Buffers &b, hipStream_t s) {
-  const size_t bytes = size_t(8) * size_t(dm.max_t) * size_t(dm.max_t + 1) / 2 + 16;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ols_factor),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_ols_factor, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.w, b.ols_flist,
-                     b.ols_fcount, b.ols_dn, b.ols_L, b.head_status);
-  return hipGetLastError();
+  if (dm.min_t <= kLdsMaxT) {
+    const int64_t mt = dm.max_t < kLdsMaxT ? dm.max_t : kLdsMaxT;
+    const size_t bytes = size_t(8) * size_t(mt) * size_t(mt + 1) / 2 + 16;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ols_factor),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_ols_factor, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.w, b.ols_flist,
+                       b.ols_fcount, b.ols_dn, b.ols_L, b.head_status);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  if (dm.max_t > kLdsMaxT) {
+    hipLaunchKernelGGL(k_ols_flist_g, dim3(unsigned(dm.H)), dim3(NT), 0, s, b.desc, b.G, b.w, b.ols_flist,
+                       b.ols_fcount, b.ols_dn);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_ols_factor_g, dim3(unsigned(dm.H)), dim3(NT), 0, s, b.desc, b.G, b.ols_flist, b.ols_fcount,
+                       b.ols_dn, b.ols_L, b.head_status);
+    return hipGetLastError();
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_ols_trsm(const Dims &dm, const Buffers &b, hipStream_t s) {
-  const size_t bytes = size_t(8) * (size_t(dm.max_t) * size_t(dm.max_t + 1) / 2 + size_t(dm.max_t) * 8) + 16;
   dim3 grid(unsigned(dm.d / 8), unsigned(dm.H));
+  if (dm.max_t > kLdsMaxT) {
+    if (dm.d == 128)
+      hipLaunchKernelGGL((k_ols_trsm_g<128>), grid, dim3(NT), 0, s, b.desc, b.rhs, b.ols_flist, b.ols_fcount,
+                         b.ols_dn, b.ols_L, b.w, b.cv_sel);
+    else
+      hipLaunchKernelGGL((k_ols_trsm_g<64>), grid, dim3(NT), 0, s, b.desc, b.rhs, b.ols_flist, b.ols_fcount,
+                         b.ols_dn, b.ols_L, b.w, b.cv_sel);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || dm.min_t > kLdsMaxT) return e;
+  }
+  const int64_t mt = dm.max_t < kLdsMaxT ? dm.max_t : kLdsMaxT;
+  const size_t bytes = size_t(8) * (size_t(mt) * size_t(mt + 1) / 2 + size_t(mt) * 8) + 16;
   hipError_t e;
   if (dm.d == 128) {
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ols_trsm<128>),
@@ -344,7 +683,8 @@ hipError_t launch_ols_trsm(const Dims &dm, const Buffers &b, hipStream_t s) {
 
 hipError_t launch_pack(const Dims &dm, const Buffers &b, void *Ck, float *beta, void *Cv, int cv_bf16,
                        int32_t *sel_idx, hipStream_t s) {
-#define AMC_PACK_ARGS b.desc, b.sel_slot, b.sel_list, b.w, b.beta_in, b.K, b.cv_sel, Ck, beta, Cv, cv_bf16, sel_idx
+#define AMC_PACK_ARGS \
+  b.desc, b.sel_slot, b.sel_list, b.w, b.beta_in, b.K, b.cv_sel, Ck, beta, Cv, cv_bf16, sel_idx, b.pos_of_slot
   if (dm.d == 128) {
     if (dm.in_bf16) hipLaunchKernelGGL((k_pack<128, true>), dim3(unsigned(dm.H)), dim3(NT), 0, s, AMC_PACK_ARGS);
     else hipLaunchKernelGGL((k_pack<128, false>), dim3(unsigned(dm.H)), dim3(NT), 0, s, AMC_PACK_ARGS);

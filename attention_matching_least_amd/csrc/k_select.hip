@@ -368,7 +368,7 @@ __global__ __launch_bounds__(256) void k_gram(const HeadDesc *__restrict__ desc,
 __global__ __launch_bounds__(256) void k_resid(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
                                                const double *__restrict__ w, const double *__restrict__ m, int cycle,
                                                int kR, int polish, double *__restrict__ r, double *__restrict__ mhat) {
-  __shared__ double ws[kLdsMaxT];
+  __shared__ double ws[256];
   const int h = blockIdx.y;
   const HeadDesc D = desc[h];
   int64_t p;
@@ -380,13 +380,20 @@ __global__ __launch_bounds__(256) void k_resid(const HeadDesc *__restrict__ desc
     if (Kc == 0) return;
     p = S0 + Kc;
   }
-  for (int a = threadIdx.x; a < p; a += 256) ws[a] = w[D.t_off + a];
-  __syncthreads();
   const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
-  if (i >= D.n) return;
+  const bool valid = i < D.n;
   const double *P = panel + D.panel_off;
   double acc = 0.0;
-  for (int64_t a = 0; a < p; ++a) acc = fma(P[a * D.n + i], ws[a], acc);
+  // the weights pass through LDS 256 at a time
+  for (int64_t a0 = 0; a0 < p; a0 += 256) {
+    __syncthreads();
+    if (a0 + threadIdx.x < p) ws[threadIdx.x] = w[D.t_off + a0 + threadIdx.x];
+    __syncthreads();
+    const int64_t cnt = p - a0 < 256 ? p - a0 : 256;
+    if (valid)
+      for (int64_t a = 0; a < cnt; ++a) acc = fma(P[(a0 + a) * D.n + i], ws[a], acc);
+  }
+  if (!valid) return;
   mhat[D.n_off + i] = acc;
   r[D.n_off + i] = m[D.n_off + i] - acc;
 }

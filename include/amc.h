@@ -102,7 +102,9 @@ typedef struct {
   int32_t head_dim;       /* d in {64, 128}; else AMC_ERR_UNSUPPORTED */
   const int64_t *cu_q;    /* HOST int64[H+1], cu_q[0] = 0, strictly increasing */
   const int64_t *cu_k;    /* HOST int64[H+1], cu_k[0] = 0, strictly increasing */
-  const int64_t *budgets; /* HOST int64[H], 1 <= budgets[h] <= T_h */
+  const int64_t *budgets; /* HOST int64[H], 1 <= budgets[h] <= min(T_h, 16384) (else
+                           * AMC_ERR_UNSUPPORTED); budgets above 176 keep the NNLS
+                           * state and above 192 the value-fit factor in the workspace */
   amc_dtype in_dtype;     /* storage type of Q, K, V (C_k is written in it too) */
   float scale;            /* logit scale; 0 means 1/sqrt(head_dim) */
 } amc_problem;

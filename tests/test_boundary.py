@@ -126,8 +126,8 @@ def test_compact_argument_errors_return_before_any_launch():
 
 
 def test_large_budget_and_phi_budget_limits():
-    # budgets above the LDS-resident solver's limit are reported as unsupported
-    p, keep = _problem(T=(300, 200), t=(250, 5))
+    # budgets above the largest supported budget are reported as unsupported
+    p, keep = _problem(T=(20000, 200), t=(16385, 5))
     o = amc.make_options()
     out = ctypes.c_uint64(0)
     assert amc.lib().amc_workspace_size(ctypes.byref(p), ctypes.byref(o), ctypes.byref(out)) == amc.AMC_ERR_UNSUPPORTED

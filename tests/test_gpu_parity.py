@@ -142,6 +142,25 @@ def test_compact_varlen_ragged(k, R):
         _assert_ok(replay_check(h.Q, h.K, h.V, budgets[i], k, R, res, i, beta_in=betas[i], trace=tr), f"head{i}")
 
 
+@pytest.mark.parametrize("k,R", [(1, 1), (4, 2)])
+def test_compact_large_budgets(k, R):
+    """Budgets past the LDS-resident limits (176 keys for the NNLS state, 192
+    for the value-fit factor) run on the workspace-resident kernels; a small
+    head in the same call stays on the LDS path."""
+    shapes = [(520, 1100, 300), (400, 900, 185), (256, 700, 60)]
+    heads = [synth.make_head([32, i], n, T, 128, True, "bf16") for i, (n, T, _) in enumerate(shapes)]
+    budgets = [t for _, _, t in shapes]
+    betas = [synth.random_beta([33, i], T, 1.0) for i, (_, T, _) in enumerate(shapes)]
+    _say(f"large budgets k={k} R={R} shapes={shapes}")
+    res = _run(heads, budgets, "bf16", k, R, beta_in=betas)
+    hs = res.head_status.cpu().numpy()
+    _say(f"head status {hs}")
+    assert np.all(hs & (amc.HS_NNLS_CAP | amc.HS_NONFINITE) == 0), hs
+    tr = res.trace()
+    for i, h in enumerate(heads):
+        _assert_ok(replay_check(h.Q, h.K, h.V, budgets[i], k, R, res, i, beta_in=betas[i], trace=tr), f"head{i}")
+
+
 def test_compact_d64_bf16_batched():
     heads = [synth.make_head([40, i], 256, 512, 64, True, "bf16") for i in range(2)]
     res = _run(heads, [32, 31], "bf16", 4, 2)
@@ -248,3 +267,30 @@ def test_workload2_full_size_sampled():
     tr = res.trace()
     for h in (0, 201):
         _assert_ok(replay_check(heads[h].Q, heads[h].K, heads[h].V, 164, 4, 2, res, h, trace=tr), f"w2 head{h}")
+
+
+@pytest.mark.slow
+def test_workload4_varlen_full_size_sampled():
+    """288 heads, T=8192, Dirichlet budgets 8..2048 (152 heads above the LDS
+    limits).  Sampled heads against the oracle; every head against the
+    properties that hold at any size: ascending unique selection, exact key
+    copies, and finite beta exactly where the weight is positive."""
+    w = synth.workload(4)
+    _say("workload 4: generating 288 heads")
+    heads = w.heads()
+    res = _run(heads, w.budgets, w.dtype, w.topk, w.refit_every)
+    hs = res.head_status.cpu().numpy()
+    _say(f"head status nonzero: {[(i, int(v)) for i, v in enumerate(hs) if v]}")
+    assert np.all(hs & (amc.HS_NNLS_CAP | amc.HS_NONFINITE) == 0)
+    tr = res.trace()
+    for h in range(w.num_heads):
+        Ck, beta, Cv, sel = head_outputs(res, h)
+        assert len(sel) == w.budgets[h] and np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < w.T
+        assert np.array_equal(Ck, np.asarray(heads[h].K, dtype=np.float64)[sel])
+        wt = np.asarray(tr["weight"][h])[np.argsort(np.asarray(tr["pick"][h]), kind="stable")]
+        assert np.array_equal(np.isfinite(beta), wt > 0)
+        assert np.all(np.isfinite(Cv))
+    for h in (3, 7, 32):
+        _say(f"w4 head {h}: t={w.budgets[h]}")
+        _assert_ok(replay_check(heads[h].Q, heads[h].K, heads[h].V, w.budgets[h], w.topk, w.refit_every, res, h,
+                                trace=tr), f"w4 head{h}")
