@@ -16,7 +16,7 @@ constexpr int kSweepCols = 256;  // columns per block of the correlation sweep
 constexpr int kMaxCycle = 255;   // largest k * R (keys per refit cycle)
 constexpr int kLdsMaxT = 192;    // largest budget of the LDS-resident value fit
 constexpr int kNnlsLdsT = 176;   // largest budget whose NNLS state fits in LDS (larger: global memory)
-constexpr int kNnlsVecPerSlot = 13;  // float64 words of global NNLS state per budget slot
+constexpr int kNnlsVecPerSlot = 15;  // float64 words of global NNLS state per budget slot
 constexpr int kMaxBudget = 16384;  // largest budget per head (packed triangles indexed in int32)
 constexpr int kMaxSweepBlocks = 1024;  // sweep column blocks per head the merge handles
 

@@ -17,24 +17,27 @@
 // a compaction starts from g = Phi_S^T r computed from the float64 panel and
 // the float64 residual of the previous refit (the corrected semi-normal
 // equations of Bjorck), and a final refit with no new key refines the weights
-// once more.  Within a refit the rows of zero variables follow every step
-// exactly (g_Z -= G_ZP delta, read from G); the rows of the free set follow
-// the factor's model: the step d solves L L^T d = g_P, so moving a fraction
-// alpha along d scales g_P by (1 - alpha).
+// once more.  Within a refit the rows of the free set follow the factor's
+// model: the step d solves L L^T d = g_P, so moving a fraction alpha along d
+// scales g_P by (1 - alpha), and y = L^-1 g_P scales with it.  The rows of
+// zero variables are brought up to date only when candidates are chosen, by
+// the exact increment from a snapshot: g_a = g_a(snap) - G_a (u - u_snap).
 //
 // The factor is updated, not recomputed.  Up to eight candidates enter
 // together: one blocked forward substitution with several right-hand sides
 // gives their factor rows and L^-1 g for the following solve, and a small
 // Cholesky of the block finishes the rows.  A variable that leaves is deleted
-// by a row shift plus a blocked rank-one update of the trailing rows.  Between
-// the refits of one compaction the factor and the free set persist in the
-// workspace.
+// by a row shift plus a blocked rank-one update of the trailing rows (Givens
+// rotations, applied to y as well, so no forward substitution is needed
+// between entries).  Between the refits of one compaction the factor and the
+// free set persist in the workspace.
 //
 // GPU mapping: one 256-thread block per system.  Triangular work runs in
 // 16-row blocks: one wave solves the 16 x 16 diagonal block in registers
 // (v_readlane broadcasts), then every thread updates one of the rows beyond
 // it.  The state lives in LDS for budgets up to kNnlsLdsT; above that the same
-// code runs on the workspace copy in global memory.
+// code runs on the workspace copy in global memory, with the two solve vectors
+// still in LDS.
 #include <hip/hip_runtime.h>
 
 #include <cfloat>
@@ -51,11 +54,14 @@ constexpr int NT = 256;
 constexpr int NW = NT / 64;
 constexpr int TB = 16;             // triangular block
 constexpr int NB = 8;              // candidates that may enter together
-constexpr int NRHS = NB + 1;       // rows of the right-hand-side scratch
+constexpr int NRHS = NB + 1;       // right-hand sides of a block entry (rows 0..8)
+constexpr int NROW = NRHS + 2;     // scratch rows: 0 solve vector, 1 change list, 2 scaled change,
+                                   // 3..6 partial sums, 7 removed column, 8 y = L^-1 g_P,
+                                   // 9 u at the last snapshot, 10 g at the last snapshot
 constexpr unsigned char F_PASSIVE = 1, F_BLOCKED = 2, F_NEW = 4, F_DROP = 8, F_CAND = 16;
 constexpr double PIV_TOL = 1e-14;  // smallest acceptable squared pivot in unit-diagonal form
 static_assert(NRHS <= 3 * NW, "diagonal solves take three right-hand sides per wave");
-static_assert(NRHS >= 8, "settle uses rows 1..7 of the right-hand-side scratch");
+static_assert(NRHS == 9, "row roles assume nine right-hand sides");
 
 __device__ __forceinline__ int tri(int r) { return r * (r + 1) / 2; }
 
@@ -144,28 +150,37 @@ struct Blk {
   int cand[NB];              // entering candidates
   int accb[NB];              // accepted candidates, in order
   int ctl[8];                // [1], [4] scan state, [2] accepted count, [3] enter one at a time
+  int wc[NW];                // per-wave counts of a compaction
   int np;                    // free-set size
 };
 
-// State of one solve.  Vectors are indexed by variable (u, g, dg, flag) or by
-// factor position (plist, rhs rows).
+// State of one solve.  Vectors are indexed by variable (u, g, dg, flag, rows
+// 9 and 10) or by factor position (plist, the other rows).
 struct St {
   double *L;      // packed lower factor of Gs_PP, rows in free-set order
   double *u;      // scaled iterate
   double *g;      // scaled gradient bs - Gs u
   double *dg;     // sqrt(G_aa)
-  double *rhs;    // NRHS rows of mp: right-hand sides; in settle row 0 = solve vector,
-                  // 1 = step, 2 = step / dg, 3..6 = partial sums, 7 = removed column
+  double *rows;   // NROW scratch rows of mp (roles at NROW)
+  double *x0;     // row 0: solve vector (may live apart from rows)
+  double *yv;     // row 8: y = L^-1 g_P (may live apart from rows)
   int *plist;     // free set in factor order
   unsigned char *flag;
   Blk *bk;
-  int mp;         // row stride of rhs (largest p of the system)
+  int mp;         // row stride (largest p of the system)
+  __device__ __forceinline__ double *row(int b) const { return b == 0 ? x0 : (b == 8 ? yv : rows + b * mp); }
 };
 
 // LDS bytes of the state for systems up to maxp variables (LDS variant)
 __host__ __device__ constexpr size_t nnls_smem_bytes(int maxp) {
-  return size_t(8) * (size_t(maxp) * (maxp + 1) / 2 + size_t(3 + NRHS) * maxp) + 4 * size_t(maxp) +
+  return size_t(8) * (size_t(maxp) * (maxp + 1) / 2 + size_t(3 + NROW) * maxp) + 4 * size_t(maxp) +
          ((size_t(maxp) + 15) & ~size_t(15));
+}
+
+// LDS bytes of the global variant: the two solve vectors, when they fit.
+constexpr int kGlobalLdsRowsMax = 4096;
+__host__ __device__ constexpr size_t nnls_global_smem_bytes(int64_t max_t) {
+  return max_t <= kGlobalLdsRowsMax ? size_t(16) * size_t(max_t) : 0;
 }
 
 __device__ __forceinline__ St carve_lds(char *base, int maxp, Blk *bk) {
@@ -181,15 +196,18 @@ __device__ __forceinline__ St carve_lds(char *base, int maxp, Blk *bk) {
   d += maxp;
   s.dg = d;
   d += maxp;
-  s.rhs = d;
-  d += NRHS * maxp;
+  s.rows = d;
+  s.x0 = d;
+  s.yv = d + 8 * maxp;
+  d += NROW * maxp;
   s.plist = reinterpret_cast<int *>(d);
   s.flag = reinterpret_cast<unsigned char *>(s.plist + maxp);
   return s;
 }
 
-// Global-memory state of one head: u, g, dg, the rhs rows, then the flag bytes.
-__device__ __forceinline__ St carve_global(double *vec, double *L, int32_t *plist, int mp, Blk *bk) {
+// Global-memory state of one head: u, g, dg, the scratch rows, then the flag
+// bytes; the solve vectors go to LDS (lds, 2 mp doubles) when given.
+__device__ __forceinline__ St carve_global(double *vec, double *L, int32_t *plist, int mp, Blk *bk, double *lds) {
   St s;
   s.mp = mp;
   s.bk = bk;
@@ -197,19 +215,20 @@ __device__ __forceinline__ St carve_global(double *vec, double *L, int32_t *plis
   s.u = vec;
   s.g = vec + mp;
   s.dg = vec + 2 * mp;
-  s.rhs = vec + 3 * mp;
-  s.flag = reinterpret_cast<unsigned char *>(vec + (3 + NRHS) * mp);
+  s.rows = vec + 3 * mp;
+  s.x0 = lds ? lds : s.rows;
+  s.yv = lds ? lds + mp : s.rows + 8 * mp;
+  s.flag = reinterpret_cast<unsigned char *>(vec + (3 + NROW) * mp);
   s.plist = plist;
   return s;
 }
-static_assert(kNnlsVecPerSlot == 3 + NRHS + 1, "global NNLS state layout");
+static_assert(kNnlsVecPerSlot == 3 + NROW + 1, "global NNLS state layout");
 
 // ---- triangular solves ----------------------------------------------------
 
-// Solves L X = R in place for the nr right-hand sides rhs[b * mp + k], k < n.
+// Solves L X = R in place for the nr right-hand sides S.row(b)[k], k < n.
 __device__ __forceinline__ void fwd_blk(const St &S, int n, int nr) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mp = S.mp;
   for (int r0 = 0; r0 < n; r0 += TB) {
     const int e = n - r0 < TB ? n - r0 : TB;
     // diagonal block: wave w solves right-hand sides w, w + 4, w + 8; lane i holds row r0 + i
@@ -227,7 +246,7 @@ __device__ __forceinline__ void fwd_blk(const St &S, int n, int nr) {
       static_for<0, 3>([&](auto Qc) {
         constexpr int q = decltype(Qc)::value;
         const int b = wave + NW * q;
-        x[q] = (act && b < nr) ? S.rhs[b * mp + r0 + i] : 0.0;
+        x[q] = (act && b < nr) ? S.row(b)[r0 + i] : 0.0;
       });
       static_for<0, TB>([&](auto K) {
         constexpr int kk = decltype(K)::value;
@@ -244,7 +263,7 @@ __device__ __forceinline__ void fwd_blk(const St &S, int n, int nr) {
       static_for<0, 3>([&](auto Qc) {
         constexpr int q = decltype(Qc)::value;
         const int b = wave + NW * q;
-        if (act && b < nr) S.rhs[b * mp + r0 + i] = x[q];
+        if (act && b < nr) S.row(b)[r0 + i] = x[q];
       });
     }
     __syncthreads();
@@ -258,14 +277,15 @@ __device__ __forceinline__ void fwd_blk(const St &S, int n, int nr) {
           Lr[j] = S.L[rb + j];
         });
         for (int b = 0; b < nr; ++b) {
-          const double *xb = S.rhs + b * mp + r0;
+          double *xr = S.row(b);
+          const double *xb = xr + r0;
           double a0 = 0.0, a1 = 0.0;
           static_for<0, TB / 2>([&](auto J) {
             constexpr int j = decltype(J)::value;
             a0 = fma(Lr[2 * j], xb[2 * j], a0);
             a1 = fma(Lr[2 * j + 1], xb[2 * j + 1], a1);
           });
-          S.rhs[b * mp + row] -= a0 + a1;
+          xr[row] -= a0 + a1;
         }
       }
       __syncthreads();
@@ -298,13 +318,19 @@ __device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
       if (act) x[r0 + i] = xv;
     }
     __syncthreads();
-    // columns before the block: x_c -= sum_k L[r0 + k][c] x_{r0 + k}
+    // columns before the block: x_c -= sum_k L[r0 + k][c] x_{r0 + k}; the loads
+    // of a column are all issued before the sums (rows past e read row r0)
     for (int c = tid; c < r0; c += NT) {
+      double l[TB];
+      static_for<0, TB>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        l[k] = S.L[tri(k < e ? r0 + k : r0) + c];
+      });
       double a0 = 0.0, a1 = 0.0;
       static_for<0, TB / 2>([&](auto K) {
         constexpr int k = decltype(K)::value;
-        if (2 * k < e) a0 = fma(S.L[tri(r0 + 2 * k) + c], x[r0 + 2 * k], a0);
-        if (2 * k + 1 < e) a1 = fma(S.L[tri(r0 + 2 * k + 1) + c], x[r0 + 2 * k + 1], a1);
+        if (2 * k < e) a0 = fma(l[2 * k], x[r0 + 2 * k], a0);
+        if (2 * k + 1 < e) a1 = fma(l[2 * k + 1], x[r0 + 2 * k + 1], a1);
       });
       x[c] -= a0 + a1;
     }
@@ -312,77 +338,110 @@ __device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
   }
 }
 
-// ---- gradient update -------------------------------------------------------
+// ---- gradient of the zero variables ---------------------------------------
 
-// After a step: rows of the free set scale by keep (the factor's model: 0 for
-// a full step, 1 - alpha for a partial one); rows of zero variables subtract
-// G_ZP delta, with delta / dg in rhs row 2.  Each wave sums a quarter of the
-// free set, with many loads of G in flight; the quarters are added in a fixed
-// order, so the result does not depend on timing.
-__device__ __forceinline__ void grad_update(const St &S, const double *G, int64_t ld, int p, double keep) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int np = S.bk->np, mp = S.mp;
-  const int k0 = (np * wave) / NW, k1 = (np * (wave + 1)) / NW;
-  const int *pl = S.plist;
-  const double *dsc = S.rhs + 2 * mp;
-  double *zp = S.rhs + (3 + wave) * mp;
-  for (int a0 = 0; a0 < p; a0 += NT) {
-    double acc[4] = {0.0, 0.0, 0.0, 0.0};
-    int ac[4];
-    static_for<0, 4>([&](auto M) {
-      constexpr int m = decltype(M)::value;
-      const int a = a0 + lane + 64 * m;
-      ac[m] = a < p ? a : p - 1;
-    });
-    int k = k0;
-    for (; k + 8 <= k1; k += 8) {
-      int c[8];
-      double s[8];
-      static_for<0, 8>([&](auto U) {
-        constexpr int u = decltype(U)::value;
-        c[u] = pl[k + u];
-        s[u] = dsc[k + u];
-      });
-      static_for<0, 4>([&](auto M) {
-        constexpr int m = decltype(M)::value;
-        if (a0 + 64 * m < p) {
-          double v[8];
-          static_for<0, 8>([&](auto U) {
-            constexpr int u = decltype(U)::value;
-            v[u] = G[int64_t(c[u]) * ld + ac[m]];
-          });
-          static_for<0, 8>([&](auto U) {
-            constexpr int u = decltype(U)::value;
-            acc[m] = fma(v[u], s[u], acc[m]);
-          });
-        }
-      });
-    }
-    for (; k < k1; ++k) {
-      const int c = pl[k];
-      const double s = dsc[k];
-      static_for<0, 4>([&](auto M) {
-        constexpr int m = decltype(M)::value;
-        if (a0 + 64 * m < p) acc[m] = fma(G[int64_t(c) * ld + ac[m]], s, acc[m]);
-      });
-    }
-    static_for<0, 4>([&](auto M) {
-      constexpr int m = decltype(M)::value;
-      const int a = a0 + lane + 64 * m;
-      if (a < p) zp[a] = acc[m];
-    });
+// u_snap = u, g_snap = g (rows 9 and 10)
+__device__ __forceinline__ void snapshot(const St &S, int p) {
+  double *us = S.rows + 9 * S.mp, *gs = S.rows + 10 * S.mp;
+  for (int a = threadIdx.x; a < p; a += NT) {
+    us[a] = S.u[a];
+    gs[a] = S.g[a];
   }
   __syncthreads();
-  const double *z = S.rhs + 3 * mp;
+}
+
+// Brings g up to date on every zero variable by the exact increment since the
+// last snapshot, g_a = g_a(snap) - Gs_a (u - u_snap), then takes a new
+// snapshot of u and g.  The change is compacted first (row 1: indices, row 2:
+// change / dg); each wave sums a quarter of it, with many loads of G in
+// flight, and the quarters are added in a fixed order, so the result does not
+// depend on timing.
+__device__ __forceinline__ void sync_z(const St &S, const double *G, int64_t ld, int p) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int mp = S.mp;
+  Blk *bk = S.bk;
+  int *lst = reinterpret_cast<int *>(S.rows + mp);
+  double *dv = S.rows + 2 * mp;
+  const double *us = S.rows + 9 * mp;
+  double *gs = S.rows + 10 * mp;
+  int ns = 0;
+  for (int c0 = 0; c0 < p; c0 += NT) {
+    const int c = c0 + tid;
+    double dl = 0.0;
+    if (c < p) dl = S.u[c] - us[c];
+    const bool pred = dl != 0.0;
+    const unsigned long long bal = __ballot(pred);
+    const int before = __popcll(bal & ((1ull << lane) - 1ull));
+    if (lane == 0) bk->wc[wave] = __popcll(bal);
+    __syncthreads();
+    int off = ns;
+    for (int v = 0; v < wave; ++v) off += bk->wc[v];
+    if (pred) {
+      lst[off + before] = c;
+      dv[off + before] = dl / S.dg[c];
+    }
+    for (int v = 0; v < NW; ++v) ns += bk->wc[v];
+    __syncthreads();
+  }
+  if (ns > 0) {
+    const int k0 = (ns * wave) / NW, k1 = (ns * (wave + 1)) / NW;
+    double *zp = S.rows + (3 + wave) * mp;
+    for (int a0 = 0; a0 < p; a0 += NT) {
+      double acc[4] = {0.0, 0.0, 0.0, 0.0};
+      int ac[4];
+      static_for<0, 4>([&](auto M) {
+        constexpr int m = decltype(M)::value;
+        const int a = a0 + lane + 64 * m;
+        ac[m] = a < p ? a : p - 1;
+      });
+      int k = k0;
+      for (; k + 8 <= k1; k += 8) {
+        int c[8];
+        double s[8];
+        static_for<0, 8>([&](auto U) {
+          constexpr int u = decltype(U)::value;
+          c[u] = lst[k + u];
+          s[u] = dv[k + u];
+        });
+        static_for<0, 4>([&](auto M) {
+          constexpr int m = decltype(M)::value;
+          if (a0 + 64 * m < p) {
+            double v[8];
+            static_for<0, 8>([&](auto U) {
+              constexpr int u = decltype(U)::value;
+              v[u] = G[int64_t(c[u]) * ld + ac[m]];
+            });
+            static_for<0, 8>([&](auto U) {
+              constexpr int u = decltype(U)::value;
+              acc[m] = fma(v[u], s[u], acc[m]);
+            });
+          }
+        });
+      }
+      for (; k < k1; ++k) {
+        const int c = lst[k];
+        const double s = dv[k];
+        static_for<0, 4>([&](auto M) {
+          constexpr int m = decltype(M)::value;
+          if (a0 + 64 * m < p) acc[m] = fma(G[int64_t(c) * ld + ac[m]], s, acc[m]);
+        });
+      }
+      static_for<0, 4>([&](auto M) {
+        constexpr int m = decltype(M)::value;
+        const int a = a0 + lane + 64 * m;
+        if (a < p) zp[a] = acc[m];
+      });
+    }
+  }
+  __syncthreads();
+  const double *z = S.rows + 3 * mp;
   for (int a = tid; a < p; a += NT) {
     const unsigned char f = S.flag[a];
-    if (f & F_PASSIVE) {
-      S.g[a] *= keep;
-    } else if (!(f & F_BLOCKED)) {
-      S.g[a] -= ((z[a] + z[mp + a]) + (z[2 * mp + a] + z[3 * mp + a])) / S.dg[a];
-    }
+    if (!(f & (F_PASSIVE | F_BLOCKED)))
+      S.g[a] = ns > 0 ? gs[a] - ((z[a] + z[mp + a]) + (z[2 * mp + a] + z[3 * mp + a])) / S.dg[a] : gs[a];
   }
   __syncthreads();
+  snapshot(S, p);
 }
 
 // ---- factor updates --------------------------------------------------------
@@ -397,20 +456,27 @@ __device__ __forceinline__ int row_of(int s) {
 
 // Deletes factor position q: rows below move up one row without column q,
 // then the trailing rows absorb the removed column by a rank-one update
-// (Givens rotations, applied 16 columns at a time).
+// (Givens rotations, applied 16 columns at a time).  y = L^-1 g_P follows:
+// its entries below q take the same rotations, with y_q as the extra entry.
 __device__ __forceinline__ void remove_at(const St &S, int q) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Blk *bk = S.bk;
   const int np = bk->np, n2 = np - 1;
-  double *xc = S.rhs + 7 * S.mp;
+  double *xc = S.rows + 7 * S.mp;
+  double *yv = S.yv;
+  double z = yv[q];  // y of the removed position, rotated into the trailing entries below
   for (int i = q + 1 + tid; i < np; i += NT) xc[i - 1] = S.L[tri(i) + q];
   // Every element moves to a lower index, so chunks taken in increasing
   // source order never overwrite a source that is still to be read.
   for (int base = q; base < n2; base += NT) {
     const int k = base + tid;
     const int pv = k < n2 ? S.plist[k + 1] : 0;
+    const double yk = k < n2 ? yv[k + 1] : 0.0;
     __syncthreads();
-    if (k < n2) S.plist[k] = pv;
+    if (k < n2) {
+      S.plist[k] = pv;
+      yv[k] = yk;
+    }
   }
   const int s0 = tri(q + 1), s1 = tri(np);
   for (int base = s0; base < s1; base += NT * 8) {
@@ -450,6 +516,7 @@ __device__ __forceinline__ void remove_at(const St &S, int q) {
         Lr[j] = (act && j <= i) ? S.L[rb + j] : 0.0;
       });
       double xv = act ? xc[k0 + i] : 0.0;
+      double yl = act ? yv[k0 + i] : 0.0;
       static_for<0, TB>([&](auto K) {
         constexpr int kk = decltype(K)::value;
         if (kk < e) {
@@ -457,6 +524,9 @@ __device__ __forceinline__ void remove_at(const St &S, int q) {
           const double t2 = fma(lkk, lkk, xk * xk);
           const double ri = rsqrt(t2);
           const double c = lkk * ri, s = xk * ri;
+          const double yk = rl(yl, kk);
+          if (i == kk) yl = fma(c, yk, s * z);
+          z = fma(c, z, -s * yk);
           if (i == kk) {
             Lr[kk] = t2 * ri;
           } else if (i > kk) {
@@ -475,6 +545,7 @@ __device__ __forceinline__ void remove_at(const St &S, int q) {
           constexpr int j = decltype(J)::value;
           if (j <= i) S.L[rb + j] = Lr[j];
         });
+        yv[k0 + i] = yl;
       }
     }
     __syncthreads();
@@ -521,19 +592,19 @@ __device__ __forceinline__ int last_position(int np, P pred, Red *red) {
 // set.  One blocked forward pass over the current factor gives each
 // candidate's row l = L^-1 Gs[P, j] and y = L^-1 g_P; a Cholesky of the block
 // finishes the rows (candidates whose pivot vanishes are blocked).  On return
-// rhs row 0 holds y = L^-1 g_P over the extended free set and bk->ctl[2] the
-// number of accepted candidates.
+// x0 holds y = L^-1 g_P over the extended free set and bk->ctl[2] the number
+// of accepted candidates.  Rows 1..8 are overwritten.
 __device__ __forceinline__ void block_append(const St &S, const double *G, int64_t ld, int nc, int *status) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Blk *bk = S.bk;
-  const int np0 = bk->np, mp = S.mp;
+  const int np0 = bk->np;
   for (int k = tid; k < np0; k += NT) {
     const int a = S.plist[k];
     const double da = S.dg[a];
-    S.rhs[k] = S.g[a];
+    S.x0[k] = S.g[a];
     for (int b = 0; b < nc; ++b) {
       const int j = bk->cand[b];
-      S.rhs[(b + 1) * mp + k] = G[int64_t(j) * ld + a] / (S.dg[j] * da);
+      S.row(b + 1)[k] = G[int64_t(j) * ld + a] / (S.dg[j] * da);
     }
   }
   if (tid < nc * nc) {
@@ -548,8 +619,9 @@ __device__ __forceinline__ void block_append(const St &S, const double *G, int64
     int b1 = 0;
     while ((b1 + 1) * (b1 + 2) / 2 <= pr) ++b1;
     const int b2 = pr - b1 * (b1 + 1) / 2;
+    const double *r1 = S.row(b1), *r2 = S.row(b2);
     double v = 0.0;
-    for (int k = lane; k < np0; k += 64) v = fma(S.rhs[b1 * mp + k], S.rhs[b2 * mp + k], v);
+    for (int k = lane; k < np0; k += 64) v = fma(r1[k], r2[k], v);
     v = wave_sum(v);
     if (lane == 0) bk->dots[b1 * NRHS + b2] = v;
   }
@@ -631,14 +703,15 @@ __device__ __forceinline__ void block_append(const St &S, const double *G, int64
     const int b = bk->accb[a];
     const int pos = np0 + a;
     const int base = tri(pos);
-    for (int k = tid; k < np0; k += NT) S.L[base + k] = S.rhs[(b + 1) * mp + k];
+    const double *rb = S.row(b + 1);
+    for (int k = tid; k < np0; k += NT) S.L[base + k] = rb[k];
     if (tid < a) S.L[base + np0 + tid] = bk->E[a * NB + tid];
     if (tid == 0) {
       const int j = bk->cand[b];
       S.L[base + pos] = bk->Dg[a];
       S.plist[pos] = j;
       S.flag[j] = F_PASSIVE | F_NEW;
-      S.rhs[pos] = bk->yb[a];
+      S.x0[pos] = bk->yb[a];
     }
   }
   __syncthreads();
@@ -648,35 +721,39 @@ __device__ __forceinline__ void block_append(const St &S, const double *G, int64
 
 // Least squares on the free set, with feasibility back-tracking, starting
 // from a feasible u whose support is the free set; variables that just
-// entered sit at zero, flagged F_NEW.  have_y: rhs row 0 holds L^-1 g_P.
+// entered sit at zero, flagged F_NEW.  have_y: x0 holds y = L^-1 g_P.
 //  - An entering variable whose solution is not positive leaves again before
 //    any step is taken.  If it entered alone it is set aside for the rest of
 //    this fit (Lawson and Hanson's guard against cycling on round-off);
 //    otherwise ctl[3] is raised so that later candidates enter one at a time.
 //  - Otherwise the iterate moves toward the solution, as far as feasibility
 //    allows, and the variables that reach zero leave.
-__device__ __forceinline__ void settle(const St &S, const double *G, int64_t ld, int p, bool have_y, bool single,
-                                       Red *red) {
+// Only the free-set rows of g change here (by the factor's model); y follows
+// every step and every removal.
+__device__ __forceinline__ void settle(const St &S, int p, bool have_y, bool single, Red *red) {
   const int tid = threadIdx.x;
   Blk *bk = S.bk;
-  const int mp = S.mp;
-  for (int guard = 0; guard < 4 * mp + 8; ++guard) {
+  __syncthreads();
+  if (bk->np == 0) return;
+  if (!have_y) {
+    for (int k = tid; k < bk->np; k += NT) S.x0[k] = S.g[S.plist[k]];
+    __syncthreads();
+    fwd_blk(S, bk->np, 1);
+  }
+  for (int k = tid; k < bk->np; k += NT) S.yv[k] = S.x0[k];
+  for (int guard = 0; guard < 4 * S.mp + 8; ++guard) {
     __syncthreads();
     const int np = bk->np;
     if (np == 0) break;
-    if (!have_y) {
-      for (int k = tid; k < np; k += NT) S.rhs[k] = S.g[S.plist[k]];
-      __syncthreads();
-      fwd_blk(S, np, 1);
-    }
-    have_y = false;
-    bwd_blk(S, np, S.rhs);  // rhs = Gs_PP^-1 g_P: the step to the free-set optimum
+    for (int k = tid; k < np; k += NT) S.x0[k] = S.yv[k];
+    __syncthreads();
+    bwd_blk(S, np, S.x0);  // x0 = Gs_PP^-1 g_P: the step to the free-set optimum
     int ndrop = 0;
     double best = INFINITY;
     int kb = -1;
     for (int k = tid; k < np; k += NT) {
       const int a = S.plist[k];
-      const double d = S.rhs[k];
+      const double d = S.x0[k];
       const double ua = S.u[a];
       if ((S.flag[a] & F_NEW) && ua == 0.0 && !(d > 0.0)) {
         S.flag[a] |= F_DROP;
@@ -708,24 +785,16 @@ __device__ __forceinline__ void settle(const St &S, const double *G, int64_t ld,
     best = -nbest;
     const bool done = kb < 0;
     const double alpha = done ? 1.0 : (best < 1.0 ? best : 1.0);
-    double *delta = S.rhs + mp, *dsc = S.rhs + 2 * mp;
+    const double keep = done ? 0.0 : 1.0 - alpha;
     for (int k = tid; k < np; k += NT) {
       const int a = S.plist[k];
       const double ua = S.u[a];
-      const double d = S.rhs[k];
-      double un = (k == kb) ? 0.0 : fma(alpha, d, ua);
-      if (!(un > 0.0)) un = 0.0;
-      const double dl = done ? d : un - ua;
-      delta[k] = dl;
-      dsc[k] = dl / S.dg[a];
-    }
-    __syncthreads();
-    grad_update(S, G, ld, p, done ? 0.0 : 1.0 - alpha);
-    for (int k = tid; k < np; k += NT) {
-      const int a = S.plist[k];
-      const double un = S.u[a] + delta[k];
+      const double d = S.x0[k];
+      const double un = done ? ua + d : ((k == kb) ? 0.0 : fma(alpha, d, ua));
       S.u[a] = un > 0.0 ? un : 0.0;
       S.flag[a] &= ~F_NEW;
+      S.g[a] *= keep;
+      S.yv[k] *= keep;
     }
     __syncthreads();
     if (done) break;
@@ -803,7 +872,7 @@ __device__ __forceinline__ void nnls_core(const St &S, const double *G, int64_t 
     }
     for (int k = tid; k < bk->np; k += NT) S.flag[S.plist[k]] &= ~F_NEW;
     // a dependent variable dropped here still carries weight: take it out of u and g
-    double *tmp = S.rhs + 2 * S.mp;
+    double *tmp = S.rows + 2 * S.mp;
     for (int a = tid; a < p; a += NT) tmp[a] = ((S.flag[a] & F_BLOCKED) && S.u[a] > 0.0) ? -S.u[a] : 0.0;
     __syncthreads();
     for (int a = tid; a < p; a += NT) {
@@ -815,10 +884,13 @@ __device__ __forceinline__ void nnls_core(const St &S, const double *G, int64_t 
     __syncthreads();
     for (int a = tid; a < p; a += NT)
       if (S.flag[a] & F_BLOCKED) S.u[a] = 0.0;
+    __syncthreads();
+    snapshot(S, p);
   }
   // refine the starting free set with the gradient given
-  settle(S, G, ld, p, false, false, red);
+  settle(S, p, false, false, red);
   for (;;) {
+    sync_z(S, G, ld, p);
     const int nc = pick_candidates(S, p, tol, bk->ctl[3] ? 1 : NB, red);
     if (nc == 0) break;
     if (iters >= cap) {
@@ -827,7 +899,7 @@ __device__ __forceinline__ void nnls_core(const St &S, const double *G, int64_t 
     }
     ++iters;
     block_append(S, G, ld, nc, status);
-    if (bk->ctl[2] > 0) settle(S, G, ld, p, true, nc == 1, red);
+    if (bk->ctl[2] > 0) settle(S, p, true, nc == 1, red);
   }
   __syncthreads();
   *iters_out = iters;
@@ -867,6 +939,8 @@ __device__ __forceinline__ double nnls_setup(const St &S, const double *G, int64
       S.g[a] = (S.flag[a] & F_BLOCKED) ? 0.0 : b[a] / S.dg[a] - acc / S.dg[a];
     }
   }
+  __syncthreads();
+  snapshot(S, p);
   double bmax;
   (void)block_argmax(bl, 0, red, &bmax);
   if (!(bmax > 0.0) || !isfinite(bmax)) return 0.0;
@@ -876,7 +950,7 @@ __device__ __forceinline__ double nnls_setup(const St &S, const double *G, int64
 // Projected-gradient warm-up (step 1/L, L a Gershgorin bound of Gs).
 __device__ __forceinline__ void pg_warmup(const St &S, const double *G, int64_t ld, int p, int iters, Red *red) {
   const int tid = threadIdx.x;
-  double *tmp = S.rhs + 2 * S.mp;
+  double *tmp = S.rows + 2 * S.mp;
   double rowmax = 0.0;
   for (int a = tid; a < p; a += NT) {
     double acc = 0.0;
@@ -900,6 +974,7 @@ __device__ __forceinline__ void pg_warmup(const St &S, const double *G, int64_t 
     for (int a = tid; a < p; a += NT) S.u[a] += tmp[a];
   }
   __syncthreads();
+  snapshot(S, p);
 }
 
 // One refit per head.  polish: no new key; refine the last fit (p = t).
@@ -936,7 +1011,9 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
   const int np_in = S0 == 0 ? 0 : nn_np[h];
   double *Lg = nn_L + D.tri_off;
   int32_t *Pg = nn_P + D.t_off;
-  const St S = kGlobal ? carve_global(nn_vec + D.t_off * kNnlsVecPerSlot, Lg, Pg, int(D.t), &bk)
+  // global variant: maxp > 0 means the launch gave LDS for two vectors of maxp
+  double *lds_rows = (kGlobal && maxp > 0 && D.t <= maxp) ? reinterpret_cast<double *>(smem) : nullptr;
+  const St S = kGlobal ? carve_global(nn_vec + D.t_off * kNnlsVecPerSlot, Lg, Pg, int(D.t), &bk, lds_rows)
                        : carve_lds(smem, maxp, &bk);
   if (tid == 0) {
     sh_status = 0;
@@ -1043,8 +1120,12 @@ hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int kR, int 
     if (e != hipSuccess) return e;
   }
   if (dm.max_t > kNnlsLdsT) {
-    hipLaunchKernelGGL(k_nnls_cycle<true>, dim3(unsigned(dm.H)), dim3(NT), 0, s, b.desc, b.G, b.bvec, b.gA, b.w,
-                       cycle, kR, polish, np, 0, b.nn_L, b.nn_P, b.nn_np, b.nn_vec, b.tr_iters, b.tr_weight,
+    const size_t bytes = nnls_global_smem_bytes(dm.max_t);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_nnls_cycle<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(k_nnls_cycle<true>, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.bvec, b.gA, b.w,
+                       cycle, kR, polish, np, bytes ? int(dm.max_t) : 0, b.nn_L, b.nn_P, b.nn_np, b.nn_vec, b.tr_iters, b.tr_weight,
                        b.head_status);
     return hipGetLastError();
   }

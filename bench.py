@@ -106,8 +106,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=2)
-    ap.add_argument("--workload", type=int, default=2, choices=[1, 2],
-                    help="1: one 8-head layer, plain OMP; 2: 288-head stack, batched selection")
+    ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 4],
+                    help="1: one 8-head layer, plain OMP; 2: 288-head stack, batched selection; "
+                         "4: 288 heads with Dirichlet budgets 8..2048")
     ap.add_argument("--cpu-sample", type=int, default=3, help="oracle heads timed for the CPU baseline (0: skip)")
     ap.add_argument("--workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
     ap.add_argument("--no-timer", action="store_true", help="do not record per-kernel events")
@@ -165,9 +166,12 @@ def main():
         kernels = timer.summary()
         sw = kernels.get("sweep")
         if sw:
-            # algorithmic bytes of one sweep launch: every head's float32 Phi read once
-            per_launch = float(sum(w.n * w.T * 4 for _ in range(H)))
-            achieved = per_launch / (sw["avg_ms"] * 1e-3) / 1e9
+            # algorithmic bytes: each sweep launch reads the float32 Phi of every head that still
+            # selects keys in that cycle once; ceil(t_h / (k R)) launches touch head h per step
+            kr = w.topk * w.refit_every
+            per_step = float(sum(-(-b // kr) * w.n * w.T * 4 for b in w.budgets))
+            per_launch = per_step * args.steps / sw["launches"]
+            achieved = per_step * args.steps / (sw["total_ms"] * 1e-3) / 1e9
             traffic = read_traffic()
             roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                         "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -189,7 +193,9 @@ def main():
         "vs_baseline": None,
         "dtype": "f64",
         "data": "synthetic (seeded clustered Gaussians, bf16)",
-        "config": {"workload": w.name, "heads": H, "T": w.T, "n": w.n, "d": w.d, "budget": w.budgets[0],
+        "config": {"workload": w.name, "heads": H, "T": w.T, "n": w.n, "d": w.d,
+                   "budget": w.budgets[0] if len(set(w.budgets)) == 1 else
+                   f"{min(w.budgets)}..{max(w.budgets)} (sum {sum(w.budgets)})",
                    "topk": w.topk, "refit_every": w.refit_every, "parallelism": "none (one GPU)"},
         "roofline": roofline,
         "cpu_baseline": cpu,
