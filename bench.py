@@ -101,6 +101,83 @@ def cpu_baseline(idx: int, sample_heads: int):
             "sample": f"first {sample_heads} heads of the workload, float64 numpy/scipy oracle, {dt:.1f} s"}
 
 
+def _online_round_bits(job):
+    r, h = job
+    w = synth.online_workload()
+    head = w.initial([h])[0]
+    budget = max(1, int(round((w.L - w.keep_newest) * w.ratio)))
+    q, k, v = w.round_tokens(r, h, head.centres, w.L - budget - w.keep_newest)
+    return synth.bf16_bits(q), synth.bf16_bits(k), synth.bf16_bits(v)
+
+
+def bench_online(args):
+    """The online loop: every round compacts all 288 heads' prefixes (4076 keys
+    to 2038, carrying beta from the rounds before) and refills the cache."""
+    import torch
+
+    from attention_matching_least_amd import amc, online
+
+    dev = torch.device("cuda:0")
+    w = synth.online_workload()
+    H = w.num_heads
+    t_gen = time.perf_counter()
+    with ProcessPoolExecutor(max_workers=args.workers) as ex:
+        heads_bits = list(ex.map(_online_init_bits, range(H), chunksize=4))
+        rb = list(ex.map(_online_round_bits, [(r, h) for r in range(w.rounds) for h in range(H)], chunksize=4))
+    gen_s = time.perf_counter() - t_gen
+
+    def up(a):
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(dev)
+
+    K0 = torch.stack([up(b[0]) for b in heads_bits])
+    V0 = torch.stack([up(b[1]) for b in heads_bits])
+    Qr = [torch.stack([up(rb[r * H + h][0]) for h in range(H)]) for r in range(w.rounds)]
+    Kr = [torch.stack([up(rb[r * H + h][1]) for h in range(H)]) for r in range(w.rounds)]
+    Vr = [torch.stack([up(rb[r * H + h][2]) for h in range(H)]) for r in range(w.rounds)]
+    del rb, heads_bits
+    timer = None if args.no_timer else amc.Timer()
+
+    def run(tm):
+        cache = online.Cache(K0, V0, torch.zeros((H, w.L), dtype=torch.float32, device=dev))
+        return online.online_loop(cache, lambda r: Qr[r], lambda r, c: (Kr[r], Vr[r]), w.rounds,
+                                  keep_newest=w.keep_newest, ratio=w.ratio, topk=w.topk,
+                                  refit_every=w.refit_every, timer=tm)
+
+    for _ in range(args.warmup):
+        run(None)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        out = run(timer)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    status = np.concatenate([rd.result.head_status.cpu().numpy() for rd in out.rounds])
+    kernels = timer.summary() if timer else {}
+    print(json.dumps({
+        "metric": "KV heads re-compacted/sec, online loop (T=4076 -> 2038 per round, d=128)",
+        "value": round(H * w.rounds * args.steps / elapsed, 3),
+        "unit": "heads/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(1000.0 * elapsed / args.steps, 1),
+        "higher_is_better": True,
+        "dtype": "f64",
+        "data": "synthetic (seeded clustered Gaussians, bf16)",
+        "config": {"workload": w.name, "heads": H, "L": w.L, "n": w.n, "d": w.d, "rounds": w.rounds,
+                   "keep_newest": w.keep_newest, "ratio": w.ratio, "topk": w.topk,
+                   "refit_every": w.refit_every},
+        "kernels_ms": {k: round(v["total_ms"] / args.steps, 1) for k, v in kernels.items()},
+        "head_status_nonzero": int(np.count_nonzero(status)),
+        "input_generation_s": round(gen_s, 1),
+    }), flush=True)
+
+
+def _online_init_bits(h):
+    head = synth.online_workload().initial([h])[0]
+    return synth.bf16_bits(head.K), synth.bf16_bits(head.V)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -112,6 +189,9 @@ def main():
     ap.add_argument("--cpu-sample", type=int, default=3, help="oracle heads timed for the CPU baseline (0: skip)")
     ap.add_argument("--workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
     ap.add_argument("--no-timer", action="store_true", help="do not record per-kernel events")
+    ap.add_argument("--online", action="store_true",
+                    help="time the online re-compaction loop (288 heads, 4096-token cache, 6 rounds of 50%%, "
+                         "newest 20 kept) instead")
     args = ap.parse_args()
 
     if args.gpus != 1:
@@ -123,6 +203,9 @@ def main():
 
     from attention_matching_least_amd import amc
 
+    if args.online:
+        bench_online(args)
+        return
     dev = torch.device("cuda:0")
     t_gen = time.perf_counter()
     w, Qb, Kb, Vb = generate(args.workload, args.workers)

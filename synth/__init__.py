@@ -201,3 +201,49 @@ def scaled_workload(idx: int, num_heads: int, n: int, T: int, budget: int, d: Op
     return Workload(w.name + f"-scaled-H{num_heads}-n{n}-T{T}-t{budget}", num_heads, n, T,
                     w.d if d is None else d, [budget] * num_heads, w.topk, w.refit_every, w.dtype,
                     w.outliers, 100 + idx, w.description + " (scaled)")
+
+
+# ----------------------------------------------------------------------------
+# online re-compaction loop (the varlen stack's second workload)
+# ----------------------------------------------------------------------------
+@dataclass
+class OnlineWorkload:
+    """A fixed physical cache of L tokens per head, re-compacted `rounds`
+    times: each round compacts all but the newest `keep_newest` tokens by
+    `ratio` with n fresh reference queries, then fresh tokens refill it."""
+    name: str
+    num_heads: int
+    L: int
+    n: int
+    d: int
+    rounds: int
+    keep_newest: int
+    ratio: float
+    topk: int
+    refit_every: int
+    seed_root: int
+    dtype: str = "bf16"
+
+    def head_seeds(self):
+        return np.random.SeedSequence(self.seed_root).spawn(self.num_heads)
+
+    def initial(self, which: Optional[List[int]] = None) -> List[Head]:
+        """The starting caches: T = L tokens of each head (its queries are unused)."""
+        seeds = self.head_seeds()
+        idx = range(self.num_heads) if which is None else which
+        return [make_head(seeds[h], self.n, self.L, self.d, True, self.dtype) for h in idx]
+
+    def round_tokens(self, r: int, h: int, centres: np.ndarray, n_fresh: int):
+        """(Q, K_new, V_new) of round r for head h: the reference queries of
+        the round and the tokens decoded after it."""
+        return fresh_tokens(np.random.SeedSequence([self.seed_root, 2, r, h]), centres, self.n, n_fresh, True,
+                            self.dtype)
+
+
+def online_workload(num_heads: int = 288, L: int = 4096, n: int = 4096, d: int = 128, rounds: int = 6,
+                    seed_root: int = 4) -> OnlineWorkload:
+    """Default: 288 heads, a 4096-token cache, 6 rounds of 50% keeping the
+    newest 20 (so T = 4076 -> t = 2038 per round), n = 4096, top-k 4, refit
+    every 2 iterations, bf16."""
+    return OnlineWorkload(f"qwen3-4b-stack-online-L{L}-x{rounds}", num_heads, L, n, d, rounds, 20, 0.5, 4, 2,
+                          seed_root)
