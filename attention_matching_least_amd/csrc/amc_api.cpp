@@ -165,8 +165,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.sum_T = TT;
   const uint64_t phi_bytes = uint64_t(phi) * 4;
   if (!features_only) {
-    pl.store_phi = phi_bytes <= o->phi_budget_bytes;
-    if (!pl.store_phi) return AMC_ERR_UNSUPPORTED;  // recompute-mode sweep not in this build
+    pl.store_phi = phi_bytes <= o->phi_budget_bytes;  // else every sweep recomputes Phi
   }
 
   uint64_t off = 0;
@@ -182,7 +181,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     pl.total = off;
     return AMC_OK;
   }
-  pl.o_phi = take(phi_bytes);
+  pl.o_phi = take(pl.store_phi ? phi_bytes : 0);
   pl.o_m = take(8ull * nn);
   pl.o_r = take(8ull * nn);
   pl.o_mhat = take(8ull * nn);
@@ -399,9 +398,10 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.sel_slot, pl.sum_T, 0, stream));
   if (head_status) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(head_status, dm.H, 0, stream));
   AMC_LAUNCH(AMC_K_SHIFT, launch_shift(dm, b, stream));
-  AMC_LAUNCH(AMC_K_PHI, launch_phi(dm, b, 1, stream));
+  AMC_LAUNCH(AMC_K_PHI, launch_phi(dm, b, pl.store_phi ? 1 : 0, stream));
   for (int c = 0; c < pl.max_cycles; ++c) {
-    AMC_LAUNCH(AMC_K_SWEEP, launch_sweep(dm, b, c, pl.kR, stream));
+    AMC_LAUNCH(AMC_K_SWEEP, pl.store_phi ? launch_sweep(dm, b, c, pl.kR, stream)
+                                         : launch_sweep_rc(dm, b, c, pl.kR, stream));
     AMC_LAUNCH(AMC_K_MERGE, launch_merge(dm, b, c, pl.kR, stream));
     AMC_LAUNCH(AMC_K_PANEL, launch_panel(dm, b, c, pl.kR, stream));
     AMC_LAUNCH(AMC_K_GRAM, launch_gram(dm, b, c, pl.kR, 0, stream));

@@ -103,6 +103,7 @@ hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t
 hipError_t launch_shift(const Dims &dm, const Buffers &b, hipStream_t s);
 hipError_t launch_phi(const Dims &dm, const Buffers &b, int store_phi, hipStream_t s);
 hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_merge(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);

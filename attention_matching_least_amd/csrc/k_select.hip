@@ -29,13 +29,14 @@ __device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
   return va > vb || (va == vb && ia < ib);
 }
 
-// Sorts 256 (value, index) pairs in LDS, best first (value descending, index ascending).
+// Sorts 256 (value, index) pairs in LDS, best first (value descending, index
+// ascending).  Threads at or above 256 only take part in the barriers.
 __device__ void block_sort256(double *v, int *ix) {
   const int tid = threadIdx.x;
   for (int k = 2; k <= 256; k <<= 1) {
     for (int j = k >> 1; j > 0; j >>= 1) {
       const int p = tid ^ j;
-      if (p > tid) {
+      if (tid < 256 && p > tid) {
         const double va = v[tid], vb = v[p];
         const int ia = ix[tid], ib = ix[p];
         const bool first_better = better(va, ia, vb, ib);
@@ -132,6 +133,150 @@ __global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc
   block_sort256(sv, si);
   if (tid <= Kc) {
     const int64_t o = (D.cblk_off + blk) * KP_STRIDE + tid;
+    cand_val[o] = sv[tid];
+    cand_idx[o] = si[tid];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// recompute sweep (Phi not stored): the same scores c_j = r^T Phi[:, j], with
+// each Phi tile rebuilt from Q and K as the mass-feature stage builds it:
+// float64 MFMA logits S^T = K Q^T from the exact inputs and a float64 exp
+// (the scores are summed from the float64 Phi, before any float32 rounding).
+// One block = 256 keys of one head in 8 waves of 32 keys; each wave keeps its
+// keys' MFMA operands in registers and the queries stream through LDS 64 at
+// a time.
+// ---------------------------------------------------------------------------
+typedef double f64x4 __attribute__((ext_vector_type(4)));
+constexpr int RC_THREADS = 512;
+
+template <typename T>
+struct InRc;
+template <>
+struct InRc<uint16_t> {
+  __device__ static float f(uint16_t v) { return __uint_as_float(uint32_t(v) << 16); }
+};
+template <>
+struct InRc<float> {
+  __device__ static float f(float v) { return v; }
+};
+
+template <int D, bool BF16>
+__global__ __launch_bounds__(RC_THREADS) void k_sweep_rc(
+    const HeadDesc *__restrict__ desc, const void *__restrict__ Qv, const void *__restrict__ Kv,
+    const float *__restrict__ beta_in, double scale, const double *__restrict__ shift, const double *__restrict__ r,
+    const int32_t *__restrict__ sel_slot, int cycle, int kR, double *__restrict__ cand_val,
+    int32_t *__restrict__ cand_idx, int32_t *__restrict__ head_status) {
+  using E = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int NS = D / 4;    // MFMA k-steps over the head dimension
+  constexpr int QT = 64;       // queries per LDS stage
+  constexpr int QSTR = D + 4;  // elements per staged query row
+  constexpr int KB = 2;        // 16-key tiles per wave
+  static_assert(RC_THREADS / 64 * KB * 16 == kSweepCols, "one block covers one sweep column block");
+  __shared__ __attribute__((aligned(16))) E qs[QT * QSTR];
+  __shared__ double rs[QT];
+  __shared__ double sv[256];
+  __shared__ int si[256];
+  const E *Q = static_cast<const E *>(Qv);
+  const E *K = static_cast<const E *>(Kv);
+  const int h = blockIdx.y;
+  const HeadDesc Dh = desc[h];
+  const int blk = blockIdx.x;
+  if (blk >= Dh.n_cblk) return;
+  int64_t S0;
+  const int Kc = cycle_keys(Dh, cycle, kR, &S0);
+  if (Kc == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const double s = shift[h];
+  const int64_t kbase = int64_t(blk) * kSweepCols + wave * (KB * 16);
+  // A operands: key kbase + 16 kb + c16, head dims 16 u + 4 g + v at k-step 4 u + v
+  double kf[KB][NS];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) {
+    const int64_t key = kbase + kb * 16 + c16;
+#pragma unroll
+    for (int u = 0; u < NS / 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        kf[kb][4 * u + v] = key < Dh.T ? double(InRc<E>::f(K[(Dh.k_off + key) * D + 16 * u + 4 * g + v])) : 0.0;
+  }
+  // output rows of tile kb: key kbase + 16 kb + g + 4 e (keys past T contribute exp(-inf) = 0)
+  double bb[KB][4], sc[KB][4];
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t key = kbase + kb * 16 + g + 4 * e;
+      bb[kb][e] = key < Dh.T ? (beta_in ? double(beta_in[Dh.k_off + key]) : 0.0) : -INFINITY;
+      sc[kb][e] = 0.0;
+    }
+
+  for (int64_t i0 = 0; i0 < Dh.n; i0 += QT) {
+    __syncthreads();
+    for (int gi = tid; gi < QT * D / 4; gi += RC_THREADS) {
+      const int qq = gi / (D / 4), c4 = gi % (D / 4);
+      const bool ok = i0 + qq < Dh.n;
+      const int64_t src = (Dh.q_off + i0 + qq) * D + 4 * c4;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) qs[qq * QSTR + 4 * c4 + e] = ok ? Q[src + e] : E(0);
+    }
+    if (tid < QT) rs[tid] = i0 + tid < Dh.n ? r[Dh.n_off + i0 + tid] : 0.0;
+    __syncthreads();
+#pragma unroll 1
+    for (int qt = 0; qt < QT / 16; ++qt) {
+      f64x4 acc[KB];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) acc[kb] = f64x4{0.0, 0.0, 0.0, 0.0};
+      const E *qp = &qs[(qt * 16 + c16) * QSTR + 4 * g];
+#pragma unroll
+      for (int u = 0; u < NS / 4; ++u)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const double bq = double(InRc<E>::f(qp[16 * u + v]));
+#pragma unroll
+          for (int kb = 0; kb < KB; ++kb)
+            acc[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(kf[kb][4 * u + v], bq, acc[kb], 0, 0, 0);
+        }
+      // output column c16 is query i0 + 16 qt + c16
+      const double rq = rs[qt * 16 + c16];
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) sc[kb][e] = fma(rq, exp(scale * acc[kb][e] + bb[kb][e] - s), sc[kb][e]);
+    }
+  }
+  // sum over the 16 query columns of each lane group, then one score per key
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      double v = sc[kb][e];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      if (c16 == 0) sv[wave * (KB * 16) + kb * 16 + g + 4 * e] = v;
+    }
+  __syncthreads();
+  if (tid < 256) {
+    const int64_t col = int64_t(blk) * kSweepCols + tid;
+    double c = sv[tid];
+    int idx = int(col);
+    if (col >= Dh.T || sel_slot[Dh.k_off + col] != 0) {
+      c = -INFINITY;
+      idx = INT_MAX;
+    } else if (!isfinite(c)) {
+      if (head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
+      c = -DBL_MAX;  // still a valid, selectable key
+    }
+    sv[tid] = c;
+    si[tid] = idx;
+  }
+  __syncthreads();
+  block_sort256(sv, si);
+  if (tid <= Kc) {
+    const int64_t o = (Dh.cblk_off + blk) * KP_STRIDE + tid;
     cand_val[o] = sv[tid];
     cand_idx[o] = si[tid];
   }
@@ -403,6 +548,21 @@ __global__ __launch_bounds__(256) void k_resid(const HeadDesc *__restrict__ desc
 hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
   hipLaunchKernelGGL(k_sweep, dim3(unsigned(dm.max_cblk), unsigned(dm.H)), dim3(256), 0, s, b.desc, b.phi, b.r,
                      b.sel_slot, cycle, kR, b.cand_val, b.cand_idx, b.head_status);
+  return hipGetLastError();
+}
+
+hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  dim3 grid(unsigned(dm.max_cblk), unsigned(dm.H));
+#define AMC_RC_ARGS b.desc, b.Q, b.K, b.beta_in, dm.scale, b.shift, b.r, b.sel_slot, cycle, kR, b.cand_val, b.cand_idx, \
+    b.head_status
+  if (dm.d == 128) {
+    if (dm.in_bf16) hipLaunchKernelGGL((k_sweep_rc<128, true>), grid, dim3(RC_THREADS), 0, s, AMC_RC_ARGS);
+    else hipLaunchKernelGGL((k_sweep_rc<128, false>), grid, dim3(RC_THREADS), 0, s, AMC_RC_ARGS);
+  } else {
+    if (dm.in_bf16) hipLaunchKernelGGL((k_sweep_rc<64, true>), grid, dim3(RC_THREADS), 0, s, AMC_RC_ARGS);
+    else hipLaunchKernelGGL((k_sweep_rc<64, false>), grid, dim3(RC_THREADS), 0, s, AMC_RC_ARGS);
+  }
+#undef AMC_RC_ARGS
   return hipGetLastError();
 }
 

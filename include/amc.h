@@ -116,7 +116,8 @@ typedef struct {
   int32_t nnls_max_iters; /* active-set iteration cap per refit (0 = 3 * budget + 30) */
   int32_t nnls_polish;    /* refinement refits after the last key (default 1) */
   double nnls_tol;        /* KKT tolerance relative to max |b| in unit-diagonal form (0 = 10 eps t) */
-  uint64_t phi_budget_bytes; /* Phi is stored when sum_h n_h T_h * 4 <= this */
+  uint64_t phi_budget_bytes; /* Phi is stored when sum_h n_h T_h * 4 <= this; else every
+                              * sweep recomputes its Phi tiles from Q and K (same scores) */
   amc_dtype cv_dtype;     /* C_v output type (default AMC_F32) */
   uint32_t flags;         /* AMC_FLAG_* */
   void *timer;            /* optional amc_timer_create() handle; NULL = none */

@@ -125,16 +125,18 @@ def test_compact_argument_errors_return_before_any_launch():
     assert st == amc.AMC_ERR_WORKSPACE
 
 
-def test_large_budget_and_phi_budget_limits():
+def test_budget_limit_and_phi_budget():
     # budgets above the largest supported budget are reported as unsupported
     p, keep = _problem(T=(20000, 200), t=(16385, 5))
     o = amc.make_options()
     out = ctypes.c_uint64(0)
     assert amc.lib().amc_workspace_size(ctypes.byref(p), ctypes.byref(o), ctypes.byref(out)) == amc.AMC_ERR_UNSUPPORTED
-    # a Phi budget below the problem's Phi asks for the recompute mode
+    # a Phi budget below the problem's Phi selects the recompute sweep: no Phi in the workspace
     p, keep = _problem()
+    stored = amc.workspace_size(p, amc.make_options())
     o = amc.make_options(phi_budget_bytes=1024)
-    assert amc.lib().amc_workspace_size(ctypes.byref(p), ctypes.byref(o), ctypes.byref(out)) == amc.AMC_ERR_UNSUPPORTED
+    assert amc.lib().amc_workspace_size(ctypes.byref(p), ctypes.byref(o), ctypes.byref(out)) == amc.AMC_OK
+    assert stored - out.value >= 4 * (100 * 300 + 50 * 200)
 
 
 def test_nnls_entry_validation():
