@@ -149,7 +149,8 @@ struct Blk {
   double cs[2 * TB];         // rotations of one block of the rank-one update
   int cand[NB];              // entering candidates
   int accb[NB];              // accepted candidates, in order
-  int ctl[8];                // [1], [4] scan state, [2] accepted count, [3] enter one at a time
+  int ctl[8];                // [1], [4] scan state, [2] accepted count, [3] largest entering block,
+                             // [5] size of the last entering block
   int wc[NW];                // per-wave counts of a compaction
   int np;                    // free-set size
 };
@@ -725,7 +726,8 @@ __device__ __forceinline__ void block_append(const St &S, const double *G, int64
 //  - An entering variable whose solution is not positive leaves again before
 //    any step is taken.  If it entered alone it is set aside for the rest of
 //    this fit (Lawson and Hanson's guard against cycling on round-off);
-//    otherwise ctl[3] is raised so that later candidates enter one at a time.
+//    otherwise later blocks of candidates are half as large (ctl[3]; one at
+//    a time once it reaches 1).
 //  - Otherwise the iterate moves toward the solution, as far as feasibility
 //    allows, and the variables that reach zero leave.
 // Only the free-set rows of g change here (by the factor's model); y follows
@@ -773,7 +775,7 @@ __device__ __forceinline__ void settle(const St &S, int p, bool have_y, bool sin
         if (q < 0) break;
         if (tid == 0) {
           S.flag[S.plist[q]] = single ? F_BLOCKED : 0;
-          if (!single) bk->ctl[3] = 1;
+          if (!single) bk->ctl[3] = bk->ctl[5] > 1 ? bk->ctl[5] / 2 : 1;
         }
         __syncthreads();
         remove_at(S, q);
@@ -891,13 +893,14 @@ __device__ __forceinline__ void nnls_core(const St &S, const double *G, int64_t 
   settle(S, p, false, false, red);
   for (;;) {
     sync_z(S, G, ld, p);
-    const int nc = pick_candidates(S, p, tol, bk->ctl[3] ? 1 : NB, red);
+    const int nc = pick_candidates(S, p, tol, bk->ctl[3], red);
     if (nc == 0) break;
     if (iters >= cap) {
       if (tid == 0) *status |= int(AMC_HS_NNLS_CAP);
       break;
     }
     ++iters;
+    if (tid == 0) bk->ctl[5] = nc;
     block_append(S, G, ld, nc, status);
     if (bk->ctl[2] > 0) settle(S, p, true, nc == 1, red);
   }
@@ -1018,7 +1021,7 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
   if (tid == 0) {
     sh_status = 0;
     bk.np = np_in;
-    bk.ctl[3] = 0;
+    bk.ctl[3] = NB;
   }
   if (!kGlobal) {
     // bring the persisted factor into LDS, eight loads in flight per thread
@@ -1085,7 +1088,7 @@ __global__ __launch_bounds__(NT) void k_nnls_batched(NnlsChunk ch, int base, con
   if (threadIdx.x == 0) {
     sh_status = 0;
     bk.np = 0;
-    bk.ctl[3] = 0;
+    bk.ctl[3] = NB;
   }
   __syncthreads();
   const double tol = nnls_setup(S, Gi, p, p, g + t0, nullptr, w + t0, warm ? p : 0, prm, &red);
