@@ -273,6 +273,9 @@ def main():
                     help="1: one 8-head layer, plain OMP; 2: 288-head stack, batched selection; "
                          "3: 60k-token stack (key-selection seconds, Phi recomputed); "
                          "4: 288 heads with Dirichlet budgets 8..2048")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="only run three device-to-device copies of BYTES (the reference kernel for "
+                         "scaling HBM byte counters)")
     ap.add_argument("--heads", type=int, default=0, help="workload 3: heads to run (0: all 288)")
     ap.add_argument("--head-batch", type=int, default=48, help="workload 3: heads per compaction call")
     ap.add_argument("--cpu-sample", type=int, default=3, help="oracle heads timed for the CPU baseline (0: skip)")
@@ -292,6 +295,14 @@ def main():
 
     from attention_matching_least_amd import amc
 
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration, dtype=torch.uint8, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": args.copy_calibration, "copies": 3}), flush=True)
+        return
     if args.online:
         bench_online(args)
         return
