@@ -418,20 +418,24 @@ __global__ __launch_bounds__(256) void k_panel(const HeadDesc *__restrict__ desc
 }
 
 // ---------------------------------------------------------------------------
-// gram: G[a][b] and G[b][a] for a < S0 + Kc, b in the new slots; b_b = Phi_b^T m;
-// and gA[a] = Phi_a^T r for every a < S0 + Kc, the gradient of the NNLS at the
-// previous weights computed from the float64 panel and residual.
-// One block = 64 rows a (the row index a == S0 + Kc stands for m) x 16 new
-// columns; the blocks of the first column tile also carry the r column.
-// polish: no new column, gA over all t slots.
+// gram: dot products over the n queries of the rows [panel rows 0..Snew-1, m]
+// with the columns [new keys S0..Snew-1, r], on float64 MFMA
+// (v_mfma_f64_16x16x4f64).  They give the new columns of G = Phi_S^T Phi_S
+// (written to both halves), b = Phi_S^T m for the new keys (the m row), and
+// gA = Phi_S^T r (the r column).  polish: no new key, only the r column.
+// One block = 64 rows x 16 columns, the queries staged through LDS 64 at a
+// time; each wave takes 16 rows.
 // ---------------------------------------------------------------------------
+typedef double f64x4g __attribute__((ext_vector_type(4)));
+
 __global__ __launch_bounds__(256) void k_gram(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
                                               const double *__restrict__ m, const double *__restrict__ r, int cycle,
                                               int kR, int polish, double *__restrict__ G, double *__restrict__ bvec,
                                               double *__restrict__ gA) {
-  constexpr int CH = 64;
-  __shared__ double xs[64][CH + 1];
-  __shared__ double zs[17][CH + 1];
+  constexpr int CH = 64;       // queries per LDS stage
+  constexpr int STR = CH + 1;  // padded row, in doubles
+  __shared__ double xs[64 * STR];
+  __shared__ double zs[16 * STR];
   const int h = blockIdx.z;
   const HeadDesc D = desc[h];
   int64_t S0;
@@ -444,20 +448,22 @@ __global__ __launch_bounds__(256) void k_gram(const HeadDesc *__restrict__ desc,
     if (Kc == 0) return;
   }
   const int64_t Snew = S0 + Kc;
+  const int64_t nrows = Kc > 0 ? Snew + 1 : Snew;  // row Snew is m
+  const int ncols = Kc + 1;                         // column Kc is r
   const int64_t a0 = int64_t(blockIdx.x) * 64;
-  const int b0 = blockIdx.y * 16;
-  const bool rcol = blockIdx.y == 0;
-  // rows a <= Snew when there are new columns (a == Snew is m), a < Snew otherwise
-  const int64_t rows = Kc > 0 ? Snew + 1 : Snew;
-  if (a0 >= rows || (b0 >= Kc && !rcol)) return;
-  const int tid = threadIdx.x;
-  const int ta = tid >> 2, tb = (tid & 3) * 4;
+  const int c0 = blockIdx.y * 16;
+  if (a0 >= nrows || c0 >= ncols) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
   const double *P = panel + D.panel_off;
   const int64_t n = D.n;
-  double acc[4] = {0.0, 0.0, 0.0, 0.0};
-  double accr = 0.0;
-  for (int64_t i0 = 0; i0 < n; i0 += CH) {
-    for (int e = tid; e < 64 * CH; e += 256) {
+  // each thread stages 16 row values and 4 column values per LDS stage; the
+  // next stage's loads are issued before the current stage's MFMAs
+  double xr[16], zr[4];
+  auto fetch = [&](int64_t i0) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = tid + 256 * u;
       const int rr = e / CH, c = e % CH;
       const int64_t a = a0 + rr, i = i0 + c;
       double v = 0.0;
@@ -465,46 +471,62 @@ __global__ __launch_bounds__(256) void k_gram(const HeadDesc *__restrict__ desc,
         if (a < Snew) v = P[a * n + i];
         else if (a == Snew && Kc > 0) v = m[D.n_off + i];
       }
-      xs[rr][c] = v;
+      xr[u] = v;
     }
-    for (int e = tid; e < 17 * CH; e += 256) {
-      const int rr = e / CH, c = e % CH;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u;
+      const int cc = e / CH, c = e % CH;
+      const int col = c0 + cc;
       const int64_t i = i0 + c;
       double v = 0.0;
       if (i < n) {
-        if (rr < 16) {
-          if (b0 + rr < Kc) v = P[(S0 + b0 + rr) * n + i];
-        } else if (rcol) {
-          v = r[D.n_off + i];
-        }
+        if (col < Kc) v = P[(S0 + col) * n + i];
+        else if (col == Kc) v = r[D.n_off + i];
       }
-      zs[rr][c] = v;
+      zr[u] = v;
     }
+  };
+  static_assert(64 * CH == 16 * 256 && 16 * CH == 4 * 256, "stage sizes");
+  f64x4g acc = {0.0, 0.0, 0.0, 0.0};
+  fetch(0);
+  for (int64_t i0 = 0; i0 < n; i0 += CH) {
     __syncthreads();
-#pragma unroll 4
-    for (int c = 0; c < CH; ++c) {
-      const double x = xs[ta][c];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[q] = fma(x, zs[tb + q][c], acc[q]);
-      accr = fma(x, zs[16][c], accr);
+    for (int u = 0; u < 16; ++u) {
+      const int e = tid + 256 * u;
+      xs[(e / CH) * STR + e % CH] = xr[u];
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int e = tid + 256 * u;
+      zs[(e / CH) * STR + e % CH] = zr[u];
     }
     __syncthreads();
+    if (i0 + CH < n) fetch(i0 + CH);
+    const double *xa = &xs[(wave * 16 + c16) * STR + g];
+    const double *zb = &zs[c16 * STR + g];
+#pragma unroll
+    for (int k = 0; k < CH / 4; ++k) acc = __builtin_amdgcn_mfma_f64_16x16x4f64(xa[4 * k], zb[4 * k], acc, 0, 0, 0);
   }
-  const int64_t a = a0 + ta;
+  // element e of lane group g holds row wave*16 + g + 4e, column c16
   const int64_t ld = D.t;
+  const int col = c0 + c16;
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int bl = b0 + tb + q;
-    if (bl >= Kc) continue;
-    const int64_t b = S0 + bl;
-    if (a < Snew) {
-      G[D.tt_off + a * ld + b] = acc[q];
-      G[D.tt_off + b * ld + a] = acc[q];
-    } else if (a == Snew) {
-      bvec[D.t_off + b] = acc[q];
+  for (int e = 0; e < 4; ++e) {
+    const int64_t a = a0 + wave * 16 + g + 4 * e;
+    if (col < Kc) {
+      const int64_t b = S0 + col;
+      if (a < Snew) {
+        G[D.tt_off + a * ld + b] = acc[e];
+        G[D.tt_off + b * ld + a] = acc[e];
+      } else if (a == Snew) {
+        bvec[D.t_off + b] = acc[e];
+      }
+    } else if (col == Kc && a < Snew) {
+      gA[D.t_off + a] = acc[e];
     }
   }
-  if (rcol && (tid & 3) == 0 && a < Snew) gA[D.t_off + a] = accr;
 }
 
 // ---------------------------------------------------------------------------
@@ -587,9 +609,9 @@ hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int kR, hip
 }
 
 hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int kR, int polish, hipStream_t s) {
-  // rows a in [0, S0 + Kc], so up to max_t + 1 rows; new columns up to kR
+  // rows [0, S0 + Kc] (the last is m), so up to max_t + 1; columns: up to kR new keys and r
   const int64_t rows = dm.max_t + 1;
-  dim3 grid(unsigned((rows + 63) / 64), unsigned(polish ? 1 : (kR + 15) / 16), unsigned(dm.H));
+  dim3 grid(unsigned((rows + 63) / 64), unsigned(polish ? 1 : (kR + 1 + 15) / 16), unsigned(dm.H));
   hipLaunchKernelGGL(k_gram, grid, dim3(256), 0, s, b.desc, b.panel, b.m, b.r, cycle, kR, polish, b.G, b.bvec, b.gA);
   return hipGetLastError();
 }
