@@ -149,10 +149,9 @@ struct In<float> {
 // i / 4 (rows interleaved across the lane groups).  With S^T = K Q^T the rows
 // are keys, so lane group g, element e of key block kb holds this key:
 __device__ __forceinline__ int phi_key(int kb, int g, int e) { return kb * 16 + g + 4 * e; }
-// The Phi V product consumes those values as its A operand at k-step (kb, e),
-// so V is stored transposed with each 16-key block permuted to make the four
-// keys a lane needs (phi_key(kb, g, 0..3)) contiguous.
-__device__ __forceinline__ int vt_pos(int key) { return (key & ~15) | ((key & 3) << 2) | ((key >> 2) & 3); }
+// The Phi V product consumes those values as its A operand at k-step (kb, e)
+// (A[query][k = g]); its B operand B[k = g][dim] is then V[phi_key(kb, g, e)][dim],
+// a row of the V tile, read directly.
 
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, const void *__restrict__ Qv,
@@ -163,11 +162,11 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
                                              double *__restrict__ m_out, double *__restrict__ r_out,
                                              float *__restrict__ Y_out, int32_t *__restrict__ head_status) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;
-  constexpr int KSTR = D + 4;   // elements per K row in LDS
-  constexpr int VSTR = 64 + 4;  // elements per transposed V row in LDS
+  constexpr int KSTR = D + 16 / int(sizeof(E));  // elements per K / V row in LDS (16-byte pad)
   constexpr int NU = D / 16;
+  constexpr int VEC = 16 / int(sizeof(E));         // elements per 16-byte access
   __shared__ __attribute__((aligned(16))) E ks[64 * KSTR];
-  __shared__ __attribute__((aligned(16))) E vt[D * VSTR];
+  __shared__ __attribute__((aligned(16))) E vs[64 * KSTR];
   __shared__ float sbias[64];
   __shared__ double s_shift;
   const E *Q = static_cast<const E *>(Qv);
@@ -213,17 +212,18 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
 
   for (int64_t k0 = 0; k0 < Dh.T; k0 += kPhiKeys) {
     __syncthreads();
-    // K tile [64][D] and V tile transposed [D][64], zero beyond T
-    for (int gi = tid; gi < 64 * D / 4; gi += 256) {
-      const int key = gi / (D / 4), c4 = gi % (D / 4);
+    // K and V tiles [64][D], zero beyond T, 16 bytes per access
+    for (int gi = tid; gi < 64 * D / VEC; gi += 256) {
+      const int key = gi / (D / VEC), cv = gi % (D / VEC);
       const bool ok = k0 + key < Dh.T;
-      const int64_t src = (Dh.k_off + k0 + key) * D + 4 * c4;
-      const int vkey = vt_pos(key);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        ks[key * KSTR + 4 * c4 + e] = ok ? K[src + e] : E(0);
-        vt[(4 * c4 + e) * VSTR + vkey] = ok ? V[src + e] : E(0);
+      const int64_t src = (Dh.k_off + k0 + key) * D + VEC * cv;
+      uint4 kq = make_uint4(0, 0, 0, 0), vq = make_uint4(0, 0, 0, 0);
+      if (ok) {
+        kq = *reinterpret_cast<const uint4 *>(K + src);
+        vq = *reinterpret_cast<const uint4 *>(V + src);
       }
+      *reinterpret_cast<uint4 *>(&ks[key * KSTR + VEC * cv]) = kq;
+      *reinterpret_cast<uint4 *>(&vs[key * KSTR + VEC * cv]) = vq;
     }
     if (tid < 64) sbias[tid] = (k0 + tid < Dh.T && beta_in) ? beta_in[Dh.k_off + k0 + tid] : 0.0f;
     __syncthreads();
@@ -249,14 +249,61 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
         if (prow && k0 + kl < Dh.T) prow[k0 + kl] = pf[kb][e];
       }
     }
+    if constexpr (BF16) {
+      // U += Phi V on bf16 MFMA (16x16x32): Phi = hi + mid + lo exactly in
+      // three bf16 terms (24 significant bits, float32's), V is exact bf16,
+      // products are exact in float32 and accumulate in float32.  Reduction
+      // index k = 8 g + 4 j + e of chunk c is key phi_key(2 c + j, g, e).
 #pragma unroll
-    for (int db = 0; db < NU; ++db) {
+      for (int c = 0; c < 2; ++c) {
+        uint32_t w[3][4];
 #pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const E *vp = &vt[(db * 16 + c16) * VSTR + kb * 16 + 4 * g];
+        for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-          uacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(pf[kb][e], In<E>::f(vp[e]), uacc[db], 0, 0, 0);
+          for (int e2 = 0; e2 < 2; ++e2) {
+            uint32_t t[3][2];
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              const float x = pf[2 * c + j][2 * e2 + h2];
+              const uint32_t hi = f32_to_bf16_bits(x);
+              const float r1 = x - bf16_bits_to_f32(hi);
+              const uint32_t mi = f32_to_bf16_bits(r1);
+              const uint32_t lo = f32_to_bf16_bits(r1 - bf16_bits_to_f32(mi));
+              t[0][h2] = hi;
+              t[1][h2] = mi;
+              t[2][h2] = lo;
+            }
+#pragma unroll
+            for (int q = 0; q < 3; ++q) w[q][2 * j + e2] = t[q][0] | (t[q][1] << 16);
+          }
+#pragma unroll
+        for (int db = 0; db < NU; ++db) {
+          uint32_t bv[4];
+#pragma unroll
+          for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int e2 = 0; e2 < 2; ++e2) {
+              const uint32_t v0 = vs[phi_key(2 * c + j, g, 2 * e2) * KSTR + db * 16 + c16];
+              const uint32_t v1 = vs[phi_key(2 * c + j, g, 2 * e2 + 1) * KSTR + db * 16 + c16];
+              bv[2 * j + e2] = v0 | (v1 << 16);
+            }
+          const bf16x8 b = as_bf16x8(make_uint4(bv[0], bv[1], bv[2], bv[3]));
+#pragma unroll
+          for (int q = 2; q >= 0; --q)
+            uacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(make_uint4(w[q][0], w[q][1], w[q][2], w[q][3])),
+                                                               b, uacc[db], 0, 0, 0);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int db = 0; db < NU; ++db) {
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            uacc[db] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                pf[kb][e], In<E>::f(vs[phi_key(kb, g, e) * KSTR + db * 16 + c16]), uacc[db], 0, 0, 0);
+        }
       }
     }
   }
