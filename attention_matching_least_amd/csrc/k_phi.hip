@@ -167,6 +167,8 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
   constexpr int VEC = 16 / int(sizeof(E));         // elements per 16-byte access
   __shared__ __attribute__((aligned(16))) E ks[64 * KSTR];
   __shared__ __attribute__((aligned(16))) E vs[64 * KSTR];
+  constexpr int PSTR = 64 + 4;  // floats per staged Phi row
+  __shared__ __attribute__((aligned(16))) float ps[4][16 * PSTR];  // per wave: 16 queries x 64 keys
   __shared__ float sbias[64];
   __shared__ double s_shift;
   const E *Q = static_cast<const E *>(Qv);
@@ -208,7 +210,6 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
 #pragma unroll
   for (int i = 0; i < NU; ++i) uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
   double msum = 0.0;
-  float *prow = (phi && qvalid) ? phi + Dh.phi_off + q * Dh.ldT : nullptr;
 
   for (int64_t k0 = 0; k0 < Dh.T; k0 += kPhiKeys) {
     __syncthreads();
@@ -246,7 +247,23 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
         if (k0 + kl < Dh.T) p = exp(scale * acc[e] + double(sbias[kl]) - s);
         msum += p;
         pf[kb][e] = float(p);
-        if (prow && k0 + kl < Dh.T) prow[k0 + kl] = pf[kb][e];
+        if (phi) ps[wave][c16 * PSTR + kl] = pf[kb][e];
+      }
+    }
+    if (phi) {
+      // the wave's 16 x 64 Phi tile leaves as 16-byte row segments (ldT is a
+      // multiple of 4, so a segment that starts below ldT ends within the row)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        const int row = (lane >> 4) + 4 * it, col = 4 * (lane & 15);
+        const int64_t qr = q0 + row;
+        if (qr < Dh.n && k0 + col < Dh.ldT) {
+          const f32x4 v = *reinterpret_cast<const f32x4 *>(&ps[wave][row * PSTR + col]);
+          __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(phi + Dh.phi_off + qr * Dh.ldT + k0 + col));
+        }
       }
     }
     if constexpr (BF16) {
