@@ -1,7 +1,9 @@
-"""Builds libamc.so (HIP, gfx950) in-tree.
+"""Builds libamc.so (HIP, gfx950) in-tree, and the peak probe ``amc_peaks``.
 
 Each source is compiled to an object under ``_build/`` in parallel, then the
 objects are linked into ``attention_matching_least_amd/libamc.so``.
+``amc_peaks`` (peaks/peaks.hip) measures the MFMA, vector and HBM rates the
+roofline figures are compared with.
 """
 from __future__ import annotations
 
@@ -17,6 +19,8 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libamc.so")
+PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
+PEAKS = os.path.join(PKG, "amc_peaks")
 
 SOURCES = ["amc_api.cpp", "k_phi.hip", "k_select.hip", "k_nnls.hip", "k_ols.hip"]
 
@@ -55,8 +59,12 @@ def build(verbose: bool = False) -> str:
     if res.returncode != 0:
         raise RuntimeError(f"link failed:\n{res.stdout}\n{res.stderr}")
     os.replace(tmp, LIB)
+    res = subprocess.run([HIPCC, *COMMON, "-x", "hip", PEAKS_SRC, "-o", PEAKS + ".tmp"], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the peak probe:\n{res.stdout}\n{res.stderr}")
+    os.replace(PEAKS + ".tmp", PEAKS)
     if verbose:
-        print(f"built {LIB}")
+        print(f"built {LIB} and {PEAKS}")
     return LIB
 
 

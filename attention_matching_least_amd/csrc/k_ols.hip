@@ -32,70 +32,94 @@ __device__ __forceinline__ void decode_tri(int e, int *r, int *c) {
 }
 
 // ---------------------------------------------------------------------------
-// normal equations: N = At At^T and rhs = At Y with At[a][i] = P[a][i] w_a / mhat_i.
-// Block tile: 64 rows a x 64 columns b, b < t -> N, b >= t -> rhs column b - t.
+// normal equations: N = At At^T and rhs = At Y with At[a][i] = P[a][i] w_a / mhat_i,
+// formed as N[a][b] = w_a w_b sum_i X[a][i] X[b][i] and rhs[a][d] = w_a sum_i
+// X[a][i] Y[i][d] with X[a][i] = P[a][i] / mhat_i, on float64 MFMA.
+// Block tile: 64 rows a x 64 columns b (b < t: N, b >= t: rhs column b - t);
+// each wave takes 16 rows; the queries are staged through LDS 64 at a time,
+// the next stage prefetched into registers.
 // ---------------------------------------------------------------------------
+typedef double f64x4o __attribute__((ext_vector_type(4)));
+
 template <int D>
 __global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
                                                    const double *__restrict__ w, const double *__restrict__ mhat,
                                                    const float *__restrict__ Y, double *__restrict__ N,
                                                    double *__restrict__ rhs) {
-  constexpr int CH = 32;
-  __shared__ double xs[64][CH + 1];
-  __shared__ double zs[64][CH + 1];
-  __shared__ double sw[128];
+  constexpr int CH = 64;       // queries per stage
+  constexpr int STR = CH + 1;  // padded row, in doubles
+  __shared__ double xs[64 * STR];
+  __shared__ double zs[64 * STR];
+  __shared__ double minv[2][CH];
   const int h = blockIdx.z;
   const HeadDesc Dh = desc[h];
   const int64_t t = Dh.t, n = Dh.n;
   const int64_t a0 = int64_t(blockIdx.x) * 64, b0 = int64_t(blockIdx.y) * 64;
   if (a0 >= t || b0 >= t + D) return;
-  const int tid = threadIdx.x;
-  const int ta = (tid >> 4) * 4, tb = (tid & 15) * 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
   const double *P = Dh.panel_off + panel;
-  if (tid < 64) sw[tid] = (a0 + tid < t) ? w[Dh.t_off + a0 + tid] : 0.0;
-  if (tid >= 64 && tid < 128) sw[tid] = (b0 + tid - 64 < t) ? w[Dh.t_off + b0 + tid - 64] : 0.0;
-  __syncthreads();
-  double acc[4][4] = {};
-  for (int64_t i0 = 0; i0 < n; i0 += CH) {
-    for (int e = tid; e < 64 * CH; e += NT) {
-      const int r = e / CH, c = e % CH;
+  // staged values before scaling by 1/mhat: 16 row and 16 column values per thread
+  double xr[16], zr[16];
+  double mr = 1.0;
+  auto fetch = [&](int64_t i0) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = tid + NT * u;
+      const int rr = e / CH, c = e % CH;
       const int64_t i = i0 + c;
-      double x = 0.0, z = 0.0;
-      if (i < n) {
-        const double inv = 1.0 / mhat[Dh.n_off + i];
-        if (a0 + r < t) x = P[(a0 + r) * n + i] * sw[r] * inv;
-        const int64_t b = b0 + r;
-        if (b < t) z = P[b * n + i] * sw[64 + r] * inv;
-        else if (b - t < D) z = double(Y[(Dh.n_off + i) * D + (b - t)]);
+      const int64_t a = a0 + rr, b = b0 + rr;
+      xr[u] = (i < n && a < t) ? P[a * n + i] : 0.0;
+      zr[u] = (i < n && b < t) ? P[b * n + i] : 0.0;
+    }
+    if (tid < CH) mr = i0 + tid < n ? mhat[Dh.n_off + i0 + tid] : 1.0;
+  };
+  static_assert(64 * CH == 16 * NT, "stage size");
+  f64x4o acc[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) acc[q] = f64x4o{0.0, 0.0, 0.0, 0.0};
+  fetch(0);
+  int buf = 0;
+  for (int64_t i0 = 0; i0 < n; i0 += CH) {
+    if (tid < CH) minv[buf][tid] = 1.0 / mr;
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+      const int e = tid + NT * u;
+      const int rr = e / CH, c = e % CH;
+      const double iv = minv[buf][c];
+      xs[rr * STR + c] = xr[u] * iv;
+      const int64_t b = b0 + rr;
+      if (b < t) {
+        zs[rr * STR + c] = zr[u] * iv;
+      } else {
+        const int64_t i = i0 + c;
+        zs[rr * STR + c] = (b - t < D && i < n) ? double(Y[(Dh.n_off + i) * D + (b - t)]) : 0.0;
       }
-      xs[r][c] = x;
-      zs[r][c] = z;
     }
     __syncthreads();
-#pragma unroll 4
-    for (int c = 0; c < CH; ++c) {
-      double xa[4], zb[4];
+    if (i0 + CH < n) fetch(i0 + CH);
+    const double *xa = &xs[(wave * 16 + c16) * STR + g];
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        xa[q] = xs[ta + q][c];
-        zb[q] = zs[tb + q][c];
-      }
+    for (int k = 0; k < CH / 4; ++k) {
+      const double av = xa[4 * k];
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-#pragma unroll
-        for (int u = 0; u < 4; ++u) acc[q][u] = fma(xa[q], zb[u], acc[q][u]);
+        acc[q] = __builtin_amdgcn_mfma_f64_16x16x4f64(av, zs[(16 * q + c16) * STR + 4 * k + g], acc[q], 0, 0, 0);
     }
-    __syncthreads();
+    buf ^= 1;
   }
+  // element e of lane group g: row wave*16 + g + 4e; tile q: column 16 q + c16
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int64_t a = a0 + ta + q;
+  for (int e = 0; e < 4; ++e) {
+    const int64_t a = a0 + wave * 16 + g + 4 * e;
     if (a >= t) continue;
+    const double wa = w[Dh.t_off + a];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int64_t b = b0 + tb + u;
-      if (b < t) N[Dh.tt_off + a * t + b] = acc[q][u];
-      else if (b - t < D) rhs[(Dh.t_off + a) * D + (b - t)] = acc[q][u];
+    for (int q = 0; q < 4; ++q) {
+      const int64_t b = b0 + 16 * q + c16;
+      if (b < t) N[Dh.tt_off + a * t + b] = acc[q][e] * wa * w[Dh.t_off + b];
+      else if (b - t < D) rhs[(Dh.t_off + a) * D + (b - t)] = acc[q][e] * wa;
     }
   }
 }

@@ -376,6 +376,7 @@ __global__ __launch_bounds__(256) void k_panel(const HeadDesc *__restrict__ desc
                                                const int32_t *__restrict__ sel_list, int cycle, int kR,
                                                double *__restrict__ panel) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int VEC = 16 / int(sizeof(E));  // elements per 16-byte load
   __shared__ float qs[64][D + 1];
   __shared__ float kbuf[4][D];
   const E *Q = static_cast<const E *>(Qv);
@@ -392,9 +393,17 @@ __global__ __launch_bounds__(256) void k_panel(const HeadDesc *__restrict__ desc
     if constexpr (BF16) return __uint_as_float(uint32_t(v) << 16);
     else return v;
   };
-  for (int e = tid; e < 64 * D; e += 256) {
-    const int r = e / D, c = e % D;
-    qs[r][c] = (q0 + r < Dh.n) ? cvt(Q[(Dh.q_off + q0 + r) * D + c]) : 0.0f;
+  for (int gi = tid; gi < 64 * D / VEC; gi += 256) {
+    const int rr = gi / (D / VEC), cv = gi % (D / VEC);
+    E x[VEC];
+    if (q0 + rr < Dh.n) {
+      *reinterpret_cast<uint4 *>(x) = *reinterpret_cast<const uint4 *>(Q + (Dh.q_off + q0 + rr) * D + VEC * cv);
+    } else {
+#pragma unroll
+      for (int u = 0; u < VEC; ++u) x[u] = E(0);
+    }
+#pragma unroll
+    for (int u = 0; u < VEC; ++u) qs[rr][VEC * cv + u] = cvt(x[u]);
   }
   __syncthreads();
   const double s = shift[h];
@@ -406,9 +415,16 @@ __global__ __launch_bounds__(256) void k_panel(const HeadDesc *__restrict__ desc
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    double dot = 0.0;
+    // products of the float32 inputs are exact in float64; four partial sums
+    double d0 = 0.0, d1 = 0.0, d2 = 0.0, d3 = 0.0;
 #pragma unroll 8
-    for (int c = 0; c < D; ++c) dot = fma(double(qs[lane][c]), double(kbuf[wave][c]), dot);
+    for (int c = 0; c < D; c += 4) {
+      d0 = fma(double(qs[lane][c]), double(kbuf[wave][c]), d0);
+      d1 = fma(double(qs[lane][c + 1]), double(kbuf[wave][c + 1]), d1);
+      d2 = fma(double(qs[lane][c + 2]), double(kbuf[wave][c + 2]), d2);
+      d3 = fma(double(qs[lane][c + 3]), double(kbuf[wave][c + 3]), d3);
+    }
+    const double dot = (d0 + d1) + (d2 + d3);
     const double bias = (beta_in && jok) ? double(beta_in[Dh.k_off + j]) : 0.0;
     if (q < Dh.n) panel[Dh.panel_off + (S0 + kk) * Dh.n + q] = jok ? exp(scale * dot + bias - s) : 0.0;
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");

@@ -273,6 +273,8 @@ def main():
                     help="1: one 8-head layer, plain OMP; 2: 288-head stack, batched selection; "
                          "3: 60k-token stack (key-selection seconds, Phi recomputed); "
                          "4: 288 heads with Dirichlet budgets 8..2048")
+    ap.add_argument("--peaks", action="store_true",
+                    help="only run the peak probe (MFMA, vector f64 and HBM read rates of this GPU)")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="only run three device-to-device copies of BYTES (the reference kernel for "
                          "scaling HBM byte counters)")
@@ -290,6 +292,14 @@ def main():
         print(f"bench.py runs on one GPU only (asked for {args.gpus}); the heads of a call are independent, "
               "so a multi-GPU run would shard them by head with no collective on the hot path.", file=sys.stderr)
         sys.exit(2)
+
+    if args.peaks:
+        import subprocess
+
+        probe = os.path.join(ROOT, "attention_matching_least_amd", "amc_peaks")
+        if not os.path.exists(probe):
+            sys.exit("amc_peaks is not built: run __graft_entry__.build() first")
+        sys.exit(subprocess.run([probe]).returncode)
 
     import torch
 
