@@ -64,7 +64,9 @@ struct Plan {
   uint64_t o_desc = 0, o_shift_part = 0, o_shift = 0, o_phi = 0, o_m = 0, o_r = 0, o_mhat = 0,
            o_Y = 0, o_sel_slot = 0, o_sel_list = 0, o_panel = 0, o_G = 0, o_bvec = 0, o_w = 0,
            o_rhs = 0, o_cvsel = 0, o_pos = 0, o_cand_val = 0, o_cand_idx = 0, o_flist = 0, o_fcount = 0,
-           o_dn = 0, o_L = 0, o_nnL = 0, o_nnP = 0, o_nnnp = 0, o_gA = 0, o_nnvec = 0, total = 0;
+           o_dn = 0, o_L = 0, o_nnL = 0, o_nnP = 0, o_nnnp = 0, o_gA = 0, o_nnvec = 0, o_cand_lo = 0,
+           o_cand_lidx = 0, o_cand_cnt = 0, o_band_list = 0, o_band_cnt = 0, o_exact = 0, o_stage = 0,
+           o_part = 0, total = 0;
 };
 
 static amc_status check_problem(const amc_problem *p) {
@@ -123,7 +125,9 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     D.t = features_only ? 1 : p->budgets[h];
     D.q_off = p->cu_q[h];
     D.k_off = p->cu_k[h];
-    D.ldT = (D.T + 3) / 4 * 4;
+    // rows of the stored Phi: float32 rows for the mass-feature entry point
+    // (4-key segments), 16-bit planes for the selection (8-key segments)
+    D.ldT = features_only ? (D.T + 3) / 4 * 4 : (D.T + 7) / 8 * 8;
     D.phi_off = phi;
     D.n_off = nn;
     D.t_off = tt;
@@ -159,6 +163,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     pl.max_cycles = std::max(pl.max_cycles, cycles);
   }
   dm.total_sblk = sblk;
+  dm.max_qblk = ceil_div(dm.max_n, kRescoreRows);
   pl.sum_t = tt;
   pl.sum_cycles = cyc;
   pl.sum_n = nn;
@@ -206,6 +211,16 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.o_nnnp = take(4ull * H);
   pl.o_gA = take(8ull * tt);
   pl.o_nnvec = dm.max_t > kNnlsLdsT ? take(8ull * kNnlsVecPerSlot * tt) : 0;
+  if (pl.store_phi) {  // bounded sweep, band and rescoring state
+    pl.o_cand_lo = take(8ull * cblk * (kMaxCycle + 1));
+    pl.o_cand_lidx = take(4ull * cblk * (kMaxCycle + 1));
+    pl.o_cand_cnt = take(4ull * cblk);
+    pl.o_band_list = take(4ull * H * kBandCap);
+    pl.o_band_cnt = take(4ull * H);
+    pl.o_exact = take(4ull * H);
+    pl.o_stage = take(8ull * nn * kBandCap);
+    pl.o_part = take(8ull * H * kBandCap * dm.max_qblk);
+  }
   pl.total = off;
   return AMC_OK;
 }
@@ -238,6 +253,15 @@ static amc_status upload_desc(const Plan &pl, HeadDesc *d_desc, hipStream_t s) {
 static bool sync_check_enabled() {
   const char *e = std::getenv("AMC_SYNC_CHECK");
   return e && e[0] == '1';
+}
+
+// Largest candidate band the float64 rescoring takes; AMC_BAND_CAP lowers it
+// (0 sends every head through the float32 sweep), for testing that path.
+static int band_cap_setting() {
+  const char *e = std::getenv("AMC_BAND_CAP");
+  if (!e || !e[0]) return kBandCap;
+  const long v = std::strtol(e, nullptr, 10);
+  return v < 0 ? 0 : (v > kBandCap ? kBandCap : int(v));
 }
 
 }  // namespace amc
@@ -354,7 +378,8 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   b.beta_in = beta_in;
   b.shift_part = reinterpret_cast<float *>(ws + pl.o_shift_part);
   b.shift = reinterpret_cast<double *>(ws + pl.o_shift);
-  b.phi = reinterpret_cast<float *>(ws + pl.o_phi);
+  b.phi = nullptr;
+  b.phi16 = pl.store_phi ? reinterpret_cast<uint16_t *>(ws + pl.o_phi) : nullptr;
   b.m = reinterpret_cast<double *>(ws + pl.o_m);
   b.r = reinterpret_cast<double *>(ws + pl.o_r);
   b.mhat = reinterpret_cast<double *>(ws + pl.o_mhat);
@@ -379,6 +404,16 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   b.nn_np = reinterpret_cast<int32_t *>(ws + pl.o_nnnp);
   b.nn_vec = pl.dm.max_t > kNnlsLdsT ? reinterpret_cast<double *>(ws + pl.o_nnvec) : nullptr;
   b.gA = reinterpret_cast<double *>(ws + pl.o_gA);
+  if (pl.store_phi) {
+    b.cand_lo = reinterpret_cast<double *>(ws + pl.o_cand_lo);
+    b.cand_lidx = reinterpret_cast<int32_t *>(ws + pl.o_cand_lidx);
+    b.cand_cnt = reinterpret_cast<int32_t *>(ws + pl.o_cand_cnt);
+    b.band_list = reinterpret_cast<int32_t *>(ws + pl.o_band_list);
+    b.band_cnt = reinterpret_cast<int32_t *>(ws + pl.o_band_cnt);
+    b.exact = reinterpret_cast<int32_t *>(ws + pl.o_exact);
+    b.stage = reinterpret_cast<double *>(ws + pl.o_stage);
+    b.part = reinterpret_cast<double *>(ws + pl.o_part);
+  }
   b.head_status = head_status;
   if (tracing) {
     char *tr = static_cast<char *>(trace);
@@ -390,6 +425,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
     b.tr_iters = reinterpret_cast<int32_t *>(tr + tl.nnls_iters);
   }
   NnlsParams np{0, o->nnls_max_iters, o->nnls_tol};
+  pl.dm.band_cap = band_cap_setting();
   const Dims &dm = pl.dm;
 
   AMC_LAUNCH(AMC_K_INIT, (upload_desc(pl, const_cast<HeadDesc *>(b.desc), stream) == AMC_OK
@@ -398,12 +434,23 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.sel_slot, pl.sum_T, 0, stream));
   if (head_status) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(head_status, dm.H, 0, stream));
   AMC_LAUNCH(AMC_K_SHIFT, launch_shift(dm, b, stream));
-  AMC_LAUNCH(AMC_K_PHI, launch_phi(dm, b, pl.store_phi ? 1 : 0, stream));
+  AMC_LAUNCH(AMC_K_PHI, launch_phi(dm, b, pl.store_phi ? 2 : 0, stream));
   for (int c = 0; c < pl.max_cycles; ++c) {
-    AMC_LAUNCH(AMC_K_SWEEP, pl.store_phi ? launch_sweep(dm, b, c, pl.kR, stream)
-                                         : launch_sweep_rc(dm, b, c, pl.kR, stream));
-    AMC_LAUNCH(AMC_K_MERGE, launch_merge(dm, b, c, pl.kR, stream));
-    AMC_LAUNCH(AMC_K_PANEL, launch_panel(dm, b, c, pl.kR, stream));
+    if (pl.store_phi) {
+      // bounded sweep and float64 rescoring of the band; the heads whose band
+      // overflowed take the float32 sweep, merge and panel
+      AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_band(dm, b, c, pl.kR, stream));
+      AMC_LAUNCH(AMC_K_MERGE, launch_band_merge(dm, b, c, pl.kR, stream));
+      AMC_LAUNCH(AMC_K_SWEEP_EXACT, launch_sweep(dm, b, c, pl.kR, 1, stream));
+      AMC_LAUNCH(AMC_K_MERGE, launch_merge(dm, b, c, pl.kR, 1, stream));
+      AMC_LAUNCH(AMC_K_RESCORE, launch_rescore(dm, b, c, pl.kR, stream));
+      AMC_LAUNCH(AMC_K_MERGE, launch_choose(dm, b, c, pl.kR, stream));
+      AMC_LAUNCH(AMC_K_PANEL, launch_panel(dm, b, c, pl.kR, 1, stream));
+    } else {
+      AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_rc(dm, b, c, pl.kR, stream));
+      AMC_LAUNCH(AMC_K_MERGE, launch_merge(dm, b, c, pl.kR, 0, stream));
+      AMC_LAUNCH(AMC_K_PANEL, launch_panel(dm, b, c, pl.kR, 0, stream));
+    }
     AMC_LAUNCH(AMC_K_GRAM, launch_gram(dm, b, c, pl.kR, 0, stream));
     AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dm, b, c, pl.kR, 0, np, stream));
     AMC_LAUNCH(AMC_K_RESID, launch_resid(dm, b, c, pl.kR, 0, stream));

@@ -19,6 +19,8 @@ constexpr int kNnlsLdsT = 176;   // largest budget whose NNLS state fits in LDS 
 constexpr int kNnlsVecPerSlot = 15;  // float64 words of global NNLS state per budget slot
 constexpr int kMaxBudget = 16384;  // largest budget per head (packed triangles indexed in int32)
 constexpr int kMaxSweepBlocks = 1024;  // sweep column blocks per head the merge handles
+constexpr int kBandCap = 128;    // candidates per head the float64 rescoring takes (more: exact sweep)
+constexpr int kRescoreRows = 64; // queries per block of the rescoring kernel
 
 // Per-head descriptor, computed on the host and copied to the device once per call.
 // All offsets are in elements of the array they index.
@@ -49,7 +51,8 @@ struct Buffers {
   const float *beta_in;
   float *shift_part;   // [sum n_sblk]
   double *shift;       // [H]
-  float *phi;          // [sum n*ldT]
+  float *phi;          // [sum n*ldT] float32 Phi (the mass-feature entry point's output)
+  uint16_t *phi16;     // per head at 2*phi_off: high plane [n][ldT], then low plane [n][ldT]
   double *m, *r, *mhat;  // [sum n]
   float *Y;            // [sum n][d]
   int32_t *sel_slot;   // [sum T]  0 = unselected, else 1 + slot
@@ -70,8 +73,16 @@ struct Buffers {
   int32_t *nn_P;       // [sum t]  NNLS free set in factor order
   int32_t *nn_np;      // [H]      NNLS free-set size
   double *nn_vec;      // [sum t][kNnlsVecPerSlot] NNLS vectors of heads above kNnlsLdsT (else null)
-  double *cand_val;    // [sum n_cblk][kMaxCycle + 1]
+  double *cand_val;    // [sum n_cblk][kMaxCycle + 1]  block top-(kR+1) scores, or band upper bounds
   int32_t *cand_idx;   // [sum n_cblk][kMaxCycle + 1]
+  double *cand_lo;     // [sum n_cblk][kMaxCycle + 1]  block top-(kR+1) lower bounds (sorted)
+  int32_t *cand_lidx;  // [sum n_cblk][kMaxCycle + 1]
+  int32_t *cand_cnt;   // [sum n_cblk]  band entries of the block (-1: non-finite bound)
+  int32_t *band_list;  // [H][kBandCap] key indices of the head's candidate band
+  int32_t *band_cnt;   // [H]
+  int32_t *exact;      // [H] 1: the head's band overflowed; this cycle takes the exact sweep
+  double *stage;       // [sum n][kBandCap] float64 Phi columns of the band, per head [kBandCap][n]
+  double *part;        // [H][kBandCap][max_qblk] partial scores of the band per query block
   int32_t *head_status;  // [H] or null
   // trace (all null when tracing is off)
   double *tr_shift, *tr_pick_score, *tr_weight, *tr_runner;
@@ -83,7 +94,8 @@ struct Dims {
   int in_bf16;         // 1: Q/K/V are bfloat16, 0: float32
   double scale;
   int64_t max_n, max_T, max_t, min_t;
-  int64_t max_sblk, max_cblk;
+  int64_t max_sblk, max_cblk, max_qblk;
+  int band_cap;        // largest band the rescoring takes (<= kBandCap)
   int64_t total_sblk;
 };
 
@@ -101,11 +113,17 @@ void timer_end(Timer *t, int cls, hipStream_t s);
 // Kernel launchers (each returns hipSuccess or the launch error).
 hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
 hipError_t launch_shift(const Dims &dm, const Buffers &b, hipStream_t s);
-hipError_t launch_phi(const Dims &dm, const Buffers &b, int store_phi, hipStream_t s);
-hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+// store: 0 = no Phi, 1 = float32 Phi to b.phi, 2 = the two 16-bit planes to b.phi16
+hipError_t launch_phi(const Dims &dm, const Buffers &b, int store, hipStream_t s);
+// gated: only the heads with b.exact[h] != 0 (else every head)
+hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int gated, hipStream_t s);
 hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
-hipError_t launch_merge(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
-hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_sweep_band(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_band_merge(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_rescore(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_choose(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_merge(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int gated, hipStream_t s);
+hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int gated, hipStream_t s);
 hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);
 hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish,
                        const NnlsParams &np, hipStream_t s);

@@ -7,8 +7,11 @@
 // conditioned like cond(Phi_S^T Phi_S) ~ 1e9, so the logits that feed m are
 // computed in float64 on the MFMA units (v_mfma_f64_16x16x4f64) from the
 // exact bf16/fp32 inputs; Phi is rounded to float32 only for storage, where
-// the memory-bound correlation sweeps read it.  The shift only needs to keep
-// exp() in range, so it comes from a cheap bf16 MFMA pass.
+// the memory-bound correlation sweeps read it.  Stored for the selection, each
+// float32 value is split into its high and low 16 bits, kept in two planes:
+// the high plane alone is Phi truncated to bfloat16 (what the bounded sweep
+// reads), both together give the float32 value back exactly.  The shift only
+// needs to keep exp() in range, so it comes from a cheap bf16 MFMA pass.
 #include <hip/hip_runtime.h>
 
 #include <cmath>
@@ -22,6 +25,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef double f64x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t u16) { return __uint_as_float(u16 << 16); }
 
@@ -132,7 +136,9 @@ __global__ __launch_bounds__(256) void k_shift(const HeadDesc *__restrict__ desc
 
 // ---------------------------------------------------------------------------
 // mass features: float64 MFMA logits (S^T = K Q^T), fused exp / row sum /
-// float32 store and float32 MFMA Phi V.  One block = 64 queries, 4 waves of 16.
+// Phi store and Phi V on MFMA.  One block = 64 queries, 4 waves of 16.
+// STORE: 0 = Phi not stored, 1 = float32 rows [n][ldT] at phi + phi_off,
+// 2 = the two 16-bit planes at phi16 + 2 phi_off (ldT a multiple of 8).
 // ---------------------------------------------------------------------------
 template <typename T>
 struct In;
@@ -153,12 +159,13 @@ __device__ __forceinline__ int phi_key(int kb, int g, int e) { return kb * 16 + 
 // (A[query][k = g]); its B operand B[k = g][dim] is then V[phi_key(kb, g, e)][dim],
 // a row of the V tile, read directly.
 
-template <int D, bool BF16>
+template <int D, bool BF16, int STORE>
 __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, const void *__restrict__ Qv,
                                              const void *__restrict__ Kv, const void *__restrict__ Vv,
                                              const float *__restrict__ beta_in, double scale,
                                              const float *__restrict__ shift_part, double *__restrict__ shift_out,
                                              double *__restrict__ tr_shift, float *__restrict__ phi,
+                                             uint16_t *__restrict__ phi16,
                                              double *__restrict__ m_out, double *__restrict__ r_out,
                                              float *__restrict__ Y_out, int32_t *__restrict__ head_status) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;
@@ -247,10 +254,10 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
         if (k0 + kl < Dh.T) p = exp(scale * acc[e] + double(sbias[kl]) - s);
         msum += p;
         pf[kb][e] = float(p);
-        if (phi) ps[wave][c16 * PSTR + kl] = pf[kb][e];
+        if constexpr (STORE != 0) ps[wave][c16 * PSTR + kl] = pf[kb][e];
       }
     }
-    if (phi) {
+    if constexpr (STORE == 1) {
       // the wave's 16 x 64 Phi tile leaves as 16-byte row segments (ldT is a
       // multiple of 4, so a segment that starts below ldT ends within the row)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -263,6 +270,40 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
         if (qr < Dh.n && k0 + col < Dh.ldT) {
           const f32x4 v = *reinterpret_cast<const f32x4 *>(&ps[wave][row * PSTR + col]);
           __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(phi + Dh.phi_off + qr * Dh.ldT + k0 + col));
+        }
+      }
+    } else if constexpr (STORE == 2) {
+      // 8 keys of one row per lane: their high halves leave as one 16-byte
+      // segment of the high plane, their low halves as one of the low plane
+      // (ldT is a multiple of 8, so a segment that starts below ldT ends
+      // within the row)
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      uint16_t *hp = phi16 + 2 * Dh.phi_off;
+      uint16_t *lp = hp + Dh.n * Dh.ldT;
+#pragma unroll
+      for (int it = 0; it < 2; ++it) {
+        const int row = (lane >> 3) + 8 * it, col = 8 * (lane & 7);
+        const int64_t qr = q0 + row;
+        if (qr < Dh.n && k0 + col < Dh.ldT) {
+          const f32x4 a = *reinterpret_cast<const f32x4 *>(&ps[wave][row * PSTR + col]);
+          const f32x4 c = *reinterpret_cast<const f32x4 *>(&ps[wave][row * PSTR + col + 4]);
+          const uint32_t u[8] = {__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
+                                 __float_as_uint(a.w), __float_as_uint(c.x), __float_as_uint(c.y),
+                                 __float_as_uint(c.z), __float_as_uint(c.w)};
+          u32x4 hv, lv;
+          hv.x = (u[0] >> 16) | (u[1] & 0xffff0000u);
+          hv.y = (u[2] >> 16) | (u[3] & 0xffff0000u);
+          hv.z = (u[4] >> 16) | (u[5] & 0xffff0000u);
+          hv.w = (u[6] >> 16) | (u[7] & 0xffff0000u);
+          lv.x = (u[0] & 0xffffu) | (u[1] << 16);
+          lv.y = (u[2] & 0xffffu) | (u[3] << 16);
+          lv.z = (u[4] & 0xffffu) | (u[5] << 16);
+          lv.w = (u[6] & 0xffffu) | (u[7] << 16);
+          const int64_t at = qr * Dh.ldT + k0 + col;
+          __builtin_nontemporal_store(hv, reinterpret_cast<u32x4 *>(hp + at));
+          __builtin_nontemporal_store(lv, reinterpret_cast<u32x4 *>(lp + at));
         }
       }
     }
@@ -389,22 +430,31 @@ hipError_t launch_shift(const Dims &dm, const Buffers &b, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_phi(const Dims &dm, const Buffers &b, int store_phi, hipStream_t s) {
+template <int STORE>
+static void launch_phi_store(const Dims &dm, const Buffers &b, hipStream_t s) {
   dim3 grid(unsigned((dm.max_n + kPhiRows - 1) / kPhiRows), unsigned(dm.H));
-  float *phi = store_phi ? b.phi : nullptr;
-#define AMC_PHI_ARGS b.desc, b.Q, b.K, b.V, b.beta_in, dm.scale, b.shift_part, b.shift, b.tr_shift, phi, b.m, b.r, b.Y, b.head_status
+#define AMC_PHI_ARGS b.desc, b.Q, b.K, b.V, b.beta_in, dm.scale, b.shift_part, b.shift, b.tr_shift, b.phi, b.phi16, \
+    b.m, b.r, b.Y, b.head_status
   if (dm.d == 128) {
     if (dm.in_bf16)
-      hipLaunchKernelGGL((k_phi<128, true>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
+      hipLaunchKernelGGL((k_phi<128, true, STORE>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
     else
-      hipLaunchKernelGGL((k_phi<128, false>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
+      hipLaunchKernelGGL((k_phi<128, false, STORE>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
   } else {
     if (dm.in_bf16)
-      hipLaunchKernelGGL((k_phi<64, true>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
+      hipLaunchKernelGGL((k_phi<64, true, STORE>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
     else
-      hipLaunchKernelGGL((k_phi<64, false>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
+      hipLaunchKernelGGL((k_phi<64, false, STORE>), grid, dim3(256), 0, s, AMC_PHI_ARGS);
   }
 #undef AMC_PHI_ARGS
+}
+
+hipError_t launch_phi(const Dims &dm, const Buffers &b, int store, hipStream_t s) {
+  if (store == 1 && !b.phi) return hipErrorInvalidValue;
+  if (store == 2 && !b.phi16) return hipErrorInvalidValue;
+  if (store == 1) launch_phi_store<1>(dm, b, s);
+  else if (store == 2) launch_phi_store<2>(dm, b, s);
+  else launch_phi_store<0>(dm, b, s);
   return hipGetLastError();
 }
 

@@ -4,6 +4,16 @@
 //   sweep  : c_j = r^T Phi[:, j] over the unselected keys, block-local top-(K+1)
 //   merge  : per-head top-(K+1) of the block candidates; appends the K picks
 //   panel  : float64 columns Phi[:, j] of the new picks, recomputed from Q, K
+//
+// With Phi stored, the sweep that runs every cycle is a bounded one: it reads
+// the high 16-bit plane of the stored float32 Phi (Phi truncated to bfloat16,
+// half the bytes) and gives every key an interval that holds its score, the
+// band merge keeps the keys whose interval reaches the (K+1)-th best lower
+// bound, the rescoring computes their float64 columns and exact scores from
+// Q and K, and the choice takes the top K+1 of those (the same keys the full
+// scores would give) and moves the picks' columns into the panel.  A head
+// whose band holds more than kBandCap keys takes the float32 sweep over both
+// planes, the merge and the panel in the same cycle.
 //   gram   : new columns of G = Phi_S^T Phi_S and of b = Phi_S^T m
 //   resid  : mhat = Phi_S w and r = m - mhat
 //
@@ -24,6 +34,8 @@ namespace {
 
 constexpr int KP_STRIDE = kMaxCycle + 1;  // candidate slots per sweep block
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 __device__ __forceinline__ bool better(double va, int ia, double vb, int ib) {
   return va > vb || (va == vb && ia < ib);
@@ -62,11 +74,23 @@ __device__ __forceinline__ int cycle_keys(const HeadDesc &D, int cycle, int kR, 
 }
 
 // ---------------------------------------------------------------------------
-// sweep: one block = 256 columns of one head, 4 waves split the rows
+// sweep over the float32 Phi, rebuilt exactly from its two 16-bit planes: one
+// block = 256 columns of one head, 4 waves split the rows.  gate: only the
+// heads with gate[h] != 0.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc, const float *__restrict__ phi,
+__device__ __forceinline__ f32x4 join_planes(u32x2 hv, u32x2 lv) {
+  f32x4 x;
+  x.x = __uint_as_float((hv.x << 16) | (lv.x & 0xffffu));
+  x.y = __uint_as_float((hv.x & 0xffff0000u) | (lv.x >> 16));
+  x.z = __uint_as_float((hv.y << 16) | (lv.y & 0xffffu));
+  x.w = __uint_as_float((hv.y & 0xffff0000u) | (lv.y >> 16));
+  return x;
+}
+
+__global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc, const uint16_t *__restrict__ phi16,
                                                const double *__restrict__ r, const int32_t *__restrict__ sel_slot,
-                                               int cycle, int kR, double *__restrict__ cand_val,
+                                               int cycle, int kR, const int32_t *__restrict__ gate,
+                                               double *__restrict__ cand_val,
                                                int32_t *__restrict__ cand_idx, int32_t *__restrict__ head_status) {
   __shared__ double red[4][256];
   __shared__ double sv[256];
@@ -78,12 +102,14 @@ __global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc
   int64_t S0;
   const int Kc = cycle_keys(D, cycle, kR, &S0);
   if (Kc == 0) return;
+  if (gate && gate[h] == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int64_t j0 = int64_t(blk) * kSweepCols + 4 * lane;
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
   if (j0 < D.T) {
-    const float *p = phi + D.phi_off + j0;
+    const uint16_t *ph = phi16 + 2 * D.phi_off + j0;
+    const uint16_t *pl = ph + D.n * D.ldT;
     const double *rr = r + D.n_off;
     const int64_t ld = D.ldT;
     int64_t i = wave;
@@ -92,7 +118,9 @@ __global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc
       double rv[8];
 #pragma unroll
       for (int u = 0; u < 8; ++u) {
-        x[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p + (i + 4 * u) * ld));
+        const int64_t at = (i + 4 * u) * ld;
+        x[u] = join_planes(__builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(ph + at)),
+                           __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(pl + at)));
         rv[u] = rr[i + 4 * u];
       }
 #pragma unroll
@@ -104,7 +132,8 @@ __global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc
       }
     }
     for (; i < D.n; i += 4) {
-      const f32x4 x = *reinterpret_cast<const f32x4 *>(p + i * ld);
+      const f32x4 x = join_planes(*reinterpret_cast<const u32x2 *>(ph + i * ld),
+                                  *reinterpret_cast<const u32x2 *>(pl + i * ld));
       const double rv = rr[i];
       a0 = fma(rv, double(x.x), a0);
       a1 = fma(rv, double(x.y), a1);
@@ -283,35 +312,30 @@ __global__ __launch_bounds__(RC_THREADS) void k_sweep_rc(
 }
 
 // ---------------------------------------------------------------------------
-// merge: one block per head; tournament over the sorted block candidate lists
+// Tournament over the sorted candidate lists of one head (list l at
+// (base + l) * KP_STRIDE, best first, read up to position last): on_rank(rank,
+// value, index) runs on thread 0 for the ranks 0..last in order.  Every thread
+// of the block must call it.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_merge(const HeadDesc *__restrict__ desc, int cycle, int kR,
-                                               const double *__restrict__ cand_val,
-                                               const int32_t *__restrict__ cand_idx, int32_t *__restrict__ sel_slot,
-                                               int32_t *__restrict__ sel_list, int32_t *__restrict__ tr_pick,
-                                               double *__restrict__ tr_pick_score, double *__restrict__ tr_runner) {
+template <typename F>
+__device__ void tournament(const double *__restrict__ val, const int32_t *__restrict__ idx, int64_t base, int nl,
+                           int last, F on_rank) {
   __shared__ double wv[4];
   __shared__ int wi[4], wl[4];
   __shared__ int win_list;
-  const int h = blockIdx.x;
-  const HeadDesc D = desc[h];
-  int64_t S0;
-  const int Kc = cycle_keys(D, cycle, kR, &S0);
-  if (Kc == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nl = int(D.n_cblk);
   // each thread owns lists tid, tid+256, tid+512, tid+768
   int pos[4] = {0, 0, 0, 0};
-  for (int rank = 0; rank <= Kc; ++rank) {
+  for (int rank = 0; rank <= last; ++rank) {
     double bv = -INFINITY;
     int bi = INT_MAX, bl = -1;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int l = tid + 256 * q;
-      if (l < nl && pos[q] <= Kc) {
-        const int64_t o = (D.cblk_off + l) * KP_STRIDE + pos[q];
-        const double v = cand_val[o];
-        const int ix = cand_idx[o];
+      if (l < nl && pos[q] <= last) {
+        const int64_t o = (base + l) * KP_STRIDE + pos[q];
+        const double v = val[o];
+        const int ix = idx[o];
         if (bl < 0 || better(v, ix, bv, bi)) {
           bv = v;
           bi = ix;
@@ -346,23 +370,237 @@ __global__ __launch_bounds__(256) void k_merge(const HeadDesc *__restrict__ desc
           l = wl[w];
         }
       win_list = l;
-      if (rank < Kc) {
-        const int64_t slot = S0 + rank;
-        if (ix >= 0 && ix < D.T) {
-          sel_list[D.t_off + slot] = ix;
-          sel_slot[D.k_off + ix] = int32_t(slot + 1);
-        }
-        if (tr_pick) {
-          tr_pick[D.t_off + slot] = ix;
-          tr_pick_score[D.t_off + slot] = v;
-        }
-      } else if (tr_runner) {
-        tr_runner[D.cyc_off + cycle] = (ix >= 0 && ix < D.T) ? v : -INFINITY;
-      }
+      on_rank(rank, v, ix);
     }
     __syncthreads();
     const int l = win_list;
     if (l >= 0 && (l & 255) == tid) pos[l >> 8]++;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// merge: one block per head; the tournament's first Kc winners are the picks,
+// the next one the runner-up.  gate: only the heads with gate[h] != 0.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_merge(const HeadDesc *__restrict__ desc, int cycle, int kR,
+                                               const int32_t *__restrict__ gate,
+                                               const double *__restrict__ cand_val,
+                                               const int32_t *__restrict__ cand_idx, int32_t *__restrict__ sel_slot,
+                                               int32_t *__restrict__ sel_list, int32_t *__restrict__ tr_pick,
+                                               double *__restrict__ tr_pick_score, double *__restrict__ tr_runner) {
+  const int h = blockIdx.x;
+  const HeadDesc D = desc[h];
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0) return;
+  if (gate && gate[h] == 0) return;
+  tournament(cand_val, cand_idx, D.cblk_off, int(D.n_cblk), Kc, [&](int rank, double v, int ix) {
+    if (rank < Kc) {
+      const int64_t slot = S0 + rank;
+      if (ix >= 0 && ix < D.T) {
+        sel_list[D.t_off + slot] = ix;
+        sel_slot[D.k_off + ix] = int32_t(slot + 1);
+      }
+      if (tr_pick) {
+        tr_pick[D.t_off + slot] = ix;
+        tr_pick_score[D.t_off + slot] = v;
+      }
+    } else if (tr_runner) {
+      tr_runner[D.cyc_off + cycle] = (ix >= 0 && ix < D.T) ? v : -INFINITY;
+    }
+  });
+}
+
+// ---------------------------------------------------------------------------
+// bounded sweep over the high plane (Phi truncated to bfloat16).  For a key j
+// with stored float32 values x_ij, high halves h_ij and exact Phi_ij:
+//   0 <= x_ij - h_ij < 2^-7 h_ij           (7 explicit significand bits kept)
+//   |Phi_ij - x_ij| <= 2^-24 Phi_ij         (float32 rounding of float64 Phi)
+// so with P_j = sum_{r_i > 0} r_i h_ij and N_j = sum_{r_i < 0} r_i h_ij,
+//   P_j + N_j + 2^-7 N_j - e_j <= r^T Phi[:, j] <= P_j + N_j + 2^-7 P_j + e_j,
+// where e_j covers the float32 accumulation of P and N (same-sign sums, so a
+// relative error of (terms per lane + 2) 2^-24 each), the float32 rounding of
+// Phi and of r, the float64 rescoring's own rounding, and an absolute term for
+// values below float32's normal range.  One block = 256 keys: each lane takes
+// 8 keys of every 8th row (16-byte loads), P and N accumulate in float32 per
+// lane and in float64 across the 8 row streams.  Out: the block's top-(Kc+1)
+// lower bounds, sorted (cand_lo / cand_lidx), and in key order every key whose
+// upper bound reaches the (Kc+1)-th of them (cand_val = upper bound,
+// cand_idx, cand_cnt = their number, -1 if a bound is not finite).
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void band_accum(const u32x4 &x, double rv, float (&P)[8], float (&N)[8], double &ra) {
+  const float rp = float(fmax(rv, 0.0)), rn = float(fmin(rv, 0.0));
+  ra += fabs(rv);  // NaN in r reaches the bounds through this sum
+  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const float v0 = __uint_as_float(w[c] << 16);
+    const float v1 = __uint_as_float(w[c] & 0xffff0000u);
+    P[2 * c] = fmaf(rp, v0, P[2 * c]);
+    N[2 * c] = fmaf(rn, v0, N[2 * c]);
+    P[2 * c + 1] = fmaf(rp, v1, P[2 * c + 1]);
+    N[2 * c + 1] = fmaf(rn, v1, N[2 * c + 1]);
+  }
+}
+
+__global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__ desc,
+                                                    const uint16_t *__restrict__ phi16, const double *__restrict__ r,
+                                                    const int32_t *__restrict__ sel_slot, int cycle, int kR,
+                                                    double *__restrict__ cand_val, int32_t *__restrict__ cand_idx,
+                                                    int32_t *__restrict__ cand_cnt, double *__restrict__ cand_lo,
+                                                    int32_t *__restrict__ cand_lidx) {
+  __shared__ __attribute__((aligned(16))) float ps_p[8][256];
+  __shared__ __attribute__((aligned(16))) float ps_n[8][256];
+  __shared__ double ra_s[8];
+  __shared__ double sv[256];
+  __shared__ int si[256];
+  __shared__ int wcnt[4];
+  const int h = blockIdx.y;
+  const HeadDesc D = desc[h];
+  const int blk = blockIdx.x;
+  if (blk >= D.n_cblk) return;
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int cg = lane & 31;
+  const int stream = 2 * wave + (lane >> 5);  // rows stream, stream + 8, ...
+  const int64_t j0 = int64_t(blk) * kSweepCols + 8 * cg;
+  float P[8], N[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) P[k] = N[k] = 0.0f;
+  double ra = 0.0;
+  if (j0 < D.ldT) {  // ldT is a multiple of 8: the 16-byte segment lies within the row
+    const uint16_t *p = phi16 + 2 * D.phi_off + j0;
+    const double *rr = r + D.n_off;
+    const int64_t ld = D.ldT;
+    int64_t i = stream;
+    for (; i + 56 < D.n; i += 64) {
+      u32x4 x[8];
+      double rv[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + (i + 8 * u) * ld));
+        rv[u] = rr[i + 8 * u];
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u) band_accum(x[u], rv[u], P, N, ra);
+    }
+    for (; i < D.n; i += 8) band_accum(*reinterpret_cast<const u32x4 *>(p + i * ld), rr[i], P, N, ra);
+  }
+  *reinterpret_cast<float4 *>(&ps_p[stream][8 * cg]) = make_float4(P[0], P[1], P[2], P[3]);
+  *reinterpret_cast<float4 *>(&ps_p[stream][8 * cg + 4]) = make_float4(P[4], P[5], P[6], P[7]);
+  *reinterpret_cast<float4 *>(&ps_n[stream][8 * cg]) = make_float4(N[0], N[1], N[2], N[3]);
+  *reinterpret_cast<float4 *>(&ps_n[stream][8 * cg + 4]) = make_float4(N[4], N[5], N[6], N[7]);
+  if (cg == 0) ra_s[stream] = ra;  // lane cg = 0 always reads (block start < T <= ldT)
+  __syncthreads();
+  const int64_t col = int64_t(blk) * kSweepCols + tid;
+  double Pd = 0.0, Nd = 0.0, rs = 0.0;
+#pragma unroll
+  for (int st = 0; st < 8; ++st) {
+    Pd += double(ps_p[st][tid]);
+    Nd += double(ps_n[st][tid]);
+    rs += ra_s[st];
+  }
+  const bool valid = col < D.T && sel_slot[D.k_off + col] == 0;
+  const double crel = 2.0 * (double(D.n) * 0.125 + 16.0) * 0x1p-24 + 0x1p-22;
+  const double slack = crel * (Pd - Nd) + (rs + double(D.n)) * 0x1p-120;
+  const double c7 = 0x1.00001p-7;
+  const double up = (Pd + Nd) + c7 * Pd + slack;
+  const double lo = (Pd + Nd) + c7 * Nd - slack;
+  const bool bad = valid && !(isfinite(up) && isfinite(lo));
+  sv[tid] = valid ? lo : -INFINITY;
+  si[tid] = valid ? int(col) : INT_MAX;
+  const int any_bad = __syncthreads_or(int(bad));
+  block_sort256(sv, si);
+  const double Lb = sv[Kc];
+  const int64_t o = (D.cblk_off + blk) * KP_STRIDE;
+  if (tid <= Kc) {
+    cand_lo[o + tid] = sv[tid];
+    cand_lidx[o + tid] = si[tid];
+  }
+  const bool take = valid && up >= Lb;
+  const uint64_t m = __ballot(take);
+  if (lane == 0) wcnt[wave] = __popcll(m);
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wcnt[w];
+  if (take) {
+    const int at = base + __popcll(m & ((uint64_t(1) << lane) - 1));
+    cand_val[o + at] = up;
+    cand_idx[o + at] = int(col);
+  }
+  if (tid == 0) cand_cnt[D.cblk_off + blk] = any_bad ? -1 : wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+}
+
+// ---------------------------------------------------------------------------
+// band merge: one block per head.  L = the (Kc+1)-th best lower bound over
+// all blocks (the tournament over the blocks' sorted lists); the band is every
+// key whose upper bound reaches L, in block and key order.  It holds the true
+// top Kc+1: each of those scores at least L, and its upper bound at least its
+// score.  exact[h] = 1 when the band overflows kBandCap (or a bound was not
+// finite): the head takes the float32 sweep this cycle.  band_cap <= kBandCap
+// (lower only to exercise the exact path).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_band_merge(const HeadDesc *__restrict__ desc, int cycle, int kR,
+                                                    const double *__restrict__ cand_val,
+                                                    const int32_t *__restrict__ cand_idx,
+                                                    const int32_t *__restrict__ cand_cnt,
+                                                    const double *__restrict__ cand_lo,
+                                                    const int32_t *__restrict__ cand_lidx,
+                                                    int band_cap, int32_t *__restrict__ band_list,
+                                                    int32_t *__restrict__ band_cnt, int32_t *__restrict__ exact) {
+  __shared__ double s_L;
+  __shared__ int wcnt[4];
+  const int h = blockIdx.x;
+  const HeadDesc D = desc[h];
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int nl = int(D.n_cblk);
+  int bad = 0;
+  for (int l = tid; l < nl; l += 256) bad |= cand_cnt[D.cblk_off + l] < 0;
+  if (__syncthreads_or(bad)) {
+    if (tid == 0) {
+      band_cnt[h] = 0;
+      exact[h] = 1;
+    }
+    return;
+  }
+  double *Lp = &s_L;
+  tournament(cand_lo, cand_lidx, D.cblk_off, nl, Kc, [&](int rank, double v, int ix) {
+    if (rank == Kc) *Lp = ix != INT_MAX ? v : -INFINITY;
+  });
+  const double L = s_L;
+  int total = 0;
+  int32_t *out = band_list + int64_t(h) * kBandCap;
+  for (int l = 0; l < nl; ++l) {
+    const int64_t o = (D.cblk_off + l) * KP_STRIDE;
+    const int cnt = cand_cnt[D.cblk_off + l];
+    for (int e0 = 0; e0 < cnt; e0 += 256) {
+      const int e = e0 + tid;
+      bool take = false;
+      int ix = 0;
+      if (e < cnt) {
+        ix = cand_idx[o + e];
+        take = ix != INT_MAX && cand_val[o + e] >= L;
+      }
+      const uint64_t m = __ballot(take);
+      if (lane == 0) wcnt[wave] = __popcll(m);
+      __syncthreads();
+      int at = total;
+      for (int w = 0; w < wave; ++w) at += wcnt[w];
+      at += __popcll(m & ((uint64_t(1) << lane) - 1));
+      if (take && at < kBandCap) out[at] = ix;
+      total += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+      __syncthreads();
+    }
+  }
+  if (tid == 0) {
+    band_cnt[h] = total;
+    exact[h] = (total > band_cap || total < Kc) ? 1 : 0;
   }
 }
 
@@ -374,7 +612,7 @@ __global__ __launch_bounds__(256) void k_panel(const HeadDesc *__restrict__ desc
                                                const void *__restrict__ Kv, const float *__restrict__ beta_in,
                                                double scale, const double *__restrict__ shift,
                                                const int32_t *__restrict__ sel_list, int cycle, int kR,
-                                               double *__restrict__ panel) {
+                                               const int32_t *__restrict__ gate, double *__restrict__ panel) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int VEC = 16 / int(sizeof(E));  // elements per 16-byte load
   __shared__ float qs[64][D + 1];
@@ -386,6 +624,7 @@ __global__ __launch_bounds__(256) void k_panel(const HeadDesc *__restrict__ desc
   int64_t S0;
   const int Kc = cycle_keys(Dh, cycle, kR, &S0);
   if (Kc == 0) return;
+  if (gate && gate[h] == 0) return;
   const int64_t q0 = int64_t(blockIdx.x) * 64;
   if (q0 >= Dh.n) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -430,6 +669,158 @@ __global__ __launch_bounds__(256) void k_panel(const HeadDesc *__restrict__ desc
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// ---------------------------------------------------------------------------
+// rescoring: float64 Phi columns of the head's band keys over 64 queries, as
+// the panel computes them (float64 MFMA logits from the exact inputs, float64
+// exp), written to the stage, and their partial scores r^T Phi[:, j] over the
+// block's queries.  One block = 64 queries in 4 waves of 16; each 16-key group
+// of the band is one v_mfma_f64_16x16x4f64 tile per wave (keys as rows).
+// ---------------------------------------------------------------------------
+template <int D, bool BF16>
+__global__ __launch_bounds__(256) void k_rescore(const HeadDesc *__restrict__ desc, const void *__restrict__ Qv,
+                                                 const void *__restrict__ Kv, const float *__restrict__ beta_in,
+                                                 double scale, const double *__restrict__ shift,
+                                                 const double *__restrict__ r, int cycle, int kR,
+                                                 const int32_t *__restrict__ band_list,
+                                                 const int32_t *__restrict__ band_cnt,
+                                                 const int32_t *__restrict__ exact, int64_t max_qblk,
+                                                 double *__restrict__ stage, double *__restrict__ part) {
+  using E = typename std::conditional<BF16, uint16_t, float>::type;
+  constexpr int NS = D / 4;  // MFMA k-steps over the head dimension
+  __shared__ double red[4][16];
+  const E *Q = static_cast<const E *>(Qv);
+  const E *K = static_cast<const E *>(Kv);
+  const int h = blockIdx.y;
+  const HeadDesc Dh = desc[h];
+  int64_t S0;
+  const int Kc = cycle_keys(Dh, cycle, kR, &S0);
+  if (Kc == 0) return;
+  if (exact[h] != 0) return;
+  const int qb = blockIdx.x;
+  const int64_t q0 = int64_t(qb) * kRescoreRows;
+  if (q0 >= Dh.n) return;
+  const int U = band_cnt[h];  // <= kBandCap when exact[h] == 0
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c16 = lane & 15, g = lane >> 4;
+  const int64_t q = q0 + 16 * wave + c16;  // B operand column / output column of this lane
+  const bool qvalid = q < Dh.n;
+  // head dims 16 u + 4 g + v at k-step 4 u + v, for the keys (A) and the queries (B)
+  double qf[NS];
+#pragma unroll
+  for (int u = 0; u < NS / 4; ++u)
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+      qf[4 * u + v] = qvalid ? double(InRc<E>::f(Q[(Dh.q_off + q) * D + 16 * u + 4 * g + v])) : 0.0;
+  const double s = shift[h];
+  const double rq = qvalid ? r[Dh.n_off + q] : 0.0;
+  double *stg = stage + Dh.n_off * kBandCap;
+  for (int g0 = 0; g0 < U; g0 += 16) {
+    const int ui = g0 + c16;
+    const bool uok = ui < U;
+    const int j = uok ? band_list[int64_t(h) * kBandCap + ui] : 0;
+    const double bj = (uok && beta_in) ? double(beta_in[Dh.k_off + j]) : 0.0;
+    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int u = 0; u < NS / 4; ++u)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const double a = uok ? double(InRc<E>::f(K[(Dh.k_off + j) * D + 16 * u + 4 * g + v])) : 0.0;
+        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, qf[4 * u + v], acc, 0, 0, 0);
+      }
+    // element e of this lane: band key g0 + g + 4 e (its bias sits in lane g + 4 e), query q
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int ue = g0 + g + 4 * e;
+      const double be = __shfl(bj, g + 4 * e);
+      double p = 0.0;
+      if (ue < U && qvalid) {
+        p = exp(scale * acc[e] + be - s);
+        stg[int64_t(ue) * Dh.n + q] = p;
+      }
+      double v = rq * p;
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      if (c16 == 0) red[wave][g + 4 * e] = v;
+    }
+    __syncthreads();
+    if (tid < 16 && g0 + tid < U)
+      part[(int64_t(h) * kBandCap + g0 + tid) * max_qblk + qb] = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+    __syncthreads();
+  }
+}
+
+// ---------------------------------------------------------------------------
+// choice: the band's exact scores (partials summed in query-block order), the
+// top Kc picks and the runner-up (score descending, key index ascending), the
+// selection update (block 0), and the picks' staged columns copied into their
+// panel rows (all blocks of the head, a share each).
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void k_choose(const HeadDesc *__restrict__ desc, int cycle, int kR,
+                                                const int32_t *__restrict__ band_list,
+                                                const int32_t *__restrict__ band_cnt,
+                                                const int32_t *__restrict__ exact, int64_t max_qblk,
+                                                const double *__restrict__ part, const double *__restrict__ stage,
+                                                int32_t *__restrict__ sel_slot, int32_t *__restrict__ sel_list,
+                                                double *__restrict__ panel, int32_t *__restrict__ tr_pick,
+                                                double *__restrict__ tr_pick_score, double *__restrict__ tr_runner,
+                                                int32_t *__restrict__ head_status) {
+  __shared__ double sc[kBandCap];
+  __shared__ int ix[kBandCap];
+  __shared__ int pick_u[kMaxCycle + 1];
+  const int h = blockIdx.y;
+  const HeadDesc D = desc[h];
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0) return;
+  if (exact[h] != 0) return;
+  const int U = band_cnt[h];  // Kc <= U <= kBandCap when exact[h] == 0
+  const int tid = threadIdx.x;
+  const int64_t nqb = (D.n + kRescoreRows - 1) / kRescoreRows;
+  if (tid < U) {
+    const double *pp = part + (int64_t(h) * kBandCap + tid) * max_qblk;
+    double sum = 0.0;
+    for (int64_t b = 0; b < nqb; ++b) sum += pp[b];
+    if (!isfinite(sum)) {
+      if (head_status && blockIdx.x == 0) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
+      sum = -DBL_MAX;  // still a valid, selectable key
+    }
+    sc[tid] = sum;
+    ix[tid] = band_list[int64_t(h) * kBandCap + tid];
+  }
+  __syncthreads();
+  if (tid < U) {
+    int rank = 0;
+    for (int v = 0; v < U; ++v) rank += better(sc[v], ix[v], sc[tid], ix[tid]) ? 1 : 0;
+    if (rank <= Kc) pick_u[rank] = tid;
+  }
+  __syncthreads();
+  if (blockIdx.x == 0) {
+    if (tid < Kc) {
+      const int u = pick_u[tid];
+      const int j = ix[u];
+      const int64_t slot = S0 + tid;
+      sel_list[D.t_off + slot] = j;
+      sel_slot[D.k_off + j] = int32_t(slot + 1);
+      if (tr_pick) {
+        tr_pick[D.t_off + slot] = j;
+        tr_pick_score[D.t_off + slot] = sc[u];
+      }
+    }
+    if (tid == 0 && tr_runner) tr_runner[D.cyc_off + cycle] = U > Kc ? sc[pick_u[Kc]] : -INFINITY;
+  }
+  const int64_t n = D.n;
+  const double *stg = stage + D.n_off * kBandCap;
+  double *pan = panel + D.panel_off + S0 * n;
+  const int64_t total = int64_t(Kc) * n;
+  for (int64_t e = int64_t(blockIdx.x) * 256 + tid; e < total; e += int64_t(gridDim.x) * 256) {
+    const int rk = int(e / n);
+    const int64_t qq = e - int64_t(rk) * n;
+    pan[e] = stg[int64_t(pick_u[rk]) * n + qq];
   }
 }
 
@@ -583,9 +974,9 @@ __global__ __launch_bounds__(256) void k_resid(const HeadDesc *__restrict__ desc
 
 }  // namespace
 
-hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
-  hipLaunchKernelGGL(k_sweep, dim3(unsigned(dm.max_cblk), unsigned(dm.H)), dim3(256), 0, s, b.desc, b.phi, b.r,
-                     b.sel_slot, cycle, kR, b.cand_val, b.cand_idx, b.head_status);
+hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int kR, int gated, hipStream_t s) {
+  hipLaunchKernelGGL(k_sweep, dim3(unsigned(dm.max_cblk), unsigned(dm.H)), dim3(256), 0, s, b.desc, b.phi16, b.r,
+                     b.sel_slot, cycle, kR, gated ? b.exact : nullptr, b.cand_val, b.cand_idx, b.head_status);
   return hipGetLastError();
 }
 
@@ -604,15 +995,51 @@ hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int kR, 
   return hipGetLastError();
 }
 
-hipError_t launch_merge(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
-  hipLaunchKernelGGL(k_merge, dim3(unsigned(dm.H)), dim3(256), 0, s, b.desc, cycle, kR, b.cand_val, b.cand_idx,
-                     b.sel_slot, b.sel_list, b.tr_pick, b.tr_pick_score, b.tr_runner);
+hipError_t launch_sweep_band(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  hipLaunchKernelGGL(k_sweep_band, dim3(unsigned(dm.max_cblk), unsigned(dm.H)), dim3(256), 0, s, b.desc, b.phi16,
+                     b.r, b.sel_slot, cycle, kR, b.cand_val, b.cand_idx, b.cand_cnt, b.cand_lo, b.cand_lidx);
   return hipGetLastError();
 }
 
-hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+hipError_t launch_band_merge(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  hipLaunchKernelGGL(k_band_merge, dim3(unsigned(dm.H)), dim3(256), 0, s, b.desc, cycle, kR, b.cand_val, b.cand_idx,
+                     b.cand_cnt, b.cand_lo, b.cand_lidx, dm.band_cap, b.band_list, b.band_cnt, b.exact);
+  return hipGetLastError();
+}
+
+hipError_t launch_rescore(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  dim3 grid(unsigned(dm.max_qblk), unsigned(dm.H));
+#define AMC_RS_ARGS b.desc, b.Q, b.K, b.beta_in, dm.scale, b.shift, b.r, cycle, kR, b.band_list, b.band_cnt, b.exact, \
+    dm.max_qblk, b.stage, b.part
+  if (dm.d == 128) {
+    if (dm.in_bf16) hipLaunchKernelGGL((k_rescore<128, true>), grid, dim3(256), 0, s, AMC_RS_ARGS);
+    else hipLaunchKernelGGL((k_rescore<128, false>), grid, dim3(256), 0, s, AMC_RS_ARGS);
+  } else {
+    if (dm.in_bf16) hipLaunchKernelGGL((k_rescore<64, true>), grid, dim3(256), 0, s, AMC_RS_ARGS);
+    else hipLaunchKernelGGL((k_rescore<64, false>), grid, dim3(256), 0, s, AMC_RS_ARGS);
+  }
+#undef AMC_RS_ARGS
+  return hipGetLastError();
+}
+
+hipError_t launch_choose(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  // a few blocks per head share the copy of the picks' columns
+  hipLaunchKernelGGL(k_choose, dim3(8, unsigned(dm.H)), dim3(256), 0, s, b.desc, cycle, kR, b.band_list, b.band_cnt,
+                     b.exact, dm.max_qblk, b.part, b.stage, b.sel_slot, b.sel_list, b.panel, b.tr_pick,
+                     b.tr_pick_score, b.tr_runner, b.head_status);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const Dims &dm, const Buffers &b, int cycle, int kR, int gated, hipStream_t s) {
+  hipLaunchKernelGGL(k_merge, dim3(unsigned(dm.H)), dim3(256), 0, s, b.desc, cycle, kR, gated ? b.exact : nullptr,
+                     b.cand_val, b.cand_idx, b.sel_slot, b.sel_list, b.tr_pick, b.tr_pick_score, b.tr_runner);
+  return hipGetLastError();
+}
+
+hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int kR, int gated, hipStream_t s) {
   dim3 grid(unsigned((dm.max_n + 63) / 64), unsigned(dm.H));
-#define AMC_PANEL_ARGS b.desc, b.Q, b.K, b.beta_in, dm.scale, b.shift, b.sel_list, cycle, kR, b.panel
+#define AMC_PANEL_ARGS b.desc, b.Q, b.K, b.beta_in, dm.scale, b.shift, b.sel_list, cycle, kR, gated ? b.exact : nullptr, \
+    b.panel
   if (dm.d == 128) {
     if (dm.in_bf16) hipLaunchKernelGGL((k_panel<128, true>), grid, dim3(256), 0, s, AMC_PANEL_ARGS);
     else hipLaunchKernelGGL((k_panel<128, false>), grid, dim3(256), 0, s, AMC_PANEL_ARGS);

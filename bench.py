@@ -30,8 +30,10 @@ if ROOT not in sys.path:
 import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
+F64_MFMA_PEAK_TFS = 78.6
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_traffic.md")
-SWEEP_SOURCE = os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_select.hip")
+KERNEL_SOURCES = {"k_sweep_band": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_select.hip"),
+                  "k_phi": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_phi.hip")}
 
 
 def _head_bits(args):
@@ -57,29 +59,30 @@ def generate(idx: int, workers: int):
     return w, Q, K, V
 
 
-def sweep_source_hash() -> str:
-    with open(SWEEP_SOURCE, "rb") as f:
+def source_hash(kernel: str) -> str:
+    with open(KERNEL_SOURCES[kernel], "rb") as f:
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def read_traffic():
-    """HBM bytes per sweep launch measured by rocprofv3 counters, if they were
-    taken on the current sweep source (else None)."""
+def read_traffic(kernel: str):
+    """HBM bytes per launch of a kernel, measured by rocprofv3 counters, if they
+    were taken on the kernel's current source (else None)."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    vals = {}
     with open(TRAFFIC_FILE) as f:
         for line in f:
-            if line.startswith("traffic:"):
-                for kv in line[len("traffic:"):].split():
-                    k, v = kv.split("=")
-                    vals[k] = v
-    if vals.get("source_sha") != sweep_source_hash():
-        return None
-    try:
-        return float(vals["bytes_per_launch"])
-    except (KeyError, ValueError):
-        return None
+            if not line.startswith("traffic:"):
+                continue
+            vals = dict(kv.split("=") for kv in line[len("traffic:"):].split())
+            if vals.get("kernel") != kernel:
+                continue
+            if vals.get("source_sha") != source_hash(kernel):
+                return None
+            try:
+                return float(vals["bytes_per_launch"])
+            except (KeyError, ValueError):
+                return None
+    return None
 
 
 def cpu_baseline(idx: int, sample_heads: int):
@@ -357,22 +360,40 @@ def main():
     value = H * args.steps / elapsed
 
     roofline = None
+    roofline_other = None
     kernels = None
     if timer:
         kernels = timer.summary()
+        found = []
+        kr = w.topk * w.refit_every
         sw = kernels.get("sweep")
         if sw:
-            # algorithmic bytes: each sweep launch reads the float32 Phi of every head that still
-            # selects keys in that cycle once; ceil(t_h / (k R)) launches touch head h per step
-            kr = w.topk * w.refit_every
-            per_step = float(sum(-(-b // kr) * w.n * w.T * 4 for b in w.budgets))
+            # algorithmic bytes: each bounded-sweep launch reads the high 16-bit plane of the
+            # stored Phi (2 bytes per query and key) of every head that still selects keys in
+            # that cycle; ceil(t_h / (k R)) launches touch head h per step
+            per_step = float(sum(-(-b // kr) * w.n * w.T * 2 for b in w.budgets))
             per_launch = per_step * args.steps / sw["launches"]
             achieved = per_step * args.steps / (sw["total_ms"] * 1e-3) / 1e9
-            traffic = read_traffic()
-            roofline = {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                        "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
-                        "kernel": "k_sweep", "avg_launch_ms": round(sw["avg_ms"], 4),
-                        "launches": sw["launches"], "algorithmic_bytes_per_launch": per_launch}
+            found.append((sw["total_ms"], {
+                "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("k_sweep_band"),
+                "kernel": "k_sweep_band", "avg_launch_ms": round(sw["avg_ms"], 4), "launches": sw["launches"],
+                "algorithmic_bytes_per_launch": per_launch}))
+        ph = kernels.get("phi")
+        if ph:
+            # algorithmic flops: the float64 logits of every head, 2 n T d per head per launch
+            per_launch = 2.0 * w.n * w.T * w.d * H
+            achieved = per_launch * ph["launches"] / (ph["total_ms"] * 1e-3) / 1e12
+            found.append((ph["total_ms"], {
+                "bound": "mfma", "achieved": round(achieved, 2), "peak": F64_MFMA_PEAK_TFS, "unit": "TFLOP/s",
+                "frac": round(achieved / F64_MFMA_PEAK_TFS, 4), "traffic": read_traffic("k_phi"),
+                "kernel": "k_phi", "avg_launch_ms": round(ph["avg_ms"], 4), "launches": ph["launches"],
+                "algorithmic_flops_per_launch": per_launch}))
+        found.sort(key=lambda x: -x[0])
+        if found:
+            roofline = found[0][1]
+        if len(found) > 1:
+            roofline_other = found[1][1]
 
     cpu = cpu_baseline(args.workload, args.cpu_sample) if args.cpu_sample > 0 else None
 
@@ -394,6 +415,7 @@ def main():
                    f"{min(w.budgets)}..{max(w.budgets)} (sum {sum(w.budgets)})",
                    "topk": w.topk, "refit_every": w.refit_every, "parallelism": "none (one GPU)"},
         "roofline": roofline,
+        "roofline_next": roofline_other,
         "cpu_baseline": cpu,
         "kernels_ms": {k: round(v["total_ms"] / args.steps, 3) for k, v in (kernels or {}).items()},
         "head_status_nonzero": int(np.count_nonzero(status)),

@@ -94,7 +94,9 @@ typedef enum {
   AMC_K_OLS_NORMAL = 9, /* normal equations of the value fit */
   AMC_K_OLS_SOLVE = 10, /* Cholesky solve of the value fit */
   AMC_K_PACK = 11,   /* sorted, packed outputs */
-  AMC_NUM_KERNEL_CLASSES = 12
+  AMC_K_SWEEP_EXACT = 12, /* float32 sweep of the heads whose candidate band overflowed */
+  AMC_K_RESCORE = 13, /* float64 scores and columns of the band's candidates */
+  AMC_NUM_KERNEL_CLASSES = 14
 } amc_kernel_class;
 
 typedef struct {
@@ -116,8 +118,13 @@ typedef struct {
   int32_t nnls_max_iters; /* active-set iteration cap per refit (0 = 3 * budget + 30) */
   int32_t nnls_polish;    /* refinement refits after the last key (default 1) */
   double nnls_tol;        /* KKT tolerance relative to max |b| in unit-diagonal form (0 = 10 eps t) */
-  uint64_t phi_budget_bytes; /* Phi is stored when sum_h n_h T_h * 4 <= this; else every
-                              * sweep recomputes its Phi tiles from Q and K (same scores) */
+  uint64_t phi_budget_bytes; /* Phi is stored when sum_h n_h ceil8(T_h) * 4 <= this, as two
+                              * 16-bit planes (the high and low halves of its float32
+                              * values): a sweep reads the high plane, bounds every score,
+                              * and rescores the keys whose bounds reach the top k R + 1 in
+                              * float64 (when more than 128 do, that head's sweep reads
+                              * both planes).  Else every sweep recomputes its Phi tiles
+                              * from Q and K.  The picks are the same either way. */
   amc_dtype cv_dtype;     /* C_v output type (default AMC_F32) */
   uint32_t flags;         /* AMC_FLAG_* */
   void *timer;            /* optional amc_timer_create() handle; NULL = none */
@@ -128,6 +135,8 @@ typedef struct {
  *   shift      double [H]          the per-head logit shift s used for Phi
  *   pick       int32  [sum t_h]    original key index, in selection order, at cu_budgets[h]
  *   pick_score double [sum t_h]    r^T Phi[:, j] of each pick in the sweep that took it
+ *                                  (float64 Phi columns, or the float32 Phi of an exact
+ *                                  sweep: within float32 rounding of each other)
  *   weight     double [sum t_h]    final NNLS weight w of each pick (selection order)
  *   runner_up  double [sum c_h]    best score not taken by each cycle, at cu_cycles[h]
  *   nnls_iters int32  [sum c_h]    active-set iterations of the refit closing each cycle

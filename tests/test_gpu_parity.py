@@ -161,6 +161,41 @@ def test_compact_large_budgets(k, R):
         _assert_ok(replay_check(h.Q, h.K, h.V, budgets[i], k, R, res, i, beta_in=betas[i], trace=tr), f"head{i}")
 
 
+@pytest.mark.parametrize("cap", [0, 9])
+@pytest.mark.parametrize("k,R", [(1, 1), (4, 2)])
+def test_compact_band_overflow_path(monkeypatch, cap, k, R):
+    """The float32 sweep over both Phi planes, taken by a head whose candidate
+    band overflows: with the band cap at 0 every head takes it every cycle;
+    at 9 the heads switch between the two paths from cycle to cycle.  Same
+    bar as the default path."""
+    monkeypatch.setenv("AMC_BAND_CAP", str(cap))
+    shapes = [(300, 700, 40), (129, 257, 23), (520, 1100, 200)]
+    heads = [synth.make_head([36, i], n, T, 128, True, "bf16") for i, (n, T, _) in enumerate(shapes)]
+    budgets = [t for _, _, t in shapes]
+    betas = [synth.random_beta([37, i], T, 1.0) for i, (_, T, _) in enumerate(shapes)]
+    _say(f"band cap {cap} k={k} R={R}")
+    res = _run(heads, budgets, "bf16", k, R, beta_in=betas)
+    hs = res.head_status.cpu().numpy()
+    assert np.all(hs & (amc.HS_NNLS_CAP | amc.HS_NONFINITE) == 0), hs
+    tr = res.trace()
+    for i, h in enumerate(heads):
+        _assert_ok(replay_check(h.Q, h.K, h.V, budgets[i], k, R, res, i, beta_in=betas[i], trace=tr), f"head{i}")
+
+
+def test_band_and_exact_paths_agree(monkeypatch):
+    """The bounded sweep with float64 rescoring and the float32 sweep pick the
+    same keys where no two scores are within float32 rounding of each other
+    (these heads have none), so the whole outputs match to rounding."""
+    heads = [synth.make_head([38, i], 256, 900, 128, True, "bf16") for i in range(3)]
+    budgets = [30, 45, 18]
+    _say("band vs exact")
+    a = _run(heads, budgets, "bf16", 4, 2)
+    monkeypatch.setenv("AMC_BAND_CAP", "0")
+    b = _run(heads, budgets, "bf16", 4, 2)
+    assert torch.equal(a.sel_idx, b.sel_idx)
+    assert torch.allclose(a.beta, b.beta, rtol=1e-5, atol=1e-5)
+
+
 @pytest.mark.parametrize("dtype,d,k,R", [("bf16", 128, 4, 2), ("bf16", 64, 1, 1), ("f32", 64, 3, 3)])
 def test_compact_recompute_sweep(dtype, d, k, R):
     """Phi over the budget: every sweep rebuilds its Phi tiles from Q and K
