@@ -20,7 +20,7 @@ constexpr int kNnlsVecPerSlot = 15;  // float64 words of global NNLS state per b
 constexpr int kMaxBudget = 16384;  // largest budget per head (packed triangles indexed in int32)
 constexpr int kMaxSweepBlocks = 1024;  // sweep column blocks per head the merge handles
 constexpr int kBandCap = 128;    // candidates per head the float64 rescoring takes (more: exact sweep)
-constexpr int kRescoreRows = 64; // queries per block of the rescoring kernel
+constexpr int kRescoreRows = 256; // queries per block of the rescoring kernel
 
 // Per-head descriptor, computed on the host and copied to the device once per call.
 // All offsets are in elements of the array they index.

@@ -190,6 +190,34 @@ struct InRc<float> {
   __device__ static float f(float v) { return v; }
 };
 
+// Elements 16 u + 4 g + v (u < D / 16, v < 4) of the row at element offset
+// `off`, as float64, at k-step 4 u + v: 8-byte loads of 4 bf16 (16 bytes of
+// float32), issued unconditionally (the caller passes a valid row), zeroed
+// when !keep.
+template <int D, typename E>
+__device__ __forceinline__ void load_row4(const E *__restrict__ base, int64_t off, int g, bool keep, double *out) {
+#pragma unroll
+  for (int u = 0; u < D / 16; ++u) {
+    const int64_t at = off + 16 * u + 4 * g;
+    float x[4];
+    if constexpr (std::is_same<E, uint16_t>::value) {
+      const u32x2 w = *reinterpret_cast<const u32x2 *>(base + at);
+      x[0] = __uint_as_float(w.x << 16);
+      x[1] = __uint_as_float(w.x & 0xffff0000u);
+      x[2] = __uint_as_float(w.y << 16);
+      x[3] = __uint_as_float(w.y & 0xffff0000u);
+    } else {
+      const f32x4 w = *reinterpret_cast<const f32x4 *>(base + at);
+      x[0] = w.x;
+      x[1] = w.y;
+      x[2] = w.z;
+      x[3] = w.w;
+    }
+#pragma unroll
+    for (int v = 0; v < 4; ++v) out[4 * u + v] = keep ? double(x[v]) : 0.0;
+  }
+}
+
 template <int D, bool BF16>
 __global__ __launch_bounds__(RC_THREADS) void k_sweep_rc(
     const HeadDesc *__restrict__ desc, const void *__restrict__ Qv, const void *__restrict__ Kv,
@@ -224,11 +252,7 @@ __global__ __launch_bounds__(RC_THREADS) void k_sweep_rc(
 #pragma unroll
   for (int kb = 0; kb < KB; ++kb) {
     const int64_t key = kbase + kb * 16 + c16;
-#pragma unroll
-    for (int u = 0; u < NS / 4; ++u)
-#pragma unroll
-      for (int v = 0; v < 4; ++v)
-        kf[kb][4 * u + v] = key < Dh.T ? double(InRc<E>::f(K[(Dh.k_off + key) * D + 16 * u + 4 * g + v])) : 0.0;
+    load_row4<D>(K, (Dh.k_off + (key < Dh.T ? key : Dh.T - 1)) * D, g, key < Dh.T, kf[kb]);
   }
   // output rows of tile kb: key kbase + 16 kb + g + 4 e (keys past T contribute exp(-inf) = 0)
   double bb[KB][4], sc[KB][4];
@@ -244,11 +268,19 @@ __global__ __launch_bounds__(RC_THREADS) void k_sweep_rc(
   for (int64_t i0 = 0; i0 < Dh.n; i0 += QT) {
     __syncthreads();
     for (int gi = tid; gi < QT * D / 4; gi += RC_THREADS) {
+      // 4 elements per access, from a real row (rows past n are zeroed)
       const int qq = gi / (D / 4), c4 = gi % (D / 4);
       const bool ok = i0 + qq < Dh.n;
-      const int64_t src = (Dh.q_off + i0 + qq) * D + 4 * c4;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) qs[qq * QSTR + 4 * c4 + e] = ok ? Q[src + e] : E(0);
+      const int64_t src = (Dh.q_off + (ok ? i0 + qq : Dh.n - 1)) * D + 4 * c4;
+      if constexpr (BF16) {
+        u32x2 w = *reinterpret_cast<const u32x2 *>(Q + src);
+        if (!ok) w = u32x2{0u, 0u};
+        *reinterpret_cast<u32x2 *>(&qs[qq * QSTR + 4 * c4]) = w;
+      } else {
+        f32x4 w = *reinterpret_cast<const f32x4 *>(Q + src);
+        if (!ok) w = f32x4{0.f, 0.f, 0.f, 0.f};
+        *reinterpret_cast<f32x4 *>(&qs[qq * QSTR + 4 * c4]) = w;
+      }
     }
     if (tid < QT) rs[tid] = i0 + tid < Dh.n ? r[Dh.n_off + i0 + tid] : 0.0;
     __syncthreads();
@@ -673,11 +705,13 @@ __global__ __launch_bounds__(256) void k_panel(const HeadDesc *__restrict__ desc
 }
 
 // ---------------------------------------------------------------------------
-// rescoring: float64 Phi columns of the head's band keys over 64 queries, as
-// the panel computes them (float64 MFMA logits from the exact inputs, float64
-// exp), written to the stage, and their partial scores r^T Phi[:, j] over the
-// block's queries.  One block = 64 queries in 4 waves of 16; each 16-key group
-// of the band is one v_mfma_f64_16x16x4f64 tile per wave (keys as rows).
+// rescoring: float64 Phi columns of the head's band keys, as the panel
+// computes them (float64 MFMA logits from the exact inputs, float64 exp),
+// written to the stage, and their partial scores r^T Phi[:, j] over the
+// block's queries.  One block = kRescoreRows = 256 queries, 4 waves of 64;
+// each 16-key group of the band keeps its keys' MFMA operands in registers
+// (keys as rows of v_mfma_f64_16x16x4f64) while a wave walks its four
+// 16-query tiles (each over two accumulation chains, even and odd k-steps).
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
 __global__ __launch_bounds__(256) void k_rescore(const HeadDesc *__restrict__ desc, const void *__restrict__ Qv,
@@ -690,6 +724,7 @@ __global__ __launch_bounds__(256) void k_rescore(const HeadDesc *__restrict__ de
                                                  double *__restrict__ stage, double *__restrict__ part) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int NS = D / 4;  // MFMA k-steps over the head dimension
+  static_assert(kRescoreRows == 256, "4 waves x 4 tiles of 16 queries");
   __shared__ double red[4][16];
   const E *Q = static_cast<const E *>(Qv);
   const E *K = static_cast<const E *>(Kv);
@@ -705,42 +740,50 @@ __global__ __launch_bounds__(256) void k_rescore(const HeadDesc *__restrict__ de
   const int U = band_cnt[h];  // <= kBandCap when exact[h] == 0
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
-  const int64_t q = q0 + 16 * wave + c16;  // B operand column / output column of this lane
-  const bool qvalid = q < Dh.n;
-  // head dims 16 u + 4 g + v at k-step 4 u + v, for the keys (A) and the queries (B)
-  double qf[NS];
-#pragma unroll
-  for (int u = 0; u < NS / 4; ++u)
-#pragma unroll
-    for (int v = 0; v < 4; ++v)
-      qf[4 * u + v] = qvalid ? double(InRc<E>::f(Q[(Dh.q_off + q) * D + 16 * u + 4 * g + v])) : 0.0;
   const double s = shift[h];
-  const double rq = qvalid ? r[Dh.n_off + q] : 0.0;
+  const int64_t qw = q0 + 64 * wave + c16;  // this lane's query in tile qt: qw + 16 qt
   double *stg = stage + Dh.n_off * kBandCap;
   for (int g0 = 0; g0 < U; g0 += 16) {
     const int ui = g0 + c16;
     const bool uok = ui < U;
     const int j = uok ? band_list[int64_t(h) * kBandCap + ui] : 0;
     const double bj = (uok && beta_in) ? double(beta_in[Dh.k_off + j]) : 0.0;
-    f64x4 acc = {0.0, 0.0, 0.0, 0.0};
+    // A operand: head dims 16 u + 4 g + v of key j at k-step 4 u + v (every
+    // lane loads a real row, 4 elements at a time; lanes past the band zero it)
+    double kd[NS];
+    load_row4<D>(K, (Dh.k_off + j) * D, g, uok, kd);
+    double be[4];
 #pragma unroll
-    for (int u = 0; u < NS / 4; ++u)
+    for (int e = 0; e < 4; ++e) be[e] = __shfl(bj, g + 4 * e);  // bias of band key g0 + g + 4 e
+    double vs[4] = {0.0, 0.0, 0.0, 0.0};  // r_q Phi_qj summed over this lane's queries
+#pragma unroll 1
+    for (int qt = 0; qt < 4; ++qt) {
+      const int64_t qa = qw + 16 * qt;
+      const bool va = qa < Dh.n;
+      double xa[NS];
+      load_row4<D>(Q, (Dh.q_off + (va ? qa : Dh.n - 1)) * D, g, va, xa);
+      const double ra = va ? r[Dh.n_off + qa] : 0.0;
+      // two accumulation chains over the even and odd k-steps
+      f64x4 a0 = {0.0, 0.0, 0.0, 0.0}, a1 = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const double a = uok ? double(InRc<E>::f(K[(Dh.k_off + j) * D + 16 * u + 4 * g + v])) : 0.0;
-        acc = __builtin_amdgcn_mfma_f64_16x16x4f64(a, qf[4 * u + v], acc, 0, 0, 0);
+      for (int k = 0; k < NS; k += 2) {
+        a0 = __builtin_amdgcn_mfma_f64_16x16x4f64(kd[k], xa[k], a0, 0, 0, 0);
+        a1 = __builtin_amdgcn_mfma_f64_16x16x4f64(kd[k + 1], xa[k + 1], a1, 0, 0, 0);
       }
-    // element e of this lane: band key g0 + g + 4 e (its bias sits in lane g + 4 e), query q
+      // element e: band key g0 + g + 4 e, query qa
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int ue = g0 + g + 4 * e;
+        if (ue < U && va) {
+          const double p = exp(scale * (a0[e] + a1[e]) + be[e] - s);
+          stg[int64_t(ue) * Dh.n + qa] = p;
+          vs[e] = fma(ra, p, vs[e]);
+        }
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const int ue = g0 + g + 4 * e;
-      const double be = __shfl(bj, g + 4 * e);
-      double p = 0.0;
-      if (ue < U && qvalid) {
-        p = exp(scale * acc[e] + be - s);
-        stg[int64_t(ue) * Dh.n + q] = p;
-      }
-      double v = rq * p;
+      double v = vs[e];
       v += __shfl_xor(v, 1);
       v += __shfl_xor(v, 2);
       v += __shfl_xor(v, 4);
