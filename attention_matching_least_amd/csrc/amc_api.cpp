@@ -66,7 +66,7 @@ struct Plan {
            o_rhs = 0, o_cvsel = 0, o_pos = 0, o_cand_val = 0, o_cand_idx = 0, o_flist = 0, o_fcount = 0,
            o_dn = 0, o_L = 0, o_nnL = 0, o_nnP = 0, o_nnnp = 0, o_gA = 0, o_nnvec = 0, o_cand_lo = 0,
            o_cand_lidx = 0, o_cand_cnt = 0, o_band_list = 0, o_band_cnt = 0, o_exact = 0, o_stage = 0,
-           o_part = 0, total = 0;
+           o_part = 0, o_vt = 0, total = 0;
 };
 
 static amc_status check_problem(const amc_problem *p) {
@@ -117,7 +117,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   dm.in_bf16 = p->in_dtype == AMC_BF16;
   dm.scale = p->scale > 0.0f ? double(p->scale) : 1.0 / std::sqrt(double(d));
   pl.desc.assign(H, HeadDesc{});
-  int64_t phi = 0, nn = 0, tt = 0, t2 = 0, panel = 0, cblk = 0, sblk = 0, cyc = 0, TT = 0, tri = 0;
+  int64_t phi = 0, nn = 0, tt = 0, t2 = 0, panel = 0, cblk = 0, sblk = 0, cyc = 0, TT = 0, tri = 0, vt = 0;
   for (int h = 0; h < H; ++h) {
     HeadDesc &D = pl.desc[h];
     D.n = p->cu_q[h + 1] - p->cu_q[h];
@@ -126,8 +126,9 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     D.q_off = p->cu_q[h];
     D.k_off = p->cu_k[h];
     // rows of the stored Phi: float32 rows for the mass-feature entry point
-    // (4-key segments), 16-bit planes for the selection (8-key segments)
-    D.ldT = features_only ? (D.T + 3) / 4 * 4 : (D.T + 7) / 8 * 8;
+    // (4-key segments), 16-bit planes for the selection (whole 64-key tiles)
+    D.ldT = features_only ? (D.T + 3) / 4 * 4 : (D.T + 63) / 64 * 64;
+    D.vt_off = vt;
     D.phi_off = phi;
     D.n_off = nn;
     D.t_off = tt;
@@ -145,6 +146,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     }
     const int64_t cycles = ceil_div(D.t, pl.kR);
     phi += D.n * D.ldT;
+    vt += (D.T + 63) / 64 * 64 * d;
     nn += D.n;
     tt += D.t;
     t2 += D.t * D.t;
@@ -221,6 +223,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     pl.o_stage = take(8ull * nn * kBandCap);
     pl.o_part = take(8ull * H * kBandCap * dm.max_qblk);
   }
+  if (dm.in_bf16) pl.o_vt = take(2ull * vt);  // transposed value tiles of the mass-feature kernel
   pl.total = off;
   return AMC_OK;
 }
@@ -380,6 +383,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   b.shift = reinterpret_cast<double *>(ws + pl.o_shift);
   b.phi = nullptr;
   b.phi16 = pl.store_phi ? reinterpret_cast<uint16_t *>(ws + pl.o_phi) : nullptr;
+  b.vt = pl.dm.in_bf16 ? reinterpret_cast<uint16_t *>(ws + pl.o_vt) : nullptr;
   b.m = reinterpret_cast<double *>(ws + pl.o_m);
   b.r = reinterpret_cast<double *>(ws + pl.o_r);
   b.mhat = reinterpret_cast<double *>(ws + pl.o_mhat);
@@ -434,6 +438,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.sel_slot, pl.sum_T, 0, stream));
   if (head_status) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(head_status, dm.H, 0, stream));
   AMC_LAUNCH(AMC_K_SHIFT, launch_shift(dm, b, stream));
+  if (b.vt) AMC_LAUNCH(AMC_K_INIT, launch_vt(dm, b, stream));
   AMC_LAUNCH(AMC_K_PHI, launch_phi(dm, b, pl.store_phi ? 2 : 0, stream));
   for (int c = 0; c < pl.max_cycles; ++c) {
     if (pl.store_phi) {

@@ -12,6 +12,7 @@ namespace amc {
 constexpr int kShiftRows = 128;  // queries per block of the logit-maximum kernel
 constexpr int kPhiRows = 64;     // queries per block of the mass-feature kernel
 constexpr int kPhiKeys = 64;     // keys per tile of the mass-feature kernel
+constexpr int kPhi16Rows = 128;  // queries per block of the bf16 mass-feature kernel
 constexpr int kSweepCols = 256;  // columns per block of the correlation sweep
 constexpr int kMaxCycle = 255;   // largest k * R (keys per refit cycle)
 constexpr int kLdsMaxT = 192;    // largest budget of the LDS-resident value fit
@@ -28,7 +29,8 @@ struct HeadDesc {
   int64_t n, T, t;        // queries, keys, budget
   int64_t q_off;          // first row of the head in Q
   int64_t k_off;          // first row of the head in K, V, beta_in; first entry in sel_slot
-  int64_t ldT;            // row stride of the head's Phi (T rounded up to 4)
+  int64_t ldT;            // row stride of the head's Phi (T rounded up to 4 for the float32
+                          // output, to 64 for the stored planes: whole 64-key tiles)
   int64_t phi_off;        // first element of the head's Phi
   int64_t n_off;          // first entry in the per-query arrays (m, r, mhat, rows of Y)
   int64_t t_off;          // first entry in the per-slot arrays (= cu_budgets[h])
@@ -40,7 +42,7 @@ struct HeadDesc {
   int64_t n_sblk;         // logit-maximum blocks of the head
   int64_t cyc_off;        // first cycle of the head in the per-cycle trace arrays
   int64_t tri_off;        // first element of the head's packed triangle (value-fit factor)
-  int64_t pad;
+  int64_t vt_off;         // first element of the head's transposed value tiles (bf16 inputs)
 };
 static_assert(sizeof(HeadDesc) == 18 * 8, "HeadDesc layout");
 
@@ -52,7 +54,9 @@ struct Buffers {
   float *shift_part;   // [sum n_sblk]
   double *shift;       // [H]
   float *phi;          // [sum n*ldT] float32 Phi (the mass-feature entry point's output)
-  uint16_t *phi16;     // per head at 2*phi_off: high plane [n][ldT], then low plane [n][ldT]
+  uint16_t *phi16;     // per head at 2*phi_off: high plane [n][ldT], then low plane [n][ldT];
+                       // within each 64-key tile, key 16 kb + g + 4 e sits at 16 g + 4 kb + e
+  uint16_t *vt;        // bf16 inputs: per head at vt_off, [T/64 tiles][d][64] values, key-permuted
   double *m, *r, *mhat;  // [sum n]
   float *Y;            // [sum n][d]
   int32_t *sel_slot;   // [sum T]  0 = unselected, else 1 + slot
@@ -113,8 +117,10 @@ void timer_end(Timer *t, int cls, hipStream_t s);
 // Kernel launchers (each returns hipSuccess or the launch error).
 hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t s);
 hipError_t launch_shift(const Dims &dm, const Buffers &b, hipStream_t s);
-// store: 0 = no Phi, 1 = float32 Phi to b.phi, 2 = the two 16-bit planes to b.phi16
+// store: 0 = no Phi, 1 = float32 Phi to b.phi, 2 = the two 16-bit planes to b.phi16.
+// bf16 inputs with b.vt set (store 0 or 2) take the tiled kernel, after launch_vt.
 hipError_t launch_phi(const Dims &dm, const Buffers &b, int store, hipStream_t s);
+hipError_t launch_vt(const Dims &dm, const Buffers &b, hipStream_t s);
 // gated: only the heads with b.exact[h] != 0 (else every head)
 hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int gated, hipStream_t s);
 hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);

@@ -155,6 +155,10 @@ struct In<float> {
 // i / 4 (rows interleaved across the lane groups).  With S^T = K Q^T the rows
 // are keys, so lane group g, element e of key block kb holds this key:
 __device__ __forceinline__ int phi_key(int kb, int g, int e) { return kb * 16 + g + 4 * e; }
+// The stored planes keep each 64-key tile in a lane-friendly order: key
+// 16 kb + g + 4 e at position 16 g + 4 kb + e, so that the 16 values a lane
+// holds for one query are 16 consecutive positions.
+__device__ __forceinline__ int store_pos(int kb, int g, int e) { return 16 * g + 4 * kb + e; }
 // The Phi V product consumes those values as its A operand at k-step (kb, e)
 // (A[query][k = g]); its B operand B[k = g][dim] is then V[phi_key(kb, g, e)][dim],
 // a row of the V tile, read directly.
@@ -254,7 +258,8 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
         if (k0 + kl < Dh.T) p = exp(scale * acc[e] + double(sbias[kl]) - s);
         msum += p;
         pf[kb][e] = float(p);
-        if constexpr (STORE != 0) ps[wave][c16 * PSTR + kl] = pf[kb][e];
+        if constexpr (STORE == 1) ps[wave][c16 * PSTR + kl] = pf[kb][e];
+        if constexpr (STORE == 2) ps[wave][c16 * PSTR + store_pos(kb, g, e)] = pf[kb][e];
       }
     }
     if constexpr (STORE == 1) {
@@ -273,10 +278,9 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
         }
       }
     } else if constexpr (STORE == 2) {
-      // 8 keys of one row per lane: their high halves leave as one 16-byte
-      // segment of the high plane, their low halves as one of the low plane
-      // (ldT is a multiple of 8, so a segment that starts below ldT ends
-      // within the row)
+      // 8 stored positions of one row per lane: their high halves leave as
+      // one 16-byte segment of the high plane, their low halves as one of the
+      // low plane (ldT is a multiple of 64: whole tiles)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -391,6 +395,319 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
   if (bad && head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
 }
 
+// ---------------------------------------------------------------------------
+// value tiles for the bf16 mass-feature kernel: per head and 64-key tile, V
+// transposed to [d][64] with the keys in the order the Phi V product reduces
+// them: position 32 c + 8 g + 4 j + e holds key 32 c + 16 j + g + 4 e (keys
+// past T are zero).  One block = one tile.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void k_vt(const HeadDesc *__restrict__ desc, const uint16_t *__restrict__ V,
+                                            uint16_t *__restrict__ vt) {
+  constexpr int VSTR = D + 8;  // bf16 per staged row (16-byte pad)
+  __shared__ __attribute__((aligned(16))) uint16_t vs[64 * VSTR];
+  const int h = blockIdx.y;
+  const HeadDesc Dh = desc[h];
+  const int tile = blockIdx.x;
+  const int64_t k0 = int64_t(tile) * 64;
+  if (k0 >= Dh.T) return;
+  const int tid = threadIdx.x;
+  for (int gi = tid; gi < 64 * D / 8; gi += 256) {
+    const int key = gi / (D / 8), c = gi % (D / 8);
+    u32x4 w = {0u, 0u, 0u, 0u};
+    if (k0 + key < Dh.T) w = *reinterpret_cast<const u32x4 *>(V + (Dh.k_off + k0 + key) * D + 8 * c);
+    *reinterpret_cast<u32x4 *>(&vs[key * VSTR + 8 * c]) = w;
+  }
+  __syncthreads();
+  uint16_t *out = vt + Dh.vt_off + int64_t(tile) * D * 64;
+  for (int gi = tid; gi < D * 8; gi += 256) {
+    const int dim = gi / 8, c8 = gi % 8;
+    uint32_t w[4];
+#pragma unroll
+    for (int t2 = 0; t2 < 4; ++t2) {
+      uint32_t pair[2];
+#pragma unroll
+      for (int h2 = 0; h2 < 2; ++h2) {
+        const int pos = 8 * c8 + 2 * t2 + h2;
+        const int c = pos >> 5, g = (pos >> 3) & 3, j = (pos >> 2) & 1, e = pos & 3;
+        pair[h2] = vs[(32 * c + 16 * j + g + 4 * e) * VSTR + dim];
+      }
+      w[t2] = pair[0] | (pair[1] << 16);
+    }
+    *reinterpret_cast<u32x4 *>(out + dim * 64 + 8 * c8) = u32x4{w[0], w[1], w[2], w[3]};
+  }
+}
+
+// ---------------------------------------------------------------------------
+// mass features for bf16 inputs, tiled for the MFMA pipes: one block = 128
+// queries in 8 waves of 16 (two waves per SIMD).  The 64-key tiles of K and of
+// the transposed V reach LDS by asynchronous global-to-LDS copies, double
+// buffered: tile t + 1 is in flight while tile t computes.  Per tile and wave:
+//   logits  S^T = K Q^T on v_mfma_f64_16x16x4f64 (keys as rows, four 16-key
+//           blocks as four accumulation chains), head dims 32 a + 8 g + b at
+//           k-step 8 a + b, so a lane's K operands for one a are one 16-byte
+//           read (K rows padded by one 16-byte slot: conflict-free reads);
+//   Phi     float64 exp, row sums for m, the two 16-bit planes written from
+//           registers (each lane's 16 values are 16 consecutive positions);
+//   Phi V   v_mfma_f32_16x16x32_bf16 with Phi = hi + mid + lo exactly (three
+//           bf16 terms, split by truncation), V operands one 16-byte read.
+// STORE: 0 = Phi not stored (every sweep recomputes it), 2 = stored planes.
+// Blocks map to heads XCD by XCD when xcd_map is set (H a multiple of 8):
+// the blocks of one head share one L2.
+// ---------------------------------------------------------------------------
+constexpr int P16_WAVES = kPhi16Rows / 16;
+
+template <int D, int STORE>
+__global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
+    const HeadDesc *__restrict__ desc, int H, int nqb, int xcd_map, const uint16_t *__restrict__ Q,
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ vt, const float *__restrict__ beta_in,
+    double scale, const float *__restrict__ shift_part, double *__restrict__ shift_out,
+    double *__restrict__ tr_shift, uint16_t *__restrict__ phi16, double *__restrict__ m_out,
+    double *__restrict__ r_out, float *__restrict__ Y_out, int32_t *__restrict__ head_status) {
+  constexpr int KCH = D / 8;        // 16-byte chunks per K row
+  constexpr int NS = D / 4;         // k-steps of the logit MFMA
+  constexpr int NA = D / 32;        // 16-byte K reads per key block
+  constexpr int NU = D / 16;        // 16-dim output blocks of Phi V
+  constexpr int KROW = KCH + 1;         // 16-byte slots per K row in LDS (one of padding)
+  constexpr int KSLOT = 64 * KROW;      // slots per K tile
+  constexpr int VSLOT = D * 9;          // slots per V tile: D rows of 8 chunks and a pad
+  constexpr int KWORDS = KSLOT * 4;     // uint32 per K tile
+  constexpr int VWORDS = VSLOT * 4;     // uint32 per V tile
+  __shared__ __attribute__((aligned(16))) uint32_t lk0[KWORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t lk1[KWORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t lv0[VWORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t lv1[VWORDS];
+  __shared__ __attribute__((aligned(16))) float sb[2][64];
+  __shared__ double s_shift;
+
+  int h, qb;
+  {
+    const int b = blockIdx.x;
+    if (xcd_map) {
+      const int x = b & 7, slot = b >> 3;
+      h = x + 8 * (slot / nqb);
+      qb = slot % nqb;
+    } else {
+      h = b / nqb;
+      qb = b % nqb;
+    }
+  }
+  if (h >= H) return;
+  const HeadDesc Dh = desc[h];
+  const int64_t q0 = int64_t(qb) * kPhi16Rows;
+  if (q0 >= Dh.n) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+
+  if (tid < 64) {
+    float v = -INFINITY;
+    for (int64_t i = tid; i < Dh.n_sblk; i += 64) v = fmaxf(v, shift_part[Dh.sblk_off + i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (tid == 0) s_shift = double(v);
+  }
+
+  // B operand of the logits: query q, head dims 32 a + 8 g + b at k-step 8 a + b
+  const int64_t qw = q0 + 16 * wave;
+  const int64_t q = qw + c16;
+  const bool qvalid = q < Dh.n;
+  // (kept as bf16 pairs; each becomes a float64 operand where it is used)
+  u32x4 qraw[NA];
+#pragma unroll
+  for (int a = 0; a < NA; ++a) {
+    qraw[a] = *reinterpret_cast<const u32x4 *>(Q + (Dh.q_off + (qvalid ? q : Dh.n - 1)) * D + 32 * a + 8 * g);
+    if (!qvalid) qraw[a] = u32x4{0u, 0u, 0u, 0u};
+  }
+
+  const int64_t T = Dh.T;
+  const int ntiles = int((T + 63) / 64);
+  // Asynchronous copies of tile `tile` into one buffer set: each copy fills
+  // 64 consecutive 16-byte slots (lane i the i-th); the copies are dealt to
+  // the waves in turn.  K rows are KROW slots (chunk m of key k at slot
+  // k KROW + m), V rows (dims) 9 slots; a padding slot takes a duplicate of
+  // the row's first chunk.  The biases take one 4-byte copy (wave 0), slot i
+  // holding key key_at(i) so that a lane's 16 biases are consecutive.
+  // Sources are a per-head base plus a 32-bit byte offset.
+  const char *kbase = reinterpret_cast<const char *>(K + Dh.k_off * D);
+  const char *vbase = reinterpret_cast<const char *>(vt + Dh.vt_off);
+  const char *bbase = beta_in ? reinterpret_cast<const char *>(beta_in + Dh.k_off) : nullptr;
+  auto issue = [&](int tile, uint32_t *lk, uint32_t *lv, float *lb) {
+    const int k0 = tile * 64;
+#pragma unroll
+    for (int inst = wave; inst < KSLOT / 64; inst += P16_WAVES) {
+      const int slot = inst * 64 + lane;
+      const int key = slot / KROW, m = slot % KROW;
+      const int row = k0 + key < T ? k0 + key : int(T) - 1;
+      const uint32_t off = uint32_t(row * D + 8 * (m < KCH ? m : 0)) * 2u;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(kbase + off),
+                                       (void __attribute__((address_space(3))) *)(lk + inst * 256), 16, 0, 0);
+    }
+#pragma unroll
+    for (int inst = wave; inst < VSLOT / 64; inst += P16_WAVES) {
+      const int slot = inst * 64 + lane;
+      const int dim = slot / 9, lc = slot % 9;
+      const uint32_t off = uint32_t((tile * D + dim) * 64 + 8 * (lc < 8 ? lc : 0)) * 2u;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(vbase + off),
+                                       (void __attribute__((address_space(3))) *)(lv + inst * 256), 16, 0, 0);
+    }
+    if (bbase && wave == 0) {
+      const int key = k0 + 16 * ((lane >> 2) & 3) + (lane >> 4) + 4 * (lane & 3);
+      const uint32_t off = uint32_t(key < T ? key : int(T) - 1) * 4u;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(bbase + off),
+                                       (void __attribute__((address_space(3))) *)lb, 4, 0, 0);
+    }
+  };
+
+  f32x4 uacc[NU];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  double msum = 0.0;
+
+  // One tile from the buffer set (lk, lv, lb).  The copies of the next tile
+  // (into the other set) go out first; this wave waits for them once, after
+  // its exps, and the barrier that closes the tile publishes them.
+  auto compute = [&](int tile, const uint32_t *lk, const uint32_t *lv, const float *lb, bool next,
+                     uint32_t *nk, uint32_t *nv, float *nb, double s) {
+    const int64_t k0 = int64_t(tile) * 64;
+    if (next) issue(tile + 1, nk, nv, nb);
+    f64x4 acc[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) acc[kb] = f64x4{0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+    for (int a = 0; a < NA; ++a) {
+      u32x4 kw[4];
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+        kw[kb] = *reinterpret_cast<const u32x4 *>(lk + ((kb * 16 + c16) * KROW + 4 * a + g) * 4);
+#pragma unroll
+      for (int b = 0; b < 8; ++b) {
+        const uint32_t qw2 = qraw[a][b >> 1];
+        const double qv = double(__uint_as_float((b & 1) ? (qw2 & 0xffff0000u) : (qw2 << 16)));
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const uint32_t wd = kw[kb][b >> 1];
+          const double kv = double(__uint_as_float((b & 1) ? (wd & 0xffff0000u) : (wd << 16)));
+          acc[kb] = __builtin_amdgcn_mfma_f64_16x16x4f64(kv, qv, acc[kb], 0, 0, 0);
+        }
+      }
+    }
+    f32x4 bz[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+      bz[kb] = bbase ? *reinterpret_cast<const f32x4 *>(lb + 16 * g + 4 * kb) : f32x4{0.f, 0.f, 0.f, 0.f};
+    // Phi for keys 16 kb + g + 4 e and query q; x = float32 Phi
+    float x[4][4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int kl = phi_key(kb, g, e);
+        double p = 0.0;
+        if (k0 + kl < T) p = exp(scale * acc[kb][e] + double(bz[kb][e]) - s);
+        msum += p;
+        x[kb][e] = float(p);
+      }
+    // the next tile's copies have landed
+    __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (STORE == 2) {
+      if (qvalid) {
+        // positions 16 g + 4 kb + e: 16 consecutive, two 16-byte segments per plane
+        uint16_t *hp = phi16 + 2 * Dh.phi_off;
+        uint16_t *lp = hp + Dh.n * Dh.ldT;
+        uint32_t hw[8], lw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t u0 = __float_as_uint(x[i >> 1][2 * (i & 1)]);
+          const uint32_t u1 = __float_as_uint(x[i >> 1][2 * (i & 1) + 1]);
+          hw[i] = (u0 >> 16) | (u1 & 0xffff0000u);
+          lw[i] = (u0 & 0xffffu) | (u1 << 16);
+        }
+        const int64_t at = q * Dh.ldT + k0 + 16 * g;
+        __builtin_nontemporal_store(u32x4{hw[0], hw[1], hw[2], hw[3]}, reinterpret_cast<u32x4 *>(hp + at));
+        __builtin_nontemporal_store(u32x4{hw[4], hw[5], hw[6], hw[7]}, reinterpret_cast<u32x4 *>(hp + at + 8));
+        __builtin_nontemporal_store(u32x4{lw[0], lw[1], lw[2], lw[3]}, reinterpret_cast<u32x4 *>(lp + at));
+        __builtin_nontemporal_store(u32x4{lw[4], lw[5], lw[6], lw[7]}, reinterpret_cast<u32x4 *>(lp + at + 8));
+      }
+    }
+    // Phi V: reduction index k = 8 g + 4 j + e of chunk c is key phi_key(2 c + j, g, e)
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t w[3][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          uint32_t t[3][2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const float v = x[2 * c + j][2 * e2 + h2];
+            const float hi = __uint_as_float(__float_as_uint(v) & 0xffff0000u);
+            const float r1 = v - hi;
+            const float mi = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+            const float lo = r1 - mi;
+            t[0][h2] = __float_as_uint(hi);
+            t[1][h2] = __float_as_uint(mi);
+            t[2][h2] = __float_as_uint(lo);
+          }
+#pragma unroll
+          for (int qq = 0; qq < 3; ++qq) w[qq][2 * j + e2] = (t[qq][0] >> 16) | (t[qq][1] & 0xffff0000u);
+        }
+#pragma unroll
+      for (int db = 0; db < NU; ++db) {
+        const u32x4 vv = *reinterpret_cast<const u32x4 *>(lv + ((db * 16 + c16) * 9 + 4 * c + g) * 4);
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+        for (int qq = 2; qq >= 0; --qq)
+          uacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, u32x4{w[qq][0], w[qq][1], w[qq][2], w[qq][3]}), bv, uacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  // prologue: tile 0 into buffer set 0
+  issue(0, lk0, lv0, sb[0]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const double s = s_shift;
+  if (qb == 0 && tid == 0) {
+    shift_out[h] = s;
+    if (tr_shift) tr_shift[h] = s;
+  }
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    // even tiles from buffer set 0, odd tiles from set 1
+    compute(tile, lk0, lv0, sb[0], tile + 1 < ntiles, lk1, lv1, sb[1], s);
+    __syncthreads();
+    if (tile + 1 >= ntiles) break;
+    compute(tile + 1, lk1, lv1, sb[1], tile + 2 < ntiles, lk0, lv0, sb[0], s);
+    __syncthreads();
+  }
+
+  // m for query q: partial sums sit in the four lanes c16, c16+16, c16+32, c16+48
+  msum += __shfl_xor(msum, 16);
+  msum += __shfl_xor(msum, 32);
+  bool bad = false;
+  if (g == 0 && qvalid) {
+    m_out[Dh.n_off + q] = msum;
+    if (r_out) r_out[Dh.n_off + q] = msum;
+    bad |= !isfinite(msum);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double mq = __shfl(msum, 4 * g + e);
+    const int64_t qy = qw + 4 * g + e;
+    if (qy < Dh.n) {
+#pragma unroll
+      for (int db = 0; db < NU; ++db) {
+        const float y = float(double(uacc[db][e]) / mq);
+        bad |= !isfinite(y);
+        Y_out[(Dh.n_off + qy) * D + db * 16 + c16] = y;
+      }
+    }
+  }
+  if (bad && head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
+}
+
 }  // namespace
 
 hipError_t launch_copy_words(uint64_t *dst, const uint64_t *src, int64_t count, hipStream_t s) {
@@ -449,9 +766,39 @@ static void launch_phi_store(const Dims &dm, const Buffers &b, hipStream_t s) {
 #undef AMC_PHI_ARGS
 }
 
+template <int STORE>
+static void launch_phi16(const Dims &dm, const Buffers &b, hipStream_t s) {
+  const int nqb = int((dm.max_n + kPhi16Rows - 1) / kPhi16Rows);
+  const int xcd_map = (dm.H % 8 == 0) ? 1 : 0;
+  dim3 grid(unsigned(nqb * dm.H));
+  const uint16_t *Q = static_cast<const uint16_t *>(b.Q);
+  const uint16_t *K = static_cast<const uint16_t *>(b.K);
+#define AMC_PHI16_ARGS b.desc, dm.H, nqb, xcd_map, Q, K, b.vt, b.beta_in, dm.scale, b.shift_part, b.shift, b.tr_shift, \
+    b.phi16, b.m, b.r, b.Y, b.head_status
+  if (dm.d == 128)
+    hipLaunchKernelGGL((k_phi16<128, STORE>), grid, dim3(kPhi16Rows * 4), 0, s, AMC_PHI16_ARGS);
+  else
+    hipLaunchKernelGGL((k_phi16<64, STORE>), grid, dim3(kPhi16Rows * 4), 0, s, AMC_PHI16_ARGS);
+#undef AMC_PHI16_ARGS
+}
+
+hipError_t launch_vt(const Dims &dm, const Buffers &b, hipStream_t s) {
+  if (!b.vt || !dm.in_bf16) return hipErrorInvalidValue;
+  dim3 grid(unsigned((dm.max_T + 63) / 64), unsigned(dm.H));
+  const uint16_t *V = static_cast<const uint16_t *>(b.V);
+  if (dm.d == 128) hipLaunchKernelGGL((k_vt<128>), grid, dim3(256), 0, s, b.desc, V, b.vt);
+  else hipLaunchKernelGGL((k_vt<64>), grid, dim3(256), 0, s, b.desc, V, b.vt);
+  return hipGetLastError();
+}
+
 hipError_t launch_phi(const Dims &dm, const Buffers &b, int store, hipStream_t s) {
   if (store == 1 && !b.phi) return hipErrorInvalidValue;
   if (store == 2 && !b.phi16) return hipErrorInvalidValue;
+  if (dm.in_bf16 && b.vt && store != 1) {
+    if (store == 2) launch_phi16<2>(dm, b, s);
+    else launch_phi16<0>(dm, b, s);
+    return hipGetLastError();
+  }
   if (store == 1) launch_phi_store<1>(dm, b, s);
   else if (store == 2) launch_phi_store<2>(dm, b, s);
   else launch_phi_store<0>(dm, b, s);

@@ -65,6 +65,13 @@ __device__ void block_sort256(double *v, int *ix) {
   }
 }
 
+// Stored Phi planes keep each 64-key tile in the order the mass-feature
+// kernel writes it: position 16 g + 4 kb + e holds key 16 kb + g + 4 e.
+__device__ __forceinline__ int64_t key_at(int64_t pos) {
+  const int p = int(pos & 63);
+  return (pos & ~int64_t(63)) + 16 * ((p >> 2) & 3) + (p >> 4) + 4 * (p & 3);
+}
+
 __device__ __forceinline__ int cycle_keys(const HeadDesc &D, int cycle, int kR, int64_t *S0) {
   const int64_t s0 = int64_t(cycle) * kR;
   *S0 = s0;
@@ -105,9 +112,9 @@ __global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc
   if (gate && gate[h] == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t j0 = int64_t(blk) * kSweepCols + 4 * lane;
+  const int64_t j0 = int64_t(blk) * kSweepCols + 4 * lane;  // stored position
   double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-  if (j0 < D.T) {
+  if (j0 < D.ldT) {  // ldT is a multiple of 64: the 8-byte segments lie within the row
     const uint16_t *ph = phi16 + 2 * D.phi_off + j0;
     const uint16_t *pl = ph + D.n * D.ldT;
     const double *rr = r + D.n_off;
@@ -146,10 +153,11 @@ __global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc
   red[wave][4 * lane + 2] = a2;
   red[wave][4 * lane + 3] = a3;
   __syncthreads();
-  const int64_t col = int64_t(blk) * kSweepCols + tid;
+  const int64_t pos = int64_t(blk) * kSweepCols + tid;
+  const int64_t col = key_at(pos);
   double c = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
   int idx = int(col);
-  if (col >= D.T || sel_slot[D.k_off + col] != 0) {
+  if (pos >= D.ldT || col >= D.T || sel_slot[D.k_off + col] != 0) {
     c = -INFINITY;
     idx = INT_MAX;
   } else if (!isfinite(c)) {
@@ -455,7 +463,8 @@ __global__ __launch_bounds__(256) void k_merge(const HeadDesc *__restrict__ desc
 // Phi and of r, the float64 rescoring's own rounding, and an absolute term for
 // values below float32's normal range.  One block = 256 keys: each lane takes
 // 8 keys of every 8th row (16-byte loads), P and N accumulate in float32 per
-// lane and in float64 across the 8 row streams.  Out: the block's top-(Kc+1)
+// lane and in float64 across the 8 row streams; each column is a stored
+// position, mapped to its key at the end.  Out: the block's top-(Kc+1)
 // lower bounds, sorted (cand_lo / cand_lidx), and in key order every key whose
 // upper bound reaches the (Kc+1)-th of them (cand_val = upper bound,
 // cand_idx, cand_cnt = their number, -1 if a bound is not finite).
@@ -503,7 +512,7 @@ __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__
 #pragma unroll
   for (int k = 0; k < 8; ++k) P[k] = N[k] = 0.0f;
   double ra = 0.0;
-  if (j0 < D.ldT) {  // ldT is a multiple of 8: the 16-byte segment lies within the row
+  if (j0 < D.ldT) {  // ldT is a multiple of 64: the 16-byte segment lies within the row
     const uint16_t *p = phi16 + 2 * D.phi_off + j0;
     const double *rr = r + D.n_off;
     const int64_t ld = D.ldT;
@@ -527,7 +536,8 @@ __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__
   *reinterpret_cast<float4 *>(&ps_n[stream][8 * cg + 4]) = make_float4(N[4], N[5], N[6], N[7]);
   if (cg == 0) ra_s[stream] = ra;  // lane cg = 0 always reads (block start < T <= ldT)
   __syncthreads();
-  const int64_t col = int64_t(blk) * kSweepCols + tid;
+  const int64_t pos = int64_t(blk) * kSweepCols + tid;  // stored position of this thread's key
+  const int64_t col = key_at(pos);
   double Pd = 0.0, Nd = 0.0, rs = 0.0;
 #pragma unroll
   for (int st = 0; st < 8; ++st) {
@@ -535,7 +545,7 @@ __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__
     Nd += double(ps_n[st][tid]);
     rs += ra_s[st];
   }
-  const bool valid = col < D.T && sel_slot[D.k_off + col] == 0;
+  const bool valid = pos < D.ldT && col < D.T && sel_slot[D.k_off + col] == 0;
   const double crel = 2.0 * (double(D.n) * 0.125 + 16.0) * 0x1p-24 + 0x1p-22;
   const double slack = crel * (Pd - Nd) + (rs + double(D.n)) * 0x1p-120;
   const double c7 = 0x1.00001p-7;
