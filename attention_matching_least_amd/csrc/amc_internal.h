@@ -133,6 +133,9 @@ hipError_t launch_panel(const Dims &dm, const Buffers &b, int cycle, int cyc_key
 hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);
 hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish,
                        const NnlsParams &np, hipStream_t s);
+// the workspace-resident refits (heads above kNnlsLdsT), called by launch_nnls
+hipError_t launch_nnls_global(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish,
+                              const NnlsParams &np, hipStream_t s);
 hipError_t launch_resid(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);
 hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s);
 hipError_t launch_pack(const Dims &dm, const Buffers &b, void *Ck, float *beta, void *Cv,

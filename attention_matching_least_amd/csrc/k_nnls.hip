@@ -32,7 +32,9 @@
 // between entries).  Between the refits of one compaction the factor and the
 // free set persist in the workspace.
 //
-// GPU mapping: one 256-thread block per system.  Triangular work runs in
+// GPU mapping: one block per system (256 threads; 512 for the workspace-
+// resident state of large budgets, whose passes over global memory are
+// latency-bound, so more rows are in flight at once).  Triangular work runs in
 // 16-row blocks: one wave solves the 16 x 16 diagonal block in registers
 // (v_readlane broadcasts), then every thread updates one of the rows beyond
 // it.  The state lives in LDS for budgets up to kNnlsLdsT; above that the same
@@ -47,1065 +49,10 @@
 
 #include "amc_internal.h"
 
+#define AMC_NNLS_NT 256
 namespace amc {
 namespace {
-
-constexpr int NT = 256;
-constexpr int NW = NT / 64;
-constexpr int TB = 16;             // triangular block
-constexpr int NB = 8;              // candidates that may enter together
-constexpr int NRHS = NB + 1;       // right-hand sides of a block entry (rows 0..8)
-constexpr int NROW = NRHS + 2;     // scratch rows: 0 solve vector, 1 change list, 2 scaled change,
-                                   // 3..6 partial sums, 7 removed column, 8 y = L^-1 g_P,
-                                   // 9 u at the last snapshot, 10 g at the last snapshot
-constexpr unsigned char F_PASSIVE = 1, F_BLOCKED = 2, F_NEW = 4, F_DROP = 8, F_CAND = 16;
-constexpr double PIV_TOL = 1e-14;  // smallest acceptable squared pivot in unit-diagonal form
-static_assert(NRHS <= 3 * NW, "diagonal solves take three right-hand sides per wave");
-static_assert(NRHS == 9, "row roles assume nine right-hand sides");
-
-__device__ __forceinline__ int tri(int r) { return r * (r + 1) / 2; }
-
-// Compile-time loop: f(integral_constant<int, I>) for I in [B, E).  Register
-// arrays indexed only through it keep constant indices, so they stay in
-// registers.
-template <int B, int E, typename F>
-__device__ __forceinline__ void static_for(F &&f) {
-  if constexpr (B < E) {
-    f(std::integral_constant<int, B>{});
-    static_for<B + 1, E>(f);
-  }
-}
-
-// double broadcast from a (wave-uniform) lane
-__device__ __forceinline__ double rl(double x, int lane) {
-  const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
-  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
-  return __hiloint2double(hi, lo);
-}
-
-__device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
-}
-
-struct Red {
-  double v[NW];
-  int i[NW];
-};
-
-// Block max of v (ties to the lower index); returns the winning index, -1 if
-// no thread passed a valid one.  Every thread gets the result.
-__device__ __forceinline__ int block_argmax(double v, int idx, Red *red, double *out_v) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const double ov = __shfl_xor(v, off);
-    const int oi = __shfl_xor(idx, off);
-    if (oi >= 0 && (idx < 0 || ov > v || (ov == v && oi < idx))) {
-      v = ov;
-      idx = oi;
-    }
-  }
-  __syncthreads();
-  if (lane == 0) {
-    red->v[wave] = v;
-    red->i[wave] = idx;
-  }
-  __syncthreads();
-  v = red->v[0];
-  idx = red->i[0];
-  for (int w = 1; w < NW; ++w) {
-    const double ov = red->v[w];
-    const int oi = red->i[w];
-    if (oi >= 0 && (idx < 0 || ov > v || (ov == v && oi < idx))) {
-      v = ov;
-      idx = oi;
-    }
-  }
-  *out_v = v;
-  return idx;
-}
-
-__device__ __forceinline__ int block_count(int c, Red *red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
-  __syncthreads();
-  if (lane == 0) red->i[wave] = c;
-  __syncthreads();
-  int s = 0;
-  for (int w = 0; w < NW; ++w) s += red->i[w];
-  return s;
-}
-
-// Small per-block scratch (always LDS).
-struct Blk {
-  double dots[NRHS * NRHS];  // Gram of the forward-solved candidate rows (lower triangle)
-  double Gc[NB * NB];        // scaled G among the candidates
-  double E[NB * NB];         // factor entries among accepted candidates
-  double Dg[NB];             // their diagonal
-  double yb[NB];             // their entries of L^-1 g
-  double cs[2 * TB];         // rotations of one block of the rank-one update
-  int cand[NB];              // entering candidates
-  int accb[NB];              // accepted candidates, in order
-  int ctl[8];                // [1], [4] scan state, [2] accepted count, [3] largest entering block,
-                             // [5] size of the last entering block
-  int wc[NW];                // per-wave counts of a compaction
-  int np;                    // free-set size
-};
-
-// State of one solve.  Vectors are indexed by variable (u, g, dg, flag, rows
-// 9 and 10) or by factor position (plist, the other rows).
-struct St {
-  double *L;      // packed lower factor of Gs_PP, rows in free-set order
-  double *u;      // scaled iterate
-  double *g;      // scaled gradient bs - Gs u
-  double *dg;     // sqrt(G_aa)
-  double *rows;   // NROW scratch rows of mp (roles at NROW)
-  double *x0;     // row 0: solve vector (may live apart from rows)
-  double *yv;     // row 8: y = L^-1 g_P (may live apart from rows)
-  int *plist;     // free set in factor order
-  unsigned char *flag;
-  Blk *bk;
-  int mp;         // row stride (largest p of the system)
-  __device__ __forceinline__ double *row(int b) const { return b == 0 ? x0 : (b == 8 ? yv : rows + b * mp); }
-};
-
-// LDS bytes of the state for systems up to maxp variables (LDS variant)
-__host__ __device__ constexpr size_t nnls_smem_bytes(int maxp) {
-  return size_t(8) * (size_t(maxp) * (maxp + 1) / 2 + size_t(3 + NROW) * maxp) + 4 * size_t(maxp) +
-         ((size_t(maxp) + 15) & ~size_t(15));
-}
-
-// LDS bytes of the global variant: the two solve vectors, when they fit.
-constexpr int kGlobalLdsRowsMax = 4096;
-__host__ __device__ constexpr size_t nnls_global_smem_bytes(int64_t max_t) {
-  return max_t <= kGlobalLdsRowsMax ? size_t(16) * size_t(max_t) : 0;
-}
-
-__device__ __forceinline__ St carve_lds(char *base, int maxp, Blk *bk) {
-  St s;
-  s.mp = maxp;
-  s.bk = bk;
-  double *d = reinterpret_cast<double *>(base);
-  s.L = d;
-  d += tri(maxp);
-  s.u = d;
-  d += maxp;
-  s.g = d;
-  d += maxp;
-  s.dg = d;
-  d += maxp;
-  s.rows = d;
-  s.x0 = d;
-  s.yv = d + 8 * maxp;
-  d += NROW * maxp;
-  s.plist = reinterpret_cast<int *>(d);
-  s.flag = reinterpret_cast<unsigned char *>(s.plist + maxp);
-  return s;
-}
-
-// Global-memory state of one head: u, g, dg, the scratch rows, then the flag
-// bytes; the solve vectors go to LDS (lds, 2 mp doubles) when given.
-__device__ __forceinline__ St carve_global(double *vec, double *L, int32_t *plist, int mp, Blk *bk, double *lds) {
-  St s;
-  s.mp = mp;
-  s.bk = bk;
-  s.L = L;
-  s.u = vec;
-  s.g = vec + mp;
-  s.dg = vec + 2 * mp;
-  s.rows = vec + 3 * mp;
-  s.x0 = lds ? lds : s.rows;
-  s.yv = lds ? lds + mp : s.rows + 8 * mp;
-  s.flag = reinterpret_cast<unsigned char *>(vec + (3 + NROW) * mp);
-  s.plist = plist;
-  return s;
-}
-static_assert(kNnlsVecPerSlot == 3 + NROW + 1, "global NNLS state layout");
-
-// ---- triangular solves ----------------------------------------------------
-
-// Solves L X = R in place for the nr right-hand sides S.row(b)[k], k < n.
-__device__ __forceinline__ void fwd_blk(const St &S, int n, int nr) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int r0 = 0; r0 < n; r0 += TB) {
-    const int e = n - r0 < TB ? n - r0 : TB;
-    // diagonal block: wave w solves right-hand sides w, w + 4, w + 8; lane i holds row r0 + i
-    if (wave < nr && lane < TB) {
-      const int i = lane;
-      const bool act = i < e;
-      const int rb = act ? tri(r0 + i) + r0 : 0;
-      double Lrow[TB];
-      static_for<0, TB>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        Lrow[j] = (act && j < i) ? S.L[rb + j] : 0.0;
-      });
-      const double rd = act ? 1.0 / S.L[rb + i] : 0.0;
-      double x[3];
-      static_for<0, 3>([&](auto Qc) {
-        constexpr int q = decltype(Qc)::value;
-        const int b = wave + NW * q;
-        x[q] = (act && b < nr) ? S.row(b)[r0 + i] : 0.0;
-      });
-      static_for<0, TB>([&](auto K) {
-        constexpr int kk = decltype(K)::value;
-        if (kk < e) {
-          static_for<0, 3>([&](auto Qc) {
-            constexpr int q = decltype(Qc)::value;
-            if (wave + NW * q < nr) {
-              const double xk = rl(x[q] * rd, kk);
-              x[q] = i == kk ? xk : (i > kk ? fma(-Lrow[kk], xk, x[q]) : x[q]);
-            }
-          });
-        }
-      });
-      static_for<0, 3>([&](auto Qc) {
-        constexpr int q = decltype(Qc)::value;
-        const int b = wave + NW * q;
-        if (act && b < nr) S.row(b)[r0 + i] = x[q];
-      });
-    }
-    __syncthreads();
-    if (r0 + TB < n) {
-      // rows below: r_row -= L[row, block] x_block
-      for (int row = r0 + TB + tid; row < n; row += NT) {
-        const int rb = tri(row) + r0;
-        double Lr[TB];
-        static_for<0, TB>([&](auto J) {
-          constexpr int j = decltype(J)::value;
-          Lr[j] = S.L[rb + j];
-        });
-        for (int b = 0; b < nr; ++b) {
-          double *xr = S.row(b);
-          const double *xb = xr + r0;
-          double a0 = 0.0, a1 = 0.0;
-          static_for<0, TB / 2>([&](auto J) {
-            constexpr int j = decltype(J)::value;
-            a0 = fma(Lr[2 * j], xb[2 * j], a0);
-            a1 = fma(Lr[2 * j + 1], xb[2 * j + 1], a1);
-          });
-          xr[row] -= a0 + a1;
-        }
-      }
-      __syncthreads();
-    }
-  }
-}
-
-// Solves L^T x = r in place for the vector x (factor order, length n >= 1).
-__device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int r0 = ((n - 1) / TB) * TB; r0 >= 0; r0 -= TB) {
-    const int e = n - r0 < TB ? n - r0 : TB;
-    if (wave == 0 && lane < TB) {
-      const int i = lane;
-      const bool act = i < e;
-      double Lc[TB];  // column i of the diagonal block, rows below i
-      static_for<0, TB>([&](auto K) {
-        constexpr int kk = decltype(K)::value;
-        Lc[kk] = (act && kk > i && kk < e) ? S.L[tri(r0 + kk) + r0 + i] : 0.0;
-      });
-      const double rd = act ? 1.0 / S.L[tri(r0 + i) + r0 + i] : 0.0;
-      double xv = act ? x[r0 + i] : 0.0;
-      static_for<0, TB>([&](auto K) {
-        constexpr int kk = TB - 1 - decltype(K)::value;
-        if (kk < e) {
-          const double xk = rl(xv * rd, kk);
-          xv = i == kk ? xk : (i < kk ? fma(-Lc[kk], xk, xv) : xv);
-        }
-      });
-      if (act) x[r0 + i] = xv;
-    }
-    __syncthreads();
-    // columns before the block: x_c -= sum_k L[r0 + k][c] x_{r0 + k}; the loads
-    // of a column are all issued before the sums (rows past e read row r0)
-    for (int c = tid; c < r0; c += NT) {
-      double l[TB];
-      static_for<0, TB>([&](auto K) {
-        constexpr int k = decltype(K)::value;
-        l[k] = S.L[tri(k < e ? r0 + k : r0) + c];
-      });
-      double a0 = 0.0, a1 = 0.0;
-      static_for<0, TB / 2>([&](auto K) {
-        constexpr int k = decltype(K)::value;
-        if (2 * k < e) a0 = fma(l[2 * k], x[r0 + 2 * k], a0);
-        if (2 * k + 1 < e) a1 = fma(l[2 * k + 1], x[r0 + 2 * k + 1], a1);
-      });
-      x[c] -= a0 + a1;
-    }
-    __syncthreads();
-  }
-}
-
-// ---- gradient of the zero variables ---------------------------------------
-
-// u_snap = u, g_snap = g (rows 9 and 10)
-__device__ __forceinline__ void snapshot(const St &S, int p) {
-  double *us = S.rows + 9 * S.mp, *gs = S.rows + 10 * S.mp;
-  for (int a = threadIdx.x; a < p; a += NT) {
-    us[a] = S.u[a];
-    gs[a] = S.g[a];
-  }
-  __syncthreads();
-}
-
-// Brings g up to date on every zero variable by the exact increment since the
-// last snapshot, g_a = g_a(snap) - Gs_a (u - u_snap), then takes a new
-// snapshot of u and g.  The change is compacted first (row 1: indices, row 2:
-// change / dg); each wave sums a quarter of it, with many loads of G in
-// flight, and the quarters are added in a fixed order, so the result does not
-// depend on timing.
-__device__ __forceinline__ void sync_z(const St &S, const double *G, int64_t ld, int p) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int mp = S.mp;
-  Blk *bk = S.bk;
-  int *lst = reinterpret_cast<int *>(S.rows + mp);
-  double *dv = S.rows + 2 * mp;
-  const double *us = S.rows + 9 * mp;
-  double *gs = S.rows + 10 * mp;
-  int ns = 0;
-  for (int c0 = 0; c0 < p; c0 += NT) {
-    const int c = c0 + tid;
-    double dl = 0.0;
-    if (c < p) dl = S.u[c] - us[c];
-    const bool pred = dl != 0.0;
-    const unsigned long long bal = __ballot(pred);
-    const int before = __popcll(bal & ((1ull << lane) - 1ull));
-    if (lane == 0) bk->wc[wave] = __popcll(bal);
-    __syncthreads();
-    int off = ns;
-    for (int v = 0; v < wave; ++v) off += bk->wc[v];
-    if (pred) {
-      lst[off + before] = c;
-      dv[off + before] = dl / S.dg[c];
-    }
-    for (int v = 0; v < NW; ++v) ns += bk->wc[v];
-    __syncthreads();
-  }
-  if (ns > 0) {
-    const int k0 = (ns * wave) / NW, k1 = (ns * (wave + 1)) / NW;
-    double *zp = S.rows + (3 + wave) * mp;
-    for (int a0 = 0; a0 < p; a0 += NT) {
-      double acc[4] = {0.0, 0.0, 0.0, 0.0};
-      int ac[4];
-      static_for<0, 4>([&](auto M) {
-        constexpr int m = decltype(M)::value;
-        const int a = a0 + lane + 64 * m;
-        ac[m] = a < p ? a : p - 1;
-      });
-      int k = k0;
-      for (; k + 8 <= k1; k += 8) {
-        int c[8];
-        double s[8];
-        static_for<0, 8>([&](auto U) {
-          constexpr int u = decltype(U)::value;
-          c[u] = lst[k + u];
-          s[u] = dv[k + u];
-        });
-        static_for<0, 4>([&](auto M) {
-          constexpr int m = decltype(M)::value;
-          if (a0 + 64 * m < p) {
-            double v[8];
-            static_for<0, 8>([&](auto U) {
-              constexpr int u = decltype(U)::value;
-              v[u] = G[int64_t(c[u]) * ld + ac[m]];
-            });
-            static_for<0, 8>([&](auto U) {
-              constexpr int u = decltype(U)::value;
-              acc[m] = fma(v[u], s[u], acc[m]);
-            });
-          }
-        });
-      }
-      for (; k < k1; ++k) {
-        const int c = lst[k];
-        const double s = dv[k];
-        static_for<0, 4>([&](auto M) {
-          constexpr int m = decltype(M)::value;
-          if (a0 + 64 * m < p) acc[m] = fma(G[int64_t(c) * ld + ac[m]], s, acc[m]);
-        });
-      }
-      static_for<0, 4>([&](auto M) {
-        constexpr int m = decltype(M)::value;
-        const int a = a0 + lane + 64 * m;
-        if (a < p) zp[a] = acc[m];
-      });
-    }
-  }
-  __syncthreads();
-  const double *z = S.rows + 3 * mp;
-  for (int a = tid; a < p; a += NT) {
-    const unsigned char f = S.flag[a];
-    if (!(f & (F_PASSIVE | F_BLOCKED)))
-      S.g[a] = ns > 0 ? gs[a] - ((z[a] + z[mp + a]) + (z[2 * mp + a] + z[3 * mp + a])) / S.dg[a] : gs[a];
-  }
-  __syncthreads();
-  snapshot(S, p);
-}
-
-// ---- factor updates --------------------------------------------------------
-
-// row of packed lower-triangle index s
-__device__ __forceinline__ int row_of(int s) {
-  int i = int((sqrtf(8.0f * float(s) + 1.0f) - 1.0f) * 0.5f);
-  if (tri(i + 1) <= s) ++i;
-  if (tri(i) > s) --i;
-  return i;
-}
-
-// Deletes factor position q: rows below move up one row without column q,
-// then the trailing rows absorb the removed column by a rank-one update
-// (Givens rotations, applied 16 columns at a time).  y = L^-1 g_P follows:
-// its entries below q take the same rotations, with y_q as the extra entry.
-__device__ __forceinline__ void remove_at(const St &S, int q) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  Blk *bk = S.bk;
-  const int np = bk->np, n2 = np - 1;
-  double *xc = S.rows + 7 * S.mp;
-  double *yv = S.yv;
-  double z = yv[q];  // y of the removed position, rotated into the trailing entries below
-  for (int i = q + 1 + tid; i < np; i += NT) xc[i - 1] = S.L[tri(i) + q];
-  // Every element moves to a lower index, so chunks taken in increasing
-  // source order never overwrite a source that is still to be read.
-  for (int base = q; base < n2; base += NT) {
-    const int k = base + tid;
-    const int pv = k < n2 ? S.plist[k + 1] : 0;
-    const double yk = k < n2 ? yv[k + 1] : 0.0;
-    __syncthreads();
-    if (k < n2) {
-      S.plist[k] = pv;
-      yv[k] = yk;
-    }
-  }
-  const int s0 = tri(q + 1), s1 = tri(np);
-  for (int base = s0; base < s1; base += NT * 8) {
-    double v[8];
-    int dst[8];
-    static_for<0, 8>([&](auto U) {
-      constexpr int u = decltype(U)::value;
-      const int s = base + u * NT + tid;
-      dst[u] = -1;
-      v[u] = 0.0;
-      if (s < s1) {
-        const int i = row_of(s);
-        const int c = s - tri(i);
-        if (c != q) {
-          dst[u] = tri(i - 1) + (c < q ? c : c - 1);
-          v[u] = S.L[s];
-        }
-      }
-    });
-    __syncthreads();
-    static_for<0, 8>([&](auto U) {
-      constexpr int u = decltype(U)::value;
-      if (dst[u] >= 0) S.L[dst[u]] = v[u];
-    });
-  }
-  __syncthreads();
-  // rank-one update: L' L'^T = L L^T + x x^T on positions q..n2-1
-  for (int k0 = q; k0 < n2; k0 += TB) {
-    const int e = n2 - k0 < TB ? n2 - k0 : TB;
-    if (wave == 0 && lane < TB) {
-      const int i = lane;
-      const bool act = i < e;
-      const int rb = act ? tri(k0 + i) + k0 : 0;
-      double Lr[TB];
-      static_for<0, TB>([&](auto J) {
-        constexpr int j = decltype(J)::value;
-        Lr[j] = (act && j <= i) ? S.L[rb + j] : 0.0;
-      });
-      double xv = act ? xc[k0 + i] : 0.0;
-      double yl = act ? yv[k0 + i] : 0.0;
-      static_for<0, TB>([&](auto K) {
-        constexpr int kk = decltype(K)::value;
-        if (kk < e) {
-          const double lkk = rl(Lr[kk], kk), xk = rl(xv, kk);
-          const double t2 = fma(lkk, lkk, xk * xk);
-          const double ri = rsqrt(t2);
-          const double c = lkk * ri, s = xk * ri;
-          const double yk = rl(yl, kk);
-          if (i == kk) yl = fma(c, yk, s * z);
-          z = fma(c, z, -s * yk);
-          if (i == kk) {
-            Lr[kk] = t2 * ri;
-          } else if (i > kk) {
-            const double l = Lr[kk];
-            Lr[kk] = fma(c, l, s * xv);
-            xv = fma(c, xv, -s * l);
-          }
-          if (lane == 0) {
-            bk->cs[2 * kk] = c;
-            bk->cs[2 * kk + 1] = s;
-          }
-        }
-      });
-      if (act) {
-        static_for<0, TB>([&](auto J) {
-          constexpr int j = decltype(J)::value;
-          if (j <= i) S.L[rb + j] = Lr[j];
-        });
-        yv[k0 + i] = yl;
-      }
-    }
-    __syncthreads();
-    if (k0 + TB < n2) {
-      for (int row = k0 + TB + tid; row < n2; row += NT) {
-        const int rb = tri(row) + k0;
-        double Lr[TB];
-        static_for<0, TB>([&](auto J) {
-          constexpr int j = decltype(J)::value;
-          Lr[j] = S.L[rb + j];
-        });
-        double xv = xc[row];
-        static_for<0, TB>([&](auto K) {
-          constexpr int kk = decltype(K)::value;
-          const double c = bk->cs[2 * kk], s = bk->cs[2 * kk + 1];
-          const double l = Lr[kk];
-          Lr[kk] = fma(c, l, s * xv);
-          xv = fma(c, xv, -s * l);
-        });
-        static_for<0, TB>([&](auto J) {
-          constexpr int j = decltype(J)::value;
-          S.L[rb + j] = Lr[j];
-        });
-        xc[row] = xv;
-      }
-      __syncthreads();
-    }
-  }
-  if (tid == 0) bk->np = n2;
-  __syncthreads();
-}
-
-// Largest factor position k < np with pred(k) true, -1 if none.
-template <typename P>
-__device__ __forceinline__ int last_position(int np, P pred, Red *red) {
-  int best = -1;
-  for (int k = threadIdx.x; k < np; k += NT)
-    if (pred(k)) best = k;
-  double v;
-  return block_argmax(double(best), best, red, &v);
-}
-
-// Appends the nc <= NB candidates in bk->cand (zero, not blocked) to the free
-// set.  One blocked forward pass over the current factor gives each
-// candidate's row l = L^-1 Gs[P, j] and y = L^-1 g_P; a Cholesky of the block
-// finishes the rows (candidates whose pivot vanishes are blocked).  On return
-// x0 holds y = L^-1 g_P over the extended free set and bk->ctl[2] the number
-// of accepted candidates.  Rows 1..8 are overwritten.
-__device__ __forceinline__ void block_append(const St &S, const double *G, int64_t ld, int nc, int *status) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  Blk *bk = S.bk;
-  const int np0 = bk->np;
-  for (int k = tid; k < np0; k += NT) {
-    const int a = S.plist[k];
-    const double da = S.dg[a];
-    S.x0[k] = S.g[a];
-    for (int b = 0; b < nc; ++b) {
-      const int j = bk->cand[b];
-      S.row(b + 1)[k] = G[int64_t(j) * ld + a] / (S.dg[j] * da);
-    }
-  }
-  if (tid < nc * nc) {
-    const int j1 = bk->cand[tid / nc], j2 = bk->cand[tid % nc];
-    bk->Gc[(tid / nc) * NB + tid % nc] = G[int64_t(j1) * ld + j2] / (S.dg[j1] * S.dg[j2]);
-  }
-  __syncthreads();
-  if (np0 > 0) fwd_blk(S, np0, nc + 1);
-  // dots[b1][b2] = <rhs_b1, rhs_b2> over the old positions, b2 <= b1 (one wave per pair)
-  const int npair = (nc + 1) * (nc + 2) / 2;
-  for (int pr = wave; pr < npair; pr += NW) {
-    int b1 = 0;
-    while ((b1 + 1) * (b1 + 2) / 2 <= pr) ++b1;
-    const int b2 = pr - b1 * (b1 + 1) / 2;
-    const double *r1 = S.row(b1), *r2 = S.row(b2);
-    double v = 0.0;
-    for (int k = lane; k < np0; k += 64) v = fma(r1[k], r2[k], v);
-    v = wave_sum(v);
-    if (lane == 0) bk->dots[b1 * NRHS + b2] = v;
-  }
-  __syncthreads();
-  // Cholesky of the candidate block in wave 0 (wave-uniform values in registers)
-  if (wave == 0) {
-    double E[NB][NB], Dg[NB], yb[NB];
-    int idx[NB];
-    int nacc = 0;
-    static_for<0, NB>([&](auto A) {
-      constexpr int a = decltype(A)::value;
-      Dg[a] = 1.0;
-      yb[a] = 0.0;
-      idx[a] = 0;
-      static_for<0, NB>([&](auto A2) { E[a][decltype(A2)::value] = 0.0; });
-    });
-    static_for<0, NB>([&](auto Bc) {
-      constexpr int b = decltype(Bc)::value;
-      if (b < nc) {
-        const int j = bk->cand[b];
-        double row[NB];
-        double ss = bk->dots[(b + 1) * NRHS + (b + 1)];
-        double yy = S.g[j] - bk->dots[(b + 1) * NRHS];
-        static_for<0, NB>([&](auto A) {
-          constexpr int a = decltype(A)::value;
-          row[a] = 0.0;
-          if (a < nacc) {
-            const int bb = idx[a];
-            double v = bk->Gc[b * NB + bb] - bk->dots[(b + 1) * NRHS + (bb + 1)];
-            static_for<0, a>([&](auto A2) {
-              constexpr int a2 = decltype(A2)::value;
-              v -= row[a2] * E[a][a2];
-            });
-            v /= Dg[a];
-            row[a] = v;
-            ss += v * v;
-            yy -= v * yb[a];
-          }
-        });
-        const double d2 = bk->Gc[b * NB + b] - ss;
-        if (d2 > PIV_TOL) {
-          const double dd = sqrt(d2);
-          static_for<0, NB>([&](auto A) {
-            constexpr int a = decltype(A)::value;
-            if (a == nacc) {
-              static_for<0, a>([&](auto A2) {
-                constexpr int a2 = decltype(A2)::value;
-                E[a][a2] = row[a2];
-              });
-              Dg[a] = dd;
-              yb[a] = yy / dd;
-              idx[a] = b;
-            }
-          });
-          ++nacc;
-        } else if (lane == 0) {
-          S.flag[j] = F_BLOCKED;
-          *status |= int(AMC_HS_NNLS_SINGULAR);
-        }
-      }
-    });
-    if (lane == 0) {
-      static_for<0, NB>([&](auto A) {
-        constexpr int a = decltype(A)::value;
-        bk->Dg[a] = Dg[a];
-        bk->yb[a] = yb[a];
-        bk->accb[a] = idx[a];
-        static_for<0, a>([&](auto A2) {
-          constexpr int a2 = decltype(A2)::value;
-          bk->E[a * NB + a2] = E[a][a2];
-        });
-      });
-      bk->ctl[2] = nacc;
-    }
-  }
-  __syncthreads();
-  const int nacc = bk->ctl[2];
-  for (int a = 0; a < nacc; ++a) {
-    const int b = bk->accb[a];
-    const int pos = np0 + a;
-    const int base = tri(pos);
-    const double *rb = S.row(b + 1);
-    for (int k = tid; k < np0; k += NT) S.L[base + k] = rb[k];
-    if (tid < a) S.L[base + np0 + tid] = bk->E[a * NB + tid];
-    if (tid == 0) {
-      const int j = bk->cand[b];
-      S.L[base + pos] = bk->Dg[a];
-      S.plist[pos] = j;
-      S.flag[j] = F_PASSIVE | F_NEW;
-      S.x0[pos] = bk->yb[a];
-    }
-  }
-  __syncthreads();
-  if (tid == 0) bk->np = np0 + nacc;
-  __syncthreads();
-}
-
-// Least squares on the free set, with feasibility back-tracking, starting
-// from a feasible u whose support is the free set; variables that just
-// entered sit at zero, flagged F_NEW.  have_y: x0 holds y = L^-1 g_P.
-//  - An entering variable whose solution is not positive leaves again before
-//    any step is taken.  If it entered alone it is set aside for the rest of
-//    this fit (Lawson and Hanson's guard against cycling on round-off);
-//    otherwise later blocks of candidates are half as large (ctl[3]; one at
-//    a time once it reaches 1).
-//  - Otherwise the iterate moves toward the solution, as far as feasibility
-//    allows, and the variables that reach zero leave.
-// Only the free-set rows of g change here (by the factor's model); y follows
-// every step and every removal.
-__device__ __forceinline__ void settle(const St &S, int p, bool have_y, bool single, Red *red) {
-  const int tid = threadIdx.x;
-  Blk *bk = S.bk;
-  __syncthreads();
-  if (bk->np == 0) return;
-  if (!have_y) {
-    for (int k = tid; k < bk->np; k += NT) S.x0[k] = S.g[S.plist[k]];
-    __syncthreads();
-    fwd_blk(S, bk->np, 1);
-  }
-  for (int k = tid; k < bk->np; k += NT) S.yv[k] = S.x0[k];
-  for (int guard = 0; guard < 4 * S.mp + 8; ++guard) {
-    __syncthreads();
-    const int np = bk->np;
-    if (np == 0) break;
-    for (int k = tid; k < np; k += NT) S.x0[k] = S.yv[k];
-    __syncthreads();
-    bwd_blk(S, np, S.x0);  // x0 = Gs_PP^-1 g_P: the step to the free-set optimum
-    int ndrop = 0;
-    double best = INFINITY;
-    int kb = -1;
-    for (int k = tid; k < np; k += NT) {
-      const int a = S.plist[k];
-      const double d = S.x0[k];
-      const double ua = S.u[a];
-      if ((S.flag[a] & F_NEW) && ua == 0.0 && !(d > 0.0)) {
-        S.flag[a] |= F_DROP;
-        ++ndrop;
-      } else if (ua + d <= 0.0) {
-        const double rt = d < 0.0 ? ua / (-d) : 0.0;
-        if (kb < 0 || rt < best) {
-          best = rt;
-          kb = k;
-        }
-      }
-    }
-    ndrop = block_count(ndrop, red);
-    if (ndrop > 0) {
-      for (;;) {
-        const int q = last_position(bk->np, [&](int k) { return (S.flag[S.plist[k]] & F_DROP) != 0; }, red);
-        if (q < 0) break;
-        if (tid == 0) {
-          S.flag[S.plist[q]] = single ? F_BLOCKED : 0;
-          if (!single) bk->ctl[3] = bk->ctl[5] > 1 ? bk->ctl[5] / 2 : 1;
-        }
-        __syncthreads();
-        remove_at(S, q);
-      }
-      continue;
-    }
-    double nbest;
-    kb = block_argmax(kb >= 0 ? -best : -INFINITY, kb, red, &nbest);
-    best = -nbest;
-    const bool done = kb < 0;
-    const double alpha = done ? 1.0 : (best < 1.0 ? best : 1.0);
-    const double keep = done ? 0.0 : 1.0 - alpha;
-    for (int k = tid; k < np; k += NT) {
-      const int a = S.plist[k];
-      const double ua = S.u[a];
-      const double d = S.x0[k];
-      const double un = done ? ua + d : ((k == kb) ? 0.0 : fma(alpha, d, ua));
-      S.u[a] = un > 0.0 ? un : 0.0;
-      S.flag[a] &= ~F_NEW;
-      S.g[a] *= keep;
-      S.yv[k] *= keep;
-    }
-    __syncthreads();
-    if (done) break;
-    // every free variable that reached zero leaves (highest position first)
-    for (;;) {
-      const int q = last_position(bk->np, [&](int k) { return !(S.u[S.plist[k]] > 0.0); }, red);
-      if (q < 0) break;
-      if (tid == 0) {
-        const int a = S.plist[q];
-        S.u[a] = 0.0;
-        S.flag[a] &= ~(F_PASSIVE | F_NEW);
-      }
-      __syncthreads();
-      remove_at(S, q);
-    }
-  }
-  __syncthreads();
-}
-
-// Up to maxc zero variables with the largest gradients above tol (ties to the
-// lower index) go to bk->cand; returns their count.
-__device__ __forceinline__ int pick_candidates(const St &S, int p, double tol, int maxc, Red *red) {
-  int nc = 0;
-  for (; nc < maxc; ++nc) {
-    double bv = -INFINITY;
-    int bi = -1;
-    for (int a = threadIdx.x; a < p; a += NT) {
-      if (!(S.flag[a] & (F_PASSIVE | F_BLOCKED | F_CAND))) {
-        const double v = S.g[a];
-        if (v > tol && (bi < 0 || v > bv)) {
-          bv = v;
-          bi = a;
-        }
-      }
-    }
-    double v;
-    bi = block_argmax(bv, bi, red, &v);
-    if (bi < 0) break;
-    if (threadIdx.x == 0) {
-      S.bk->cand[nc] = bi;
-      S.flag[bi] |= F_CAND;
-    }
-    __syncthreads();
-  }
-  return nc;
-}
-
-// One block solves one system on the state S (u, g, dg, flag set up by
-// nnls_setup for a < p; L, plist and bk->np hold the starting free set).
-//   tol, cap : KKT tolerance on the scaled gradient and outer-iteration cap
-//   support  : the positive entries of u enter the free set first (warm
-//              start of the stand-alone solver)
-__device__ __forceinline__ void nnls_core(const St &S, const double *G, int64_t ld, int p, double tol, int cap,
-                                          bool support, Red *red, int *status, int *iters_out) {
-  const int tid = threadIdx.x;
-  Blk *bk = S.bk;
-  int iters = 0;
-  if (support) {
-    // the support of the warm start becomes the free set, NB variables at a time
-    int a0 = 0;
-    for (;;) {
-      __syncthreads();
-      if (tid == 0) {
-        int nc = 0;
-        for (; a0 < p && nc < NB; ++a0)
-          if (S.u[a0] > 0.0 && !(S.flag[a0] & (F_PASSIVE | F_BLOCKED))) bk->cand[nc++] = a0;
-        bk->ctl[1] = nc;
-        bk->ctl[4] = a0;
-      }
-      __syncthreads();
-      const int nc = bk->ctl[1];
-      a0 = bk->ctl[4];
-      if (nc == 0) break;
-      block_append(S, G, ld, nc, status);
-    }
-    for (int k = tid; k < bk->np; k += NT) S.flag[S.plist[k]] &= ~F_NEW;
-    // a dependent variable dropped here still carries weight: take it out of u and g
-    double *tmp = S.rows + 2 * S.mp;
-    for (int a = tid; a < p; a += NT) tmp[a] = ((S.flag[a] & F_BLOCKED) && S.u[a] > 0.0) ? -S.u[a] : 0.0;
-    __syncthreads();
-    for (int a = tid; a < p; a += NT) {
-      double acc = 0.0;
-      for (int c = 0; c < p; ++c)
-        if (tmp[c] != 0.0) acc = fma(G[int64_t(c) * ld + a], tmp[c] / S.dg[c], acc);
-      S.g[a] -= acc / S.dg[a];
-    }
-    __syncthreads();
-    for (int a = tid; a < p; a += NT)
-      if (S.flag[a] & F_BLOCKED) S.u[a] = 0.0;
-    __syncthreads();
-    snapshot(S, p);
-  }
-  // refine the starting free set with the gradient given
-  settle(S, p, false, false, red);
-  for (;;) {
-    sync_z(S, G, ld, p);
-    const int nc = pick_candidates(S, p, tol, bk->ctl[3], red);
-    if (nc == 0) break;
-    if (iters >= cap) {
-      if (tid == 0) *status |= int(AMC_HS_NNLS_CAP);
-      break;
-    }
-    ++iters;
-    if (tid == 0) bk->ctl[5] = nc;
-    block_append(S, G, ld, nc, status);
-    if (bk->ctl[2] > 0) settle(S, p, true, nc == 1, red);
-  }
-  __syncthreads();
-  *iters_out = iters;
-}
-
-// Sets up u, g, dg, flag for a < p from G, b, the warm start (first nwarm
-// entries of w) and the accurate gradient gA (nullable: formed from G and
-// b), and marks the starting free set.  Returns the KKT tolerance, 0 when
-// there is nothing to fit.
-__device__ __forceinline__ double nnls_setup(const St &S, const double *G, int64_t ld, int p, const double *b,
-                                             const double *gA, const double *w, int nwarm, const NnlsParams &prm,
-                                             Red *red) {
-  const int tid = threadIdx.x;
-  double bl = 0.0;
-  for (int a = tid; a < p; a += NT) {
-    const double gaa = G[int64_t(a) * ld + a];
-    double dg = sqrt(gaa);
-    unsigned char f = 0;
-    if (!(dg > 0.0) || !isfinite(dg)) {
-      dg = 1.0;
-      f = F_BLOCKED;
-    }
-    S.dg[a] = dg;
-    const double u0 = (a < nwarm && !f) ? fmax(w[a], 0.0) * dg : 0.0;
-    S.u[a] = u0 > 0.0 ? u0 : 0.0;
-    S.flag[a] = f;
-    bl = fmax(bl, f ? 0.0 : fabs(b[a] / dg));
-  }
-  __syncthreads();
-  for (int k = tid; k < S.bk->np; k += NT) S.flag[S.plist[k]] |= F_PASSIVE;
-  if (gA) {
-    for (int a = tid; a < p; a += NT) S.g[a] = (S.flag[a] & F_BLOCKED) ? 0.0 : gA[a] / S.dg[a];
-  } else {
-    for (int a = tid; a < p; a += NT) {
-      double acc = 0.0;
-      for (int c = 0; c < p; ++c) acc = fma(G[int64_t(c) * ld + a], S.u[c] / S.dg[c], acc);
-      S.g[a] = (S.flag[a] & F_BLOCKED) ? 0.0 : b[a] / S.dg[a] - acc / S.dg[a];
-    }
-  }
-  __syncthreads();
-  snapshot(S, p);
-  double bmax;
-  (void)block_argmax(bl, 0, red, &bmax);
-  if (!(bmax > 0.0) || !isfinite(bmax)) return 0.0;
-  return (prm.tol > 0.0 ? prm.tol : 10.0 * DBL_EPSILON * double(p)) * bmax;
-}
-
-// Projected-gradient warm-up (step 1/L, L a Gershgorin bound of Gs).
-__device__ __forceinline__ void pg_warmup(const St &S, const double *G, int64_t ld, int p, int iters, Red *red) {
-  const int tid = threadIdx.x;
-  double *tmp = S.rows + 2 * S.mp;
-  double rowmax = 0.0;
-  for (int a = tid; a < p; a += NT) {
-    double acc = 0.0;
-    for (int c = 0; c < p; ++c) acc += fabs(G[int64_t(c) * ld + a]) / S.dg[c];
-    if (!(S.flag[a] & F_BLOCKED)) rowmax = fmax(rowmax, acc / S.dg[a]);
-  }
-  double Lmax;
-  (void)block_argmax(rowmax, 0, red, &Lmax);
-  const double step = Lmax > 0.0 ? 1.0 / Lmax : 0.0;
-  for (int it = 0; it < iters; ++it) {
-    __syncthreads();
-    for (int a = tid; a < p; a += NT)
-      tmp[a] = (S.flag[a] & F_BLOCKED) ? 0.0 : fmax(0.0, S.u[a] + step * S.g[a]) - S.u[a];
-    __syncthreads();
-    for (int a = tid; a < p; a += NT) {
-      double acc = 0.0;
-      for (int c = 0; c < p; ++c) acc = fma(G[int64_t(c) * ld + a], tmp[c] / S.dg[c], acc);
-      S.g[a] -= acc / S.dg[a];
-    }
-    __syncthreads();
-    for (int a = tid; a < p; a += NT) S.u[a] += tmp[a];
-  }
-  __syncthreads();
-  snapshot(S, p);
-}
-
-// One refit per head.  polish: no new key; refine the last fit (p = t).
-// kGlobal: the state lives in the workspace (budgets above kNnlsLdsT); else
-// in LDS.  Each variant skips the heads of the other.
-template <bool kGlobal>
-__global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ desc, const double *__restrict__ G,
-                                                   const double *__restrict__ bvec, const double *__restrict__ gA,
-                                                   double *__restrict__ w, int cycle, int kR, int polish,
-                                                   NnlsParams prm, int maxp, double *__restrict__ nn_L,
-                                                   int32_t *__restrict__ nn_P, int32_t *__restrict__ nn_np,
-                                                   double *__restrict__ nn_vec, int32_t *__restrict__ tr_iters,
-                                                   double *__restrict__ tr_weight,
-                                                   int32_t *__restrict__ head_status) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ Blk bk;
-  __shared__ Red red;
-  __shared__ int sh_status;
-  const int h = blockIdx.x;
-  const HeadDesc D = desc[h];
-  if ((D.t > kNnlsLdsT) != kGlobal) return;
-  int64_t S0;
-  int Kc;
-  if (polish) {
-    S0 = D.t;
-    Kc = 0;
-  } else {
-    S0 = int64_t(cycle) * kR;
-    if (S0 >= D.t) return;
-    Kc = int(D.t - S0 < kR ? D.t - S0 : kR);
-  }
-  const int tid = threadIdx.x;
-  const int p = int(S0) + Kc;
-  const int np_in = S0 == 0 ? 0 : nn_np[h];
-  double *Lg = nn_L + D.tri_off;
-  int32_t *Pg = nn_P + D.t_off;
-  // global variant: maxp > 0 means the launch gave LDS for two vectors of maxp
-  double *lds_rows = (kGlobal && maxp > 0 && D.t <= maxp) ? reinterpret_cast<double *>(smem) : nullptr;
-  const St S = kGlobal ? carve_global(nn_vec + D.t_off * kNnlsVecPerSlot, Lg, Pg, int(D.t), &bk, lds_rows)
-                       : carve_lds(smem, maxp, &bk);
-  if (tid == 0) {
-    sh_status = 0;
-    bk.np = np_in;
-    bk.ctl[3] = NB;
-  }
-  if (!kGlobal) {
-    // bring the persisted factor into LDS, eight loads in flight per thread
-    const int ne = tri(np_in);
-    for (int e0 = 0; e0 < ne; e0 += 8 * NT) {
-      double v[8];
-      static_for<0, 8>([&](auto U) {
-        constexpr int u = decltype(U)::value;
-        const int e = e0 + u * NT + tid;
-        v[u] = e < ne ? Lg[e] : 0.0;
-      });
-      static_for<0, 8>([&](auto U) {
-        constexpr int u = decltype(U)::value;
-        const int e = e0 + u * NT + tid;
-        if (e < ne) S.L[e] = v[u];
-      });
-    }
-    for (int k = tid; k < np_in; k += NT) S.plist[k] = Pg[k];
-  }
-  __syncthreads();
-  const double tol = nnls_setup(S, G + D.tt_off, D.t, p, bvec + D.t_off, gA + D.t_off, w + D.t_off, int(S0), prm,
-                                &red);
-  int iters = 0;
-  if (tol > 0.0) {
-    const int cap = prm.max_iters > 0 ? prm.max_iters : 3 * p + 30;
-    nnls_core(S, G + D.tt_off, D.t, p, tol, cap, false, &red, &sh_status, &iters);
-  }
-  __syncthreads();
-  for (int a = tid; a < p; a += NT) w[D.t_off + a] = S.u[a] / S.dg[a];
-  const int np = bk.np;
-  if (!kGlobal) {
-    for (int e = tid; e < tri(np); e += NT) Lg[e] = S.L[e];
-    for (int k = tid; k < np; k += NT) Pg[k] = S.plist[k];
-  }
-  if (tid == 0) {
-    nn_np[h] = np;
-    if (tr_iters && !polish) tr_iters[D.cyc_off + cycle] = iters;
-    if (sh_status && head_status) atomicOr(head_status + h, sh_status);
-  }
-  if (tr_weight)
-    for (int a = tid; a < p; a += NT) tr_weight[D.t_off + a] = S.u[a] / S.dg[a];
-}
-
-struct NnlsChunk {
-  int count;
-  int64_t cu_t[65];
-  int64_t cu_t2[65];
-};
-
-__global__ __launch_bounds__(NT) void k_nnls_batched(NnlsChunk ch, int base, const double *__restrict__ G,
-                                                     const double *__restrict__ g, double *__restrict__ w, int warm,
-                                                     NnlsParams prm, int maxp, int32_t *__restrict__ iters,
-                                                     int32_t *__restrict__ status) {
-  extern __shared__ __attribute__((aligned(16))) char smem[];
-  __shared__ Blk bk;
-  __shared__ Red red;
-  __shared__ int sh_status;
-  const int i = blockIdx.x;
-  if (i >= ch.count) return;
-  const int64_t t0 = ch.cu_t[i];
-  const int p = int(ch.cu_t[i + 1] - t0);
-  const double *Gi = G + ch.cu_t2[i];
-  const St S = carve_lds(smem, maxp, &bk);
-  if (threadIdx.x == 0) {
-    sh_status = 0;
-    bk.np = 0;
-    bk.ctl[3] = NB;
-  }
-  __syncthreads();
-  const double tol = nnls_setup(S, Gi, p, p, g + t0, nullptr, w + t0, warm ? p : 0, prm, &red);
-  int it = 0;
-  if (tol > 0.0) {
-    if (prm.pg_iters > 0) pg_warmup(S, Gi, p, p, prm.pg_iters, &red);
-    const int cap = prm.max_iters > 0 ? prm.max_iters : 3 * p + 30;
-    nnls_core(S, Gi, p, p, tol, cap, true, &red, &sh_status, &it);
-  }
-  __syncthreads();
-  for (int a = threadIdx.x; a < p; a += NT) w[t0 + a] = S.u[a] / S.dg[a];
-  if (threadIdx.x == 0) {
-    if (iters) iters[base + i] = it;
-    if (status) status[base + i] = sh_status;
-  }
-}
-
+#include "k_nnls_body.h"
 }  // namespace
 
 hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int kR, int polish, const NnlsParams &np,
@@ -1122,16 +69,7 @@ hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int kR, int 
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
-  if (dm.max_t > kNnlsLdsT) {
-    const size_t bytes = nnls_global_smem_bytes(dm.max_t);
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_nnls_cycle<true>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(k_nnls_cycle<true>, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.bvec, b.gA, b.w,
-                       cycle, kR, polish, np, bytes ? int(dm.max_t) : 0, b.nn_L, b.nn_P, b.nn_np, b.nn_vec, b.tr_iters, b.tr_weight,
-                       b.head_status);
-    return hipGetLastError();
-  }
+  if (dm.max_t > kNnlsLdsT) return launch_nnls_global(dm, b, cycle, kR, polish, np, s);
   return hipSuccess;
 }
 
