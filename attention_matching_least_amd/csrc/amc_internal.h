@@ -55,7 +55,7 @@ struct Buffers {
   double *shift;       // [H]
   float *phi;          // [sum n*ldT] float32 Phi (the mass-feature entry point's output)
   uint16_t *phi16;     // per head at 2*phi_off: high plane [n][ldT], then low plane [n][ldT];
-                       // within each 64-key tile, key 16 kb + g + 4 e sits at 16 g + 4 kb + e
+                       // within each 64-key tile, key 16 kb + g + 4 e sits at 32 (kb/2) + 8 g + 4 (kb%2) + e
   uint16_t *vt;        // bf16 inputs: per head at vt_off, [T/64 tiles][d][64] values, key-permuted
   double *m, *r, *mhat;  // [sum n]
   float *Y;            // [sum n][d]

@@ -45,16 +45,30 @@ template <int D>
 __global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
                                                    const double *__restrict__ w, const double *__restrict__ mhat,
                                                    const float *__restrict__ Y, double *__restrict__ N,
-                                                   double *__restrict__ rhs) {
+                                                   double *__restrict__ rhs, int H, int tx, int ty, int xcd_map) {
   constexpr int CH = 64;       // queries per stage
   constexpr int STR = CH + 1;  // padded row, in doubles
   __shared__ double xs[64 * STR];
   __shared__ double zs[64 * STR];
   __shared__ double minv[2][CH];
-  const int h = blockIdx.z;
+  // tx * ty tiles per head; with xcd_map (H a multiple of 8) the tiles of a
+  // head go to one XCD, so its panel is fetched into one L2
+  int h, j;
+  {
+    const int b = blockIdx.x, per = tx * ty;
+    if (xcd_map) {
+      const int slot = b >> 3;
+      h = (b & 7) + 8 * (slot / per);
+      j = slot % per;
+    } else {
+      h = b / per;
+      j = b % per;
+    }
+  }
+  if (h >= H) return;
   const HeadDesc Dh = desc[h];
   const int64_t t = Dh.t, n = Dh.n;
-  const int64_t a0 = int64_t(blockIdx.x) * 64, b0 = int64_t(blockIdx.y) * 64;
+  const int64_t a0 = int64_t(j % tx) * 64, b0 = int64_t(j / tx) * 64;
   if (a0 >= t || b0 >= t + D) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
@@ -642,11 +656,15 @@ __global__ __launch_bounds__(NT) void k_ols_trsm_g(const HeadDesc *__restrict__ 
 }  // namespace
 
 hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s) {
-  dim3 grid(unsigned((dm.max_t + 63) / 64), unsigned((dm.max_t + dm.d + 63) / 64), unsigned(dm.H));
+  const int tx = int((dm.max_t + 63) / 64), ty = int((dm.max_t + dm.d + 63) / 64);
+  const int xcd_map = dm.H % 8 == 0 ? 1 : 0;
+  dim3 grid(unsigned(tx * ty * dm.H));
   if (dm.d == 128)
-    hipLaunchKernelGGL((k_ols_normal<128>), grid, dim3(NT), 0, s, b.desc, b.panel, b.w, b.mhat, b.Y, b.G, b.rhs);
+    hipLaunchKernelGGL((k_ols_normal<128>), grid, dim3(NT), 0, s, b.desc, b.panel, b.w, b.mhat, b.Y, b.G, b.rhs,
+                       dm.H, tx, ty, xcd_map);
   else
-    hipLaunchKernelGGL((k_ols_normal<64>), grid, dim3(NT), 0, s, b.desc, b.panel, b.w, b.mhat, b.Y, b.G, b.rhs);
+    hipLaunchKernelGGL((k_ols_normal<64>), grid, dim3(NT), 0, s, b.desc, b.panel, b.w, b.mhat, b.Y, b.G, b.rhs,
+                       dm.H, tx, ty, xcd_map);
   return hipGetLastError();
 }
 

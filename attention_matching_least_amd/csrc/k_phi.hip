@@ -156,9 +156,10 @@ struct In<float> {
 // are keys, so lane group g, element e of key block kb holds this key:
 __device__ __forceinline__ int phi_key(int kb, int g, int e) { return kb * 16 + g + 4 * e; }
 // The stored planes keep each 64-key tile in a lane-friendly order: key
-// 16 kb + g + 4 e at position 16 g + 4 kb + e, so that the 16 values a lane
-// holds for one query are 16 consecutive positions.
-__device__ __forceinline__ int store_pos(int kb, int g, int e) { return 16 * g + 4 * kb + e; }
+// 16 kb + g + 4 e at position 32 (kb / 2) + 8 g + 4 (kb % 2) + e.  The 16
+// values a lane holds for one query are then two runs of 8 positions, and the
+// four lanes of a query write 64 contiguous bytes of a plane per store.
+__device__ __forceinline__ int store_pos(int kb, int g, int e) { return 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + e; }
 // The Phi V product consumes those values as its A operand at k-step (kb, e)
 // (A[query][k = g]); its B operand B[k = g][dim] is then V[phi_key(kb, g, e)][dim],
 // a row of the V tile, read directly.
@@ -527,7 +528,8 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
   // the waves in turn.  K rows are KROW slots (chunk m of key k at slot
   // k KROW + m), V rows (dims) 9 slots; a padding slot takes a duplicate of
   // the row's first chunk.  The biases take one 4-byte copy (wave 0), slot i
-  // holding key key_at(i) so that a lane's 16 biases are consecutive.
+  // holding the key stored at position i (store_pos), so that a lane's 16
+  // biases are two runs of 8.
   // Sources are a per-head base plus a 32-bit byte offset.
   const char *kbase = reinterpret_cast<const char *>(K + Dh.k_off * D);
   const char *vbase = reinterpret_cast<const char *>(vt + Dh.vt_off);
@@ -552,7 +554,7 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
                                        (void __attribute__((address_space(3))) *)(lv + inst * 256), 16, 0, 0);
     }
     if (bbase && wave == 0) {
-      const int key = k0 + 16 * ((lane >> 2) & 3) + (lane >> 4) + 4 * (lane & 3);
+      const int key = k0 + 16 * (2 * (lane >> 5) + ((lane >> 2) & 1)) + ((lane >> 3) & 3) + 4 * (lane & 3);
       const uint32_t off = uint32_t(key < T ? key : int(T) - 1) * 4u;
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(bbase + off),
                                        (void __attribute__((address_space(3))) *)lb, 4, 0, 0);
@@ -595,7 +597,7 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
     f32x4 bz[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
-      bz[kb] = bbase ? *reinterpret_cast<const f32x4 *>(lb + 16 * g + 4 * kb) : f32x4{0.f, 0.f, 0.f, 0.f};
+      bz[kb] = bbase ? *reinterpret_cast<const f32x4 *>(lb + store_pos(kb, g, 0)) : f32x4{0.f, 0.f, 0.f, 0.f};
     // Phi for keys 16 kb + g + 4 e and query q; x = float32 Phi
     float x[4][4];
 #pragma unroll
@@ -612,7 +614,7 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
     __builtin_amdgcn_s_waitcnt(0);
     if constexpr (STORE == 2) {
       if (qvalid) {
-        // positions 16 g + 4 kb + e: 16 consecutive, two 16-byte segments per plane
+        // positions 8 g + (0..7) and 32 + 8 g + (0..7): one 16-byte segment each, per plane
         uint16_t *hp = phi16 + 2 * Dh.phi_off;
         uint16_t *lp = hp + Dh.n * Dh.ldT;
         uint32_t hw[8], lw[8];
@@ -623,11 +625,11 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
           hw[i] = (u0 >> 16) | (u1 & 0xffff0000u);
           lw[i] = (u0 & 0xffffu) | (u1 << 16);
         }
-        const int64_t at = q * Dh.ldT + k0 + 16 * g;
+        const int64_t at = q * Dh.ldT + k0 + 8 * g;
         __builtin_nontemporal_store(u32x4{hw[0], hw[1], hw[2], hw[3]}, reinterpret_cast<u32x4 *>(hp + at));
-        __builtin_nontemporal_store(u32x4{hw[4], hw[5], hw[6], hw[7]}, reinterpret_cast<u32x4 *>(hp + at + 8));
+        __builtin_nontemporal_store(u32x4{hw[4], hw[5], hw[6], hw[7]}, reinterpret_cast<u32x4 *>(hp + at + 32));
         __builtin_nontemporal_store(u32x4{lw[0], lw[1], lw[2], lw[3]}, reinterpret_cast<u32x4 *>(lp + at));
-        __builtin_nontemporal_store(u32x4{lw[4], lw[5], lw[6], lw[7]}, reinterpret_cast<u32x4 *>(lp + at + 8));
+        __builtin_nontemporal_store(u32x4{lw[4], lw[5], lw[6], lw[7]}, reinterpret_cast<u32x4 *>(lp + at + 32));
       }
     }
     // Phi V: reduction index k = 8 g + 4 j + e of chunk c is key phi_key(2 c + j, g, e)

@@ -66,10 +66,12 @@ __device__ void block_sort256(double *v, int *ix) {
 }
 
 // Stored Phi planes keep each 64-key tile in the order the mass-feature
-// kernel writes it: position 16 g + 4 kb + e holds key 16 kb + g + 4 e.
+// kernel writes it: position 32 (kb / 2) + 8 g + 4 (kb % 2) + e holds key
+// 16 kb + g + 4 e.
 __device__ __forceinline__ int64_t key_at(int64_t pos) {
   const int p = int(pos & 63);
-  return (pos & ~int64_t(63)) + 16 * ((p >> 2) & 3) + (p >> 4) + 4 * (p & 3);
+  const int kb = 2 * (p >> 5) + ((p >> 2) & 1), g = (p >> 3) & 3, e = p & 3;
+  return (pos & ~int64_t(63)) + 16 * kb + g + 4 * e;
 }
 
 __device__ __forceinline__ int cycle_keys(const HeadDesc &D, int cycle, int kR, int64_t *S0) {
