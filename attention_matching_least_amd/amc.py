@@ -63,6 +63,7 @@ class Options(ctypes.Structure):
         ("nnls_tol", ctypes.c_double),
         ("phi_budget_bytes", ctypes.c_uint64),
         ("cv_dtype", ctypes.c_int32),
+        ("head_groups", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
         ("timer", ctypes.c_void_p),
     ]
@@ -180,7 +181,8 @@ def make_problem(num_heads: int, head_dim: int, cu_q: Sequence[int], cu_k: Seque
 
 def make_options(select: str = "omp", topk: int = 1, refit_every: int = 1, nnls_polish: int = 1,
                  nnls_max_iters: int = 0, nnls_tol: float = 0.0, phi_budget_bytes: Optional[int] = None,
-                 cv_dtype: torch.dtype = torch.float32, trace: bool = False, timer: "Timer" = None) -> Options:
+                 cv_dtype: torch.dtype = torch.float32, trace: bool = False, timer: "Timer" = None,
+                 head_groups: int = 0) -> Options:
     o = Options()
     lib().amc_default_options(ctypes.byref(o))
     o.select = {"omp": AMC_SEL_OMP, "batched": AMC_SEL_OMP_BATCHED}[select]
@@ -193,6 +195,7 @@ def make_options(select: str = "omp", topk: int = 1, refit_every: int = 1, nnls_
         o.phi_budget_bytes = int(phi_budget_bytes)
     o.cv_dtype = AMC_BF16 if cv_dtype == torch.bfloat16 else AMC_F32
     o.flags = AMC_FLAG_TRACE if trace else 0
+    o.head_groups = int(head_groups)
     o.timer = timer.handle if timer is not None else None
     return o
 
@@ -321,7 +324,7 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
             nnls_polish: int = 1, nnls_max_iters: int = 0, nnls_tol: float = 0.0,
             phi_budget_bytes: Optional[int] = None, cv_dtype: torch.dtype = torch.float32, trace: bool = False,
             timer: Optional[Timer] = None, scale: float = 0.0, stream=None,
-            workspace: Optional[torch.Tensor] = None) -> CompactResult:
+            workspace: Optional[torch.Tensor] = None, head_groups: int = 0) -> CompactResult:
     """amc_compact on torch tensors.  Q: (H, n, d) or packed (sum n, d) with
     cu_q; K, V: (H, T, d) or packed with cu_k; budgets: int or per-head list."""
     if not (Q.is_cuda and K.is_cuda and V.is_cuda):
@@ -341,7 +344,7 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
         raise ValueError("one budget per head")
     prob, keep = make_problem(H, d, cq, ck, bud, _dtype_code(Qp), scale)
     opts = make_options(select, topk, refit_every, nnls_polish, nnls_max_iters, nnls_tol, phi_budget_bytes,
-                        cv_dtype, trace, timer)
+                        cv_dtype, trace, timer, head_groups)
     ws_bytes = workspace_size(prob, opts)
     cb = output_offsets(prob)
     dev = Qp.device

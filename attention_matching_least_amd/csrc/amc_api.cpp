@@ -94,6 +94,7 @@ static amc_status check_options(const amc_options *o) {
   if (o->select == AMC_SEL_OMP && (o->topk != 1 || o->refit_every != 1)) return AMC_ERR_INVALID_ARG;
   if (int64_t(o->topk) * o->refit_every > kMaxCycle) return AMC_ERR_UNSUPPORTED;
   if (o->nnls_max_iters < 0 || o->nnls_polish < 0 || o->nnls_polish > 8) return AMC_ERR_INVALID_ARG;
+  if (o->head_groups < 0 || o->head_groups > 16) return AMC_ERR_INVALID_ARG;
   if (!(o->nnls_tol >= 0.0) || !std::isfinite(o->nnls_tol)) return AMC_ERR_INVALID_ARG;
   if (o->cv_dtype != AMC_F32 && o->cv_dtype != AMC_BF16) return AMC_ERR_INVALID_ARG;
   if (o->flags & ~uint32_t(AMC_FLAG_TRACE)) return AMC_ERR_INVALID_ARG;
@@ -258,6 +259,32 @@ static bool sync_check_enabled() {
   return e && e[0] == '1';
 }
 
+// Head groups of one call (each on its own stream): the option, else four for
+// stacks of at least 256 heads that split into multiples of 8 (the XCD
+// mapping of the tiled kernels), else one; never more than H.
+static int head_groups(int requested, int H) {
+  const int g = requested > 0 ? requested : ((H >= 256 && H % 32 == 0) ? 4 : 1);
+  return g < H ? g : H;
+}
+
+// The buffers of heads [h0, ...): the descriptor table and the arrays indexed
+// by head number start at h0; everything else is reached through the
+// descriptors' offsets.
+static Buffers head_range(const Buffers &b, int h0, int64_t max_qblk) {
+  Buffers r = b;
+  r.desc = b.desc + h0;
+  r.shift = b.shift + h0;
+  if (b.head_status) r.head_status = b.head_status + h0;
+  if (b.tr_shift) r.tr_shift = b.tr_shift + h0;
+  r.nn_np = b.nn_np + h0;
+  r.ols_fcount = b.ols_fcount + h0;
+  if (b.band_list) r.band_list = b.band_list + int64_t(h0) * kBandCap;
+  if (b.band_cnt) r.band_cnt = b.band_cnt + h0;
+  if (b.exact) r.exact = b.exact + h0;
+  if (b.part) r.part = b.part + int64_t(h0) * kBandCap * max_qblk;
+  return r;
+}
+
 // Largest candidate band the float64 rescoring takes; AMC_BAND_CAP lowers it
 // (0 sends every head through the float32 sweep), for testing that path.
 static int band_cap_setting() {
@@ -287,6 +314,7 @@ void amc_default_options(amc_options *o) {
   o->nnls_tol = 0.0;
   o->phi_budget_bytes = 64ull << 30;
   o->cv_dtype = AMC_F32;
+  o->head_groups = 0;
   o->flags = 0;
   o->timer = nullptr;
 }
@@ -437,39 +465,93 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
                               : hipErrorLaunchFailure));
   AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.sel_slot, pl.sum_T, 0, stream));
   if (head_status) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(head_status, dm.H, 0, stream));
-  AMC_LAUNCH(AMC_K_SHIFT, launch_shift(dm, b, stream));
-  if (b.vt) AMC_LAUNCH(AMC_K_INIT, launch_vt(dm, b, stream));
-  AMC_LAUNCH(AMC_K_PHI, launch_phi(dm, b, pl.store_phi ? 2 : 0, stream));
-  for (int c = 0; c < pl.max_cycles; ++c) {
-    if (pl.store_phi) {
-      // bounded sweep and float64 rescoring of the band; the heads whose band
-      // overflowed take the float32 sweep, merge and panel
-      AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_band(dm, b, c, pl.kR, stream));
-      AMC_LAUNCH(AMC_K_MERGE, launch_band_merge(dm, b, c, pl.kR, stream));
-      AMC_LAUNCH(AMC_K_SWEEP_EXACT, launch_sweep(dm, b, c, pl.kR, 1, stream));
-      AMC_LAUNCH(AMC_K_MERGE, launch_merge(dm, b, c, pl.kR, 1, stream));
-      AMC_LAUNCH(AMC_K_RESCORE, launch_rescore(dm, b, c, pl.kR, stream));
-      AMC_LAUNCH(AMC_K_MERGE, launch_choose(dm, b, c, pl.kR, stream));
-      AMC_LAUNCH(AMC_K_PANEL, launch_panel(dm, b, c, pl.kR, 1, stream));
-    } else {
-      AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_rc(dm, b, c, pl.kR, stream));
-      AMC_LAUNCH(AMC_K_MERGE, launch_merge(dm, b, c, pl.kR, 0, stream));
-      AMC_LAUNCH(AMC_K_PANEL, launch_panel(dm, b, c, pl.kR, 0, stream));
+
+  // The heads run in groups, each on a stream of its own (the caller's for the
+  // first), joined back to the caller's stream by events: the groups' mass
+  // features run one after another, each overlapping the selection loops of
+  // the groups before it (MFMA-bound against HBM- and latency-bound work).
+  const int ngroups = head_groups(o->head_groups, dm.H);
+  std::vector<hipStream_t> gs(size_t(ngroups), stream);
+  std::vector<hipEvent_t> ev;
+  auto cleanup = [&]() {
+    for (hipEvent_t e : ev) (void)hipEventDestroy(e);
+    for (int g = 1; g < ngroups; ++g)
+      if (gs[size_t(g)] != stream) (void)hipStreamDestroy(gs[size_t(g)]);
+  };
+  auto new_event = [&](hipEvent_t *e) {
+    if (hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess) return false;
+    ev.push_back(*e);
+    return true;
+  };
+  hipEvent_t ev_start = nullptr;
+  std::vector<hipEvent_t> ev_phi(size_t(ngroups), nullptr), ev_done(size_t(ngroups), nullptr);
+  if (ngroups > 1) {
+    bool ok = new_event(&ev_start) && hipEventRecord(ev_start, stream) == hipSuccess;
+    for (int g = 1; ok && g < ngroups; ++g) {
+      ok = hipStreamCreateWithFlags(&gs[size_t(g)], hipStreamNonBlocking) == hipSuccess;
+      if (!ok) gs[size_t(g)] = stream;
+      ok = ok && hipStreamWaitEvent(gs[size_t(g)], ev_start, 0) == hipSuccess;
     }
-    AMC_LAUNCH(AMC_K_GRAM, launch_gram(dm, b, c, pl.kR, 0, stream));
-    AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dm, b, c, pl.kR, 0, np, stream));
-    AMC_LAUNCH(AMC_K_RESID, launch_resid(dm, b, c, pl.kR, 0, stream));
+    for (int g = 0; ok && g < ngroups; ++g) ok = new_event(&ev_phi[size_t(g)]) && new_event(&ev_done[size_t(g)]);
+    if (!ok) {
+      cleanup();
+      return AMC_ERR_HIP;
+    }
   }
-  for (int r = 0; r < o->nnls_polish; ++r) {
-    AMC_LAUNCH(AMC_K_GRAM, launch_gram(dm, b, 0, pl.kR, 1, stream));
-    AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dm, b, 0, pl.kR, 1, np, stream));
-    AMC_LAUNCH(AMC_K_RESID, launch_resid(dm, b, 0, pl.kR, 1, stream));
+  amc_status result = AMC_OK;
+  for (int g = 0; g < ngroups && result == AMC_OK; ++g) {
+    const int h0 = int(int64_t(dm.H) * g / ngroups), h1 = int(int64_t(dm.H) * (g + 1) / ngroups);
+    const Buffers bg = head_range(b, h0, dm.max_qblk);
+    Dims dg = dm;
+    dg.H = h1 - h0;
+    int64_t cycles = 0;
+    for (int h = h0; h < h1; ++h) cycles = std::max(cycles, ceil_div(pl.desc[size_t(h)].t, pl.kR));
+    result = [&]() -> amc_status {
+      hipStream_t stream = gs[size_t(g)];
+      if (g > 0 && hipStreamWaitEvent(stream, ev_phi[size_t(g - 1)], 0) != hipSuccess) return AMC_ERR_HIP;
+      AMC_LAUNCH(AMC_K_SHIFT, launch_shift(dg, bg, stream));
+      if (bg.vt) AMC_LAUNCH(AMC_K_INIT, launch_vt(dg, bg, stream));
+      AMC_LAUNCH(AMC_K_PHI, launch_phi(dg, bg, pl.store_phi ? 2 : 0, stream));
+      if (ngroups > 1 && hipEventRecord(ev_phi[size_t(g)], stream) != hipSuccess) return AMC_ERR_HIP;
+      for (int c = 0; c < cycles; ++c) {
+        if (pl.store_phi) {
+          // bounded sweep and float64 rescoring of the band; the heads whose
+          // band overflowed take the float32 sweep, merge and panel
+          AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_band(dg, bg, c, pl.kR, stream));
+          AMC_LAUNCH(AMC_K_MERGE, launch_band_merge(dg, bg, c, pl.kR, stream));
+          AMC_LAUNCH(AMC_K_SWEEP_EXACT, launch_sweep(dg, bg, c, pl.kR, 1, stream));
+          AMC_LAUNCH(AMC_K_MERGE, launch_merge(dg, bg, c, pl.kR, 1, stream));
+          AMC_LAUNCH(AMC_K_RESCORE, launch_rescore(dg, bg, c, pl.kR, stream));
+          AMC_LAUNCH(AMC_K_MERGE, launch_choose(dg, bg, c, pl.kR, stream));
+          AMC_LAUNCH(AMC_K_PANEL, launch_panel(dg, bg, c, pl.kR, 1, stream));
+        } else {
+          AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_rc(dg, bg, c, pl.kR, stream));
+          AMC_LAUNCH(AMC_K_MERGE, launch_merge(dg, bg, c, pl.kR, 0, stream));
+          AMC_LAUNCH(AMC_K_PANEL, launch_panel(dg, bg, c, pl.kR, 0, stream));
+        }
+        AMC_LAUNCH(AMC_K_GRAM, launch_gram(dg, bg, c, pl.kR, 0, stream));
+        AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dg, bg, c, pl.kR, 0, np, stream));
+        AMC_LAUNCH(AMC_K_RESID, launch_resid(dg, bg, c, pl.kR, 0, stream));
+      }
+      for (int r = 0; r < o->nnls_polish; ++r) {
+        AMC_LAUNCH(AMC_K_GRAM, launch_gram(dg, bg, 0, pl.kR, 1, stream));
+        AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dg, bg, 0, pl.kR, 1, np, stream));
+        AMC_LAUNCH(AMC_K_RESID, launch_resid(dg, bg, 0, pl.kR, 1, stream));
+      }
+      AMC_LAUNCH(AMC_K_OLS_NORMAL, launch_ols_normal(dg, bg, stream));
+      AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_factor(dg, bg, stream));
+      AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_trsm(dg, bg, stream));
+      AMC_LAUNCH(AMC_K_PACK, launch_pack(dg, bg, Ck, beta, Cv, o->cv_dtype == AMC_BF16, sel_idx, stream));
+      if (ngroups > 1 && g > 0 && hipEventRecord(ev_done[size_t(g)], stream) != hipSuccess) return AMC_ERR_HIP;
+      return AMC_OK;
+    }();
   }
-  AMC_LAUNCH(AMC_K_OLS_NORMAL, launch_ols_normal(dm, b, stream));
-  AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_factor(dm, b, stream));
-  AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_trsm(dm, b, stream));
-  AMC_LAUNCH(AMC_K_PACK, launch_pack(dm, b, Ck, beta, Cv, o->cv_dtype == AMC_BF16, sel_idx, stream));
-  return AMC_OK;
+  // the caller's stream waits for every group (also after a failed launch, so
+  // that nothing is left running apart from it)
+  for (int g = 1; g < ngroups; ++g)
+    if (hipStreamWaitEvent(stream, ev_done[size_t(g)], 0) != hipSuccess && result == AMC_OK) result = AMC_ERR_HIP;
+  cleanup();
+  return result;
 }
 
 amc_status amc_mass_features(const amc_problem *p, const void *Q, const void *K, const void *V,

@@ -474,11 +474,13 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
   constexpr int VSLOT = D * 9;          // slots per V tile: D rows of 8 chunks and a pad
   constexpr int KWORDS = KSLOT * 4;     // uint32 per K tile
   constexpr int VWORDS = VSLOT * 4;     // uint32 per V tile
-  __shared__ __attribute__((aligned(16))) uint32_t lk0[KWORDS];
-  __shared__ __attribute__((aligned(16))) uint32_t lk1[KWORDS];
-  __shared__ __attribute__((aligned(16))) uint32_t lv0[VWORDS];
-  __shared__ __attribute__((aligned(16))) uint32_t lv1[VWORDS];
+  // both K buffers in one array and both V buffers in another, so that every
+  // operand read is one base register plus an immediate offset
+  __shared__ __attribute__((aligned(16))) uint32_t lk_all[2 * KWORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t lv_all[2 * VWORDS];
   __shared__ __attribute__((aligned(16))) float sb[2][64];
+  uint32_t *const lk0 = lk_all, *const lk1 = lk_all + KWORDS;
+  uint32_t *const lv0 = lv_all, *const lv1 = lv_all + VWORDS;
   __shared__ double s_shift;
 
   int h, qb;
@@ -573,6 +575,10 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
                      uint32_t *nk, uint32_t *nv, float *nb, double s) {
     const int64_t k0 = int64_t(tile) * 64;
     if (next) issue(tile + 1, nk, nv, nb);
+    // this lane's first K slot and V slot; every operand below is a constant
+    // number of slots past them
+    const u32x4 *kl4 = reinterpret_cast<const u32x4 *>(lk) + (c16 * KROW + g);
+    const u32x4 *vl4 = reinterpret_cast<const u32x4 *>(lv) + (c16 * 9 + g);
     f64x4 acc[4];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) acc[kb] = f64x4{0.0, 0.0, 0.0, 0.0};
@@ -581,7 +587,7 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
       u32x4 kw[4];
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb)
-        kw[kb] = *reinterpret_cast<const u32x4 *>(lk + ((kb * 16 + c16) * KROW + 4 * a + g) * 4);
+        kw[kb] = kl4[kb * 16 * KROW + 4 * a];
 #pragma unroll
       for (int b = 0; b < 8; ++b) {
         const uint32_t qw2 = qraw[a][b >> 1];
@@ -657,7 +663,7 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
         }
 #pragma unroll
       for (int db = 0; db < NU; ++db) {
-        const u32x4 vv = *reinterpret_cast<const u32x4 *>(lv + ((db * 16 + c16) * 9 + 4 * c + g) * 4);
+        const u32x4 vv = vl4[db * 16 * 9 + 4 * c];
         const bf16x8 bv = __builtin_bit_cast(bf16x8, vv);
 #pragma unroll
         for (int qq = 2; qq >= 0; --qq)

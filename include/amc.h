@@ -126,6 +126,14 @@ typedef struct {
                               * both planes).  Else every sweep recomputes its Phi tiles
                               * from Q and K.  The picks are the same either way. */
   amc_dtype cv_dtype;     /* C_v output type (default AMC_F32) */
+  int32_t head_groups;    /* amc_compact splits the heads into this many groups of
+                           * consecutive heads (at most H are used), each run on a
+                           * stream of its own created for the call and joined back
+                           * to the caller's stream: the groups' mass-feature passes
+                           * (matrix-core bound) overlap the selection loops of the
+                           * groups before them.  Results are the same bits for any
+                           * value.  0 = automatic (4 for H >= 256 with H a multiple
+                           * of 32, else 1); 1..16, else AMC_ERR_INVALID_ARG. */
   uint32_t flags;         /* AMC_FLAG_* */
   void *timer;            /* optional amc_timer_create() handle; NULL = none */
 } amc_options;

@@ -96,6 +96,11 @@ def test_invalid_options_are_rejected():
     assert L.amc_workspace_size(ctypes.byref(p), ctypes.byref(o), ctypes.byref(out)) == amc.AMC_ERR_UNSUPPORTED
     o = amc.make_options(nnls_tol=-1.0)
     assert L.amc_workspace_size(ctypes.byref(p), ctypes.byref(o), ctypes.byref(out)) == amc.AMC_ERR_INVALID_ARG
+    for g in (-1, 17):
+        o = amc.make_options(head_groups=g)
+        assert L.amc_workspace_size(ctypes.byref(p), ctypes.byref(o), ctypes.byref(out)) == amc.AMC_ERR_INVALID_ARG
+    o = amc.make_options(head_groups=16)
+    assert L.amc_workspace_size(ctypes.byref(p), ctypes.byref(o), ctypes.byref(out)) == amc.AMC_OK
 
 
 def test_compact_argument_errors_return_before_any_launch():

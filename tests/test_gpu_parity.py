@@ -196,6 +196,30 @@ def test_band_and_exact_paths_agree(monkeypatch):
     assert torch.allclose(a.beta, b.beta, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("dtype,k,R,groups", [("bf16", 4, 2, 3), ("f32", 1, 1, 4), ("bf16", 2, 3, 7)])
+def test_head_groups_agree(dtype, k, R, groups):
+    """Heads split into groups on separate streams give the same bits as one
+    group: no kernel's arithmetic for a head depends on the other heads of the
+    launch (uneven group sizes, heads with different cycle counts)."""
+    shapes = [(200, 700, 40), (129, 257, 23), (256, 1000, 64), (64, 300, 9), (300, 513, 50),
+              (100, 900, 31), (150, 640, 12), (90, 400, 77)]
+    heads = [synth.make_head([41, i], n, T, 128, dtype == "bf16", dtype) for i, (n, T, _) in enumerate(shapes)]
+    budgets = [t for _, _, t in shapes]
+    _say(f"head groups {dtype} k={k} R={R} groups={groups}")
+    a = _run(heads, budgets, dtype, k, R, head_groups=1)
+    b = _run(heads, budgets, dtype, k, R, head_groups=groups)
+    assert torch.equal(a.sel_idx, b.sel_idx)
+    assert torch.equal(a.beta, b.beta)
+    assert torch.equal(a.Ck, b.Ck)
+    assert torch.equal(a.Cv, b.Cv)
+    assert torch.equal(a.head_status, b.head_status)
+    ta, tb = a.trace(), b.trace()
+    assert np.array_equal(ta["shift"], tb["shift"])
+    for key in ("pick", "pick_score", "weight", "runner_up", "nnls_iters"):
+        for h in range(len(heads)):
+            assert np.array_equal(ta[key][h], tb[key][h]), (key, h)
+
+
 @pytest.mark.parametrize("dtype,d,k,R", [("bf16", 128, 4, 2), ("bf16", 64, 1, 1), ("f32", 64, 3, 3)])
 def test_compact_recompute_sweep(dtype, d, k, R):
     """Phi over the budget: every sweep rebuilds its Phi tiles from Q and K
