@@ -66,7 +66,7 @@ struct Plan {
            o_rhs = 0, o_cvsel = 0, o_pos = 0, o_cand_val = 0, o_cand_idx = 0, o_flist = 0, o_fcount = 0,
            o_dn = 0, o_L = 0, o_nnL = 0, o_nnP = 0, o_nnnp = 0, o_gA = 0, o_nnvec = 0, o_cand_lo = 0,
            o_cand_lidx = 0, o_cand_cnt = 0, o_band_list = 0, o_band_cnt = 0, o_exact = 0, o_stage = 0,
-           o_part = 0, o_vt = 0, total = 0;
+           o_part = 0, o_vt = 0, o_qdig = 0, o_kdig = 0, o_qexp = 0, o_kexp = 0, o_f64h = 0, total = 0;
 };
 
 static amc_status check_problem(const amc_problem *p) {
@@ -224,7 +224,15 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     pl.o_stage = take(8ull * nn * kBandCap);
     pl.o_part = take(8ull * H * kBandCap * dm.max_qblk);
   }
-  if (dm.in_bf16) pl.o_vt = take(2ull * vt);  // transposed value tiles of the mass-feature kernel
+  if (dm.in_bf16) {
+    pl.o_vt = take(2ull * vt);  // transposed value tiles of the mass-feature kernel
+    // digit form of the rows for the int8 logits
+    pl.o_qdig = take(5ull * d * nn);
+    pl.o_kdig = take(5ull * d * TT);
+    pl.o_qexp = take(4ull * nn);
+    pl.o_kexp = take(4ull * TT);
+    pl.o_f64h = take(4ull * H);
+  }
   pl.total = off;
   return AMC_OK;
 }
@@ -282,7 +290,15 @@ static Buffers head_range(const Buffers &b, int h0, int64_t max_qblk) {
   if (b.band_cnt) r.band_cnt = b.band_cnt + h0;
   if (b.exact) r.exact = b.exact + h0;
   if (b.part) r.part = b.part + int64_t(h0) * kBandCap * max_qblk;
+  if (b.f64_heads) r.f64_heads = b.f64_heads + h0;
   return r;
+}
+
+// AMC_PHI_LOGITS=f64 sends every head of a bf16 call to the float64-MFMA
+// logit kernel (the int8 digit kernel is the default).
+static bool phi_logits_f64() {
+  const char *e = std::getenv("AMC_PHI_LOGITS");
+  return e && std::strcmp(e, "f64") == 0;
 }
 
 // Largest candidate band the float64 rescoring takes; AMC_BAND_CAP lowers it
@@ -412,6 +428,13 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   b.phi = nullptr;
   b.phi16 = pl.store_phi ? reinterpret_cast<uint16_t *>(ws + pl.o_phi) : nullptr;
   b.vt = pl.dm.in_bf16 ? reinterpret_cast<uint16_t *>(ws + pl.o_vt) : nullptr;
+  if (pl.dm.in_bf16 && !phi_logits_f64()) {
+    b.qdig = reinterpret_cast<int8_t *>(ws + pl.o_qdig);
+    b.kdig = reinterpret_cast<int8_t *>(ws + pl.o_kdig);
+    b.qexp = reinterpret_cast<int32_t *>(ws + pl.o_qexp);
+    b.kexp = reinterpret_cast<int32_t *>(ws + pl.o_kexp);
+    b.f64_heads = reinterpret_cast<int32_t *>(ws + pl.o_f64h);
+  }
   b.m = reinterpret_cast<double *>(ws + pl.o_m);
   b.r = reinterpret_cast<double *>(ws + pl.o_r);
   b.mhat = reinterpret_cast<double *>(ws + pl.o_mhat);

@@ -57,6 +57,10 @@ struct Buffers {
   uint16_t *phi16;     // per head at 2*phi_off: high plane [n][ldT], then low plane [n][ldT];
                        // within each 64-key tile, key 16 kb + g + 4 e sits at 32 (kb/2) + 8 g + 4 (kb%2) + e
   uint16_t *vt;        // bf16 inputs: per head at vt_off, [T/64 tiles][d][64] values, key-permuted
+  int8_t *qdig, *kdig; // bf16 inputs: rows of Q and K as five base-256 digit rows each ([rows][5][d]);
+                       // null: every head takes the float64 logit kernel
+  int32_t *qexp, *kexp;  // row exponents of the digit form, [rows of Q], [rows of K]
+  int32_t *f64_heads;  // [H] 1: a row of the head is not exact in digit form (float64 logits)
   double *m, *r, *mhat;  // [sum n]
   float *Y;            // [sum n][d]
   int32_t *sel_slot;   // [sum T]  0 = unselected, else 1 + slot

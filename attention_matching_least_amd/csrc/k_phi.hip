@@ -5,8 +5,10 @@
 //
 // The fit side of the method (m, and later the Gram system and residual) is
 // conditioned like cond(Phi_S^T Phi_S) ~ 1e9, so the logits that feed m are
-// computed in float64 on the MFMA units (v_mfma_f64_16x16x4f64) from the
-// exact bf16/fp32 inputs; Phi is rounded to float32 only for storage, where
+// float64 dot products of the exact bf16/fp32 inputs: for bf16 rows, exact
+// integer products on the int8 MFMA units (the rows written as base-256
+// digits) joined in float64; otherwise v_mfma_f64_16x16x4f64.  Phi is
+// rounded to float32 only for storage, where
 // the memory-bound correlation sweeps read it.  Stored for the selection, each
 // float32 value is split into its high and low 16 bits, kept in two planes:
 // the high plane alone is Phi truncated to bfloat16 (what the bounded sweep
@@ -454,7 +456,8 @@ __global__ __launch_bounds__(256) void k_vt(const HeadDesc *__restrict__ desc, c
 //           bf16 terms, split by truncation), V operands one 16-byte read.
 // STORE: 0 = Phi not stored (every sweep recomputes it), 2 = stored planes.
 // Blocks map to heads XCD by XCD when xcd_map is set (H a multiple of 8):
-// the blocks of one head share one L2.
+// the blocks of one head share one L2.  gate (nullable): only the heads with
+// gate[h] != 0.
 // ---------------------------------------------------------------------------
 constexpr int P16_WAVES = kPhi16Rows / 16;
 
@@ -464,7 +467,8 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ vt, const float *__restrict__ beta_in,
     double scale, const float *__restrict__ shift_part, double *__restrict__ shift_out,
     double *__restrict__ tr_shift, uint16_t *__restrict__ phi16, double *__restrict__ m_out,
-    double *__restrict__ r_out, float *__restrict__ Y_out, int32_t *__restrict__ head_status) {
+    double *__restrict__ r_out, float *__restrict__ Y_out, int32_t *__restrict__ head_status,
+    const int32_t *__restrict__ gate) {
   constexpr int KCH = D / 8;        // 16-byte chunks per K row
   constexpr int NS = D / 4;         // k-steps of the logit MFMA
   constexpr int NA = D / 32;        // 16-byte K reads per key block
@@ -496,6 +500,7 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
     }
   }
   if (h >= H) return;
+  if (gate && gate[h] == 0) return;
   const HeadDesc Dh = desc[h];
   const int64_t q0 = int64_t(qb) * kPhi16Rows;
   if (q0 >= Dh.n) return;
@@ -716,6 +721,430 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
   if (bad && head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
 }
 
+// ---------------------------------------------------------------------------
+// Exact integer form of bf16 rows for the int8 logit kernel.  Per row of Q or
+// K, E is the largest binary exponent of its nonzero entries; each entry x
+// becomes the integer N = x 2^(37 - E) (|N| < 2^38), stored as five balanced
+// base-256 digits d_0..d_4 in [-128, 127] with N = sum_s d_s 256^s.  x lies on
+// this grid when its last significand bit is worth at least 2^(E - 37): for a
+// normal bf16, when its exponent is at least E - 30.  A head with an entry
+// off the grid, or a non-finite entry, gets f64_heads[h] = 1 and takes the
+// float64 logit kernel.
+// Layout: digit s of dims 8 j .. 8 j + 7 of row r at byte 5 D r + D s + 8 j, E
+// at exps[r]; rows are numbered as in Q and K.  One block = 256 / (D / 8)
+// rows, a head's n query rows first, then its T key rows.
+// ---------------------------------------------------------------------------
+constexpr int kDigits = 5;
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+
+// 2^(j/32) for j = 0..31, each rounded to the nearest float64.
+__constant__ double kExp2Tab32[32] = {
+    1.0, 1.0218971486541166, 1.0442737824274138, 1.0671404006768237,
+    1.0905077326652577, 1.1143867425958924, 1.1387886347566916, 1.1637248587775775,
+    1.189207115002721, 1.215247359980469, 1.241857812073484, 1.2690509571917332,
+    1.2968395546510096, 1.3252366431597413, 1.3542555469368927, 1.383909881963832,
+    1.4142135623730951, 1.4451808069770467, 1.4768261459394993, 1.5091644275934228,
+    1.5422108254079407, 1.5759808451078865, 1.6104903319492543, 1.645755478153965,
+    1.681792830507429, 1.718619298122478, 1.7562521603732995, 1.7947090750031072,
+    1.8340080864093424, 1.8741676341103, 1.9152065613971474, 1.9571441241754002};
+
+// exp(x) in float64 by the table-driven reduction of P. T. P. Tang (ACM
+// TOMS 15(2), 1989): x = (32 m + j) ln2/32 + r with |r| <= ln2/64 (ln2/32 in
+// two parts, so that r carries no cancellation error), exp(x) = 2^m 2^(j/32)
+// exp(r), and exp(r) - 1 from its Taylor polynomial of degree 6 (truncation
+// below 2^-58 for such r).  Within 1 ulp for x >= -745 (checked against a
+// 50-digit reference); x below that, and -inf, give 0; NaN stays NaN.
+// tab: the 32 values of kExp2Tab32.
+__device__ __forceinline__ double exp_tang(double x, const double *tab) {
+  const double N = __builtin_rint(x * 46.16624130844683);  // 32 / ln2
+  const int k = int(N);
+  double r = __builtin_fma(-N, 0.02166084939249829, x);  // ln2/32, leading part
+  r = __builtin_fma(-N, 7.247021293269686e-19, r);        // ln2/32, trailing part
+  double p = 1.0 / 720.0;
+  p = __builtin_fma(p, r, 1.0 / 120.0);
+  p = __builtin_fma(p, r, 1.0 / 24.0);
+  p = __builtin_fma(p, r, 1.0 / 6.0);
+  p = __builtin_fma(p, r, 0.5);
+  p = __builtin_fma(p, r, 1.0);
+  p *= r;
+  const double t = tab[k & 31];
+  const double e = __builtin_amdgcn_ldexp(__builtin_fma(t, p, t), k >> 5);
+  return x < -745.2 ? 0.0 : e;
+}
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+template <int D>
+__global__ __launch_bounds__(256) void k_digits(const HeadDesc *__restrict__ desc, const uint16_t *__restrict__ Q,
+                                                const uint16_t *__restrict__ K, int8_t *__restrict__ qdig,
+                                                int8_t *__restrict__ kdig, int32_t *__restrict__ qexp,
+                                                int32_t *__restrict__ kexp, int32_t *__restrict__ f64_heads) {
+  constexpr int TPR = D / 8;      // threads per row, 8 entries each
+  constexpr int RPB = 256 / TPR;  // rows per block
+  const int h = blockIdx.y;
+  const HeadDesc Dh = desc[h];
+  const int tid = threadIdx.x, j = tid % TPR;
+  const int64_t r = int64_t(blockIdx.x) * RPB + tid / TPR;
+  const bool active = r < Dh.n + Dh.T;
+  const bool isq = r < Dh.n;
+  const int64_t row = isq ? Dh.q_off + r : Dh.k_off + (r - Dh.n);
+  u32x4 w = {0u, 0u, 0u, 0u};
+  if (active) w = *reinterpret_cast<const u32x4 *>((isq ? Q : K) + row * D + 8 * j);
+  // x = M 2^P with M a signed integer (0 for zero)
+  int32_t M[8], P[8];
+  int emax = -100000, pmin = 100000;
+  int bad = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const uint32_t b = (w[i >> 1] >> (16 * (i & 1))) & 0xffffu;
+    const uint32_t ef = (b >> 7) & 0xffu, mt = b & 0x7fu;
+    int m = 0, p = 0;
+    if (ef == 0xffu) {
+      bad = 1;
+    } else if (ef == 0u) {
+      m = int(mt);  // zero or subnormal: mt 2^-133
+      p = -133;
+    } else {
+      m = int(mt | 0x80u);  // (128 + mt) 2^(ef - 134)
+      p = int(ef) - 134;
+    }
+    if (m != 0) {
+      emax = max(emax, p + 31 - __clz(m));
+      pmin = min(pmin, p);
+    }
+    M[i] = (b & 0x8000u) ? -m : m;
+    P[i] = p;
+  }
+#pragma unroll
+  for (int off = TPR / 2; off >= 1; off >>= 1) {
+    emax = max(emax, __shfl_xor(emax, off));
+    pmin = min(pmin, __shfl_xor(pmin, off));
+    bad |= __shfl_xor(bad, off);
+  }
+  const int E = emax == -100000 ? 0 : emax;
+  if (pmin < E - 37) bad = 1;
+  uint32_t dg[kDigits][2];
+#pragma unroll
+  for (int s = 0; s < kDigits; ++s) dg[s][0] = dg[s][1] = 0u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    int64_t N = (bad || M[i] == 0) ? 0 : int64_t(M[i]) * (int64_t(1) << (P[i] + 37 - E));
+#pragma unroll
+    for (int s = 0; s < kDigits; ++s) {
+      const int32_t d = int32_t(int8_t(uint8_t(uint64_t(N) & 0xffu)));
+      N = (N - d) >> 8;
+      dg[s][i >> 2] |= (uint32_t(d) & 0xffu) << (8 * (i & 3));
+    }
+  }
+  if (active) {
+    int8_t *out = (isq ? qdig : kdig) + row * (kDigits * D) + 8 * j;
+#pragma unroll
+    for (int s = 0; s < kDigits; ++s) *reinterpret_cast<u32x2 *>(out + s * D) = u32x2{dg[s][0], dg[s][1]};
+    if (j == 0) {
+      (isq ? qexp : kexp)[row] = E;
+      if (bad) atomicOr(f64_heads + h, 1);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Mass features for bf16 inputs with the logits on the int8 matrix units:
+// blocks, tiles, copies, Phi planes and Phi V as in k_phi16.  With the rows
+// in digit form (k_digits), the logit of query q and key k is
+//   2^(E_q + E_k - 74) sum_c C_c 256^c,  C_c = sum over digit pairs s + t = c
+//   of the int32 dot products of Q digit s and K digit t,
+// each product on v_mfma_i32_16x16x64_i8 (exact: |C_c| < 2^24).  The nine C_c
+// are joined in float64 (one rounding per join) and the power of two and the
+// logit scale applied in one multiply, so the result is the float64 dot
+// product of the bf16 inputs to within a few roundings, as the float64 MFMA
+// gives it.  The K digits of a tile arrive by the same asynchronous copies
+// (KROW slots per key: five digit rows and a pad), the key exponents like
+// the biases.  MFMA row 4 g + e is fed key g + 4 e of its 16-key block, so
+// the outputs land where the float64 kernel has them.  Heads with
+// f64_heads[h] != 0 return at once (the float64 kernel takes them).
+// ---------------------------------------------------------------------------
+template <int D, int STORE>
+__global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
+    const HeadDesc *__restrict__ desc, int H, int nqb, int xcd_map, const int8_t *__restrict__ qdig,
+    const int8_t *__restrict__ kdig, const int32_t *__restrict__ qexp, const int32_t *__restrict__ kexp,
+    const int32_t *__restrict__ f64_heads, const uint16_t *__restrict__ vt, const float *__restrict__ beta_in,
+    double scale, const float *__restrict__ shift_part, double *__restrict__ shift_out,
+    double *__restrict__ tr_shift, uint16_t *__restrict__ phi16, double *__restrict__ m_out,
+    double *__restrict__ r_out, float *__restrict__ Y_out, int32_t *__restrict__ head_status) {
+  constexpr int NCH = D / 64;             // 64-dim k-steps of the int8 MFMA
+  constexpr int DSL = kDigits * D / 16;   // 16-byte slots of one key's digits
+  constexpr int KROW = DSL + 1;           // slots per key row in LDS (one of padding)
+  constexpr int KSLOT = 64 * KROW;        // slots per K tile
+  constexpr int VSLOT = D * 9;            // slots per V tile
+  constexpr int NU = D / 16;              // 16-dim output blocks of Phi V
+  constexpr int KWORDS = KSLOT * 4;
+  constexpr int VWORDS = VSLOT * 4;
+  constexpr int NC = 2 * kDigits - 1;     // digit-pair classes s + t
+  static_assert(KSLOT % 64 == 0 && VSLOT % 64 == 0, "whole copies");
+  __shared__ __attribute__((aligned(16))) uint32_t lk_all[2 * KWORDS];
+  __shared__ __attribute__((aligned(16))) uint32_t lv_all[2 * VWORDS];
+  __shared__ __attribute__((aligned(16))) float sb[2][64];
+  __shared__ __attribute__((aligned(16))) int32_t se[2][64];
+  __shared__ double s_tab[32];
+  uint32_t *const lk0 = lk_all, *const lk1 = lk_all + KWORDS;
+  uint32_t *const lv0 = lv_all, *const lv1 = lv_all + VWORDS;
+  __shared__ double s_shift;
+
+  int h, qb;
+  {
+    const int b = blockIdx.x;
+    if (xcd_map) {
+      const int x = b & 7, slot = b >> 3;
+      h = x + 8 * (slot / nqb);
+      qb = slot % nqb;
+    } else {
+      h = b / nqb;
+      qb = b % nqb;
+    }
+  }
+  if (h >= H) return;
+  if (f64_heads[h] != 0) return;
+  const HeadDesc Dh = desc[h];
+  const int64_t q0 = int64_t(qb) * kPhi16Rows;
+  if (q0 >= Dh.n) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int c16 = lane & 15, g = lane >> 4;
+
+  if (tid < 64) {
+    float v = -INFINITY;
+    for (int64_t i = tid; i < Dh.n_sblk; i += 64) v = fmaxf(v, shift_part[Dh.sblk_off + i]);
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+    if (tid == 0) s_shift = double(v);
+  } else if (tid < 96) {
+    s_tab[tid - 64] = kExp2Tab32[tid - 64];
+  } else if (!beta_in && tid < 96 + 128) {
+    sb[(tid - 96) >> 6][(tid - 96) & 63] = 0.0f;  // no biases: both buffers stay zero
+  }
+
+  // B operand: query q, digit s, dims 64 c + 16 g + (0..15) at k-step c
+  const int64_t qw = q0 + 16 * wave;
+  const int64_t q = qw + c16;
+  const bool qvalid = q < Dh.n;
+  const int64_t qrow = Dh.q_off + (qvalid ? q : Dh.n - 1);
+  u32x4 qd[kDigits][NCH];
+#pragma unroll
+  for (int sd = 0; sd < kDigits; ++sd)
+#pragma unroll
+    for (int c = 0; c < NCH; ++c) {
+      qd[sd][c] = *reinterpret_cast<const u32x4 *>(qdig + qrow * (kDigits * D) + sd * D + 64 * c + 16 * g);
+      if (!qvalid) qd[sd][c] = u32x4{0u, 0u, 0u, 0u};
+    }
+  // scale 2^(E_q - 74): times 2^(E_k) per key, an exact power-of-two rescaling
+  const double qscale = ldexp(scale, qexp[qrow] - 74);
+
+  const int64_t T = Dh.T;
+  const int ntiles = int((T + 63) / 64);
+  // Copies as in k_phi16; K rows are KROW slots (slot m < DSL of key k holds
+  // bytes 16 m.. of its digit row), the pad duplicates slot 0.  Biases (wave
+  // 0) and key exponents (wave 1) take one 4-byte copy each, slot i holding
+  // the key stored at position i.
+  const char *kbase = reinterpret_cast<const char *>(kdig + Dh.k_off * (kDigits * D));
+  const char *vbase = reinterpret_cast<const char *>(vt + Dh.vt_off);
+  const char *bbase = beta_in ? reinterpret_cast<const char *>(beta_in + Dh.k_off) : nullptr;
+  const char *ebase = reinterpret_cast<const char *>(kexp + Dh.k_off);
+  const int Ti = int(T);
+  auto issue = [&](int tile, uint32_t *lk, uint32_t *lv, float *lb, int32_t *le) {
+    const int k0 = tile * 64;
+    // the lane index, opaque to the compiler here: the per-copy offsets are
+    // recomputed for every tile rather than held in registers across the loop
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+#pragma unroll
+    for (int inst = wave; inst < KSLOT / 64; inst += P16_WAVES) {
+      const int slot = inst * 64 + ln;
+      const int key = slot / KROW, m = slot % KROW;
+      const int row = k0 + key < Ti ? k0 + key : Ti - 1;
+      const uint32_t off = uint32_t(row * (kDigits * D) + 16 * (m < DSL ? m : 0));
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(kbase + off),
+                                       (void __attribute__((address_space(3))) *)(lk + inst * 256), 16, 0, 0);
+    }
+#pragma unroll
+    for (int inst = wave; inst < VSLOT / 64; inst += P16_WAVES) {
+      const int slot = inst * 64 + ln;
+      const int dim = slot / 9, lc = slot % 9;
+      const uint32_t off = uint32_t((tile * D + dim) * 64 + 8 * (lc < 8 ? lc : 0)) * 2u;
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(vbase + off),
+                                       (void __attribute__((address_space(3))) *)(lv + inst * 256), 16, 0, 0);
+    }
+    if (wave < 2) {
+      const int key = k0 + 16 * (2 * (ln >> 5) + ((ln >> 2) & 1)) + ((ln >> 3) & 3) + 4 * (ln & 3);
+      const uint32_t off = uint32_t(key < Ti ? key : Ti - 1) * 4u;
+      if (wave == 0 && bbase)
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(bbase + off),
+                                         (void __attribute__((address_space(3))) *)lb, 4, 0, 0);
+      if (wave == 1)
+        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(ebase + off),
+                                         (void __attribute__((address_space(3))) *)le, 4, 0, 0);
+    }
+  };
+
+  f32x4 uacc[NU];
+#pragma unroll
+  for (int i = 0; i < NU; ++i) uacc[i] = f32x4{0.f, 0.f, 0.f, 0.f};
+  double msum = 0.0;
+  // MFMA row c16 of a 16-key block is fed key (c16 >> 2) + 4 (c16 & 3)
+  const int krow = (c16 >> 2) + 4 * (c16 & 3);
+
+  auto compute = [&](int tile, const uint32_t *lk, const uint32_t *lv, const float *lb, const int32_t *le,
+                     bool next, uint32_t *nk, uint32_t *nv, float *nb, int32_t *ne, double s) {
+    const int64_t k0 = int64_t(tile) * 64;
+    if (next) issue(tile + 1, nk, nv, nb, ne);
+    const u32x4 *kl4 = reinterpret_cast<const u32x4 *>(lk) + (krow * KROW + g);
+    const u32x4 *vl4 = reinterpret_cast<const u32x4 *>(lv) + (c16 * 9 + g);
+    // Software pipeline over the four 16-key blocks: the exps of block kb - 1
+    // are independent of the MFMAs of block kb, so the two interleave.
+    float x[4][4];
+    double arg[4][4];  // exp arguments (scaled logit + bias - shift)
+#pragma unroll
+    for (int kb = 0; kb <= 4; ++kb) {
+      i32x4 acc[NC];
+      if (kb < 4) {
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[c] = i32x4{0, 0, 0, 0};
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+          u32x4 kd[kDigits];
+#pragma unroll
+          for (int t = 0; t < kDigits; ++t) kd[t] = kl4[kb * 16 * KROW + t * (D / 16) + 4 * c];
+#pragma unroll
+          for (int t = 0; t < kDigits; ++t)
+#pragma unroll
+            for (int sd = 0; sd < kDigits; ++sd)
+              acc[sd + t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, kd[t]),
+                                                                  __builtin_bit_cast(i32x4, qd[sd][c]), acc[sd + t],
+                                                                  0, 0, 0);
+        }
+      }
+      if (kb > 0) {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const double p = exp_tang(arg[kb - 1][e], s_tab);
+          const double pm = int(k0) + phi_key(kb - 1, g, e) < Ti ? p : 0.0;
+          msum += pm;
+          x[kb - 1][e] = float(pm);
+        }
+      }
+      if (kb < 4) {
+        const f32x4 bz = *reinterpret_cast<const f32x4 *>(lb + store_pos(kb, g, 0));
+        const i32x4 ke = *reinterpret_cast<const i32x4 *>(le + store_pos(kb, g, 0));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // C_0 + 256 C_1 and C_7 + 256 C_8 stay within int32 (|C_0| <= 2^21,
+          // |C_1| <= 2^22; the top digits are at most 64 in size, so
+          // |C_7| < 2^21.1, |C_8| < 2^19.1); the rest join in float64
+          double v = double(acc[0][e] + (acc[1][e] << 8));
+          double w256 = 256.0;
+#pragma unroll
+          for (int c = 2; c < NC - 2; ++c) {
+            w256 *= 256.0;
+            v = fma(double(acc[c][e]), w256, v);
+          }
+          v = fma(double(acc[NC - 2][e] + (acc[NC - 1][e] << 8)), w256 * 256.0, v);
+          arg[kb][e] = v * ldexp(qscale, ke[e]) + double(bz[e]) - s;
+        }
+      }
+    }
+    // the next tile's copies have landed
+    __builtin_amdgcn_s_waitcnt(0);
+    if constexpr (STORE == 2) {
+      if (qvalid) {
+        uint16_t *hp = phi16 + 2 * Dh.phi_off;
+        uint16_t *lp = hp + Dh.n * Dh.ldT;
+        uint32_t hw[8], lw[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t u0 = __float_as_uint(x[i >> 1][2 * (i & 1)]);
+          const uint32_t u1 = __float_as_uint(x[i >> 1][2 * (i & 1) + 1]);
+          hw[i] = (u0 >> 16) | (u1 & 0xffff0000u);
+          lw[i] = (u0 & 0xffffu) | (u1 << 16);
+        }
+        const int64_t at = q * Dh.ldT + k0 + 8 * g;
+        __builtin_nontemporal_store(u32x4{hw[0], hw[1], hw[2], hw[3]}, reinterpret_cast<u32x4 *>(hp + at));
+        __builtin_nontemporal_store(u32x4{hw[4], hw[5], hw[6], hw[7]}, reinterpret_cast<u32x4 *>(hp + at + 32));
+        __builtin_nontemporal_store(u32x4{lw[0], lw[1], lw[2], lw[3]}, reinterpret_cast<u32x4 *>(lp + at));
+        __builtin_nontemporal_store(u32x4{lw[4], lw[5], lw[6], lw[7]}, reinterpret_cast<u32x4 *>(lp + at + 32));
+      }
+    }
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      uint32_t w[3][4];
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int e2 = 0; e2 < 2; ++e2) {
+          uint32_t t[3][2];
+#pragma unroll
+          for (int h2 = 0; h2 < 2; ++h2) {
+            const float v = x[2 * c + j][2 * e2 + h2];
+            const float hi = __uint_as_float(__float_as_uint(v) & 0xffff0000u);
+            const float r1 = v - hi;
+            const float mi = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+            const float lo = r1 - mi;
+            t[0][h2] = __float_as_uint(hi);
+            t[1][h2] = __float_as_uint(mi);
+            t[2][h2] = __float_as_uint(lo);
+          }
+#pragma unroll
+          for (int qq = 0; qq < 3; ++qq) w[qq][2 * j + e2] = (t[qq][0] >> 16) | (t[qq][1] & 0xffff0000u);
+        }
+#pragma unroll
+      for (int db = 0; db < NU; ++db) {
+        const u32x4 vv = vl4[db * 16 * 9 + 4 * c];
+        const bf16x8 bv = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+        for (int qq = 2; qq >= 0; --qq)
+          uacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+              __builtin_bit_cast(bf16x8, u32x4{w[qq][0], w[qq][1], w[qq][2], w[qq][3]}), bv, uacc[db], 0, 0, 0);
+      }
+    }
+  };
+
+  issue(0, lk0, lv0, sb[0], se[0]);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  const double s = s_shift;
+  if (qb == 0 && tid == 0) {
+    shift_out[h] = s;
+    if (tr_shift) tr_shift[h] = s;
+  }
+  for (int tile = 0; tile < ntiles; tile += 2) {
+    compute(tile, lk0, lv0, sb[0], se[0], tile + 1 < ntiles, lk1, lv1, sb[1], se[1], s);
+    __syncthreads();
+    if (tile + 1 >= ntiles) break;
+    compute(tile + 1, lk1, lv1, sb[1], se[1], tile + 2 < ntiles, lk0, lv0, sb[0], se[0], s);
+    __syncthreads();
+  }
+
+  msum += __shfl_xor(msum, 16);
+  msum += __shfl_xor(msum, 32);
+  bool bad = false;
+  if (g == 0 && qvalid) {
+    m_out[Dh.n_off + q] = msum;
+    if (r_out) r_out[Dh.n_off + q] = msum;
+    bad |= !isfinite(msum);
+  }
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    const double mq = __shfl(msum, 4 * g + e);
+    const int64_t qy = qw + 4 * g + e;
+    if (qy < Dh.n) {
+#pragma unroll
+      for (int db = 0; db < NU; ++db) {
+        const float y = float(double(uacc[db][e]) / mq);
+        bad |= !isfinite(y);
+        Y_out[(Dh.n_off + qy) * D + db * 16 + c16] = y;
+      }
+    }
+  }
+  if (bad && head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
+}
+
 }  // namespace
 
 hipError_t launch_copy_words(uint64_t *dst, const uint64_t *src, int64_t count, hipStream_t s) {
@@ -775,14 +1204,28 @@ static void launch_phi_store(const Dims &dm, const Buffers &b, hipStream_t s) {
 }
 
 template <int STORE>
-static void launch_phi16(const Dims &dm, const Buffers &b, hipStream_t s) {
+static void launch_phi8(const Dims &dm, const Buffers &b, hipStream_t s) {
+  const int nqb = int((dm.max_n + kPhi16Rows - 1) / kPhi16Rows);
+  const int xcd_map = (dm.H % 8 == 0) ? 1 : 0;
+  dim3 grid(unsigned(nqb * dm.H));
+#define AMC_PHI8_ARGS b.desc, dm.H, nqb, xcd_map, b.qdig, b.kdig, b.qexp, b.kexp, b.f64_heads, b.vt, b.beta_in, \
+    dm.scale, b.shift_part, b.shift, b.tr_shift, b.phi16, b.m, b.r, b.Y, b.head_status
+  if (dm.d == 128)
+    hipLaunchKernelGGL((k_phi8<128, STORE>), grid, dim3(kPhi16Rows * 4), 0, s, AMC_PHI8_ARGS);
+  else
+    hipLaunchKernelGGL((k_phi8<64, STORE>), grid, dim3(kPhi16Rows * 4), 0, s, AMC_PHI8_ARGS);
+#undef AMC_PHI8_ARGS
+}
+
+template <int STORE>
+static void launch_phi16(const Dims &dm, const Buffers &b, const int32_t *gate, hipStream_t s) {
   const int nqb = int((dm.max_n + kPhi16Rows - 1) / kPhi16Rows);
   const int xcd_map = (dm.H % 8 == 0) ? 1 : 0;
   dim3 grid(unsigned(nqb * dm.H));
   const uint16_t *Q = static_cast<const uint16_t *>(b.Q);
   const uint16_t *K = static_cast<const uint16_t *>(b.K);
 #define AMC_PHI16_ARGS b.desc, dm.H, nqb, xcd_map, Q, K, b.vt, b.beta_in, dm.scale, b.shift_part, b.shift, b.tr_shift, \
-    b.phi16, b.m, b.r, b.Y, b.head_status
+    b.phi16, b.m, b.r, b.Y, b.head_status, gate
   if (dm.d == 128)
     hipLaunchKernelGGL((k_phi16<128, STORE>), grid, dim3(kPhi16Rows * 4), 0, s, AMC_PHI16_ARGS);
   else
@@ -803,8 +1246,32 @@ hipError_t launch_phi(const Dims &dm, const Buffers &b, int store, hipStream_t s
   if (store == 1 && !b.phi) return hipErrorInvalidValue;
   if (store == 2 && !b.phi16) return hipErrorInvalidValue;
   if (dm.in_bf16 && b.vt && store != 1) {
-    if (store == 2) launch_phi16<2>(dm, b, s);
-    else launch_phi16<0>(dm, b, s);
+    if (b.qdig) {
+      // int8 logits for the heads whose rows are exact in digit form, float64
+      // MFMA logits for the rest
+      hipError_t e = launch_fill_i32(b.f64_heads, dm.H, 0, s);
+      if (e != hipSuccess) return e;
+      constexpr int kRowsPerBlock128 = 256 / 16, kRowsPerBlock64 = 256 / 8;
+      const int64_t rows = dm.max_n + dm.max_T;
+      const uint16_t *Q = static_cast<const uint16_t *>(b.Q);
+      const uint16_t *K = static_cast<const uint16_t *>(b.K);
+      if (dm.d == 128)
+        hipLaunchKernelGGL(k_digits<128>, dim3(unsigned((rows + kRowsPerBlock128 - 1) / kRowsPerBlock128), unsigned(dm.H)),
+                           dim3(256), 0, s, b.desc, Q, K, b.qdig, b.kdig, b.qexp, b.kexp, b.f64_heads);
+      else
+        hipLaunchKernelGGL(k_digits<64>, dim3(unsigned((rows + kRowsPerBlock64 - 1) / kRowsPerBlock64), unsigned(dm.H)),
+                           dim3(256), 0, s, b.desc, Q, K, b.qdig, b.kdig, b.qexp, b.kexp, b.f64_heads);
+      if (store == 2) {
+        launch_phi8<2>(dm, b, s);
+        launch_phi16<2>(dm, b, b.f64_heads, s);
+      } else {
+        launch_phi8<0>(dm, b, s);
+        launch_phi16<0>(dm, b, b.f64_heads, s);
+      }
+      return hipGetLastError();
+    }
+    if (store == 2) launch_phi16<2>(dm, b, nullptr, s);
+    else launch_phi16<0>(dm, b, nullptr, s);
     return hipGetLastError();
   }
   if (store == 1) launch_phi_store<1>(dm, b, s);

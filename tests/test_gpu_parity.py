@@ -196,6 +196,41 @@ def test_band_and_exact_paths_agree(monkeypatch):
     assert torch.allclose(a.beta, b.beta, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("d,k,R", [(128, 4, 2), (128, 1, 1), (64, 4, 2)])
+def test_int8_and_f64_logits(monkeypatch, d, k, R):
+    """bf16 logits on the int8 matrix units (the rows as exact base-256 digit
+    integers) against the float64-MFMA kernel: the same picks, and weights and
+    values equal to float64 rounding.  A query entry of head 0 and a key entry
+    of head 1 sit 2^-40 below their rows' largest, off the digit grid: those
+    heads take the float64 kernel within the same call.  Every head still
+    matches the oracle."""
+    if d == 128:
+        shapes = [(300, 700, 40), (129, 257, 23), (200, 1000, 64)]
+        heads = [synth.make_head([30, i], n, T, d, True, "bf16") for i, (n, T, _) in enumerate(shapes)]
+        betas = [synth.random_beta([31, i], T, 1.0) for i, (_, T, _) in enumerate(shapes)]
+    else:
+        shapes = [(256, 512, 32), (256, 512, 31), (200, 300, 20)]
+        heads = [synth.make_head([40, i], n, T, d, True, "bf16") for i, (n, T, _) in enumerate(shapes)]
+        betas = None
+    heads[0].Q[5, 3] = 1.5 * 2.0 ** -40
+    heads[1].K[7, 10] = -1.25 * 2.0 ** -38
+    budgets = [t for _, _, t in shapes]
+    _say(f"int8 vs f64 logits d={d} k={k} R={R}")
+    a = _run(heads, budgets, "bf16", k, R, beta_in=betas)
+    monkeypatch.setenv("AMC_PHI_LOGITS", "f64")
+    b = _run(heads, budgets, "bf16", k, R, beta_in=betas)
+    _say(f"head status {a.head_status.cpu().numpy()}")
+    assert torch.equal(a.head_status, b.head_status)
+    assert np.all(a.head_status.cpu().numpy() == 0)
+    assert torch.equal(a.sel_idx, b.sel_idx)
+    assert torch.allclose(a.beta, b.beta, rtol=1e-6, atol=1e-6)
+    assert torch.allclose(a.Cv, b.Cv, rtol=1e-5, atol=1e-5)
+    tr = a.trace()
+    for i, h in enumerate(heads):
+        bi = None if betas is None else betas[i]
+        _assert_ok(replay_check(h.Q, h.K, h.V, budgets[i], k, R, a, i, beta_in=bi, trace=tr), f"head{i}")
+
+
 @pytest.mark.parametrize("dtype,k,R,groups", [("bf16", 4, 2, 3), ("f32", 1, 1, 4), ("bf16", 2, 3, 7)])
 def test_head_groups_agree(dtype, k, R, groups):
     """Heads split into groups on separate streams give the same bits as one
