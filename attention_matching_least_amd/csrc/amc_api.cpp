@@ -66,7 +66,7 @@ struct Plan {
            o_rhs = 0, o_cvsel = 0, o_pos = 0, o_cand_val = 0, o_cand_idx = 0, o_flist = 0, o_fcount = 0,
            o_dn = 0, o_L = 0, o_nnL = 0, o_nnP = 0, o_nnnp = 0, o_gA = 0, o_nnvec = 0, o_cand_lo = 0,
            o_cand_lidx = 0, o_cand_cnt = 0, o_band_list = 0, o_band_cnt = 0, o_exact = 0, o_stage = 0,
-           o_part = 0, o_vt = 0, o_qdig = 0, o_kdig = 0, o_qexp = 0, o_kexp = 0, o_f64h = 0, total = 0;
+           o_part = 0, o_vt = 0, o_qdig = 0, o_kdig = 0, o_qexp = 0, o_ktab = 0, o_f64h = 0, total = 0;
 };
 
 static amc_status check_problem(const amc_problem *p) {
@@ -118,7 +118,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   dm.in_bf16 = p->in_dtype == AMC_BF16;
   dm.scale = p->scale > 0.0f ? double(p->scale) : 1.0 / std::sqrt(double(d));
   pl.desc.assign(H, HeadDesc{});
-  int64_t phi = 0, nn = 0, tt = 0, t2 = 0, panel = 0, cblk = 0, sblk = 0, cyc = 0, TT = 0, tri = 0, vt = 0;
+  int64_t phi = 0, nn = 0, tt = 0, t2 = 0, panel = 0, cblk = 0, sblk = 0, cyc = 0, TT = 0, tri = 0, vt = 0, ktr = 0;
   for (int h = 0; h < H; ++h) {
     HeadDesc &D = pl.desc[h];
     D.n = p->cu_q[h + 1] - p->cu_q[h];
@@ -130,6 +130,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     // (4-key segments), 16-bit planes for the selection (whole 64-key tiles)
     D.ldT = features_only ? (D.T + 3) / 4 * 4 : (D.T + 63) / 64 * 64;
     D.vt_off = vt;
+    D.kt_off = ktr;
     D.phi_off = phi;
     D.n_off = nn;
     D.t_off = tt;
@@ -147,7 +148,8 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     }
     const int64_t cycles = ceil_div(D.t, pl.kR);
     phi += D.n * D.ldT;
-    vt += (D.T + 63) / 64 * 64 * d;
+    vt += (D.T + 63) / 64 * 72 * d;
+    ktr += (D.T + 63) / 64 * 64;
     nn += D.n;
     tt += D.t;
     t2 += D.t * D.t;
@@ -228,9 +230,9 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     pl.o_vt = take(2ull * vt);  // transposed value tiles of the mass-feature kernel
     // digit form of the rows for the int8 logits
     pl.o_qdig = take(5ull * d * nn);
-    pl.o_kdig = take(5ull * d * TT);
     pl.o_qexp = take(4ull * nn);
-    pl.o_kexp = take(4ull * TT);
+    pl.o_kdig = take((5ull * d + 16) * ktr);
+    pl.o_ktab = take(16ull * ktr);
     pl.o_f64h = take(4ull * H);
   }
   pl.total = off;
@@ -430,9 +432,9 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   b.vt = pl.dm.in_bf16 ? reinterpret_cast<uint16_t *>(ws + pl.o_vt) : nullptr;
   if (pl.dm.in_bf16 && !phi_logits_f64()) {
     b.qdig = reinterpret_cast<int8_t *>(ws + pl.o_qdig);
-    b.kdig = reinterpret_cast<int8_t *>(ws + pl.o_kdig);
     b.qexp = reinterpret_cast<int32_t *>(ws + pl.o_qexp);
-    b.kexp = reinterpret_cast<int32_t *>(ws + pl.o_kexp);
+    b.kdig = reinterpret_cast<int8_t *>(ws + pl.o_kdig);
+    b.ktab = reinterpret_cast<uint8_t *>(ws + pl.o_ktab);
     b.f64_heads = reinterpret_cast<int32_t *>(ws + pl.o_f64h);
   }
   b.m = reinterpret_cast<double *>(ws + pl.o_m);

@@ -43,8 +43,9 @@ struct HeadDesc {
   int64_t cyc_off;        // first cycle of the head in the per-cycle trace arrays
   int64_t tri_off;        // first element of the head's packed triangle (value-fit factor)
   int64_t vt_off;         // first element of the head's transposed value tiles (bf16 inputs)
+  int64_t kt_off;         // first row of the head in the arrays of keys padded to whole 64-key tiles
 };
-static_assert(sizeof(HeadDesc) == 18 * 8, "HeadDesc layout");
+static_assert(sizeof(HeadDesc) == 19 * 8, "HeadDesc layout");
 
 // Device pointers of the workspace carve-up and of the caller's buffers.
 struct Buffers {
@@ -56,10 +57,15 @@ struct Buffers {
   float *phi;          // [sum n*ldT] float32 Phi (the mass-feature entry point's output)
   uint16_t *phi16;     // per head at 2*phi_off: high plane [n][ldT], then low plane [n][ldT];
                        // within each 64-key tile, key 16 kb + g + 4 e sits at 32 (kb/2) + 8 g + 4 (kb%2) + e
-  uint16_t *vt;        // bf16 inputs: per head at vt_off, [T/64 tiles][d][64] values, key-permuted
-  int8_t *qdig, *kdig; // bf16 inputs: rows of Q and K as five base-256 digit rows each ([rows][5][d]);
-                       // null: every head takes the float64 logit kernel
-  int32_t *qexp, *kexp;  // row exponents of the digit form, [rows of Q], [rows of K]
+  uint16_t *vt;        // bf16 inputs: per head at vt_off, [T/64 tiles][d][72] values, key-permuted
+                       // (64 per row and a pad of 8, the layout the mass-feature kernels stage)
+  int8_t *qdig;        // bf16 inputs: rows of Q as five base-256 digit rows ([rows][5][d]); null:
+                       // every head takes the float64 logit kernel
+  int32_t *qexp;       // [rows of Q] row exponents of the digit form
+  int8_t *kdig;        // per head at kt_off rows: K rows padded to whole tiles, each row its five
+                       // digit rows and 16 bytes of pad ([rows][5 d + 16])
+  uint8_t *ktab;       // per head at kt_off / 64: per 64-key tile 1 KiB, float64 (bias - shift)
+                       // of each key (-inf past T), then its int32 row exponent, in stored order
   int32_t *f64_heads;  // [H] 1: a row of the head is not exact in digit form (float64 logits)
   double *m, *r, *mhat;  // [sum n]
   float *Y;            // [sum n][d]

@@ -399,10 +399,13 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
 }
 
 // ---------------------------------------------------------------------------
-// value tiles for the bf16 mass-feature kernel: per head and 64-key tile, V
-// transposed to [d][64] with the keys in the order the Phi V product reduces
+// value tiles for the bf16 mass-feature kernels: per head and 64-key tile, V
+// transposed to [d][72] with the keys in the order the Phi V product reduces
 // them: position 32 c + 8 g + 4 j + e holds key 32 c + 16 j + g + 4 e (keys
-// past T are zero).  One block = one tile.
+// past T are zero), positions 64..71 zero.  Each row is thus the nine 16-byte
+// slots the kernels stage in LDS (eight and a pad that spreads the reads over
+// the banks), and a tile reaches LDS as one contiguous copy.  One block = one
+// tile.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_vt(const HeadDesc *__restrict__ desc, const uint16_t *__restrict__ V,
@@ -422,9 +425,13 @@ __global__ __launch_bounds__(256) void k_vt(const HeadDesc *__restrict__ desc, c
     *reinterpret_cast<u32x4 *>(&vs[key * VSTR + 8 * c]) = w;
   }
   __syncthreads();
-  uint16_t *out = vt + Dh.vt_off + int64_t(tile) * D * 64;
-  for (int gi = tid; gi < D * 8; gi += 256) {
-    const int dim = gi / 8, c8 = gi % 8;
+  uint16_t *out = vt + Dh.vt_off + int64_t(tile) * D * 72;
+  for (int gi = tid; gi < D * 9; gi += 256) {
+    const int dim = gi / 9, c8 = gi % 9;
+    if (c8 == 8) {
+      *reinterpret_cast<u32x4 *>(out + dim * 72 + 64) = u32x4{0u, 0u, 0u, 0u};
+      continue;
+    }
     uint32_t w[4];
 #pragma unroll
     for (int t2 = 0; t2 < 4; ++t2) {
@@ -437,7 +444,7 @@ __global__ __launch_bounds__(256) void k_vt(const HeadDesc *__restrict__ desc, c
       }
       w[t2] = pair[0] | (pair[1] << 16);
     }
-    *reinterpret_cast<u32x4 *>(out + dim * 64 + 8 * c8) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4 *>(out + dim * 72 + 8 * c8) = u32x4{w[0], w[1], w[2], w[3]};
   }
 }
 
@@ -533,10 +540,10 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
   // Asynchronous copies of tile `tile` into one buffer set: each copy fills
   // 64 consecutive 16-byte slots (lane i the i-th); the copies are dealt to
   // the waves in turn.  K rows are KROW slots (chunk m of key k at slot
-  // k KROW + m), V rows (dims) 9 slots; a padding slot takes a duplicate of
-  // the row's first chunk.  The biases take one 4-byte copy (wave 0), slot i
-  // holding the key stored at position i (store_pos), so that a lane's 16
-  // biases are two runs of 8.
+  // k KROW + m; the padding slot takes a duplicate of the row's first chunk),
+  // V rows (dims) 9 slots, copied as they lie in the value tiles.  The
+  // biases take one 4-byte copy (wave 0), slot i holding the key stored at
+  // position i (store_pos), so that a lane's 16 biases are two runs of 8.
   // Sources are a per-head base plus a 32-bit byte offset.
   const char *kbase = reinterpret_cast<const char *>(K + Dh.k_off * D);
   const char *vbase = reinterpret_cast<const char *>(vt + Dh.vt_off);
@@ -554,9 +561,7 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
     }
 #pragma unroll
     for (int inst = wave; inst < VSLOT / 64; inst += P16_WAVES) {
-      const int slot = inst * 64 + lane;
-      const int dim = slot / 9, lc = slot % 9;
-      const uint32_t off = uint32_t((tile * D + dim) * 64 + 8 * (lc < 8 ? lc : 0)) * 2u;
+      const uint32_t off = uint32_t(tile * (VSLOT * 16) + inst * 1024 + lane * 16);
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(vbase + off),
                                        (void __attribute__((address_space(3))) *)(lv + inst * 256), 16, 0, 0);
     }
@@ -721,21 +726,10 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
   if (bad && head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
 }
 
-// ---------------------------------------------------------------------------
-// Exact integer form of bf16 rows for the int8 logit kernel.  Per row of Q or
-// K, E is the largest binary exponent of its nonzero entries; each entry x
-// becomes the integer N = x 2^(37 - E) (|N| < 2^38), stored as five balanced
-// base-256 digits d_0..d_4 in [-128, 127] with N = sum_s d_s 256^s.  x lies on
-// this grid when its last significand bit is worth at least 2^(E - 37): for a
-// normal bf16, when its exponent is at least E - 30.  A head with an entry
-// off the grid, or a non-finite entry, gets f64_heads[h] = 1 and takes the
-// float64 logit kernel.
-// Layout: digit s of dims 8 j .. 8 j + 7 of row r at byte 5 D r + D s + 8 j, E
-// at exps[r]; rows are numbered as in Q and K.  One block = 256 / (D / 8)
-// rows, a head's n query rows first, then its T key rows.
-// ---------------------------------------------------------------------------
 constexpr int kDigits = 5;
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef double f64x2 __attribute__((ext_vector_type(2)));
 
 // 2^(j/32) for j = 0..31, each rounded to the nearest float64.
 __constant__ double kExp2Tab32[32] = {
@@ -771,24 +765,65 @@ __device__ __forceinline__ double exp_tang(double x, const double *tab) {
   const double e = __builtin_amdgcn_ldexp(__builtin_fma(t, p, t), k >> 5);
   return x < -745.2 ? 0.0 : e;
 }
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
+// ---------------------------------------------------------------------------
+// Exact integer form of bf16 rows for the int8 logit kernel.  Per row of Q or
+// K, E is the largest binary exponent of its nonzero entries; each entry x
+// becomes the integer N = x 2^(37 - E) (|N| < 2^38), stored as five balanced
+// base-256 digits d_0..d_4 in [-128, 127] with N = sum_s d_s 256^s.  x lies on
+// this grid when its last significand bit is worth at least 2^(E - 37): for a
+// normal bf16, when its exponent is at least E - 30.  A head with an entry
+// off the grid, or a non-finite entry, gets f64_heads[h] = 1 and takes the
+// float64 logit kernel.
+// Layouts: a Q row r: digit s of dims 8 j .. 8 j + 7 at qdig[5 D r + D s + 8 j],
+// 4 E + z at qexp[r] (rows numbered as in Q), z the row's low digits that are
+// zero in all its entries, counted up to 2.  K rows run over the head's keys
+// padded to whole 64-key tiles (rows past T all zero), 5 D + 16 bytes each
+// (the five digit rows, then 16 bytes that only keep the rows of a tile
+// spread over the LDS banks once staged), from row kt_off.  Per tile, 1 KiB
+// of ktab: the float64 bias - shift of each key (-inf past T), then its int32
+// E, both in stored-key order (position store_pos of the key), then at byte
+// 768 z of each 16-key block (its smallest row z).  One block = 256 / (D / 8)
+// rows, a head's n query rows first (to a whole block), then its padded key
+// rows.
+// ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void k_digits(const HeadDesc *__restrict__ desc, const uint16_t *__restrict__ Q,
-                                                const uint16_t *__restrict__ K, int8_t *__restrict__ qdig,
-                                                int8_t *__restrict__ kdig, int32_t *__restrict__ qexp,
-                                                int32_t *__restrict__ kexp, int32_t *__restrict__ f64_heads) {
+                                                const uint16_t *__restrict__ K, const float *__restrict__ beta_in,
+                                                const float *__restrict__ shift_part, int8_t *__restrict__ qdig,
+                                                int32_t *__restrict__ qexp, int8_t *__restrict__ kdig,
+                                                uint8_t *__restrict__ ktab, int32_t *__restrict__ f64_heads) {
   constexpr int TPR = D / 8;      // threads per row, 8 entries each
   constexpr int RPB = 256 / TPR;  // rows per block
+  constexpr int KROWB = kDigits * D + 16;
+  __shared__ float s_shift;
+  __shared__ int s_zmin[2];
   const int h = blockIdx.y;
   const HeadDesc Dh = desc[h];
   const int tid = threadIdx.x, j = tid % TPR;
-  const int64_t r = int64_t(blockIdx.x) * RPB + tid / TPR;
-  const bool active = r < Dh.n + Dh.T;
-  const bool isq = r < Dh.n;
-  const int64_t row = isq ? Dh.q_off + r : Dh.k_off + (r - Dh.n);
+  const int64_t Tp = (Dh.T + 63) / 64 * 64;
+  const int64_t nR = (Dh.n + RPB - 1) / RPB * RPB;  // key rows start on a block boundary
+  const int64_t r0 = int64_t(blockIdx.x) * RPB;
+  if (r0 >= nR + Tp) return;
+  const bool kblock = r0 >= nR;
+  if (kblock) {  // the block holds key rows: the head's shift
+    if (tid < 2) s_zmin[tid] = 2;
+    if (tid < 64) {
+      float v = -INFINITY;
+      for (int64_t i = tid; i < Dh.n_sblk; i += 64) v = fmaxf(v, shift_part[Dh.sblk_off + i]);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
+      if (tid == 0) s_shift = v;
+    }
+    __syncthreads();
+  }
+  const int64_t r = r0 + tid / TPR;
+  const bool isq = !kblock;
+  const bool active = isq ? r < Dh.n : r < nR + Tp;
+  const int64_t key = r - nR;
+  const bool live = active && (isq || key < Dh.T);  // a row with data (not tile padding)
   u32x4 w = {0u, 0u, 0u, 0u};
-  if (active) w = *reinterpret_cast<const u32x4 *>((isq ? Q : K) + row * D + 8 * j);
+  if (live) w = *reinterpret_cast<const u32x4 *>((isq ? Q + (Dh.q_off + r) * D : K + (Dh.k_off + key) * D) + 8 * j);
   // x = M 2^P with M a signed integer (0 for zero)
   int32_t M[8], P[8];
   int emax = -100000, pmin = 100000;
@@ -822,57 +857,83 @@ __global__ __launch_bounds__(256) void k_digits(const HeadDesc *__restrict__ des
   }
   const int E = emax == -100000 ? 0 : emax;
   if (pmin < E - 37) bad = 1;
+  // low digits that are zero in every entry of the row (N a multiple of
+  // 2^(pmin + 37 - E)), counted up to 2
+  const int z = pmin == 100000 ? 2 : min(2, (pmin + 37 - E) >> 3);
   uint32_t dg[kDigits][2];
 #pragma unroll
-  for (int s = 0; s < kDigits; ++s) dg[s][0] = dg[s][1] = 0u;
+  for (int sd = 0; sd < kDigits; ++sd) dg[sd][0] = dg[sd][1] = 0u;
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int64_t N = (bad || M[i] == 0) ? 0 : int64_t(M[i]) * (int64_t(1) << (P[i] + 37 - E));
 #pragma unroll
-    for (int s = 0; s < kDigits; ++s) {
-      const int32_t d = int32_t(int8_t(uint8_t(uint64_t(N) & 0xffu)));
-      N = (N - d) >> 8;
-      dg[s][i >> 2] |= (uint32_t(d) & 0xffu) << (8 * (i & 3));
+    for (int sd = 0; sd < kDigits; ++sd) {
+      const int32_t dd = int32_t(int8_t(uint8_t(uint64_t(N) & 0xffu)));
+      N = (N - dd) >> 8;
+      dg[sd][i >> 2] |= (uint32_t(dd) & 0xffu) << (8 * (i & 3));
     }
   }
   if (active) {
-    int8_t *out = (isq ? qdig : kdig) + row * (kDigits * D) + 8 * j;
+    int8_t *out = isq ? qdig + (Dh.q_off + r) * (kDigits * D) : kdig + (Dh.kt_off + key) * KROWB;
 #pragma unroll
-    for (int s = 0; s < kDigits; ++s) *reinterpret_cast<u32x2 *>(out + s * D) = u32x2{dg[s][0], dg[s][1]};
+    for (int sd = 0; sd < kDigits; ++sd) *reinterpret_cast<u32x2 *>(out + sd * D + 8 * j) = u32x2{dg[sd][0], dg[sd][1]};
     if (j == 0) {
-      (isq ? qexp : kexp)[row] = E;
+      if (isq) {
+        qexp[Dh.q_off + r] = E * 4 + z;
+      } else {
+        const int kk = int(key & 63);
+        const int pos = store_pos(kk >> 4, kk & 3, (kk >> 2) & 3);
+        uint8_t *tb = ktab + ((Dh.kt_off + key) >> 6) * 1024;
+        double bms = -INFINITY;
+        if (key < Dh.T) bms = (beta_in ? double(beta_in[Dh.k_off + key]) : 0.0) - double(s_shift);
+        reinterpret_cast<double *>(tb)[pos] = bms;
+        reinterpret_cast<int32_t *>(tb + 512)[pos] = E;
+        atomicMin(&s_zmin[(tid / TPR) >> 4], z);
+      }
       if (bad) atomicOr(f64_heads + h, 1);
+    }
+  }
+  if (kblock) {
+    // per 16-key block: the low digits zero in all its keys
+    __syncthreads();
+    if (tid < RPB / 16) {
+      const int64_t k16 = r0 - nR + 16 * tid;
+      if (k16 < Tp)
+        reinterpret_cast<int32_t *>(ktab + ((Dh.kt_off + k16) >> 6) * 1024 + 768)[(k16 & 63) >> 4] = s_zmin[tid];
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Mass features for bf16 inputs with the logits on the int8 matrix units:
-// blocks, tiles, copies, Phi planes and Phi V as in k_phi16.  With the rows
-// in digit form (k_digits), the logit of query q and key k is
+// blocks, Phi planes and Phi V as in k_phi16.  With the rows in digit form
+// (k_digits), the logit of query q and key k is
 //   2^(E_q + E_k - 74) sum_c C_c 256^c,  C_c = sum over digit pairs s + t = c
 //   of the int32 dot products of Q digit s and K digit t,
 // each product on v_mfma_i32_16x16x64_i8 (exact: |C_c| < 2^24).  The nine C_c
-// are joined in float64 (one rounding per join) and the power of two and the
-// logit scale applied in one multiply, so the result is the float64 dot
-// product of the bf16 inputs to within a few roundings, as the float64 MFMA
-// gives it.  The K digits of a tile arrive by the same asynchronous copies
-// (KROW slots per key: five digit rows and a pad), the key exponents like
-// the biases.  MFMA row 4 g + e is fed key g + 4 e of its 16-key block, so
-// the outputs land where the float64 kernel has them.  Heads with
-// f64_heads[h] != 0 return at once (the float64 kernel takes them).
+// are joined in float64 (one rounding per join), and the power of two, the
+// logit scale, the bias and the shift applied in one fused multiply-add, so
+// the result is the float64 dot product of the bf16 inputs to within a few
+// roundings, as the float64 MFMA gives it.  Per 64-key tile three contiguous
+// asynchronous copies stage the K digit rows (KROW slots per key), the value
+// tile and the key table (bias - shift, -inf past T, so padding keys give 0
+// with no test; row exponents).  MFMA row 4 g + e is fed key g + 4 e of its
+// 16-key block, so the outputs land where the float64 kernel has them.  The
+// exps of a block are software-pipelined against the next block's MFMAs.
+// Heads with f64_heads[h] != 0 return at once (the float64 kernel takes
+// them).
 // ---------------------------------------------------------------------------
 template <int D, int STORE>
 __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
     const HeadDesc *__restrict__ desc, int H, int nqb, int xcd_map, const int8_t *__restrict__ qdig,
-    const int8_t *__restrict__ kdig, const int32_t *__restrict__ qexp, const int32_t *__restrict__ kexp,
-    const int32_t *__restrict__ f64_heads, const uint16_t *__restrict__ vt, const float *__restrict__ beta_in,
-    double scale, const float *__restrict__ shift_part, double *__restrict__ shift_out,
-    double *__restrict__ tr_shift, uint16_t *__restrict__ phi16, double *__restrict__ m_out,
-    double *__restrict__ r_out, float *__restrict__ Y_out, int32_t *__restrict__ head_status) {
+    const int32_t *__restrict__ qexp, const int8_t *__restrict__ kdig, const uint8_t *__restrict__ ktab,
+    const int32_t *__restrict__ f64_heads, const uint16_t *__restrict__ vt, double scale,
+    const float *__restrict__ shift_part, double *__restrict__ shift_out, double *__restrict__ tr_shift,
+    uint16_t *__restrict__ phi16, double *__restrict__ m_out, double *__restrict__ r_out, float *__restrict__ Y_out,
+    int32_t *__restrict__ head_status) {
   constexpr int NCH = D / 64;             // 64-dim k-steps of the int8 MFMA
   constexpr int DSL = kDigits * D / 16;   // 16-byte slots of one key's digits
-  constexpr int KROW = DSL + 1;           // slots per key row in LDS (one of padding)
+  constexpr int KROW = DSL + 1;           // slots per key row (one of padding)
   constexpr int KSLOT = 64 * KROW;        // slots per K tile
   constexpr int VSLOT = D * 9;            // slots per V tile
   constexpr int NU = D / 16;              // 16-dim output blocks of Phi V
@@ -882,11 +943,11 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
   static_assert(KSLOT % 64 == 0 && VSLOT % 64 == 0, "whole copies");
   __shared__ __attribute__((aligned(16))) uint32_t lk_all[2 * KWORDS];
   __shared__ __attribute__((aligned(16))) uint32_t lv_all[2 * VWORDS];
-  __shared__ __attribute__((aligned(16))) float sb[2][64];
-  __shared__ __attribute__((aligned(16))) int32_t se[2][64];
+  __shared__ __attribute__((aligned(16))) uint32_t lt_all[2 * 256];  // key tables
   __shared__ double s_tab[32];
   uint32_t *const lk0 = lk_all, *const lk1 = lk_all + KWORDS;
   uint32_t *const lv0 = lv_all, *const lv1 = lv_all + VWORDS;
+  uint32_t *const lt0 = lt_all, *const lt1 = lt_all + 256;
   __shared__ double s_shift;
 
   int h, qb;
@@ -918,8 +979,6 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
     if (tid == 0) s_shift = double(v);
   } else if (tid < 96) {
     s_tab[tid - 64] = kExp2Tab32[tid - 64];
-  } else if (!beta_in && tid < 96 + 128) {
-    sb[(tid - 96) >> 6][(tid - 96) & 63] = 0.0f;  // no biases: both buffers stay zero
   }
 
   // B operand: query q, digit s, dims 64 c + 16 g + (0..15) at k-step c
@@ -936,51 +995,40 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
       if (!qvalid) qd[sd][c] = u32x4{0u, 0u, 0u, 0u};
     }
   // scale 2^(E_q - 74): times 2^(E_k) per key, an exact power-of-two rescaling
-  const double qscale = ldexp(scale, qexp[qrow] - 74);
+  const int qx = qexp[qrow];
+  const double qscale = ldexp(scale, (qx >> 2) - 74);
+  // low Q digits zero in all 16 queries of the wave (0, 1 or 2: most waves
+  // have every entry within 14 binades of its row's largest, two)
+  int zq = qvalid ? (qx & 3) : 2;
+#pragma unroll
+  for (int off = 1; off < 16; off <<= 1) zq = min(zq, __shfl_xor(zq, off));
+  zq = __builtin_amdgcn_readfirstlane(zq);
 
-  const int64_t T = Dh.T;
-  const int ntiles = int((T + 63) / 64);
-  // Copies as in k_phi16; K rows are KROW slots (slot m < DSL of key k holds
-  // bytes 16 m.. of its digit row), the pad duplicates slot 0.  Biases (wave
-  // 0) and key exponents (wave 1) take one 4-byte copy each, slot i holding
-  // the key stored at position i.
-  const char *kbase = reinterpret_cast<const char *>(kdig + Dh.k_off * (kDigits * D));
+  const int ntiles = int((Dh.T + 63) / 64);
+  // Copies of tile `tile`: K digit rows, value tile and key table, each lying
+  // contiguously in global memory as it lies in LDS; copy i of a kind moves
+  // bytes 1024 i .. 1024 i + 1023 (lane l the 16 at 16 l), dealt to the waves
+  // in turn.
+  const char *kbase = reinterpret_cast<const char *>(kdig + Dh.kt_off * (kDigits * D + 16));
   const char *vbase = reinterpret_cast<const char *>(vt + Dh.vt_off);
-  const char *bbase = beta_in ? reinterpret_cast<const char *>(beta_in + Dh.k_off) : nullptr;
-  const char *ebase = reinterpret_cast<const char *>(kexp + Dh.k_off);
-  const int Ti = int(T);
-  auto issue = [&](int tile, uint32_t *lk, uint32_t *lv, float *lb, int32_t *le) {
-    const int k0 = tile * 64;
-    // the lane index, opaque to the compiler here: the per-copy offsets are
-    // recomputed for every tile rather than held in registers across the loop
-    int ln = lane;
-    asm volatile("" : "+v"(ln));
+  const char *tbase = reinterpret_cast<const char *>(ktab + (Dh.kt_off >> 6) * 1024);
+  auto issue = [&](int tile, uint32_t *lk, uint32_t *lv, uint32_t *lt) __attribute__((always_inline)) {
 #pragma unroll
     for (int inst = wave; inst < KSLOT / 64; inst += P16_WAVES) {
-      const int slot = inst * 64 + ln;
-      const int key = slot / KROW, m = slot % KROW;
-      const int row = k0 + key < Ti ? k0 + key : Ti - 1;
-      const uint32_t off = uint32_t(row * (kDigits * D) + 16 * (m < DSL ? m : 0));
+      const uint32_t off = uint32_t(tile * (KSLOT * 16) + inst * 1024 + lane * 16);
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(kbase + off),
                                        (void __attribute__((address_space(3))) *)(lk + inst * 256), 16, 0, 0);
     }
 #pragma unroll
     for (int inst = wave; inst < VSLOT / 64; inst += P16_WAVES) {
-      const int slot = inst * 64 + ln;
-      const int dim = slot / 9, lc = slot % 9;
-      const uint32_t off = uint32_t((tile * D + dim) * 64 + 8 * (lc < 8 ? lc : 0)) * 2u;
+      const uint32_t off = uint32_t(tile * (VSLOT * 16) + inst * 1024 + lane * 16);
       __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(vbase + off),
                                        (void __attribute__((address_space(3))) *)(lv + inst * 256), 16, 0, 0);
     }
-    if (wave < 2) {
-      const int key = k0 + 16 * (2 * (ln >> 5) + ((ln >> 2) & 1)) + ((ln >> 3) & 3) + 4 * (ln & 3);
-      const uint32_t off = uint32_t(key < Ti ? key : Ti - 1) * 4u;
-      if (wave == 0 && bbase)
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(bbase + off),
-                                         (void __attribute__((address_space(3))) *)lb, 4, 0, 0);
-      if (wave == 1)
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(ebase + off),
-                                         (void __attribute__((address_space(3))) *)le, 4, 0, 0);
+    if (wave == P16_WAVES - 1) {
+      const uint32_t off = uint32_t(tile * 1024 + lane * 16);
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(tbase + off),
+                                       (void __attribute__((address_space(3))) *)lt, 16, 0, 0);
     }
   };
 
@@ -991,12 +1039,18 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
   // MFMA row c16 of a 16-key block is fed key (c16 >> 2) + 4 (c16 & 3)
   const int krow = (c16 >> 2) + 4 * (c16 & 3);
 
-  auto compute = [&](int tile, const uint32_t *lk, const uint32_t *lv, const float *lb, const int32_t *le,
-                     bool next, uint32_t *nk, uint32_t *nv, float *nb, int32_t *ne, double s) {
+  // ZQ: Q digits below ZQ are zero for the whole wave and skipped; per 16-key
+  // block, K digits below its zk likewise.
+  auto compute = [&](auto zq_c, int tile, const uint32_t *lk, const uint32_t *lv, const uint32_t *lt, bool next,
+                     uint32_t *nk, uint32_t *nv, uint32_t *nt) __attribute__((always_inline)) {
+    constexpr int ZQ = decltype(zq_c)::value;
     const int64_t k0 = int64_t(tile) * 64;
-    if (next) issue(tile + 1, nk, nv, nb, ne);
+    if (next) issue(tile + 1, nk, nv, nt);
     const u32x4 *kl4 = reinterpret_cast<const u32x4 *>(lk) + (krow * KROW + g);
     const u32x4 *vl4 = reinterpret_cast<const u32x4 *>(lv) + (c16 * 9 + g);
+    const double *tbm = reinterpret_cast<const double *>(lt);
+    const int32_t *tke = reinterpret_cast<const int32_t *>(lt) + 128;
+    const int32_t *tzk = reinterpret_cast<const int32_t *>(lt) + 192;
     // Software pipeline over the four 16-key blocks: the exps of block kb - 1
     // are independent of the MFMAs of block kb, so the two interleave.
     float x[4][4];
@@ -1007,46 +1061,51 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
       if (kb < 4) {
 #pragma unroll
         for (int c = 0; c < NC; ++c) acc[c] = i32x4{0, 0, 0, 0};
+        const int zk = __builtin_amdgcn_readfirstlane(tzk[kb]);
 #pragma unroll
         for (int c = 0; c < NCH; ++c) {
-          u32x4 kd[kDigits];
 #pragma unroll
-          for (int t = 0; t < kDigits; ++t) kd[t] = kl4[kb * 16 * KROW + t * (D / 16) + 4 * c];
+          for (int t = 0; t < kDigits; ++t) {
+            if (t >= 2 || t >= zk) {
+              const u32x4 kd = kl4[kb * 16 * KROW + t * (D / 16) + 4 * c];
 #pragma unroll
-          for (int t = 0; t < kDigits; ++t)
-#pragma unroll
-            for (int sd = 0; sd < kDigits; ++sd)
-              acc[sd + t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, kd[t]),
-                                                                  __builtin_bit_cast(i32x4, qd[sd][c]), acc[sd + t],
-                                                                  0, 0, 0);
+              for (int sd = ZQ; sd < kDigits; ++sd)
+                acc[sd + t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, kd),
+                                                                    __builtin_bit_cast(i32x4, qd[sd][c]),
+                                                                    acc[sd + t], 0, 0, 0);
+            }
+          }
         }
       }
       if (kb > 0) {
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           const double p = exp_tang(arg[kb - 1][e], s_tab);
-          const double pm = int(k0) + phi_key(kb - 1, g, e) < Ti ? p : 0.0;
-          msum += pm;
-          x[kb - 1][e] = float(pm);
+          msum += p;
+          x[kb - 1][e] = float(p);
         }
       }
       if (kb < 4) {
-        const f32x4 bz = *reinterpret_cast<const f32x4 *>(lb + store_pos(kb, g, 0));
-        const i32x4 ke = *reinterpret_cast<const i32x4 *>(le + store_pos(kb, g, 0));
+        const int pos = store_pos(kb, g, 0);
+        const f64x2 bm0 = *reinterpret_cast<const f64x2 *>(tbm + pos);
+        const f64x2 bm1 = *reinterpret_cast<const f64x2 *>(tbm + pos + 2);
+        const i32x4 ke = *reinterpret_cast<const i32x4 *>(tke + pos);
+        const double bms[4] = {bm0[0], bm0[1], bm1[0], bm1[1]};
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
           // C_0 + 256 C_1 and C_7 + 256 C_8 stay within int32 (|C_0| <= 2^21,
           // |C_1| <= 2^22; the top digits are at most 64 in size, so
           // |C_7| < 2^21.1, |C_8| < 2^19.1); the rest join in float64
-          double v = double(acc[0][e] + (acc[1][e] << 8));
-          double w256 = 256.0;
+          // (classes below ZQ are zero)
+          double v = ZQ >= 2 ? double(acc[2][e]) : double((ZQ >= 1 ? 0 : acc[0][e]) + (acc[1][e] << 8));
+          double w256 = ZQ >= 2 ? 65536.0 : 256.0;
 #pragma unroll
-          for (int c = 2; c < NC - 2; ++c) {
+          for (int c = ZQ >= 2 ? 3 : 2; c < NC - 2; ++c) {
             w256 *= 256.0;
             v = fma(double(acc[c][e]), w256, v);
           }
           v = fma(double(acc[NC - 2][e] + (acc[NC - 1][e] << 8)), w256 * 256.0, v);
-          arg[kb][e] = v * ldexp(qscale, ke[e]) + double(bz[e]) - s;
+          arg[kb][e] = fma(v, ldexp(qscale, ke[e]), bms[e]);
         }
       }
     }
@@ -1105,21 +1164,27 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
     }
   };
 
-  issue(0, lk0, lv0, sb[0], se[0]);
+  issue(0, lk0, lv0, lt0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  const double s = s_shift;
   if (qb == 0 && tid == 0) {
-    shift_out[h] = s;
-    if (tr_shift) tr_shift[h] = s;
+    shift_out[h] = s_shift;
+    if (tr_shift) tr_shift[h] = s_shift;
   }
-  for (int tile = 0; tile < ntiles; tile += 2) {
-    compute(tile, lk0, lv0, sb[0], se[0], tile + 1 < ntiles, lk1, lv1, sb[1], se[1], s);
-    __syncthreads();
-    if (tile + 1 >= ntiles) break;
-    compute(tile + 1, lk1, lv1, sb[1], se[1], tile + 2 < ntiles, lk0, lv0, sb[0], se[0], s);
-    __syncthreads();
-  }
+  // waves of one block may take different variants; every path meets the
+  // same barriers
+  auto run = [&](auto zq_c) __attribute__((always_inline)) {
+    for (int tile = 0; tile < ntiles; tile += 2) {
+      compute(zq_c, tile, lk0, lv0, lt0, tile + 1 < ntiles, lk1, lv1, lt1);
+      __syncthreads();
+      if (tile + 1 >= ntiles) break;
+      compute(zq_c, tile + 1, lk1, lv1, lt1, tile + 2 < ntiles, lk0, lv0, lt0);
+      __syncthreads();
+    }
+  };
+  if (zq >= 2) run(std::integral_constant<int, 2>{});
+  else if (zq == 1) run(std::integral_constant<int, 1>{});
+  else run(std::integral_constant<int, 0>{});
 
   msum += __shfl_xor(msum, 16);
   msum += __shfl_xor(msum, 32);
@@ -1208,8 +1273,8 @@ static void launch_phi8(const Dims &dm, const Buffers &b, hipStream_t s) {
   const int nqb = int((dm.max_n + kPhi16Rows - 1) / kPhi16Rows);
   const int xcd_map = (dm.H % 8 == 0) ? 1 : 0;
   dim3 grid(unsigned(nqb * dm.H));
-#define AMC_PHI8_ARGS b.desc, dm.H, nqb, xcd_map, b.qdig, b.kdig, b.qexp, b.kexp, b.f64_heads, b.vt, b.beta_in, \
-    dm.scale, b.shift_part, b.shift, b.tr_shift, b.phi16, b.m, b.r, b.Y, b.head_status
+#define AMC_PHI8_ARGS b.desc, dm.H, nqb, xcd_map, b.qdig, b.qexp, b.kdig, b.ktab, b.f64_heads, b.vt, dm.scale, \
+    b.shift_part, b.shift, b.tr_shift, b.phi16, b.m, b.r, b.Y, b.head_status
   if (dm.d == 128)
     hipLaunchKernelGGL((k_phi8<128, STORE>), grid, dim3(kPhi16Rows * 4), 0, s, AMC_PHI8_ARGS);
   else
@@ -1252,15 +1317,17 @@ hipError_t launch_phi(const Dims &dm, const Buffers &b, int store, hipStream_t s
       hipError_t e = launch_fill_i32(b.f64_heads, dm.H, 0, s);
       if (e != hipSuccess) return e;
       constexpr int kRowsPerBlock128 = 256 / 16, kRowsPerBlock64 = 256 / 8;
-      const int64_t rows = dm.max_n + dm.max_T;
+      const int64_t rows = dm.max_n + 32 + (dm.max_T + 63) / 64 * 64;  // queries to a whole block, then keys
       const uint16_t *Q = static_cast<const uint16_t *>(b.Q);
       const uint16_t *K = static_cast<const uint16_t *>(b.K);
+#define AMC_DIGITS_ARGS b.desc, Q, K, b.beta_in, b.shift_part, b.qdig, b.qexp, b.kdig, b.ktab, b.f64_heads
       if (dm.d == 128)
         hipLaunchKernelGGL(k_digits<128>, dim3(unsigned((rows + kRowsPerBlock128 - 1) / kRowsPerBlock128), unsigned(dm.H)),
-                           dim3(256), 0, s, b.desc, Q, K, b.qdig, b.kdig, b.qexp, b.kexp, b.f64_heads);
+                           dim3(256), 0, s, AMC_DIGITS_ARGS);
       else
         hipLaunchKernelGGL(k_digits<64>, dim3(unsigned((rows + kRowsPerBlock64 - 1) / kRowsPerBlock64), unsigned(dm.H)),
-                           dim3(256), 0, s, b.desc, Q, K, b.qdig, b.kdig, b.qexp, b.kexp, b.f64_heads);
+                           dim3(256), 0, s, AMC_DIGITS_ARGS);
+#undef AMC_DIGITS_ARGS
       if (store == 2) {
         launch_phi8<2>(dm, b, s);
         launch_phi16<2>(dm, b, b.f64_heads, s);
