@@ -25,7 +25,7 @@ AMC_FLAG_TRACE = 1
 HS_CHOL_JITTER, HS_NNLS_CAP, HS_NONFINITE, HS_NNLS_SINGULAR = 1, 2, 4, 8
 
 KERNEL_CLASSES = ["init", "shift", "phi", "sweep", "merge", "panel", "gram", "nnls", "resid",
-                  "ols_normal", "ols_solve", "pack", "sweep_exact", "rescore"]
+                  "ols_normal", "ols_solve", "pack", "sweep_exact", "rescore", "prune"]
 
 EXPORTED = [
     "amc_default_options", "amc_workspace_size", "amc_output_offsets", "amc_cycle_offsets",

@@ -66,7 +66,8 @@ struct Plan {
            o_rhs = 0, o_cvsel = 0, o_pos = 0, o_cand_val = 0, o_cand_idx = 0, o_flist = 0, o_fcount = 0,
            o_dn = 0, o_L = 0, o_nnL = 0, o_nnP = 0, o_nnnp = 0, o_gA = 0, o_nnvec = 0, o_cand_lo = 0,
            o_cand_lidx = 0, o_cand_cnt = 0, o_band_list = 0, o_band_cnt = 0, o_exact = 0, o_stage = 0,
-           o_part = 0, o_vt = 0, o_qdig = 0, o_kdig = 0, o_qexp = 0, o_ktab = 0, o_f64h = 0, total = 0;
+           o_part = 0, o_vt = 0, o_qdig = 0, o_kdig = 0, o_qexp = 0, o_ktab = 0, o_f64h = 0, o_colsum = 0, o_rpn = 0, o_rabs = 0,
+           o_surv = 0, o_survcnt = 0, total = 0;
 };
 
 static amc_status check_problem(const amc_problem *p) {
@@ -129,6 +130,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     // rows of the stored Phi: float32 rows for the mass-feature entry point
     // (4-key segments), 16-bit planes for the selection (whole 64-key tiles)
     D.ldT = features_only ? (D.T + 3) / 4 * 4 : (D.T + 63) / 64 * 64;
+    D.ldN = (D.n + 63) / 64 * 64;
     D.vt_off = vt;
     D.kt_off = ktr;
     D.phi_off = phi;
@@ -147,7 +149,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
       if (D.n_cblk > kMaxSweepBlocks) return AMC_ERR_UNSUPPORTED;
     }
     const int64_t cycles = ceil_div(D.t, pl.kR);
-    phi += D.n * D.ldT;
+    phi += (features_only ? D.n : D.ldN) * D.ldT;
     vt += (D.T + 63) / 64 * 72 * d;
     ktr += (D.T + 63) / 64 * 64;
     nn += D.n;
@@ -169,13 +171,15 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   }
   dm.total_sblk = sblk;
   dm.max_qblk = ceil_div(dm.max_n, kRescoreRows);
+  dm.qb128 = ceil_div(dm.max_n, 128);
   pl.sum_t = tt;
   pl.sum_cycles = cyc;
   pl.sum_n = nn;
   pl.sum_T = TT;
   const uint64_t phi_bytes = uint64_t(phi) * 4;
   if (!features_only) {
-    pl.store_phi = phi_bytes <= o->phi_budget_bytes;  // else every sweep recomputes Phi
+    // else every sweep recomputes Phi
+    pl.store_phi = phi_bytes <= o->phi_budget_bytes && dm.max_n <= kStoredMaxN;
   }
 
   uint64_t off = 0;
@@ -217,14 +221,19 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.o_gA = take(8ull * tt);
   pl.o_nnvec = dm.max_t > kNnlsLdsT ? take(8ull * kNnlsVecPerSlot * tt) : 0;
   if (pl.store_phi) {  // bounded sweep, band and rescoring state
-    pl.o_cand_lo = take(8ull * cblk * (kMaxCycle + 1));
-    pl.o_cand_lidx = take(4ull * cblk * (kMaxCycle + 1));
-    pl.o_cand_cnt = take(4ull * cblk);
+    pl.o_cand_lo = take(8ull * ktr);   // sweep upper bounds
+    pl.o_cand_lidx = take(8ull * ktr); // sweep lower bounds
+    pl.o_cand_cnt = take(4ull * ktr);  // swept keys
     pl.o_band_list = take(4ull * H * kBandCap);
     pl.o_band_cnt = take(4ull * H);
     pl.o_exact = take(4ull * H);
     pl.o_stage = take(8ull * nn * kBandCap);
     pl.o_part = take(8ull * H * kBandCap * dm.max_qblk);
+    pl.o_colsum = take(4ull * ktr * dm.qb128);
+    pl.o_rpn = take(8ull * nn);
+    pl.o_rabs = take(8ull * H);
+    pl.o_surv = take(4ull * ktr);
+    pl.o_survcnt = take(4ull * H);
   }
   if (dm.in_bf16) {
     pl.o_vt = take(2ull * vt);  // transposed value tiles of the mass-feature kernel
@@ -293,6 +302,8 @@ static Buffers head_range(const Buffers &b, int h0, int64_t max_qblk) {
   if (b.exact) r.exact = b.exact + h0;
   if (b.part) r.part = b.part + int64_t(h0) * kBandCap * max_qblk;
   if (b.f64_heads) r.f64_heads = b.f64_heads + h0;
+  if (b.rabs) r.rabs = b.rabs + h0;
+  if (b.surv_cnt) r.surv_cnt = b.surv_cnt + h0;
   return r;
 }
 
@@ -462,14 +473,19 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   b.nn_vec = pl.dm.max_t > kNnlsLdsT ? reinterpret_cast<double *>(ws + pl.o_nnvec) : nullptr;
   b.gA = reinterpret_cast<double *>(ws + pl.o_gA);
   if (pl.store_phi) {
-    b.cand_lo = reinterpret_cast<double *>(ws + pl.o_cand_lo);
-    b.cand_lidx = reinterpret_cast<int32_t *>(ws + pl.o_cand_lidx);
-    b.cand_cnt = reinterpret_cast<int32_t *>(ws + pl.o_cand_cnt);
+    b.sw_up = reinterpret_cast<double *>(ws + pl.o_cand_lo);
+    b.sw_lo = reinterpret_cast<double *>(ws + pl.o_cand_lidx);
+    b.sw_key = reinterpret_cast<int32_t *>(ws + pl.o_cand_cnt);
     b.band_list = reinterpret_cast<int32_t *>(ws + pl.o_band_list);
     b.band_cnt = reinterpret_cast<int32_t *>(ws + pl.o_band_cnt);
     b.exact = reinterpret_cast<int32_t *>(ws + pl.o_exact);
     b.stage = reinterpret_cast<double *>(ws + pl.o_stage);
     b.part = reinterpret_cast<double *>(ws + pl.o_part);
+    b.colsum = reinterpret_cast<float *>(ws + pl.o_colsum);
+    b.rpn = reinterpret_cast<float *>(ws + pl.o_rpn);
+    b.rabs = reinterpret_cast<double *>(ws + pl.o_rabs);
+    b.surv_list = reinterpret_cast<int32_t *>(ws + pl.o_surv);
+    b.surv_cnt = reinterpret_cast<int32_t *>(ws + pl.o_survcnt);
   }
   b.head_status = head_status;
   if (tracing) {
@@ -542,6 +558,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
         if (pl.store_phi) {
           // bounded sweep and float64 rescoring of the band; the heads whose
           // band overflowed take the float32 sweep, merge and panel
+          AMC_LAUNCH(AMC_K_PRUNE, launch_prune(dg, bg, c, pl.kR, stream));
           AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_band(dg, bg, c, pl.kR, stream));
           AMC_LAUNCH(AMC_K_MERGE, launch_band_merge(dg, bg, c, pl.kR, stream));
           AMC_LAUNCH(AMC_K_SWEEP_EXACT, launch_sweep(dg, bg, c, pl.kR, 1, stream));

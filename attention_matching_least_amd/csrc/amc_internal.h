@@ -22,6 +22,7 @@ constexpr int kMaxBudget = 16384;  // largest budget per head (packed triangles 
 constexpr int kMaxSweepBlocks = 1024;  // sweep column blocks per head the merge handles
 constexpr int kBandCap = 128;    // candidates per head the float64 rescoring takes (more: exact sweep)
 constexpr int kRescoreRows = 256; // queries per block of the rescoring kernel
+constexpr int kStoredMaxN = 8192; // longest head (queries) the stored-Phi path takes
 
 // Per-head descriptor, computed on the host and copied to the device once per call.
 // All offsets are in elements of the array they index.
@@ -44,8 +45,9 @@ struct HeadDesc {
   int64_t tri_off;        // first element of the head's packed triangle (value-fit factor)
   int64_t vt_off;         // first element of the head's transposed value tiles (bf16 inputs)
   int64_t kt_off;         // first row of the head in the arrays of keys padded to whole 64-key tiles
+  int64_t ldN;            // stored planes: column stride (n rounded up to 64)
 };
-static_assert(sizeof(HeadDesc) == 19 * 8, "HeadDesc layout");
+static_assert(sizeof(HeadDesc) == 20 * 8, "HeadDesc layout");
 
 // Device pointers of the workspace carve-up and of the caller's buffers.
 struct Buffers {
@@ -55,8 +57,14 @@ struct Buffers {
   float *shift_part;   // [sum n_sblk]
   double *shift;       // [H]
   float *phi;          // [sum n*ldT] float32 Phi (the mass-feature entry point's output)
-  uint16_t *phi16;     // per head at 2*phi_off: high plane [n][ldT], then low plane [n][ldT];
-                       // within each 64-key tile, key 16 kb + g + 4 e sits at 32 (kb/2) + 8 g + 4 (kb%2) + e
+  uint16_t *phi16;     // per head at 2*phi_off: high plane [ldT keys][ldN queries], then low plane
+                       // [ldT][ldN] (key columns; queries from n to ldN and keys past T are zero)
+  float *colsum;       // per head at kt_off * qb128: [key][128-query block] sums of the high
+                       // plane, rounded down (written by the first sweep)
+  float *rpn;          // [sum n][2] float32 positive and negative parts of r (per cycle)
+  double *rabs;        // [H] sum |r| (per cycle)
+  int32_t *surv_list;  // per head at kt_off: keys the cycle's bounded sweep reads
+  int32_t *surv_cnt;   // [H] their number, -1: every key
   uint16_t *vt;        // bf16 inputs: per head at vt_off, [T/64 tiles][d][72] values, key-permuted
                        // (64 per row and a pad of 8, the layout the mass-feature kernels stage)
   int8_t *qdig;        // bf16 inputs: rows of Q as five base-256 digit rows ([rows][5][d]); null:
@@ -89,9 +97,8 @@ struct Buffers {
   double *nn_vec;      // [sum t][kNnlsVecPerSlot] NNLS vectors of heads above kNnlsLdsT (else null)
   double *cand_val;    // [sum n_cblk][kMaxCycle + 1]  block top-(kR+1) scores, or band upper bounds
   int32_t *cand_idx;   // [sum n_cblk][kMaxCycle + 1]
-  double *cand_lo;     // [sum n_cblk][kMaxCycle + 1]  block top-(kR+1) lower bounds (sorted)
-  int32_t *cand_lidx;  // [sum n_cblk][kMaxCycle + 1]
-  int32_t *cand_cnt;   // [sum n_cblk]  band entries of the block (-1: non-finite bound)
+  double *sw_up, *sw_lo;  // per head at kt_off: bounded-sweep bounds of the listed keys, in list order
+  int32_t *sw_key;     // per head at kt_off: the listed keys
   int32_t *band_list;  // [H][kBandCap] key indices of the head's candidate band
   int32_t *band_cnt;   // [H]
   int32_t *exact;      // [H] 1: the head's band overflowed; this cycle takes the exact sweep
@@ -110,6 +117,7 @@ struct Dims {
   int64_t max_n, max_T, max_t, min_t;
   int64_t max_sblk, max_cblk, max_qblk;
   int band_cap;        // largest band the rescoring takes (<= kBandCap)
+  int64_t qb128;       // 128-query blocks of the longest head (column sums per key)
   int64_t total_sblk;
 };
 
@@ -135,6 +143,8 @@ hipError_t launch_vt(const Dims &dm, const Buffers &b, hipStream_t s);
 hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int gated, hipStream_t s);
 hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_sweep_band(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+// per cycle of the stored-Phi selection: r's parts and the keys the bounded sweep reads
+hipError_t launch_prune(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_band_merge(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_rescore(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_choose(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);

@@ -162,6 +162,25 @@ __device__ __forceinline__ int phi_key(int kb, int g, int e) { return kb * 16 + 
 // values a lane holds for one query are then two runs of 8 positions, and the
 // four lanes of a query write 64 contiguous bytes of a plane per store.
 __device__ __forceinline__ int store_pos(int kb, int g, int e) { return 32 * (kb >> 1) + 8 * g + 4 * (kb & 1) + e; }
+// Stored planes are key columns: the high and low 16 bits of the float32 Phi
+// of key k and query q at k * ldN + q of the head's high and low plane.  A
+// lane's 16 values of one tile (keys k0 + 16 kb + g + 4 e, query q) leave as
+// 16-bit stores; the 16 lanes of one g write 32 contiguous bytes of a column.
+// Queries from n to ldN get zeros (the caller passes x = 0 for them).
+__device__ __forceinline__ void store_planes(uint16_t *hp, uint16_t *lp, int64_t ldN, int64_t k0, int g, int64_t q,
+                                             const float (&x)[4][4]) {
+  const uint32_t lane_off = uint32_t((int64_t(g) * ldN + q) * 2);
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t col = (k0 + 16 * kb + 4 * e) * ldN;
+      const uint32_t u = __float_as_uint(x[kb][e]);
+      *reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(hp + col) + lane_off) = uint16_t(u >> 16);
+      *reinterpret_cast<uint16_t *>(reinterpret_cast<char *>(lp + col) + lane_off) = uint16_t(u & 0xffffu);
+    }
+}
+
 // The Phi V product consumes those values as its A operand at k-step (kb, e)
 // (A[query][k = g]); its B operand B[k = g][dim] is then V[phi_key(kb, g, e)][dim],
 // a row of the V tile, read directly.
@@ -262,7 +281,7 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
         msum += p;
         pf[kb][e] = float(p);
         if constexpr (STORE == 1) ps[wave][c16 * PSTR + kl] = pf[kb][e];
-        if constexpr (STORE == 2) ps[wave][c16 * PSTR + store_pos(kb, g, e)] = pf[kb][e];
+        if constexpr (STORE == 2) ps[wave][c16 * PSTR + kl] = qvalid ? pf[kb][e] : 0.0f;
       }
     }
     if constexpr (STORE == 1) {
@@ -281,37 +300,27 @@ __global__ __launch_bounds__(256) void k_phi(const HeadDesc *__restrict__ desc, 
         }
       }
     } else if constexpr (STORE == 2) {
-      // 8 stored positions of one row per lane: their high halves leave as
-      // one 16-byte segment of the high plane, their low halves as one of the
-      // low plane (ldT is a multiple of 64: whole tiles)
+      // lane l takes key k0 + l: the wave's 16 queries of its column leave as
+      // 32 contiguous bytes of each plane (ldN is a multiple of 64, so the
+      // wave's 16 queries lie all below it or all above)
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-      uint16_t *hp = phi16 + 2 * Dh.phi_off;
-      uint16_t *lp = hp + Dh.n * Dh.ldT;
+      if (q0 < Dh.ldN) {
+        uint16_t *hp = phi16 + 2 * Dh.phi_off + (k0 + lane) * Dh.ldN + q0;
+        uint16_t *lp = hp + Dh.ldT * Dh.ldN;
+        uint32_t hw[8], lw[8];
 #pragma unroll
-      for (int it = 0; it < 2; ++it) {
-        const int row = (lane >> 3) + 8 * it, col = 8 * (lane & 7);
-        const int64_t qr = q0 + row;
-        if (qr < Dh.n && k0 + col < Dh.ldT) {
-          const f32x4 a = *reinterpret_cast<const f32x4 *>(&ps[wave][row * PSTR + col]);
-          const f32x4 c = *reinterpret_cast<const f32x4 *>(&ps[wave][row * PSTR + col + 4]);
-          const uint32_t u[8] = {__float_as_uint(a.x), __float_as_uint(a.y), __float_as_uint(a.z),
-                                 __float_as_uint(a.w), __float_as_uint(c.x), __float_as_uint(c.y),
-                                 __float_as_uint(c.z), __float_as_uint(c.w)};
-          u32x4 hv, lv;
-          hv.x = (u[0] >> 16) | (u[1] & 0xffff0000u);
-          hv.y = (u[2] >> 16) | (u[3] & 0xffff0000u);
-          hv.z = (u[4] >> 16) | (u[5] & 0xffff0000u);
-          hv.w = (u[6] >> 16) | (u[7] & 0xffff0000u);
-          lv.x = (u[0] & 0xffffu) | (u[1] << 16);
-          lv.y = (u[2] & 0xffffu) | (u[3] << 16);
-          lv.z = (u[4] & 0xffffu) | (u[5] << 16);
-          lv.w = (u[6] & 0xffffu) | (u[7] << 16);
-          const int64_t at = qr * Dh.ldT + k0 + col;
-          __builtin_nontemporal_store(hv, reinterpret_cast<u32x4 *>(hp + at));
-          __builtin_nontemporal_store(lv, reinterpret_cast<u32x4 *>(lp + at));
+        for (int i = 0; i < 8; ++i) {
+          const uint32_t u0 = __float_as_uint(ps[wave][(2 * i) * PSTR + lane]);
+          const uint32_t u1 = __float_as_uint(ps[wave][(2 * i + 1) * PSTR + lane]);
+          hw[i] = (u0 >> 16) | (u1 & 0xffff0000u);
+          lw[i] = (u0 & 0xffffu) | (u1 << 16);
         }
+        *reinterpret_cast<u32x4 *>(hp) = u32x4{hw[0], hw[1], hw[2], hw[3]};
+        *reinterpret_cast<u32x4 *>(hp + 8) = u32x4{hw[4], hw[5], hw[6], hw[7]};
+        *reinterpret_cast<u32x4 *>(lp) = u32x4{lw[0], lw[1], lw[2], lw[3]};
+        *reinterpret_cast<u32x4 *>(lp + 8) = u32x4{lw[4], lw[5], lw[6], lw[7]};
       }
     }
     if constexpr (BF16) {
@@ -629,23 +638,14 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
     // the next tile's copies have landed
     __builtin_amdgcn_s_waitcnt(0);
     if constexpr (STORE == 2) {
-      if (qvalid) {
-        // positions 8 g + (0..7) and 32 + 8 g + (0..7): one 16-byte segment each, per plane
+      if (q < Dh.ldN) {
         uint16_t *hp = phi16 + 2 * Dh.phi_off;
-        uint16_t *lp = hp + Dh.n * Dh.ldT;
-        uint32_t hw[8], lw[8];
+        float xs[4][4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t u0 = __float_as_uint(x[i >> 1][2 * (i & 1)]);
-          const uint32_t u1 = __float_as_uint(x[i >> 1][2 * (i & 1) + 1]);
-          hw[i] = (u0 >> 16) | (u1 & 0xffff0000u);
-          lw[i] = (u0 & 0xffffu) | (u1 << 16);
-        }
-        const int64_t at = q * Dh.ldT + k0 + 8 * g;
-        __builtin_nontemporal_store(u32x4{hw[0], hw[1], hw[2], hw[3]}, reinterpret_cast<u32x4 *>(hp + at));
-        __builtin_nontemporal_store(u32x4{hw[4], hw[5], hw[6], hw[7]}, reinterpret_cast<u32x4 *>(hp + at + 32));
-        __builtin_nontemporal_store(u32x4{lw[0], lw[1], lw[2], lw[3]}, reinterpret_cast<u32x4 *>(lp + at));
-        __builtin_nontemporal_store(u32x4{lw[4], lw[5], lw[6], lw[7]}, reinterpret_cast<u32x4 *>(lp + at + 32));
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xs[kb][e] = qvalid ? x[kb][e] : 0.0f;
+        store_planes(hp, hp + Dh.ldT * Dh.ldN, Dh.ldN, k0, g, q, xs);
       }
     }
     // Phi V: reduction index k = 8 g + 4 j + e of chunk c is key phi_key(2 c + j, g, e)
@@ -1112,22 +1112,14 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
     // the next tile's copies have landed
     __builtin_amdgcn_s_waitcnt(0);
     if constexpr (STORE == 2) {
-      if (qvalid) {
+      if (q < Dh.ldN) {
         uint16_t *hp = phi16 + 2 * Dh.phi_off;
-        uint16_t *lp = hp + Dh.n * Dh.ldT;
-        uint32_t hw[8], lw[8];
+        float xs[4][4];
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const uint32_t u0 = __float_as_uint(x[i >> 1][2 * (i & 1)]);
-          const uint32_t u1 = __float_as_uint(x[i >> 1][2 * (i & 1) + 1]);
-          hw[i] = (u0 >> 16) | (u1 & 0xffff0000u);
-          lw[i] = (u0 & 0xffffu) | (u1 << 16);
-        }
-        const int64_t at = q * Dh.ldT + k0 + 8 * g;
-        __builtin_nontemporal_store(u32x4{hw[0], hw[1], hw[2], hw[3]}, reinterpret_cast<u32x4 *>(hp + at));
-        __builtin_nontemporal_store(u32x4{hw[4], hw[5], hw[6], hw[7]}, reinterpret_cast<u32x4 *>(hp + at + 32));
-        __builtin_nontemporal_store(u32x4{lw[0], lw[1], lw[2], lw[3]}, reinterpret_cast<u32x4 *>(lp + at));
-        __builtin_nontemporal_store(u32x4{lw[4], lw[5], lw[6], lw[7]}, reinterpret_cast<u32x4 *>(lp + at + 32));
+        for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) xs[kb][e] = qvalid ? x[kb][e] : 0.0f;
+        store_planes(hp, hp + Dh.ldT * Dh.ldN, Dh.ldN, k0, g, q, xs);
       }
     }
 #pragma unroll

@@ -65,15 +65,6 @@ __device__ void block_sort256(double *v, int *ix) {
   }
 }
 
-// Stored Phi planes keep each 64-key tile in the order the mass-feature
-// kernel writes it: position 32 (kb / 2) + 8 g + 4 (kb % 2) + e holds key
-// 16 kb + g + 4 e.
-__device__ __forceinline__ int64_t key_at(int64_t pos) {
-  const int p = int(pos & 63);
-  const int kb = 2 * (p >> 5) + ((p >> 2) & 1), g = (p >> 3) & 3, e = p & 3;
-  return (pos & ~int64_t(63)) + 16 * kb + g + 4 * e;
-}
-
 __device__ __forceinline__ int cycle_keys(const HeadDesc &D, int cycle, int kR, int64_t *S0) {
   const int64_t s0 = int64_t(cycle) * kR;
   *S0 = s0;
@@ -83,9 +74,13 @@ __device__ __forceinline__ int cycle_keys(const HeadDesc &D, int cycle, int kR, 
 }
 
 // ---------------------------------------------------------------------------
-// sweep over the float32 Phi, rebuilt exactly from its two 16-bit planes: one
-// block = 256 columns of one head, 4 waves split the rows.  gate: only the
-// heads with gate[h] != 0.
+// Stored Phi is two 16-bit planes of key columns (high and low halves of the
+// float32 values, key k at k * ldN; queries from n to ldN are zero).  The
+// sweeps read whole columns: a wave takes 8 keys at a time, 8 lanes per key,
+// lane `sub` of a key reading queries 64 i + 8 sub .. 64 i + 8 sub + 7 (one
+// 16-byte load per plane) for i = 0 .. ldN / 64 - 1, so each load
+// instruction moves 8 full 128-byte lines.  r (or its float32 parts) is staged
+// in LDS per block; the partial sums of a key meet across its 8 lanes.
 // ---------------------------------------------------------------------------
 __device__ __forceinline__ f32x4 join_planes(u32x2 hv, u32x2 lv) {
   f32x4 x;
@@ -96,12 +91,36 @@ __device__ __forceinline__ f32x4 join_planes(u32x2 hv, u32x2 lv) {
   return x;
 }
 
+// float64 v moved across lanes by a DPP pattern (CTRL) within rows of 16
+template <int CTRL>
+__device__ __forceinline__ double dpp_f64(double v) {
+  const int64_t b = __double_as_longlong(v);
+  const int lo = __builtin_amdgcn_update_dpp(0, int(uint32_t(b)), CTRL, 0xf, 0xf, false);
+  const int hi = __builtin_amdgcn_update_dpp(0, int(uint32_t(uint64_t(b) >> 32)), CTRL, 0xf, 0xf, false);
+  return __longlong_as_double(int64_t((uint64_t(uint32_t(hi)) << 32) | uint32_t(lo)));
+}
+
+// sum over each aligned group of 8 lanes, in every lane of the group: swap
+// neighbours, swap pairs (quad permutations), then each half of the group
+// with the other (the half-row mirror pairs lane i with 7 - i)
+__device__ __forceinline__ double sum8_lanes(double v) {
+  v += dpp_f64<0xB1>(v);   // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(v);   // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(v);  // row_half_mirror
+  return v;
+}
+
+// ---------------------------------------------------------------------------
+// exact sweep over the float32 Phi rebuilt from both planes, float64 sums:
+// one block = 256 keys of one head (4 waves x 8 rounds of 8 keys).  gate:
+// only the heads with gate[h] != 0.
+// ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc, const uint16_t *__restrict__ phi16,
                                                const double *__restrict__ r, const int32_t *__restrict__ sel_slot,
                                                int cycle, int kR, const int32_t *__restrict__ gate,
                                                double *__restrict__ cand_val,
                                                int32_t *__restrict__ cand_idx, int32_t *__restrict__ head_status) {
-  __shared__ double red[4][256];
+  __shared__ double s_r[kStoredMaxN];
   __shared__ double sv[256];
   __shared__ int si[256];
   const int h = blockIdx.y;
@@ -114,52 +133,45 @@ __global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc
   if (gate && gate[h] == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int64_t j0 = int64_t(blk) * kSweepCols + 4 * lane;  // stored position
-  double a0 = 0.0, a1 = 0.0, a2 = 0.0, a3 = 0.0;
-  if (j0 < D.ldT) {  // ldT is a multiple of 64: the 8-byte segments lie within the row
-    const uint16_t *ph = phi16 + 2 * D.phi_off + j0;
-    const uint16_t *pl = ph + D.n * D.ldT;
-    const double *rr = r + D.n_off;
-    const int64_t ld = D.ldT;
-    int64_t i = wave;
-    for (; i + 28 < D.n; i += 32) {
-      f32x4 x[8];
-      double rv[8];
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        const int64_t at = (i + 4 * u) * ld;
-        x[u] = join_planes(__builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(ph + at)),
-                           __builtin_nontemporal_load(reinterpret_cast<const u32x2 *>(pl + at)));
-        rv[u] = rr[i + 4 * u];
-      }
-#pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        a0 = fma(rv[u], double(x[u].x), a0);
-        a1 = fma(rv[u], double(x[u].y), a1);
-        a2 = fma(rv[u], double(x[u].z), a2);
-        a3 = fma(rv[u], double(x[u].w), a3);
-      }
-    }
-    for (; i < D.n; i += 4) {
-      const f32x4 x = join_planes(*reinterpret_cast<const u32x2 *>(ph + i * ld),
-                                  *reinterpret_cast<const u32x2 *>(pl + i * ld));
-      const double rv = rr[i];
-      a0 = fma(rv, double(x.x), a0);
-      a1 = fma(rv, double(x.y), a1);
-      a2 = fma(rv, double(x.z), a2);
-      a3 = fma(rv, double(x.w), a3);
-    }
-  }
-  red[wave][4 * lane + 0] = a0;
-  red[wave][4 * lane + 1] = a1;
-  red[wave][4 * lane + 2] = a2;
-  red[wave][4 * lane + 3] = a3;
+  const int kq = lane >> 3, sub = lane & 7;
+  for (int64_t q = tid; q < D.ldN; q += 256) s_r[q] = q < D.n ? r[D.n_off + q] : 0.0;
   __syncthreads();
-  const int64_t pos = int64_t(blk) * kSweepCols + tid;
-  const int64_t col = key_at(pos);
-  double c = ((red[0][tid] + red[1][tid]) + red[2][tid]) + red[3][tid];
+  const uint16_t *hp0 = phi16 + 2 * D.phi_off;
+  const uint16_t *lp0 = hp0 + D.ldT * D.ldN;
+  const int nit = int(D.ldN >> 6);
+  for (int round = 0; round < 8; ++round) {
+    const int slot = 64 * wave + 8 * round + kq;
+    const int64_t key = int64_t(blk) * kSweepCols + slot;  // < ldT: a stored (possibly zero) column
+    const uint16_t *hp = hp0 + key * D.ldN + 8 * sub;
+    const uint16_t *lp = lp0 + key * D.ldN + 8 * sub;
+    double a[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
+    if (key < D.ldT) {
+#pragma unroll 4
+      for (int i = 0; i < nit; ++i) {
+        const u32x4 hv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 64 * i));
+        const u32x4 lv = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(lp + 64 * i));
+        const f32x4 x0 = join_planes(u32x2{hv.x, hv.y}, u32x2{lv.x, lv.y});
+        const f32x4 x1 = join_planes(u32x2{hv.z, hv.w}, u32x2{lv.z, lv.w});
+        const double *rr = s_r + 64 * i + 8 * sub;
+        a[0] = fma(rr[0], double(x0.x), a[0]);
+        a[1] = fma(rr[1], double(x0.y), a[1]);
+        a[2] = fma(rr[2], double(x0.z), a[2]);
+        a[3] = fma(rr[3], double(x0.w), a[3]);
+        a[4] = fma(rr[4], double(x1.x), a[4]);
+        a[5] = fma(rr[5], double(x1.y), a[5]);
+        a[6] = fma(rr[6], double(x1.z), a[6]);
+        a[7] = fma(rr[7], double(x1.w), a[7]);
+      }
+    }
+    const double c = sum8_lanes(((a[0] + a[1]) + (a[2] + a[3])) + ((a[4] + a[5]) + (a[6] + a[7])));
+    if (sub == 0) sv[slot] = c;
+  }
+  __syncthreads();
+  const int64_t col = int64_t(blk) * kSweepCols + tid;
+  double c = sv[tid];
   int idx = int(col);
-  if (pos >= D.ldT || col >= D.T || sel_slot[D.k_off + col] != 0) {
+  __syncthreads();
+  if (col >= D.T || sel_slot[D.k_off + col] != 0) {
     c = -INFINITY;
     idx = INT_MAX;
   } else if (!isfinite(c)) {
@@ -461,151 +473,366 @@ __global__ __launch_bounds__(256) void k_merge(const HeadDesc *__restrict__ desc
 // so with P_j = sum_{r_i > 0} r_i h_ij and N_j = sum_{r_i < 0} r_i h_ij,
 //   P_j + N_j + 2^-7 N_j - e_j <= r^T Phi[:, j] <= P_j + N_j + 2^-7 P_j + e_j,
 // where e_j covers the float32 accumulation of P and N (same-sign sums, so a
-// relative error of (terms per lane + 2) 2^-24 each), the float32 rounding of
-// Phi and of r, the float64 rescoring's own rounding, and an absolute term for
-// values below float32's normal range.  One block = 256 keys: each lane takes
-// 8 keys of every 8th row (16-byte loads), P and N accumulate in float32 per
-// lane and in float64 across the 8 row streams; each column is a stored
-// position, mapped to its key at the end.  Out: the block's top-(Kc+1)
-// lower bounds, sorted (cand_lo / cand_lidx), and in key order every key whose
-// upper bound reaches the (Kc+1)-th of them (cand_val = upper bound,
-// cand_idx, cand_cnt = their number, -1 if a bound is not finite).
+// relative error of (terms per accumulator + 2) 2^-24 each), the float32
+// rounding of Phi and of r, the float64 rescoring's own rounding, and an
+// absolute term for values below float32's normal range.  Each lane keeps 8
+// float32 accumulators per sign (one per query of its 16-byte loads: ldN / 64
+// terms each); a key's 8 lanes meet in float64.
+// The keys: every key on the first cycle (which also writes each key's
+// high-plane sums over 128-query blocks, rounded down, for the pruning), else
+// the cycle's survivor list (or every key when the list is off).  One block =
+// 32 of them (4 waves of 8), so that a short list still spreads over the
+// chip.  Out, per listed key: its upper and lower bound (sw_up, sw_lo; -inf
+// for a selected key) and the key (sw_key), at its place in the list.
 // ---------------------------------------------------------------------------
-__device__ __forceinline__ void band_accum(const u32x4 &x, double rv, float (&P)[8], float (&N)[8], double &ra) {
-  const float rp = float(fmax(rv, 0.0)), rn = float(fmin(rv, 0.0));
-  ra += fabs(rv);  // NaN in r reaches the bounds through this sum
-  const uint32_t w[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const float v0 = __uint_as_float(w[c] << 16);
-    const float v1 = __uint_as_float(w[c] & 0xffff0000u);
-    P[2 * c] = fmaf(rp, v0, P[2 * c]);
-    N[2 * c] = fmaf(rn, v0, N[2 * c]);
-    P[2 * c + 1] = fmaf(rp, v1, P[2 * c + 1]);
-    N[2 * c + 1] = fmaf(rn, v1, N[2 * c + 1]);
-  }
-}
+constexpr int SB_KEYS = 32;  // keys per block of the bounded sweep
 
+template <bool FIRST>
 __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__ desc,
-                                                    const uint16_t *__restrict__ phi16, const double *__restrict__ r,
+                                                    const uint16_t *__restrict__ phi16, const float *__restrict__ rpn,
+                                                    const double *__restrict__ rabs,
+                                                    const int32_t *__restrict__ surv_list,
+                                                    const int32_t *__restrict__ surv_cnt,
                                                     const int32_t *__restrict__ sel_slot, int cycle, int kR,
-                                                    double *__restrict__ cand_val, int32_t *__restrict__ cand_idx,
-                                                    int32_t *__restrict__ cand_cnt, double *__restrict__ cand_lo,
-                                                    int32_t *__restrict__ cand_lidx) {
-  __shared__ __attribute__((aligned(16))) float ps_p[8][256];
-  __shared__ __attribute__((aligned(16))) float ps_n[8][256];
-  __shared__ double ra_s[8];
-  __shared__ double sv[256];
-  __shared__ int si[256];
-  __shared__ int wcnt[4];
+                                                    int64_t qb128, float *__restrict__ colsum,
+                                                    double *__restrict__ sw_up, double *__restrict__ sw_lo,
+                                                    int32_t *__restrict__ sw_key) {
+  extern __shared__ __attribute__((aligned(16))) float s_rpn[];  // (r+, r-) per query, ldN of them
   const int h = blockIdx.y;
   const HeadDesc D = desc[h];
   const int blk = blockIdx.x;
-  if (blk >= D.n_cblk) return;
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0) return;
+  const int list = FIRST ? -1 : surv_cnt[h];
+  const int64_t cnt = list < 0 ? D.T : list;
+  if (int64_t(blk) * SB_KEYS >= cnt) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = lane >> 3, sub = lane & 7;
+  for (int64_t q = tid; q < D.ldN; q += 256) {
+    float2 v = make_float2(0.0f, 0.0f);
+    if (q < D.n) v = *reinterpret_cast<const float2 *>(rpn + 2 * (D.n_off + q));
+    *reinterpret_cast<float2 *>(s_rpn + 2 * q) = v;
+  }
+  __syncthreads();
+  const int64_t at = int64_t(blk) * SB_KEYS + 8 * wave + kq;
+  int64_t key = -1;
+  if (at < cnt) key = list < 0 ? at : int64_t(surv_list[D.kt_off + at]);
+  const uint16_t *hp = phi16 + 2 * D.phi_off + (key < 0 ? 0 : key) * D.ldN + 8 * sub;
+  const int nit = int(D.ldN >> 6);
+  float P[8], N[8];
+#pragma unroll
+  for (int e = 0; e < 8; ++e) P[e] = N[e] = 0.0f;
+  auto step = [&](int i, const u32x4 &xv) __attribute__((always_inline)) {
+    const f32x4 *rr = reinterpret_cast<const f32x4 *>(s_rpn + 2 * (64 * i + 8 * sub));
+    const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      const f32x4 pr = rr[c];  // (r+, r-) of queries 2 c and 2 c + 1
+      const float v0 = __uint_as_float(w[c] << 16);
+      const float v1 = __uint_as_float(w[c] & 0xffff0000u);
+      P[2 * c] = fmaf(pr.x, v0, P[2 * c]);
+      N[2 * c] = fmaf(pr.y, v0, N[2 * c]);
+      P[2 * c + 1] = fmaf(pr.z, v1, P[2 * c + 1]);
+      N[2 * c + 1] = fmaf(pr.w, v1, N[2 * c + 1]);
+    }
+  };
+  // FIRST: the high-plane sum of 128-query block b from this lane's 16 values
+  // of it (two loads).  The float32 lane sums of 16 positive terms are within
+  // 2^-20 of exact: scaled down by that much and rounded down, the stored sum
+  // is at most the exact one and at least (1 - 2^-18.9) of it.
+  auto hsum = [&](const u32x4 &a, const u32x4 &b) __attribute__((always_inline)) {
+    float t = 0.0f;
+    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+    for (int c = 0; c < 8; ++c) t += __uint_as_float(w[c] << 16) + __uint_as_float(w[c] & 0xffff0000u);
+    return t;
+  };
+  auto put_sum = [&](int blk128, float t) __attribute__((always_inline)) {
+    const double bs = sum8_lanes(double(t));
+    if (sub == 0) colsum[(D.kt_off + key) * qb128 + blk128] = __double2float_rd(bs * (1.0 - 0x1p-20));
+  };
+  if (key >= 0) {
+    // sixteen 16-byte loads in flight per lane
+    int i = 0;
+    for (; i + 16 <= nit; i += 16) {
+      u32x4 xv[16];
+#pragma unroll
+      for (int u = 0; u < 16; ++u) xv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 64 * (i + u)));
+      __builtin_amdgcn_sched_barrier(0);  // all sixteen issue before any is used
+#pragma unroll
+      for (int u = 0; u < 16; ++u) step(i + u, xv[u]);
+      if constexpr (FIRST) {
+#pragma unroll
+        for (int u = 0; u < 16; u += 2) put_sum((i + u) >> 1, hsum(xv[u], xv[u + 1]));
+      }
+    }
+    for (; i < nit; i += 2) {
+      const u32x4 x0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 64 * i));
+      const u32x4 x1 = i + 1 < nit ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 64 * (i + 1)))
+                                   : u32x4{0u, 0u, 0u, 0u};
+      step(i, x0);
+      if (i + 1 < nit) step(i + 1, x1);
+      if constexpr (FIRST) put_sum(i >> 1, hsum(x0, x1));
+    }
+  }
+  double Pd = 0.0, Nd = 0.0;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    Pd += double(P[e]);
+    Nd += double(N[e]);
+  }
+  Pd = sum8_lanes(Pd);
+  Nd = sum8_lanes(Nd);
+  if (sub == 0 && key >= 0) {
+    const bool valid = key < D.T && sel_slot[D.k_off + key] == 0;
+    const double rs = rabs[h];
+    const double crel = 2.0 * (double(nit) + 16.0) * 0x1p-24 + 0x1p-22;
+    const double slack = crel * (Pd - Nd) + (rs + double(D.n)) * 0x1p-120;
+    const double c7 = 0x1.00001p-7;
+    sw_up[D.kt_off + at] = valid ? (Pd + Nd) + c7 * Pd + slack : -INFINITY;
+    sw_lo[D.kt_off + at] = valid ? (Pd + Nd) + c7 * Nd - slack : -INFINITY;
+    sw_key[D.kt_off + at] = int(key);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Pruning for the bounded sweep, one block of 1024 threads per head.  With
+// H_Bk the high-plane sum of key k over the 128-query block B (written by the
+// first cycle's sweep, rounded down to within 2^-18 of the sum) and rmax_B the
+// largest r_q in B,
+//   r^T Phi[:, k] = sum_B sum_{q in B} r_q Phi_qk <= sum_B rmax_B M_Bk = U_k,
+// M_Bk bounding sum_{q in B} Phi_qk from above where rmax_B >= 0 and from
+// below where it is negative (H_Bk scaled by (1 + 2^-7)(1 + 2^-18), resp.
+// by 1 - 2^-23: the plane truncates, float32 rounds), plus a float64 rounding
+// allowance.  Each thread's best key by U over its share; the 64 best of
+// those are scored from both planes (the float32 Phi, float64 sums) and bounded
+// below by that score less the float32 rounding of Phi and the sum's own:
+// L = the (Kc+1)-th best of those lower bounds is at most the (Kc+1)-th best
+// score, so no key with U_k < L is among this cycle's top Kc+1 and the sweep
+// skips it.
+// Also writes r's float32 positive and negative parts and sum |r| for the
+// sweep.  The first cycle (no sums yet), a non-finite r, Kc + 1 > 64 and
+// heads longer than the list's LDS keep every key (surv_cnt = -1).
+// ---------------------------------------------------------------------------
+constexpr int PR_THREADS = 1024;
+constexpr int PR_CAND = 64;
+constexpr int PR_MAXT = 16384;  // keys whose U stays in LDS
+
+__device__ void block_sort1024(double *v, int *ix) {
+  const int tid = threadIdx.x;
+  for (int k = 2; k <= 1024; k <<= 1) {
+    for (int j = k >> 1; j > 0; j >>= 1) {
+      const int p = tid ^ j;
+      if (p > tid) {
+        const double va = v[tid], vb = v[p];
+        const int ia = ix[tid], ib = ix[p];
+        if (better(va, ia, vb, ib) != ((tid & k) == 0)) {
+          v[tid] = vb;
+          v[p] = va;
+          ix[tid] = ib;
+          ix[p] = ia;
+        }
+      }
+      __syncthreads();
+    }
+  }
+}
+
+__global__ __launch_bounds__(PR_THREADS) void k_prune(const HeadDesc *__restrict__ desc,
+                                                      const double *__restrict__ r,
+                                                      const int32_t *__restrict__ sel_slot,
+                                                      const uint16_t *__restrict__ phi16,
+                                                      const float *__restrict__ colsum, int64_t qb128, int cycle,
+                                                      int kR, float *__restrict__ rpn, double *__restrict__ rabs,
+                                                      int32_t *__restrict__ surv_list,
+                                                      int32_t *__restrict__ surv_cnt) {
+  __shared__ double s_r[kStoredMaxN];
+  __shared__ float s_u[PR_MAXT];
+  __shared__ double s_wmax[kStoredMaxN / 64];
+  __shared__ double s_rmax[kStoredMaxN / 128];
+  __shared__ double s_cv[PR_THREADS];
+  __shared__ int s_ci[PR_THREADS];
+  __shared__ double s_part[PR_THREADS / 64];
+  __shared__ double s_lo[PR_CAND];
+  __shared__ int s_wc[PR_THREADS / 64];
+  __shared__ double s_L;
+  const int h = blockIdx.x;
+  const HeadDesc D = desc[h];
   int64_t S0;
   const int Kc = cycle_keys(D, cycle, kR, &S0);
   if (Kc == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int cg = lane & 31;
-  const int stream = 2 * wave + (lane >> 5);  // rows stream, stream + 8, ...
-  const int64_t j0 = int64_t(blk) * kSweepCols + 8 * cg;
-  float P[8], N[8];
-#pragma unroll
-  for (int k = 0; k < 8; ++k) P[k] = N[k] = 0.0f;
+  // r's parts, sum |r|, and the largest r of every 64 queries
   double ra = 0.0;
-  if (j0 < D.ldT) {  // ldT is a multiple of 64: the 16-byte segment lies within the row
-    const uint16_t *p = phi16 + 2 * D.phi_off + j0;
-    const double *rr = r + D.n_off;
-    const int64_t ld = D.ldT;
-    int64_t i = stream;
-    for (; i + 56 < D.n; i += 64) {
-      u32x4 x[8];
-      double rv[8];
+  for (int64_t q0 = 0; q0 < D.ldN; q0 += PR_THREADS) {
+    const int64_t q = q0 + tid;
+    double rv = 0.0, rm = -INFINITY;
+    if (q < D.n) {
+      rv = r[D.n_off + q];
+      rm = rv;
+      *reinterpret_cast<float2 *>(rpn + 2 * (D.n_off + q)) = make_float2(float(fmax(rv, 0.0)), float(fmin(rv, 0.0)));
+    }
+    if (q < D.ldN) s_r[q] = rv;
+    ra += fabs(rv);
 #pragma unroll
-      for (int u = 0; u < 8; ++u) {
-        x[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p + (i + 8 * u) * ld));
-        rv[u] = rr[i + 8 * u];
+    for (int off = 32; off >= 1; off >>= 1) rm = fmax(rm, __shfl_xor(rm, off));
+    if (lane == 0 && q < D.ldN) s_wmax[q >> 6] = rm;
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ra += __shfl_xor(ra, off);
+  if (lane == 0) s_part[wave] = ra;
+  __syncthreads();
+  if (tid == 0) {
+    double t = 0.0;
+    for (int w = 0; w < PR_THREADS / 64; ++w) t += s_part[w];
+    rabs[h] = t;
+    s_L = t;
+  }
+  const int nb = int((D.n + 127) >> 7);
+  if (tid < nb) s_rmax[tid] = fmax(s_wmax[2 * tid], 2 * tid + 1 < (D.ldN >> 6) ? s_wmax[2 * tid + 1] : -INFINITY);
+  __syncthreads();
+  const bool keep_all = cycle == 0 || !isfinite(s_L) || Kc + 1 > PR_CAND || D.T > PR_MAXT;
+  if (keep_all) {
+    if (tid == 0) surv_cnt[h] = -1;
+    return;
+  }
+  // U for every key (-inf for selected keys), each thread's best
+  const double kup = (1.0 + 0x1p-7) * (1.0 + 0x1p-18) + 0x1p-40;  // the plane truncates; the sums round down
+  const double kdn = 1.0 - 0x1p-23;
+  double bv = -INFINITY;
+  int bi = INT_MAX;
+  for (int64_t k = tid; k < D.T; k += PR_THREADS) {
+    double u = -INFINITY;
+    if (sel_slot[D.k_off + k] == 0) {
+      const float *cs = colsum + (D.kt_off + k) * qb128;
+      double s = 0.0, a = 0.0;
+      for (int b = 0; b < nb; ++b) {
+        const double rm = s_rmax[b];
+        const double c = double(cs[b]);
+        const double t = rm * (rm >= 0.0 ? c * kup : c * kdn);
+        s += t;
+        a += fabs(t);
+      }
+      u = s + a * double(nb + 2) * 0x1p-50;
+      if (better(u, int(k), bv, bi)) {
+        bv = u;
+        bi = int(k);
+      }
+    }
+    if (u != u) u = INFINITY;  // a NaN bound keeps the key
+    s_u[k] = __double2float_ru(u);  // rounded up: the stored value bounds u
+  }
+  s_cv[tid] = bv;
+  s_ci[tid] = bi;
+  __syncthreads();
+  block_sort1024(s_cv, s_ci);
+  // lower bounds of the PR_CAND best candidates (4 per wave) from the float32 Phi
+  const uint16_t *hp0 = phi16 + 2 * D.phi_off;
+  const uint16_t *lp0 = hp0 + D.ldT * D.ldN;
+  for (int cnd = wave; cnd < PR_CAND; cnd += PR_THREADS / 64) {
+    const int key = s_ci[cnd];
+    double lo = -INFINITY;
+    if (key != INT_MAX) {
+      const uint16_t *hp = hp0 + int64_t(key) * D.ldN;
+      const uint16_t *lp = lp0 + int64_t(key) * D.ldN;
+      double sc = 0.0, ab = 0.0;
+      for (int64_t q = 8 * lane; q < D.ldN; q += 512) {
+        const u32x4 hv = *reinterpret_cast<const u32x4 *>(hp + q);
+        const u32x4 lv = *reinterpret_cast<const u32x4 *>(lp + q);
+        const f32x4 x0 = join_planes(u32x2{hv.x, hv.y}, u32x2{lv.x, lv.y});
+        const f32x4 x1 = join_planes(u32x2{hv.z, hv.w}, u32x2{lv.z, lv.w});
+        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const double t = s_r[q + e] * double(xs[e]);
+          sc += t;
+          ab += fabs(t);
+        }
       }
 #pragma unroll
-      for (int u = 0; u < 8; ++u) band_accum(x[u], rv[u], P, N, ra);
+      for (int off = 32; off >= 1; off >>= 1) {
+        sc += __shfl_xor(sc, off);
+        ab += __shfl_xor(ab, off);
+      }
+      // |Phi - x| <= 2^-24 (1 + 2^-23) x, float64 products and sums within n 2^-52 of ab
+      lo = sc - ab * (0x1p-24 + 0x1p-46 + double(D.ldN) * 0x1p-52) - (s_L + double(D.n)) * 0x1p-120;
+      if (!isfinite(lo)) lo = -INFINITY;
     }
-    for (; i < D.n; i += 8) band_accum(*reinterpret_cast<const u32x4 *>(p + i * ld), rr[i], P, N, ra);
+    if (lane == 0) s_lo[cnd] = lo;
   }
-  *reinterpret_cast<float4 *>(&ps_p[stream][8 * cg]) = make_float4(P[0], P[1], P[2], P[3]);
-  *reinterpret_cast<float4 *>(&ps_p[stream][8 * cg + 4]) = make_float4(P[4], P[5], P[6], P[7]);
-  *reinterpret_cast<float4 *>(&ps_n[stream][8 * cg]) = make_float4(N[0], N[1], N[2], N[3]);
-  *reinterpret_cast<float4 *>(&ps_n[stream][8 * cg + 4]) = make_float4(N[4], N[5], N[6], N[7]);
-  if (cg == 0) ra_s[stream] = ra;  // lane cg = 0 always reads (block start < T <= ldT)
   __syncthreads();
-  const int64_t pos = int64_t(blk) * kSweepCols + tid;  // stored position of this thread's key
-  const int64_t col = key_at(pos);
-  double Pd = 0.0, Nd = 0.0, rs = 0.0;
-#pragma unroll
-  for (int st = 0; st < 8; ++st) {
-    Pd += double(ps_p[st][tid]);
-    Nd += double(ps_n[st][tid]);
-    rs += ra_s[st];
+  if (wave == 0) {
+    // L: the (Kc+1)-th best lower bound (ranks by value, then candidate slot)
+    const double v = s_lo[lane];
+    int rank = 0;
+    for (int j = 0; j < PR_CAND; ++j) {
+      const double o = s_lo[j];
+      rank += (o > v || (o == v && j < lane)) ? 1 : 0;
+    }
+    if (rank == Kc) s_L = v;
   }
-  const bool valid = pos < D.ldT && col < D.T && sel_slot[D.k_off + col] == 0;
-  const double crel = 2.0 * (double(D.n) * 0.125 + 16.0) * 0x1p-24 + 0x1p-22;
-  const double slack = crel * (Pd - Nd) + (rs + double(D.n)) * 0x1p-120;
-  const double c7 = 0x1.00001p-7;
-  const double up = (Pd + Nd) + c7 * Pd + slack;
-  const double lo = (Pd + Nd) + c7 * Nd - slack;
-  const bool bad = valid && !(isfinite(up) && isfinite(lo));
-  sv[tid] = valid ? lo : -INFINITY;
-  si[tid] = valid ? int(col) : INT_MAX;
-  const int any_bad = __syncthreads_or(int(bad));
-  block_sort256(sv, si);
-  const double Lb = sv[Kc];
-  const int64_t o = (D.cblk_off + blk) * KP_STRIDE;
-  if (tid <= Kc) {
-    cand_lo[o + tid] = sv[tid];
-    cand_lidx[o + tid] = si[tid];
-  }
-  const bool take = valid && up >= Lb;
-  const uint64_t m = __ballot(take);
-  if (lane == 0) wcnt[wave] = __popcll(m);
   __syncthreads();
-  int base = 0;
-  for (int w = 0; w < wave; ++w) base += wcnt[w];
-  if (take) {
-    const int at = base + __popcll(m & ((uint64_t(1) << lane) - 1));
-    cand_val[o + at] = up;
-    cand_idx[o + at] = int(col);
+  const double L = s_L;
+  // survivors: unselected keys with U >= L, in key order
+  int total = 0;
+  for (int64_t k0 = 0; k0 < D.T; k0 += PR_THREADS) {
+    const int64_t k = k0 + tid;
+    const bool take = k < D.T && double(s_u[k]) >= L;
+    const uint64_t m = __ballot(take);
+    if (lane == 0) s_wc[wave] = __popcll(m);
+    __syncthreads();
+    int at = total;
+    for (int w = 0; w < wave; ++w) at += s_wc[w];
+    at += __popcll(m & ((uint64_t(1) << lane) - 1));
+    if (take) surv_list[D.kt_off + at] = int(k);
+    for (int w = 0; w < PR_THREADS / 64; ++w) total += s_wc[w];
+    __syncthreads();
   }
-  if (tid == 0) cand_cnt[D.cblk_off + blk] = any_bad ? -1 : wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+  if (tid == 0) surv_cnt[h] = total;
 }
 
 // ---------------------------------------------------------------------------
-// band merge: one block per head.  L = the (Kc+1)-th best lower bound over
-// all blocks (the tournament over the blocks' sorted lists); the band is every
-// key whose upper bound reaches L, in block and key order.  It holds the true
-// top Kc+1: each of those scores at least L, and its upper bound at least its
-// score.  exact[h] = 1 when the band overflows kBandCap (or a bound was not
-// finite): the head takes the float32 sweep this cycle.  band_cap <= kBandCap
-// (lower only to exercise the exact path).
+// band merge: one block of 1024 threads per head.  L = the (Kc+1)-th best
+// lower bound over the swept keys, found by radix selection on the bounds'
+// order-preserving 64-bit images (8 passes of 8 bits); the band is every key
+// whose upper bound reaches L, in list order.  It holds the true top Kc+1:
+// each of those scores at least L, and its upper bound at least its score.
+// exact[h] = 1 when the band overflows band_cap (<= kBandCap; lower only to
+// exercise the exact path), holds fewer than Kc keys, or a bound of an
+// unselected key is not finite: the head takes the float32 sweep this cycle.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void k_band_merge(const HeadDesc *__restrict__ desc, int cycle, int kR,
-                                                    const double *__restrict__ cand_val,
-                                                    const int32_t *__restrict__ cand_idx,
-                                                    const int32_t *__restrict__ cand_cnt,
-                                                    const double *__restrict__ cand_lo,
-                                                    const int32_t *__restrict__ cand_lidx,
-                                                    int band_cap, int32_t *__restrict__ band_list,
-                                                    int32_t *__restrict__ band_cnt, int32_t *__restrict__ exact) {
-  __shared__ double s_L;
-  __shared__ int wcnt[4];
+__device__ __forceinline__ uint64_t order_key(double v) {
+  const uint64_t b = __double_as_longlong(v);
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__global__ __launch_bounds__(1024) void k_band_merge(const HeadDesc *__restrict__ desc, int cycle, int kR,
+                                                     const double *__restrict__ sw_up,
+                                                     const double *__restrict__ sw_lo,
+                                                     const int32_t *__restrict__ sw_key,
+                                                     const int32_t *__restrict__ surv_cnt, int band_cap,
+                                                     int32_t *__restrict__ band_list, int32_t *__restrict__ band_cnt,
+                                                     int32_t *__restrict__ exact) {
+  __shared__ int hist[256];
+  __shared__ int s_wc[16];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_need;
   const int h = blockIdx.x;
   const HeadDesc D = desc[h];
   int64_t S0;
   const int Kc = cycle_keys(D, cycle, kR, &S0);
   if (Kc == 0) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int nl = int(D.n_cblk);
+  const int sc = surv_cnt[h];
+  const int64_t cnt = sc < 0 ? D.T : sc;
+  const double *up = sw_up + D.kt_off;
+  const double *lo = sw_lo + D.kt_off;
   int bad = 0;
-  for (int l = tid; l < nl; l += 256) bad |= cand_cnt[D.cblk_off + l] < 0;
+  for (int64_t e = tid; e < cnt; e += 1024)
+    bad |= (lo[e] != -INFINITY || up[e] != -INFINITY) && !(isfinite(up[e]) && isfinite(lo[e]));
   if (__syncthreads_or(bad)) {
     if (tid == 0) {
       band_cnt[h] = 0;
@@ -613,34 +840,52 @@ __global__ __launch_bounds__(256) void k_band_merge(const HeadDesc *__restrict__
     }
     return;
   }
-  double *Lp = &s_L;
-  tournament(cand_lo, cand_lidx, D.cblk_off, nl, Kc, [&](int rank, double v, int ix) {
-    if (rank == Kc) *Lp = ix != INT_MAX ? v : -INFINITY;
-  });
-  const double L = s_L;
+  // radix selection of the (Kc+1)-th largest order key among the lower bounds
+  if (tid == 0) {
+    s_prefix = 0;
+    s_need = Kc + 1;
+  }
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    const uint64_t prefix = s_prefix;
+    const uint64_t pmask = pass == 0 ? 0ull : (~0ull << (shift + 8));
+    for (int64_t e = tid; e < cnt; e += 1024) {
+      const uint64_t k = order_key(lo[e]);
+      if ((k & pmask) == prefix) atomicAdd(&hist[int((k >> shift) & 255u)], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int need = s_need, d = 255;
+      for (; d > 0; --d) {
+        if (hist[d] >= need) break;
+        need -= hist[d];
+      }
+      s_need = need;
+      s_prefix = prefix | (uint64_t(d) << shift);
+    }
+    __syncthreads();
+  }
+  // (with fewer than Kc + 1 keys the selection runs off the bottom: L = -inf,
+  // the band is every unselected key)
+  const uint64_t kL = s_prefix;
+  double L = __longlong_as_double(int64_t((kL >> 63) ? (kL & 0x7fffffffffffffffull) : ~kL));
+  if (L != L) L = -INFINITY;
   int total = 0;
   int32_t *out = band_list + int64_t(h) * kBandCap;
-  for (int l = 0; l < nl; ++l) {
-    const int64_t o = (D.cblk_off + l) * KP_STRIDE;
-    const int cnt = cand_cnt[D.cblk_off + l];
-    for (int e0 = 0; e0 < cnt; e0 += 256) {
-      const int e = e0 + tid;
-      bool take = false;
-      int ix = 0;
-      if (e < cnt) {
-        ix = cand_idx[o + e];
-        take = ix != INT_MAX && cand_val[o + e] >= L;
-      }
-      const uint64_t m = __ballot(take);
-      if (lane == 0) wcnt[wave] = __popcll(m);
-      __syncthreads();
-      int at = total;
-      for (int w = 0; w < wave; ++w) at += wcnt[w];
-      at += __popcll(m & ((uint64_t(1) << lane) - 1));
-      if (take && at < kBandCap) out[at] = ix;
-      total += wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
-      __syncthreads();
-    }
+  for (int64_t e0 = 0; e0 < cnt; e0 += 1024) {
+    const int64_t e = e0 + tid;
+    const bool take = e < cnt && up[e] != -INFINITY && up[e] >= L;
+    const uint64_t m = __ballot(take);
+    if (lane == 0) s_wc[wave] = __popcll(m);
+    __syncthreads();
+    int at = total;
+    for (int w = 0; w < wave; ++w) at += s_wc[w];
+    at += __popcll(m & ((uint64_t(1) << lane) - 1));
+    if (take && at < kBandCap) out[at] = sw_key[D.kt_off + e];
+    for (int w = 0; w < 16; ++w) total += s_wc[w];
+    __syncthreads();
   }
   if (tid == 0) {
     band_cnt[h] = total;
@@ -1051,14 +1296,25 @@ hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int kR, 
 }
 
 hipError_t launch_sweep_band(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
-  hipLaunchKernelGGL(k_sweep_band, dim3(unsigned(dm.max_cblk), unsigned(dm.H)), dim3(256), 0, s, b.desc, b.phi16,
-                     b.r, b.sel_slot, cycle, kR, b.cand_val, b.cand_idx, b.cand_cnt, b.cand_lo, b.cand_lidx);
+  const dim3 grid(unsigned((dm.max_T + SB_KEYS - 1) / SB_KEYS), unsigned(dm.H));
+  const size_t lds = size_t((dm.max_n + 63) / 64 * 64) * 8;
+#define AMC_SB_ARGS b.desc, b.phi16, b.rpn, b.rabs, b.surv_list, b.surv_cnt, b.sel_slot, cycle, kR, dm.qb128, b.colsum, \
+    b.sw_up, b.sw_lo, b.sw_key
+  if (cycle == 0) hipLaunchKernelGGL(k_sweep_band<true>, grid, dim3(256), lds, s, AMC_SB_ARGS);
+  else hipLaunchKernelGGL(k_sweep_band<false>, grid, dim3(256), lds, s, AMC_SB_ARGS);
+#undef AMC_SB_ARGS
+  return hipGetLastError();
+}
+
+hipError_t launch_prune(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  hipLaunchKernelGGL(k_prune, dim3(unsigned(dm.H)), dim3(PR_THREADS), 0, s, b.desc, b.r, b.sel_slot, b.phi16, b.colsum,
+                     dm.qb128, cycle, kR, b.rpn, b.rabs, b.surv_list, b.surv_cnt);
   return hipGetLastError();
 }
 
 hipError_t launch_band_merge(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
-  hipLaunchKernelGGL(k_band_merge, dim3(unsigned(dm.H)), dim3(256), 0, s, b.desc, cycle, kR, b.cand_val, b.cand_idx,
-                     b.cand_cnt, b.cand_lo, b.cand_lidx, dm.band_cap, b.band_list, b.band_cnt, b.exact);
+  hipLaunchKernelGGL(k_band_merge, dim3(unsigned(dm.H)), dim3(1024), 0, s, b.desc, cycle, kR, b.sw_up, b.sw_lo,
+                     b.sw_key, b.surv_cnt, dm.band_cap, b.band_list, b.band_cnt, b.exact);
   return hipGetLastError();
 }
 

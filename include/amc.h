@@ -96,7 +96,8 @@ typedef enum {
   AMC_K_PACK = 11,   /* sorted, packed outputs */
   AMC_K_SWEEP_EXACT = 12, /* float32 sweep of the heads whose candidate band overflowed */
   AMC_K_RESCORE = 13, /* float64 scores and columns of the band's candidates */
-  AMC_NUM_KERNEL_CLASSES = 14
+  AMC_K_PRUNE = 14,   /* per-cycle bound that drops keys from the bounded sweep */
+  AMC_NUM_KERNEL_CLASSES = 15
 } amc_kernel_class;
 
 typedef struct {
