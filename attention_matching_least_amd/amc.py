@@ -25,7 +25,7 @@ AMC_FLAG_TRACE = 1
 HS_CHOL_JITTER, HS_NNLS_CAP, HS_NONFINITE, HS_NNLS_SINGULAR = 1, 2, 4, 8
 
 KERNEL_CLASSES = ["init", "shift", "phi", "sweep", "merge", "panel", "gram", "nnls", "resid",
-                  "ols_normal", "ols_solve", "pack", "sweep_exact", "rescore", "prune"]
+                  "ols_normal", "ols_solve", "pack", "sweep_exact", "rescore", "prune", "digits", "phi_f64"]
 
 EXPORTED = [
     "amc_default_options", "amc_workspace_size", "amc_output_offsets", "amc_cycle_offsets",
@@ -71,7 +71,8 @@ class Options(ctypes.Structure):
 
 class TraceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in
-                ("shift", "pick", "pick_score", "weight", "runner_up", "nnls_iters", "total_bytes")]
+                ("shift", "pick", "pick_score", "weight", "runner_up", "nnls_iters", "swept_keys",
+                 "total_bytes")]
 
 
 _lib = None
@@ -308,6 +309,7 @@ class CompactResult:
         weight = sec(L.weight, np.float64, st)
         runner = sec(L.runner_up, np.float64, sc)
         iters = sec(L.nnls_iters, np.int32, sc)
+        swept = sec(L.swept_keys, np.int32, sc)
         cb, cc = self.cu_budgets, self.cu_cycles
         return {
             "shift": shift,
@@ -316,6 +318,7 @@ class CompactResult:
             "weight": [weight[cb[h]:cb[h + 1]] for h in range(H)],
             "runner_up": [runner[cc[h]:cc[h + 1]] for h in range(H)],
             "nnls_iters": [iters[cc[h]:cc[h + 1]] for h in range(H)],
+            "swept_keys": [swept[cc[h]:cc[h + 1]] for h in range(H)],
         }
 
 

@@ -242,7 +242,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     pl.o_qexp = take(4ull * nn);
     pl.o_kdig = take((5ull * d + 16) * ktr);
     pl.o_ktab = take(16ull * ktr);
-    pl.o_f64h = take(4ull * H);
+    pl.o_f64h = take(4ull * 3 * H);  // flags, the list of flagged heads, its length (per head group)
   }
   pl.total = off;
   return AMC_OK;
@@ -261,6 +261,7 @@ static void trace_layout(const Plan &pl, amc_trace_layout *L) {
   L->weight = take(8ull * pl.sum_t);
   L->runner_up = take(8ull * pl.sum_cycles);
   L->nnls_iters = take(4ull * pl.sum_cycles);
+  L->swept_keys = take(4ull * pl.sum_cycles);
   L->total_bytes = off;
 }
 
@@ -301,7 +302,11 @@ static Buffers head_range(const Buffers &b, int h0, int64_t max_qblk) {
   if (b.band_cnt) r.band_cnt = b.band_cnt + h0;
   if (b.exact) r.exact = b.exact + h0;
   if (b.part) r.part = b.part + int64_t(h0) * kBandCap * max_qblk;
-  if (b.f64_heads) r.f64_heads = b.f64_heads + h0;
+  if (b.f64_heads) {
+    r.f64_heads = b.f64_heads + h0;
+    r.f64_list = b.f64_list + h0;  // a group's list holds its own heads (group-relative numbers)
+    r.f64_cnt = b.f64_cnt + h0;
+  }
   if (b.rabs) r.rabs = b.rabs + h0;
   if (b.surv_cnt) r.surv_cnt = b.surv_cnt + h0;
   return r;
@@ -447,6 +452,8 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
     b.kdig = reinterpret_cast<int8_t *>(ws + pl.o_kdig);
     b.ktab = reinterpret_cast<uint8_t *>(ws + pl.o_ktab);
     b.f64_heads = reinterpret_cast<int32_t *>(ws + pl.o_f64h);
+    b.f64_list = b.f64_heads + pl.dm.H;
+    b.f64_cnt = b.f64_heads + 2 * pl.dm.H;
   }
   b.m = reinterpret_cast<double *>(ws + pl.o_m);
   b.r = reinterpret_cast<double *>(ws + pl.o_r);
@@ -496,6 +503,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
     b.tr_weight = reinterpret_cast<double *>(tr + tl.weight);
     b.tr_runner = reinterpret_cast<double *>(tr + tl.runner_up);
     b.tr_iters = reinterpret_cast<int32_t *>(tr + tl.nnls_iters);
+    b.tr_swept = reinterpret_cast<int32_t *>(tr + tl.swept_keys);
   }
   NnlsParams np{0, o->nnls_max_iters, o->nnls_tol};
   pl.dm.band_cap = band_cap_setting();
@@ -506,6 +514,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
                               : hipErrorLaunchFailure));
   AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.sel_slot, pl.sum_T, 0, stream));
   if (head_status) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(head_status, dm.H, 0, stream));
+  if (b.tr_swept && !pl.store_phi) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.tr_swept, pl.sum_cycles, 0, stream));
 
   // The heads run in groups, each on a stream of its own (the caller's for the
   // first), joined back to the caller's stream by events: the groups' mass
@@ -552,7 +561,9 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
       if (g > 0 && hipStreamWaitEvent(stream, ev_phi[size_t(g - 1)], 0) != hipSuccess) return AMC_ERR_HIP;
       AMC_LAUNCH(AMC_K_SHIFT, launch_shift(dg, bg, stream));
       if (bg.vt) AMC_LAUNCH(AMC_K_INIT, launch_vt(dg, bg, stream));
+      if (bg.qdig) AMC_LAUNCH(AMC_K_DIGITS, launch_digits(dg, bg, stream));
       AMC_LAUNCH(AMC_K_PHI, launch_phi(dg, bg, pl.store_phi ? 2 : 0, stream));
+      if (bg.qdig) AMC_LAUNCH(AMC_K_PHI_F64, launch_phi_fallback(dg, bg, pl.store_phi ? 2 : 0, stream));
       if (ngroups > 1 && hipEventRecord(ev_phi[size_t(g)], stream) != hipSuccess) return AMC_ERR_HIP;
       for (int c = 0; c < cycles; ++c) {
         if (pl.store_phi) {

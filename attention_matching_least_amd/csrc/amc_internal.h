@@ -75,6 +75,8 @@ struct Buffers {
   uint8_t *ktab;       // per head at kt_off / 64: per 64-key tile 1 KiB, float64 (bias - shift)
                        // of each key (-inf past T), then its int32 row exponent, in stored order
   int32_t *f64_heads;  // [H] 1: a row of the head is not exact in digit form (float64 logits)
+  int32_t *f64_list;   // [H] those heads, listed per launch (a group's from its first entry)
+  int32_t *f64_cnt;    // [H] the list's length, at the launch's first head
   double *m, *r, *mhat;  // [sum n]
   float *Y;            // [sum n][d]
   int32_t *sel_slot;   // [sum T]  0 = unselected, else 1 + slot
@@ -107,7 +109,7 @@ struct Buffers {
   int32_t *head_status;  // [H] or null
   // trace (all null when tracing is off)
   double *tr_shift, *tr_pick_score, *tr_weight, *tr_runner;
-  int32_t *tr_pick, *tr_iters;
+  int32_t *tr_pick, *tr_iters, *tr_swept;
 };
 
 struct Dims {
@@ -139,6 +141,10 @@ hipError_t launch_shift(const Dims &dm, const Buffers &b, hipStream_t s);
 // bf16 inputs with b.vt set (store 0 or 2) take the tiled kernel, after launch_vt.
 hipError_t launch_phi(const Dims &dm, const Buffers &b, int store, hipStream_t s);
 hipError_t launch_vt(const Dims &dm, const Buffers &b, hipStream_t s);
+// bf16 inputs with b.qdig set: the digit form of the rows, before launch_phi; after it, the
+// float64 kernel over the heads off the digit grid
+hipError_t launch_digits(const Dims &dm, const Buffers &b, hipStream_t s);
+hipError_t launch_phi_fallback(const Dims &dm, const Buffers &b, int store, hipStream_t s);
 // gated: only the heads with b.exact[h] != 0 (else every head)
 hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int gated, hipStream_t s);
 hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);

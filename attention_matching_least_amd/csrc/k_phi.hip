@@ -478,13 +478,12 @@ __global__ __launch_bounds__(256) void k_vt(const HeadDesc *__restrict__ desc, c
 constexpr int P16_WAVES = kPhi16Rows / 16;
 
 template <int D, int STORE>
-__global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
-    const HeadDesc *__restrict__ desc, int H, int nqb, int xcd_map, const uint16_t *__restrict__ Q,
+__device__ __forceinline__ void phi16_block(
+    int h, int qb, const HeadDesc *__restrict__ desc, const uint16_t *__restrict__ Q,
     const uint16_t *__restrict__ K, const uint16_t *__restrict__ vt, const float *__restrict__ beta_in,
     double scale, const float *__restrict__ shift_part, double *__restrict__ shift_out,
     double *__restrict__ tr_shift, uint16_t *__restrict__ phi16, double *__restrict__ m_out,
-    double *__restrict__ r_out, float *__restrict__ Y_out, int32_t *__restrict__ head_status,
-    const int32_t *__restrict__ gate) {
+    double *__restrict__ r_out, float *__restrict__ Y_out, int32_t *__restrict__ head_status) {
   constexpr int KCH = D / 8;        // 16-byte chunks per K row
   constexpr int NS = D / 4;         // k-steps of the logit MFMA
   constexpr int NA = D / 32;        // 16-byte K reads per key block
@@ -503,20 +502,6 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
   uint32_t *const lv0 = lv_all, *const lv1 = lv_all + VWORDS;
   __shared__ double s_shift;
 
-  int h, qb;
-  {
-    const int b = blockIdx.x;
-    if (xcd_map) {
-      const int x = b & 7, slot = b >> 3;
-      h = x + 8 * (slot / nqb);
-      qb = slot % nqb;
-    } else {
-      h = b / nqb;
-      qb = b % nqb;
-    }
-  }
-  if (h >= H) return;
-  if (gate && gate[h] == 0) return;
   const HeadDesc Dh = desc[h];
   const int64_t q0 = int64_t(qb) * kPhi16Rows;
   if (q0 >= Dh.n) return;
@@ -724,6 +709,64 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
     }
   }
   if (bad && head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
+}
+
+// One launch of the float64 kernel: with `list` null, block b takes head and
+// query block from b (XCD by XCD when xcd_map is set); else the blocks walk
+// the (head, query block) pairs of the *list_cnt heads in `list` (the heads
+// the int8 kernel leaves to it), so that the launch costs next to nothing
+// when the list is empty.
+template <int D, int STORE>
+__global__ __launch_bounds__(kPhi16Rows * 4) void k_phi16(
+    const HeadDesc *__restrict__ desc, int H, int nqb, int xcd_map, const uint16_t *__restrict__ Q,
+    const uint16_t *__restrict__ K, const uint16_t *__restrict__ vt, const float *__restrict__ beta_in,
+    double scale, const float *__restrict__ shift_part, double *__restrict__ shift_out,
+    double *__restrict__ tr_shift, uint16_t *__restrict__ phi16, double *__restrict__ m_out,
+    double *__restrict__ r_out, float *__restrict__ Y_out, int32_t *__restrict__ head_status,
+    const int32_t *__restrict__ list, const int32_t *__restrict__ list_cnt) {
+#define AMC_P16_BODY desc, Q, K, vt, beta_in, scale, shift_part, shift_out, tr_shift, phi16, m_out, r_out, Y_out, head_status
+  if (list) {
+    const int items = *list_cnt * nqb;
+    for (int it = blockIdx.x; it < items; it += gridDim.x) {
+      phi16_block<D, STORE>(list[it / nqb], it % nqb, AMC_P16_BODY);
+      __syncthreads();
+    }
+    return;
+  }
+  const int b = blockIdx.x;
+  int h, qb;
+  if (xcd_map) {
+    const int x = b & 7, slot = b >> 3;
+    h = x + 8 * (slot / nqb);
+    qb = slot % nqb;
+  } else {
+    h = b / nqb;
+    qb = b % nqb;
+  }
+  if (h >= H) return;
+  phi16_block<D, STORE>(h, qb, AMC_P16_BODY);
+#undef AMC_P16_BODY
+}
+
+// The heads with flag[h] != 0, in order, and their number (one block).
+__global__ __launch_bounds__(256) void k_list_flags(const int32_t *__restrict__ flag, int H, int32_t *__restrict__ list,
+                                                    int32_t *__restrict__ cnt) {
+  __shared__ int s_wc[4];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int total = 0;
+  for (int h0 = 0; h0 < H; h0 += 256) {
+    const bool take = h0 + tid < H && flag[h0 + tid] != 0;
+    const uint64_t m = __ballot(take);
+    if (lane == 0) s_wc[wave] = __popcll(m);
+    __syncthreads();
+    int at = total;
+    for (int w = 0; w < wave; ++w) at += s_wc[w];
+    at += __popcll(m & ((uint64_t(1) << lane) - 1));
+    if (take) list[at] = h0 + tid;
+    total += s_wc[0] + s_wc[1] + s_wc[2] + s_wc[3];
+    __syncthreads();
+  }
+  if (tid == 0) *cnt = total;
 }
 
 constexpr int kDigits = 5;
@@ -1275,14 +1318,15 @@ static void launch_phi8(const Dims &dm, const Buffers &b, hipStream_t s) {
 }
 
 template <int STORE>
-static void launch_phi16(const Dims &dm, const Buffers &b, const int32_t *gate, hipStream_t s) {
+static void launch_phi16(const Dims &dm, const Buffers &b, const int32_t *list, const int32_t *list_cnt,
+                         hipStream_t s) {
   const int nqb = int((dm.max_n + kPhi16Rows - 1) / kPhi16Rows);
   const int xcd_map = (dm.H % 8 == 0) ? 1 : 0;
-  dim3 grid(unsigned(nqb * dm.H));
+  dim3 grid(unsigned(list ? 256 : nqb * dm.H));
   const uint16_t *Q = static_cast<const uint16_t *>(b.Q);
   const uint16_t *K = static_cast<const uint16_t *>(b.K);
 #define AMC_PHI16_ARGS b.desc, dm.H, nqb, xcd_map, Q, K, b.vt, b.beta_in, dm.scale, b.shift_part, b.shift, b.tr_shift, \
-    b.phi16, b.m, b.r, b.Y, b.head_status, gate
+    b.phi16, b.m, b.r, b.Y, b.head_status, list, list_cnt
   if (dm.d == 128)
     hipLaunchKernelGGL((k_phi16<128, STORE>), grid, dim3(kPhi16Rows * 4), 0, s, AMC_PHI16_ARGS);
   else
@@ -1299,43 +1343,52 @@ hipError_t launch_vt(const Dims &dm, const Buffers &b, hipStream_t s) {
   return hipGetLastError();
 }
 
+hipError_t launch_digits(const Dims &dm, const Buffers &b, hipStream_t s) {
+  if (!b.qdig || !dm.in_bf16) return hipErrorInvalidValue;
+  hipError_t e = launch_fill_i32(b.f64_heads, dm.H, 0, s);
+  if (e != hipSuccess) return e;
+  constexpr int kRowsPerBlock128 = 256 / 16, kRowsPerBlock64 = 256 / 8;
+  const int64_t rows = dm.max_n + 32 + (dm.max_T + 63) / 64 * 64;  // queries to a whole block, then keys
+  const uint16_t *Q = static_cast<const uint16_t *>(b.Q);
+  const uint16_t *K = static_cast<const uint16_t *>(b.K);
+#define AMC_DIGITS_ARGS b.desc, Q, K, b.beta_in, b.shift_part, b.qdig, b.qexp, b.kdig, b.ktab, b.f64_heads
+  if (dm.d == 128)
+    hipLaunchKernelGGL(k_digits<128>, dim3(unsigned((rows + kRowsPerBlock128 - 1) / kRowsPerBlock128), unsigned(dm.H)),
+                       dim3(256), 0, s, AMC_DIGITS_ARGS);
+  else
+    hipLaunchKernelGGL(k_digits<64>, dim3(unsigned((rows + kRowsPerBlock64 - 1) / kRowsPerBlock64), unsigned(dm.H)),
+                       dim3(256), 0, s, AMC_DIGITS_ARGS);
+#undef AMC_DIGITS_ARGS
+  // the heads off the digit grid, listed for the float64 kernel
+  hipLaunchKernelGGL(k_list_flags, dim3(1), dim3(256), 0, s, b.f64_heads, dm.H, b.f64_list, b.f64_cnt);
+  return hipGetLastError();
+}
+
 hipError_t launch_phi(const Dims &dm, const Buffers &b, int store, hipStream_t s) {
   if (store == 1 && !b.phi) return hipErrorInvalidValue;
   if (store == 2 && !b.phi16) return hipErrorInvalidValue;
   if (dm.in_bf16 && b.vt && store != 1) {
+    // int8 logits (after launch_digits) for the heads on the digit grid, else
+    // the float64-MFMA kernel for every head
     if (b.qdig) {
-      // int8 logits for the heads whose rows are exact in digit form, float64
-      // MFMA logits for the rest
-      hipError_t e = launch_fill_i32(b.f64_heads, dm.H, 0, s);
-      if (e != hipSuccess) return e;
-      constexpr int kRowsPerBlock128 = 256 / 16, kRowsPerBlock64 = 256 / 8;
-      const int64_t rows = dm.max_n + 32 + (dm.max_T + 63) / 64 * 64;  // queries to a whole block, then keys
-      const uint16_t *Q = static_cast<const uint16_t *>(b.Q);
-      const uint16_t *K = static_cast<const uint16_t *>(b.K);
-#define AMC_DIGITS_ARGS b.desc, Q, K, b.beta_in, b.shift_part, b.qdig, b.qexp, b.kdig, b.ktab, b.f64_heads
-      if (dm.d == 128)
-        hipLaunchKernelGGL(k_digits<128>, dim3(unsigned((rows + kRowsPerBlock128 - 1) / kRowsPerBlock128), unsigned(dm.H)),
-                           dim3(256), 0, s, AMC_DIGITS_ARGS);
-      else
-        hipLaunchKernelGGL(k_digits<64>, dim3(unsigned((rows + kRowsPerBlock64 - 1) / kRowsPerBlock64), unsigned(dm.H)),
-                           dim3(256), 0, s, AMC_DIGITS_ARGS);
-#undef AMC_DIGITS_ARGS
-      if (store == 2) {
-        launch_phi8<2>(dm, b, s);
-        launch_phi16<2>(dm, b, b.f64_heads, s);
-      } else {
-        launch_phi8<0>(dm, b, s);
-        launch_phi16<0>(dm, b, b.f64_heads, s);
-      }
-      return hipGetLastError();
+      if (store == 2) launch_phi8<2>(dm, b, s);
+      else launch_phi8<0>(dm, b, s);
+    } else {
+      if (store == 2) launch_phi16<2>(dm, b, nullptr, nullptr, s);
+      else launch_phi16<0>(dm, b, nullptr, nullptr, s);
     }
-    if (store == 2) launch_phi16<2>(dm, b, nullptr, s);
-    else launch_phi16<0>(dm, b, nullptr, s);
     return hipGetLastError();
   }
   if (store == 1) launch_phi_store<1>(dm, b, s);
   else if (store == 2) launch_phi_store<2>(dm, b, s);
   else launch_phi_store<0>(dm, b, s);
+  return hipGetLastError();
+}
+
+hipError_t launch_phi_fallback(const Dims &dm, const Buffers &b, int store, hipStream_t s) {
+  if (!b.qdig || !dm.in_bf16 || !b.vt || store == 1) return hipErrorInvalidValue;
+  if (store == 2) launch_phi16<2>(dm, b, b.f64_list, b.f64_cnt, s);
+  else launch_phi16<0>(dm, b, b.f64_list, b.f64_cnt, s);
   return hipGetLastError();
 }
 

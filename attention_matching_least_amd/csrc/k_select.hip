@@ -647,7 +647,8 @@ __global__ __launch_bounds__(PR_THREADS) void k_prune(const HeadDesc *__restrict
                                                       const float *__restrict__ colsum, int64_t qb128, int cycle,
                                                       int kR, float *__restrict__ rpn, double *__restrict__ rabs,
                                                       int32_t *__restrict__ surv_list,
-                                                      int32_t *__restrict__ surv_cnt) {
+                                                      int32_t *__restrict__ surv_cnt,
+                                                      int32_t *__restrict__ tr_swept) {
   __shared__ double s_r[kStoredMaxN];
   __shared__ float s_u[PR_MAXT];
   __shared__ double s_wmax[kStoredMaxN / 64];
@@ -696,7 +697,10 @@ __global__ __launch_bounds__(PR_THREADS) void k_prune(const HeadDesc *__restrict
   __syncthreads();
   const bool keep_all = cycle == 0 || !isfinite(s_L) || Kc + 1 > PR_CAND || D.T > PR_MAXT;
   if (keep_all) {
-    if (tid == 0) surv_cnt[h] = -1;
+    if (tid == 0) {
+      surv_cnt[h] = -1;
+      if (tr_swept) tr_swept[D.cyc_off + cycle] = int32_t(D.T);
+    }
     return;
   }
   // U for every key (-inf for selected keys), each thread's best
@@ -791,7 +795,10 @@ __global__ __launch_bounds__(PR_THREADS) void k_prune(const HeadDesc *__restrict
     for (int w = 0; w < PR_THREADS / 64; ++w) total += s_wc[w];
     __syncthreads();
   }
-  if (tid == 0) surv_cnt[h] = total;
+  if (tid == 0) {
+    surv_cnt[h] = total;
+    if (tr_swept) tr_swept[D.cyc_off + cycle] = total;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1308,7 +1315,7 @@ hipError_t launch_sweep_band(const Dims &dm, const Buffers &b, int cycle, int kR
 
 hipError_t launch_prune(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
   hipLaunchKernelGGL(k_prune, dim3(unsigned(dm.H)), dim3(PR_THREADS), 0, s, b.desc, b.r, b.sel_slot, b.phi16, b.colsum,
-                     dm.qb128, cycle, kR, b.rpn, b.rabs, b.surv_list, b.surv_cnt);
+                     dm.qb128, cycle, kR, b.rpn, b.rabs, b.surv_list, b.surv_cnt, b.tr_swept);
   return hipGetLastError();
 }
 

@@ -35,6 +35,7 @@ import synth  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 F64_MFMA_PEAK_TFS = 78.6
+I8_MFMA_PEAK_TOPS = 5000.0  # dense int8 matrix peak of the MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_traffic.md")
 KERNEL_SOURCES = {"k_sweep_band": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_select.hip"),
                   "k_phi": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_phi.hip")}
@@ -61,6 +62,62 @@ def generate(idx: int, workers: int):
     K = np.concatenate([p[1] for p in parts])
     V = np.concatenate([p[2] for p in parts])
     return w, Q, K, V
+
+
+# 2^(bit length - 1) of a 1..255 significand
+_TOPBIT = np.array([0] + [int(v).bit_length() - 1 for v in range(1, 256)], dtype=np.int32)
+
+
+def digit_zeros(bits: np.ndarray):
+    """Per row of bf16 bit patterns, as the int8 logit kernel sees it: z = the
+    low base-256 digits that are zero in all entries of the row (up to 2;
+    rows on the digit grid of 2^(E - 37), E the row's largest exponent), and
+    whether the row is off that grid (or non-finite)."""
+    zs, bads = [], []
+    for r0 in range(0, bits.shape[0], 32768):
+        b = bits[r0:r0 + 32768].astype(np.int32)
+        ef, mt = (b >> 7) & 0xff, b & 0x7f
+        nz = (b & 0x7fff) != 0
+        p = np.where(ef == 0, -133, ef - 134)
+        e = p + _TOPBIT[np.where(ef == 0, mt, mt | 0x80)]
+        E = np.where(nz, e, -100000).max(axis=1)
+        pmin = np.where(nz, p, 100000).min(axis=1)
+        anynz = nz.any(axis=1)
+        E = np.where(anynz, E, 0)
+        z = np.where(anynz, np.clip((pmin + 37 - E) >> 3, 0, 2), 2)
+        bad = (anynz & (pmin < E - 37)) | (ef == 255).any(axis=1)
+        zs.append(z)
+        bads.append(bad)
+    return np.concatenate(zs), np.concatenate(bads)
+
+
+def phi_matrix_ops(Qb: np.ndarray, Kb: np.ndarray, w) -> float:
+    """Matrix-core work of one mass-feature pass over the stack, in int8-equivalent
+    operations: per head on the digit grid, for every wave of 16 queries and
+    16-key block, (d / 64) (5 - zq) (5 - zk) int8 16x16x64 products (zq, zk the
+    wave's and the block's all-zero low digits), and 6 d / 16 bf16 16x16x32
+    products of the Phi V split per wave and 64-key tile (a bf16 operation
+    counting as two at half the int8 rate).  Heads off the grid (float64
+    kernel) are left out."""
+    H, n, T, d = w.num_heads, w.n, w.T, w.d
+    zq, bq = digit_zeros(Qb)
+    zk, bk = digit_zeros(Kb)
+    nq16, nk16 = -(-n // 16), -(-((T + 63) // 64 * 64) // 16)
+    total = 0.0
+    for h in range(H):
+        if bq[h * n:(h + 1) * n].any() or bk[h * T:(h + 1) * T].any():
+            continue
+        q = np.full(nq16 * 16, 2, np.int32)
+        q[:n] = zq[h * n:(h + 1) * n]
+        k = np.full(nk16 * 16, 2, np.int32)
+        k[:T] = zk[h * T:(h + 1) * T]
+        a = float((5 - q.reshape(-1, 16).min(axis=1)).sum())
+        b = float((5 - k.reshape(-1, 16).min(axis=1)).sum())
+        i8 = (d // 64) * a * b * 32768.0
+        waves = -(-n // 128) * 8
+        bf16 = waves * ((T + 63) // 64) * (6 * d // 16) * 16384.0
+        total += i8 + 2.0 * bf16
+    return total
 
 
 def source_hash(kernel: str) -> str:
@@ -339,6 +396,7 @@ def main():
         return (t.view(torch.bfloat16) if a.dtype == np.uint16 else t).to(dev)
 
     Q, K, V = up(Qb), up(Kb), up(Vb)
+    phi_ops = phi_matrix_ops(Qb, Kb, w) if (w.dtype == "bf16" and not args.no_timer) else None
     del Qb, Kb, Vb
     H = w.num_heads
     cu_q = [w.n * h for h in range(H + 1)]
@@ -372,7 +430,8 @@ def main():
         torch.cuda.synchronize()
         t1 = time.perf_counter()
         for _ in range(args.steps):
-            amc.compact(Q, K, V, w.budgets, workspace=workspace, head_groups=1, timer=timer, **kw)
+            kres = amc.compact(Q, K, V, w.budgets, workspace=workspace, head_groups=1, timer=timer, trace=True,
+                               **kw)
         torch.cuda.synchronize()
         kernel_pass = {"head_groups": 1, "steps": args.steps,
                        "ms_per_step": round(1000.0 * (time.perf_counter() - t1) / args.steps, 3)}
@@ -381,33 +440,30 @@ def main():
         kr = w.topk * w.refit_every
         sw = kernels.get("sweep")
         if sw:
-            # algorithmic bytes: each bounded-sweep launch reads the high 16-bit plane of the
-            # stored Phi (2 bytes per query and key) of every head that still selects keys in
-            # that cycle; ceil(t_h / (k R)) launches touch head h per step
-            per_step = float(sum(-(-b // kr) * w.n * w.T * 2 for b in w.budgets))
-            per_launch = per_step * args.steps / sw["launches"]
+            # algorithmic bytes: the stored high plane's columns of the keys each bounded
+            # sweep reads (every key on the first cycle, the pruning's survivors after),
+            # ldN = n rounded up to 64 queries of 2 bytes each, from the trace
+            ldn = (w.n + 63) // 64 * 64
+            swept = sum(int(c.sum()) for c in kres.trace()["swept_keys"])
+            per_step = float(swept) * ldn * 2
             achieved = per_step * args.steps / (sw["total_ms"] * 1e-3) / 1e9
             found.append((sw["total_ms"], {
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("k_sweep_band"),
                 "kernel": "k_sweep_band", "avg_launch_ms": round(sw["avg_ms"], 4), "launches": sw["launches"],
-                "algorithmic_bytes_per_launch": per_launch}))
+                "algorithmic_bytes_per_launch": per_step * args.steps / sw["launches"],
+                "swept_keys_per_step": swept, "keys_per_step_unpruned": int(sum(-(-b // kr) for b in w.budgets)) * w.T}))
         ph = kernels.get("phi")
-        if ph:
-            # the mass features: n T exps, logits and Phi V products per head.  The logits
-            # run as exact int8 digit products (up to 25 per float64 product) next to a
-            # float64 exp per element, so no single peak bounds the kernel: it is reported
-            # as elements per second and float64-equivalent logit TFLOP/s (2 n T d per
-            # head), with the matrix-core utilisation taken from counters in the profiles
-            elems = float(w.n) * w.T * H
-            per_launch = elems * args.steps / ph["launches"]
+        if ph and phi_ops:
+            # matrix-core work of the mass features (phi_matrix_ops), int8-equivalent operations
             secs = ph["total_ms"] * 1e-3
+            achieved = phi_ops * args.steps / secs / 1e12
             found.append((ph["total_ms"], {
-                "bound": "mfma+valu", "achieved": round(elems * args.steps / secs / 1e9, 1), "peak": None,
-                "unit": "Gelem/s", "frac": None, "traffic": read_traffic("k_phi"),
-                "f64_equivalent_logit_tflops": round(2.0 * elems * w.d * args.steps / secs / 1e12, 2),
+                "bound": "mfma", "achieved": round(achieved, 1), "peak": I8_MFMA_PEAK_TOPS, "unit": "TOP/s",
+                "frac": round(achieved / I8_MFMA_PEAK_TOPS, 4), "traffic": read_traffic("k_phi"),
                 "kernel": "k_phi8", "avg_launch_ms": round(ph["avg_ms"], 4), "launches": ph["launches"],
-                "elements_per_launch": per_launch}))
+                "algorithmic_ops_per_launch": phi_ops * args.steps / ph["launches"],
+                "f64_equivalent_logit_tflops": round(2.0 * w.n * w.T * w.d * H * args.steps / secs / 1e12, 2)}))
         found.sort(key=lambda x: -x[0])
         if found:
             roofline = found[0][1]

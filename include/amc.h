@@ -97,7 +97,9 @@ typedef enum {
   AMC_K_SWEEP_EXACT = 12, /* float32 sweep of the heads whose candidate band overflowed */
   AMC_K_RESCORE = 13, /* float64 scores and columns of the band's candidates */
   AMC_K_PRUNE = 14,   /* per-cycle bound that drops keys from the bounded sweep */
-  AMC_NUM_KERNEL_CLASSES = 15
+  AMC_K_DIGITS = 15,  /* bf16 rows in exact base-256 digit form for the int8 logits */
+  AMC_K_PHI_F64 = 16, /* float64-MFMA mass features of the heads off the digit grid */
+  AMC_NUM_KERNEL_CLASSES = 17
 } amc_kernel_class;
 
 typedef struct {
@@ -149,10 +151,13 @@ typedef struct {
  *   weight     double [sum t_h]    final NNLS weight w of each pick (selection order)
  *   runner_up  double [sum c_h]    best score not taken by each cycle, at cu_cycles[h]
  *   nnls_iters int32  [sum c_h]    active-set iterations of the refit closing each cycle
+ *   swept_keys int32  [sum c_h]    keys whose stored Phi columns the cycle's bounded sweep
+ *                                  read (T_h when every key is read; 0 when Phi is not
+ *                                  stored)
  * where a "cycle" is the R iterations between two refits; head h has
  * c_h = ceil(t_h / (k R)) cycles (amc_cycle_offsets). */
 typedef struct {
-  uint64_t shift, pick, pick_score, weight, runner_up, nnls_iters;
+  uint64_t shift, pick, pick_score, weight, runner_up, nnls_iters, swept_keys;
   uint64_t total_bytes;
 } amc_trace_layout;
 
