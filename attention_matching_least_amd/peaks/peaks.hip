@@ -10,6 +10,7 @@
 typedef double d4 __attribute__((ext_vector_type(4)));
 typedef float f4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf8 __attribute__((ext_vector_type(8)));
+typedef int i4 __attribute__((ext_vector_type(4)));
 
 #define CHECK(x)                                                         \
   do {                                                                   \
@@ -73,6 +74,20 @@ __global__ __launch_bounds__(256) void p_bf16_16x16x32(double *o, int iters) {
   o[blockIdx.x * blockDim.x + threadIdx.x] = a0[0] + a1[1] + a2[2] + a3[3];
 }
 
+// eight accumulation chains (the int8 MFMA needs more in flight than the others)
+__global__ __launch_bounds__(256) void p_i8_16x16x64(double *o, int iters) {
+  i4 a[8];
+  for (int c = 0; c < 8; ++c) a[c] = i4{c, 0, 0, 0};
+  const i4 x = {int(threadIdx.x), 3, 5, 7}, y = {1, int(threadIdx.x) * 3, 9, 11};
+  for (int i = 0; i < iters; ++i) {
+#pragma unroll
+    for (int c = 0; c < 8; ++c) a[c] = __builtin_amdgcn_mfma_i32_16x16x64_i8((c & 1) ? x : y, (c & 2) ? y : x, a[c], 0, 0, 0);
+  }
+  double t = 0.0;
+  for (int c = 0; c < 8; ++c) t += double(a[c][c & 3]);
+  o[blockIdx.x * blockDim.x + threadIdx.x] = t;
+}
+
 __global__ __launch_bounds__(256) void p_f64_fma(double *o, int iters) {
   double a0 = 0, a1 = 0, a2 = 0, a3 = 0;
   const double x = threadIdx.x * 1e-3, y = 1.0 + x;
@@ -130,12 +145,14 @@ int main() {
   const double t2 = time_ms(p_f32_16x16x4, dim3(blocks), o, iters);
   const double t3 = time_ms(p_bf16_16x16x32, dim3(blocks), o, iters);
   const double t4 = time_ms(p_f64_fma, dim3(blocks), o, iters * 64);
+  const double t5 = time_ms(p_i8_16x16x64, dim3(blocks), o, iters);
   const double tf = 1e9;  // (flop / ms) -> TFLOP/s
   const double f64_16 = waves_x_chains * (16 * 16 * 4 * 2) / t0 / tf;
   const double f64_4 = waves_x_chains * (4 * 4 * 4 * 2 * 4) / t1 / tf;  // four 4x4 blocks per instruction
   const double f32_16 = waves_x_chains * (16 * 16 * 4 * 2) / t2 / tf;
   const double bf16 = waves_x_chains * (16 * 16 * 32 * 2) / t3 / tf;
   const double fma64 = waves_x_chains * 64 * (64 * 2) / t4 / tf;
+  const double i8 = 2.0 * waves_x_chains * (16 * 16 * 64 * 2) / t5 / tf;  // eight chains
   // HBM read stream over 8 GiB
   const int64_t nbytes = int64_t(8) << 30;
   f4 *buf = nullptr;
@@ -159,8 +176,9 @@ int main() {
   const double read_gbs = double(nbytes) / (rms * 1e-3) / 1e9;
   std::printf(
       "{\"mfma_f64_16x16x4_tflops\": %.1f, \"mfma_f64_4x4x4_tflops\": %.1f, \"mfma_f32_16x16x4_tflops\": %.1f, "
-      "\"mfma_bf16_16x16x32_tflops\": %.1f, \"vector_f64_fma_tflops\": %.1f, \"hbm_read_gbs\": %.0f}\n",
-      f64_16, f64_4, f32_16, bf16, fma64, read_gbs);
+      "\"mfma_bf16_16x16x32_tflops\": %.1f, \"mfma_i8_16x16x64_tops\": %.1f, \"vector_f64_fma_tflops\": %.1f, "
+      "\"hbm_read_gbs\": %.0f}\n",
+      f64_16, f64_4, f32_16, bf16, i8, fma64, read_gbs);
   CHECK(hipFree(buf));
   CHECK(hipFree(part));
   CHECK(hipFree(o));

@@ -36,7 +36,7 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 F64_MFMA_PEAK_TFS = 78.6
 I8_MFMA_PEAK_TOPS = 5000.0  # dense int8 matrix peak of the MI355X
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "sweep_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3-4b-stack-T8192-50x.md")
 KERNEL_SOURCES = {"k_sweep_band": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_select.hip"),
                   "k_phi": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_phi.hip")}
 
