@@ -72,7 +72,7 @@ class Options(ctypes.Structure):
 class TraceLayout(ctypes.Structure):
     _fields_ = [(n, ctypes.c_uint64) for n in
                 ("shift", "pick", "pick_score", "weight", "runner_up", "nnls_iters", "swept_keys",
-                 "total_bytes")]
+                 "swept_keys8", "total_bytes")]
 
 
 _lib = None
@@ -310,6 +310,7 @@ class CompactResult:
         runner = sec(L.runner_up, np.float64, sc)
         iters = sec(L.nnls_iters, np.int32, sc)
         swept = sec(L.swept_keys, np.int32, sc)
+        swept8 = sec(L.swept_keys8, np.int32, sc)
         cb, cc = self.cu_budgets, self.cu_cycles
         return {
             "shift": shift,
@@ -319,6 +320,7 @@ class CompactResult:
             "runner_up": [runner[cc[h]:cc[h + 1]] for h in range(H)],
             "nnls_iters": [iters[cc[h]:cc[h + 1]] for h in range(H)],
             "swept_keys": [swept[cc[h]:cc[h + 1]] for h in range(H)],
+            "swept_keys8": [swept8[cc[h]:cc[h + 1]] for h in range(H)],
         }
 
 

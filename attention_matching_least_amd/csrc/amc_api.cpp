@@ -67,8 +67,17 @@ struct Plan {
            o_dn = 0, o_L = 0, o_nnL = 0, o_nnP = 0, o_nnnp = 0, o_gA = 0, o_nnvec = 0, o_cand_lo = 0,
            o_cand_lidx = 0, o_cand_cnt = 0, o_band_list = 0, o_band_cnt = 0, o_exact = 0, o_stage = 0,
            o_part = 0, o_vt = 0, o_qdig = 0, o_kdig = 0, o_qexp = 0, o_ktab = 0, o_f64h = 0, o_colsum = 0, o_rpn = 0, o_rabs = 0,
-           o_surv = 0, o_survcnt = 0, total = 0;
+           o_surv = 0, o_survcnt = 0, o_pruneL = 0, o_q8 = 0, o_q8bad = 0, o_surv2 = 0, o_surv2cnt = 0,
+           total = 0;
+  bool store_q8 = false;  // the 8-bit plane of the second pruning stage fits the budget too
 };
+
+// AMC_PRUNE_Q8=0 leaves the 8-bit plane and the second pruning stage out
+// (the selection is the same either way; for testing and measurement).
+static bool q8_stage_enabled() {
+  const char *e = std::getenv("AMC_PRUNE_Q8");
+  return !(e && std::strcmp(e, "0") == 0);
+}
 
 static amc_status check_problem(const amc_problem *p) {
   if (!p || p->num_heads < 1 || !p->cu_q || !p->cu_k || !p->budgets) return AMC_ERR_INVALID_ARG;
@@ -180,6 +189,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   if (!features_only) {
     // else every sweep recomputes Phi
     pl.store_phi = phi_bytes <= o->phi_budget_bytes && dm.max_n <= kStoredMaxN;
+    pl.store_q8 = pl.store_phi && phi_bytes + uint64_t(phi) <= o->phi_budget_bytes && q8_stage_enabled();
   }
 
   uint64_t off = 0;
@@ -234,6 +244,13 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     pl.o_rabs = take(8ull * H);
     pl.o_surv = take(4ull * ktr);
     pl.o_survcnt = take(4ull * H);
+    pl.o_pruneL = take(8ull * H);
+    if (pl.store_q8) {
+      pl.o_q8 = take(uint64_t(phi));
+      pl.o_q8bad = take(4ull * H);
+      pl.o_surv2 = take(4ull * ktr);
+      pl.o_surv2cnt = take(4ull * H);
+    }
   }
   if (dm.in_bf16) {
     pl.o_vt = take(2ull * vt);  // transposed value tiles of the mass-feature kernel
@@ -262,6 +279,7 @@ static void trace_layout(const Plan &pl, amc_trace_layout *L) {
   L->runner_up = take(8ull * pl.sum_cycles);
   L->nnls_iters = take(4ull * pl.sum_cycles);
   L->swept_keys = take(4ull * pl.sum_cycles);
+  L->swept_keys8 = take(4ull * pl.sum_cycles);
   L->total_bytes = off;
 }
 
@@ -309,6 +327,9 @@ static Buffers head_range(const Buffers &b, int h0, int64_t max_qblk) {
   }
   if (b.rabs) r.rabs = b.rabs + h0;
   if (b.surv_cnt) r.surv_cnt = b.surv_cnt + h0;
+  if (b.prune_L) r.prune_L = b.prune_L + h0;
+  if (b.q8_bad) r.q8_bad = b.q8_bad + h0;
+  if (b.surv2_cnt) r.surv2_cnt = b.surv2_cnt + h0;
   return r;
 }
 
@@ -493,6 +514,13 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
     b.rabs = reinterpret_cast<double *>(ws + pl.o_rabs);
     b.surv_list = reinterpret_cast<int32_t *>(ws + pl.o_surv);
     b.surv_cnt = reinterpret_cast<int32_t *>(ws + pl.o_survcnt);
+    b.prune_L = reinterpret_cast<double *>(ws + pl.o_pruneL);
+    if (pl.store_q8) {
+      b.q8 = reinterpret_cast<uint8_t *>(ws + pl.o_q8);
+      b.q8_bad = reinterpret_cast<int32_t *>(ws + pl.o_q8bad);
+      b.surv2_list = reinterpret_cast<int32_t *>(ws + pl.o_surv2);
+      b.surv2_cnt = reinterpret_cast<int32_t *>(ws + pl.o_surv2cnt);
+    }
   }
   b.head_status = head_status;
   if (tracing) {
@@ -504,6 +532,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
     b.tr_runner = reinterpret_cast<double *>(tr + tl.runner_up);
     b.tr_iters = reinterpret_cast<int32_t *>(tr + tl.nnls_iters);
     b.tr_swept = reinterpret_cast<int32_t *>(tr + tl.swept_keys);
+    b.tr_swept8 = reinterpret_cast<int32_t *>(tr + tl.swept_keys8);
   }
   NnlsParams np{0, o->nnls_max_iters, o->nnls_tol};
   pl.dm.band_cap = band_cap_setting();
@@ -515,6 +544,8 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.sel_slot, pl.sum_T, 0, stream));
   if (head_status) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(head_status, dm.H, 0, stream));
   if (b.tr_swept && !pl.store_phi) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.tr_swept, pl.sum_cycles, 0, stream));
+  if (b.tr_swept8) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.tr_swept8, pl.sum_cycles, 0, stream));
+  if (b.q8_bad) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.q8_bad, dm.H, 0, stream));
 
   // The heads run in groups, each on a stream of its own (the caller's for the
   // first), joined back to the caller's stream by events: the groups' mass
@@ -569,9 +600,18 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
         if (pl.store_phi) {
           // bounded sweep and float64 rescoring of the band; the heads whose
           // band overflowed take the float32 sweep, merge and panel
+          // (after the first cycle, with the 8-bit plane, a second pruning stage
+          // narrows the list the bounded sweep reads)
           AMC_LAUNCH(AMC_K_PRUNE, launch_prune(dg, bg, c, pl.kR, stream));
-          AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_band(dg, bg, c, pl.kR, stream));
-          AMC_LAUNCH(AMC_K_MERGE, launch_band_merge(dg, bg, c, pl.kR, stream));
+          Buffers bs = bg;
+          if (bg.q8 && c > 0) {
+            AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_q8(dg, bg, c, pl.kR, stream));
+            AMC_LAUNCH(AMC_K_PRUNE, launch_q8_compact(dg, bg, c, pl.kR, stream));
+            bs.surv_list = bg.surv2_list;
+            bs.surv_cnt = bg.surv2_cnt;
+          }
+          AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_band(dg, bs, c, pl.kR, stream));
+          AMC_LAUNCH(AMC_K_MERGE, launch_band_merge(dg, bs, c, pl.kR, stream));
           AMC_LAUNCH(AMC_K_SWEEP_EXACT, launch_sweep(dg, bg, c, pl.kR, 1, stream));
           AMC_LAUNCH(AMC_K_MERGE, launch_merge(dg, bg, c, pl.kR, 1, stream));
           AMC_LAUNCH(AMC_K_RESCORE, launch_rescore(dg, bg, c, pl.kR, stream));

@@ -63,8 +63,14 @@ struct Buffers {
                        // plane, rounded down (written by the first sweep)
   float *rpn;          // [sum n][2] float32 positive and negative parts of r (per cycle)
   double *rabs;        // [H] sum |r| (per cycle)
-  int32_t *surv_list;  // per head at kt_off: keys the cycle's bounded sweep reads
+  int32_t *surv_list;  // per head at kt_off: keys that pass the cycle's first pruning stage
   int32_t *surv_cnt;   // [H] their number, -1: every key
+  double *prune_L;     // [H] the first stage's threshold (-inf: every key kept)
+  uint8_t *q8;         // per head at phi_off: 8-bit plane [ldT keys][ldN queries] (null: no
+                       // second stage)
+  int32_t *q8_bad;     // [H] 1: the head's 8-bit plane is out of range (stage skipped)
+  int32_t *surv2_list; // per head at kt_off: keys that pass both stages (the bounded sweep's list)
+  int32_t *surv2_cnt;  // [H] their number, -1: every key
   uint16_t *vt;        // bf16 inputs: per head at vt_off, [T/64 tiles][d][72] values, key-permuted
                        // (64 per row and a pad of 8, the layout the mass-feature kernels stage)
   int8_t *qdig;        // bf16 inputs: rows of Q as five base-256 digit rows ([rows][5][d]); null:
@@ -109,7 +115,7 @@ struct Buffers {
   int32_t *head_status;  // [H] or null
   // trace (all null when tracing is off)
   double *tr_shift, *tr_pick_score, *tr_weight, *tr_runner;
-  int32_t *tr_pick, *tr_iters, *tr_swept;
+  int32_t *tr_pick, *tr_iters, *tr_swept, *tr_swept8;
 };
 
 struct Dims {
@@ -151,6 +157,9 @@ hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int cyc_
 hipError_t launch_sweep_band(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 // per cycle of the stored-Phi selection: r's parts and the keys the bounded sweep reads
 hipError_t launch_prune(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+// second pruning stage from the 8-bit plane, then the list the bounded sweep reads
+hipError_t launch_sweep_q8(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
+hipError_t launch_q8_compact(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_band_merge(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_rescore(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
 hipError_t launch_choose(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);

@@ -124,6 +124,7 @@ struct St {
   unsigned char *flag;
   Blk *bk;
   int mp;         // row stride (largest p of the system)
+  bool lds;       // L lives in LDS (the one-wave solves apply up to kWaveRows rows)
   __device__ __forceinline__ double *row(int b) const { return b == 0 ? x0 : (b == 8 ? yv : rows + b * mp); }
 };
 
@@ -143,6 +144,7 @@ __device__ __forceinline__ St carve_lds(char *base, int maxp, Blk *bk) {
   St s;
   s.mp = maxp;
   s.bk = bk;
+  s.lds = true;
   double *d = reinterpret_cast<double *>(base);
   s.L = d;
   d += tri(maxp);
@@ -167,6 +169,7 @@ __device__ __forceinline__ St carve_global(double *vec, double *L, int32_t *plis
   St s;
   s.mp = mp;
   s.bk = bk;
+  s.lds = false;
   s.L = L;
   s.u = vec;
   s.g = vec + mp;
@@ -363,6 +366,187 @@ __device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
   }
 }
 
+// ---- one-wave triangular solves (factor in LDS, n <= kWaveRows) ----------
+//
+// Column-oriented substitution in a single wave, with no block barriers: lane
+// l holds rows l, l + 64 and l + 128; once x_k is known (r_k / L_kk, read
+// from its lane) it is applied to the rows still open.  Every update is a
+// plain fma with a zero coefficient where a row is not touched, so the lanes
+// run without branches.  The substitution is the same sequence of
+// operations as the blocked solves, one product at a time.
+
+constexpr int kWaveRows = 192;
+
+// Columns in flight ahead of the one being applied: the LDS latency spans a
+// few substitution steps.  The empty asm with a memory clobber after each
+// step's loads keeps the compiler from folding the loop-carried loads back
+// into one load per step at the point of use.
+constexpr int kPD = 4;
+
+// L X = R for the nr right-hand sides S.row(b), b < nr, in place: wave w
+// takes right-hand sides w, w + NW and w + 2 NW.  Column k of L, below row k,
+// is read from the packed rows (L[tri(i) + k]).
+__device__ __forceinline__ void fwd_wave(const St &S, int n, int nr) {
+  const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  if (wave < nr) {
+    int rbase[3];
+    double rd[3], xv[3][3];
+    static_for<0, 3>([&](auto Mc) {
+      constexpr int m = decltype(Mc)::value;
+      const int i = lane + 64 * m;
+      rbase[m] = i < n ? tri(i) : 0;  // rows past n read row 0's area (the value is not used)
+      rd[m] = i < n ? 1.0 / S.L[rbase[m] + i] : 0.0;
+      static_for<0, 3>([&](auto Qc) {
+        constexpr int q = decltype(Qc)::value;
+        const int b = wave + NW * q;
+        xv[q][m] = (b < nr && i < n) ? S.row(b)[i] : 0.0;
+      });
+    });
+    static_for<0, 3>([&](auto Mc) {
+      constexpr int M = decltype(Mc)::value;
+      const int k0 = 64 * M, k1 = n < 64 * M + 64 ? n : 64 * M + 64;
+      if (k0 < k1) {
+        double ring[kPD][3];
+        static_for<0, kPD>([&](auto Pc) {
+          constexpr int j = decltype(Pc)::value;
+          const int kc = k0 + j < k1 ? k0 + j : k1 - 1;
+          static_for<0, 3>([&](auto Rc) {
+            constexpr int m = decltype(Rc)::value;
+            ring[j][m] = m >= M ? S.L[rbase[m] + kc] : 0.0;
+          });
+        });
+        // step k applies column k, held in ring slot k % kPD, then refills the
+        // slot with column k + kPD (full trips of kPD steps; the last few steps
+        // take no refill, so no step is conditional inside a trip)
+        auto step = [&](int k, double(&slot)[3], auto refill) __attribute__((always_inline)) {
+          const int kl = k - 64 * M;
+          double lc[3];
+          static_for<M, 3>([&](auto Rc) {
+            constexpr int m = decltype(Rc)::value;
+            lc[m] = ((m > M || lane > kl) && lane + 64 * m < n) ? slot[m] : 0.0;
+          });
+          if constexpr (decltype(refill)::value) {
+            const int kn = k + kPD < k1 ? k + kPD : k1 - 1;
+            static_for<M, 3>([&](auto Rc) {
+              constexpr int m = decltype(Rc)::value;
+              slot[m] = S.L[rbase[m] + kn];
+            });
+            asm volatile("" ::: "memory");
+          }
+          static_for<0, 3>([&](auto Qc) {
+            constexpr int q = decltype(Qc)::value;
+            if (wave + NW * q < nr) {
+              const double xk = rl(xv[q][M] * rd[M], kl);
+              static_for<M, 3>([&](auto Rc) {
+                constexpr int m = decltype(Rc)::value;
+                xv[q][m] = fma(-lc[m], xk, xv[q][m]);
+              });
+            }
+          });
+        };
+        int k = k0;
+        for (; k + kPD <= k1; k += kPD)
+          static_for<0, kPD>([&](auto Pc) { step(k + decltype(Pc)::value, ring[decltype(Pc)::value], std::true_type{}); });
+        static_for<0, kPD - 1>([&](auto Pc) {
+          constexpr int j = decltype(Pc)::value;
+          if (k + j < k1) step(k + j, ring[j], std::false_type{});
+        });
+      }
+    });
+    static_for<0, 3>([&](auto Mc) {
+      constexpr int m = decltype(Mc)::value;
+      const int i = lane + 64 * m;
+      static_for<0, 3>([&](auto Qc) {
+        constexpr int q = decltype(Qc)::value;
+        const int b = wave + NW * q;
+        if (b < nr && i < n) S.row(b)[i] = xv[q][m] * rd[m];
+      });
+    });
+  }
+  __syncthreads();
+}
+
+// L^T x = r in place for the vector x, in wave 0.  Column k of L^T is row k
+// of L, contiguous in the packed factor.
+__device__ __forceinline__ void bwd_wave(const St &S, int n, double *x) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave == 0) {
+    double rd[3], xv[3];
+    static_for<0, 3>([&](auto Mc) {
+      constexpr int m = decltype(Mc)::value;
+      const int i = lane + 64 * m;
+      rd[m] = i < n ? 1.0 / S.L[tri(i) + i] : 0.0;
+      xv[m] = i < n ? x[i] : 0.0;
+    });
+    static_for<0, 3>([&](auto Mc) {
+      constexpr int M = 2 - decltype(Mc)::value;
+      const int kt = 64 * M, k1 = (n < 64 * M + 64 ? n : 64 * M + 64) - 1;
+      if (k1 >= kt) {
+        // row k of L at the lanes' columns (columns at or past k read the
+        // row's first entry; the value is not used)
+        auto load_row = [&](int k, double(&slot)[3]) __attribute__((always_inline)) {
+          static_for<0, M + 1>([&](auto Rc) {
+            constexpr int m = decltype(Rc)::value;
+            slot[m] = S.L[tri(k) + (m < M || lane < k - kt ? lane + 64 * m : 0)];
+          });
+        };
+        double ring[kPD][3];
+        static_for<0, kPD>([&](auto Pc) {
+          constexpr int j = decltype(Pc)::value;
+          load_row(k1 - j >= kt ? k1 - j : kt, ring[j]);
+        });
+        auto step = [&](int k, double(&slot)[3], auto refill) __attribute__((always_inline)) {
+          const int kl = k - kt;
+          double use[3];
+          static_for<0, M + 1>([&](auto Rc) {
+            constexpr int m = decltype(Rc)::value;
+            use[m] = slot[m];
+          });
+          if constexpr (decltype(refill)::value) {
+            load_row(k - kPD >= kt ? k - kPD : kt, slot);
+            asm volatile("" ::: "memory");
+          }
+          const double xk = rl(xv[M] * rd[M], kl);
+          static_for<0, M>([&](auto Rc) {
+            constexpr int m = decltype(Rc)::value;
+            xv[m] = fma(-use[m], xk, xv[m]);
+          });
+          const double l = lane < kl ? use[M] : 0.0;
+          xv[M] = fma(-l, xk, xv[M]);
+        };
+        int k = k1;
+        for (; k - (kPD - 1) >= kt; k -= kPD)
+          static_for<0, kPD>([&](auto Pc) { step(k - decltype(Pc)::value, ring[decltype(Pc)::value], std::true_type{}); });
+        static_for<0, kPD - 1>([&](auto Pc) {
+          constexpr int j = decltype(Pc)::value;
+          if (k - j >= kt) step(k - j, ring[j], std::false_type{});
+        });
+      }
+    });
+    static_for<0, 3>([&](auto Mc) {
+      constexpr int m = decltype(Mc)::value;
+      const int i = lane + 64 * m;
+      if (i < n) x[i] = xv[m] * rd[m];
+    });
+  }
+  __syncthreads();
+}
+
+// Forward and backward solves: one wave when the factor is in LDS and small
+// enough, else the blocked form.
+__device__ __forceinline__ void fwd_solve(const St &S, int n, int nr) {
+  if (S.lds && n <= kWaveRows)
+    fwd_wave(S, n, nr);
+  else
+    fwd_blk(S, n, nr);
+}
+__device__ __forceinline__ void bwd_solve(const St &S, int n, double *x) {
+  if (S.lds && n <= kWaveRows)
+    bwd_wave(S, n, x);
+  else
+    bwd_blk(S, n, x);
+}
+
 // ---- gradient of the zero variables ---------------------------------------
 
 // u_snap = u, g_snap = g (rows 9 and 10)
@@ -519,6 +703,55 @@ __device__ __forceinline__ void remove_at(const St &S, int q) {
   }
   __syncthreads();
   // rank-one update: L' L'^T = L L^T + x x^T on positions q..n2-1
+  if (S.lds && n2 <= kWaveRows) {
+    // in wave 0: rotation k comes from (L_kk, x_k), read from lane k's
+    // registers, and turns column k of every row below it at once
+    if (wave == 0) {
+      int rbase[3];
+      double xv[3], yl[3];
+      static_for<0, 3>([&](auto Mc) {
+        constexpr int m = decltype(Mc)::value;
+        const int i = lane + 64 * m;
+        const bool act = i >= q && i < n2;
+        rbase[m] = act ? tri(i) : 0;
+        xv[m] = act ? xc[i] : 0.0;
+        yl[m] = act ? yv[i] : 0.0;
+      });
+      static_for<0, 3>([&](auto Mc) {
+        constexpr int M = decltype(Mc)::value;
+        const int k1 = n2 < 64 * M + 64 ? n2 : 64 * M + 64;
+        for (int k = q > 64 * M ? q : 64 * M; k < k1; ++k) {
+          const int kl = k - 64 * M;
+          const int dk = tri(k) + k;
+          const double lkk = S.L[dk];
+          const double xk = rl(xv[M], kl);
+          const double t2 = fma(lkk, lkk, xk * xk);
+          const double ri = rsqrt(t2);
+          const double c = lkk * ri, s = xk * ri;
+          const double yk = rl(yl[M], kl);
+          if (lane == kl) {
+            yl[M] = fma(c, yk, s * z);
+            S.L[dk] = t2 * ri;
+          }
+          z = fma(c, z, -s * yk);
+          static_for<M, 3>([&](auto Rc) {
+            constexpr int m = decltype(Rc)::value;
+            if ((m > M || lane > kl) && lane + 64 * m < n2) {
+              const double l = S.L[rbase[m] + k];
+              S.L[rbase[m] + k] = fma(c, l, s * xv[m]);
+              xv[m] = fma(c, xv[m], -s * l);
+            }
+          });
+        }
+      });
+      static_for<0, 3>([&](auto Mc) {
+        constexpr int m = decltype(Mc)::value;
+        const int i = lane + 64 * m;
+        if (i >= q && i < n2) yv[i] = yl[m];
+      });
+    }
+    __syncthreads();
+  } else
   for (int k0 = q; k0 < n2; k0 += TB) {
     const int e = n2 - k0 < TB ? n2 - k0 : TB;
     if (wave == 0 && lane < TB) {
@@ -634,7 +867,7 @@ __device__ __forceinline__ void block_append(const St &S, const double *G, int64
     bk->Gc[(tid / nc) * NB + tid % nc] = G[int64_t(j1) * ld + j2] / (S.dg[j1] * S.dg[j2]);
   }
   __syncthreads();
-  if (np0 > 0) fwd_blk(S, np0, nc + 1);
+  if (np0 > 0) fwd_solve(S, np0, nc + 1);
   // dots[b1][b2] = <rhs_b1, rhs_b2> over the old positions, b2 <= b1 (one wave per pair)
   const int npair = (nc + 1) * (nc + 2) / 2;
   for (int pr = wave; pr < npair; pr += NW) {
@@ -761,7 +994,7 @@ __device__ __forceinline__ void settle(const St &S, int p, bool have_y, bool sin
   if (!have_y) {
     for (int k = tid; k < bk->np; k += NT) S.x0[k] = S.g[S.plist[k]];
     __syncthreads();
-    fwd_blk(S, bk->np, 1);
+    fwd_solve(S, bk->np, 1);
   }
   for (int k = tid; k < bk->np; k += NT) S.yv[k] = S.x0[k];
   for (int guard = 0; guard < 4 * S.mp + 8; ++guard) {
@@ -770,7 +1003,7 @@ __device__ __forceinline__ void settle(const St &S, int p, bool have_y, bool sin
     if (np == 0) break;
     for (int k = tid; k < np; k += NT) S.x0[k] = S.yv[k];
     __syncthreads();
-    bwd_blk(S, np, S.x0);  // x0 = Gs_PP^-1 g_P: the step to the free-set optimum
+    bwd_solve(S, np, S.x0);  // x0 = Gs_PP^-1 g_P: the step to the free-set optimum
     int ndrop = 0;
     double best = INFINITY;
     int kb = -1;

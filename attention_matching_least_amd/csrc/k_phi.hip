@@ -72,18 +72,33 @@ __global__ void k_fill_i32(int32_t *p, int64_t count, int32_t v) {
 }
 
 // ---------------------------------------------------------------------------
-// logit maximum: one partial per (head, 128 queries), bf16 MFMA 16x16x32
+// logit maximum: one partial per (head, 128 queries), bf16 MFMA 16x16x32.
+// Blocks map to heads XCD by XCD when xcd_map is set (H a multiple of 8), so
+// that the blocks of one head read its keys through one L2.
 // ---------------------------------------------------------------------------
 template <int D, bool BF16>
-__global__ __launch_bounds__(256) void k_shift(const HeadDesc *__restrict__ desc, const void *__restrict__ Q,
-                                               const void *__restrict__ K, const float *__restrict__ beta_in,
-                                               float scale, float *__restrict__ shift_part) {
+__global__ __launch_bounds__(256) void k_shift(const HeadDesc *__restrict__ desc, int H, int nsb, int xcd_map,
+                                               const void *__restrict__ Q, const void *__restrict__ K,
+                                               const float *__restrict__ beta_in, float scale,
+                                               float *__restrict__ shift_part) {
   constexpr int KC = D / 32;
   constexpr int KSTR = D + 8;  // bf16 elements per LDS row (16-byte pad)
   __shared__ __attribute__((aligned(16))) uint16_t ks[64 * KSTR];
   __shared__ float red[4];
-  const HeadDesc Dh = desc[blockIdx.y];
-  const int blk = blockIdx.x;
+  int h, blk;
+  {
+    const int b = blockIdx.x;
+    if (xcd_map) {
+      const int x = b & 7, slot = b >> 3;
+      h = x + 8 * (slot / nsb);
+      blk = slot % nsb;
+    } else {
+      h = b / nsb;
+      blk = b % nsb;
+    }
+  }
+  if (h >= H) return;
+  const HeadDesc Dh = desc[h];
   if (blk >= Dh.n_sblk) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
@@ -1268,19 +1283,19 @@ hipError_t launch_fill_i32(int32_t *p, int64_t count, int32_t value, hipStream_t
 }
 
 hipError_t launch_shift(const Dims &dm, const Buffers &b, hipStream_t s) {
-  dim3 grid(unsigned(dm.max_sblk), unsigned(dm.H));
+  const int nsb = int(dm.max_sblk);
+  const int xcd_map = (dm.H % 8 == 0) ? 1 : 0;
+  dim3 grid(unsigned(nsb * dm.H));
   const float sc = float(dm.scale);
+#define AMC_SHIFT_ARGS b.desc, dm.H, nsb, xcd_map, b.Q, b.K, b.beta_in, sc, b.shift_part
   if (dm.d == 128) {
-    if (dm.in_bf16)
-      hipLaunchKernelGGL((k_shift<128, true>), grid, dim3(256), 0, s, b.desc, b.Q, b.K, b.beta_in, sc, b.shift_part);
-    else
-      hipLaunchKernelGGL((k_shift<128, false>), grid, dim3(256), 0, s, b.desc, b.Q, b.K, b.beta_in, sc, b.shift_part);
+    if (dm.in_bf16) hipLaunchKernelGGL((k_shift<128, true>), grid, dim3(256), 0, s, AMC_SHIFT_ARGS);
+    else hipLaunchKernelGGL((k_shift<128, false>), grid, dim3(256), 0, s, AMC_SHIFT_ARGS);
   } else {
-    if (dm.in_bf16)
-      hipLaunchKernelGGL((k_shift<64, true>), grid, dim3(256), 0, s, b.desc, b.Q, b.K, b.beta_in, sc, b.shift_part);
-    else
-      hipLaunchKernelGGL((k_shift<64, false>), grid, dim3(256), 0, s, b.desc, b.Q, b.K, b.beta_in, sc, b.shift_part);
+    if (dm.in_bf16) hipLaunchKernelGGL((k_shift<64, true>), grid, dim3(256), 0, s, AMC_SHIFT_ARGS);
+    else hipLaunchKernelGGL((k_shift<64, false>), grid, dim3(256), 0, s, AMC_SHIFT_ARGS);
   }
+#undef AMC_SHIFT_ARGS
   return hipGetLastError();
 }
 

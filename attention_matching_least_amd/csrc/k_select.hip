@@ -22,6 +22,8 @@
 // k*R keys of a single sweep; the sweep runs once per cycle.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
+
 #include <cfloat>
 #include <climits>
 #include <cmath>
@@ -475,17 +477,65 @@ __global__ __launch_bounds__(256) void k_merge(const HeadDesc *__restrict__ desc
 // where e_j covers the float32 accumulation of P and N (same-sign sums, so a
 // relative error of (terms per accumulator + 2) 2^-24 each), the float32
 // rounding of Phi and of r, the float64 rescoring's own rounding, and an
-// absolute term for values below float32's normal range.  Each lane keeps 8
-// float32 accumulators per sign (one per query of its 16-byte loads: ldN / 64
-// terms each); a key's 8 lanes meet in float64.
+// absolute term for values below float32's normal range.  A key's 8 lanes
+// take 16 consecutive queries of every 128 each; a lane keeps 8 float32
+// accumulators per sign (two of its 16 queries per block: ldN / 64 terms
+// each), and the lanes meet in float64.
 // The keys: every key on the first cycle (which also writes each key's
-// high-plane sums over 128-query blocks, rounded down, for the pruning), else
-// the cycle's survivor list (or every key when the list is off).  One block =
-// 32 of them (4 waves of 8), so that a short list still spreads over the
-// chip.  Out, per listed key: its upper and lower bound (sw_up, sw_lo; -inf
-// for a selected key) and the key (sw_key), at its place in the list.
+// high-plane sums over 128-query blocks, rounded down, for the pruning, and
+// the 8-bit plane of the second pruning stage), else the cycle's survivor list
+// (or every key when the list is off), in groups of 32 (4 waves of 8).  A
+// block takes every gridDim.x-th group of its head's list: one group per block
+// on the first cycle, after it a few blocks per head, each staging r once for
+// all of its groups (the lists are short, and most of a grid sized for every
+// key would find nothing to do).  Out, per listed key: its upper and lower
+// bound (sw_up, sw_lo; -inf for a selected key) and the key (sw_key), at its
+// place in the list.
 // ---------------------------------------------------------------------------
 constexpr int SB_KEYS = 32;  // keys per block of the bounded sweep
+
+// ---------------------------------------------------------------------------
+// 8-bit plane.  The grid g(c) = the float32 with bits Q8_BASE + c 2^20, c =
+// 0..254: 2^-31 (1 + m/8) 2^e, three significand bits, up to 1.75.  The code
+// of a value h of the high plane is the smallest c with g(c) >= next(h), the
+// bfloat16 above h; since Phi < next(h) (the plane truncates the float32 Phi,
+// which is within 2^-24 of Phi), g(c) bounds Phi from above.  From below,
+// Phi >= g(c - 2) for c >= 2: [h, next(h)] spans less than one step of the
+// grid, so g(c - 1) < next(h) puts g(c - 2) below h (1 - 2^-24).  Two codes
+// apart the grid values differ by at most 4/5 (1.25 against 1.0), so Phi >=
+// (51/64) g(c) for c >= 2, and Phi >= 0 > (51/64) g(c) - 2^-31 for c < 2.
+// In bfloat16 bits hb: c = ceil((hb + 1 - Q8_BASE / 2^16) / 16).  A value that
+// would need code 255 (h >= 1.75, which a shifted Phi never reaches) marks the
+// head's plane unusable.
+// ---------------------------------------------------------------------------
+constexpr uint32_t Q8_BASE = 96u << 23;   // bits of 2^-31
+constexpr int Q8_HB_OFF = (96 << 7) - 16;  // hb - this, over 16, rounded down, is the code
+constexpr float Q8_KAPPA = 51.0f / 64.0f;  // g(c - 2) >= Q8_KAPPA g(c)
+
+typedef short s16x2 __attribute__((ext_vector_type(2)));
+
+// codes of the two bfloat16 values packed in w (low half first), one per
+// 16-bit half; hmax keeps the largest raw value for the range check
+__device__ __forceinline__ uint32_t q8_codes2(uint32_t w, s16x2 &hmax) {
+  s16x2 v = __builtin_bit_cast(s16x2, w);
+  hmax = hmax > v ? hmax : v;
+  // (values below the grid, sign bit included, take code 0)
+  const s16x2 off = {short(Q8_HB_OFF), short(Q8_HB_OFF)}, top = {254, 254};
+  v = v > off ? v : off;
+  s16x2 c = (v - off) >> short(4);
+  c = c < top ? c : top;
+  return __builtin_bit_cast(uint32_t, c);
+}
+
+typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+// eight codes of a 16-byte load of the high plane (queries in order), as 8 bytes
+__device__ __forceinline__ u32x2v q8_pack8(const u32x4 &xv, s16x2 &hmax) {
+  const uint32_t a = q8_codes2(xv.x, hmax), b = q8_codes2(xv.y, hmax);
+  const uint32_t c = q8_codes2(xv.z, hmax), d = q8_codes2(xv.w, hmax);
+  // bytes 0 and 2 of each code pair
+  return u32x2v{__builtin_amdgcn_perm(b, a, 0x06040200u), __builtin_amdgcn_perm(d, c, 0x06040200u)};
+}
 
 template <bool FIRST>
 __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__ desc,
@@ -495,105 +545,316 @@ __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__
                                                     const int32_t *__restrict__ surv_cnt,
                                                     const int32_t *__restrict__ sel_slot, int cycle, int kR,
                                                     int64_t qb128, float *__restrict__ colsum,
+                                                    uint8_t *__restrict__ q8, int32_t *__restrict__ q8_bad,
                                                     double *__restrict__ sw_up, double *__restrict__ sw_lo,
                                                     int32_t *__restrict__ sw_key) {
   extern __shared__ __attribute__((aligned(16))) float s_rpn[];  // (r+, r-) per query, ldN of them
   const int h = blockIdx.y;
   const HeadDesc D = desc[h];
-  const int blk = blockIdx.x;
   int64_t S0;
   const int Kc = cycle_keys(D, cycle, kR, &S0);
   if (Kc == 0) return;
   const int list = FIRST ? -1 : surv_cnt[h];
   const int64_t cnt = list < 0 ? D.T : list;
-  if (int64_t(blk) * SB_KEYS >= cnt) return;
+  if (int64_t(blockIdx.x) * SB_KEYS >= cnt) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int kq = lane >> 3, sub = lane & 7;
+  // (r+, r-) of query 128 i + 16 sb + 2 j + e at 16-byte slot 64 i + 8 j + sb,
+  // half e: the 8 lanes of a key read 128 consecutive bytes
   for (int64_t q = tid; q < D.ldN; q += 256) {
     float2 v = make_float2(0.0f, 0.0f);
     if (q < D.n) v = *reinterpret_cast<const float2 *>(rpn + 2 * (D.n_off + q));
-    *reinterpret_cast<float2 *>(s_rpn + 2 * q) = v;
+    const int64_t i = q >> 7, sb = (q >> 4) & 7, j = (q >> 1) & 7, e = q & 1;
+    *reinterpret_cast<float2 *>(s_rpn + 4 * (64 * i + 8 * j + sb) + 2 * e) = v;
   }
   __syncthreads();
-  const int64_t at = int64_t(blk) * SB_KEYS + 8 * wave + kq;
-  int64_t key = -1;
-  if (at < cnt) key = list < 0 ? at : int64_t(surv_list[D.kt_off + at]);
-  const uint16_t *hp = phi16 + 2 * D.phi_off + (key < 0 ? 0 : key) * D.ldN + 8 * sub;
-  const int nit = int(D.ldN >> 6);
-  float P[8], N[8];
+  const int nb = int(D.ldN >> 7);                   // full 128-query blocks
+  const bool half = (D.ldN & 64) != 0 && sub < 4;  // this lane's part of a last 64-query block
+  const double rs = rabs[h];
+  // the block's keys: groups of SB_KEYS, gridDim.x apart in the list
+  for (int64_t kb = blockIdx.x; kb * SB_KEYS < cnt; kb += gridDim.x) {
+    const int64_t at = kb * SB_KEYS + 8 * wave + kq;
+    int64_t key = -1;
+    if (at < cnt) key = list < 0 ? at : int64_t(surv_list[D.kt_off + at]);
+    // lane sub: queries 16 sub .. 16 sub + 15 of every 128 (two 16-byte loads)
+    const uint16_t *hp = phi16 + 2 * D.phi_off + (key < 0 ? 0 : key) * D.ldN + 16 * sub;
+    float P[8], N[8];
 #pragma unroll
-  for (int e = 0; e < 8; ++e) P[e] = N[e] = 0.0f;
-  auto step = [&](int i, const u32x4 &xv) __attribute__((always_inline)) {
-    const f32x4 *rr = reinterpret_cast<const f32x4 *>(s_rpn + 2 * (64 * i + 8 * sub));
-    const uint32_t w[4] = {xv.x, xv.y, xv.z, xv.w};
+    for (int e = 0; e < 8; ++e) P[e] = N[e] = 0.0f;
+    auto step = [&](int b, const u32x4 &xa, const u32x4 &xb) __attribute__((always_inline)) {
+      const f32x4 *ww = reinterpret_cast<const f32x4 *>(s_rpn) + 64 * b + sub;
+      const uint32_t w[8] = {xa.x, xa.y, xa.z, xa.w, xb.x, xb.y, xb.z, xb.w};
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const f32x4 pr = rr[c];  // (r+, r-) of queries 2 c and 2 c + 1
-      const float v0 = __uint_as_float(w[c] << 16);
-      const float v1 = __uint_as_float(w[c] & 0xffff0000u);
-      P[2 * c] = fmaf(pr.x, v0, P[2 * c]);
-      N[2 * c] = fmaf(pr.y, v0, N[2 * c]);
-      P[2 * c + 1] = fmaf(pr.z, v1, P[2 * c + 1]);
-      N[2 * c + 1] = fmaf(pr.w, v1, N[2 * c + 1]);
-    }
-  };
-  // FIRST: the high-plane sum of 128-query block b from this lane's 16 values
-  // of it (two loads).  The float32 lane sums of 16 positive terms are within
-  // 2^-20 of exact: scaled down by that much and rounded down, the stored sum
-  // is at most the exact one and at least (1 - 2^-18.9) of it.
-  auto hsum = [&](const u32x4 &a, const u32x4 &b) __attribute__((always_inline)) {
-    float t = 0.0f;
-    const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-#pragma unroll
-    for (int c = 0; c < 8; ++c) t += __uint_as_float(w[c] << 16) + __uint_as_float(w[c] & 0xffff0000u);
-    return t;
-  };
-  auto put_sum = [&](int blk128, float t) __attribute__((always_inline)) {
-    const double bs = sum8_lanes(double(t));
-    if (sub == 0) colsum[(D.kt_off + key) * qb128 + blk128] = __double2float_rd(bs * (1.0 - 0x1p-20));
-  };
-  if (key >= 0) {
-    // sixteen 16-byte loads in flight per lane
-    int i = 0;
-    for (; i + 16 <= nit; i += 16) {
-      u32x4 xv[16];
-#pragma unroll
-      for (int u = 0; u < 16; ++u) xv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 64 * (i + u)));
-      __builtin_amdgcn_sched_barrier(0);  // all sixteen issue before any is used
-#pragma unroll
-      for (int u = 0; u < 16; ++u) step(i + u, xv[u]);
-      if constexpr (FIRST) {
-#pragma unroll
-        for (int u = 0; u < 16; u += 2) put_sum((i + u) >> 1, hsum(xv[u], xv[u + 1]));
+      for (int j = 0; j < 8; ++j) {
+        const f32x4 pr = ww[8 * j];  // (r+, r-) of the lane's queries 2 j and 2 j + 1
+        const float v0 = __uint_as_float(w[j] << 16);
+        const float v1 = __uint_as_float(w[j] & 0xffff0000u);
+        const int e = (2 * j) & 7;
+        P[e] = fmaf(pr.x, v0, P[e]);
+        N[e] = fmaf(pr.y, v0, N[e]);
+        P[e + 1] = fmaf(pr.z, v1, P[e + 1]);
+        N[e + 1] = fmaf(pr.w, v1, N[e + 1]);
       }
-    }
-    for (; i < nit; i += 2) {
-      const u32x4 x0 = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 64 * i));
-      const u32x4 x1 = i + 1 < nit ? __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 64 * (i + 1)))
-                                   : u32x4{0u, 0u, 0u, 0u};
-      step(i, x0);
-      if (i + 1 < nit) step(i + 1, x1);
-      if constexpr (FIRST) put_sum(i >> 1, hsum(x0, x1));
-    }
-  }
-  double Pd = 0.0, Nd = 0.0;
+    };
+    // FIRST: the high-plane sum of 128-query block b from this lane's 16 values
+    // of it.  The float32 lane sums of 16 positive terms are within 2^-20 of
+    // exact: scaled down by that much and rounded down, the stored sum is at
+    // most the exact one and at least (1 - 2^-18.9) of it.
+    auto hsum = [&](const u32x4 &a, const u32x4 &b) __attribute__((always_inline)) {
+      float t = 0.0f;
+      const uint32_t w[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
 #pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    Pd += double(P[e]);
-    Nd += double(N[e]);
+      for (int c = 0; c < 8; ++c) t += __uint_as_float(w[c] << 16) + __uint_as_float(w[c] & 0xffff0000u);
+      return t;
+    };
+    // FIRST with the 8-bit plane: the codes of the lane's 16 queries of a block
+    // (128 consecutive bytes per key from its 8 lanes)
+    s16x2 hmax = {0, 0};
+    u32x4 *q8p = (FIRST && q8) ? reinterpret_cast<u32x4 *>(q8 + D.phi_off + (key < 0 ? 0 : key) * D.ldN + 16 * sub)
+                               : nullptr;
+    auto block = [&](int b, const u32x4 &xa, const u32x4 &xb) __attribute__((always_inline)) {
+      step(b, xa, xb);
+      if constexpr (FIRST) {
+        const double bs = sum8_lanes(double(hsum(xa, xb)));
+        if (sub == 0) colsum[(D.kt_off + key) * qb128 + b] = __double2float_rd(bs * (1.0 - 0x1p-20));
+        if (q8p) {
+          const u32x2v ca = q8_pack8(xa, hmax), cb = q8_pack8(xb, hmax);
+          q8p[8 * b] = u32x4{ca.x, ca.y, cb.x, cb.y};
+        }
+      }
+    };
+    if (key >= 0) {
+      // sixteen 16-byte loads (eight blocks) in flight per lane; eight on the
+      // first cycle, whose blocks also do the sums and the 8-bit codes
+      constexpr int NBL = FIRST ? 4 : 8;
+      int b = 0;
+      for (; b + NBL <= nb; b += NBL) {
+        u32x4 xv[2 * NBL];
+#pragma unroll
+        for (int u = 0; u < NBL; ++u) {
+          xv[2 * u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 128 * (b + u)));
+          xv[2 * u + 1] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 128 * (b + u) + 8));
+        }
+        __builtin_amdgcn_sched_barrier(0);  // all of them issue before any is used
+#pragma unroll
+        for (int u = 0; u < NBL; ++u) block(b + u, xv[2 * u], xv[2 * u + 1]);
+      }
+      for (; b < nb; ++b)
+        block(b, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 128 * b)),
+              __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 128 * b + 8)));
+    }
+    // a last 64-query block: lanes 0..3 hold its queries, the others add zeros
+    if ((D.ldN & 64) != 0) {
+      u32x4 xa = {0u, 0u, 0u, 0u}, xb = {0u, 0u, 0u, 0u};
+      if (key >= 0 && half) {
+        xa = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 128 * nb));
+        xb = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(hp + 128 * nb + 8));
+      }
+      if constexpr (FIRST) {
+        const double bs = sum8_lanes(double(hsum(xa, xb)));
+        if (sub == 0 && key >= 0) colsum[(D.kt_off + key) * qb128 + nb] = __double2float_rd(bs * (1.0 - 0x1p-20));
+        if (q8p && key >= 0 && half) {
+          const u32x2v ca = q8_pack8(xa, hmax), cb = q8_pack8(xb, hmax);
+          q8p[8 * nb] = u32x4{ca.x, ca.y, cb.x, cb.y};
+        }
+      }
+      if (key >= 0 && half) step(nb, xa, xb);
+    }
+    if (FIRST && q8p && key >= 0 &&
+        (hmax.x >= short(Q8_HB_OFF + 16 * 255) || hmax.y >= short(Q8_HB_OFF + 16 * 255)))
+      q8_bad[h] = 1;
+    double Pd = 0.0, Nd = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      Pd += double(P[e]);
+      Nd += double(N[e]);
+    }
+    Pd = sum8_lanes(Pd);
+    Nd = sum8_lanes(Nd);
+    if (sub == 0 && key >= 0) {
+      const bool valid = key < D.T && sel_slot[D.k_off + key] == 0;
+      const double crel = 2.0 * (double(D.ldN >> 6) + 16.0) * 0x1p-24 + 0x1p-22;
+      const double slack = crel * (Pd - Nd) + (rs + double(D.n)) * 0x1p-120;
+      const double c7 = 0x1.00001p-7;
+      sw_up[D.kt_off + at] = valid ? (Pd + Nd) + c7 * Pd + slack : -INFINITY;
+      sw_lo[D.kt_off + at] = valid ? (Pd + Nd) + c7 * Nd - slack : -INFINITY;
+      sw_key[D.kt_off + at] = int(key);
+    }
   }
-  Pd = sum8_lanes(Pd);
-  Nd = sum8_lanes(Nd);
-  if (sub == 0 && key >= 0) {
-    const bool valid = key < D.T && sel_slot[D.k_off + key] == 0;
-    const double rs = rabs[h];
-    const double crel = 2.0 * (double(nit) + 16.0) * 0x1p-24 + 0x1p-22;
-    const double slack = crel * (Pd - Nd) + (rs + double(D.n)) * 0x1p-120;
-    const double c7 = 0x1.00001p-7;
-    sw_up[D.kt_off + at] = valid ? (Pd + Nd) + c7 * Pd + slack : -INFINITY;
-    sw_lo[D.kt_off + at] = valid ? (Pd + Nd) + c7 * Nd - slack : -INFINITY;
-    sw_key[D.kt_off + at] = int(key);
+}
+
+// ---------------------------------------------------------------------------
+// Second pruning stage, between k_prune and the bounded sweep: for each key of
+// the survivor list an upper bound of r^T Phi[:, k] from the 8-bit plane,
+//   U8_k = sum_{r_q > 0} r_q g(c_qk) + (51/64) sum_{r_q < 0} r_q g(c_qk)
+//          + 2^-31 sum |r|
+// (Phi <= g(c), Phi >= (51/64) g(c) less 2^-31 where c < 2), plus the
+// float32 accumulation, rounding and underflow allowances of the bounded
+// sweep (the product (51/64) r- is rounded to float32 once more).  Nothing is
+// done where k_prune kept every key (its L is -inf) or the plane is unusable.
+// Groups of 64 keys (8 waves of 8), 8 lanes per key, each lane 16 queries of
+// every 128 (one 16-byte load), sixteen loads in flight; a block takes every
+// gridDim.x-th group of its head's list.  The (r+, (51/64) r-) pairs sit in
+// LDS lane-interleaved: pair j of lane sub's 16 queries of 128-query block i
+// at 16-byte slot 64 i + 8 j + sub, so the 8 lanes of a key read 128
+// consecutive bytes.  Out: sw_up and sw_key at the key's place in the list
+// (-inf for a selected key).
+// ---------------------------------------------------------------------------
+constexpr int Q8_KEYS = 64;
+constexpr int Q8_THREADS = 512;
+
+__global__ __launch_bounds__(Q8_THREADS) void k_sweep_q8(const HeadDesc *__restrict__ desc,
+                                                         const uint8_t *__restrict__ q8,
+                                                         const float *__restrict__ rpn,
+                                                         const double *__restrict__ rabs,
+                                                         const double *__restrict__ prune_L,
+                                                         const int32_t *__restrict__ q8_bad,
+                                                         const int32_t *__restrict__ surv_list,
+                                                         const int32_t *__restrict__ surv_cnt,
+                                                         const int32_t *__restrict__ sel_slot, int cycle, int kR,
+                                                         double *__restrict__ sw_up, int32_t *__restrict__ sw_key) {
+  extern __shared__ __attribute__((aligned(16))) float s_w[];  // (r+, (51/64) r-) pairs, 2 per 16-byte slot
+  const int h = blockIdx.y;
+  const HeadDesc D = desc[h];
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0 || q8_bad[h] || prune_L[h] == -INFINITY) return;
+  const int list = surv_cnt[h];
+  const int64_t cnt = list < 0 ? D.T : list;
+  if (int64_t(blockIdx.x) * Q8_KEYS >= cnt) return;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int kq = lane >> 3, sub = lane & 7;
+  // query q = 128 i + 16 sb + 2 j + e  ->  float2 at slot 64 i + 8 j + sb, half e
+  for (int64_t q = tid; q < D.ldN; q += Q8_THREADS) {
+    float2 v = make_float2(0.0f, 0.0f);
+    if (q < D.n) v = *reinterpret_cast<const float2 *>(rpn + 2 * (D.n_off + q));
+    v.y *= Q8_KAPPA;
+    const int64_t i = q >> 7, sb = (q >> 4) & 7, j = (q >> 1) & 7, e = q & 1;
+    *reinterpret_cast<float2 *>(s_w + 4 * (64 * i + 8 * j + sb) + 2 * e) = v;
+  }
+  __syncthreads();
+  const int nit = int(D.ldN >> 7);                      // full 128-query steps
+  const bool half = (D.ldN & 64) != 0 && 16 * sub < 64;  // this lane's part of a last 64-query step
+  const double rs = rabs[h];
+  for (int64_t kb = blockIdx.x; kb * Q8_KEYS < cnt; kb += gridDim.x) {
+    const int64_t at = kb * Q8_KEYS + 8 * wave + kq;
+    int64_t key = -1;
+    if (at < cnt) key = list < 0 ? at : int64_t(surv_list[D.kt_off + at]);
+    const uint8_t *cp = q8 + D.phi_off + (key < 0 ? 0 : key) * D.ldN + 16 * sub;
+    float P[8], N[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) P[e] = N[e] = 0.0f;
+    auto step = [&](int i, const u32x4 &cv) __attribute__((always_inline)) {
+      const f32x4 *ww = reinterpret_cast<const f32x4 *>(s_w) + 64 * i + sub;
+      const uint32_t cw[4] = {cv.x, cv.y, cv.z, cv.w};
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const f32x4 w01 = ww[8 * (2 * c)], w23 = ww[8 * (2 * c + 1)];  // pairs of queries 4 c .. 4 c + 3
+        const float g0 = __uint_as_float((__builtin_amdgcn_ubfe(cw[c], 0, 8) << 20) + Q8_BASE);
+        const float g1 = __uint_as_float((__builtin_amdgcn_ubfe(cw[c], 8, 8) << 20) + Q8_BASE);
+        const float g2 = __uint_as_float((__builtin_amdgcn_ubfe(cw[c], 16, 8) << 20) + Q8_BASE);
+        const float g3 = __uint_as_float(((cw[c] >> 24) << 20) + Q8_BASE);
+        const int e = (4 * c) & 7;
+        P[e] = fmaf(w01.x, g0, P[e]);
+        N[e] = fmaf(w01.y, g0, N[e]);
+        P[e + 1] = fmaf(w01.z, g1, P[e + 1]);
+        N[e + 1] = fmaf(w01.w, g1, N[e + 1]);
+        P[e + 2] = fmaf(w23.x, g2, P[e + 2]);
+        N[e + 2] = fmaf(w23.y, g2, N[e + 2]);
+        P[e + 3] = fmaf(w23.z, g3, P[e + 3]);
+        N[e + 3] = fmaf(w23.w, g3, N[e + 3]);
+      }
+    };
+    if (key >= 0) {
+      int i = 0;
+      for (; i + 16 <= nit; i += 16) {
+        u32x4 cv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u)
+          cv[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cp + 128 * (i + u)));
+        __builtin_amdgcn_sched_barrier(0);  // all sixteen issue before any is used
+#pragma unroll
+        for (int u = 0; u < 16; ++u) step(i + u, cv[u]);
+      }
+      for (; i < nit; ++i) step(i, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cp + 128 * i)));
+      if (half) step(nit, __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(cp + 128 * nit)));
+    }
+    double Pd = 0.0, Nd = 0.0;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      Pd += double(P[e]);
+      Nd += double(N[e]);
+    }
+    Pd = sum8_lanes(Pd);
+    Nd = sum8_lanes(Nd);
+    if (sub == 0 && key >= 0) {
+      const bool valid = key < D.T && sel_slot[D.k_off + key] == 0;
+      const double crel = 2.0 * (double(D.ldN >> 6) + 16.0) * 0x1p-24 + 0x1p-21;
+      const double u = (Pd + Nd) + crel * (Pd - Nd) + rs * 0x1p-31 + (rs + double(D.n)) * 0x1p-120;
+      sw_up[D.kt_off + at] = valid ? u : -INFINITY;
+      sw_key[D.kt_off + at] = int(key);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// The keys the bounded sweep reads after the second stage: one block of 1024
+// threads per head keeps, in list order, each listed key whose U8 reaches the
+// threshold L of k_prune (a NaN bound keeps its key).  Where the stage did not
+// run the list passes through unchanged.  Trace: keys read from the 8-bit
+// plane and from the high plane this cycle.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(1024) void k_q8_compact(const HeadDesc *__restrict__ desc, int cycle, int kR,
+                                                     const double *__restrict__ prune_L,
+                                                     const int32_t *__restrict__ q8_bad,
+                                                     const int32_t *__restrict__ surv_list,
+                                                     const int32_t *__restrict__ surv_cnt,
+                                                     const double *__restrict__ sw_up,
+                                                     const int32_t *__restrict__ sw_key,
+                                                     int32_t *__restrict__ surv2_list, int32_t *__restrict__ surv2_cnt,
+                                                     int32_t *__restrict__ tr_swept, int32_t *__restrict__ tr_swept8) {
+  __shared__ int s_wc[16];
+  const int h = blockIdx.x;
+  const HeadDesc D = desc[h];
+  int64_t S0;
+  const int Kc = cycle_keys(D, cycle, kR, &S0);
+  if (Kc == 0) return;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int sc = surv_cnt[h];
+  const double L = prune_L[h];
+  if (q8_bad[h] || L == -INFINITY) {
+    for (int e = tid; e < sc; e += 1024) surv2_list[D.kt_off + e] = surv_list[D.kt_off + e];
+    if (tid == 0) {
+      surv2_cnt[h] = sc;
+      if (tr_swept8) tr_swept8[D.cyc_off + cycle] = 0;
+    }
+    return;
+  }
+  const int64_t cnt = sc < 0 ? D.T : sc;
+  int total = 0;
+  for (int64_t e0 = 0; e0 < cnt; e0 += 1024) {
+    const int64_t e = e0 + tid;
+    int key = -1;
+    if (e < cnt) {
+      const double u = sw_up[D.kt_off + e];
+      if (u != -INFINITY && !(u < L)) key = sw_key[D.kt_off + e];
+    }
+    const uint64_t m = __ballot(key >= 0);
+    if (lane == 0) s_wc[wave] = __popcll(m);
+    __syncthreads();
+    int at = total;
+    for (int w = 0; w < wave; ++w) at += s_wc[w];
+    at += __popcll(m & ((uint64_t(1) << lane) - 1));
+    if (key >= 0) surv2_list[D.kt_off + at] = key;
+    for (int w = 0; w < 16; ++w) total += s_wc[w];
+    __syncthreads();
+  }
+  if (tid == 0) {
+    surv2_cnt[h] = total;
+    if (tr_swept) tr_swept[D.cyc_off + cycle] = total;
+    if (tr_swept8) tr_swept8[D.cyc_off + cycle] = int32_t(cnt);
   }
 }
 
@@ -647,7 +908,7 @@ __global__ __launch_bounds__(PR_THREADS) void k_prune(const HeadDesc *__restrict
                                                       const float *__restrict__ colsum, int64_t qb128, int cycle,
                                                       int kR, float *__restrict__ rpn, double *__restrict__ rabs,
                                                       int32_t *__restrict__ surv_list,
-                                                      int32_t *__restrict__ surv_cnt,
+                                                      int32_t *__restrict__ surv_cnt, double *__restrict__ prune_L,
                                                       int32_t *__restrict__ tr_swept) {
   __shared__ double s_r[kStoredMaxN];
   __shared__ float s_u[PR_MAXT];
@@ -699,6 +960,7 @@ __global__ __launch_bounds__(PR_THREADS) void k_prune(const HeadDesc *__restrict
   if (keep_all) {
     if (tid == 0) {
       surv_cnt[h] = -1;
+      if (prune_L) prune_L[h] = -INFINITY;
       if (tr_swept) tr_swept[D.cyc_off + cycle] = int32_t(D.T);
     }
     return;
@@ -797,6 +1059,7 @@ __global__ __launch_bounds__(PR_THREADS) void k_prune(const HeadDesc *__restrict
   }
   if (tid == 0) {
     surv_cnt[h] = total;
+    if (prune_L) prune_L[h] = L;
     if (tr_swept) tr_swept[D.cyc_off + cycle] = total;
   }
 }
@@ -1302,11 +1565,19 @@ hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int kR, 
   return hipGetLastError();
 }
 
+// Blocks per head of the bounded sweep after the first cycle and of the
+// 8-bit stage: each loops over its share of the head's list.
+constexpr int SB_BLOCKS_Q8 = 4;   // the list after both pruning stages (about 1% of the keys)
+constexpr int SB_BLOCKS = 16;     // the list after the first stage alone
+constexpr int Q8_BLOCKS = 16;
+
 hipError_t launch_sweep_band(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
-  const dim3 grid(unsigned((dm.max_T + SB_KEYS - 1) / SB_KEYS), unsigned(dm.H));
-  const size_t lds = size_t((dm.max_n + 63) / 64 * 64) * 8;
+  const int64_t all = (dm.max_T + SB_KEYS - 1) / SB_KEYS;
+  const int64_t bph = cycle == 0 ? all : std::min<int64_t>(all, b.q8 ? SB_BLOCKS_Q8 : SB_BLOCKS);
+  const dim3 grid(unsigned(bph), unsigned(dm.H));
+  const size_t lds = size_t((dm.max_n + 127) / 128 * 128) * 8;
 #define AMC_SB_ARGS b.desc, b.phi16, b.rpn, b.rabs, b.surv_list, b.surv_cnt, b.sel_slot, cycle, kR, dm.qb128, b.colsum, \
-    b.sw_up, b.sw_lo, b.sw_key
+    b.q8, b.q8_bad, b.sw_up, b.sw_lo, b.sw_key
   if (cycle == 0) hipLaunchKernelGGL(k_sweep_band<true>, grid, dim3(256), lds, s, AMC_SB_ARGS);
   else hipLaunchKernelGGL(k_sweep_band<false>, grid, dim3(256), lds, s, AMC_SB_ARGS);
 #undef AMC_SB_ARGS
@@ -1315,7 +1586,21 @@ hipError_t launch_sweep_band(const Dims &dm, const Buffers &b, int cycle, int kR
 
 hipError_t launch_prune(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
   hipLaunchKernelGGL(k_prune, dim3(unsigned(dm.H)), dim3(PR_THREADS), 0, s, b.desc, b.r, b.sel_slot, b.phi16, b.colsum,
-                     dm.qb128, cycle, kR, b.rpn, b.rabs, b.surv_list, b.surv_cnt, b.tr_swept);
+                     dm.qb128, cycle, kR, b.rpn, b.rabs, b.surv_list, b.surv_cnt, b.prune_L, b.tr_swept);
+  return hipGetLastError();
+}
+
+hipError_t launch_sweep_q8(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  const dim3 grid(unsigned(std::min<int64_t>((dm.max_T + Q8_KEYS - 1) / Q8_KEYS, Q8_BLOCKS)), unsigned(dm.H));
+  const size_t lds = size_t((dm.max_n + 127) / 128 * 128) * 8;
+  hipLaunchKernelGGL(k_sweep_q8, grid, dim3(Q8_THREADS), lds, s, b.desc, b.q8, b.rpn, b.rabs, b.prune_L, b.q8_bad,
+                     b.surv_list, b.surv_cnt, b.sel_slot, cycle, kR, b.sw_up, b.sw_key);
+  return hipGetLastError();
+}
+
+hipError_t launch_q8_compact(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
+  hipLaunchKernelGGL(k_q8_compact, dim3(unsigned(dm.H)), dim3(1024), 0, s, b.desc, cycle, kR, b.prune_L, b.q8_bad,
+                     b.surv_list, b.surv_cnt, b.sw_up, b.sw_key, b.surv2_list, b.surv2_cnt, b.tr_swept, b.tr_swept8);
   return hipGetLastError();
 }
 

@@ -442,17 +442,23 @@ def main():
         if sw:
             # algorithmic bytes: the stored high plane's columns of the keys each bounded
             # sweep reads (every key on the first cycle, the pruning's survivors after),
-            # ldN = n rounded up to 64 queries of 2 bytes each, from the trace
+            # ldN = n rounded up to 64 queries of 2 bytes each, the 8-bit plane's columns
+            # the second pruning stage reads (1 byte per query), and the 8-bit plane the
+            # first cycle writes (every key), from the trace
             ldn = (w.n + 63) // 64 * 64
-            swept = sum(int(c.sum()) for c in kres.trace()["swept_keys"])
-            per_step = float(swept) * ldn * 2
+            ktr = kres.trace()
+            swept = sum(int(c.sum()) for c in ktr["swept_keys"])
+            swept8 = sum(int(c.sum()) for c in ktr["swept_keys8"])
+            q8_written = H * w.T if swept8 > 0 else 0
+            per_step = float(swept) * ldn * 2 + float(swept8 + q8_written) * ldn
             achieved = per_step * args.steps / (sw["total_ms"] * 1e-3) / 1e9
             found.append((sw["total_ms"], {
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("k_sweep_band"),
-                "kernel": "k_sweep_band", "avg_launch_ms": round(sw["avg_ms"], 4), "launches": sw["launches"],
+                "kernel": "k_sweep_band+k_sweep_q8", "avg_launch_ms": round(sw["avg_ms"], 4), "launches": sw["launches"],
                 "algorithmic_bytes_per_launch": per_step * args.steps / sw["launches"],
-                "swept_keys_per_step": swept, "keys_per_step_unpruned": int(sum(-(-b // kr) for b in w.budgets)) * w.T}))
+                "swept_keys_per_step": swept, "swept_keys8_per_step": swept8,
+                "keys_per_step_unpruned": int(sum(-(-b // kr) for b in w.budgets)) * w.T}))
         ph = kernels.get("phi")
         if ph and phi_ops:
             # matrix-core work of the mass features (phi_matrix_ops), int8-equivalent operations

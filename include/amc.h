@@ -154,10 +154,12 @@ typedef struct {
  *   swept_keys int32  [sum c_h]    keys whose stored Phi columns the cycle's bounded sweep
  *                                  read (T_h when every key is read; 0 when Phi is not
  *                                  stored)
+ *   swept_keys8 int32 [sum c_h]    keys whose columns of the 8-bit copy of Phi the cycle's
+ *                                  second pruning stage read (0 where it did not run)
  * where a "cycle" is the R iterations between two refits; head h has
  * c_h = ceil(t_h / (k R)) cycles (amc_cycle_offsets). */
 typedef struct {
-  uint64_t shift, pick, pick_score, weight, runner_up, nnls_iters, swept_keys;
+  uint64_t shift, pick, pick_score, weight, runner_up, nnls_iters, swept_keys, swept_keys8;
   uint64_t total_bytes;
 } amc_trace_layout;
 

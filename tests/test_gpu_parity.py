@@ -196,6 +196,37 @@ def test_band_and_exact_paths_agree(monkeypatch):
     assert torch.allclose(a.beta, b.beta, rtol=1e-5, atol=1e-5)
 
 
+@pytest.mark.parametrize("shape,k,R", [((512, 2048, 64), 4, 2), ((300, 1500, 30), 1, 1),
+                                         ((4096, 8192, 164), 4, 2)])
+def test_prune_stages_agree(monkeypatch, shape, k, R):
+    """The second pruning stage (bounds from the 8-bit copy of Phi) only drops
+    keys that cannot be among a cycle's picks, so the whole compaction is the
+    same bit for bit with and without it.  It runs from the second cycle on and
+    reads fewer keys of the 16-bit plane than the first stage alone."""
+    n, T, t = shape
+    heads = [synth.make_head([41, i], n, T, 128, True, "bf16") for i in range(2)]
+    budgets = [t, t - 5]
+    _say(f"prune stages n={n} T={T} t={t} k={k} R={R}")
+    a = _run(heads, budgets, "bf16", k, R)
+    monkeypatch.setenv("AMC_PRUNE_Q8", "0")
+    b = _run(heads, budgets, "bf16", k, R)
+    assert np.all(a.head_status.cpu().numpy() == 0)
+    assert torch.equal(a.sel_idx, b.sel_idx)
+    assert torch.equal(a.beta, b.beta)
+    assert torch.equal(a.Ck, b.Ck) and torch.equal(a.Cv, b.Cv)
+    ta, tb = a.trace(), b.trace()
+    for i in range(len(heads)):
+        assert np.array_equal(ta["pick"][i], tb["pick"][i])
+        assert np.array_equal(ta["weight"][i], tb["weight"][i])
+        s8, sa, sb = ta["swept_keys8"][i], ta["swept_keys"][i], tb["swept_keys"][i]
+        _say(f"head {i}: 8-bit plane keys {s8.tolist()}; 16-bit plane keys {sa.tolist()} (one stage: {sb.tolist()})")
+        assert s8[0] == 0 and np.all(tb["swept_keys8"][i] == 0)
+        assert sa[0] == T and np.all(sa <= np.where(s8 > 0, s8, T))
+        assert np.all(sa[1:] <= sb[1:])
+        if n == 4096:
+            assert sa[1:].sum() < sb[1:].sum()
+
+
 @pytest.mark.parametrize("d,k,R", [(128, 4, 2), (128, 1, 1), (64, 4, 2)])
 def test_int8_and_f64_logits(monkeypatch, d, k, R):
     """bf16 logits on the int8 matrix units (the rows as exact base-256 digit
