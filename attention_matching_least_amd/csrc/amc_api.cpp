@@ -589,13 +589,17 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
     for (int h = h0; h < h1; ++h) cycles = std::max(cycles, ceil_div(pl.desc[size_t(h)].t, pl.kR));
     result = [&]() -> amc_status {
       hipStream_t stream = gs[size_t(g)];
-      if (g > 0 && hipStreamWaitEvent(stream, ev_phi[size_t(g - 1)], 0) != hipSuccess) return AMC_ERR_HIP;
+      // the shift, value tiles and digit rows of a group run beside the
+      // previous group's mass features; its own wait for them (one at a time,
+      // matrix-bound) comes just before them, and the float64 fallback heads
+      // run beside the next group's
       AMC_LAUNCH(AMC_K_SHIFT, launch_shift(dg, bg, stream));
       if (bg.vt) AMC_LAUNCH(AMC_K_INIT, launch_vt(dg, bg, stream));
       if (bg.qdig) AMC_LAUNCH(AMC_K_DIGITS, launch_digits(dg, bg, stream));
+      if (g > 0 && hipStreamWaitEvent(stream, ev_phi[size_t(g - 1)], 0) != hipSuccess) return AMC_ERR_HIP;
       AMC_LAUNCH(AMC_K_PHI, launch_phi(dg, bg, pl.store_phi ? 2 : 0, stream));
-      if (bg.qdig) AMC_LAUNCH(AMC_K_PHI_F64, launch_phi_fallback(dg, bg, pl.store_phi ? 2 : 0, stream));
       if (ngroups > 1 && hipEventRecord(ev_phi[size_t(g)], stream) != hipSuccess) return AMC_ERR_HIP;
+      if (bg.qdig) AMC_LAUNCH(AMC_K_PHI_F64, launch_phi_fallback(dg, bg, pl.store_phi ? 2 : 0, stream));
       for (int c = 0; c < cycles; ++c) {
         if (pl.store_phi) {
           // bounded sweep and float64 rescoring of the band; the heads whose

@@ -1003,6 +1003,9 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
   __shared__ __attribute__((aligned(16))) uint32_t lv_all[2 * VWORDS];
   __shared__ __attribute__((aligned(16))) uint32_t lt_all[2 * 256];  // key tables
   __shared__ double s_tab[32];
+  // STORE == 2: each wave's Phi of a tile, [64 keys][16 queries], turned into
+  // key rows for 16-byte stores of the two planes
+  __shared__ __attribute__((aligned(16))) uint32_t lx_all[STORE == 2 ? P16_WAVES * 1024 : 1];
   uint32_t *const lk0 = lk_all, *const lk1 = lk_all + KWORDS;
   uint32_t *const lv0 = lv_all, *const lv1 = lv_all + VWORDS;
   uint32_t *const lt0 = lt_all, *const lt1 = lt_all + 256;
@@ -1170,14 +1173,31 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
     // the next tile's copies have landed
     __builtin_amdgcn_s_waitcnt(0);
     if constexpr (STORE == 2) {
-      if (q < Dh.ldN) {
-        uint16_t *hp = phi16 + 2 * Dh.phi_off;
-        float xs[4][4];
+      if (qw < Dh.ldN) {
+        // lane (c16, g) puts its values at [key][c16] of the wave's block; then
+        // lane l takes (key, 8 queries) items l and l + 64 and writes the high
+        // and the low halves of the 8 values as one 16-byte store each (the
+        // wave's own LDS writes land before its reads)
+        uint32_t *lx = lx_all + wave * 1024;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) xs[kb][e] = qvalid ? x[kb][e] : 0.0f;
-        store_planes(hp, hp + Dh.ldT * Dh.ldN, Dh.ldN, k0, g, q, xs);
+          for (int e = 0; e < 4; ++e) lx[(16 * kb + g + 4 * e) * 16 + c16] = __float_as_uint(qvalid ? x[kb][e] : 0.0f);
+        uint16_t *hp = phi16 + 2 * Dh.phi_off;
+        uint16_t *lp = hp + Dh.ldT * Dh.ldN;
+#pragma unroll
+        for (int it = 0; it < 2; ++it) {
+          const int item = lane + 64 * it, key = item >> 1, hf = item & 1;
+          const u32x4 a = *reinterpret_cast<const u32x4 *>(lx + key * 16 + 8 * hf);
+          const u32x4 b = *reinterpret_cast<const u32x4 *>(lx + key * 16 + 8 * hf + 4);
+          const u32x4 hv = {__builtin_amdgcn_perm(a.y, a.x, 0x07060302u), __builtin_amdgcn_perm(a.w, a.z, 0x07060302u),
+                            __builtin_amdgcn_perm(b.y, b.x, 0x07060302u), __builtin_amdgcn_perm(b.w, b.z, 0x07060302u)};
+          const u32x4 lv = {__builtin_amdgcn_perm(a.y, a.x, 0x05040100u), __builtin_amdgcn_perm(a.w, a.z, 0x05040100u),
+                            __builtin_amdgcn_perm(b.y, b.x, 0x05040100u), __builtin_amdgcn_perm(b.w, b.z, 0x05040100u)};
+          const int64_t at = (k0 + key) * Dh.ldN + qw + 8 * hf;
+          *reinterpret_cast<u32x4 *>(hp + at) = hv;
+          *reinterpret_cast<u32x4 *>(lp + at) = lv;
+        }
       }
     }
 #pragma unroll
