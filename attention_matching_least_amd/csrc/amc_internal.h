@@ -59,8 +59,8 @@ struct Buffers {
   float *phi;          // [sum n*ldT] float32 Phi (the mass-feature entry point's output)
   uint16_t *phi16;     // per head at 2*phi_off: high plane [ldT keys][ldN queries], then low plane
                        // [ldT][ldN] (key columns; queries from n to ldN and keys past T are zero)
-  float *colsum;       // per head at kt_off * qb128: [key][128-query block] sums of the high
-                       // plane, rounded down (written by the first sweep)
+  float *colsum;       // per head at kt_off * qb128: [128-query block][keys, T rounded up to 64]
+                       // sums of the high plane, rounded down (written by the first sweep)
   float *rpn;          // [sum n][2] float32 positive and negative parts of r (per cycle)
   double *rabs;        // [H] sum |r| (per cycle)
   int32_t *surv_list;  // per head at kt_off: keys that pass the cycle's first pruning stage

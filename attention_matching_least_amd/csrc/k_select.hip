@@ -497,20 +497,20 @@ constexpr int SB_KEYS = 32;  // keys per block of the bounded sweep
 // ---------------------------------------------------------------------------
 // 8-bit plane.  The grid g(c) = the float32 with bits Q8_BASE + c 2^20, c =
 // 0..254: 2^-31 (1 + m/8) 2^e, three significand bits, up to 1.75.  The code
-// of a value h of the high plane is the smallest c with g(c) >= next(h), the
-// bfloat16 above h; since Phi < next(h) (the plane truncates the float32 Phi,
-// which is within 2^-24 of Phi), g(c) bounds Phi from above.  From below,
-// Phi >= g(c - 2) for c >= 2: [h, next(h)] spans less than one step of the
-// grid, so g(c - 1) < next(h) puts g(c - 2) below h (1 - 2^-24).  Two codes
-// apart the grid values differ by at most 4/5 (1.25 against 1.0), so Phi >=
-// (51/64) g(c) for c >= 2, and Phi >= 0 > (51/64) g(c) - 2^-31 for c < 2.
-// In bfloat16 bits hb: c = ceil((hb + 1 - Q8_BASE / 2^16) / 16).  A value that
-// would need code 255 (h >= 1.75, which a shifted Phi never reaches) marks the
-// head's plane unusable.
+// of a value h of the high plane is the smallest c with g(c) > h, i.e. with
+// g(c) >= next(h), the bfloat16 above h; since Phi < next(h) (the plane
+// truncates the float32 Phi, which is within 2^-24 of Phi), g(c) bounds Phi
+// from above.  From below, g(c - 1) <= h, so for c >= 1 the float32 just
+// under g(c - 1) is at most h (1 - 2^-24) <= Phi; two neighbours of the grid
+// differ by at most 8/9 (1.0 against 1.125), so Phi >= (113/128) g(c) for
+// c >= 1, and Phi >= 0 > (113/128) g(0) - 2^-31.  In bfloat16 bits hb:
+// c = floor((hb - Q8_BASE / 2^16) / 16) + 1.  A value that would need code
+// 255 (h >= 1.75, which a shifted Phi never reaches) marks the head's plane
+// unusable.
 // ---------------------------------------------------------------------------
 constexpr uint32_t Q8_BASE = 96u << 23;   // bits of 2^-31
 constexpr int Q8_HB_OFF = (96 << 7) - 16;  // hb - this, over 16, rounded down, is the code
-constexpr float Q8_KAPPA = 51.0f / 64.0f;  // g(c - 2) >= Q8_KAPPA g(c)
+constexpr float Q8_KAPPA = 113.0f / 128.0f;  // Phi >= Q8_KAPPA g(c) for code c >= 1
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
@@ -572,6 +572,7 @@ __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__
   const int nb = int(D.ldN >> 7);                   // full 128-query blocks
   const bool half = (D.ldN & 64) != 0 && sub < 4;  // this lane's part of a last 64-query block
   const double rs = rabs[h];
+  const int64_t ldTp = (D.T + 63) / 64 * 64;        // keys per 128-query block of the sums
   // the block's keys: groups of SB_KEYS, gridDim.x apart in the list
   for (int64_t kb = blockIdx.x; kb * SB_KEYS < cnt; kb += gridDim.x) {
     const int64_t at = kb * SB_KEYS + 8 * wave + kq;
@@ -617,7 +618,7 @@ __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__
       step(b, xa, xb);
       if constexpr (FIRST) {
         const double bs = sum8_lanes(double(hsum(xa, xb)));
-        if (sub == 0) colsum[(D.kt_off + key) * qb128 + b] = __double2float_rd(bs * (1.0 - 0x1p-20));
+        if (sub == 0) colsum[D.kt_off * qb128 + b * ldTp + key] = __double2float_rd(bs * (1.0 - 0x1p-20));
         if (q8p) {
           const u32x2v ca = q8_pack8(xa, hmax), cb = q8_pack8(xb, hmax);
           q8p[8 * b] = u32x4{ca.x, ca.y, cb.x, cb.y};
@@ -653,7 +654,7 @@ __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__
       }
       if constexpr (FIRST) {
         const double bs = sum8_lanes(double(hsum(xa, xb)));
-        if (sub == 0 && key >= 0) colsum[(D.kt_off + key) * qb128 + nb] = __double2float_rd(bs * (1.0 - 0x1p-20));
+        if (sub == 0 && key >= 0) colsum[D.kt_off * qb128 + nb * ldTp + key] = __double2float_rd(bs * (1.0 - 0x1p-20));
         if (q8p && key >= 0 && half) {
           const u32x2v ca = q8_pack8(xa, hmax), cb = q8_pack8(xb, hmax);
           q8p[8 * nb] = u32x4{ca.x, ca.y, cb.x, cb.y};
@@ -687,15 +688,15 @@ __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__
 // ---------------------------------------------------------------------------
 // Second pruning stage, between k_prune and the bounded sweep: for each key of
 // the survivor list an upper bound of r^T Phi[:, k] from the 8-bit plane,
-//   U8_k = sum_{r_q > 0} r_q g(c_qk) + (51/64) sum_{r_q < 0} r_q g(c_qk)
+//   U8_k = sum_{r_q > 0} r_q g(c_qk) + (113/128) sum_{r_q < 0} r_q g(c_qk)
 //          + 2^-31 sum |r|
-// (Phi <= g(c), Phi >= (51/64) g(c) less 2^-31 where c < 2), plus the
+// (Phi <= g(c), Phi >= (113/128) g(c) less 2^-31 where c = 0), plus the
 // float32 accumulation, rounding and underflow allowances of the bounded
-// sweep (the product (51/64) r- is rounded to float32 once more).  Nothing is
+// sweep (the product (113/128) r- is rounded to float32 once more).  Nothing is
 // done where k_prune kept every key (its L is -inf) or the plane is unusable.
 // Groups of 64 keys (8 waves of 8), 8 lanes per key, each lane 16 queries of
 // every 128 (one 16-byte load), sixteen loads in flight; a block takes every
-// gridDim.x-th group of its head's list.  The (r+, (51/64) r-) pairs sit in
+// gridDim.x-th group of its head's list.  The (r+, (113/128) r-) pairs sit in
 // LDS lane-interleaved: pair j of lane sub's 16 queries of 128-query block i
 // at 16-byte slot 64 i + 8 j + sub, so the 8 lanes of a key read 128
 // consecutive bytes.  Out: sw_up and sw_key at the key's place in the list
@@ -714,7 +715,7 @@ __global__ __launch_bounds__(Q8_THREADS) void k_sweep_q8(const HeadDesc *__restr
                                                          const int32_t *__restrict__ surv_cnt,
                                                          const int32_t *__restrict__ sel_slot, int cycle, int kR,
                                                          double *__restrict__ sw_up, int32_t *__restrict__ sw_key) {
-  extern __shared__ __attribute__((aligned(16))) float s_w[];  // (r+, (51/64) r-) pairs, 2 per 16-byte slot
+  extern __shared__ __attribute__((aligned(16))) float s_w[];  // (r+, (113/128) r-) pairs, 2 per 16-byte slot
   const int h = blockIdx.y;
   const HeadDesc D = desc[h];
   int64_t S0;
@@ -973,11 +974,12 @@ __global__ __launch_bounds__(PR_THREADS) void k_prune(const HeadDesc *__restrict
   for (int64_t k = tid; k < D.T; k += PR_THREADS) {
     double u = -INFINITY;
     if (sel_slot[D.k_off + k] == 0) {
-      const float *cs = colsum + (D.kt_off + k) * qb128;
+      const float *cs = colsum + D.kt_off * qb128 + k;
+      const int64_t ldTp = (D.T + 63) / 64 * 64;
       double s = 0.0, a = 0.0;
       for (int b = 0; b < nb; ++b) {
         const double rm = s_rmax[b];
-        const double c = double(cs[b]);
+        const double c = double(cs[b * ldTp]);
         const double t = rm * (rm >= 0.0 ? c * kup : c * kdn);
         s += t;
         a += fabs(t);
@@ -1005,9 +1007,7 @@ __global__ __launch_bounds__(PR_THREADS) void k_prune(const HeadDesc *__restrict
       const uint16_t *hp = hp0 + int64_t(key) * D.ldN;
       const uint16_t *lp = lp0 + int64_t(key) * D.ldN;
       double sc = 0.0, ab = 0.0;
-      for (int64_t q = 8 * lane; q < D.ldN; q += 512) {
-        const u32x4 hv = *reinterpret_cast<const u32x4 *>(hp + q);
-        const u32x4 lv = *reinterpret_cast<const u32x4 *>(lp + q);
+      auto part = [&](int64_t q, const u32x4 &hv, const u32x4 &lv) __attribute__((always_inline)) {
         const f32x4 x0 = join_planes(u32x2{hv.x, hv.y}, u32x2{lv.x, lv.y});
         const f32x4 x1 = join_planes(u32x2{hv.z, hv.w}, u32x2{lv.z, lv.w});
         const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
@@ -1017,7 +1017,21 @@ __global__ __launch_bounds__(PR_THREADS) void k_prune(const HeadDesc *__restrict
           sc += t;
           ab += fabs(t);
         }
+      };
+      // eight 512-query steps of both planes in flight at once
+      int64_t q = 8 * lane;
+      for (; q + 7 * 512 < D.ldN; q += 8 * 512) {
+        u32x4 hv[8], lv[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) {
+          hv[u] = *reinterpret_cast<const u32x4 *>(hp + q + 512 * u);
+          lv[u] = *reinterpret_cast<const u32x4 *>(lp + q + 512 * u);
+        }
+#pragma unroll
+        for (int u = 0; u < 8; ++u) part(q + 512 * u, hv[u], lv[u]);
       }
+      for (; q < D.ldN; q += 512)
+        part(q, *reinterpret_cast<const u32x4 *>(hp + q), *reinterpret_cast<const u32x4 *>(lp + q));
 #pragma unroll
       for (int off = 32; off >= 1; off >>= 1) {
         sc += __shfl_xor(sc, off);
