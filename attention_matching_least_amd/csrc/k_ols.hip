@@ -35,9 +35,11 @@ __device__ __forceinline__ void decode_tri(int e, int *r, int *c) {
 // normal equations: N = At At^T and rhs = At Y with At[a][i] = P[a][i] w_a / mhat_i,
 // formed as N[a][b] = w_a w_b sum_i X[a][i] X[b][i] and rhs[a][d] = w_a sum_i
 // X[a][i] Y[i][d] with X[a][i] = P[a][i] / mhat_i, on float64 MFMA.
-// Block tile: 64 rows a x 64 columns b (b < t: N, b >= t: rhs column b - t);
-// each wave takes 16 rows; the queries are staged through LDS 64 at a time,
-// the next stage prefetched into registers.
+// Block tile: 64 rows a x 64 columns, of N (column tiles below tx = ceil(t /
+// 64)) or of rhs (the D columns after them); each wave takes 16 rows; the
+// queries are staged through LDS 64 at a time, the next stage prefetched into
+// registers.  N is symmetric and its readers take the lower triangle, so the
+// tiles wholly above the diagonal are skipped.
 // ---------------------------------------------------------------------------
 typedef double f64x4o __attribute__((ext_vector_type(4)));
 
@@ -68,8 +70,11 @@ __global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ 
   if (h >= H) return;
   const HeadDesc Dh = desc[h];
   const int64_t t = Dh.t, n = Dh.n;
-  const int64_t a0 = int64_t(j % tx) * 64, b0 = int64_t(j / tx) * 64;
-  if (a0 >= t || b0 >= t + D) return;
+  const int64_t a0 = int64_t(j % tx) * 64;
+  const int bt = j / tx;
+  const bool isN = bt < tx;
+  const int64_t b0 = isN ? int64_t(bt) * 64 : int64_t(bt - tx) * 64;  // N column or rhs column
+  if (a0 >= t || (isN && (b0 >= t || b0 > a0)) || (!isN && b0 >= D)) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int c16 = lane & 15, g = lane >> 4;
   const double *P = Dh.panel_off + panel;
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ 
       const int64_t i = i0 + c;
       const int64_t a = a0 + rr, b = b0 + rr;
       xr[u] = (i < n && a < t) ? P[a * n + i] : 0.0;
-      zr[u] = (i < n && b < t) ? P[b * n + i] : 0.0;
+      zr[u] = (isN && i < n && b < t) ? P[b * n + i] : 0.0;
     }
     if (tid < CH) mr = i0 + tid < n ? mhat[Dh.n_off + i0 + tid] : 1.0;
   };
@@ -104,11 +109,11 @@ __global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ 
       const double iv = minv[buf][c];
       xs[rr * STR + c] = xr[u] * iv;
       const int64_t b = b0 + rr;
-      if (b < t) {
+      if (isN) {
         zs[rr * STR + c] = zr[u] * iv;
       } else {
         const int64_t i = i0 + c;
-        zs[rr * STR + c] = (b - t < D && i < n) ? double(Y[(Dh.n_off + i) * D + (b - t)]) : 0.0;
+        zs[rr * STR + c] = (b < D && i < n) ? double(Y[(Dh.n_off + i) * D + b]) : 0.0;
       }
     }
     __syncthreads();
@@ -132,8 +137,11 @@ __global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ 
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int64_t b = b0 + 16 * q + c16;
-      if (b < t) N[Dh.tt_off + a * t + b] = acc[q][e] * wa * w[Dh.t_off + b];
-      else if (b - t < D) rhs[(Dh.t_off + a) * D + (b - t)] = acc[q][e] * wa;
+      if (isN) {
+        if (b < t) N[Dh.tt_off + a * t + b] = acc[q][e] * wa * w[Dh.t_off + b];
+      } else if (b < D) {
+        rhs[(Dh.t_off + a) * D + b] = acc[q][e] * wa;
+      }
     }
   }
 }
@@ -656,7 +664,7 @@ __global__ __launch_bounds__(NT) void k_ols_trsm_g(const HeadDesc *__restrict__ 
 }  // namespace
 
 hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s) {
-  const int tx = int((dm.max_t + 63) / 64), ty = int((dm.max_t + dm.d + 63) / 64);
+  const int tx = int((dm.max_t + 63) / 64), ty = tx + int((dm.d + 63) / 64);
   const int xcd_map = dm.H % 8 == 0 ? 1 : 0;
   dim3 grid(unsigned(tx * ty * dm.H));
   if (dm.d == 128)
