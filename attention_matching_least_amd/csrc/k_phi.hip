@@ -113,14 +113,49 @@ __global__ __launch_bounds__(256) void k_shift(const HeadDesc *__restrict__ desc
       qf[rb][c] = row < Dh.n ? load8_bf16<BF16>(Q, (Dh.q_off + row) * D + 32 * c + 8 * g) : make_uint4(0, 0, 0, 0);
   }
   float mx = -INFINITY;
+  // Without a bias and with a positive scale the largest logit is the scale
+  // times the largest dot product (rounding is monotonic), so tiles whose rows
+  // and keys all exist keep the raw maximum, one v_max per value.
+  float mxr = -INFINITY;
+  const bool raw_ok = beta_in == nullptr && scale > 0.0f && qb + 32 <= Dh.n;
+  // the next 64-key tile is loaded into registers while the current one is
+  // multiplied
+  constexpr int PER = 64 * D / 8 / 256;  // 16-byte pieces of a tile per thread
+  uint4 pre[PER];
+  auto fetch = [&](int64_t k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int gi = tid + 256 * u, key = gi / (D / 8), c8 = gi % (D / 8);
+      pre[u] = (k0 + key < Dh.T) ? load8_bf16<BF16>(K, (Dh.k_off + k0 + key) * D + 8 * c8) : make_uint4(0, 0, 0, 0);
+    }
+  };
+  fetch(0);
   for (int64_t k0 = 0; k0 < Dh.T; k0 += 64) {
     __syncthreads();
-    for (int gi = tid; gi < 64 * D / 8; gi += 256) {
-      const int key = gi / (D / 8), c8 = gi % (D / 8);
-      const uint4 v = (k0 + key < Dh.T) ? load8_bf16<BF16>(K, (Dh.k_off + k0 + key) * D + 8 * c8) : make_uint4(0, 0, 0, 0);
-      *reinterpret_cast<uint4 *>(&ks[key * KSTR + 8 * c8]) = v;
+#pragma unroll
+    for (int u = 0; u < PER; ++u) {
+      const int gi = tid + 256 * u, key = gi / (D / 8), c8 = gi % (D / 8);
+      *reinterpret_cast<uint4 *>(&ks[key * KSTR + 8 * c8]) = pre[u];
     }
     __syncthreads();
+    if (k0 + 64 < Dh.T) fetch(k0 + 64);
+    if (raw_ok && k0 + 64 <= Dh.T) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        uint4 kf[KC];
+#pragma unroll
+        for (int c = 0; c < KC; ++c) kf[c] = *reinterpret_cast<const uint4 *>(&ks[(kb * 16 + c16) * KSTR + 32 * c + 8 * g]);
+#pragma unroll
+        for (int rb = 0; rb < 2; ++rb) {
+          f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < KC; ++c)
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(qf[rb][c]), as_bf16x8(kf[c]), acc, 0, 0, 0);
+          mxr = fmaxf(mxr, fmaxf(fmaxf(acc[0], acc[1]), fmaxf(acc[2], acc[3])));
+        }
+      }
+      continue;
+    }
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb) {
       uint4 kf[KC];
@@ -144,6 +179,7 @@ __global__ __launch_bounds__(256) void k_shift(const HeadDesc *__restrict__ desc
       }
     }
   }
+  if (mxr != -INFINITY) mx = fmaxf(mx, scale * mxr);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   if (lane == 0) red[wave] = mx;

@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0
 F64_MFMA_PEAK_TFS = 78.6
 I8_MFMA_PEAK_TOPS = 5000.0  # dense int8 matrix peak of the MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3-4b-stack-T8192-50x.md")
-KERNEL_SOURCES = {"k_sweep_band": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_select.hip"),
+KERNEL_SOURCES = {"k_sweep": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_select.hip"),
                   "k_phi": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_phi.hip")}
 
 
@@ -454,7 +454,7 @@ def main():
             achieved = per_step * args.steps / (sw["total_ms"] * 1e-3) / 1e9
             found.append((sw["total_ms"], {
                 "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("k_sweep_band"),
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("k_sweep"),
                 "kernel": "k_sweep_band+k_sweep_q8", "avg_launch_ms": round(sw["avg_ms"], 4), "launches": sw["launches"],
                 "algorithmic_bytes_per_launch": per_step * args.steps / sw["launches"],
                 "swept_keys_per_step": swept, "swept_keys8_per_step": swept8,
