@@ -223,59 +223,105 @@ __global__ __launch_bounds__(NT) void k_ols_factor(const HeadDesc *__restrict__ 
 }
 
 // ---------------------------------------------------------------------------
-// triangular solves for 8 right-hand-side columns per block; C_v[F] = D^-1 X.
+// triangular solves, 32 right-hand-side columns per block and 8 per wave; each
+// wave substitutes column by column with no block barriers: lane l holds rows
+// l, l + 64 and l + 128 of its 8 columns, x_k = r_k / L_kk comes from its
+// lane, and column k of L (forward) or row k (backward) is applied to the rows
+// still open.  C_v[F] = D^-1 X.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ double rl64(double x, int lane) {
+  const int lo = __builtin_amdgcn_readlane(__double2loint(x), lane);
+  const int hi = __builtin_amdgcn_readlane(__double2hiint(x), lane);
+  return __hiloint2double(hi, lo);
+}
+
 template <int D>
 __global__ __launch_bounds__(NT) void k_ols_trsm(const HeadDesc *__restrict__ desc, const double *__restrict__ rhs,
                                                  const int32_t *__restrict__ flist,
                                                  const int32_t *__restrict__ fcount, const double *__restrict__ dn,
                                                  const double *__restrict__ Lg, const double *__restrict__ w,
                                                  float *__restrict__ cv_sel) {
-  constexpr int NC = 8;
+  constexpr int NCB = 32, NCW = 8;
+  static_assert(kLdsMaxT <= 192, "three rows per lane");
   extern __shared__ __attribute__((aligned(16))) double sm[];
   const int h = blockIdx.y;
   const HeadDesc Dh = desc[h];
   if (Dh.t > kLdsMaxT) return;  // k_ols_trsm_g
   const int t = int(Dh.t);
-  const int c0 = blockIdx.x * NC;
+  const int c0 = blockIdx.x * NCB;
   const int f = fcount[h];
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   double *Ls = sm;
-  double *X = sm + tri(f);  // [f][NC]
   for (int e = tid; e < tri(f); e += NT) Ls[e] = Lg[Dh.tri_off + e];
-  for (int e = tid; e < f * NC; e += NT) {
-    const int k = e / NC, c = e % NC;
-    X[e] = rhs[(Dh.t_off + flist[Dh.t_off + k]) * D + c0 + c] / dn[Dh.t_off + k];
-  }
   // keys with w = 0 get a zero value row
-  for (int e = tid; e < t * NC; e += NT) {
-    const int a = e / NC, c = e % NC;
+  for (int e = tid; e < t * NCB; e += NT) {
+    const int a = e / NCB, c = e % NCB;
     if (!(w[Dh.t_off + a] > 0.0)) cv_sel[(Dh.t_off + a) * D + c0 + c] = 0.0f;
   }
   __syncthreads();
-  for (int k = 0; k < f; ++k) {
-    if (tid < NC) X[k * NC + tid] /= Ls[tri(k) + k];
-    __syncthreads();
-    const int cnt = (f - k - 1) * NC;
-    for (int e = tid; e < cnt; e += NT) {
-      const int r = k + 1 + e / NC, c = e % NC;
-      X[r * NC + c] -= Ls[tri(r) + k] * X[k * NC + c];
-    }
-    __syncthreads();
+  const int cw = c0 + NCW * wave;
+  int rbase[3];
+  double rd[3], xv[NCW][3];
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const int i = lane + 64 * m;
+    rbase[m] = i < f ? tri(i) : 0;
+    rd[m] = i < f ? 1.0 / Ls[rbase[m] + i] : 0.0;
+    const int64_t row = i < f ? (Dh.t_off + flist[Dh.t_off + i]) * D : 0;
+    const double di = i < f ? dn[Dh.t_off + i] : 1.0;
+#pragma unroll
+    for (int q = 0; q < NCW; ++q) xv[q][m] = i < f ? rhs[row + cw + q] / di : 0.0;
   }
-  for (int k = f - 1; k >= 0; --k) {
-    if (tid < NC) X[k * NC + tid] /= Ls[tri(k) + k];
-    __syncthreads();
-    const int cnt = k * NC;
-    for (int e = tid; e < cnt; e += NT) {
-      const int r = e / NC, c = e % NC;
-      X[r * NC + c] -= Ls[tri(k) + r] * X[k * NC + c];
+  // forward: L y = x, column k of L below row k
+#pragma unroll
+  for (int M = 0; M < 3; ++M) {
+    const int k1 = f < 64 * M + 64 ? f : 64 * M + 64;
+    for (int k = 64 * M; k < k1; ++k) {
+      const int kl = k - 64 * M;
+      double lc[3];
+#pragma unroll
+      for (int m = 0; m < 3; ++m)
+        lc[m] = (m >= M && (m > M || lane > kl) && lane + 64 * m < f) ? Ls[rbase[m] + k] : 0.0;
+#pragma unroll
+      for (int q = 0; q < NCW; ++q) {
+        const double xk = rl64(xv[q][M] * rd[M], kl);
+#pragma unroll
+        for (int m = M; m < 3; ++m) xv[q][m] = fma(-lc[m], xk, xv[q][m]);
+      }
     }
-    __syncthreads();
   }
-  for (int e = tid; e < f * NC; e += NT) {
-    const int k = e / NC, c = e % NC;
-    cv_sel[(Dh.t_off + flist[Dh.t_off + k]) * D + c0 + c] = float(X[e] / dn[Dh.t_off + k]);
+#pragma unroll
+  for (int q = 0; q < NCW; ++q)
+#pragma unroll
+    for (int m = 0; m < 3; ++m) xv[q][m] *= rd[m];
+  // backward: L^T z = y, row k of L left of column k
+#pragma unroll
+  for (int MM = 0; MM < 3; ++MM) {
+    const int M = 2 - MM;
+    for (int k = (f < 64 * M + 64 ? f : 64 * M + 64) - 1; k >= 64 * M; --k) {
+      const int kl = k - 64 * M;
+      const double *Lk = Ls + tri(k);
+      double lr[3];
+#pragma unroll
+      for (int m = 0; m < 3; ++m) lr[m] = m < M ? Lk[lane + 64 * m] : (m == M && lane < kl ? Lk[lane + 64 * M] : 0.0);
+#pragma unroll
+      for (int q = 0; q < NCW; ++q) {
+        const double xk = rl64(xv[q][M] * rd[M], kl);
+#pragma unroll
+        for (int m = 0; m <= M; ++m) xv[q][m] = fma(-lr[m], xk, xv[q][m]);
+      }
+    }
+  }
+#pragma unroll
+  for (int m = 0; m < 3; ++m) {
+    const int i = lane + 64 * m;
+    if (i < f) {
+      const int64_t row = (Dh.t_off + flist[Dh.t_off + i]) * D;
+      const double di = dn[Dh.t_off + i];
+#pragma unroll
+      for (int q = 0; q < NCW; ++q) cv_sel[row + cw + q] = float(xv[q][m] * rd[m] / di);
+    }
   }
 }
 
@@ -713,7 +759,8 @@ hipError_t launch_ols_trsm(const Dims &dm, const Buffers &b, hipStream_t s) {
     if (e != hipSuccess || dm.min_t > kLdsMaxT) return e;
   }
   const int64_t mt = dm.max_t < kLdsMaxT ? dm.max_t : kLdsMaxT;
-  const size_t bytes = size_t(8) * (size_t(mt) * size_t(mt + 1) / 2 + size_t(mt) * 8) + 16;
+  const size_t bytes = size_t(8) * (size_t(mt) * size_t(mt + 1) / 2) + 16;
+  grid = dim3(unsigned(dm.d / 32), unsigned(dm.H));
   hipError_t e;
   if (dm.d == 128) {
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ols_trsm<128>),
