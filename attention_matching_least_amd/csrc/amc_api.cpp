@@ -305,6 +305,22 @@ static int head_groups(int requested, int H) {
   return g < H ? g : H;
 }
 
+// First head of group g: the groups shrink by a factor 0.8 one to the next
+// (the last group's selection loop runs alone at the end, so a smaller last
+// group shortens that tail), with bounds on multiples of 8 heads when the
+// count allows (the mass-feature kernels map heads to XCDs in eights).
+static int group_bound(int H, int ngroups, int g) {
+  if (g <= 0) return 0;
+  if (g >= ngroups) return H;
+  double tot = 0.0, acc = 0.0;
+  for (int i = 0; i < ngroups; ++i) tot += std::pow(0.8, i);
+  for (int i = 0; i < g; ++i) acc += std::pow(0.8, i);
+  const double x = double(H) * acc / tot;
+  int b = (H % 8 == 0 && H >= 8 * ngroups) ? 8 * int(std::lround(x / 8.0)) : int(std::lround(x));
+  const int lo = group_bound(H, ngroups, g - 1) + 1, hi = H - (ngroups - g);  // every group keeps a head
+  return b < lo ? lo : (b > hi ? hi : b);
+}
+
 // The buffers of heads [h0, ...): the descriptor table and the arrays indexed
 // by head number start at h0; everything else is reached through the
 // descriptors' offsets.
@@ -581,7 +597,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   }
   amc_status result = AMC_OK;
   for (int g = 0; g < ngroups && result == AMC_OK; ++g) {
-    const int h0 = int(int64_t(dm.H) * g / ngroups), h1 = int(int64_t(dm.H) * (g + 1) / ngroups);
+    const int h0 = group_bound(dm.H, ngroups, g), h1 = group_bound(dm.H, ngroups, g + 1);
     const Buffers bg = head_range(b, h0, dm.max_qblk);
     Dims dg = dm;
     dg.H = h1 - h0;
