@@ -37,10 +37,62 @@ __device__ __forceinline__ double rl(double x, int lane) {
   return __hiloint2double(hi, lo);
 }
 
+// Values moved across lanes by a DPP pattern; rows that ROWMASK leaves out
+// keep `old`.  The wave reductions below combine lanes within rows of 16
+// (quad permutations, the half-row and row mirrors), then row 0 into row 1 and
+// row 2 into row 3 (row_bcast:15), then row 1 into rows 2 and 3
+// (row_bcast:31): lane 63 holds the result, which v_readlane broadcasts.
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ int dpp_i32(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWMASK, 0xf, false);
+}
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ double dpp_f64(double old, double v) {
+  const int lo = dpp_i32<CTRL, ROWMASK>(__double2loint(old), __double2loint(v));
+  const int hi = dpp_i32<CTRL, ROWMASK>(__double2hiint(old), __double2hiint(v));
+  return __hiloint2double(hi, lo);
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off);
-  return v;
+  v += dpp_f64<0xB1>(0.0, v);        // quad_perm [1, 0, 3, 2]
+  v += dpp_f64<0x4E>(0.0, v);        // quad_perm [2, 3, 0, 1]
+  v += dpp_f64<0x141>(0.0, v);       // row_half_mirror
+  v += dpp_f64<0x140>(0.0, v);       // row_mirror
+  v += dpp_f64<0x142, 0xa>(0.0, v);  // row_bcast:15
+  v += dpp_f64<0x143, 0xc>(0.0, v);  // row_bcast:31
+  return rl(v, 63);
+}
+
+__device__ __forceinline__ int wave_count(int c) {
+  c += dpp_i32<0xB1>(0, c);
+  c += dpp_i32<0x4E>(0, c);
+  c += dpp_i32<0x141>(0, c);
+  c += dpp_i32<0x140>(0, c);
+  c += dpp_i32<0x142, 0xa>(0, c);
+  c += dpp_i32<0x143, 0xc>(0, c);
+  return __builtin_amdgcn_readlane(c, 63);
+}
+
+// wave-wide best of (v, idx): larger value, ties to the lower index; idx < 0
+// is empty
+template <int CTRL, int ROWMASK = 0xf>
+__device__ __forceinline__ void best_step(double &v, int &idx) {
+  const double ov = dpp_f64<CTRL, ROWMASK>(v, v);
+  const int oi = dpp_i32<CTRL, ROWMASK>(idx, idx);
+  if (oi >= 0 && (idx < 0 || ov > v || (ov == v && oi < idx))) {
+    v = ov;
+    idx = oi;
+  }
+}
+__device__ __forceinline__ void wave_best(double &v, int &idx) {
+  best_step<0xB1>(v, idx);
+  best_step<0x4E>(v, idx);
+  best_step<0x141>(v, idx);
+  best_step<0x140>(v, idx);
+  best_step<0x142, 0xa>(v, idx);
+  best_step<0x143, 0xc>(v, idx);
+  v = rl(v, 63);
+  idx = __builtin_amdgcn_readlane(idx, 63);
 }
 
 struct Red {
@@ -52,15 +104,7 @@ struct Red {
 // no thread passed a valid one.  Every thread gets the result.
 __device__ __forceinline__ int block_argmax(double v, int idx, Red *red, double *out_v) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    const double ov = __shfl_xor(v, off);
-    const int oi = __shfl_xor(idx, off);
-    if (oi >= 0 && (idx < 0 || ov > v || (ov == v && oi < idx))) {
-      v = ov;
-      idx = oi;
-    }
-  }
+  wave_best(v, idx);
   __syncthreads();
   if (lane == 0) {
     red->v[wave] = v;
@@ -83,8 +127,7 @@ __device__ __forceinline__ int block_argmax(double v, int idx, Red *red, double 
 
 __device__ __forceinline__ int block_count(int c, Red *red) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) c += __shfl_xor(c, off);
+  c = wave_count(c);
   __syncthreads();
   if (lane == 0) red->i[wave] = c;
   __syncthreads();
