@@ -760,30 +760,59 @@ __device__ __forceinline__ void remove_at(const St &S, int q) {
         xv[m] = act ? xc[i] : 0.0;
         yl[m] = act ? yv[i] : 0.0;
       });
+      // (columns and diagonals kPD steps ahead are loaded before a step's
+      // rotation; a step writes only its own column and diagonal)
       static_for<0, 3>([&](auto Mc) {
         constexpr int M = decltype(Mc)::value;
-        const int k1 = n2 < 64 * M + 64 ? n2 : 64 * M + 64;
-        for (int k = q > 64 * M ? q : 64 * M; k < k1; ++k) {
-          const int kl = k - 64 * M;
-          const int dk = tri(k) + k;
-          const double lkk = S.L[dk];
-          const double xk = rl(xv[M], kl);
-          const double t2 = fma(lkk, lkk, xk * xk);
-          const double ri = rsqrt(t2);
-          const double c = lkk * ri, s = xk * ri;
-          const double yk = rl(yl[M], kl);
-          if (lane == kl) {
-            yl[M] = fma(c, yk, s * z);
-            S.L[dk] = t2 * ri;
-          }
-          z = fma(c, z, -s * yk);
-          static_for<M, 3>([&](auto Rc) {
-            constexpr int m = decltype(Rc)::value;
-            if ((m > M || lane > kl) && lane + 64 * m < n2) {
-              const double l = S.L[rbase[m] + k];
-              S.L[rbase[m] + k] = fma(c, l, s * xv[m]);
-              xv[m] = fma(c, xv[m], -s * l);
+        const int kb = q > 64 * M ? q : 64 * M, k1 = n2 < 64 * M + 64 ? n2 : 64 * M + 64;
+        if (kb < k1) {
+          double ring[kPD][4];  // column k at the lane's rows m >= M, then L_kk
+          auto load_col = [&](int k, double(&sl)[4]) __attribute__((always_inline)) {
+            static_for<M, 3>([&](auto Rc) {
+              constexpr int m = decltype(Rc)::value;
+              sl[m] = S.L[rbase[m] + k];
+            });
+            sl[3] = S.L[tri(k) + k];
+          };
+          static_for<0, kPD>([&](auto Pc) {
+            constexpr int j = decltype(Pc)::value;
+            load_col(kb + j < k1 ? kb + j : k1 - 1, ring[j]);
+          });
+          auto step = [&](int k, double(&sl)[4], auto refill) __attribute__((always_inline)) {
+            double use[4];
+            static_for<0, 4>([&](auto Uc) { use[decltype(Uc)::value] = sl[decltype(Uc)::value]; });
+            if constexpr (decltype(refill)::value) {
+              load_col(k + kPD < k1 ? k + kPD : k1 - 1, sl);
+              asm volatile("" ::: "memory");
             }
+            const int kl = k - 64 * M;
+            const int dk = tri(k) + k;
+            const double lkk = use[3];
+            const double xk = rl(xv[M], kl);
+            const double t2 = fma(lkk, lkk, xk * xk);
+            const double ri = rsqrt(t2);
+            const double c = lkk * ri, s = xk * ri;
+            const double yk = rl(yl[M], kl);
+            if (lane == kl) {
+              yl[M] = fma(c, yk, s * z);
+              S.L[dk] = t2 * ri;
+            }
+            z = fma(c, z, -s * yk);
+            static_for<M, 3>([&](auto Rc) {
+              constexpr int m = decltype(Rc)::value;
+              if ((m > M || lane > kl) && lane + 64 * m < n2) {
+                const double l = use[m];
+                S.L[rbase[m] + k] = fma(c, l, s * xv[m]);
+                xv[m] = fma(c, xv[m], -s * l);
+              }
+            });
+          };
+          int k = kb;
+          for (; k + kPD <= k1; k += kPD)
+            static_for<0, kPD>([&](auto Pc) { step(k + decltype(Pc)::value, ring[decltype(Pc)::value], std::true_type{}); });
+          static_for<0, kPD - 1>([&](auto Pc) {
+            constexpr int j = decltype(Pc)::value;
+            if (k + j < k1) step(k + j, ring[j], std::false_type{});
           });
         }
       });
