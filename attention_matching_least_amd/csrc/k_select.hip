@@ -496,21 +496,25 @@ constexpr int SB_KEYS = 32;  // keys per block of the bounded sweep
 
 // ---------------------------------------------------------------------------
 // 8-bit plane.  The grid g(c) = the float32 with bits Q8_BASE + c 2^20, c =
-// 0..254: 2^-31 (1 + m/8) 2^e, three significand bits, up to 1.75.  The code
-// of a value h of the high plane is the smallest c with g(c) > h, i.e. with
-// g(c) >= next(h), the bfloat16 above h; since Phi < next(h) (the plane
-// truncates the float32 Phi, which is within 2^-24 of Phi), g(c) bounds Phi
-// from above.  From below, g(c - 1) <= h, so for c >= 1 the float32 just
-// under g(c - 1) is at most h (1 - 2^-24) <= Phi; two neighbours of the grid
-// differ by at most 8/9 (1.0 against 1.125), so Phi >= (113/128) g(c) for
-// c >= 1, and Phi >= 0 > (113/128) g(0) - 2^-31.  In bfloat16 bits hb:
-// c = floor((hb - Q8_BASE / 2^16) / 16) + 1.  A value that would need code
-// 255 (h >= 1.75, which a shifted Phi never reaches) marks the head's plane
+// 8..254: 2^-31 (1 + m/8) 2^e, three significand bits, from 2^-30 up to 1.75.
+// The code of a value h of the high plane is the smallest c with g(c) > h,
+// i.e. with g(c) >= next(h), the bfloat16 above h, but at least 8; since Phi <
+// next(h) (the plane truncates the float32 Phi, which is within 2^-24 of
+// Phi), g(c) bounds Phi from above.  From below, for a code not raised to 8,
+// g(c - 1) <= h, so the float32 just under g(c - 1) is at most h (1 - 2^-24)
+// <= Phi; two neighbours of the grid differ by at most 8/9 (1.0 against
+// 1.125), so Phi >= (113/128) g(c); where the code was raised to 8, Phi >= 0 >
+// (113/128) g(8) - 2^-30.  In bfloat16 bits hb: c = max(8, floor((hb -
+// Q8_BASE / 2^16) / 16) + 1).  g(c) = 2^96 times the float32 with bits c 2^20
+// (a normal number for c >= 8), so the sweep decodes a code with one shift
+// and takes the 2^96 into its weights.  A value that would need code 255
+// (h >= 1.75, which a shifted Phi never reaches) marks the head's plane
 // unusable.
 // ---------------------------------------------------------------------------
 constexpr uint32_t Q8_BASE = 96u << 23;   // bits of 2^-31
 constexpr int Q8_HB_OFF = (96 << 7) - 16;  // hb - this, over 16, rounded down, is the code
-constexpr float Q8_KAPPA = 113.0f / 128.0f;  // Phi >= Q8_KAPPA g(c) for code c >= 1
+constexpr float Q8_KAPPA = 113.0f / 128.0f;  // Phi >= Q8_KAPPA g(c) for a code not raised to 8
+constexpr int Q8_CMIN = 8;                    // smallest code (a normal float32 for bits c 2^20)
 
 typedef short s16x2 __attribute__((ext_vector_type(2)));
 
@@ -519,15 +523,36 @@ typedef short s16x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint32_t q8_codes2(uint32_t w, s16x2 &hmax) {
   s16x2 v = __builtin_bit_cast(s16x2, w);
   hmax = hmax > v ? hmax : v;
-  // (values below the grid, sign bit included, take code 0)
+  // (values below g(7), sign bit included, take code 8)
   const s16x2 off = {short(Q8_HB_OFF), short(Q8_HB_OFF)}, top = {254, 254};
-  v = v > off ? v : off;
+  const s16x2 low = {short(Q8_HB_OFF + 16 * Q8_CMIN), short(Q8_HB_OFF + 16 * Q8_CMIN)};
+  v = v > low ? v : low;
   s16x2 c = (v - off) >> short(4);
   c = c < top ? c : top;
   return __builtin_bit_cast(uint32_t, c);
 }
 
 typedef uint32_t u32x2v __attribute__((ext_vector_type(2)));
+
+// 2^-96 g(c) for the code in byte B of w: the float32 with bits c 2^20, one
+// SDWA shift of the selected byte (tw holds the shift count, 20)
+template <int B>
+__device__ __forceinline__ float q8_grid(uint32_t w, uint32_t tw) {
+  uint32_t r;
+  if constexpr (B == 0)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_0"
+        : "=v"(r) : "v"(tw), "v"(w));
+  else if constexpr (B == 1)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_1"
+        : "=v"(r) : "v"(tw), "v"(w));
+  else if constexpr (B == 2)
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_2"
+        : "=v"(r) : "v"(tw), "v"(w));
+  else
+    asm("v_lshlrev_b32_sdwa %0, %1, %2 dst_sel:DWORD dst_unused:UNUSED_PAD src0_sel:DWORD src1_sel:BYTE_3"
+        : "=v"(r) : "v"(tw), "v"(w));
+  return __uint_as_float(r);
+}
 
 // eight codes of a 16-byte load of the high plane (queries in order), as 8 bytes
 __device__ __forceinline__ u32x2v q8_pack8(const u32x4 &xv, s16x2 &hmax) {
@@ -689,10 +714,13 @@ __global__ __launch_bounds__(256) void k_sweep_band(const HeadDesc *__restrict__
 // Second pruning stage, between k_prune and the bounded sweep: for each key of
 // the survivor list an upper bound of r^T Phi[:, k] from the 8-bit plane,
 //   U8_k = sum_{r_q > 0} r_q g(c_qk) + (113/128) sum_{r_q < 0} r_q g(c_qk)
-//          + 2^-31 sum |r|
-// (Phi <= g(c), Phi >= (113/128) g(c) less 2^-31 where c = 0), plus the
-// float32 accumulation, rounding and underflow allowances of the bounded
-// sweep (the product (113/128) r- is rounded to float32 once more).  Nothing is
+//          + 2^-30 sum |r|
+// (Phi <= g(c), Phi >= (113/128) g(c) less 2^-30 where the code was raised to
+// 8), plus the float32 accumulation, rounding and underflow allowances of the
+// bounded sweep (the product (113/128) r- is rounded to float32 once more).
+// A code decodes with one SDWA shift of its byte to 2^-96 g(c), and the
+// weights carry the factor 2^96 (exact), so the products are r g(c) and stay
+// in float32's normal range.  Nothing is
 // done where k_prune kept every key (its L is -inf) or the plane is unusable.
 // Groups of 64 keys (8 waves of 8), 8 lanes per key, each lane 16 queries of
 // every 128 (one 16-byte load), sixteen loads in flight; a block takes every
@@ -732,6 +760,8 @@ __global__ __launch_bounds__(Q8_THREADS) void k_sweep_q8(const HeadDesc *__restr
     float2 v = make_float2(0.0f, 0.0f);
     if (q < D.n) v = *reinterpret_cast<const float2 *>(rpn + 2 * (D.n_off + q));
     v.y *= Q8_KAPPA;
+    v.x *= 0x1p96f;
+    v.y *= 0x1p96f;
     const int64_t i = q >> 7, sb = (q >> 4) & 7, j = (q >> 1) & 7, e = q & 1;
     *reinterpret_cast<float2 *>(s_w + 4 * (64 * i + 8 * j + sb) + 2 * e) = v;
   }
@@ -739,6 +769,7 @@ __global__ __launch_bounds__(Q8_THREADS) void k_sweep_q8(const HeadDesc *__restr
   const int nit = int(D.ldN >> 7);                      // full 128-query steps
   const bool half = (D.ldN & 64) != 0 && 16 * sub < 64;  // this lane's part of a last 64-query step
   const double rs = rabs[h];
+  const uint32_t twenty = 20;
   for (int64_t kb = blockIdx.x; kb * Q8_KEYS < cnt; kb += gridDim.x) {
     const int64_t at = kb * Q8_KEYS + 8 * wave + kq;
     int64_t key = -1;
@@ -753,10 +784,8 @@ __global__ __launch_bounds__(Q8_THREADS) void k_sweep_q8(const HeadDesc *__restr
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
         const f32x4 w01 = ww[8 * (2 * c)], w23 = ww[8 * (2 * c + 1)];  // pairs of queries 4 c .. 4 c + 3
-        const float g0 = __uint_as_float((__builtin_amdgcn_ubfe(cw[c], 0, 8) << 20) + Q8_BASE);
-        const float g1 = __uint_as_float((__builtin_amdgcn_ubfe(cw[c], 8, 8) << 20) + Q8_BASE);
-        const float g2 = __uint_as_float((__builtin_amdgcn_ubfe(cw[c], 16, 8) << 20) + Q8_BASE);
-        const float g3 = __uint_as_float(((cw[c] >> 24) << 20) + Q8_BASE);
+        const float g0 = q8_grid<0>(cw[c], twenty), g1 = q8_grid<1>(cw[c], twenty);
+        const float g2 = q8_grid<2>(cw[c], twenty), g3 = q8_grid<3>(cw[c], twenty);
         const int e = (4 * c) & 7;
         P[e] = fmaf(w01.x, g0, P[e]);
         N[e] = fmaf(w01.y, g0, N[e]);
@@ -793,7 +822,7 @@ __global__ __launch_bounds__(Q8_THREADS) void k_sweep_q8(const HeadDesc *__restr
     if (sub == 0 && key >= 0) {
       const bool valid = key < D.T && sel_slot[D.k_off + key] == 0;
       const double crel = 2.0 * (double(D.ldN >> 6) + 16.0) * 0x1p-24 + 0x1p-21;
-      const double u = (Pd + Nd) + crel * (Pd - Nd) + rs * 0x1p-31 + (rs + double(D.n)) * 0x1p-120;
+      const double u = (Pd + Nd) + crel * (Pd - Nd) + rs * 0x1p-30 + (rs + double(D.n)) * 0x1p-120;
       sw_up[D.kt_off + at] = valid ? u : -INFINITY;
       sw_key[D.kt_off + at] = int(key);
     }

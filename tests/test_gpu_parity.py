@@ -222,6 +222,11 @@ def test_prune_stages_agree(monkeypatch, shape, k, R):
         _say(f"head {i}: 8-bit plane keys {s8.tolist()}; 16-bit plane keys {sa.tolist()} (one stage: {sb.tolist()})")
         assert s8[0] == 0 and np.all(tb["swept_keys8"][i] == 0)
         assert sa[0] == T and np.all(sa <= np.where(s8 > 0, s8, T))
+        # the keys scoring at least the cycle's threshold pass both stages: the
+        # top kR + 1 of every cycle that has that many unselected keys
+        kr = k * R
+        left = T - kr * np.arange(len(sa))
+        assert np.all(sa[1:] >= np.minimum(kr + 1, left[1:]))
         assert np.all(sa[1:] <= sb[1:])
         if n == 4096:
             assert sa[1:].sum() < sb[1:].sum()
