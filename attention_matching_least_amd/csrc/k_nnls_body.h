@@ -4,6 +4,7 @@
 // bound by the latency of their global-memory passes).  The including file
 // defines AMC_NNLS_NT and opens a namespace of its own.
 constexpr int NT = AMC_NNLS_NT;  // threads per block (set by the including file)
+constexpr bool kGrowBlocks = NT > 256;  // entering blocks grow back (the workspace-resident build)
 constexpr int NW = NT / 64;
 constexpr int TB = 16;             // triangular block
 constexpr int NB = 8;              // candidates that may enter together
@@ -148,7 +149,7 @@ struct Blk {
   int cand[NB];              // entering candidates
   int accb[NB];              // accepted candidates, in order
   int ctl[8];                // [1], [4] scan state, [2] accepted count, [3] largest entering block,
-                             // [5] size of the last entering block
+                             // [5] size of the last entering block, [6] an entering variable left
   int wc[NW];                // per-wave counts of a compaction
   int np;                    // free-set size
 };
@@ -1053,7 +1054,10 @@ __device__ __forceinline__ void block_append(const St &S, const double *G, int64
 //    any step is taken.  If it entered alone it is set aside for the rest of
 //    this fit (Lawson and Hanson's guard against cycling on round-off);
 //    otherwise later blocks of candidates are half as large (ctl[3]; one at
-//    a time once it reaches 1).
+//    a time once it reaches 1).  In the workspace-resident build (large
+//    budgets) a block none of whose variables leaves this way doubles the
+//    size again, up to NB (ctl[6] records a drop), so that a refit with many
+//    new keys does not take the rest of them one by one.
 //  - Otherwise the iterate moves toward the solution, as far as feasibility
 //    allows, and the variables that reach zero leave.
 // Only the free-set rows of g change here (by the factor's model); y follows
@@ -1102,6 +1106,7 @@ __device__ __forceinline__ void settle(const St &S, int p, bool have_y, bool sin
         if (tid == 0) {
           S.flag[S.plist[q]] = single ? F_BLOCKED : 0;
           if (!single) bk->ctl[3] = bk->ctl[5] > 1 ? bk->ctl[5] / 2 : 1;
+          bk->ctl[6] = 1;
         }
         __syncthreads();
         remove_at(S, q);
@@ -1226,9 +1231,14 @@ __device__ __forceinline__ void nnls_core(const St &S, const double *G, int64_t 
       break;
     }
     ++iters;
-    if (tid == 0) bk->ctl[5] = nc;
+    if (tid == 0) {
+      bk->ctl[5] = nc;
+      bk->ctl[6] = 0;
+    }
     block_append(S, G, ld, nc, status);
     if (bk->ctl[2] > 0) settle(S, p, true, nc == 1, red);
+    if (kGrowBlocks && tid == 0 && bk->ctl[6] == 0 && bk->ctl[2] == nc)
+      bk->ctl[3] = bk->ctl[3] < NB / 2 ? 2 * bk->ctl[3] : NB;
   }
   __syncthreads();
   *iters_out = iters;
