@@ -342,6 +342,20 @@ __device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   for (int r0 = ((n - 1) / TB) * TB; r0 >= 0; r0 -= TB) {
     const int e = n - r0 < TB ? n - r0 : TB;
+#if AMC_NNLS_NT > 256
+    // the first pass of the column update reads no value the diagonal block
+    // changes: its L loads are issued before the block is solved
+    double pl[TB], pl2[TB];
+    {
+      const int c = tid < r0 ? tid : 0, c2 = tid + NT < r0 ? tid + NT : c;
+      static_for<0, TB>([&](auto K) {
+        constexpr int k = decltype(K)::value;
+        const int rk = tri(k < e ? r0 + k : r0);
+        pl[k] = S.L[rk + c];
+        pl2[k] = S.L[rk + c2];
+      });
+    }
+#endif
     if (wave == 0 && lane < TB) {
       const int i = lane;
       const bool act = i < e;
@@ -368,12 +382,19 @@ __device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
     for (int c = tid; c < r0; c += 2 * NT) {
       const int c2 = c + NT < r0 ? c + NT : c;
       double l[TB], l2[TB];
-      static_for<0, TB>([&](auto K) {
-        constexpr int k = decltype(K)::value;
-        const int rk = tri(k < e ? r0 + k : r0);
-        l[k] = S.L[rk + c];
-        l2[k] = S.L[rk + c2];
-      });
+      if (c == tid) {
+        static_for<0, TB>([&](auto K) {
+          l[decltype(K)::value] = pl[decltype(K)::value];
+          l2[decltype(K)::value] = pl2[decltype(K)::value];
+        });
+      } else {
+        static_for<0, TB>([&](auto K) {
+          constexpr int k = decltype(K)::value;
+          const int rk = tri(k < e ? r0 + k : r0);
+          l[k] = S.L[rk + c];
+          l2[k] = S.L[rk + c2];
+        });
+      }
       const double xc = x[c], xc2 = x[c2];
       double a0 = 0.0, a1 = 0.0, b0 = 0.0, b1 = 0.0;
       static_for<0, TB / 2>([&](auto K) {
