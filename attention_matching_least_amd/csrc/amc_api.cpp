@@ -225,7 +225,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.o_fcount = take(4ull * H);
   pl.o_dn = take(8ull * tt);
   pl.o_L = take(8ull * tri);
-  pl.o_nnL = take(8ull * tri);
+  pl.o_nnL = take(8ull * t2);  // rows of t entries (slotted rows above kNnlsLdsT)
   pl.o_nnP = take(4ull * tt);
   pl.o_nnnp = take(4ull * H);
   pl.o_gA = take(8ull * tt);

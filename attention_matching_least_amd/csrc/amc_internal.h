@@ -99,7 +99,7 @@ struct Buffers {
   int32_t *ols_fcount; // [H]
   double *ols_dn;      // [sum t]  diagonal scaling of the normal matrix
   double *ols_L;       // [sum t*(t+1)/2] packed Cholesky factor of the scaled normal matrix
-  double *nn_L;        // [sum t*(t+1)/2] NNLS factor of the free set, kept between refits
+  double *nn_L;        // [sum t*t] NNLS factor of the free set, kept between refits (at tt_off)
   int32_t *nn_P;       // [sum t]  NNLS free set in factor order
   int32_t *nn_np;      // [H]      NNLS free-set size
   double *nn_vec;      // [sum t][kNnlsVecPerSlot] NNLS vectors of heads above kNnlsLdsT (else null)

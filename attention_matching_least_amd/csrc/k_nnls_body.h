@@ -5,6 +5,10 @@
 // defines AMC_NNLS_NT and opens a namespace of its own.
 constexpr int NT = AMC_NNLS_NT;  // threads per block (set by the including file)
 constexpr bool kGrowBlocks = NT > 256;  // entering blocks grow back (the workspace-resident build)
+// Factor rows in fixed slots of mp entries (the workspace-resident build):
+// a removal rotates the rows below it in place instead of moving every later
+// row up by one.  The LDS build keeps packed rows.
+constexpr bool kSlotRows = NT > 256;
 constexpr int NW = NT / 64;
 constexpr int TB = 16;             // triangular block
 constexpr int NB = 8;              // candidates that may enter together
@@ -165,11 +169,19 @@ struct St {
   double *x0;     // row 0: solve vector (may live apart from rows)
   double *yv;     // row 8: y = L^-1 g_P (may live apart from rows)
   int *plist;     // free set in factor order
+  int *slot;      // slot of each factor row (kSlotRows; positions past np hold the free slots)
   unsigned char *flag;
   Blk *bk;
   int mp;         // row stride (largest p of the system)
   bool lds;       // L lives in LDS (the one-wave solves apply up to kWaveRows rows)
   __device__ __forceinline__ double *row(int b) const { return b == 0 ? x0 : (b == 8 ? yv : rows + b * mp); }
+  // first element of factor row i (column c of row i is L[rowoff(i) + c])
+  __device__ __forceinline__ int rowoff(int i) const {
+    if constexpr (kSlotRows)
+      return slot[i] * mp;
+    else
+      return tri(i);
+  }
 };
 
 // LDS bytes of the state for systems up to maxp variables (LDS variant)
@@ -178,10 +190,14 @@ __host__ __device__ constexpr size_t nnls_smem_bytes(int maxp) {
          ((size_t(maxp) + 15) & ~size_t(15));
 }
 
-// LDS bytes of the global variant: the two solve vectors, when they fit.
-constexpr int kGlobalLdsRowsMax = 4096;
-__host__ __device__ constexpr size_t nnls_global_smem_bytes(int64_t max_t) {
+// LDS bytes of the global variant: the two solve vectors, when they fit,
+// then the row slots (one int per budget slot).
+constexpr int kGlobalLdsRowsMax = 7680;
+__host__ __device__ constexpr size_t nnls_global_vec_bytes(int64_t max_t) {
   return max_t <= kGlobalLdsRowsMax ? size_t(16) * size_t(max_t) : 0;
+}
+__host__ __device__ constexpr size_t nnls_global_smem_bytes(int64_t max_t) {
+  return nnls_global_vec_bytes(max_t) + size_t(4) * ((size_t(max_t) + 3) & ~size_t(3));
 }
 
 __device__ __forceinline__ St carve_lds(char *base, int maxp, Blk *bk) {
@@ -202,14 +218,21 @@ __device__ __forceinline__ St carve_lds(char *base, int maxp, Blk *bk) {
   s.x0 = d;
   s.yv = d + 8 * maxp;
   d += NROW * maxp;
+  s.slot = nullptr;
   s.plist = reinterpret_cast<int *>(d);
   s.flag = reinterpret_cast<unsigned char *>(s.plist + maxp);
   return s;
 }
 
 // Global-memory state of one head: u, g, dg, the scratch rows, then the flag
-// bytes; the solve vectors go to LDS (lds, 2 mp doubles) when given.
-__device__ __forceinline__ St carve_global(double *vec, double *L, int32_t *plist, int mp, Blk *bk, double *lds) {
+// bytes (and after them, from the next 16-byte boundary, the row slots kept
+// between refits); the solve vectors go to LDS (lds, 2 mp doubles) when
+// given, the working copy of the row slots to slot_lds.
+__host__ __device__ inline int32_t *persisted_slots(double *vec, int mp) {
+  return reinterpret_cast<int32_t *>(reinterpret_cast<unsigned char *>(vec + (3 + NROW) * mp) + ((mp + 15) & ~15));
+}
+__device__ __forceinline__ St carve_global(double *vec, double *L, int32_t *plist, int mp, Blk *bk, double *lds,
+                                           int *slot_lds) {
   St s;
   s.mp = mp;
   s.bk = bk;
@@ -223,6 +246,7 @@ __device__ __forceinline__ St carve_global(double *vec, double *L, int32_t *plis
   s.yv = lds ? lds + mp : s.rows + 8 * mp;
   s.flag = reinterpret_cast<unsigned char *>(vec + (3 + NROW) * mp);
   s.plist = plist;
+  s.slot = slot_lds;
   return s;
 }
 static_assert(kNnlsVecPerSlot == 3 + NROW + 1, "global NNLS state layout");
@@ -238,7 +262,7 @@ __device__ __forceinline__ void fwd_blk(const St &S, int n, int nr) {
     if (wave < nr && lane < TB) {
       const int i = lane;
       const bool act = i < e;
-      const int rb = act ? tri(r0 + i) + r0 : 0;
+      const int rb = act ? S.rowoff(r0 + i) + r0 : 0;
       double Lrow[TB];
       static_for<0, TB>([&](auto J) {
         constexpr int j = decltype(J)::value;
@@ -282,7 +306,7 @@ __device__ __forceinline__ void fwd_blk(const St &S, int n, int nr) {
       const double *xs = S.bk->xblk;
       for (int row = r0 + TB + tid; row < n; row += 2 * NT) {
         const int row2 = row + NT < n ? row + NT : row;
-        const int rb = tri(row) + r0, rb2 = tri(row2) + r0;
+        const int rb = S.rowoff(row) + r0, rb2 = S.rowoff(row2) + r0;
         double La[TB], Lb[TB], xa[NRHS], xb2[NRHS];
         static_for<0, TB>([&](auto J) {
           constexpr int j = decltype(J)::value;
@@ -315,7 +339,7 @@ __device__ __forceinline__ void fwd_blk(const St &S, int n, int nr) {
       // rows below: r_row -= L[row, block] x_block
       const double *xs = S.bk->xblk;
       for (int row = r0 + TB + tid; row < n; row += NT) {
-        const int rb = tri(row) + r0;
+        const int rb = S.rowoff(row) + r0;
         double Lr[TB];
         static_for<0, TB>([&](auto J) {
           constexpr int j = decltype(J)::value;
@@ -350,7 +374,7 @@ __device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
       const int c = tid < r0 ? tid : 0, c2 = tid + NT < r0 ? tid + NT : c;
       static_for<0, TB>([&](auto K) {
         constexpr int k = decltype(K)::value;
-        const int rk = tri(k < e ? r0 + k : r0);
+        const int rk = S.rowoff(k < e ? r0 + k : r0);
         pl[k] = S.L[rk + c];
         pl2[k] = S.L[rk + c2];
       });
@@ -362,9 +386,9 @@ __device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
       double Lc[TB];  // column i of the diagonal block, rows below i
       static_for<0, TB>([&](auto K) {
         constexpr int kk = decltype(K)::value;
-        Lc[kk] = (act && kk > i && kk < e) ? S.L[tri(r0 + kk) + r0 + i] : 0.0;
+        Lc[kk] = (act && kk > i && kk < e) ? S.L[S.rowoff(r0 + kk) + r0 + i] : 0.0;
       });
-      const double rd = act ? 1.0 / S.L[tri(r0 + i) + r0 + i] : 0.0;
+      const double rd = act ? 1.0 / S.L[S.rowoff(act ? r0 + i : r0) + r0 + i] : 0.0;
       double xv = act ? x[r0 + i] : 0.0;
       static_for<0, TB>([&](auto K) {
         constexpr int kk = TB - 1 - decltype(K)::value;
@@ -390,7 +414,7 @@ __device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
       } else {
         static_for<0, TB>([&](auto K) {
           constexpr int k = decltype(K)::value;
-          const int rk = tri(k < e ? r0 + k : r0);
+          const int rk = S.rowoff(k < e ? r0 + k : r0);
           l[k] = S.L[rk + c];
           l2[k] = S.L[rk + c2];
         });
@@ -416,7 +440,7 @@ __device__ __forceinline__ void bwd_blk(const St &S, int n, double *x) {
       double l[TB];
       static_for<0, TB>([&](auto K) {
         constexpr int k = decltype(K)::value;
-        l[k] = S.L[tri(k < e ? r0 + k : r0) + c];
+        l[k] = S.L[S.rowoff(k < e ? r0 + k : r0) + c];
       });
       double a0 = 0.0, a1 = 0.0;
       static_for<0, TB / 2>([&](auto K) {
@@ -718,10 +742,14 @@ __device__ __forceinline__ int row_of(int s) {
   return i;
 }
 
-// Deletes factor position q: rows below move up one row without column q,
-// then the trailing rows absorb the removed column by a rank-one update
+// Deletes factor position q: rows below move up one position without column
+// q, then the trailing rows absorb the removed column by a rank-one update
 // (Givens rotations, applied 16 columns at a time).  y = L^-1 g_P follows:
 // its entries below q take the same rotations, with y_q as the extra entry.
+// Packed rows move in memory; slotted rows (kSlotRows) stay in their slots,
+// the removed row's slot goes to the free end of the slot list, and the
+// rotation pass reads each row's columns past q one place to the right of
+// where it writes them.
 __device__ __forceinline__ void remove_at(const St &S, int q) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   Blk *bk = S.bk;
@@ -729,19 +757,29 @@ __device__ __forceinline__ void remove_at(const St &S, int q) {
   double *xc = S.rows + 7 * S.mp;
   double *yv = S.yv;
   double z = yv[q];  // y of the removed position, rotated into the trailing entries below
-  for (int i = q + 1 + tid; i < np; i += NT) xc[i - 1] = S.L[tri(i) + q];
+  const int freed = kSlotRows ? S.slot[q] : 0;
+  if constexpr (!kSlotRows)
+    for (int i = q + 1 + tid; i < np; i += NT) xc[i - 1] = S.L[tri(i) + q];
   // Every element moves to a lower index, so chunks taken in increasing
   // source order never overwrite a source that is still to be read.
   for (int base = q; base < n2; base += NT) {
     const int k = base + tid;
     const int pv = k < n2 ? S.plist[k + 1] : 0;
     const double yk = k < n2 ? yv[k + 1] : 0.0;
+    int sv = 0;
+    if constexpr (kSlotRows) sv = k < n2 ? S.slot[k + 1] : 0;
     __syncthreads();
     if (k < n2) {
       S.plist[k] = pv;
       yv[k] = yk;
+      if constexpr (kSlotRows) S.slot[k] = sv;
     }
   }
+  if constexpr (kSlotRows) {
+    if (tid == 0) S.slot[n2] = freed;
+    __syncthreads();
+    for (int k = q + tid; k < n2; k += NT) xc[k] = S.L[S.rowoff(k) + q];
+  } else {
   const int s0 = tri(q + 1), s1 = tri(np);
   for (int base = s0; base < s1; base += NT * 16) {
     double v[16];
@@ -766,9 +804,11 @@ __device__ __forceinline__ void remove_at(const St &S, int q) {
       if (dst[u] >= 0) S.L[dst[u]] = v[u];
     });
   }
+  }
   __syncthreads();
   // rank-one update: L' L'^T = L L^T + x x^T on positions q..n2-1
-  if (S.lds && n2 <= kWaveRows) {
+  constexpr int sh = kSlotRows ? 1 : 0;  // column offset of a row's unrotated entries past q
+  if (!kSlotRows && S.lds && n2 <= kWaveRows) {
     // in wave 0: rotation k comes from (L_kk, x_k), read from lane k's
     // registers, and turns column k of every row below it at once
     if (wave == 0) {
@@ -851,11 +891,11 @@ __device__ __forceinline__ void remove_at(const St &S, int q) {
     if (wave == 0 && lane < TB) {
       const int i = lane;
       const bool act = i < e;
-      const int rb = act ? tri(k0 + i) + k0 : 0;
+      const int rb = act ? S.rowoff(k0 + i) + k0 : 0;
       double Lr[TB];
       static_for<0, TB>([&](auto J) {
         constexpr int j = decltype(J)::value;
-        Lr[j] = (act && j <= i) ? S.L[rb + j] : 0.0;
+        Lr[j] = (act && j <= i) ? S.L[rb + j + sh] : 0.0;
       });
       double xv = act ? xc[k0 + i] : 0.0;
       double yl = act ? yv[k0 + i] : 0.0;
@@ -893,11 +933,11 @@ __device__ __forceinline__ void remove_at(const St &S, int q) {
     __syncthreads();
     if (k0 + TB < n2) {
       for (int row = k0 + TB + tid; row < n2; row += NT) {
-        const int rb = tri(row) + k0;
+        const int rb = S.rowoff(row) + k0;
         double Lr[TB];
         static_for<0, TB>([&](auto J) {
           constexpr int j = decltype(J)::value;
-          Lr[j] = S.L[rb + j];
+          Lr[j] = S.L[rb + j + sh];
         });
         double xv = xc[row];
         static_for<0, TB>([&](auto K) {
@@ -1051,7 +1091,7 @@ __device__ __forceinline__ void block_append(const St &S, const double *G, int64
   for (int a = 0; a < nacc; ++a) {
     const int b = bk->accb[a];
     const int pos = np0 + a;
-    const int base = tri(pos);
+    const int base = S.rowoff(pos);
     const double *rb = S.row(b + 1);
     for (int k = tid; k < np0; k += NT) S.L[base + k] = rb[k];
     if (tid < a) S.L[base + np0 + tid] = bk->E[a * NB + tid];
@@ -1369,11 +1409,14 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
   const int tid = threadIdx.x;
   const int p = int(S0) + Kc;
   const int np_in = S0 == 0 ? 0 : nn_np[h];
-  double *Lg = nn_L + D.tri_off;
+  double *Lg = nn_L + D.tt_off;
   int32_t *Pg = nn_P + D.t_off;
-  // global variant: maxp > 0 means the launch gave LDS for two vectors of maxp
+  // global variant: maxp > 0 means the launch gave LDS for two vectors of
+  // maxp; the row slots follow them
   double *lds_rows = (kGlobal && maxp > 0 && D.t <= maxp) ? reinterpret_cast<double *>(smem) : nullptr;
-  const St S = kGlobal ? carve_global(nn_vec + D.t_off * kNnlsVecPerSlot, Lg, Pg, int(D.t), &bk, lds_rows)
+  int *lds_slot = reinterpret_cast<int *>(smem + (maxp > 0 ? size_t(16) * size_t(maxp) : 0));
+  double *vec_g = kGlobal ? nn_vec + D.t_off * kNnlsVecPerSlot : nullptr;
+  const St S = kGlobal ? carve_global(vec_g, Lg, Pg, int(D.t), &bk, lds_rows, lds_slot)
                        : carve_lds(smem, maxp, &bk);
   if (tid == 0) {
     sh_status = 0;
@@ -1398,6 +1441,11 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
     }
     for (int k = tid; k < np_in; k += NT) S.plist[k] = Pg[k];
   }
+  if constexpr (kGlobal && kSlotRows) {
+    // the slots as the last refit left them (any order serves an empty factor)
+    const int32_t *sg = persisted_slots(vec_g, int(D.t));
+    for (int k = tid; k < int(D.t); k += NT) S.slot[k] = np_in > 0 ? sg[k] : k;
+  }
   __syncthreads();
   const double tol = nnls_setup(S, G + D.tt_off, D.t, p, bvec + D.t_off, gA + D.t_off, w + D.t_off, int(S0), prm,
                                 &red);
@@ -1412,6 +1460,10 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
   if (!kGlobal) {
     for (int e = tid; e < tri(np); e += NT) Lg[e] = S.L[e];
     for (int k = tid; k < np; k += NT) Pg[k] = S.plist[k];
+  }
+  if constexpr (kGlobal && kSlotRows) {
+    int32_t *sg = persisted_slots(vec_g, int(D.t));
+    for (int k = tid; k < int(D.t); k += NT) sg[k] = S.slot[k];
   }
   if (tid == 0) {
     nn_np[h] = np;

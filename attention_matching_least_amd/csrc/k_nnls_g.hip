@@ -22,7 +22,7 @@ hipError_t launch_nnls_global(const Dims &dm, const Buffers &b, int cycle, int k
                                      hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_nnls_cycle<true>, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.bvec, b.gA, b.w,
-                     cycle, kR, polish, np, bytes ? int(dm.max_t) : 0, b.nn_L, b.nn_P, b.nn_np, b.nn_vec, b.tr_iters,
+                     cycle, kR, polish, np, nnls_global_vec_bytes(dm.max_t) ? int(dm.max_t) : 0, b.nn_L, b.nn_P, b.nn_np, b.nn_vec, b.tr_iters,
                      b.tr_weight, b.head_status);
   return hipGetLastError();
 }

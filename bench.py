@@ -343,7 +343,7 @@ def main():
                     help="only run three device-to-device copies of BYTES (the reference kernel for "
                          "scaling HBM byte counters)")
     ap.add_argument("--heads", type=int, default=0, help="workload 3: heads to run (0: all 288)")
-    ap.add_argument("--head-batch", type=int, default=96, help="workload 3: heads per compaction call")
+    ap.add_argument("--head-batch", type=int, default=144, help="workload 3: heads per compaction call")
     ap.add_argument("--cpu-sample", type=int, default=3, help="oracle heads timed for the CPU baseline (0: skip)")
     ap.add_argument("--workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
     ap.add_argument("--no-timer", action="store_true", help="skip the kernel pass (per-kernel events, roofline)")
