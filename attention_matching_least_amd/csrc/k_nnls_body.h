@@ -656,13 +656,16 @@ __device__ __forceinline__ void snapshot(const St &S, int p) {
 // When few variables changed, the row is read at the changed positions only
 // (row 1: their indices, in increasing order, and their scaled change packed
 // in row 3).  One wave per zero variable (list in row 4), lanes over the row
-// in a fixed order, so the result does not depend on timing.
+// in a fixed order, so the result does not depend on timing.  Where the
+// solve vector lives apart from the scratch rows (in LDS), the dense change
+// takes its place: every wave reads it once per zero variable, and the solve
+// vector holds nothing between a settle and the next block entry.
 __device__ __forceinline__ void sync_z(const St &S, const double *G, int64_t ld, int p) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int mp = S.mp;
   Blk *bk = S.bk;
   int *lst = reinterpret_cast<int *>(S.rows + mp);
-  double *dv = S.rows + 2 * mp;
+  double *dv = S.x0 != S.rows ? S.x0 : S.rows + 2 * mp;
   double *dvc = S.rows + 3 * mp;
   int *zl = reinterpret_cast<int *>(S.rows + 4 * mp);
   const double *us = S.rows + 9 * mp;
