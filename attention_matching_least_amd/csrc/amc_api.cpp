@@ -128,7 +128,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   dm.in_bf16 = p->in_dtype == AMC_BF16;
   dm.scale = p->scale > 0.0f ? double(p->scale) : 1.0 / std::sqrt(double(d));
   pl.desc.assign(H, HeadDesc{});
-  int64_t phi = 0, nn = 0, tt = 0, t2 = 0, panel = 0, cblk = 0, sblk = 0, cyc = 0, TT = 0, tri = 0, vt = 0, ktr = 0;
+  int64_t phi = 0, nn = 0, tt = 0, t2 = 0, panel = 0, cblk = 0, sblk = 0, cyc = 0, TT = 0, vt = 0, ktr = 0;
   for (int h = 0; h < H; ++h) {
     HeadDesc &D = pl.desc[h];
     D.n = p->cu_q[h + 1] - p->cu_q[h];
@@ -152,7 +152,6 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     D.sblk_off = sblk;
     D.n_sblk = ceil_div(D.n, kShiftRows);
     D.cyc_off = cyc;
-    D.tri_off = tri;
     if (!features_only) {
       if (D.t > kMaxBudget) return AMC_ERR_UNSUPPORTED;
       if (D.n_cblk > kMaxSweepBlocks) return AMC_ERR_UNSUPPORTED;
@@ -164,7 +163,6 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     nn += D.n;
     tt += D.t;
     t2 += D.t * D.t;
-    tri += D.t * (D.t + 1) / 2;
     panel += D.t * D.n;
     cblk += D.n_cblk;
     sblk += D.n_sblk;
@@ -224,8 +222,11 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.o_flist = take(4ull * tt);
   pl.o_fcount = take(4ull * H);
   pl.o_dn = take(8ull * tt);
-  pl.o_L = take(8ull * tri);
   pl.o_nnL = take(8ull * t2);  // rows of t entries (slotted rows above kNnlsLdsT)
+  // The value fit's packed factor of a head takes the first t(t+1)/2 entries
+  // of that head's NNLS factor: it is formed after the head's last refit, on
+  // the same stream, and the NNLS factor is not read again in the call.
+  pl.o_L = pl.o_nnL;
   pl.o_nnP = take(4ull * tt);
   pl.o_nnnp = take(4ull * H);
   pl.o_gA = take(8ull * tt);

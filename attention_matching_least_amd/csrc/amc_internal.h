@@ -42,12 +42,11 @@ struct HeadDesc {
   int64_t sblk_off;       // first logit-maximum block of the head
   int64_t n_sblk;         // logit-maximum blocks of the head
   int64_t cyc_off;        // first cycle of the head in the per-cycle trace arrays
-  int64_t tri_off;        // first element of the head's packed triangle (value-fit factor)
   int64_t vt_off;         // first element of the head's transposed value tiles (bf16 inputs)
   int64_t kt_off;         // first row of the head in the arrays of keys padded to whole 64-key tiles
   int64_t ldN;            // stored planes: column stride (n rounded up to 64)
 };
-static_assert(sizeof(HeadDesc) == 20 * 8, "HeadDesc layout");
+static_assert(sizeof(HeadDesc) == 19 * 8, "HeadDesc layout");
 
 // Device pointers of the workspace carve-up and of the caller's buffers.
 struct Buffers {
@@ -98,7 +97,7 @@ struct Buffers {
   int32_t *ols_flist;  // [sum t]  slots with w > 0, ascending
   int32_t *ols_fcount; // [H]
   double *ols_dn;      // [sum t]  diagonal scaling of the normal matrix
-  double *ols_L;       // [sum t*(t+1)/2] packed Cholesky factor of the scaled normal matrix
+  double *ols_L;       // packed Cholesky factor of the scaled normal matrix, at tt_off (shares nn_L)
   double *nn_L;        // [sum t*t] NNLS factor of the free set, kept between refits (at tt_off)
   int32_t *nn_P;       // [sum t]  NNLS free set in factor order
   int32_t *nn_np;      // [H]      NNLS free-set size

@@ -214,7 +214,7 @@ __global__ __launch_bounds__(NT) void k_ols_factor(const HeadDesc *__restrict__ 
     if (tid == 0 && head_status) atomicOr(head_status + h, int32_t(AMC_HS_CHOL_JITTER));
     __syncthreads();
   }
-  for (int e = tid; e < tri(f); e += NT) Lout[Dh.tri_off + e] = Ls[e];
+  for (int e = tid; e < tri(f); e += NT) Lout[Dh.tt_off + e] = Ls[e];
   for (int k = tid; k < f; k += NT) {
     flist[Dh.t_off + k] = sf[k];
     dn[Dh.t_off + k] = sdn[k];
@@ -253,7 +253,7 @@ __global__ __launch_bounds__(NT) void k_ols_trsm(const HeadDesc *__restrict__ de
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   double *Ls = sm;
-  for (int e = tid; e < tri(f); e += NT) Ls[e] = Lg[Dh.tri_off + e];
+  for (int e = tid; e < tri(f); e += NT) Ls[e] = Lg[Dh.tt_off + e];
   // keys with w = 0 get a zero value row
   for (int e = tid; e < t * NCB; e += NT) {
     const int a = e / NCB, c = e % NCB;
@@ -466,7 +466,7 @@ __global__ __launch_bounds__(NT) void k_ols_factor_g(const HeadDesc *__restrict_
   const int32_t *fl = flist + Dh.t_off;
   const double *dnh = dn + Dh.t_off;
   const double *Nh = N + Dh.tt_off;
-  double *Lh = L + Dh.tri_off;
+  double *Lh = L + Dh.tt_off;
   double jitter = 0.0;
   for (int attempt = 0; attempt < 6; ++attempt) {
     for (int e = tid; e < tri(f); e += NT) {
@@ -619,7 +619,7 @@ __global__ __launch_bounds__(NT) void k_ols_trsm_g(const HeadDesc *__restrict__ 
   const int tid = threadIdx.x;
   const int32_t *fl = flist + Dh.t_off;
   const double *dnh = dn + Dh.t_off;
-  const double *Lh = L + Dh.tri_off;
+  const double *Lh = L + Dh.tt_off;
   auto X = [&](int k) -> double * { return rhs + (Dh.t_off + fl[k]) * D + c0; };
   for (int e = tid; e < t * NC; e += NT) {
     const int a = e / NC, c = e % NC;
