@@ -70,6 +70,7 @@ struct Plan {
            o_surv = 0, o_survcnt = 0, o_pruneL = 0, o_q8 = 0, o_q8bad = 0, o_surv2 = 0, o_surv2cnt = 0,
            total = 0;
   bool store_q8 = false;  // the 8-bit plane of the second pruning stage fits the budget too
+  bool alias_digits = false;  // digit rows and value tiles lie in the panel (recompute mode)
 };
 
 // AMC_PRUNE_Q8=0 leaves the 8-bit plane and the second pruning stage out
@@ -254,12 +255,22 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     }
   }
   if (dm.in_bf16) {
+    // In recompute mode the digit rows and the value tiles serve only the
+    // mass-feature pass, which every head group finishes before any group
+    // writes its first panel rows (amc_compact orders the groups so): then
+    // they take the start of the panel when they fit there.
+    const uint64_t dig_bytes = align256(2ull * vt) + align256(5ull * d * nn) + align256(4ull * nn) +
+                               align256((5ull * d + 16) * ktr) + align256(16ull * ktr);
+    pl.alias_digits = !features_only && !pl.store_phi && dig_bytes <= 8ull * uint64_t(panel);
+    const uint64_t resume = off;
+    if (pl.alias_digits) off = pl.o_panel;
     pl.o_vt = take(2ull * vt);  // transposed value tiles of the mass-feature kernel
     // digit form of the rows for the int8 logits
     pl.o_qdig = take(5ull * d * nn);
     pl.o_qexp = take(4ull * nn);
     pl.o_kdig = take((5ull * d + 16) * ktr);
     pl.o_ktab = take(16ull * ktr);
+    if (pl.alias_digits) off = resume;
     pl.o_f64h = take(4ull * 3 * H);  // flags, the list of flagged heads, its length (per head group)
   }
   pl.total = off;
@@ -582,7 +593,8 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
     return true;
   };
   hipEvent_t ev_start = nullptr;
-  std::vector<hipEvent_t> ev_phi(size_t(ngroups), nullptr), ev_done(size_t(ngroups), nullptr);
+  std::vector<hipEvent_t> ev_phi(size_t(ngroups), nullptr), ev_done(size_t(ngroups), nullptr),
+      ev_pre(size_t(ngroups), nullptr);
   if (ngroups > 1) {
     bool ok = new_event(&ev_start) && hipEventRecord(ev_start, stream) == hipSuccess;
     for (int g = 1; ok && g < ngroups; ++g) {
@@ -590,14 +602,22 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
       if (!ok) gs[size_t(g)] = stream;
       ok = ok && hipStreamWaitEvent(gs[size_t(g)], ev_start, 0) == hipSuccess;
     }
-    for (int g = 0; ok && g < ngroups; ++g) ok = new_event(&ev_phi[size_t(g)]) && new_event(&ev_done[size_t(g)]);
+    for (int g = 0; ok && g < ngroups; ++g)
+      ok = new_event(&ev_phi[size_t(g)]) && new_event(&ev_done[size_t(g)]) &&
+           (!pl.alias_digits || new_event(&ev_pre[size_t(g)]));
     if (!ok) {
       cleanup();
       return AMC_ERR_HIP;
     }
   }
   amc_status result = AMC_OK;
+  // With the digit rows in the panel, every group's mass-feature pass is
+  // enqueued first (pass 0) and every group's selection waits for all of them
+  // (pass 1); otherwise one pass does both.
+  const int npass = pl.alias_digits ? 2 : 1;
+  for (int pass = 0; pass < npass && result == AMC_OK; ++pass)
   for (int g = 0; g < ngroups && result == AMC_OK; ++g) {
+    const bool do_phi = pass == 0, do_sel = pass == npass - 1;
     const int h0 = group_bound(dm.H, ngroups, g), h1 = group_bound(dm.H, ngroups, g + 1);
     const Buffers bg = head_range(b, h0, dm.max_qblk);
     Dims dg = dm;
@@ -610,13 +630,20 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
       // previous group's mass features; its own wait for them (one at a time,
       // matrix-bound) comes just before them, and the float64 fallback heads
       // run beside the next group's
-      AMC_LAUNCH(AMC_K_SHIFT, launch_shift(dg, bg, stream));
-      if (bg.vt) AMC_LAUNCH(AMC_K_INIT, launch_vt(dg, bg, stream));
-      if (bg.qdig) AMC_LAUNCH(AMC_K_DIGITS, launch_digits(dg, bg, stream));
-      if (g > 0 && hipStreamWaitEvent(stream, ev_phi[size_t(g - 1)], 0) != hipSuccess) return AMC_ERR_HIP;
-      AMC_LAUNCH(AMC_K_PHI, launch_phi(dg, bg, pl.store_phi ? 2 : 0, stream));
-      if (ngroups > 1 && hipEventRecord(ev_phi[size_t(g)], stream) != hipSuccess) return AMC_ERR_HIP;
-      if (bg.qdig) AMC_LAUNCH(AMC_K_PHI_F64, launch_phi_fallback(dg, bg, pl.store_phi ? 2 : 0, stream));
+      if (do_phi) {
+        AMC_LAUNCH(AMC_K_SHIFT, launch_shift(dg, bg, stream));
+        if (bg.vt) AMC_LAUNCH(AMC_K_INIT, launch_vt(dg, bg, stream));
+        if (bg.qdig) AMC_LAUNCH(AMC_K_DIGITS, launch_digits(dg, bg, stream));
+        if (g > 0 && hipStreamWaitEvent(stream, ev_phi[size_t(g - 1)], 0) != hipSuccess) return AMC_ERR_HIP;
+        AMC_LAUNCH(AMC_K_PHI, launch_phi(dg, bg, pl.store_phi ? 2 : 0, stream));
+        if (ngroups > 1 && hipEventRecord(ev_phi[size_t(g)], stream) != hipSuccess) return AMC_ERR_HIP;
+        if (bg.qdig) AMC_LAUNCH(AMC_K_PHI_F64, launch_phi_fallback(dg, bg, pl.store_phi ? 2 : 0, stream));
+        if (npass > 1 && ngroups > 1 && hipEventRecord(ev_pre[size_t(g)], stream) != hipSuccess) return AMC_ERR_HIP;
+      }
+      if (!do_sel) return AMC_OK;
+      if (npass > 1)
+        for (int g2 = 0; g2 < ngroups; ++g2)
+          if (g2 != g && hipStreamWaitEvent(stream, ev_pre[size_t(g2)], 0) != hipSuccess) return AMC_ERR_HIP;
       for (int c = 0; c < cycles; ++c) {
         if (pl.store_phi) {
           // bounded sweep and float64 rescoring of the band; the heads whose

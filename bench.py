@@ -241,9 +241,12 @@ SELECT_CLASSES = ("init", "shift", "phi", "sweep", "merge", "panel", "gram", "nn
 
 
 def bench_long(args):
-    """The 60k-token stack: key-selection seconds (shift, mass features,
-    sweeps with Phi recomputed, panel, Gram, NNLS refits, residuals; the value
-    fit and packing are timed apart), over the heads in batches sized for HBM."""
+    """The 60k-token stack: wall-clock seconds of the compaction calls over all
+    heads (key selection: shift, mass features, sweeps with Phi recomputed,
+    panel, Gram, NNLS refits, residuals; plus the value fit and packing, so the
+    figure bounds the key selection from above), in as few calls as the free
+    device memory allows.  The per-kernel sums are reported beside it; with
+    head groups on several streams they overlap and exceed the wall time."""
     import torch
 
     from attention_matching_least_amd import amc
@@ -251,15 +254,29 @@ def bench_long(args):
     dev = torch.device("cuda:0")
     w = synth.workload(3)
     H = args.heads if args.heads > 0 else w.num_heads
-    B = max(1, min(args.head_batch, H))
     # all inputs are generated before anything touches the GPU (the worker
     # processes are forked from this one)
     t_gen = time.perf_counter()
+    flat = []
     with ProcessPoolExecutor(max_workers=args.workers) as ex:
-        allparts = []
-        for b0 in range(0, H, B):
-            allparts.append(list(ex.map(_head_bits, [(3, h) for h in range(b0, min(H, b0 + B))], chunksize=1)))
-            print(f"generated heads up to {min(H, b0 + B)}", file=sys.stderr, flush=True)
+        for g0 in range(0, H, 48):
+            flat.extend(ex.map(_head_bits, [(3, h) for h in range(g0, min(H, g0 + 48))], chunksize=1))
+            print(f"generated heads up to {min(H, g0 + 48)}", file=sys.stderr, flush=True)
+    if args.head_batch > 0:
+        B = max(1, min(args.head_batch, H))
+    else:
+        # the fewest calls whose workspace and inputs fit in free memory, less 4 GB
+        free = torch.cuda.mem_get_info(dev)[0] - (4 << 30)
+        per_in = w.n * w.d * 2 + 2 * w.T * w.d * 2
+        for ncall in range(1, H + 1):
+            B = -(-H // ncall)
+            need = amc.compact_workspace_bytes([w.n * h for h in range(B + 1)], [w.T * h for h in range(B + 1)],
+                                               w.budgets[:B], w.d, select="batched", topk=w.topk,
+                                               refit_every=w.refit_every, phi_budget_bytes=0)
+            if need + B * per_in <= free:
+                break
+    allparts = [flat[b0:b0 + B] for b0 in range(0, H, B)]
+    flat = None
     gen_s = time.perf_counter() - t_gen
     timer = None if args.no_timer else amc.Timer()
     sel_ms, call_s, statuses, kern = 0.0, 0.0, [], {}
@@ -301,7 +318,8 @@ def bench_long(args):
     scale = w.num_heads / H
     print(json.dumps({
         "metric": "OMP key-select s at T=60k",
-        "value": round(sel_s * scale, 2) if sel_s is not None else None,
+        "value": round(call_s * scale, 2),
+        "value_covers": "wall-clock seconds of the compaction calls: key selection plus the value fit and packing",
         "unit": "s",
         "n_gpus": 1,
         "steps": 1,
@@ -314,9 +332,10 @@ def bench_long(args):
         "config": {"workload": w.name, "heads_run": H, "heads_total": w.num_heads, "head_batch": B, "T": w.T,
                    "n": w.n, "d": w.d, "budget": w.budgets[0], "topk": w.topk, "refit_every": w.refit_every,
                    "phi": "recomputed in every sweep"},
-        "key_select_s_measured": round(sel_s, 3) if sel_s is not None else None,
+        "calls": len(allparts),
         "extrapolated_from_heads": H if H < w.num_heads else None,
         "full_call_s_measured": round(call_s, 3),
+        "key_select_kernel_sum_s": round(sel_s, 3) if sel_s is not None else None,
         "kernels_ms_measured": {k: round(v, 1) for k, v in kern.items()},
         "head_status_nonzero": int(np.count_nonzero(status)),
         "input_generation_s": round(gen_s, 1),
@@ -343,7 +362,8 @@ def main():
                     help="only run three device-to-device copies of BYTES (the reference kernel for "
                          "scaling HBM byte counters)")
     ap.add_argument("--heads", type=int, default=0, help="workload 3: heads to run (0: all 288)")
-    ap.add_argument("--head-batch", type=int, default=144, help="workload 3: heads per compaction call")
+    ap.add_argument("--head-batch", type=int, default=0,
+                    help="workload 3: heads per compaction call (0: as many as free memory allows)")
     ap.add_argument("--cpu-sample", type=int, default=3, help="oracle heads timed for the CPU baseline (0: skip)")
     ap.add_argument("--workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
     ap.add_argument("--no-timer", action="store_true", help="skip the kernel pass (per-kernel events, roofline)")
