@@ -52,6 +52,13 @@ void timer_end(Timer *t, int c, hipStream_t s) {
 // planning
 // ---------------------------------------------------------------------------
 static inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
+
+// AMC_DIGITS_IN_PANEL=0 keeps the digit rows and value tiles apart from the
+// panel in recompute mode (for comparison runs).
+static bool digits_in_panel_enabled() {
+  const char *v = std::getenv("AMC_DIGITS_IN_PANEL");
+  return !(v && v[0] == '0');
+}
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
@@ -261,7 +268,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     // they take the start of the panel when they fit there.
     const uint64_t dig_bytes = align256(2ull * vt) + align256(5ull * d * nn) + align256(4ull * nn) +
                                align256((5ull * d + 16) * ktr) + align256(16ull * ktr);
-    pl.alias_digits = !features_only && !pl.store_phi && dig_bytes <= 8ull * uint64_t(panel);
+    pl.alias_digits = !features_only && !pl.store_phi && dig_bytes <= 8ull * uint64_t(panel) && digits_in_panel_enabled();
     const uint64_t resume = off;
     if (pl.alias_digits) off = pl.o_panel;
     pl.o_vt = take(2ull * vt);  // transposed value tiles of the mass-feature kernel

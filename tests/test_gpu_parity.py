@@ -310,6 +310,40 @@ def test_compact_recompute_sweep(dtype, d, k, R):
         _assert_ok(replay_check(h.Q, h.K, h.V, budgets[i], k, R, res, i, beta_in=betas[i], trace=tr), f"head{i}")
 
 
+
+def test_recompute_digit_rows_in_panel(monkeypatch):
+    """Recompute mode with budgets large enough that the int8 digit rows and
+    value tiles of the mass-feature pass lie in the panel buffer (they are
+    written before any panel row, by every head group, and the selection of
+    each group waits for all of them).  Full replay against the oracle, and
+    bitwise the same outputs as with those buffers kept apart."""
+    shapes = [(1024, 1024, 300), (768, 1024, 240)]
+
+    def a256(x):
+        return (x + 255) // 256 * 256
+
+    # sizing precondition: the buffers shared with the panel fit in it
+    nn = sum(n for n, _, _ in shapes)
+    ktr = sum((T + 63) // 64 * 64 for _, T, _ in shapes)
+    vt = sum((T + 63) // 64 * 72 * 128 for _, T, _ in shapes)
+    dig = a256(2 * vt) + a256(5 * 128 * nn) + a256(4 * nn) + a256((5 * 128 + 16) * ktr) + a256(16 * ktr)
+    assert dig <= 8 * sum(n * t for n, _, t in shapes)
+    heads = [synth.make_head([36, i], n, T, 128, True, "bf16") for i, (n, T, _) in enumerate(shapes)]
+    budgets = [t for _, _, t in shapes]
+    _say(f"recompute with digit rows in the panel, shapes={shapes}")
+    res = _run(heads, budgets, "bf16", 4, 2, phi_budget_bytes=0)
+    hs = res.head_status.cpu().numpy()
+    _say(f"head status {hs}")
+    assert np.all(hs & (amc.HS_NNLS_CAP | amc.HS_NONFINITE) == 0), hs
+    monkeypatch.setenv("AMC_DIGITS_IN_PANEL", "0")
+    apart = _run(heads, budgets, "bf16", 4, 2, phi_budget_bytes=0)
+    assert torch.equal(res.sel_idx, apart.sel_idx)
+    assert torch.equal(res.beta, apart.beta)
+    assert torch.equal(res.Ck, apart.Ck) and torch.equal(res.Cv, apart.Cv)
+    tr = res.trace()
+    for i, h in enumerate(heads):
+        _assert_ok(replay_check(h.Q, h.K, h.V, budgets[i], 4, 2, res, i, trace=tr), f"head{i}")
+
 def test_compact_d64_bf16_batched():
     heads = [synth.make_head([40, i], 256, 512, 64, True, "bf16") for i in range(2)]
     res = _run(heads, [32, 31], "bf16", 4, 2)
