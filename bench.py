@@ -354,7 +354,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=2)
     ap.add_argument("--workload", type=int, default=2, choices=[1, 2, 3, 4],
                     help="1: one 8-head layer, plain OMP; 2: 288-head stack, batched selection; "
-                         "3: 60k-token stack (key-selection seconds, Phi recomputed); "
+                         "3: 60k-token stack (wall-clock seconds of the compaction calls, Phi recomputed); "
                          "4: 288 heads with Dirichlet budgets 8..2048")
     ap.add_argument("--peaks", action="store_true",
                     help="only run the peak probe (MFMA, vector f64 and HBM read rates of this GPU)")
