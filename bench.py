@@ -296,7 +296,7 @@ def bench_long(args):
         # the whole stack's Phi (566 GB) is over the 64 GB budget, so each batch
         # runs as the whole call would: every sweep recomputes Phi
         kw = dict(cu_q=cu_q, cu_k=cu_k, select="batched", topk=w.topk, refit_every=w.refit_every,
-                  phi_budget_bytes=0)
+                  phi_budget_bytes=0, head_groups=args.head_groups)
         if timer:
             timer.reset()
         torch.cuda.synchronize()
