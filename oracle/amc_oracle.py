@@ -172,11 +172,139 @@ def fnnls(G, b, w0=None, tol=None, max_outer=None):
         cand = np.where(~passive, g, -np.inf)
         j = int(np.argmax(cand))
         if cand[j] <= tol:
-            break
+            return u / dg
         passive = passive.copy()
         passive[j] = True
         u, passive = solve_passive(u, passive)
-    return u / dg
+    raise RuntimeError(f"fnnls: no KKT point within {max_outer} outer iterations")
+
+
+def _householder_r(M):
+    """Upper-triangular factor R of M = QR by Householder reflections, for
+    dtypes numpy's LAPACK binding does not take (extended precision)."""
+    A = np.array(M, copy=True)
+    rows, cols = A.shape
+    for j in range(min(rows, cols)):
+        x = A[j:, j]
+        nrm = np.sqrt(np.sum(x * x))
+        if nrm == 0:
+            continue
+        alpha = -nrm if x[0] >= 0 else nrm
+        v = x.copy()
+        v[0] -= alpha
+        vtv = np.sum(v * v)
+        A[j:, j:] -= np.outer(v, (v @ A[j:, j:]) * (2 / vtv))
+        A[j + 1:, j] = 0
+    return A[:min(rows, cols)]
+
+
+def _qr_r(M):
+    M = np.asarray(M)
+    if M.dtype == np.float64:
+        return np.linalg.qr(M, mode="r")
+    return _householder_r(M)
+
+
+# Lawson-Hanson on the reduced system: a zero column enters when its part
+# orthogonal to the free columns makes a cosine above COS_TOL with the
+# residual; a column whose orthogonal part is below DEP_TOL (unit columns)
+# counts as dependent on the free set.
+COS_TOL = 1e-10
+DEP_TOL = 1e-12
+
+
+def nnls_qr(PhiS, m, w0=None, max_outer=None, dtype=np.float64):
+    """min_{w >= 0} ||Phi_S w - m||_2 by Lawson and Hanson's active-set method,
+    with every least-squares step taken through an orthogonal factorisation
+    of Phi_S itself, never its Gram matrix (whose conditioning is the square
+    of Phi_S's, the whole difference when the selected keys are nearly
+    collinear and the mass is almost fitted).
+
+    1. Columns are scaled to unit norm (w = u / ||phi_j||, a bijection of the
+       non-negative orthant, so the minimiser is the same) and [Phi_S D^-1 m]
+       is reduced to its triangular factor [[A y] [0 rho]]: for every u,
+       ||Phi_S D^-1 u - m||^2 = ||A u - y||^2 + rho^2, so the problem is
+       min_{u >= 0} ||A u - y|| with A square upper triangular.
+    2. Each active-set iteration factors the columns of A ordered [free | zero]
+       next to y.  The leading block gives the least-squares solution on the
+       free set; the trailing block holds the residual and every zero
+       column's component orthogonal to the free columns.  A free variable
+       that would turn non-positive makes the usual Lawson-Hanson step back
+       to feasibility and leaves; otherwise the zero column whose orthogonal
+       component is best aligned with the residual enters (the entering test
+       of Lawson and Hanson, measured in the complement, where rounding is
+       relative to the residual rather than to m).
+
+    ``w0``: optional feasible warm start; its support is the starting free
+    set.  The minimiser is unique when Phi_S has full column rank, so the
+    warm start does not change it.  ``dtype``: arithmetic of the solve
+    (numpy.longdouble for an extended-precision cross-check).
+    """
+    A0 = np.asarray(PhiS, dtype=dtype)
+    y0 = np.asarray(m, dtype=dtype)
+    n, t = A0.shape
+    dg = np.sqrt(np.sum(A0 * A0, axis=0))
+    live = dg > 0
+    dg = np.where(live, dg, 1)
+    R = _qr_r(np.column_stack([A0 / dg, y0]))
+    A = np.zeros((t, t), dtype=dtype)
+    y = np.zeros(t, dtype=dtype)
+    k = min(R.shape[0], t)
+    A[:k] = R[:k, :t]
+    y[:k] = R[:k, t]
+    if max_outer is None:
+        max_outer = 3 * t + 30
+    u = np.zeros(t, dtype=dtype)
+    if w0 is not None:
+        u[: len(w0)] = np.maximum(np.asarray(w0, dtype=dtype), 0) * dg[: len(w0)]
+    u[~live] = 0
+    free = [a for a in range(t) if u[a] > 0]
+    blocked = set(np.flatnonzero(~live).tolist())
+    for _ in range(max_outer):
+        zero = [a for a in range(t) if u[a] == 0 and a not in blocked and a not in free]
+        f = len(free)
+        T = _qr_r(np.column_stack([A[:, free + zero], y]))
+        Tf = np.zeros((t, t + 1), dtype=dtype)
+        Tf[: T.shape[0]] = T
+        c = Tf[:, f + len(zero)]
+        dep = [i for i in range(f) if abs(Tf[i, i]) <= DEP_TOL]
+        if dep:  # dependent on the free columns before it: out for good
+            a = free[dep[0]]
+            blocked.add(a)
+            u[a] = 0
+            free.remove(a)
+            continue
+        z = np.zeros(f, dtype=dtype)
+        for i in range(f - 1, -1, -1):
+            z[i] = (c[i] - Tf[i, i + 1:f] @ z[i + 1:]) / Tf[i, i]
+        if np.any(z <= 0):
+            # step from the feasible u toward z until the first free variable hits zero
+            neg = np.flatnonzero(z <= 0)
+            uf = u[free]
+            ratios = uf[neg] / (uf[neg] - z[neg])
+            i_min = int(neg[int(np.argmin(ratios))])
+            uf = uf + ratios.min() * (z - uf)
+            uf[i_min] = 0
+            u[free] = np.maximum(uf, 0)
+            free = [a for a in free if u[a] > 0]
+            continue
+        u[:] = 0
+        u[free] = z
+        rz = c[f:]
+        nr = np.sqrt(np.sum(rz * rz))
+        best, enter = COS_TOL, -1
+        for q, a in enumerate(zero):
+            col = Tf[f:f + q + 1, f + q]
+            den = np.sqrt(np.sum(col * col))
+            if den <= DEP_TOL or nr == 0:
+                continue
+            cos = (col @ rz[: q + 1]) / (den * nr)
+            if cos > best:
+                best, enter = cos, a
+        if enter < 0:
+            return (u / dg).astype(np.float64)
+        free.append(enter)
+    raise RuntimeError(f"nnls_qr: no KKT point within {max_outer} iterations")
 
 
 def nnls_exact(PhiS, m, w_prev=None):
@@ -186,18 +314,18 @@ def nnls_exact(PhiS, m, w_prev=None):
 
     The pages' GPU solver is projected gradient (p2 Fig. 2); what it converges
     to is this minimiser, which the oracle computes directly: Lawson-Hanson
-    for up to 256 columns, FNNLS on the Gram form above that.
+    (scipy) for up to 256 columns, above that Lawson-Hanson on the
+    triangular factor of [Phi_S m] (nnls_qr), warm-started from the previous
+    refit's weights.  Both work on Phi_S through orthogonal factorisations.
     """
     t = PhiS.shape[1]
     if t <= 256:
         return nnls_lawson_hanson(PhiS, m)
-    G = PhiS.T @ PhiS
-    b = PhiS.T @ m
     w0 = None
     if w_prev is not None:
         w0 = np.zeros(t)
         w0[: len(w_prev)] = w_prev
-    return fnnls(G, b, w0)
+    return nnls_qr(PhiS, m, w0)
 
 
 def nnls_kkt_violation(G, b, w):

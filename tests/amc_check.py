@@ -12,13 +12,14 @@ relative mass and attention-output errors of the GPU's compacted block are
 within 1e-3 (absolute) of the oracle's own.
 
 The beta rule presumes the NNLS weights are determined to that accuracy in
-float64.  For each head the check first measures the oracle's own envelope:
-the final NNLS solved by two exact methods (Lawson-Hanson on Phi_S and FNNLS
-on its Gram matrix).  Where those disagree by more than the beta tolerance,
-the weights are not identifiable at float64 (nearly collinear columns: the
-fitted mass agrees to ~1e-7 while single weights move by large factors); the
-report says so with the envelope, and the GPU's weights are held to the
-minimum instead: their NNLS residual within 1e-6 (relative) of Lawson-Hanson's.
+float64.  Where the GPU's beta misses it, the check asks the oracle whether
+they are: it solves the same NNLS again in extended precision (long double,
+warm-started from its float64 minimiser) and measures how far beta moves (the
+envelope).  Only where the envelope itself exceeds the beta tolerance (nearly
+collinear columns whose single weights float64 cannot pin down while the
+fitted mass agrees) are the GPU's weights held to the minimum value instead:
+their NNLS residual within 1e-6 (relative) of the oracle's.  Such heads are
+counted; a test fails when more than FALLBACK_SHARE of its heads need it.
 """
 from __future__ import annotations
 
@@ -34,6 +35,8 @@ BETA_TOL = 1e-3
 ERR_TOL = 1e-3
 WEIGHT_REL = 1e-6
 RESID_REL = 1e-6
+FALLBACK_SHARE = 0.25  # largest share of a test's heads held to the minimum value only
+LD_MAX_T = 512  # largest budget the extended-precision envelope is computed for
 
 
 def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -87,30 +90,32 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
     both = act_g & act_r
     rep["beta_maxdiff"] = float(np.max(np.abs(beta[both] - ref.beta[both]))) if np.any(both) else 0.0
     rep["one_sided_ok"] = _one_sided_ok(w_gpu, w_ref)
-    # the oracle's own envelope for these weights
     P = ref.features.Phi[:, np.asarray(ref.sel_idx)]
     m = ref.features.m
-    w_alt = O.fnnls(P.T @ P, P.T @ m) if len(w_ref) <= 256 else O.nnls_lawson_hanson(P, m)
-    lw_r, lw_a = np.log(np.where(w_ref > 0, w_ref, 1.0)), np.log(np.where(w_alt > 0, w_alt, 1.0))
-    both_o = (w_ref > 0) & (w_alt > 0)
-    env = float(np.max(np.abs(lw_r - lw_a)[both_o])) if np.any(both_o) else 0.0
-    rep["beta_envelope"] = env
-    rep["beta_identifiable"] = env <= BETA_TOL and _one_sided_ok(w_alt, w_ref)
     # the GPU's float64 weights (trace, selection order) in ascending key order
     order = np.argsort(np.asarray(trace["pick"][h]), kind="stable")
     w_gpu64 = np.asarray(trace["weight"][h], dtype=np.float64)[order]
     res_g = float(np.linalg.norm(m - P @ w_gpu64))
     res_r = float(np.linalg.norm(m - P @ w_ref))
     rep["resid_excess"] = (res_g - res_r) / max(res_r, 1e-300)
+    rep["rel_resid"] = res_r / float(np.linalg.norm(m))
     e_gpu = oracle.errors(Q, K, V, Ck, beta, Cv, beta_in)
     e_ref = oracle.errors(Q, K, V, ref.Ck, ref.beta, ref.Cv, beta_in)
     rep["e_gpu"], rep["e_ref"] = e_gpu, e_ref
     rep["e_mass_diff"] = abs(e_gpu[0] - e_ref[0])
     rep["e_out_diff"] = abs(e_gpu[1] - e_ref[1])
-    if rep["beta_identifiable"]:
-        weights_ok = rep["beta_maxdiff"] <= BETA_TOL and rep["one_sided_ok"]
-    else:
-        weights_ok = rep["resid_excess"] <= RESID_REL
+    rep["fallback"] = False
+    rep["beta_envelope"] = None
+    weights_ok = rep["beta_maxdiff"] <= BETA_TOL and rep["one_sided_ok"]
+    if not weights_ok and len(w_ref) <= LD_MAX_T:
+        # is beta determined at float64?  the same NNLS in extended precision
+        w_ld = O.nnls_qr(P, m, w0=w_ref, dtype=np.longdouble)
+        both_o = (w_ref > 0) & (w_ld > 0)
+        env = float(np.max(np.abs(np.log(w_ref[both_o]) - np.log(w_ld[both_o])))) if np.any(both_o) else 0.0
+        rep["beta_envelope"] = env
+        if env > BETA_TOL or not _one_sided_ok(w_ld, w_ref):
+            rep["fallback"] = True
+            weights_ok = rep["resid_excess"] <= RESID_REL
     rep["ok"] = (not rep["mismatch_iters"] and rep["same_set"] and rep["ck_exact"] and weights_ok and
                  rep["e_mass_diff"] <= ERR_TOL and rep["e_out_diff"] <= ERR_TOL)
     return rep
@@ -122,3 +127,10 @@ def _one_sided_ok(wa, wb):
     only_b = (wb > 0) & ~(wa > 0)
     return bool(np.all(wa[only_a] <= WEIGHT_REL * wa.max(initial=0.0)) and
                 np.all(wb[only_b] <= WEIGHT_REL * wb.max(initial=0.0)))
+
+
+def assert_fallback_share(reports, share=FALLBACK_SHARE):
+    """At most ``share`` of a test's heads may be held to the NNLS minimum
+    value instead of the beta rule."""
+    n_fb = sum(1 for r in reports if r.get("fallback"))
+    assert n_fb <= share * len(reports), f"{n_fb} of {len(reports)} heads needed the residual gate"

@@ -159,6 +159,123 @@ def test_fnnls_warm_start_same_minimiser():
     assert np.linalg.norm(A @ (cold - warm)) <= 1e-9 * np.linalg.norm(y)
 
 
+def _collinear_selection(t=40):
+    """A nearly collinear selection with an almost exact mass fit: 40 keys of
+    plain OMP on a 300-query, 700-key head (d = 64), where cond(Phi_S) reaches
+    1e8 and the relative residual 6e-10.  Gram-form solvers lose this regime
+    (the Gram matrix's conditioning is the square of Phi_S's)."""
+    h = synth.make_head([34, 0], 300, 700, 64, True, "bf16")
+    b = synth.random_beta([35, 0], 700, 1.0)
+    f = oracle.mass_features(h.Q, h.K, h.V, b)
+    sel = O.omp_select(f.Phi, f.m, t)
+    return f.Phi[:, sel.S], f.m
+
+
+def _objective(A, y, w):
+    """||A w - y|| in extended precision (the objective, free of the rounding
+    of the fp64 evaluation)."""
+    r = np.asarray(y, dtype=np.longdouble) - np.asarray(A, dtype=np.longdouble) @ np.asarray(w, dtype=np.longdouble)
+    return float(np.sqrt(np.sum(r * r)))
+
+
+@pytest.mark.parametrize("t", [5, 40, 120])
+def test_nnls_qr_matches_lawson_hanson(t):
+    """The QR-reduced active-set solver and scipy's Lawson-Hanson on Phi_S
+    reach the same minimiser on well-conditioned systems."""
+    rng = np.random.default_rng(300 + t)
+    for _ in range(3):
+        A = _phi_like(rng, 2 * t + 50, t)
+        y = A @ (np.abs(rng.normal(size=t)) * (rng.random(t) > 0.3)) + 0.05 * rng.normal(size=2 * t + 50) * A.mean()
+        w_lh = oracle.nnls_lawson_hanson(A, y)
+        w_qr = oracle.nnls_qr(A, y)
+        assert abs(_objective(A, y, w_qr) / _objective(A, y, w_lh) - 1) < 1e-12
+        big = w_lh > 1e-6 * w_lh.max()
+        assert np.allclose(w_qr[big], w_lh[big], rtol=1e-6)
+        assert np.all(w_qr[~big] <= 1e-6 * w_lh.max())
+
+
+def test_nnls_qr_large_selection_matches_lawson_hanson():
+    """Above 256 keys the oracle's refit is nnls_qr: at t = 300 on a real
+    selection (512 queries) it agrees with Lawson-Hanson on Phi_S, which the
+    Gram-form FNNLS does not do there."""
+    h = synth.make_head([36, 0], 512, 1024, 128, True, "bf16")
+    f = oracle.mass_features(h.Q, h.K, h.V)
+    sel = O.omp_select(f.Phi, f.m, 300, 4, 2)
+    P = f.Phi[:, sel.S]
+    w_lh = oracle.nnls_lawson_hanson(P, f.m)
+    w_qr = oracle.nnls_exact(P, f.m)
+    ob_lh, ob_qr = _objective(P, f.m, w_lh), _objective(P, f.m, w_qr)
+    assert abs(ob_qr / ob_lh - 1) < 1e-10
+    both = (w_lh > 0) & (w_qr > 0)
+    assert np.max(np.abs(np.log(w_lh[both]) - np.log(w_qr[both]))) < 1e-6
+    assert np.array_equal(w_lh > 0, w_qr > 0)
+
+
+def test_nnls_qr_extended_precision_on_collinear_selection():
+    """On the nearly collinear selection the float64 solve reaches the minimum
+    that the same method finds in extended precision (objective to 1e-10,
+    beta to 1e-6), and so does Lawson-Hanson; a gradient-threshold test on the
+    Gram form stops well above it."""
+    P, m = _collinear_selection()
+    w64 = oracle.nnls_qr(P, m)
+    wld = oracle.nnls_qr(P, m, dtype=np.longdouble)
+    w_lh = oracle.nnls_lawson_hanson(P, m)
+    ob = _objective(P, m, wld)
+    assert abs(_objective(P, m, w64) / ob - 1) < 1e-10
+    assert abs(_objective(P, m, w_lh) / ob - 1) < 1e-10
+    both = (w64 > 0) & (wld > 0)
+    assert np.array_equal(w64 > 0, wld > 0)
+    assert np.max(np.abs(np.log(w64[both]) - np.log(wld[both]))) < 1e-6
+    # the Gram form: its KKT point is not the minimiser here
+    w_g = oracle.fnnls(P.T @ P, P.T @ m)
+    assert _objective(P, m, w_g) / ob - 1 > 1e-3
+
+
+def test_nnls_qr_warm_start_same_minimiser():
+    P, m = _collinear_selection(32)
+    cold = oracle.nnls_qr(P, m)
+    rng = np.random.default_rng(9)
+    warm = oracle.nnls_qr(P, m, w0=np.abs(rng.normal(size=P.shape[1])) * (rng.random(P.shape[1]) > 0.5))
+    assert abs(_objective(P, m, warm) / _objective(P, m, cold) - 1) < 1e-10
+    assert np.array_equal(cold > 0, warm > 0)
+
+
+def test_nnls_iteration_caps_raise():
+    """An exhausted iteration cap is an error, not a silent return."""
+    rng = np.random.default_rng(12)
+    A = _phi_like(rng, 80, 30)
+    y = A @ np.abs(rng.normal(size=30))
+    with pytest.raises(RuntimeError):
+        oracle.fnnls(A.T @ A, A.T @ y, max_outer=2)
+    with pytest.raises(RuntimeError):
+        oracle.nnls_qr(A, y, max_outer=2)
+
+
+def test_planted_coarse_dependence_test_misses_minimiser(monkeypatch):
+    """Planted mistake: a dependence threshold of 1e-6 on the complement norm
+    (unit columns) rejects keys the minimiser needs on the collinear
+    selection (their complement norms lie near 1e-7); the objective rises far
+    above the extended-precision minimum the pin above compares against."""
+    P, m = _collinear_selection()
+    good = _objective(P, m, oracle.nnls_qr(P, m))
+    monkeypatch.setattr(O, "DEP_TOL", 1e-6)
+    bad = _objective(P, m, oracle.nnls_qr(P, m))
+    assert bad / good - 1 > 1e-3
+
+
+def test_errors_hand_computed():
+    """errors() on a case worked by hand: d = 1 (scale 1), keys 0 and log 3
+    with values 1 and 2; queries 1 and 0.  Original masses (4, 2), outputs
+    (7/4, 3/2).  Compacted to key 0 with beta = log 2 and value 1: masses
+    (2, 2), outputs (1, 1)."""
+    Q = np.array([[1.0], [0.0]])
+    K = np.array([[0.0], [math.log(3.0)]])
+    V = np.array([[1.0], [2.0]])
+    e_mass, e_out = oracle.errors(Q, K, V, np.array([[0.0]]), np.array([math.log(2.0)]), np.array([[1.0]]))
+    assert abs(e_mass - math.sqrt(4.0) / math.sqrt(20.0)) < 1e-14
+    assert abs(e_out - math.sqrt(0.75 ** 2 + 0.5 ** 2) / math.sqrt(1.75 ** 2 + 1.5 ** 2)) < 1e-14
+
+
 # ----------------------------------------------------------------------------
 # closed form: budget t = T
 # ----------------------------------------------------------------------------
