@@ -22,7 +22,8 @@ AMC_OK, AMC_ERR_INVALID_ARG, AMC_ERR_UNSUPPORTED, AMC_ERR_WORKSPACE, AMC_ERR_HIP
 AMC_F32, AMC_BF16 = 0, 1
 AMC_SEL_OMP, AMC_SEL_OMP_BATCHED = 0, 1
 AMC_FLAG_TRACE = 1
-HS_CHOL_JITTER, HS_NNLS_CAP, HS_NONFINITE, HS_NNLS_SINGULAR = 1, 2, 4, 8
+HS_CHOL_JITTER, HS_NNLS_CAP, HS_NONFINITE, HS_NNLS_SINGULAR, HS_NNLS_QR = 1, 2, 4, 8, 16
+EXACT_REFIT = {"auto": 0, "always": 1, "never": 2}
 
 KERNEL_CLASSES = ["init", "shift", "phi", "sweep", "merge", "panel", "gram", "nnls", "resid",
                   "ols_normal", "ols_solve", "pack", "sweep_exact", "rescore", "prune", "digits", "phi_f64"]
@@ -64,6 +65,8 @@ class Options(ctypes.Structure):
         ("phi_budget_bytes", ctypes.c_uint64),
         ("cv_dtype", ctypes.c_int32),
         ("head_groups", ctypes.c_int32),
+        ("exact_refit", ctypes.c_int32),
+        ("digits_in_panel", ctypes.c_int32),
         ("flags", ctypes.c_uint32),
         ("timer", ctypes.c_void_p),
     ]
@@ -183,7 +186,7 @@ def make_problem(num_heads: int, head_dim: int, cu_q: Sequence[int], cu_k: Seque
 def make_options(select: str = "omp", topk: int = 1, refit_every: int = 1, nnls_polish: int = 1,
                  nnls_max_iters: int = 0, nnls_tol: float = 0.0, phi_budget_bytes: Optional[int] = None,
                  cv_dtype: torch.dtype = torch.float32, trace: bool = False, timer: "Timer" = None,
-                 head_groups: int = 0) -> Options:
+                 head_groups: int = 0, exact_refit: str = "auto", digits_in_panel: bool = True) -> Options:
     o = Options()
     lib().amc_default_options(ctypes.byref(o))
     o.select = {"omp": AMC_SEL_OMP, "batched": AMC_SEL_OMP_BATCHED}[select]
@@ -197,6 +200,8 @@ def make_options(select: str = "omp", topk: int = 1, refit_every: int = 1, nnls_
     o.cv_dtype = AMC_BF16 if cv_dtype == torch.bfloat16 else AMC_F32
     o.flags = AMC_FLAG_TRACE if trace else 0
     o.head_groups = int(head_groups)
+    o.exact_refit = EXACT_REFIT[exact_refit]
+    o.digits_in_panel = 1 if digits_in_panel else 0
     o.timer = timer.handle if timer is not None else None
     return o
 
@@ -329,7 +334,8 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
             nnls_polish: int = 1, nnls_max_iters: int = 0, nnls_tol: float = 0.0,
             phi_budget_bytes: Optional[int] = None, cv_dtype: torch.dtype = torch.float32, trace: bool = False,
             timer: Optional[Timer] = None, scale: float = 0.0, stream=None,
-            workspace: Optional[torch.Tensor] = None, head_groups: int = 0) -> CompactResult:
+            workspace: Optional[torch.Tensor] = None, head_groups: int = 0, exact_refit: str = "auto",
+            digits_in_panel: bool = True) -> CompactResult:
     """amc_compact on torch tensors.  Q: (H, n, d) or packed (sum n, d) with
     cu_q; K, V: (H, T, d) or packed with cu_k; budgets: int or per-head list."""
     if not (Q.is_cuda and K.is_cuda and V.is_cuda):
@@ -349,7 +355,7 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
         raise ValueError("one budget per head")
     prob, keep = make_problem(H, d, cq, ck, bud, _dtype_code(Qp), scale)
     opts = make_options(select, topk, refit_every, nnls_polish, nnls_max_iters, nnls_tol, phi_budget_bytes,
-                        cv_dtype, trace, timer, head_groups)
+                        cv_dtype, trace, timer, head_groups, exact_refit, digits_in_panel)
     ws_bytes = workspace_size(prob, opts)
     cb = output_offsets(prob)
     dev = Qp.device

@@ -22,7 +22,7 @@ LIB = os.path.join(PKG, "libamc.so")
 PEAKS_SRC = os.path.join(PKG, "peaks", "peaks.hip")
 PEAKS = os.path.join(PKG, "amc_peaks")
 
-SOURCES = ["amc_api.cpp", "k_phi.hip", "k_select.hip", "k_nnls.hip", "k_nnls_g.hip", "k_ols.hip"]
+SOURCES = ["amc_api.cpp", "k_phi.hip", "k_select.hip", "k_nnls.hip", "k_nnls_g.hip", "k_nnls_qr.hip", "k_ols.hip"]
 
 ARCH = os.environ.get("AMC_OFFLOAD_ARCH", "gfx950")
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")

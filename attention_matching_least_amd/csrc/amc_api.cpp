@@ -53,12 +53,6 @@ void timer_end(Timer *t, int c, hipStream_t s) {
 // ---------------------------------------------------------------------------
 static inline uint64_t align256(uint64_t x) { return (x + 255) & ~uint64_t(255); }
 
-// AMC_DIGITS_IN_PANEL=0 keeps the digit rows and value tiles apart from the
-// panel in recompute mode (for comparison runs).
-static bool digits_in_panel_enabled() {
-  const char *v = std::getenv("AMC_DIGITS_IN_PANEL");
-  return !(v && v[0] == '0');
-}
 static inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
 struct Plan {
@@ -75,7 +69,8 @@ struct Plan {
            o_cand_lidx = 0, o_cand_cnt = 0, o_band_list = 0, o_band_cnt = 0, o_exact = 0, o_stage = 0,
            o_part = 0, o_vt = 0, o_qdig = 0, o_kdig = 0, o_qexp = 0, o_ktab = 0, o_f64h = 0, o_colsum = 0, o_rpn = 0, o_rabs = 0,
            o_surv = 0, o_survcnt = 0, o_pruneL = 0, o_q8 = 0, o_q8bad = 0, o_surv2 = 0, o_surv2cnt = 0,
-           total = 0;
+           o_qrflag = 0, o_qrbuf = 0, o_rpart = 0, total = 0;
+  bool exact_path = false;  // some head may take the orthogonal-factorisation refit
   bool store_q8 = false;  // the 8-bit plane of the second pruning stage fits the budget too
   bool alias_digits = false;  // digit rows and value tiles lie in the panel (recompute mode)
 };
@@ -113,6 +108,9 @@ static amc_status check_options(const amc_options *o) {
   if (int64_t(o->topk) * o->refit_every > kMaxCycle) return AMC_ERR_UNSUPPORTED;
   if (o->nnls_max_iters < 0 || o->nnls_polish < 0 || o->nnls_polish > 8) return AMC_ERR_INVALID_ARG;
   if (o->head_groups < 0 || o->head_groups > 16) return AMC_ERR_INVALID_ARG;
+  if (o->head_groups > 8) return AMC_ERR_UNSUPPORTED;
+  if (o->exact_refit < 0 || o->exact_refit > 2) return AMC_ERR_INVALID_ARG;
+  if (o->digits_in_panel != 0 && o->digits_in_panel != 1) return AMC_ERR_INVALID_ARG;
   if (!(o->nnls_tol >= 0.0) || !std::isfinite(o->nnls_tol)) return AMC_ERR_INVALID_ARG;
   if (o->cv_dtype != AMC_F32 && o->cv_dtype != AMC_BF16) return AMC_ERR_INVALID_ARG;
   if (o->flags & ~uint32_t(AMC_FLAG_TRACE)) return AMC_ERR_INVALID_ARG;
@@ -136,7 +134,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   dm.in_bf16 = p->in_dtype == AMC_BF16;
   dm.scale = p->scale > 0.0f ? double(p->scale) : 1.0 / std::sqrt(double(d));
   pl.desc.assign(H, HeadDesc{});
-  int64_t phi = 0, nn = 0, tt = 0, t2 = 0, panel = 0, cblk = 0, sblk = 0, cyc = 0, TT = 0, vt = 0, ktr = 0;
+  int64_t phi = 0, nn = 0, tt = 0, t2 = 0, panel = 0, cblk = 0, sblk = 0, cyc = 0, TT = 0, vt = 0, ktr = 0, qrb = 0;
   for (int h = 0; h < H; ++h) {
     HeadDesc &D = pl.desc[h];
     D.n = p->cu_q[h + 1] - p->cu_q[h];
@@ -160,6 +158,14 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     D.sblk_off = sblk;
     D.n_sblk = ceil_div(D.n, kShiftRows);
     D.cyc_off = cyc;
+    D.qr_off = -1;
+    if (!features_only && o->exact_refit != 2 && D.t <= kQrMaxT) {
+      // two (t + 129) x (t + 129) float64 factors (the value fit's has t + d + 1 columns)
+      const int64_t ldq = D.t + 1 + 128;
+      D.qr_off = qrb;
+      qrb += 2 * ldq * ldq;
+      pl.exact_path = true;
+    }
     if (!features_only) {
       if (D.t > kMaxBudget) return AMC_ERR_UNSUPPORTED;
       if (D.n_cblk > kMaxSweepBlocks) return AMC_ERR_UNSUPPORTED;
@@ -187,6 +193,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   dm.total_sblk = sblk;
   dm.max_qblk = ceil_div(dm.max_n, kRescoreRows);
   dm.qb128 = ceil_div(dm.max_n, 128);
+  dm.nrb = ceil_div(dm.max_n, kResidRows);
   pl.sum_t = tt;
   pl.sum_cycles = cyc;
   pl.sum_n = nn;
@@ -239,6 +246,11 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.o_nnnp = take(4ull * H);
   pl.o_gA = take(8ull * tt);
   pl.o_nnvec = dm.max_t > kNnlsLdsT ? take(8ull * kNnlsVecPerSlot * tt) : 0;
+  pl.o_rpart = take(16ull * H * dm.nrb);
+  if (pl.exact_path) {
+    pl.o_qrflag = take(4ull * H);
+    pl.o_qrbuf = take(8ull * uint64_t(qrb));
+  }
   if (pl.store_phi) {  // bounded sweep, band and rescoring state
     pl.o_cand_lo = take(8ull * ktr);   // sweep upper bounds
     pl.o_cand_lidx = take(8ull * ktr); // sweep lower bounds
@@ -268,7 +280,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     // they take the start of the panel when they fit there.
     const uint64_t dig_bytes = align256(2ull * vt) + align256(5ull * d * nn) + align256(4ull * nn) +
                                align256((5ull * d + 16) * ktr) + align256(16ull * ktr);
-    pl.alias_digits = !features_only && !pl.store_phi && dig_bytes <= 8ull * uint64_t(panel) && digits_in_panel_enabled();
+    pl.alias_digits = !features_only && !pl.store_phi && dig_bytes <= 8ull * uint64_t(panel) && o->digits_in_panel != 0;
     const uint64_t resume = off;
     if (pl.alias_digits) off = pl.o_panel;
     pl.o_vt = take(2ull * vt);  // transposed value tiles of the mass-feature kernel
@@ -343,7 +355,7 @@ static int group_bound(int H, int ngroups, int g) {
 // The buffers of heads [h0, ...): the descriptor table and the arrays indexed
 // by head number start at h0; everything else is reached through the
 // descriptors' offsets.
-static Buffers head_range(const Buffers &b, int h0, int64_t max_qblk) {
+static Buffers head_range(const Buffers &b, int h0, int64_t max_qblk, int64_t nrb) {
   Buffers r = b;
   r.desc = b.desc + h0;
   r.shift = b.shift + h0;
@@ -365,6 +377,8 @@ static Buffers head_range(const Buffers &b, int h0, int64_t max_qblk) {
   if (b.prune_L) r.prune_L = b.prune_L + h0;
   if (b.q8_bad) r.q8_bad = b.q8_bad + h0;
   if (b.surv2_cnt) r.surv2_cnt = b.surv2_cnt + h0;
+  if (b.qr_flag) r.qr_flag = b.qr_flag + h0;
+  if (b.rpart) r.rpart = b.rpart + int64_t(h0) * 2 * nrb;
   return r;
 }
 
@@ -405,6 +419,8 @@ void amc_default_options(amc_options *o) {
   o->phi_budget_bytes = 64ull << 30;
   o->cv_dtype = AMC_F32;
   o->head_groups = 0;
+  o->exact_refit = 0;
+  o->digits_in_panel = 1;
   o->flags = 0;
   o->timer = nullptr;
 }
@@ -558,6 +574,11 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
     }
   }
   b.head_status = head_status;
+  b.rpart = reinterpret_cast<double *>(ws + pl.o_rpart);
+  if (pl.exact_path) {
+    b.qr_flag = reinterpret_cast<int32_t *>(ws + pl.o_qrflag);
+    b.qrbuf = reinterpret_cast<double *>(ws + pl.o_qrbuf);
+  }
   if (tracing) {
     char *tr = static_cast<char *>(trace);
     b.tr_shift = reinterpret_cast<double *>(tr + tl.shift);
@@ -581,6 +602,8 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   if (b.tr_swept && !pl.store_phi) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.tr_swept, pl.sum_cycles, 0, stream));
   if (b.tr_swept8) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.tr_swept8, pl.sum_cycles, 0, stream));
   if (b.q8_bad) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.q8_bad, dm.H, 0, stream));
+  // exact refit: 2 sends every eligible head there from its first refit
+  if (b.qr_flag) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.qr_flag, dm.H, o->exact_refit == 1 ? 2 : 0, stream));
 
   // The heads run in groups, each on a stream of its own (the caller's for the
   // first), joined back to the caller's stream by events: the groups' mass
@@ -626,7 +649,7 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   for (int g = 0; g < ngroups && result == AMC_OK; ++g) {
     const bool do_phi = pass == 0, do_sel = pass == npass - 1;
     const int h0 = group_bound(dm.H, ngroups, g), h1 = group_bound(dm.H, ngroups, g + 1);
-    const Buffers bg = head_range(b, h0, dm.max_qblk);
+    const Buffers bg = head_range(b, h0, dm.max_qblk, dm.nrb);
     Dims dg = dm;
     dg.H = h1 - h0;
     int64_t cycles = 0;
@@ -679,16 +702,19 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
         }
         AMC_LAUNCH(AMC_K_GRAM, launch_gram(dg, bg, c, pl.kR, 0, stream));
         AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dg, bg, c, pl.kR, 0, np, stream));
+        if (bg.qr_flag) AMC_LAUNCH(AMC_K_NNLS, launch_nnls_qr(dg, bg, c, pl.kR, 0, stream));
         AMC_LAUNCH(AMC_K_RESID, launch_resid(dg, bg, c, pl.kR, 0, stream));
       }
       for (int r = 0; r < o->nnls_polish; ++r) {
         AMC_LAUNCH(AMC_K_GRAM, launch_gram(dg, bg, 0, pl.kR, 1, stream));
         AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dg, bg, 0, pl.kR, 1, np, stream));
+        if (bg.qr_flag) AMC_LAUNCH(AMC_K_NNLS, launch_nnls_qr(dg, bg, 0, pl.kR, 1, stream));
         AMC_LAUNCH(AMC_K_RESID, launch_resid(dg, bg, 0, pl.kR, 1, stream));
       }
       AMC_LAUNCH(AMC_K_OLS_NORMAL, launch_ols_normal(dg, bg, stream));
       AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_factor(dg, bg, stream));
       AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_trsm(dg, bg, stream));
+      if (bg.qr_flag) AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_qr(dg, bg, stream));
       AMC_LAUNCH(AMC_K_PACK, launch_pack(dg, bg, Ck, beta, Cv, o->cv_dtype == AMC_BF16, sel_idx, stream));
       if (ngroups > 1 && g > 0 && hipEventRecord(ev_done[size_t(g)], stream) != hipSuccess) return AMC_ERR_HIP;
       return AMC_OK;

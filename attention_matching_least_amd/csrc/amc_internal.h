@@ -23,6 +23,10 @@ constexpr int kMaxSweepBlocks = 1024;  // sweep column blocks per head the merge
 constexpr int kBandCap = 128;    // candidates per head the float64 rescoring takes (more: exact sweep)
 constexpr int kRescoreRows = 256; // queries per block of the rescoring kernel
 constexpr int kStoredMaxN = 8192; // longest head (queries) the stored-Phi path takes
+constexpr int kQrMaxT = 640;     // largest budget the orthogonal-factorisation refit takes
+constexpr double kQrCond = 1e5;  // estimated cond(Phi_S D^-1) above which a head's refits leave the Gram form
+constexpr double kQrRelResid = 1e-6;  // relative mass residual below which they do
+constexpr int kResidRows = 256;  // queries per block of the residual kernel (one partial sum each)
 
 // Per-head descriptor, computed on the host and copied to the device once per call.
 // All offsets are in elements of the array they index.
@@ -45,8 +49,10 @@ struct HeadDesc {
   int64_t vt_off;         // first element of the head's transposed value tiles (bf16 inputs)
   int64_t kt_off;         // first row of the head in the arrays of keys padded to whole 64-key tiles
   int64_t ldN;            // stored planes: column stride (n rounded up to 64)
+  int64_t qr_off;         // first element of the head's two factors of the exact refit (-1: none;
+                          // each (t + 129) x (t + 129) float64, row stride t + 129)
 };
-static_assert(sizeof(HeadDesc) == 19 * 8, "HeadDesc layout");
+static_assert(sizeof(HeadDesc) == 20 * 8, "HeadDesc layout");
 
 // Device pointers of the workspace carve-up and of the caller's buffers.
 struct Buffers {
@@ -112,6 +118,10 @@ struct Buffers {
   double *stage;       // [sum n][kBandCap] float64 Phi columns of the band, per head [kBandCap][n]
   double *part;        // [H][kBandCap][max_qblk] partial scores of the band per query block
   int32_t *head_status;  // [H] or null
+  int32_t *qr_flag;    // [H] exact refit: 0 Gram form, 1 flagged at this refit, 2 every later refit
+                       // (null: the path is off)
+  double *qrbuf;       // per head at qr_off: two factors of the exact refit
+  double *rpart;       // [H][nrb][2] per 256-query block: sum r^2 and sum m^2 of the last residual
   // trace (all null when tracing is off)
   double *tr_shift, *tr_pick_score, *tr_weight, *tr_runner;
   int32_t *tr_pick, *tr_iters, *tr_swept, *tr_swept8;
@@ -126,6 +136,7 @@ struct Dims {
   int band_cap;        // largest band the rescoring takes (<= kBandCap)
   int64_t qb128;       // 128-query blocks of the longest head (column sums per key)
   int64_t total_sblk;
+  int64_t nrb;         // residual blocks per head (max n / kResidRows, rounded up)
 };
 
 struct NnlsParams {
@@ -182,5 +193,8 @@ hipError_t launch_nnls_batched(int num, const int64_t *h_cu_t, const int64_t *h_
 hipError_t launch_copy_words(uint64_t *dst, const uint64_t *src, int64_t count, hipStream_t s);
 hipError_t launch_ols_factor(const Dims &dm, const Buffers &b, hipStream_t s);
 hipError_t launch_ols_trsm(const Dims &dm, const Buffers &b, hipStream_t s);
+// exact refit and value fit of the heads flagged in b.qr_flag (no-ops when it is null)
+hipError_t launch_nnls_qr(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);
+hipError_t launch_ols_qr(const Dims &dm, const Buffers &b, hipStream_t s);
 
 }  // namespace amc

@@ -65,7 +65,7 @@ hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int kR, int 
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_nnls_cycle<false>, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.bvec, b.gA,
                        b.w, cycle, kR, polish, np, maxp, b.nn_L, b.nn_P, b.nn_np, b.nn_vec, b.tr_iters, b.tr_weight,
-                       b.head_status);
+                       b.head_status, b.qr_flag, b.rpart, int(dm.nrb));
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }

@@ -141,6 +141,17 @@ __device__ __forceinline__ int block_count(int c, Red *red) {
   return s;
 }
 
+__device__ __forceinline__ double block_sum_d(double v, Red *red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) red->v[wave] = v;
+  __syncthreads();
+  double s = 0.0;
+  for (int w = 0; w < NW; ++w) s += red->v[w];
+  return s;
+}
+
 // Small per-block scratch (always LDS).
 struct Blk {
   double dots[NRHS * NRHS];  // Gram of the forward-solved candidate rows (lower triangle)
@@ -1380,6 +1391,35 @@ __device__ __forceinline__ void pg_warmup(const St &S, const double *G, int64_t 
   snapshot(S, p);
 }
 
+// Largest eigenvalue of (L L^T)^-1 = Gs_PP^-1 (the free set's scaled Gram
+// matrix), by three steps of inverse power iteration from x = 1: a lower
+// bound that the first steps already bring within a small factor.  With the
+// unit diagonal, lambda_max(Gs_PP) <= np, so np times it bounds
+// cond(Phi_P D^-1)^2 from above by roughly that factor.
+__device__ double inv_lambda_est(const St &S, int np, Red *red) {
+  const int tid = threadIdx.x;
+  __syncthreads();
+  for (int k = tid; k < np; k += NT) S.x0[k] = 1.0;
+  double nx = sqrt(double(np)), lam = 0.0;
+  for (int it = 0; it < 3; ++it) {
+    __syncthreads();
+    fwd_solve(S, np, 1);
+    __syncthreads();
+    bwd_solve(S, np, S.x0);
+    __syncthreads();
+    double s = 0.0;
+    for (int k = tid; k < np; k += NT) s = fma(S.x0[k], S.x0[k], s);
+    const double ny = sqrt(block_sum_d(s, red));
+    if (!(ny > 0.0) || !isfinite(ny)) return INFINITY;
+    lam = ny / nx;
+    const double inv = 1.0 / ny;
+    for (int k = tid; k < np; k += NT) S.x0[k] *= inv;
+    nx = 1.0;
+  }
+  __syncthreads();
+  return lam;
+}
+
 // One refit per head.  polish: no new key; refine the last fit (p = t).
 // kGlobal: the state lives in the workspace (budgets above kNnlsLdsT); else
 // in LDS.  Each variant skips the heads of the other.
@@ -1391,7 +1431,9 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
                                                    int32_t *__restrict__ nn_P, int32_t *__restrict__ nn_np,
                                                    double *__restrict__ nn_vec, int32_t *__restrict__ tr_iters,
                                                    double *__restrict__ tr_weight,
-                                                   int32_t *__restrict__ head_status) {
+                                                   int32_t *__restrict__ head_status,
+                                                   int32_t *__restrict__ qr_flag,
+                                                   const double *__restrict__ rpart, int nrb) {
   extern __shared__ __attribute__((aligned(16))) char smem[];
   __shared__ Blk bk;
   __shared__ Red red;
@@ -1399,6 +1441,9 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
   const int h = blockIdx.x;
   const HeadDesc D = desc[h];
   if ((D.t > kNnlsLdsT) != kGlobal) return;
+  // heads whose refits went to the orthogonal-factorisation path stay there
+  const bool qr_ok = qr_flag && D.qr_off >= 0;
+  if (qr_ok && qr_flag[h] >= 2) return;
   int64_t S0;
   int Kc;
   if (polish) {
@@ -1468,10 +1513,33 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
     int32_t *sg = persisted_slots(vec_g, int(D.t));
     for (int k = tid; k < int(D.t); k += NT) sg[k] = S.slot[k];
   }
+  // Does the Gram form resolve this head's minimiser?  Not when the free set
+  // is nearly collinear (estimated cond(Phi_P D^-1) above kQrCond), when the
+  // mass is fitted to a relative residual below kQrRelResid (the last
+  // residual's partial sums), or when a candidate proved singular or the cap
+  // was hit: then this refit and every later one of the head go to the
+  // orthogonal-factorisation path, which reports its own status.
+  bool gate = false;
+  if (qr_ok && tol > 0.0) {
+    gate = (sh_status & int(AMC_HS_NNLS_CAP | AMC_HS_NNLS_SINGULAR)) != 0;
+    if (!gate && S0 > 0 && rpart) {
+      double rr = 0.0, mm = 0.0;
+      for (int k = 0; k < nrb; ++k) {
+        rr += rpart[(int64_t(h) * nrb + k) * 2];
+        mm += rpart[(int64_t(h) * nrb + k) * 2 + 1];
+      }
+      gate = rr < kQrRelResid * kQrRelResid * mm;
+    }
+    if (!gate && np > 1) {
+      const double lam = inv_lambda_est(S, np, &red);
+      gate = !(lam * double(np) <= kQrCond * kQrCond);
+    }
+  }
   if (tid == 0) {
     nn_np[h] = np;
     if (tr_iters && !polish) tr_iters[D.cyc_off + cycle] = iters;
-    if (sh_status && head_status) atomicOr(head_status + h, sh_status);
+    if (gate) qr_flag[h] = 1;
+    else if (sh_status && head_status) atomicOr(head_status + h, sh_status);
   }
   if (tr_weight)
     for (int a = tid; a < p; a += NT) tr_weight[D.t_off + a] = S.u[a] / S.dg[a];

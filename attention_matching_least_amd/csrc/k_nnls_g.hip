@@ -23,7 +23,7 @@ hipError_t launch_nnls_global(const Dims &dm, const Buffers &b, int cycle, int k
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(k_nnls_cycle<true>, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.bvec, b.gA, b.w,
                      cycle, kR, polish, np, nnls_global_vec_bytes(dm.max_t) ? int(dm.max_t) : 0, b.nn_L, b.nn_P, b.nn_np, b.nn_vec, b.tr_iters,
-                     b.tr_weight, b.head_status);
+                     b.tr_weight, b.head_status, b.qr_flag, b.rpart, int(dm.nrb));
   return hipGetLastError();
 }
 

@@ -47,7 +47,8 @@ template <int D>
 __global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
                                                    const double *__restrict__ w, const double *__restrict__ mhat,
                                                    const float *__restrict__ Y, double *__restrict__ N,
-                                                   double *__restrict__ rhs, int H, int tx, int ty, int xcd_map) {
+                                                   double *__restrict__ rhs, int H, int tx, int ty, int xcd_map,
+    const int32_t *__restrict__ qr_flag) {
   constexpr int CH = 64;       // queries per stage
   constexpr int STR = CH + 1;  // padded row, in doubles
   __shared__ double xs[64 * STR];
@@ -69,6 +70,7 @@ __global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ 
   }
   if (h >= H) return;
   const HeadDesc Dh = desc[h];
+  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
   const int64_t t = Dh.t, n = Dh.n;
   const int64_t a0 = int64_t(j % tx) * 64;
   const int bt = j / tx;
@@ -152,13 +154,15 @@ __global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ 
 __global__ __launch_bounds__(NT) void k_ols_factor(const HeadDesc *__restrict__ desc, const double *__restrict__ N,
                                                    const double *__restrict__ w, int32_t *__restrict__ flist,
                                                    int32_t *__restrict__ fcount, double *__restrict__ dn,
-                                                   double *__restrict__ Lout, int32_t *__restrict__ head_status) {
+                                                   double *__restrict__ Lout, int32_t *__restrict__ head_status,
+    const int32_t *__restrict__ qr_flag) {
   extern __shared__ __attribute__((aligned(16))) double Ls[];
   __shared__ int sf[kLdsMaxT];
   __shared__ double sdn[kLdsMaxT];
   __shared__ int sh_f, sh_fail;
   const int h = blockIdx.x;
   const HeadDesc Dh = desc[h];
+  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
   if (Dh.t > kLdsMaxT) return;  // k_ols_factor_g
   const int t = int(Dh.t);
   const int tid = threadIdx.x;
@@ -240,12 +244,14 @@ __global__ __launch_bounds__(NT) void k_ols_trsm(const HeadDesc *__restrict__ de
                                                  const int32_t *__restrict__ flist,
                                                  const int32_t *__restrict__ fcount, const double *__restrict__ dn,
                                                  const double *__restrict__ Lg, const double *__restrict__ w,
-                                                 float *__restrict__ cv_sel) {
+                                                 float *__restrict__ cv_sel,
+    const int32_t *__restrict__ qr_flag) {
   constexpr int NCB = 32, NCW = 8;
   static_assert(kLdsMaxT <= 192, "three rows per lane");
   extern __shared__ __attribute__((aligned(16))) double sm[];
   const int h = blockIdx.y;
   const HeadDesc Dh = desc[h];
+  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
   if (Dh.t > kLdsMaxT) return;  // k_ols_trsm_g
   const int t = int(Dh.t);
   const int c0 = blockIdx.x * NCB;
@@ -417,10 +423,12 @@ __device__ __forceinline__ double rl(double x, int lane) {
 // F = {a : w_a > 0} ascending, its size, and the diagonal scaling of N_FF.
 __global__ __launch_bounds__(NT) void k_ols_flist_g(const HeadDesc *__restrict__ desc, const double *__restrict__ N,
                                                     const double *__restrict__ w, int32_t *__restrict__ flist,
-                                                    int32_t *__restrict__ fcount, double *__restrict__ dn) {
+                                                    int32_t *__restrict__ fcount, double *__restrict__ dn,
+    const int32_t *__restrict__ qr_flag) {
   __shared__ int wcnt[NT / 64];
   const int h = blockIdx.x;
   const HeadDesc Dh = desc[h];
+  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
   if (Dh.t <= kLdsMaxT) return;
   const int t = int(Dh.t);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -454,11 +462,13 @@ __global__ __launch_bounds__(NT) void k_ols_flist_g(const HeadDesc *__restrict__
 __global__ __launch_bounds__(NT) void k_ols_factor_g(const HeadDesc *__restrict__ desc, const double *__restrict__ N,
                                                      const int32_t *__restrict__ flist,
                                                      const int32_t *__restrict__ fcount, const double *__restrict__ dn,
-                                                     double *__restrict__ L, int32_t *__restrict__ head_status) {
+                                                     double *__restrict__ L, int32_t *__restrict__ head_status,
+    const int32_t *__restrict__ qr_flag) {
   __shared__ double Db[TBO * TBO];
   __shared__ int sh_fail;
   const int h = blockIdx.x;
   const HeadDesc Dh = desc[h];
+  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
   if (Dh.t <= kLdsMaxT) return;
   const int t = int(Dh.t);
   const int f = fcount[h];
@@ -606,12 +616,14 @@ __global__ __launch_bounds__(NT) void k_ols_trsm_g(const HeadDesc *__restrict__ 
                                                    const int32_t *__restrict__ flist,
                                                    const int32_t *__restrict__ fcount, const double *__restrict__ dn,
                                                    const double *__restrict__ L, const double *__restrict__ w,
-                                                   float *__restrict__ cv_sel) {
+                                                   float *__restrict__ cv_sel,
+    const int32_t *__restrict__ qr_flag) {
   constexpr int NC = 8;
   __shared__ double Db[TBO * TBO];
   __shared__ double Xb[TBO * NC];
   const int h = blockIdx.y;
   const HeadDesc Dh = desc[h];
+  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
   if (Dh.t <= kLdsMaxT) return;
   const int t = int(Dh.t);
   const int c0 = blockIdx.x * NC;
@@ -715,10 +727,10 @@ hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s) {
   dim3 grid(unsigned(tx * ty * dm.H));
   if (dm.d == 128)
     hipLaunchKernelGGL((k_ols_normal<128>), grid, dim3(NT), 0, s, b.desc, b.panel, b.w, b.mhat, b.Y, b.G, b.rhs,
-                       dm.H, tx, ty, xcd_map);
+                       dm.H, tx, ty, xcd_map, b.qr_flag);
   else
     hipLaunchKernelGGL((k_ols_normal<64>), grid, dim3(NT), 0, s, b.desc, b.panel, b.w, b.mhat, b.Y, b.G, b.rhs,
-                       dm.H, tx, ty, xcd_map);
+                       dm.H, tx, ty, xcd_map, b.qr_flag);
   return hipGetLastError();
 }
 
@@ -730,17 +742,17 @@ hipError_t launch_ols_factor(const Dims &dm, const Buffers &b, hipStream_t s) {
                                        hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_ols_factor, dim3(unsigned(dm.H)), dim3(NT), bytes, s, b.desc, b.G, b.w, b.ols_flist,
-                       b.ols_fcount, b.ols_dn, b.ols_L, b.head_status);
+                       b.ols_fcount, b.ols_dn, b.ols_L, b.head_status, b.qr_flag);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
   if (dm.max_t > kLdsMaxT) {
     hipLaunchKernelGGL(k_ols_flist_g, dim3(unsigned(dm.H)), dim3(NT), 0, s, b.desc, b.G, b.w, b.ols_flist,
-                       b.ols_fcount, b.ols_dn);
+                       b.ols_fcount, b.ols_dn, b.qr_flag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(k_ols_factor_g, dim3(unsigned(dm.H)), dim3(NT), 0, s, b.desc, b.G, b.ols_flist, b.ols_fcount,
-                       b.ols_dn, b.ols_L, b.head_status);
+                       b.ols_dn, b.ols_L, b.head_status, b.qr_flag);
     return hipGetLastError();
   }
   return hipSuccess;
@@ -751,10 +763,10 @@ hipError_t launch_ols_trsm(const Dims &dm, const Buffers &b, hipStream_t s) {
   if (dm.max_t > kLdsMaxT) {
     if (dm.d == 128)
       hipLaunchKernelGGL((k_ols_trsm_g<128>), grid, dim3(NT), 0, s, b.desc, b.rhs, b.ols_flist, b.ols_fcount,
-                         b.ols_dn, b.ols_L, b.w, b.cv_sel);
+                         b.ols_dn, b.ols_L, b.w, b.cv_sel, b.qr_flag);
     else
       hipLaunchKernelGGL((k_ols_trsm_g<64>), grid, dim3(NT), 0, s, b.desc, b.rhs, b.ols_flist, b.ols_fcount,
-                         b.ols_dn, b.ols_L, b.w, b.cv_sel);
+                         b.ols_dn, b.ols_L, b.w, b.cv_sel, b.qr_flag);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || dm.min_t > kLdsMaxT) return e;
   }
@@ -767,13 +779,13 @@ hipError_t launch_ols_trsm(const Dims &dm, const Buffers &b, hipStream_t s) {
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_ols_trsm<128>), grid, dim3(NT), bytes, s, b.desc, b.rhs, b.ols_flist, b.ols_fcount,
-                       b.ols_dn, b.ols_L, b.w, b.cv_sel);
+                       b.ols_dn, b.ols_L, b.w, b.cv_sel, b.qr_flag);
   } else {
     e = hipFuncSetAttribute(reinterpret_cast<const void *>(&k_ols_trsm<64>),
                             hipFuncAttributeMaxDynamicSharedMemorySize, int(bytes));
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL((k_ols_trsm<64>), grid, dim3(NT), bytes, s, b.desc, b.rhs, b.ols_flist, b.ols_fcount,
-                       b.ols_dn, b.ols_L, b.w, b.cv_sel);
+                       b.ols_dn, b.ols_L, b.w, b.cv_sel, b.qr_flag);
   }
   return hipGetLastError();
 }

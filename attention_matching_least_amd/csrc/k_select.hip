@@ -1554,8 +1554,11 @@ __global__ __launch_bounds__(256) void k_gram(const HeadDesc *__restrict__ desc,
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void k_resid(const HeadDesc *__restrict__ desc, const double *__restrict__ panel,
                                                const double *__restrict__ w, const double *__restrict__ m, int cycle,
-                                               int kR, int polish, double *__restrict__ r, double *__restrict__ mhat) {
+                                               int kR, int polish, double *__restrict__ r, double *__restrict__ mhat,
+                                               double *__restrict__ rpart) {
+  static_assert(kResidRows == 256, "one query per thread");
   __shared__ double ws[256];
+  __shared__ double red[2][4];
   const int h = blockIdx.y;
   const HeadDesc D = desc[h];
   int64_t p;
@@ -1580,9 +1583,32 @@ __global__ __launch_bounds__(256) void k_resid(const HeadDesc *__restrict__ desc
     if (valid)
       for (int64_t a = 0; a < cnt; ++a) acc = fma(P[(a0 + a) * D.n + i], ws[a], acc);
   }
-  if (!valid) return;
-  mhat[D.n_off + i] = acc;
-  r[D.n_off + i] = m[D.n_off + i] - acc;
+  double rv = 0.0, mv = 0.0;
+  if (valid) {
+    const double mi = m[D.n_off + i];
+    rv = mi - acc;
+    mv = mi;
+    mhat[D.n_off + i] = acc;
+    r[D.n_off + i] = rv;
+  }
+  // the block's sums of r^2 and m^2 (the relative residual the exact-refit
+  // gate reads), in a fixed order
+  double s0 = rv * rv, s1 = mv * mv;
+  for (int o = 32; o > 0; o >>= 1) {
+    s0 += __shfl_xor(s0, o);
+    s1 += __shfl_xor(s1, o);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    red[0][wave] = s0;
+    red[1][wave] = s1;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0 && rpart) {
+    const int64_t at = (int64_t(h) * gridDim.x + blockIdx.x) * 2;
+    rpart[at] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    rpart[at + 1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  }
 }
 
 }  // namespace
@@ -1706,8 +1732,9 @@ hipError_t launch_gram(const Dims &dm, const Buffers &b, int cycle, int kR, int 
 }
 
 hipError_t launch_resid(const Dims &dm, const Buffers &b, int cycle, int kR, int polish, hipStream_t s) {
-  dim3 grid(unsigned((dm.max_n + 255) / 256), unsigned(dm.H));
-  hipLaunchKernelGGL(k_resid, grid, dim3(256), 0, s, b.desc, b.panel, b.w, b.m, cycle, kR, polish, b.r, b.mhat);
+  dim3 grid(unsigned(dm.nrb), unsigned(dm.H));
+  hipLaunchKernelGGL(k_resid, grid, dim3(256), 0, s, b.desc, b.panel, b.w, b.m, cycle, kR, polish, b.r, b.mhat,
+                     b.rpart);
   return hipGetLastError();
 }
 

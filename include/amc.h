@@ -76,6 +76,8 @@ typedef enum {
 #define AMC_HS_NNLS_CAP 2u       /* an NNLS refit hit its iteration cap */
 #define AMC_HS_NONFINITE 4u      /* Q, K, V or beta_in produced a non-finite logit or output */
 #define AMC_HS_NNLS_SINGULAR 8u  /* a candidate key was linearly dependent on the active set */
+#define AMC_HS_NNLS_QR 16u       /* the head's refits and value fit went through orthogonal
+                                  * factorisations of Phi_S (amc_options.exact_refit) */
 
 /* amc_options.flags */
 #define AMC_FLAG_TRACE 1u /* fill the trace buffer (selection order, scores, weights) */
@@ -136,7 +138,27 @@ typedef struct {
                            * (matrix-core bound) overlap the selection loops of the
                            * groups before them.  Results are the same bits for any
                            * value.  0 = automatic (4 for H >= 256 with H a multiple
-                           * of 32, else 1); 1..16, else AMC_ERR_INVALID_ARG. */
+                           * of 32, else 1); 1..8; 9..16 AMC_ERR_UNSUPPORTED (a
+                           * 16-group run of the 60k-token stack left no result; the
+                           * cause was not established); else AMC_ERR_INVALID_ARG. */
+  int32_t exact_refit;    /* which heads' NNLS refits (and value fit) leave the Gram form
+                           * Phi_S^T Phi_S for orthogonal factorisations of Phi_S itself
+                           * (Lawson-Hanson on the triangular factor of [Phi_S m]; the value
+                           * fit from the factor of [A Y]), which resolve the minimiser when
+                           * the selected keys are nearly collinear or the mass is almost
+                           * fitted (zhichai.net deep-dive, section 1.6; xinfinite.net
+                           * article, section 2, steps 2 and 3).  Budgets up to 640 only.
+                           * 0 (default): a head moves there, for the rest of the call, at
+                           * the first refit whose free set has an estimated
+                           * cond(Phi_P D^-1) above 1e5, whose last relative mass residual
+                           * is below 1e-6, or that met a singular candidate or the cap;
+                           * 1: every head from its first refit; 2: never.  Such heads carry
+                           * AMC_HS_NNLS_QR. */
+  int32_t digits_in_panel; /* recompute mode with bf16 inputs: 1 (default) lets the int8 digit
+                           * rows and value tiles of the mass-feature pass share the panel's
+                           * first bytes (every head group's pass is enqueued before any
+                           * group's selection, which waits for all of them); 0 keeps them
+                           * apart (a larger workspace).  The outputs are the same bits. */
   uint32_t flags;         /* AMC_FLAG_* */
   void *timer;            /* optional amc_timer_create() handle; NULL = none */
 } amc_options;
@@ -164,8 +186,8 @@ typedef struct {
 } amc_trace_layout;
 
 /* Fills *o with the defaults: plain OMP (k = R = 1), automatic NNLS cap and
- * tolerance, one polish refit, 64 GiB Phi budget, float32 C_v, no trace, no
- * timer.  Every refit starts from the previous refit's exact minimiser and
+ * tolerance, one polish refit, 64 GiB Phi budget, float32 C_v, automatic head
+ * groups and exact-refit gate, digit rows in the panel, no trace, no timer.  Every refit starts from the previous refit's exact minimiser and
  * from the gradient Phi_S^T r of its float64 residual; a polish refit repeats
  * that once with no new key. */
 void amc_default_options(amc_options *o);

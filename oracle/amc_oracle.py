@@ -391,7 +391,7 @@ def _rank(c):
 
 
 def omp_select(Phi, m, t, k=1, R=1, replay: Optional[Sequence[Sequence[int]]] = None,
-               margin_tol: float = 1e-6) -> Selection:
+               margin_tol: float = 1e-6, tie_ulps: float = 0.0) -> Selection:
     """Greedy OMP key selection with NNLS refits (p1 section 1.6).
 
     r = m, S = {}.  Each iteration scores every unselected key by r^T Phi[:, j]
@@ -404,6 +404,15 @@ def omp_select(Phi, m, t, k=1, R=1, replay: Optional[Sequence[Sequence[int]]] = 
     oracle's own margin exceeds ``margin_tol`` the picks must equal the
     oracle's (a mismatch is recorded); the oracle then follows the given
     picks either way, so later steps share the same history.
+
+    ``tie_ulps``: the float64 resolution of the scores.  r = m - Phi_S w is a
+    difference of nearly equal sums, so each score c_j carries a rounding
+    error up to about tie_ulps * eps * (Phi[:, j]^T m) (summation bounds for
+    r and c, plus the ulp-level differences two implementations' exp and
+    logits leave in Phi).  A replayed pick whose oracle score lies within the
+    two keys' bounds of the oracle's own pick is a tie, whatever the relative
+    margin: once the mass is fitted to ~1e-9 these bounds exceed 1e-6 of the
+    top score, and no float64 computation decides those picks.
     """
     Phi = np.asarray(Phi, dtype=np.float64)
     m = np.asarray(m, dtype=np.float64)
@@ -415,6 +424,7 @@ def omp_select(Phi, m, t, k=1, R=1, replay: Optional[Sequence[Sequence[int]]] = 
     r = m.copy()
     steps: List[Step] = []
     selected = np.zeros(T, dtype=bool)
+    b_all = np.abs(Phi).T @ np.abs(m)  # scale of each score's rounding error
     for it, (kk, refit) in enumerate(iteration_sizes(t, k, R), start=1):
         c = Phi.T @ r
         c[selected] = NEG_INF
@@ -436,7 +446,18 @@ def omp_select(Phi, m, t, k=1, R=1, replay: Optional[Sequence[Sequence[int]]] = 
             if len(given) != kk or len(set(given)) != kk or any(selected[j] for j in given):
                 raise ValueError(f"replay iteration {it}: invalid picks {given}")
             if set(given) != set(picks):
-                if margin > margin_tol:
+                # the given set differs from the oracle's: it is a different
+                # selection if some key left out scores above some given key
+                # by more than both the margin and the two keys' rounding
+                # bounds (then no ordering within float64 resolution makes
+                # the given set a top kk)
+                eb = tie_ulps * np.finfo(np.float64).eps
+                out = ~selected
+                out[given] = False
+                c_out, b_out = c[out], b_all[out]
+                thr = margin_tol * abs(top)
+                resolved = any(np.any((c_out - c[g] > thr) & (c_out - c[g] > eb * (b_out + b_all[g]))) for g in given)
+                if resolved:
                     st.mismatch = True
                 else:
                     st.forced = True
@@ -498,13 +519,23 @@ def log_weights(w):
         return np.where(w > 0, np.log(np.where(w > 0, w, 1.0)), NEG_INF)
 
 
+def score_tie_ulps(Q, K, t, beta_in=None, scale=None):
+    """Rounding bound of the selection scores, in units of eps * (Phi[:, j]^T m):
+    2 (t + 1) for the sums that form r and c, plus 2 (max |logit| + 2) for
+    the ulp differences of Phi between two float64 implementations (a logit
+    error of eps |l| becomes a relative error of Phi)."""
+    L = logits(Q, K, beta_in, scale)
+    return 2.0 * (t + 1) + 2.0 * (float(np.max(np.abs(L[np.isfinite(L)]))) + 2.0)
+
+
 def compact(Q, K, V, t, k=1, R=1, beta_in=None, scale=None, shift=None, replay=None,
             margin_tol=1e-6) -> Compaction:
     """Compact one head's (K, V) to t keys: C_k (a subset of K), per-key bias
     beta and fitted values C_v (p2 section 2; p3 pipeline)."""
     K = np.asarray(K, dtype=np.float64)
     feats = mass_features(Q, K, V, beta_in, scale, shift)
-    sel = omp_select(feats.Phi, feats.m, t, k, R, replay, margin_tol)
+    tie = score_tie_ulps(Q, K, t, beta_in, scale) if replay is not None else 0.0
+    sel = omp_select(feats.Phi, feats.m, t, k, R, replay, margin_tol, tie)
     S = np.asarray(sel.S, dtype=np.int64)
     Cv = ols_values(feats.Phi[:, S], sel.w, feats.Y)
     beta = log_weights(sel.w)

@@ -11,15 +11,22 @@ on one side only carries at most 1e-6 of that side's largest weight, and the
 relative mass and attention-output errors of the GPU's compacted block are
 within 1e-3 (absolute) of the oracle's own.
 
-The beta rule presumes the NNLS weights are determined to that accuracy in
-float64.  Where the GPU's beta misses it, the check asks the oracle whether
-they are: it solves the same NNLS again in extended precision (long double,
-warm-started from its float64 minimiser) and measures how far beta moves (the
-envelope).  Only where the envelope itself exceeds the beta tolerance (nearly
-collinear columns whose single weights float64 cannot pin down while the
-fitted mass agrees) are the GPU's weights held to the minimum value instead:
-their NNLS residual within 1e-6 (relative) of the oracle's.  Such heads are
-counted; a test fails when more than FALLBACK_SHARE of its heads need it.
+The beta rule presumes the NNLS weights are determined to that accuracy by
+the float64 data.  Where the GPU's beta misses it, the check asks whether
+they are: (i) the columns of the two supports together must have full
+numerical rank (relative smallest singular value above NULL_SV; below it the
+minimisers form a face and both weight vectors lie on it), and (ii) the same
+NNLS solved again in extended precision (long double, warm-started from the
+oracle's float64 minimiser) must not move beta past the tolerance.  Only
+where one of these fails are the GPU's weights held to the minimum value
+instead: their NNLS residual within 1e-6 (relative) of the oracle's.  Such
+heads are counted; a test fails when more than FALLBACK_SHARE of its heads
+need it.
+
+Replayed picks: the oracle's scores carry a float64 rounding bound (see
+oracle.omp_select, tie_ulps); a replayed pick is a mismatch only where a key
+it leaves out scores higher by more than both 1e-6 of the top score and the
+two keys' bounds.
 """
 from __future__ import annotations
 
@@ -37,6 +44,7 @@ WEIGHT_REL = 1e-6
 RESID_REL = 1e-6
 FALLBACK_SHARE = 0.25  # largest share of a test's heads held to the minimum value only
 LD_MAX_T = 512  # largest budget the extended-precision envelope is computed for
+NULL_SV = 1e-10  # relative singular value below which columns count as dependent
 
 
 def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
@@ -107,13 +115,26 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
     rep["fallback"] = False
     rep["beta_envelope"] = None
     weights_ok = rep["beta_maxdiff"] <= BETA_TOL and rep["one_sided_ok"]
-    if not weights_ok and len(w_ref) <= LD_MAX_T:
-        # is beta determined at float64?  the same NNLS in extended precision
-        w_ld = O.nnls_qr(P, m, w0=w_ref, dtype=np.longdouble)
-        both_o = (w_ref > 0) & (w_ld > 0)
-        env = float(np.max(np.abs(np.log(w_ref[both_o]) - np.log(w_ld[both_o])))) if np.any(both_o) else 0.0
+    if not weights_ok:
+        # Is beta determined by the float64 data?  Not when the columns of
+        # both supports together are numerically dependent (their smallest
+        # singular value, unit columns, below NULL_SV: the NNLS minimisers form
+        # a face and the two weight vectors are both on it), nor when the same
+        # NNLS solved again in extended precision moves beta past the tolerance.
+        U = (w_gpu64 > 0) | (w_ref > 0)
+        Pu = P[:, U]
+        nrm = np.linalg.norm(Pu, axis=0)
+        sv = np.linalg.svd(Pu / np.where(nrm > 0, nrm, 1.0), compute_uv=False) if Pu.shape[1] else np.ones(1)
+        rep["union_sv_min"] = float(sv[-1] / sv[0])
+        env = None
+        if len(w_ref) <= LD_MAX_T:
+            w_ld = O.nnls_qr(P, m, w0=w_ref, dtype=np.longdouble)
+            both_o = (w_ref > 0) & (w_ld > 0)
+            env = float(np.max(np.abs(np.log(w_ref[both_o]) - np.log(w_ld[both_o])))) if np.any(both_o) else 0.0
+            if not _one_sided_ok(w_ld, w_ref):
+                env = float("inf")
         rep["beta_envelope"] = env
-        if env > BETA_TOL or not _one_sided_ok(w_ld, w_ref):
+        if rep["union_sv_min"] < NULL_SV or (env is not None and env > BETA_TOL):
             rep["fallback"] = True
             weights_ok = rep["resid_excess"] <= RESID_REL
     rep["ok"] = (not rep["mismatch_iters"] and rep["same_set"] and rep["ck_exact"] and weights_ok and

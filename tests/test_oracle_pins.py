@@ -263,6 +263,54 @@ def test_planted_coarse_dependence_test_misses_minimiser(monkeypatch):
     assert bad / good - 1 > 1e-3
 
 
+def test_score_tie_bound_covers_float64_spread():
+    """The replay's tie bound (score_tie_ulps) against what float64 actually
+    resolves.  On the collinear selection, two exact solvers (Lawson-Hanson
+    and nnls_qr, equal objectives to 1e-12) give scores whose spread on the
+    top two keys reaches their gap (at 38 keys they even order them
+    differently): the bound covers that spread.  At 30 keys the scores are
+    resolved, and the bound is far below the gap."""
+    h = synth.make_head([34, 0], 300, 700, 64, True, "bf16")
+    b = synth.random_beta([35, 0], 700, 1.0)
+    f = oracle.mass_features(h.Q, h.K, h.V, b)
+    sel = O.omp_select(f.Phi, f.m, 40)
+    eb = O.score_tie_ulps(h.Q, h.K, 40, b) * np.finfo(np.float64).eps
+    bj = f.Phi.T @ f.m
+    for it, resolved in ((30, True), (32, False), (36, False), (38, False)):
+        S = sel.S[:it]
+        P = f.Phi[:, S]
+        c1 = f.Phi.T @ (f.m - P @ oracle.nnls_lawson_hanson(P, f.m))
+        c2 = f.Phi.T @ (f.m - P @ oracle.nnls_qr(P, f.m))
+        c1[S] = c2[S] = -np.inf
+        top = np.argsort(-c1)[:2]
+        bound = eb * (bj[top[0]] + bj[top[1]])
+        gap = c1[top[0]] - c1[top[1]]
+        spread = np.max(np.abs(c1[top] - c2[top]))
+        assert spread <= bound
+        if resolved:
+            assert bound < 1e-6 * gap
+        else:
+            assert gap < bound
+
+
+def test_replay_flags_a_resolved_swap():
+    """Planted mistake in a replayed selection: at iteration 5 of workload 0
+    the replay takes the oracle's second-best key.  The scores are resolved
+    there, so the replay reports a mismatch (the tie bound does not hide it)."""
+    h = synth.workload(0).head(0)
+    ref = oracle.compact(h.Q, h.K, h.V, 12)
+    f = ref.features
+    picks = [[j] for j in ref.selection.S]
+    S4 = ref.selection.S[:4]
+    w = oracle.nnls_exact(f.Phi[:, S4], f.m)
+    c = f.Phi.T @ (f.m - f.Phi[:, S4] @ w)
+    c[S4] = -np.inf
+    second = int(np.argsort(-c)[1])
+    bad = picks[:4] + [[second]] + [[j] for j in ref.selection.S[4:] if j != second][:7]
+    rep = oracle.compact(h.Q, h.K, h.V, 12, replay=bad)
+    assert rep.selection.steps[4].mismatch
+
+
 def test_errors_hand_computed():
     """errors() on a case worked by hand: d = 1 (scale 1), keys 0 and log 3
     with values 1 and 2; queries 1 and 0.  Original masses (4, 2), outputs
