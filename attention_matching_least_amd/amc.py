@@ -32,7 +32,7 @@ EXPORTED = [
     "amc_default_options", "amc_workspace_size", "amc_output_offsets", "amc_cycle_offsets",
     "amc_trace_layout_for", "amc_compact", "amc_mass_features", "amc_mass_features_workspace", "amc_nnls",
     "amc_timer_create", "amc_timer_reset", "amc_timer_read", "amc_timer_destroy", "amc_status_string",
-    "amc_version",
+    "amc_version", "amc_compact_noalloc", "amc_noalloc_max_workspace",
 ]
 
 
@@ -99,6 +99,9 @@ def lib() -> ctypes.CDLL:
     L.amc_cycle_offsets.argtypes = [P, O, ctypes.POINTER(i64)]
     L.amc_trace_layout_for.argtypes = [P, O, ctypes.POINTER(TraceLayout)]
     L.amc_compact.argtypes = [P, O, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64, vp, u64, vp]
+    L.amc_compact_noalloc.argtypes = [P, O, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64, vp]
+    L.amc_noalloc_max_workspace.argtypes = []
+    L.amc_noalloc_max_workspace.restype = u64
     L.amc_mass_features.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64, vp]
     L.amc_mass_features_workspace.argtypes = [P, ctypes.POINTER(u64)]
     L.amc_nnls.argtypes = [i32, ctypes.POINTER(i64), vp, vp, vp, i32, i32, i32, dbl, vp, vp, vp]
@@ -111,7 +114,7 @@ def lib() -> ctypes.CDLL:
     L.amc_status_string.restype = ctypes.c_char_p
     L.amc_version.restype = ctypes.c_int
     for name in ("amc_workspace_size", "amc_output_offsets", "amc_cycle_offsets", "amc_trace_layout_for",
-                 "amc_compact", "amc_mass_features", "amc_mass_features_workspace", "amc_nnls",
+                 "amc_compact", "amc_compact_noalloc", "amc_mass_features", "amc_mass_features_workspace", "amc_nnls",
                  "amc_timer_create", "amc_timer_reset", "amc_timer_read"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -335,9 +338,11 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
             phi_budget_bytes: Optional[int] = None, cv_dtype: torch.dtype = torch.float32, trace: bool = False,
             timer: Optional[Timer] = None, scale: float = 0.0, stream=None,
             workspace: Optional[torch.Tensor] = None, head_groups: int = 0, exact_refit: str = "auto",
-            digits_in_panel: bool = True) -> CompactResult:
+            digits_in_panel: bool = True, noalloc: bool = False) -> CompactResult:
     """amc_compact on torch tensors.  Q: (H, n, d) or packed (sum n, d) with
-    cu_q; K, V: (H, T, d) or packed with cu_k; budgets: int or per-head list."""
+    cu_q; K, V: (H, T, d) or packed with cu_k; budgets: int or per-head list.
+    noalloc: amc_compact_noalloc (the library's static per-GPU workspace; no
+    workspace tensor is allocated here)."""
     if not (Q.is_cuda and K.is_cuda and V.is_cuda):
         raise ValueError("Q, K and V must be device tensors")
     if not (Q.dtype == K.dtype == V.dtype):
@@ -356,7 +361,7 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
     prob, keep = make_problem(H, d, cq, ck, bud, _dtype_code(Qp), scale)
     opts = make_options(select, topk, refit_every, nnls_polish, nnls_max_iters, nnls_tol, phi_budget_bytes,
                         cv_dtype, trace, timer, head_groups, exact_refit, digits_in_panel)
-    ws_bytes = workspace_size(prob, opts)
+    ws_bytes = 0 if noalloc else workspace_size(prob, opts)
     cb = output_offsets(prob)
     dev = Qp.device
     S = cb[-1]
@@ -365,7 +370,9 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
     Cv = torch.empty((S, d), dtype=cv_dtype, device=dev)
     sel = torch.empty(S, dtype=torch.int32, device=dev)
     hs = torch.empty(H, dtype=torch.int32, device=dev)
-    if workspace is not None and workspace.numel() >= ws_bytes + 256:
+    if noalloc:
+        ws_buf, ws_ptr = None, None
+    elif workspace is not None and workspace.numel() >= ws_bytes + 256:
         ws_buf = workspace
         ws_ptr = (workspace.data_ptr() + 255) // 256 * 256
     else:
@@ -381,11 +388,17 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
         if beta_in.dtype != torch.float32 or beta_in.numel() != ck[-1] or not beta_in.is_cuda:
             raise ValueError("beta_in must be a float32 device tensor with one entry per key")
         beta_in = beta_in.contiguous()
-    st = lib().amc_compact(ctypes.byref(prob), ctypes.byref(opts), Qp.data_ptr(), Kp.data_ptr(), Vp.data_ptr(),
-                           beta_in.data_ptr() if beta_in is not None else None, Ck.data_ptr(), beta.data_ptr(),
-                           Cv.data_ptr(), sel.data_ptr(), hs.data_ptr(), tr_ptr, tr_bytes, ws_ptr, ws_bytes,
-                           _stream_ptr(stream))
-    _check(st, "amc_compact")
+    bi_ptr = beta_in.data_ptr() if beta_in is not None else None
+    if noalloc:
+        st = lib().amc_compact_noalloc(ctypes.byref(prob), ctypes.byref(opts), Qp.data_ptr(), Kp.data_ptr(),
+                                       Vp.data_ptr(), bi_ptr, Ck.data_ptr(), beta.data_ptr(), Cv.data_ptr(),
+                                       sel.data_ptr(), hs.data_ptr(), tr_ptr, tr_bytes, _stream_ptr(stream))
+        _check(st, "amc_compact_noalloc")
+    else:
+        st = lib().amc_compact(ctypes.byref(prob), ctypes.byref(opts), Qp.data_ptr(), Kp.data_ptr(), Vp.data_ptr(),
+                               bi_ptr, Ck.data_ptr(), beta.data_ptr(), Cv.data_ptr(), sel.data_ptr(), hs.data_ptr(),
+                               tr_ptr, tr_bytes, ws_ptr, ws_bytes, _stream_ptr(stream))
+        _check(st, "amc_compact")
     res = CompactResult(Ck, beta, Cv, sel, cb, hs, None, tl, cc, H)
     if trace:
         # view of the aligned trace region
@@ -393,6 +406,11 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
         res.trace_buf = tr_buf[off: off + tr_bytes]
     res._keep = (ws_buf, tr_buf, keep)
     return res
+
+
+def noalloc_max_workspace() -> int:
+    """Bytes of the static per-GPU workspace of amc_compact_noalloc."""
+    return int(lib().amc_noalloc_max_workspace())
 
 
 def compact_workspace_bytes(cu_q, cu_k, budgets, head_dim: int, dtype: torch.dtype = torch.bfloat16,

@@ -7,6 +7,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <vector>
 
@@ -398,6 +399,34 @@ static int band_cap_setting() {
   return v < 0 ? 0 : (v > kBandCap ? kBandCap : int(v));
 }
 
+// ---------------------------------------------------------------------------
+// static scratch of the allocation-free entry point
+// ---------------------------------------------------------------------------
+// amc_compact_noalloc carves its workspace out of this array instead of a
+// caller buffer.  Each GPU the library runs on holds its own copy, at its own
+// address, until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address comes from
+// hipGetSymbolAddress, once per device, and only that pointer is used.
+constexpr uint64_t kScratchBytes = 256ull << 20;
+static __device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void *g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of `scratch` on the current device (nullptr on error).
+static void *scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+
 }  // namespace amc
 
 using namespace amc;
@@ -485,10 +514,10 @@ amc_status amc_trace_layout_for(const amc_problem *p, const amc_options *o, amc_
     }                                                                             \
   } while (0)
 
-amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q, const void *K,
-                       const void *V, const float *beta_in, void *Ck, float *beta, void *Cv,
-                       int32_t *sel_idx, int32_t *head_status, void *trace, uint64_t trace_bytes,
-                       void *workspace, uint64_t workspace_bytes, void *stream_ptr) {
+static amc_status compact_impl(const amc_problem *p, const amc_options *o, const void *Q, const void *K,
+                               const void *V, const float *beta_in, void *Ck, float *beta, void *Cv,
+                               int32_t *sel_idx, int32_t *head_status, void *trace, uint64_t trace_bytes,
+                               void *workspace, uint64_t workspace_bytes, void *stream_ptr) {
   Plan pl;
   amc_status st = make_plan(p, o, false, pl);
   if (st != AMC_OK) return st;
@@ -727,6 +756,36 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
   cleanup();
   return result;
 }
+
+amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q, const void *K,
+                       const void *V, const float *beta_in, void *Ck, float *beta, void *Cv,
+                       int32_t *sel_idx, int32_t *head_status, void *trace, uint64_t trace_bytes,
+                       void *workspace, uint64_t workspace_bytes, void *stream_ptr) {
+  return compact_impl(p, o, Q, K, V, beta_in, Ck, beta, Cv, sel_idx, head_status, trace, trace_bytes, workspace,
+                      workspace_bytes, stream_ptr);
+}
+
+amc_status amc_compact_noalloc(const amc_problem *p, const amc_options *o, const void *Q, const void *K,
+                               const void *V, const float *beta_in, void *Ck, float *beta, void *Cv,
+                               int32_t *sel_idx, int32_t *head_status, void *trace, uint64_t trace_bytes,
+                               void *stream_ptr) {
+  if (!o) return AMC_ERR_INVALID_ARG;
+  // one head group (no streams or events created) and no timer (its events)
+  amc_options oo = *o;
+  if (oo.head_groups < 0 || oo.head_groups > 16) return AMC_ERR_INVALID_ARG;
+  oo.head_groups = 1;
+  oo.timer = nullptr;
+  Plan pl;
+  amc_status st = make_plan(p, &oo, false, pl);
+  if (st != AMC_OK) return st;
+  if (pl.total > kScratchBytes) return AMC_ERR_WORKSPACE;
+  void *ws = scratch_on_current_device();
+  if (!ws) return AMC_ERR_HIP;
+  return compact_impl(p, &oo, Q, K, V, beta_in, Ck, beta, Cv, sel_idx, head_status, trace, trace_bytes, ws,
+                      kScratchBytes, stream_ptr);
+}
+
+uint64_t amc_noalloc_max_workspace(void) { return kScratchBytes; }
 
 amc_status amc_mass_features(const amc_problem *p, const void *Q, const void *K, const void *V,
                              const float *beta_in, double *shift, float *phi, double *m, float *Y,

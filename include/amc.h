@@ -42,8 +42,10 @@
  *     AMC_ERR_HIP.
  *   - Data-dependent numeric events are reported per head in head_status
  *     (device int32[H], optional) as AMC_HS_* bits; the call still completes.
- *   - The library holds no global mutable state; calls are reentrant.  Two
- *     calls that share a workspace must not overlap in time.
+ *   - The library holds no global mutable state apart from the per-device
+ *     static workspace of amc_compact_noalloc; calls are reentrant.  Two calls
+ *     that share a workspace (or, for amc_compact_noalloc, a GPU) must not
+ *     overlap in time.
  */
 #ifndef AMC_H
 #define AMC_H
@@ -225,6 +227,28 @@ amc_status amc_compact(const amc_problem *p, const amc_options *o, const void *Q
                        const void *V, const float *beta_in, void *Ck, float *beta, void *Cv,
                        int32_t *sel_idx, int32_t *head_status, void *trace, uint64_t trace_bytes,
                        void *workspace, uint64_t workspace_bytes, void *stream);
+
+/* amc_compact without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc).  The workspace is a static device array of the
+ * library, amc_noalloc_max_workspace() bytes (256 MiB) per GPU, held until the
+ * process ends; the call itself allocates nothing (no hipMalloc/hipFree, no
+ * streams or events: the heads run as one group, and options.timer and
+ * options.head_groups are ignored).  The first call on a device looks up that
+ * device's copy of the array (hipGetSymbolAddress).  Outputs, trace and
+ * arguments as for amc_compact; results are the same bits as amc_compact with
+ * head_groups = 1.  Errors: AMC_ERR_WORKSPACE when amc_workspace_size for this
+ * problem exceeds amc_noalloc_max_workspace() (nothing is enqueued); the others
+ * as for amc_compact.  Every call on one GPU shares its array: calls that
+ * overlap in time on one GPU (other streams or threads) race and must be
+ * serialised by the caller. */
+amc_status amc_compact_noalloc(const amc_problem *p, const amc_options *o, const void *Q, const void *K,
+                               const void *V, const float *beta_in, void *Ck, float *beta, void *Cv,
+                               int32_t *sel_idx, int32_t *head_status, void *trace, uint64_t trace_bytes,
+                               void *stream);
+
+/* Bytes of the static workspace amc_compact_noalloc uses on each GPU. */
+uint64_t amc_noalloc_max_workspace(void);
 
 /* Stage 1 alone: the per-head shift s_h (logit maximum, float64[H]), the mass
  * features Phi = exp(l - s) (float32 [n_h][T_h] per head, packed at
