@@ -70,7 +70,7 @@ struct Plan {
            o_cand_lidx = 0, o_cand_cnt = 0, o_band_list = 0, o_band_cnt = 0, o_exact = 0, o_stage = 0,
            o_part = 0, o_vt = 0, o_qdig = 0, o_kdig = 0, o_qexp = 0, o_ktab = 0, o_f64h = 0, o_colsum = 0, o_rpn = 0, o_rabs = 0,
            o_surv = 0, o_survcnt = 0, o_pruneL = 0, o_q8 = 0, o_q8bad = 0, o_surv2 = 0, o_surv2cnt = 0,
-           o_qrflag = 0, o_qrbuf = 0, o_rpart = 0, total = 0;
+           o_qrflag = 0, o_qrbuilt = 0, o_qrbuf = 0, o_rpart = 0, total = 0;
   bool exact_path = false;  // some head may take the orthogonal-factorisation refit
   bool store_q8 = false;  // the 8-bit plane of the second pruning stage fits the budget too
   bool alias_digits = false;  // digit rows and value tiles lie in the panel (recompute mode)
@@ -160,11 +160,9 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     D.n_sblk = ceil_div(D.n, kShiftRows);
     D.cyc_off = cyc;
     D.qr_off = -1;
-    if (!features_only && o->exact_refit != 2 && D.t <= kQrMaxT) {
-      // two (t + 129) x (t + 129) float64 factors (the value fit's has t + d + 1 columns)
-      const int64_t ldq = D.t + 1 + 128;
+    if (!features_only && o->exact_refit != 2 && D.t <= kQrMaxT && D.n <= kQrMaxN) {
       D.qr_off = qrb;
-      qrb += 2 * ldq * ldq;
+      qrb += qr_layout(D.t, D.n).total;
       pl.exact_path = true;
     }
     if (!features_only) {
@@ -250,6 +248,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.o_rpart = take(16ull * H * dm.nrb);
   if (pl.exact_path) {
     pl.o_qrflag = take(4ull * H);
+    pl.o_qrbuilt = take(4ull * H);
     pl.o_qrbuf = take(8ull * uint64_t(qrb));
   }
   if (pl.store_phi) {  // bounded sweep, band and rescoring state
@@ -379,6 +378,7 @@ static Buffers head_range(const Buffers &b, int h0, int64_t max_qblk, int64_t nr
   if (b.q8_bad) r.q8_bad = b.q8_bad + h0;
   if (b.surv2_cnt) r.surv2_cnt = b.surv2_cnt + h0;
   if (b.qr_flag) r.qr_flag = b.qr_flag + h0;
+  if (b.qr_built) r.qr_built = b.qr_built + h0;
   if (b.rpart) r.rpart = b.rpart + int64_t(h0) * 2 * nrb;
   return r;
 }
@@ -606,6 +606,7 @@ static amc_status compact_impl(const amc_problem *p, const amc_options *o, const
   b.rpart = reinterpret_cast<double *>(ws + pl.o_rpart);
   if (pl.exact_path) {
     b.qr_flag = reinterpret_cast<int32_t *>(ws + pl.o_qrflag);
+    b.qr_built = reinterpret_cast<int32_t *>(ws + pl.o_qrbuilt);
     b.qrbuf = reinterpret_cast<double *>(ws + pl.o_qrbuf);
   }
   if (tracing) {
@@ -631,8 +632,10 @@ static amc_status compact_impl(const amc_problem *p, const amc_options *o, const
   if (b.tr_swept && !pl.store_phi) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.tr_swept, pl.sum_cycles, 0, stream));
   if (b.tr_swept8) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.tr_swept8, pl.sum_cycles, 0, stream));
   if (b.q8_bad) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.q8_bad, dm.H, 0, stream));
-  // exact refit: 2 sends every eligible head there from its first refit
-  if (b.qr_flag) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.qr_flag, dm.H, o->exact_refit == 1 ? 2 : 0, stream));
+  // exact refit: 2 sends every eligible head there from its first refit; 0
+  // leaves it to the Gram solver until that flags the head
+  if (b.qr_flag) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.qr_flag, dm.H, o->exact_refit == 0 ? 2 : 0, stream));
+  if (b.qr_built) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.qr_built, dm.H, 0, stream));
 
   // The heads run in groups, each on a stream of its own (the caller's for the
   // first), joined back to the caller's stream by events: the groups' mass

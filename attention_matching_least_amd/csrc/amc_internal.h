@@ -24,7 +24,8 @@ constexpr int kBandCap = 128;    // candidates per head the float64 rescoring ta
 constexpr int kRescoreRows = 256; // queries per block of the rescoring kernel
 constexpr int kStoredMaxN = 8192; // longest head (queries) the stored-Phi path takes
 constexpr int kQrMaxT = 640;     // largest budget the orthogonal-factorisation refit takes
-constexpr double kQrCond = 1e5;  // estimated cond(Phi_S D^-1) above which a head's refits leave the Gram form
+constexpr int kQrMaxN = 8192;    // most queries it takes (the append kernel holds a head's rows in registers)
+constexpr int kQrChunk = 8;      // slots per block reflector of its factorisation
 constexpr double kQrRelResid = 1e-6;  // relative mass residual below which they do
 constexpr int kResidRows = 256;  // queries per block of the residual kernel (one partial sum each)
 
@@ -49,10 +50,36 @@ struct HeadDesc {
   int64_t vt_off;         // first element of the head's transposed value tiles (bf16 inputs)
   int64_t kt_off;         // first row of the head in the arrays of keys padded to whole 64-key tiles
   int64_t ldN;            // stored planes: column stride (n rounded up to 64)
-  int64_t qr_off;         // first element of the head's two factors of the exact refit (-1: none;
-                          // each (t + 129) x (t + 129) float64, row stride t + 129)
+  int64_t qr_off;         // first element of the head's exact-refit state (-1: none), laid out
+                          // by qr_layout
 };
 static_assert(sizeof(HeadDesc) == 20 * 8, "HeadDesc layout");
+
+// Float64 words of one head's exact-refit state, in this order (each part to a
+// multiple of 32 words): V [t][n] Householder vectors, Rb [t][t] triangular
+// factor (column-packed), cb [t] leading part of the rotated mass, Tw [t / 4][8][8]
+// block-reflector factors, mt [n] rotated mass, W: the work area of the
+// Lawson-Hanson steps (a packed triangle) and of the value fit ((t + 129)^2
+// triangle and t x 128 solution).
+struct QrLayout {
+  int64_t V, Rb, cb, Tw, mt, W, total;
+};
+__host__ __device__ inline QrLayout qr_layout(int64_t t, int64_t n) {
+  const auto pad = [](int64_t x) { return (x + 31) & ~int64_t(31); };
+  const int64_t ld = t + 129;
+  QrLayout L;
+  L.V = 0;
+  L.Rb = pad(t * n);
+  L.cb = L.Rb + pad(t * t);
+  L.Tw = L.cb + pad(t);
+  L.mt = L.Tw + pad((t + 3) / 4 * kQrChunk * kQrChunk);  // chunks of 4 slots at the most
+  L.W = L.mt + pad(n);
+  // the larger of the value fit's (triangle and solution) and the Lawson-Hanson
+  // steps' (packed free block, right-hand side and t full-height columns)
+  const int64_t ols = ld * ld + t * 128, lh = t * (t + 3) / 2 + t + t * t + 64;
+  L.total = L.W + pad(ols > lh ? ols : lh);
+  return L;
+}
 
 // Device pointers of the workspace carve-up and of the caller's buffers.
 struct Buffers {
@@ -118,9 +145,11 @@ struct Buffers {
   double *stage;       // [sum n][kBandCap] float64 Phi columns of the band, per head [kBandCap][n]
   double *part;        // [H][kBandCap][max_qblk] partial scores of the band per query block
   int32_t *head_status;  // [H] or null
-  int32_t *qr_flag;    // [H] exact refit: 0 Gram form, 1 flagged at this refit, 2 every later refit
-                       // (null: the path is off)
-  double *qrbuf;       // per head at qr_off: two factors of the exact refit
+  int32_t *qr_flag;    // [H] exact refit: 0 Gram form, 1 flagged at this refit, 2 every later refit,
+                       // bit 4: the value fit too (null: the path is off; heads with qr_off < 0
+                       // keep the Gram form)
+  int32_t *qr_built;   // [H] slots of the head's orthogonal factorisation that are current
+  double *qrbuf;       // per head at qr_off: the exact refit's factorisation and work triangles
   double *rpart;       // [H][nrb][2] per 256-query block: sum r^2 and sum m^2 of the last residual
   // trace (all null when tracing is off)
   double *tr_shift, *tr_pick_score, *tr_weight, *tr_runner;

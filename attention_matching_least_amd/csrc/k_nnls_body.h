@@ -1391,35 +1391,6 @@ __device__ __forceinline__ void pg_warmup(const St &S, const double *G, int64_t 
   snapshot(S, p);
 }
 
-// Largest eigenvalue of (L L^T)^-1 = Gs_PP^-1 (the free set's scaled Gram
-// matrix), by three steps of inverse power iteration from x = 1: a lower
-// bound that the first steps already bring within a small factor.  With the
-// unit diagonal, lambda_max(Gs_PP) <= np, so np times it bounds
-// cond(Phi_P D^-1)^2 from above by roughly that factor.
-__device__ double inv_lambda_est(const St &S, int np, Red *red) {
-  const int tid = threadIdx.x;
-  __syncthreads();
-  for (int k = tid; k < np; k += NT) S.x0[k] = 1.0;
-  double nx = sqrt(double(np)), lam = 0.0;
-  for (int it = 0; it < 3; ++it) {
-    __syncthreads();
-    fwd_solve(S, np, 1);
-    __syncthreads();
-    bwd_solve(S, np, S.x0);
-    __syncthreads();
-    double s = 0.0;
-    for (int k = tid; k < np; k += NT) s = fma(S.x0[k], S.x0[k], s);
-    const double ny = sqrt(block_sum_d(s, red));
-    if (!(ny > 0.0) || !isfinite(ny)) return INFINITY;
-    lam = ny / nx;
-    const double inv = 1.0 / ny;
-    for (int k = tid; k < np; k += NT) S.x0[k] *= inv;
-    nx = 1.0;
-  }
-  __syncthreads();
-  return lam;
-}
-
 // One refit per head.  polish: no new key; refine the last fit (p = t).
 // kGlobal: the state lives in the workspace (budgets above kNnlsLdsT); else
 // in LDS.  Each variant skips the heads of the other.
@@ -1513,12 +1484,13 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
     int32_t *sg = persisted_slots(vec_g, int(D.t));
     for (int k = tid; k < int(D.t); k += NT) sg[k] = S.slot[k];
   }
-  // Does the Gram form resolve this head's minimiser?  Not when the free set
-  // is nearly collinear (estimated cond(Phi_P D^-1) above kQrCond), when the
-  // mass is fitted to a relative residual below kQrRelResid (the last
-  // residual's partial sums), or when a candidate proved singular or the cap
-  // was hit: then this refit and every later one of the head go to the
-  // orthogonal-factorisation path, which reports its own status.
+  // Does the Gram form resolve this head's minimiser?  Not when the mass is
+  // fitted to a relative residual below kQrRelResid (the last residual's
+  // partial sums: the KKT decisions then rest on gradients at rounding level),
+  // nor when a candidate proved singular (a pivot below 1e-7 in unit-diagonal
+  // form, cond(Phi_P D^-1) beyond 1e7) or the cap was hit: then this refit and
+  // every later one of the head go to the orthogonal-factorisation path, which
+  // reports its own status.
   bool gate = false;
   if (qr_ok && tol > 0.0) {
     gate = (sh_status & int(AMC_HS_NNLS_CAP | AMC_HS_NNLS_SINGULAR)) != 0;
@@ -1529,10 +1501,6 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
         mm += rpart[(int64_t(h) * nrb + k) * 2 + 1];
       }
       gate = rr < kQrRelResid * kQrRelResid * mm;
-    }
-    if (!gate && np > 1) {
-      const double lam = inv_lambda_est(S, np, &red);
-      gate = !(lam * double(np) <= kQrCond * kQrCond);
     }
   }
   if (tid == 0) {

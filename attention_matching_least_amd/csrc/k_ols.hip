@@ -70,7 +70,7 @@ __global__ __launch_bounds__(NT) void k_ols_normal(const HeadDesc *__restrict__ 
   }
   if (h >= H) return;
   const HeadDesc Dh = desc[h];
-  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
+  if (qr_flag && (qr_flag[h] & 4)) return;  // the value fit of k_ols_qr
   const int64_t t = Dh.t, n = Dh.n;
   const int64_t a0 = int64_t(j % tx) * 64;
   const int bt = j / tx;
@@ -162,7 +162,7 @@ __global__ __launch_bounds__(NT) void k_ols_factor(const HeadDesc *__restrict__ 
   __shared__ int sh_f, sh_fail;
   const int h = blockIdx.x;
   const HeadDesc Dh = desc[h];
-  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
+  if (qr_flag && (qr_flag[h] & 4)) return;  // the value fit of k_ols_qr
   if (Dh.t > kLdsMaxT) return;  // k_ols_factor_g
   const int t = int(Dh.t);
   const int tid = threadIdx.x;
@@ -251,7 +251,7 @@ __global__ __launch_bounds__(NT) void k_ols_trsm(const HeadDesc *__restrict__ de
   extern __shared__ __attribute__((aligned(16))) double sm[];
   const int h = blockIdx.y;
   const HeadDesc Dh = desc[h];
-  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
+  if (qr_flag && (qr_flag[h] & 4)) return;  // the value fit of k_ols_qr
   if (Dh.t > kLdsMaxT) return;  // k_ols_trsm_g
   const int t = int(Dh.t);
   const int c0 = blockIdx.x * NCB;
@@ -428,7 +428,7 @@ __global__ __launch_bounds__(NT) void k_ols_flist_g(const HeadDesc *__restrict__
   __shared__ int wcnt[NT / 64];
   const int h = blockIdx.x;
   const HeadDesc Dh = desc[h];
-  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
+  if (qr_flag && (qr_flag[h] & 4)) return;  // the value fit of k_ols_qr
   if (Dh.t <= kLdsMaxT) return;
   const int t = int(Dh.t);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -468,7 +468,7 @@ __global__ __launch_bounds__(NT) void k_ols_factor_g(const HeadDesc *__restrict_
   __shared__ int sh_fail;
   const int h = blockIdx.x;
   const HeadDesc Dh = desc[h];
-  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
+  if (qr_flag && (qr_flag[h] & 4)) return;  // the value fit of k_ols_qr
   if (Dh.t <= kLdsMaxT) return;
   const int t = int(Dh.t);
   const int f = fcount[h];
@@ -623,7 +623,7 @@ __global__ __launch_bounds__(NT) void k_ols_trsm_g(const HeadDesc *__restrict__ 
   __shared__ double Xb[TBO * NC];
   const int h = blockIdx.y;
   const HeadDesc Dh = desc[h];
-  if (qr_flag && qr_flag[h] != 0) return;  // the value fit of k_ols_qr
+  if (qr_flag && (qr_flag[h] & 4)) return;  // the value fit of k_ols_qr
   if (Dh.t <= kLdsMaxT) return;
   const int t = int(Dh.t);
   const int c0 = blockIdx.x * NC;

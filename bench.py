@@ -14,6 +14,11 @@ group and the library's HIP-event timer attached, so that every event pair
 brackets one kernel running alone: the per-kernel times and the dominant
 kernel's roofline figure come from it.  The CPU baseline is the float64 oracle
 on a small seeded sample of the same heads.
+
+The same run (default workload, unless --no-long) also measures the metric's
+second half: the wall-clock seconds of compacting the 60k-token stack (288
+heads, T = 60000, n = 8192, t = 6000, top-k 32, refit every 4, Phi recomputed
+in every sweep), reported under "long_context".
 """
 from __future__ import annotations
 
@@ -36,6 +41,7 @@ import synth  # noqa: E402
 HBM_PEAK_GBS = 8000.0
 F64_MFMA_PEAK_TFS = 78.6
 I8_MFMA_PEAK_TOPS = 5000.0  # dense int8 matrix peak of the MI355X
+BF16_MFMA_PEAK_TFS = 2500.0  # dense bf16 matrix peak of the MI355X
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic_qwen3-4b-stack-T8192-50x.md")
 KERNEL_SOURCES = {"k_sweep": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_select.hip"),
                   "k_phi": os.path.join(ROOT, "attention_matching_least_amd", "csrc", "k_phi.hip")}
@@ -240,28 +246,29 @@ def bench_online(args):
 SELECT_CLASSES = ("init", "shift", "phi", "sweep", "merge", "panel", "gram", "nnls", "resid")
 
 
-def bench_long(args):
-    """The 60k-token stack: wall-clock seconds of the compaction calls over all
+def gen_long(args, H: int):
+    """Inputs of the 60k-token stack (H heads), bf16 bit patterns per head.
+    Generated in worker processes before anything touches the GPU."""
+    flat = []
+    with ProcessPoolExecutor(max_workers=args.workers) as ex:
+        for g0 in range(0, H, 48):
+            flat.extend(ex.map(_head_bits, [(3, h) for h in range(g0, min(H, g0 + 48))], chunksize=1))
+            print(f"60k-token stack: generated heads up to {min(H, g0 + 48)}", file=sys.stderr, flush=True)
+    return flat
+
+
+def run_long(args, flat, H: int, timer=None):
+    """Wall-clock seconds of the compaction calls over the 60k-token stack's H
     heads (key selection: shift, mass features, sweeps with Phi recomputed,
     panel, Gram, NNLS refits, residuals; plus the value fit and packing, so the
     figure bounds the key selection from above), in as few calls as the free
-    device memory allows.  The per-kernel sums are reported beside it; with
-    head groups on several streams they overlap and exceed the wall time."""
+    device memory allows.  Returns the JSON fields of the measurement."""
     import torch
 
     from attention_matching_least_amd import amc
 
     dev = torch.device("cuda:0")
     w = synth.workload(3)
-    H = args.heads if args.heads > 0 else w.num_heads
-    # all inputs are generated before anything touches the GPU (the worker
-    # processes are forked from this one)
-    t_gen = time.perf_counter()
-    flat = []
-    with ProcessPoolExecutor(max_workers=args.workers) as ex:
-        for g0 in range(0, H, 48):
-            flat.extend(ex.map(_head_bits, [(3, h) for h in range(g0, min(H, g0 + 48))], chunksize=1))
-            print(f"generated heads up to {min(H, g0 + 48)}", file=sys.stderr, flush=True)
     if args.head_batch > 0:
         B = max(1, min(args.head_batch, H))
     else:
@@ -276,9 +283,7 @@ def bench_long(args):
             if need + B * per_in <= free:
                 break
     allparts = [flat[b0:b0 + B] for b0 in range(0, H, B)]
-    flat = None
-    gen_s = time.perf_counter() - t_gen
-    timer = None if args.no_timer else amc.Timer()
+    flat.clear()
     sel_ms, call_s, statuses, kern = 0.0, 0.0, [], {}
     for bi, b0 in enumerate(range(0, H, B)):
         hs = list(range(b0, min(H, b0 + B)))
@@ -300,6 +305,7 @@ def bench_long(args):
         if timer:
             timer.reset()
         torch.cuda.synchronize()
+        print(f"60k-token stack: call {bi} on heads {hs[0]}..{hs[-1]}", file=sys.stderr, flush=True)
         t0 = time.perf_counter()
         res = amc.compact(Q, K, V, w.budgets[b0:b0 + nb], timer=timer, **kw)
         torch.cuda.synchronize()
@@ -312,34 +318,44 @@ def bench_long(args):
                 kern[k] = kern.get(k, 0.0) + v["total_ms"]
         del Q, K, V, res
         torch.cuda.empty_cache()
-        print(f"batch {b0 // B}: heads {hs[0]}..{hs[-1]} done, {call_s:.1f} s so far", file=sys.stderr, flush=True)
+        print(f"60k-token stack: call {bi} done, {call_s:.1f} s so far", file=sys.stderr, flush=True)
     status = np.concatenate(statuses)
-    sel_s = sel_ms / 1e3 if timer else None
     scale = w.num_heads / H
-    print(json.dumps({
+    out = {
         "metric": "OMP key-select s at T=60k",
         "value": round(call_s * scale, 2),
         "value_covers": "wall-clock seconds of the compaction calls: key selection plus the value fit and packing",
         "unit": "s",
-        "n_gpus": 1,
-        "steps": 1,
-        "warmup": 0,
         "higher_is_better": False,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "f64",
-        "data": "synthetic (seeded clustered Gaussians, bf16)",
         "config": {"workload": w.name, "heads_run": H, "heads_total": w.num_heads, "head_batch": B, "T": w.T,
                    "n": w.n, "d": w.d, "budget": w.budgets[0], "topk": w.topk, "refit_every": w.refit_every,
                    "phi": "recomputed in every sweep"},
         "calls": len(allparts),
         "extrapolated_from_heads": H if H < w.num_heads else None,
         "full_call_s_measured": round(call_s, 3),
-        "key_select_kernel_sum_s": round(sel_s, 3) if sel_s is not None else None,
-        "kernels_ms_measured": {k: round(v, 1) for k, v in kern.items()},
         "head_status_nonzero": int(np.count_nonzero(status)),
-        "input_generation_s": round(gen_s, 1),
-    }), flush=True)
+        "heads_exact_refit": int(np.count_nonzero(status & 16)),
+    }
+    if timer:
+        out["key_select_kernel_sum_s"] = round(sel_ms / 1e3, 3)
+        out["kernels_ms_measured"] = {k: round(v, 1) for k, v in kern.items()}
+    return out
+
+
+def bench_long(args):
+    """The 60k-token stack alone (--workload 3), with the per-kernel timer."""
+    from attention_matching_least_amd import amc
+
+    w = synth.workload(3)
+    H = args.heads if args.heads > 0 else w.num_heads
+    t_gen = time.perf_counter()
+    flat = gen_long(args, H)
+    gen_s = time.perf_counter() - t_gen
+    timer = None if args.no_timer else amc.Timer()
+    res = run_long(args, flat, H, timer)
+    res.update({"n_gpus": 1, "steps": 1, "warmup": 0, "scaling": "weak", "vs_baseline": None, "dtype": "f64",
+                "data": "synthetic (seeded clustered Gaussians, bf16)", "input_generation_s": round(gen_s, 1)})
+    print(json.dumps(res), flush=True)
 
 
 def _online_init_bits(h):
@@ -364,8 +380,13 @@ def main():
     ap.add_argument("--heads", type=int, default=0, help="workload 3: heads to run (0: all 288)")
     ap.add_argument("--head-batch", type=int, default=0,
                     help="workload 3: heads per compaction call (0: as many as free memory allows)")
-    ap.add_argument("--cpu-sample", type=int, default=3, help="oracle heads timed for the CPU baseline (0: skip)")
+    ap.add_argument("--cpu-sample", type=int, default=8, help="oracle heads timed for the CPU baseline (0: skip)")
+    ap.add_argument("--no-long", action="store_true",
+                    help="leave out the 60k-token stack's key-selection seconds (run by default with workload 2)")
     ap.add_argument("--workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
+    ap.add_argument("--exact-refit", default="auto", choices=["auto", "gated", "never"],
+                    help="NNLS refits through the orthogonal factorisation: every head it takes, heads the "
+                         "Gram solver flags, none")
     ap.add_argument("--no-timer", action="store_true", help="skip the kernel pass (per-kernel events, roofline)")
     ap.add_argument("--head-groups", type=int, default=0,
                     help="head groups (streams) of the timed steps; 0: the library's choice")
@@ -409,6 +430,13 @@ def main():
     t_gen = time.perf_counter()
     w, Qb, Kb, Vb = generate(args.workload, args.workers)
     gen_s = time.perf_counter() - t_gen
+    # the 60k-token stack's inputs too, before anything touches the GPU
+    long_flat, long_H, long_gen_s = None, 0, 0.0
+    if args.workload == 2 and not args.no_long:
+        long_H = args.heads if args.heads > 0 else synth.workload(3).num_heads
+        t_lg = time.perf_counter()
+        long_flat = gen_long(args, long_H)
+        long_gen_s = time.perf_counter() - t_lg
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
     def up(a):
@@ -422,9 +450,10 @@ def main():
     cu_q = [w.n * h for h in range(H + 1)]
     cu_k = [w.T * h for h in range(H + 1)]
     select = "omp" if (w.topk == 1 and w.refit_every == 1) else "batched"
-    kw = dict(cu_q=cu_q, cu_k=cu_k, select=select, topk=w.topk, refit_every=w.refit_every)
+    kw = dict(cu_q=cu_q, cu_k=cu_k, select=select, topk=w.topk, refit_every=w.refit_every,
+              exact_refit=args.exact_refit)
     ws_bytes = amc.compact_workspace_bytes(cu_q, cu_k, w.budgets, w.d, tdt, select=select, topk=w.topk,
-                                           refit_every=w.refit_every)
+                                           refit_every=w.refit_every, exact_refit=args.exact_refit)
     workspace = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     timer = None if args.no_timer else amc.Timer()
 
@@ -480,16 +509,25 @@ def main():
                 "swept_keys_per_step": swept, "swept_keys8_per_step": swept8,
                 "keys_per_step_unpruned": int(sum(-(-b // kr) for b in w.budgets)) * w.T}))
         ph = kernels.get("phi")
-        if ph and phi_ops:
-            # matrix-core work of the mass features (phi_matrix_ops), int8-equivalent operations
+        if ph:
+            # algorithmic work of the mass features per head: Phi written (n T float32 values,
+            # as its two 16-bit planes), Q, K, V read (bf16), m (float64) and Y (float32)
+            # written; 2 n T d flops for Q K^T and 2 n T d for Phi V
             secs = ph["total_ms"] * 1e-3
-            achieved = phi_ops * args.steps / secs / 1e12
+            esz = 2 if w.dtype == "bf16" else 4
+            bytes_head = 4.0 * w.n * w.T + esz * (w.n + 2 * w.T) * w.d + 8.0 * w.n + 4.0 * w.n * w.d
+            per_step = bytes_head * H
+            achieved = per_step * args.steps / secs / 1e9
+            flops = 4.0 * w.n * w.T * w.d * H * args.steps
             found.append((ph["total_ms"], {
-                "bound": "mfma", "achieved": round(achieved, 1), "peak": I8_MFMA_PEAK_TOPS, "unit": "TOP/s",
-                "frac": round(achieved / I8_MFMA_PEAK_TOPS, 4), "traffic": read_traffic("k_phi"),
+                "bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": read_traffic("k_phi"),
                 "kernel": "k_phi8", "avg_launch_ms": round(ph["avg_ms"], 4), "launches": ph["launches"],
-                "algorithmic_ops_per_launch": phi_ops * args.steps / ph["launches"],
-                "f64_equivalent_logit_tflops": round(2.0 * w.n * w.T * w.d * H * args.steps / secs / 1e12, 2)}))
+                "algorithmic_bytes_per_launch": per_step * args.steps / ph["launches"],
+                "bf16_mfma_tflops": round(flops / secs / 1e12, 2),
+                "bf16_mfma_frac": round(flops / secs / 1e12 / BF16_MFMA_PEAK_TFS, 4),
+                "int8_ops_executed_per_launch": (phi_ops * args.steps / ph["launches"]) if phi_ops else None,
+                "int8_ops_frac": round(phi_ops * args.steps / secs / 1e12 / I8_MFMA_PEAK_TOPS, 4) if phi_ops else None}))
         found.sort(key=lambda x: -x[0])
         if found:
             roofline = found[0][1]
@@ -497,6 +535,16 @@ def main():
             roofline_other = found[1][1]
 
     cpu = cpu_baseline(args.workload, args.cpu_sample) if args.cpu_sample > 0 else None
+    long_ctx = None
+    if long_flat is not None:
+        # the headline's buffers go before the 60k-token stack takes the card
+        del Q, K, V, workspace, res
+        if timer:
+            del kres
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        long_ctx = run_long(args, long_flat, long_H)
+        long_ctx["input_generation_s"] = round(long_gen_s, 1)
 
     out = {
         "metric": "KV heads compacted/sec at T=8192,50x (d=128)",
@@ -521,7 +569,9 @@ def main():
         "kernel_pass": kernel_pass,
         "kernels_ms": {k: round(v["total_ms"] / args.steps, 3) for k, v in (kernels or {}).items()},
         "head_status_nonzero": int(np.count_nonzero(status)),
+        "heads_exact_refit": int(np.count_nonzero(status & 16)),
         "input_generation_s": round(gen_s, 1),
+        "long_context": long_ctx,
     }
     print(json.dumps(out), flush=True)
 

@@ -149,12 +149,14 @@ typedef struct {
                            * fit from the factor of [A Y]), which resolve the minimiser when
                            * the selected keys are nearly collinear or the mass is almost
                            * fitted (zhichai.net deep-dive, section 1.6; xinfinite.net
-                           * article, section 2, steps 2 and 3).  Budgets up to 640 only.
-                           * 0 (default): a head moves there, for the rest of the call, at
-                           * the first refit whose free set has an estimated
-                           * cond(Phi_P D^-1) above 1e5, whose last relative mass residual
-                           * is below 1e-6, or that met a singular candidate or the cap;
-                           * 1: every head from its first refit; 2: never.  Such heads carry
+                           * article, section 2, steps 2 and 3).  Heads with budget up to
+                           * 640 and at most 8192 queries only; the others keep the Gram form.
+                           * 0 (default): every such head, from its first refit;
+                           * 1: a head moves there, for the rest of the call, at the first
+                           * refit whose last relative mass residual is below 1e-6 or whose
+                           * Gram solve met a singular candidate or the iteration cap (faster
+                           * where few heads need it, but the Gram form can miss the
+                           * minimiser without either sign); 2: never.  Such heads carry
                            * AMC_HS_NNLS_QR. */
   int32_t digits_in_panel; /* recompute mode with bf16 inputs: 1 (default) lets the int8 digit
                            * rows and value tiles of the mass-feature pass share the panel's
