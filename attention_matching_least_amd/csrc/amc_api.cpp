@@ -136,6 +136,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   dm.scale = p->scale > 0.0f ? double(p->scale) : 1.0 / std::sqrt(double(d));
   pl.desc.assign(H, HeadDesc{});
   int64_t phi = 0, nn = 0, tt = 0, t2 = 0, panel = 0, cblk = 0, sblk = 0, cyc = 0, TT = 0, vt = 0, ktr = 0, qrb = 0;
+  int64_t dense = 0;
   for (int h = 0; h < H; ++h) {
     HeadDesc &D = pl.desc[h];
     D.n = p->cu_q[h + 1] - p->cu_q[h];
@@ -143,9 +144,12 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     D.t = features_only ? 1 : p->budgets[h];
     D.q_off = p->cu_q[h];
     D.k_off = p->cu_k[h];
-    // rows of the stored Phi: float32 rows for the mass-feature entry point
-    // (4-key segments), 16-bit planes for the selection (whole 64-key tiles)
-    D.ldT = features_only ? (D.T + 3) / 4 * 4 : (D.T + 63) / 64 * 64;
+    // rows of the stored Phi: float32 rows for the mass-feature entry point on
+    // float32 inputs (4-key segments), 16-bit planes otherwise (whole 64-key
+    // tiles; the mass-feature entry point then unpacks them)
+    D.ldT = (features_only && !dm.in_bf16) ? (D.T + 3) / 4 * 4 : (D.T + 63) / 64 * 64;
+    D.out_off = dense;
+    dense += D.n * D.T;
     D.ldN = (D.n + 63) / 64 * 64;
     D.vt_off = vt;
     D.kt_off = ktr;
@@ -170,7 +174,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
       if (D.n_cblk > kMaxSweepBlocks) return AMC_ERR_UNSUPPORTED;
     }
     const int64_t cycles = ceil_div(D.t, pl.kR);
-    phi += (features_only ? D.n : D.ldN) * D.ldT;
+    phi += (features_only && !dm.in_bf16 ? D.n : D.ldN) * D.ldT;
     vt += (D.T + 63) / 64 * 72 * d;
     ktr += (D.T + 63) / 64 * 64;
     nn += D.n;
@@ -214,6 +218,17 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.o_shift_part = take(4ull * sblk);
   pl.o_shift = take(8ull * H);
   if (features_only) {
+    if (dm.in_bf16) {
+      // the selection's own mass-feature kernels: value tiles, digit rows,
+      // the two Phi planes
+      pl.o_phi = take(phi_bytes);
+      pl.o_vt = take(2ull * vt);
+      pl.o_qdig = take(5ull * d * nn);
+      pl.o_qexp = take(4ull * nn);
+      pl.o_kdig = take((5ull * d + 16) * ktr);
+      pl.o_ktab = take(16ull * ktr);
+      pl.o_f64h = take(4ull * 3 * H);
+    }
     pl.total = off;
     return AMC_OK;
   }
@@ -311,6 +326,7 @@ static void trace_layout(const Plan &pl, amc_trace_layout *L) {
   L->nnls_iters = take(4ull * pl.sum_cycles);
   L->swept_keys = take(4ull * pl.sum_cycles);
   L->swept_keys8 = take(4ull * pl.sum_cycles);
+  L->relres = take(8ull * pl.sum_cycles);
   L->total_bytes = off;
 }
 
@@ -619,6 +635,7 @@ static amc_status compact_impl(const amc_problem *p, const amc_options *o, const
     b.tr_iters = reinterpret_cast<int32_t *>(tr + tl.nnls_iters);
     b.tr_swept = reinterpret_cast<int32_t *>(tr + tl.swept_keys);
     b.tr_swept8 = reinterpret_cast<int32_t *>(tr + tl.swept_keys8);
+    b.tr_relres = reinterpret_cast<double *>(tr + tl.relres);
   }
   NnlsParams np{0, o->nnls_max_iters, o->nnls_tol};
   pl.dm.band_cap = band_cap_setting();
@@ -736,12 +753,14 @@ static amc_status compact_impl(const amc_problem *p, const amc_options *o, const
         AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dg, bg, c, pl.kR, 0, np, stream));
         if (bg.qr_flag) AMC_LAUNCH(AMC_K_NNLS, launch_nnls_qr(dg, bg, c, pl.kR, 0, stream));
         AMC_LAUNCH(AMC_K_RESID, launch_resid(dg, bg, c, pl.kR, 0, stream));
+        if (bg.tr_relres) AMC_LAUNCH(AMC_K_RESID, launch_relres(dg, bg, c, pl.kR, 0, stream));
       }
       for (int r = 0; r < o->nnls_polish; ++r) {
         AMC_LAUNCH(AMC_K_GRAM, launch_gram(dg, bg, 0, pl.kR, 1, stream));
         AMC_LAUNCH(AMC_K_NNLS, launch_nnls(dg, bg, 0, pl.kR, 1, np, stream));
         if (bg.qr_flag) AMC_LAUNCH(AMC_K_NNLS, launch_nnls_qr(dg, bg, 0, pl.kR, 1, stream));
         AMC_LAUNCH(AMC_K_RESID, launch_resid(dg, bg, 0, pl.kR, 1, stream));
+        if (bg.tr_relres) AMC_LAUNCH(AMC_K_RESID, launch_relres(dg, bg, 0, pl.kR, 1, stream));
       }
       AMC_LAUNCH(AMC_K_OLS_NORMAL, launch_ols_normal(dg, bg, stream));
       AMC_LAUNCH(AMC_K_OLS_SOLVE, launch_ols_factor(dg, bg, stream));
@@ -803,9 +822,12 @@ amc_status amc_mass_features(const amc_problem *p, const void *Q, const void *K,
   hipStream_t stream = reinterpret_cast<hipStream_t>(stream_ptr);
   Timer *timer = nullptr;
   const bool sync_check = sync_check_enabled();
-  // The caller's Phi is packed densely ([n][T] per head); the kernel writes rows
-  // of stride ldT, so a caller Phi is only accepted when every T is a multiple of 4.
-  if (phi) {
+  // The caller's Phi is packed densely ([n][T] per head).  float32 inputs: the
+  // kernel writes rows of stride ldT, so a caller Phi is only accepted when
+  // every T is a multiple of 4.  bfloat16 inputs run the selection's kernels
+  // (int8 digit logits, float64 fallback heads) into the 16-bit planes, which
+  // are then unpacked.
+  if (phi && !pl.dm.in_bf16) {
     for (const HeadDesc &D : pl.desc)
       if (D.ldT != D.T) return AMC_ERR_UNSUPPORTED;
   }
@@ -827,6 +849,28 @@ amc_status amc_mass_features(const amc_problem *p, const void *Q, const void *K,
                               ? hipSuccess
                               : hipErrorLaunchFailure));
   if (head_status) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(head_status, pl.dm.H, 0, stream));
+  if (pl.dm.in_bf16) {
+    b.phi = phi;
+    b.phi16 = reinterpret_cast<uint16_t *>(ws + pl.o_phi);
+    b.vt = reinterpret_cast<uint16_t *>(ws + pl.o_vt);
+    if (!phi_logits_f64()) {
+      b.qdig = reinterpret_cast<int8_t *>(ws + pl.o_qdig);
+      b.qexp = reinterpret_cast<int32_t *>(ws + pl.o_qexp);
+      b.kdig = reinterpret_cast<int8_t *>(ws + pl.o_kdig);
+      b.ktab = reinterpret_cast<uint8_t *>(ws + pl.o_ktab);
+      b.f64_heads = reinterpret_cast<int32_t *>(ws + pl.o_f64h);
+      b.f64_list = b.f64_heads + pl.dm.H;
+      b.f64_cnt = b.f64_heads + 2 * pl.dm.H;
+    }
+    const int store = phi ? 2 : 0;
+    AMC_LAUNCH(AMC_K_SHIFT, launch_shift(pl.dm, b, stream));
+    AMC_LAUNCH(AMC_K_INIT, launch_vt(pl.dm, b, stream));
+    if (b.qdig) AMC_LAUNCH(AMC_K_DIGITS, launch_digits(pl.dm, b, stream));
+    AMC_LAUNCH(AMC_K_PHI, launch_phi(pl.dm, b, store, stream));
+    if (b.qdig) AMC_LAUNCH(AMC_K_PHI_F64, launch_phi_fallback(pl.dm, b, store, stream));
+    if (phi) AMC_LAUNCH(AMC_K_PACK, launch_planes_to_phi(pl.dm, b, stream));
+    return AMC_OK;
+  }
   AMC_LAUNCH(AMC_K_SHIFT, launch_shift(pl.dm, b, stream));
   AMC_LAUNCH(AMC_K_PHI, launch_phi(pl.dm, b, phi != nullptr, stream));
   return AMC_OK;

@@ -52,8 +52,10 @@ struct HeadDesc {
   int64_t ldN;            // stored planes: column stride (n rounded up to 64)
   int64_t qr_off;         // first element of the head's exact-refit state (-1: none), laid out
                           // by qr_layout
+  int64_t out_off;        // mass-feature stage: first element of the head in the caller's dense
+                          // float32 Phi ([n][T] per head, packed)
 };
-static_assert(sizeof(HeadDesc) == 20 * 8, "HeadDesc layout");
+static_assert(sizeof(HeadDesc) == 21 * 8, "HeadDesc layout");
 
 // Float64 words of one head's exact-refit state, in this order (each part to a
 // multiple of 32 words): V [t][n] Householder vectors, Rb [t][t] triangular
@@ -154,6 +156,7 @@ struct Buffers {
   // trace (all null when tracing is off)
   double *tr_shift, *tr_pick_score, *tr_weight, *tr_runner;
   int32_t *tr_pick, *tr_iters, *tr_swept, *tr_swept8;
+  double *tr_relres;
 };
 
 struct Dims {
@@ -190,6 +193,8 @@ hipError_t launch_vt(const Dims &dm, const Buffers &b, hipStream_t s);
 // float64 kernel over the heads off the digit grid
 hipError_t launch_digits(const Dims &dm, const Buffers &b, hipStream_t s);
 hipError_t launch_phi_fallback(const Dims &dm, const Buffers &b, int store, hipStream_t s);
+// the two 16-bit planes of the stored Phi to the caller's dense float32 Phi (at out_off)
+hipError_t launch_planes_to_phi(const Dims &dm, const Buffers &b, hipStream_t s);
 // gated: only the heads with b.exact[h] != 0 (else every head)
 hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int gated, hipStream_t s);
 hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, hipStream_t s);
@@ -211,6 +216,8 @@ hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int cyc_keys
 hipError_t launch_nnls_global(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish,
                               const NnlsParams &np, hipStream_t s);
 hipError_t launch_resid(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);
+// trace only (no-op without it): relative mass residual of each head after the refit
+hipError_t launch_relres(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);
 hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s);
 hipError_t launch_pack(const Dims &dm, const Buffers &b, void *Ck, float *beta, void *Cv,
                        int cv_bf16, int32_t *sel_idx, hipStream_t s);

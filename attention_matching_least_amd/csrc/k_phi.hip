@@ -1405,6 +1405,42 @@ static void launch_phi16(const Dims &dm, const Buffers &b, const int32_t *list, 
 #undef AMC_PHI16_ARGS
 }
 
+// The two 16-bit planes of a head's stored Phi ([ldT keys][ldN queries]: the
+// high and the low halves of the float32 bits) to the caller's dense float32
+// Phi ([n][T] rows from out_off), one 64 x 64 tile per block through LDS (reads
+// along queries, writes along keys).
+__global__ __launch_bounds__(256) void k_planes_to_phi(const HeadDesc *__restrict__ desc,
+                                                       const uint16_t *__restrict__ phi16, float *__restrict__ phi) {
+  __shared__ float tile[64][65];
+  const HeadDesc D = desc[blockIdx.y];
+  const int64_t ntq = (D.n + 63) / 64, ntk = (D.T + 63) / 64;
+  if (int64_t(blockIdx.x) >= ntq * ntk) return;
+  const int64_t q0 = (blockIdx.x % ntq) * 64, k0 = (blockIdx.x / ntq) * 64;
+  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  const uint16_t *hp = phi16 + 2 * D.phi_off;
+  const uint16_t *lp = hp + D.ldT * D.ldN;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int kl = ty + 4 * i;
+    const int64_t at = (k0 + kl) * D.ldN + q0 + tx;  // inside the padded planes
+    tile[kl][tx] = __uint_as_float((uint32_t(hp[at]) << 16) | lp[at]);
+  }
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    const int ql = ty + 4 * i;
+    const int64_t q = q0 + ql, k = k0 + tx;
+    if (q < D.n && k < D.T) phi[D.out_off + q * D.T + k] = tile[tx][ql];
+  }
+}
+
+hipError_t launch_planes_to_phi(const Dims &dm, const Buffers &b, hipStream_t s) {
+  if (!b.phi16 || !b.phi) return hipErrorInvalidValue;
+  const int64_t tiles = ((dm.max_n + 63) / 64) * ((dm.max_T + 63) / 64);
+  hipLaunchKernelGGL(k_planes_to_phi, dim3(unsigned(tiles), unsigned(dm.H)), dim3(256), 0, s, b.desc, b.phi16, b.phi);
+  return hipGetLastError();
+}
+
 hipError_t launch_vt(const Dims &dm, const Buffers &b, hipStream_t s) {
   if (!b.vt || !dm.in_bf16) return hipErrorInvalidValue;
   dim3 grid(unsigned((dm.max_T + 63) / 64), unsigned(dm.H));

@@ -1611,7 +1611,42 @@ __global__ __launch_bounds__(256) void k_resid(const HeadDesc *__restrict__ desc
   }
 }
 
+// Trace: the relative mass residual ||r|| / ||m|| of each head after the
+// cycle's refit (the last cycle's entry after the polish refits), from
+// k_resid's per-block sums in a fixed order.
+__global__ __launch_bounds__(64) void k_relres(const HeadDesc *__restrict__ desc, int cycle, int kR, int polish,
+                                               int nrb, const double *__restrict__ rpart,
+                                               double *__restrict__ tr_relres) {
+  const int h = blockIdx.x;
+  const HeadDesc D = desc[h];
+  int64_t cyc;
+  if (polish) {
+    cyc = (D.t + kR - 1) / kR - 1;
+  } else {
+    int64_t S0;
+    if (cycle_keys(D, cycle, kR, &S0) == 0) return;
+    cyc = cycle;
+  }
+  double r2 = 0.0, m2 = 0.0;
+  for (int k = threadIdx.x; k < nrb; k += 64) {
+    r2 += rpart[(int64_t(h) * nrb + k) * 2];
+    m2 += rpart[(int64_t(h) * nrb + k) * 2 + 1];
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    r2 += __shfl_xor(r2, o);
+    m2 += __shfl_xor(m2, o);
+  }
+  if (threadIdx.x == 0) tr_relres[D.cyc_off + cyc] = m2 > 0.0 ? sqrt(r2 / m2) : 0.0;
+}
+
 }  // namespace
+
+hipError_t launch_relres(const Dims &dm, const Buffers &b, int cycle, int kR, int polish, hipStream_t s) {
+  if (!b.tr_relres || !b.rpart) return hipSuccess;
+  hipLaunchKernelGGL(k_relres, dim3(unsigned(dm.H)), dim3(64), 0, s, b.desc, cycle, kR, polish, int(dm.nrb), b.rpart,
+                     b.tr_relres);
+  return hipGetLastError();
+}
 
 hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int kR, int gated, hipStream_t s) {
   hipLaunchKernelGGL(k_sweep, dim3(unsigned(dm.max_cblk), unsigned(dm.H)), dim3(256), 0, s, b.desc, b.phi16, b.r,

@@ -182,10 +182,13 @@ typedef struct {
  *                                  stored)
  *   swept_keys8 int32 [sum c_h]    keys whose columns of the 8-bit copy of Phi the cycle's
  *                                  second pruning stage read (0 where it did not run)
+ *   relres     double [sum c_h]    relative mass residual ||m - Phi_S w|| / ||m|| after the
+ *                                  cycle's refit (float64 residual; the last cycle's entry
+ *                                  after the polish refits)
  * where a "cycle" is the R iterations between two refits; head h has
  * c_h = ceil(t_h / (k R)) cycles (amc_cycle_offsets). */
 typedef struct {
-  uint64_t shift, pick, pick_score, weight, runner_up, nnls_iters, swept_keys, swept_keys8;
+  uint64_t shift, pick, pick_score, weight, runner_up, nnls_iters, swept_keys, swept_keys8, relres;
   uint64_t total_bytes;
 } amc_trace_layout;
 

@@ -119,6 +119,32 @@ def fresh_tokens(seed, centres: np.ndarray, n_q: int, n_kv: int, outliers: bool,
     return store_round(Q, dtype), store_round(K, dtype), store_round(V, dtype)
 
 
+def digit_variant_head(seed, n: int, T: int, d: int, kind: str) -> Head:
+    """A bf16 head whose rows exercise the exact-digit logit kernel's cases.
+
+    kind "z2": every entry within a factor 2 of its row's largest (its two low
+    base-256 digits are zero); "z1" / "z0": magnitudes log-uniform over 2^-15
+    / 2^-24 of the largest (one / no low digit zero); "offgrid": as "z1" with
+    one query entry 2^-40 below its row's largest (off the 38-bit digit grid,
+    so the head takes the float64 logit kernel).  Values are plain random
+    draws, bf16-rounded.
+    """
+    rng = np.random.default_rng(seed)
+    span = {"z2": 1.0, "z1": 15.0, "z0": 24.0, "offgrid": 15.0}[kind]
+
+    def rows(m):
+        mag = np.exp2(-rng.uniform(0.0, span, size=(m, d)))
+        mag[:, 0] = 1.0  # each row's largest
+        x = rng.choice([-1.0, 1.0], size=(m, d)) * mag * 1.5
+        return x
+
+    Q, K, V = rows(n), rows(T) * 0.25, rng.normal(0.0, 1.0, size=(T, d))
+    if kind == "offgrid":
+        Q[n // 2, 3] = 1.5 * 2.0 ** -40
+    Qb, Kb, Vb = store_round(Q, "bf16"), store_round(K, "bf16"), store_round(V, "bf16")
+    return Head(Qb, Kb, Vb, np.zeros((1, d)), False)
+
+
 def random_beta(seed, T: int, scale: float = 1.0) -> np.ndarray:
     """A float32-representable per-key bias, for re-compaction inputs."""
     rng = np.random.default_rng(seed)

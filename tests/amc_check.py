@@ -46,6 +46,8 @@ FALLBACK_SHARE = 0.25  # largest share of a test's heads held to the minimum val
 LD_MAX_T = 512  # largest budget the extended-precision envelope is computed for
 NULL_SV = 1e-10  # relative singular value below which columns count as dependent
 
+REPORTS = []  # every replay report of the session (summarised at its end by conftest)
+
 
 def to_device(x: np.ndarray, dtype: str, device="cuda") -> torch.Tensor:
     if dtype == "bf16":
@@ -107,6 +109,15 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
     res_r = float(np.linalg.norm(m - P @ w_ref))
     rep["resid_excess"] = (res_g - res_r) / max(res_r, 1e-300)
     rep["rel_resid"] = res_r / float(np.linalg.norm(m))
+    # the trace's relative residual after the last refit is that of the GPU's
+    # own weights (float64 residuals on both sides; cancellation leaves about
+    # 1e-16 / relres of relative difference)
+    rep["relres_ok"] = True
+    if "relres" in trace and len(trace["relres"][h]):
+        rg = float(trace["relres"][h][-1])
+        want = res_g / float(np.linalg.norm(m))
+        rep["relres_gpu"] = rg
+        rep["relres_ok"] = abs(rg - want) <= 1e-6 * want + 1e-13
     e_gpu = oracle.errors(Q, K, V, Ck, beta, Cv, beta_in)
     e_ref = oracle.errors(Q, K, V, ref.Ck, ref.beta, ref.Cv, beta_in)
     rep["e_gpu"], rep["e_ref"] = e_gpu, e_ref
@@ -138,7 +149,9 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
             rep["fallback"] = True
             weights_ok = rep["resid_excess"] <= RESID_REL
     rep["ok"] = (not rep["mismatch_iters"] and rep["same_set"] and rep["ck_exact"] and weights_ok and
-                 rep["e_mass_diff"] <= ERR_TOL and rep["e_out_diff"] <= ERR_TOL)
+                 rep["e_mass_diff"] <= ERR_TOL and rep["e_out_diff"] <= ERR_TOL and rep["relres_ok"])
+    rep["t"] = int(t)
+    REPORTS.append(rep)
     return rep
 
 

@@ -56,6 +56,41 @@ def test_mass_features(dtype, d, ns, Ts, with_beta):
         assert np.max(np.abs(yy - f.Y)) < 2e-5 * max(1.0, np.max(np.abs(f.Y)))
 
 
+@pytest.mark.parametrize("d", [128, 64])
+def test_mass_features_digit_kernel_elementwise(d):
+    """bf16 mass features come from the selection's own kernels (exact
+    base-256 digit logits on the int8 matrix units, the float64 kernel for a
+    head off the digit grid): Phi, m and Y element by element against the
+    oracle, for rows with two, one and no zero low digits, an off-grid head,
+    ragged query and key tiles and a per-key bias."""
+    kinds = ["z2", "z1", "z0", "offgrid"]
+    shapes = [(77, 200), (130, 64), (16, 333), (65, 129)]
+    heads = [synth.digit_variant_head([24, d, i], n, T, d, k) for i, (k, (n, T)) in enumerate(zip(kinds, shapes))]
+    betas = [synth.random_beta([25, i], T, 1.0) for i, (_, T) in enumerate(shapes)]
+    _say(f"digit-kernel mass features d={d} kinds={kinds} shapes={shapes}")
+    Q, K, V, cu_q, cu_k = pack_heads(heads, "bf16")
+    beta = torch.from_numpy(np.concatenate(betas).astype(np.float32)).cuda()
+    shift, phi, m, Y, hs = amc.mass_features(Q, K, V, cu_q=cu_q, cu_k=cu_k, beta_in=beta)
+    shift, phi, m, Y = shift.cpu().numpy(), phi.cpu().numpy(), m.cpu().numpy(), Y.cpu().numpy()
+    assert np.all(hs.cpu().numpy() == 0)
+    po = 0
+    for i, h in enumerate(heads):
+        n, T = h.Q.shape[0], h.K.shape[0]
+        f = oracle.mass_features(h.Q, h.K, h.V, betas[i], shift=shift[i])
+        L = oracle.logits(h.Q, h.K, betas[i])
+        assert abs(shift[i] - L.max()) <= 1e-3 * abs(L.max()) + 1e-3
+        ph = phi[po: po + n * T].reshape(n, T)
+        po += n * T
+        rel = np.max(np.abs(ph - f.Phi) / np.maximum(f.Phi, 1e-30))
+        mm = m[cu_q[i]: cu_q[i + 1]]
+        yy = Y[cu_q[i]: cu_q[i + 1]]
+        _say(f"{kinds[i]} n={n} T={T}: Phi rel {rel:.2e}, m rel {np.max(np.abs(mm - f.m) / f.m):.2e}, "
+             f"Y abs {np.max(np.abs(yy - f.Y)):.2e}")
+        assert np.all(np.abs(ph - f.Phi) <= 2e-7 * f.Phi + 1e-37)
+        assert np.max(np.abs(mm - f.m) / f.m) < 1e-12
+        assert np.max(np.abs(yy - f.Y)) < 2e-5 * max(1.0, np.max(np.abs(f.Y)))
+
+
 # ----------------------------------------------------------------------------
 # NNLS on given Gram systems
 # ----------------------------------------------------------------------------
