@@ -20,7 +20,7 @@ LIB_PATH = os.path.join(_HERE, "libamc.so")
 
 AMC_OK, AMC_ERR_INVALID_ARG, AMC_ERR_UNSUPPORTED, AMC_ERR_WORKSPACE, AMC_ERR_HIP = 0, 1, 2, 3, 4
 AMC_F32, AMC_BF16 = 0, 1
-AMC_SEL_OMP, AMC_SEL_OMP_BATCHED = 0, 1
+AMC_SEL_OMP, AMC_SEL_OMP_BATCHED, AMC_SEL_HIGHEST = 0, 1, 2
 AMC_FLAG_TRACE = 1
 HS_CHOL_JITTER, HS_NNLS_CAP, HS_NONFINITE, HS_NNLS_SINGULAR, HS_NNLS_QR = 1, 2, 4, 8, 16
 EXACT_REFIT = {"auto": 0, "gated": 1, "never": 2}
@@ -32,7 +32,7 @@ EXPORTED = [
     "amc_default_options", "amc_workspace_size", "amc_output_offsets", "amc_cycle_offsets",
     "amc_trace_layout_for", "amc_compact", "amc_mass_features", "amc_mass_features_workspace", "amc_nnls",
     "amc_timer_create", "amc_timer_reset", "amc_timer_read", "amc_timer_destroy", "amc_status_string",
-    "amc_version", "amc_compact_noalloc", "amc_noalloc_max_workspace",
+    "amc_version", "amc_compact_noalloc", "amc_noalloc_max_workspace", "amc_greedy_swap_budgets",
 ]
 
 
@@ -105,6 +105,7 @@ def lib() -> ctypes.CDLL:
     L.amc_mass_features.argtypes = [P, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, u64, vp]
     L.amc_mass_features_workspace.argtypes = [P, ctypes.POINTER(u64)]
     L.amc_nnls.argtypes = [i32, ctypes.POINTER(i64), vp, vp, vp, i32, i32, i32, dbl, vp, vp, vp]
+    L.amc_greedy_swap_budgets.argtypes = [i32, i32, vp, i64, i64, ctypes.POINTER(i64), ctypes.POINTER(i64)]
     L.amc_timer_create.argtypes = [ctypes.POINTER(vp)]
     L.amc_timer_reset.argtypes = [vp]
     L.amc_timer_read.argtypes = [vp, i32, ctypes.POINTER(i64), ctypes.POINTER(dbl)]
@@ -115,6 +116,7 @@ def lib() -> ctypes.CDLL:
     L.amc_version.restype = ctypes.c_int
     for name in ("amc_workspace_size", "amc_output_offsets", "amc_cycle_offsets", "amc_trace_layout_for",
                  "amc_compact", "amc_compact_noalloc", "amc_mass_features", "amc_mass_features_workspace", "amc_nnls",
+                 "amc_greedy_swap_budgets",
                  "amc_timer_create", "amc_timer_reset", "amc_timer_read"):
         getattr(L, name).restype = ctypes.c_int
     _lib = L
@@ -192,7 +194,7 @@ def make_options(select: str = "omp", topk: int = 1, refit_every: int = 1, nnls_
                  head_groups: int = 0, exact_refit: str = "auto", digits_in_panel: bool = True) -> Options:
     o = Options()
     lib().amc_default_options(ctypes.byref(o))
-    o.select = {"omp": AMC_SEL_OMP, "batched": AMC_SEL_OMP_BATCHED}[select]
+    o.select = {"omp": AMC_SEL_OMP, "batched": AMC_SEL_OMP_BATCHED, "highest": AMC_SEL_HIGHEST}[select]
     o.topk = int(topk)
     o.refit_every = int(refit_every)
     o.nnls_polish = int(nnls_polish)
@@ -413,6 +415,108 @@ def compact(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, *, cu_q=
 def noalloc_max_workspace() -> int:
     """Bytes of the static per-GPU workspace of amc_compact_noalloc."""
     return int(lib().amc_noalloc_max_workspace())
+
+
+def chunk_split(T: int, t: int, chunk_keys: int) -> List[tuple]:
+    """The chunks [c L, min((c+1) L, T)) of L = chunk_keys keys and their
+    budgets: t shared in proportion to the chunks' lengths by largest
+    remainders (ties to the earlier chunk), each at least 1 and at most its
+    length.  Returns [(k0, k1, t_c)]."""
+    if not (1 <= t <= T) or chunk_keys < 1:
+        raise ValueError("need 1 <= t <= T and chunk_keys >= 1")
+    bounds = [(k0, min(k0 + chunk_keys, T)) for k0 in range(0, T, chunk_keys)]
+    if t < len(bounds):
+        raise ValueError("budget below one key per chunk")
+    # exact rational quotas t * len / T as integer floor and remainder
+    floors = [t * (k1 - k0) // T for k0, k1 in bounds]
+    rems = [t * (k1 - k0) % T for k0, k1 in bounds]
+    tc = [max(1, min(k1 - k0, f)) for (k0, k1), f in zip(bounds, floors)]
+    left = t - sum(tc)
+    order = sorted(range(len(bounds)), key=lambda c: (-rems[c], c))
+    while left != 0:
+        moved = False
+        for c in order:
+            k0, k1 = bounds[c]
+            if left > 0 and tc[c] < k1 - k0:
+                tc[c] += 1
+                left -= 1
+                moved = True
+            elif left < 0 and tc[c] > 1:
+                tc[c] -= 1
+                left += 1
+                moved = True
+            if left == 0:
+                break
+        if not moved:
+            raise ValueError("no feasible split")
+    return [(k0, k1, c) for (k0, k1), c in zip(bounds, tc)]
+
+
+@dataclass
+class ChunkedResult:
+    """amc_compact over the chunks of every head (each chunk a head of its own),
+    in each head's output range.  sel_idx counts keys within the original head."""
+    result: CompactResult  # per chunk-head outputs and trace
+    split: List[List[tuple]]  # per original head: (k0, k1, t_c) of each chunk
+    cu_budgets: List[int]
+    sel_idx: torch.Tensor
+
+    def head(self, h: int):
+        a, b = self.cu_budgets[h], self.cu_budgets[h + 1]
+        r = self.result
+        return r.Ck[a:b], r.beta[a:b], r.Cv[a:b], self.sel_idx[a:b]
+
+    def chunk_head(self, h: int, c: int) -> int:
+        """Index of head h's chunk c among the chunk-heads of the call."""
+        return sum(len(s) for s in self.split[:h]) + c
+
+
+def compact_chunked(Q: torch.Tensor, K: torch.Tensor, V: torch.Tensor, budgets, chunk_keys: int, *, cu_q=None,
+                    cu_k=None, beta_in: Optional[torch.Tensor] = None, **kw) -> ChunkedResult:
+    """KV-based chunked compaction (xinfinite.net article, section 3, chunked
+    compression; zhichai.net deep-dive, section 4.3): every head's keys are cut
+    into chunks of chunk_keys consecutive keys, each chunk is compacted as a
+    head of its own against the head's reference queries (budget shared by
+    chunk_split), and the compacted chunks stay in key order in the head's
+    output range.  One amc_compact call: the chunks' keys, values and bias
+    are the caller's rows as they are; each chunk-head gets its own copy of
+    the head's query rows.  Other arguments as for compact()."""
+    Qp, cq = _as_packed(Q, cu_q, "Q")
+    Kp, ck = _as_packed(K, cu_k, "K")
+    Vp, _ = _as_packed(V, cu_k, "V")
+    H = len(cq) - 1
+    tb = [int(budgets)] * H if isinstance(budgets, int) else [int(b) for b in budgets]
+    split, rows, cq2, ck2, b2, off = [], [], [0], [0], [], []
+    for h in range(H):
+        sp = chunk_split(ck[h + 1] - ck[h], tb[h], chunk_keys)
+        split.append(sp)
+        n = cq[h + 1] - cq[h]
+        for k0, k1, tc in sp:
+            rows.append(torch.arange(cq[h], cq[h + 1], device=Qp.device))
+            cq2.append(cq2[-1] + n)
+            ck2.append(ck[h] + k1)
+            b2.append(tc)
+            off.extend([k0] * tc)
+    Q2 = Qp.index_select(0, torch.cat(rows)).contiguous()
+    res = compact(Q2, Kp, Vp, b2, cu_q=cq2, cu_k=ck2, beta_in=beta_in, **kw)
+    sel = res.sel_idx + torch.tensor(off, dtype=torch.int32, device=res.sel_idx.device)
+    cub = [0]
+    for b in tb:
+        cub.append(cub[-1] + b)
+    return ChunkedResult(res, split, cub, sel)
+
+
+def greedy_swap_budgets(loss, unit: int, total: int):
+    """amc_greedy_swap_budgets: per-head budgets (keys) from sensitivity curves
+    loss[h][j] (head h keeping (j+1) * unit keys) summing to total; returns
+    (budgets, moves)."""
+    L = np.ascontiguousarray(np.asarray(loss, dtype=np.float64))
+    H, J = L.shape
+    out = (ctypes.c_int64 * H)()
+    mv = ctypes.c_int64(0)
+    _check(lib().amc_greedy_swap_budgets(H, J, L.ctypes.data_as(ctypes.c_void_p), int(unit), int(total), out,
+                                         ctypes.byref(mv)), "amc_greedy_swap_budgets")
+    return [int(x) for x in out], int(mv.value)
 
 
 def compact_workspace_bytes(cu_q, cu_k, budgets, head_dim: int, dtype: torch.dtype = torch.bfloat16,

@@ -62,6 +62,7 @@ struct Plan {
   int kR = 1;
   int64_t max_cycles = 0, sum_t = 0, sum_cycles = 0, sum_n = 0, sum_T = 0;
   bool store_phi = true;
+  bool highest = false;  // AM-Highest selection: one cycle with every key of each head
   // byte offsets in the workspace
   uint64_t o_desc = 0, o_shift_part = 0, o_shift = 0, o_phi = 0, o_m = 0, o_r = 0, o_mhat = 0,
            o_Y = 0, o_sel_slot = 0, o_sel_list = 0, o_panel = 0, o_G = 0, o_bvec = 0, o_w = 0,
@@ -70,7 +71,7 @@ struct Plan {
            o_cand_lidx = 0, o_cand_cnt = 0, o_band_list = 0, o_band_cnt = 0, o_exact = 0, o_stage = 0,
            o_part = 0, o_vt = 0, o_qdig = 0, o_kdig = 0, o_qexp = 0, o_ktab = 0, o_f64h = 0, o_colsum = 0, o_rpn = 0, o_rabs = 0,
            o_surv = 0, o_survcnt = 0, o_pruneL = 0, o_q8 = 0, o_q8bad = 0, o_surv2 = 0, o_surv2cnt = 0,
-           o_qrflag = 0, o_qrbuilt = 0, o_qrbuf = 0, o_rpart = 0, total = 0;
+           o_qrflag = 0, o_qrbuilt = 0, o_qrbuf = 0, o_rpart = 0, o_score = 0, total = 0;
   bool exact_path = false;  // some head may take the orthogonal-factorisation refit
   bool store_q8 = false;  // the 8-bit plane of the second pruning stage fits the budget too
   bool alias_digits = false;  // digit rows and value tiles lie in the panel (recompute mode)
@@ -103,9 +104,11 @@ static amc_status check_problem(const amc_problem *p) {
 
 static amc_status check_options(const amc_options *o) {
   if (!o) return AMC_ERR_INVALID_ARG;
-  if (o->select != AMC_SEL_OMP && o->select != AMC_SEL_OMP_BATCHED) return AMC_ERR_INVALID_ARG;
+  if (o->select != AMC_SEL_OMP && o->select != AMC_SEL_OMP_BATCHED && o->select != AMC_SEL_HIGHEST)
+    return AMC_ERR_INVALID_ARG;
   if (o->topk < 1 || o->refit_every < 1) return AMC_ERR_INVALID_ARG;
-  if (o->select == AMC_SEL_OMP && (o->topk != 1 || o->refit_every != 1)) return AMC_ERR_INVALID_ARG;
+  if ((o->select == AMC_SEL_OMP || o->select == AMC_SEL_HIGHEST) && (o->topk != 1 || o->refit_every != 1))
+    return AMC_ERR_INVALID_ARG;
   if (int64_t(o->topk) * o->refit_every > kMaxCycle) return AMC_ERR_UNSUPPORTED;
   if (o->nnls_max_iters < 0 || o->nnls_polish < 0 || o->nnls_polish > 8) return AMC_ERR_INVALID_ARG;
   if (o->head_groups < 0 || o->head_groups > 16) return AMC_ERR_INVALID_ARG;
@@ -129,6 +132,13 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   const int H = p->num_heads;
   const int d = p->head_dim;
   pl.kR = features_only ? 1 : o->topk * o->refit_every;
+  pl.highest = !features_only && o->select == AMC_SEL_HIGHEST;
+  if (pl.highest) {
+    // one cycle per head takes all of its keys
+    int64_t tmax = 1;
+    for (int h = 0; h < p->num_heads; ++h) tmax = std::max<int64_t>(tmax, p->budgets[h]);
+    pl.kR = int(std::min<int64_t>(tmax, kMaxBudget));
+  }
   Dims &dm = pl.dm;
   dm.H = H;
   dm.d = d;
@@ -261,6 +271,7 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
   pl.o_gA = take(8ull * tt);
   pl.o_nnvec = dm.max_t > kNnlsLdsT ? take(8ull * kNnlsVecPerSlot * tt) : 0;
   pl.o_rpart = take(16ull * H * dm.nrb);
+  if (pl.highest) pl.o_score = take(8ull * TT);  // every key's AM-Highest score
   if (pl.exact_path) {
     pl.o_qrflag = take(4ull * H);
     pl.o_qrbuilt = take(4ull * H);
@@ -505,7 +516,8 @@ amc_status amc_cycle_offsets(const amc_problem *p, const amc_options *o, int64_t
   if (st != AMC_OK) return st;
   const int64_t kR = int64_t(o->topk) * o->refit_every;
   cu_cycles[0] = 0;
-  for (int h = 0; h < p->num_heads; ++h) cu_cycles[h + 1] = cu_cycles[h] + ceil_div(p->budgets[h], kR);
+  for (int h = 0; h < p->num_heads; ++h)
+    cu_cycles[h + 1] = cu_cycles[h] + (o->select == AMC_SEL_HIGHEST ? 1 : ceil_div(p->budgets[h], kR));
   return AMC_OK;
 }
 
@@ -620,6 +632,7 @@ static amc_status compact_impl(const amc_problem *p, const amc_options *o, const
   }
   b.head_status = head_status;
   b.rpart = reinterpret_cast<double *>(ws + pl.o_rpart);
+  b.score_all = pl.highest ? reinterpret_cast<double *>(ws + pl.o_score) : nullptr;
   if (pl.exact_path) {
     b.qr_flag = reinterpret_cast<int32_t *>(ws + pl.o_qrflag);
     b.qr_built = reinterpret_cast<int32_t *>(ws + pl.o_qrbuilt);
@@ -724,7 +737,17 @@ static amc_status compact_impl(const amc_problem *p, const amc_options *o, const
         for (int g2 = 0; g2 < ngroups; ++g2)
           if (g2 != g && hipStreamWaitEvent(stream, ev_pre[size_t(g2)], 0) != hipSuccess) return AMC_ERR_HIP;
       for (int c = 0; c < cycles; ++c) {
-        if (pl.store_phi) {
+        if (pl.highest) {
+          // one sweep scores every key by its attention summed over the
+          // queries (r = 1 / m), then each head's top t are the picks
+          Buffers bh = bg;
+          bh.r = bg.mhat;  // 1 / m (r itself stays m, the Gram solver's gradient)
+          AMC_LAUNCH(AMC_K_SWEEP, launch_recip(dg, bg, stream));
+          if (pl.store_phi) AMC_LAUNCH(AMC_K_SWEEP_EXACT, launch_sweep(dg, bh, c, pl.kR, 0, stream));
+          else AMC_LAUNCH(AMC_K_SWEEP, launch_sweep_rc(dg, bh, c, pl.kR, stream));
+          AMC_LAUNCH(AMC_K_MERGE, launch_topt(dg, bg, stream));
+          AMC_LAUNCH(AMC_K_PANEL, launch_panel(dg, bg, c, pl.kR, 0, stream));
+        } else if (pl.store_phi) {
           // bounded sweep and float64 rescoring of the band; the heads whose
           // band overflowed take the float32 sweep, merge and panel
           // (after the first cycle, with the 8-bit plane, a second pruning stage
@@ -873,6 +896,57 @@ amc_status amc_mass_features(const amc_problem *p, const void *Q, const void *K,
   }
   AMC_LAUNCH(AMC_K_SHIFT, launch_shift(pl.dm, b, stream));
   AMC_LAUNCH(AMC_K_PHI, launch_phi(pl.dm, b, phi != nullptr, stream));
+  return AMC_OK;
+}
+
+amc_status amc_greedy_swap_budgets(int32_t num_heads, int32_t steps, const double *loss, int64_t unit,
+                                   int64_t total, int64_t *budgets, int64_t *swaps) {
+  if (num_heads < 1 || steps < 1 || !loss || !budgets || unit < 1) return AMC_ERR_INVALID_ARG;
+  const int64_t H = num_heads, J = steps;
+  if (total % unit != 0) return AMC_ERR_INVALID_ARG;
+  const int64_t units = total / unit;
+  if (units < H || units > H * J) return AMC_ERR_INVALID_ARG;
+  for (int64_t e = 0; e < H * J; ++e)
+    if (!std::isfinite(loss[e])) return AMC_ERR_INVALID_ARG;
+  // u[h]: head h's units, 1..J; loss at u units is loss[h][u - 1]
+  std::vector<int64_t> u(size_t(H), units / H);
+  for (int64_t h = 0; h < units % H; ++h) ++u[size_t(h)];
+  int64_t moves = 0;
+  for (;;) {
+    // the most valuable unit to receive, and the cheapest one to give up
+    // among the other heads
+    int64_t donor = -1, recv = -1;
+    double cost = 0.0, gain = 0.0;
+    for (int64_t h = 0; h < H; ++h) {
+      const double *lh = loss + h * J;
+      const int64_t k = u[size_t(h)];
+      if (k < J) {
+        const double g = lh[k - 1] - lh[k];  // fall of the loss with one unit more
+        if (recv < 0 || g > gain) {
+          recv = h;
+          gain = g;
+        }
+      }
+    }
+    if (recv < 0) break;
+    for (int64_t h = 0; h < H; ++h) {
+      const int64_t k = u[size_t(h)];
+      if (h == recv || k <= 1) continue;
+      const double *lh = loss + h * J;
+      const double c = lh[k - 2] - lh[k - 1];  // rise of the loss with one unit less
+      if (donor < 0 || c < cost) {
+        donor = h;
+        cost = c;
+      }
+    }
+    if (donor < 0 || !(gain > cost)) break;
+    --u[size_t(donor)];
+    ++u[size_t(recv)];
+    ++moves;
+    if (moves > H * J * J) break;  // cannot happen while each move lowers the sum; a guard only
+  }
+  for (int64_t h = 0; h < H; ++h) budgets[h] = u[size_t(h)] * unit;
+  if (swaps) *swaps = moves;
   return AMC_OK;
 }
 

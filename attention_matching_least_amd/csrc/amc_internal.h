@@ -153,6 +153,7 @@ struct Buffers {
   int32_t *qr_built;   // [H] slots of the head's orthogonal factorisation that are current
   double *qrbuf;       // per head at qr_off: the exact refit's factorisation and work triangles
   double *rpart;       // [H][nrb][2] per 256-query block: sum r^2 and sum m^2 of the last residual
+  double *score_all;   // [sum T] AM-Highest: every key's score from the sweep (null otherwise)
   // trace (all null when tracing is off)
   double *tr_shift, *tr_pick_score, *tr_weight, *tr_runner;
   int32_t *tr_pick, *tr_iters, *tr_swept, *tr_swept8;
@@ -216,6 +217,11 @@ hipError_t launch_nnls(const Dims &dm, const Buffers &b, int cycle, int cyc_keys
 hipError_t launch_nnls_global(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish,
                               const NnlsParams &np, hipStream_t s);
 hipError_t launch_resid(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);
+// AM-Highest: 1 / m into b.mhat (the sweep, given it as r, then scores sum_i Phi_ij / m_i
+// into b.score_all), and
+// the top t of those scores per head (ties to the lower key) as the cycle's picks
+hipError_t launch_recip(const Dims &dm, const Buffers &b, hipStream_t s);
+hipError_t launch_topt(const Dims &dm, const Buffers &b, hipStream_t s);
 // trace only (no-op without it): relative mass residual of each head after the refit
 hipError_t launch_relres(const Dims &dm, const Buffers &b, int cycle, int cyc_keys, int polish, hipStream_t s);
 hipError_t launch_ols_normal(const Dims &dm, const Buffers &b, hipStream_t s);

@@ -121,7 +121,8 @@ __global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc
                                                const double *__restrict__ r, const int32_t *__restrict__ sel_slot,
                                                int cycle, int kR, const int32_t *__restrict__ gate,
                                                double *__restrict__ cand_val,
-                                               int32_t *__restrict__ cand_idx, int32_t *__restrict__ head_status) {
+                                               int32_t *__restrict__ cand_idx, int32_t *__restrict__ head_status,
+                                               double *__restrict__ score_all) {
   __shared__ double s_r[kStoredMaxN];
   __shared__ double sv[256];
   __shared__ int si[256];
@@ -180,6 +181,7 @@ __global__ __launch_bounds__(256) void k_sweep(const HeadDesc *__restrict__ desc
     if (head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
     c = -DBL_MAX;  // still a valid, selectable key
   }
+  if (score_all && col < D.T) score_all[D.k_off + col] = c;
   sv[tid] = c;
   si[tid] = idx;
   __syncthreads();
@@ -247,7 +249,7 @@ __global__ __launch_bounds__(RC_THREADS) void k_sweep_rc(
     const HeadDesc *__restrict__ desc, const void *__restrict__ Qv, const void *__restrict__ Kv,
     const float *__restrict__ beta_in, double scale, const double *__restrict__ shift, const double *__restrict__ r,
     const int32_t *__restrict__ sel_slot, int cycle, int kR, double *__restrict__ cand_val,
-    int32_t *__restrict__ cand_idx, int32_t *__restrict__ head_status) {
+    int32_t *__restrict__ cand_idx, int32_t *__restrict__ head_status, double *__restrict__ score_all) {
   using E = typename std::conditional<BF16, uint16_t, float>::type;
   constexpr int NS = D / 4;    // MFMA k-steps over the head dimension
   constexpr int QT = 64;       // queries per LDS stage
@@ -355,12 +357,13 @@ __global__ __launch_bounds__(RC_THREADS) void k_sweep_rc(
       if (head_status) atomicOr(head_status + h, int32_t(AMC_HS_NONFINITE));
       c = -DBL_MAX;  // still a valid, selectable key
     }
+    if (score_all && col < Dh.T) score_all[Dh.k_off + col] = c;
     sv[tid] = c;
     si[tid] = idx;
   }
   __syncthreads();
   block_sort256(sv, si);
-  if (tid <= Kc) {
+  if (tid <= Kc && tid < 256) {
     const int64_t o = (Dh.cblk_off + blk) * KP_STRIDE + tid;
     cand_val[o] = sv[tid];
     cand_idx[o] = si[tid];
@@ -1611,6 +1614,106 @@ __global__ __launch_bounds__(256) void k_resid(const HeadDesc *__restrict__ desc
   }
 }
 
+// AM-Highest: 1 / m into the m-hat buffer (unused until the first residual),
+// which the sweep then takes as its r: r^T Phi[:, j] is key j's attention
+// summed over the queries.
+__global__ __launch_bounds__(256) void k_recip(const HeadDesc *__restrict__ desc, const double *__restrict__ m,
+                                               double *__restrict__ r) {
+  const HeadDesc D = desc[blockIdx.y];
+  const int64_t i = int64_t(blockIdx.x) * 256 + threadIdx.x;
+  if (i >= D.n) return;
+  const double mi = m[D.n_off + i];
+  r[D.n_off + i] = mi > 0.0 ? 1.0 / mi : 0.0;
+}
+
+// AM-Highest: each head's t largest scores (ties to the lower key) become
+// its picks, in ascending key order: radix selection of the t-th largest
+// order key (8 passes of 8 bits), then one pass that takes every key above it
+// and the first keys equal to it.  The trace gets the picks, their scores and
+// the best score left out.
+__global__ __launch_bounds__(1024) void k_topt(const HeadDesc *__restrict__ desc,
+                                               const double *__restrict__ score_all,
+                                               int32_t *__restrict__ sel_slot, int32_t *__restrict__ sel_list,
+                                               int32_t *__restrict__ tr_pick, double *__restrict__ tr_pick_score,
+                                               double *__restrict__ tr_runner) {
+  __shared__ int hist[256];
+  __shared__ int s_wt[16], s_we[16];
+  __shared__ double s_wmax[16];
+  __shared__ uint64_t s_prefix;
+  __shared__ int s_need;
+  const int h = blockIdx.x;
+  const HeadDesc D = desc[h];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t T = D.T;
+  const double *sc = score_all + D.k_off;
+  if (tid == 0) {
+    s_prefix = 0;
+    s_need = int(D.t);
+  }
+  for (int pass = 0; pass < 8; ++pass) {
+    const int shift = 56 - 8 * pass;
+    if (tid < 256) hist[tid] = 0;
+    __syncthreads();
+    const uint64_t prefix = s_prefix;
+    const uint64_t pmask = pass == 0 ? 0ull : (~0ull << (shift + 8));
+    for (int64_t e = tid; e < T; e += 1024) {
+      const uint64_t k = order_key(sc[e]);
+      if ((k & pmask) == prefix) atomicAdd(&hist[int((k >> shift) & 255u)], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int need = s_need, dg = 255;
+      for (; dg > 0; --dg) {
+        if (hist[dg] >= need) break;
+        need -= hist[dg];
+      }
+      s_need = need;
+      s_prefix = prefix | (uint64_t(dg) << shift);
+    }
+    __syncthreads();
+  }
+  const uint64_t kL = s_prefix;
+  const int need = s_need;  // keys equal to the t-th largest that are taken
+  int taken = 0, eq_seen = 0;
+  double runner = -INFINITY;
+  for (int64_t e0 = 0; e0 < T; e0 += 1024) {
+    const int64_t e = e0 + tid;
+    const bool valid = e < T;
+    const double v = valid ? sc[e] : -INFINITY;
+    const uint64_t k = valid ? order_key(v) : 0ull;
+    const bool gt = valid && k > kL, eq = valid && k == kL;
+    const uint64_t me = __ballot(eq);
+    if (lane == 0) s_we[wave] = __popcll(me);
+    __syncthreads();
+    int eq_rank = eq_seen;
+    for (int w = 0; w < wave; ++w) eq_rank += s_we[w];
+    eq_rank += __popcll(me & ((uint64_t(1) << lane) - 1));
+    const bool take = gt || (eq && eq_rank < need);
+    const uint64_t mt = __ballot(take);
+    if (lane == 0) s_wt[wave] = __popcll(mt);
+    double best = (valid && !take) ? v : -INFINITY;
+    for (int o = 32; o > 0; o >>= 1) best = fmax(best, __shfl_xor(best, o));
+    if (lane == 0) s_wmax[wave] = best;
+    __syncthreads();
+    int at = taken;
+    for (int w = 0; w < wave; ++w) at += s_wt[w];
+    at += __popcll(mt & ((uint64_t(1) << lane) - 1));
+    if (take && at < D.t) {
+      sel_list[D.t_off + at] = int32_t(e);
+      sel_slot[D.k_off + e] = at + 1;
+      if (tr_pick) tr_pick[D.t_off + at] = int32_t(e);
+      if (tr_pick_score) tr_pick_score[D.t_off + at] = v;
+    }
+    for (int w = 0; w < 16; ++w) {
+      taken += s_wt[w];
+      eq_seen += s_we[w];
+      runner = fmax(runner, s_wmax[w]);
+    }
+    __syncthreads();
+  }
+  if (tid == 0 && tr_runner) tr_runner[D.cyc_off] = runner;
+}
+
 // Trace: the relative mass residual ||r|| / ||m|| of each head after the
 // cycle's refit (the last cycle's entry after the polish refits), from
 // k_resid's per-block sums in a fixed order.
@@ -1641,6 +1744,19 @@ __global__ __launch_bounds__(64) void k_relres(const HeadDesc *__restrict__ desc
 
 }  // namespace
 
+hipError_t launch_recip(const Dims &dm, const Buffers &b, hipStream_t s) {
+  hipLaunchKernelGGL(k_recip, dim3(unsigned((dm.max_n + 255) / 256), unsigned(dm.H)), dim3(256), 0, s, b.desc, b.m,
+                     b.mhat);
+  return hipGetLastError();
+}
+
+hipError_t launch_topt(const Dims &dm, const Buffers &b, hipStream_t s) {
+  if (!b.score_all) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_topt, dim3(unsigned(dm.H)), dim3(1024), 0, s, b.desc, b.score_all, b.sel_slot, b.sel_list,
+                     b.tr_pick, b.tr_pick_score, b.tr_runner);
+  return hipGetLastError();
+}
+
 hipError_t launch_relres(const Dims &dm, const Buffers &b, int cycle, int kR, int polish, hipStream_t s) {
   if (!b.tr_relres || !b.rpart) return hipSuccess;
   hipLaunchKernelGGL(k_relres, dim3(unsigned(dm.H)), dim3(64), 0, s, b.desc, cycle, kR, polish, int(dm.nrb), b.rpart,
@@ -1650,14 +1766,15 @@ hipError_t launch_relres(const Dims &dm, const Buffers &b, int cycle, int kR, in
 
 hipError_t launch_sweep(const Dims &dm, const Buffers &b, int cycle, int kR, int gated, hipStream_t s) {
   hipLaunchKernelGGL(k_sweep, dim3(unsigned(dm.max_cblk), unsigned(dm.H)), dim3(256), 0, s, b.desc, b.phi16, b.r,
-                     b.sel_slot, cycle, kR, gated ? b.exact : nullptr, b.cand_val, b.cand_idx, b.head_status);
+                     b.sel_slot, cycle, kR, gated ? b.exact : nullptr, b.cand_val, b.cand_idx, b.head_status,
+                     b.score_all);
   return hipGetLastError();
 }
 
 hipError_t launch_sweep_rc(const Dims &dm, const Buffers &b, int cycle, int kR, hipStream_t s) {
   dim3 grid(unsigned(dm.max_cblk), unsigned(dm.H));
 #define AMC_RC_ARGS b.desc, b.Q, b.K, b.beta_in, dm.scale, b.shift, b.r, b.sel_slot, cycle, kR, b.cand_val, b.cand_idx, \
-    b.head_status
+    b.head_status, b.score_all
   if (dm.d == 128) {
     if (dm.in_bf16) hipLaunchKernelGGL((k_sweep_rc<128, true>), grid, dim3(RC_THREADS), 0, s, AMC_RC_ARGS);
     else hipLaunchKernelGGL((k_sweep_rc<128, false>), grid, dim3(RC_THREADS), 0, s, AMC_RC_ARGS);

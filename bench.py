@@ -387,6 +387,7 @@ def main():
     ap.add_argument("--exact-refit", default="auto", choices=["auto", "gated", "never"],
                     help="NNLS refits through the orthogonal factorisation: every head it takes, heads the "
                          "Gram solver flags, none")
+    ap.add_argument("--no-highest", action="store_true", help="leave out the AM-Highest line")
     ap.add_argument("--no-timer", action="store_true", help="skip the kernel pass (per-kernel events, roofline)")
     ap.add_argument("--head-groups", type=int, default=0,
                     help="head groups (streams) of the timed steps; 0: the library's choice")
@@ -534,6 +535,28 @@ def main():
         if len(found) > 1:
             roofline_other = found[1][1]
 
+    highest = None
+    if not args.no_highest:
+        # AM-Highest on the same resident inputs (one scoring sweep, top t, one
+        # refit, the value fit): the method family's fast member, beside the metric
+        ws_h = amc.compact_workspace_bytes(cu_q, cu_k, w.budgets, w.d, tdt, select="highest")
+        if ws_h + 256 > workspace.numel():
+            workspace = torch.empty(ws_h + 256, dtype=torch.uint8, device=dev)
+        kh = dict(cu_q=cu_q, cu_k=cu_k, select="highest", exact_refit=args.exact_refit)
+        for _ in range(args.warmup):
+            amc.compact(Q, K, V, w.budgets, workspace=workspace, head_groups=args.head_groups, **kh)
+        torch.cuda.synchronize()
+        th = time.perf_counter()
+        for _ in range(args.steps):
+            hres = amc.compact(Q, K, V, w.budgets, workspace=workspace, head_groups=args.head_groups, **kh)
+        torch.cuda.synchronize()
+        hsec = time.perf_counter() - th
+        hstat = hres.head_status.cpu().numpy()
+        highest = {"select": "AM-Highest", "value": round(H * args.steps / hsec, 2), "unit": "heads/s",
+                   "ms_per_step": round(1000.0 * hsec / args.steps, 3),
+                   "heads_exact_refit": int(np.count_nonzero(hstat & 16))}
+        del hres
+
     cpu = cpu_baseline(args.workload, args.cpu_sample) if args.cpu_sample > 0 else None
     long_ctx = None
     if long_flat is not None:
@@ -572,6 +595,7 @@ def main():
         "heads_exact_refit": int(np.count_nonzero(status & 16)),
         "input_generation_s": round(gen_s, 1),
         "long_context": long_ctx,
+        "highest": highest,
     }
     print(json.dumps(out), flush=True)
 

@@ -69,8 +69,14 @@ typedef enum {
 typedef enum { AMC_F32 = 0, AMC_BF16 = 1 } amc_dtype;
 
 typedef enum {
-  AMC_SEL_OMP = 0,        /* one key per iteration, NNLS refit after each */
-  AMC_SEL_OMP_BATCHED = 1 /* top-k keys per iteration, refit every R iterations */
+  AMC_SEL_OMP = 0,         /* one key per iteration, NNLS refit after each */
+  AMC_SEL_OMP_BATCHED = 1, /* top-k keys per iteration, refit every R iterations */
+  AMC_SEL_HIGHEST = 2      /* AM-Highest: the t keys with the largest attention summed over the
+                            * reference queries, sum_i Phi_ij / m_i (ties to the lower index),
+                            * then one NNLS refit and the value fit (zhichai.net English summary,
+                            * "Method Family and Trade-offs"; youleyou.com, the highest-attention
+                            * keys method).  topk and refit_every must be 1; one cycle per head.
+                            * The picks are recorded in ascending key order. */
 } amc_select;
 
 /* head_status bits */
@@ -283,6 +289,28 @@ amc_status amc_mass_features_workspace(const amc_problem *p, uint64_t *bytes);
 amc_status amc_nnls(int32_t num, const int64_t *cu_t, const double *G, const double *g, double *w,
                     int32_t warm, int32_t pg_iters, int32_t max_iters, double tol, int32_t *iters,
                     int32_t *status, void *stream);
+
+/* Non-uniform per-head budgets by greedy swaps (zhichai.net deep-dive, section
+ * 4.2: sensitivity curves rank the heads once, a greedy-swap algorithm gives
+ * each head its own compression; xinfinite.net article, section 4, Fig. 3 and
+ * 4).  Host only; no device work.
+ *   loss     HOST double [H][J]: head h's sensitivity (e.g. its reconstruction
+ *            loss) when it keeps (j + 1) * unit keys, j = 0..J-1
+ *   unit     keys per budget step (>= 1)
+ *   total    the budgets' sum, a multiple of unit with H * unit <= total <= H * J * unit
+ *   budgets  HOST int64 [H] out
+ *   swaps    HOST int64 out, nullable: the unit moves made
+ * Every head starts with total / (H unit) units, the remainder one unit each
+ * to the lowest heads; then, while it lowers the summed loss, one unit moves
+ * to the head whose loss falls most by receiving it from the other head whose
+ * loss rises least by giving it up (ties to the lower head), a head keeping
+ * between 1 and J units.  With curves that fall by less at each further step
+ * (the usual shape) no single move then improves the sum, which makes it the
+ * minimum.  Errors:
+ * AMC_ERR_INVALID_ARG for a null pointer, non-finite loss or a total out of
+ * range. */
+amc_status amc_greedy_swap_budgets(int32_t num_heads, int32_t steps, const double *loss, int64_t unit,
+                                   int64_t total, int64_t *budgets, int64_t *swaps);
 
 /* Kernel timer: HIP events recorded around every launch of an amc_compact
  * call whose options carry the handle.  Reading synchronises on the events. */

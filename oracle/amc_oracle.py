@@ -211,6 +211,7 @@ def _qr_r(M):
 # counts as dependent on the free set.
 COS_TOL = 1e-10
 DEP_TOL = 1e-12
+KKT_ACCEPT = 1e-8  # largest relative KKT violation of scipy's Lawson-Hanson result kept by nnls_exact
 
 
 def nnls_qr(PhiS, m, w0=None, max_outer=None, dtype=np.float64):
@@ -320,7 +321,14 @@ def nnls_exact(PhiS, m, w_prev=None):
     """
     t = PhiS.shape[1]
     if t <= 256:
-        return nnls_lawson_hanson(PhiS, m)
+        # scipy's result is kept only where it meets the optimality conditions:
+        # on a rank-deficient system (fewer queries than keys) it can stop
+        # short of the minimiser, and nnls_qr then solves it
+        w = nnls_lawson_hanson(PhiS, m)
+        A = np.asarray(PhiS, dtype=np.float64)
+        if nnls_kkt_violation(A.T @ A, A.T @ np.asarray(m, dtype=np.float64), w) <= KKT_ACCEPT:
+            return w
+        return nnls_qr(PhiS, m)
     w0 = None
     if w_prev is not None:
         w0 = np.zeros(t)
@@ -477,6 +485,56 @@ def omp_select(Phi, m, t, k=1, R=1, replay: Optional[Sequence[Sequence[int]]] = 
     return Selection(S, w, r, steps)
 
 
+def highest_scores(Phi, m):
+    """AM-Highest key scores (p3 "Method Family and Trade-offs": highest-
+    attention key selection; p4, the highest-attention-keys method): each
+    key's attention summed over the reference queries, sum_i Phi_ij / m_i
+    (row i of Phi divided by its mass is query i's softmax over the keys)."""
+    Phi = np.asarray(Phi, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    return (Phi / m[:, None]).sum(axis=0)
+
+
+def highest_select(Phi, m, t, given=None, margin_tol: float = 1e-6) -> Selection:
+    """AM-Highest: the t keys with the largest highest_scores (ties to the
+    lower index), then one exact NNLS refit of their weights.
+
+    ``given``: another implementation's key set.  Where a key it leaves out
+    scores above a key it takes by more than ``margin_tol`` of the top score
+    the step is a mismatch; the oracle then continues with the given set (so
+    the weights and values that follow are compared on the same keys)."""
+    c = highest_scores(Phi, m)
+    T = c.shape[0]
+    if not (1 <= t <= T):
+        raise ValueError("budget must satisfy 1 <= t <= T")
+    order = _rank(c)
+    picks = [int(j) for j in order[:t]]
+    top = float(c[order[0]])
+    runner = float(c[order[t]]) if t < T else NEG_INF
+    last = float(c[order[t - 1]])
+    margin = np.inf if runner == NEG_INF else ((last - runner) / abs(top) if top != 0.0 else 0.0)
+    st = Step(1, picks, [float(c[j]) for j in picks], runner, top, margin, True)
+    if given is not None:
+        g = [int(j) for j in given]
+        if len(g) != t or len(set(g)) != t:
+            raise ValueError("given: invalid key set")
+        out = np.ones(T, dtype=bool)
+        out[g] = False
+        thr = margin_tol * abs(top)
+        c_in_min = min(float(c[j]) for j in g)
+        if np.any(c[out] - c_in_min > thr):
+            st.mismatch = True
+        elif set(g) != set(picks):
+            st.forced = True
+        picks = g
+        st.picks = g
+        st.scores = [float(c[j]) for j in g]
+    S = picks
+    w = nnls_exact(np.asarray(Phi, dtype=np.float64)[:, S], m)
+    r = np.asarray(m, dtype=np.float64) - np.asarray(Phi, dtype=np.float64)[:, S] @ w
+    return Selection(S, w, r, [st])
+
+
 # ----------------------------------------------------------------------------
 # OLS value fit
 # ----------------------------------------------------------------------------
@@ -529,13 +587,18 @@ def score_tie_ulps(Q, K, t, beta_in=None, scale=None):
 
 
 def compact(Q, K, V, t, k=1, R=1, beta_in=None, scale=None, shift=None, replay=None,
-            margin_tol=1e-6) -> Compaction:
+            margin_tol=1e-6, select: str = "omp") -> Compaction:
     """Compact one head's (K, V) to t keys: C_k (a subset of K), per-key bias
-    beta and fitted values C_v (p2 section 2; p3 pipeline)."""
+    beta and fitted values C_v (p2 section 2; p3 pipeline).  select: "omp"
+    (greedy OMP, plain or batched by k and R) or "highest" (AM-Highest; k, R
+    unused; ``replay`` is then the other implementation's key set)."""
     K = np.asarray(K, dtype=np.float64)
     feats = mass_features(Q, K, V, beta_in, scale, shift)
-    tie = score_tie_ulps(Q, K, t, beta_in, scale) if replay is not None else 0.0
-    sel = omp_select(feats.Phi, feats.m, t, k, R, replay, margin_tol, tie)
+    if select == "highest":
+        sel = highest_select(feats.Phi, feats.m, t, replay, margin_tol)
+    else:
+        tie = score_tie_ulps(Q, K, t, beta_in, scale) if replay is not None else 0.0
+        sel = omp_select(feats.Phi, feats.m, t, k, R, replay, margin_tol, tie)
     S = np.asarray(sel.S, dtype=np.int64)
     Cv = ols_values(feats.Phi[:, S], sel.w, feats.Y)
     beta = log_weights(sel.w)
@@ -543,6 +606,107 @@ def compact(Q, K, V, t, k=1, R=1, beta_in=None, scale=None, shift=None, replay=N
         beta = beta + np.asarray(beta_in, dtype=np.float64)[S]
     order = np.argsort(S, kind="stable")
     return Compaction(S[order], K[S[order]], beta[order], Cv[order], sel.w[order], sel, feats)
+
+
+def chunk_budgets(T: int, t: int, chunk_keys: int):
+    """KV-based chunked compaction's split (p2 section 3, chunked compression:
+    the prefilled KV is sliced into consecutive chunks, each compacted on its
+    own; p1 section 4.3): chunks [c L, min((c+1) L, T)) of L = chunk_keys keys,
+    and budget t shared in proportion to the chunks' lengths by largest
+    remainders (ties to the earlier chunk), each at least 1 and at most its
+    length.  Returns [(k0, k1, t_c)]."""
+    if not (1 <= t <= T) or chunk_keys < 1:
+        raise ValueError("need 1 <= t <= T and chunk_keys >= 1")
+    bounds = [(k0, min(k0 + chunk_keys, T)) for k0 in range(0, T, chunk_keys)]
+    if t < len(bounds):
+        raise ValueError("budget below one key per chunk")
+    quota = [t * (k1 - k0) / T for k0, k1 in bounds]
+    base = [max(1, min(k1 - k0, int(np.floor(q)))) for (k0, k1), q in zip(bounds, quota)]
+    left = t - sum(base)
+    order = sorted(range(len(bounds)), key=lambda c: (-(quota[c] - np.floor(quota[c])), c))
+    while left != 0:
+        moved = False
+        for c in order:
+            k0, k1 = bounds[c]
+            if left > 0 and base[c] < k1 - k0:
+                base[c] += 1
+                left -= 1
+                moved = True
+            elif left < 0 and base[c] > 1:
+                base[c] -= 1
+                left += 1
+                moved = True
+            if left == 0:
+                break
+        if not moved:
+            raise ValueError("no feasible split")
+    return [(k0, k1, tc) for (k0, k1), tc in zip(bounds, base)]
+
+
+@dataclass
+class ChunkedCompaction:
+    sel_idx: np.ndarray  # (t,) ascending original indices
+    Ck: np.ndarray
+    beta: np.ndarray
+    Cv: np.ndarray
+    chunks: List[Compaction]  # per chunk, indices within the chunk
+    split: List[tuple]  # (k0, k1, t_c)
+
+
+def compact_chunked(Q, K, V, t, chunk_keys, k=1, R=1, beta_in=None, scale=None, select: str = "omp",
+                    replay=None, margin_tol=1e-6) -> ChunkedCompaction:
+    """KV-based chunked compaction: each chunk of chunk_keys consecutive keys
+    compacted against the same reference queries (its own shift, features and
+    fits), the compacted chunks concatenated in key order.  By the mixing
+    identity (p1 section 1.3) attention over the concatenation combines the
+    chunks' outputs by their masses, so each chunk matching its own output and
+    mass makes the concatenation match the whole block's.  ``replay``: per
+    chunk, what ``compact`` takes."""
+    K = np.asarray(K, dtype=np.float64)
+    V = np.asarray(V, dtype=np.float64)
+    split = chunk_budgets(K.shape[0], t, chunk_keys)
+    parts = []
+    for c, (k0, k1, tc) in enumerate(split):
+        bi = None if beta_in is None else np.asarray(beta_in, dtype=np.float64)[k0:k1]
+        parts.append(compact(Q, K[k0:k1], V[k0:k1], tc, k, R, beta_in=bi, scale=scale, select=select,
+                             replay=None if replay is None else replay[c], margin_tol=margin_tol))
+    sel = np.concatenate([p.sel_idx + k0 for p, (k0, _, _) in zip(parts, split)])
+    return ChunkedCompaction(sel, np.concatenate([p.Ck for p in parts]), np.concatenate([p.beta for p in parts]),
+                             np.concatenate([p.Cv for p in parts]), parts, split)
+
+
+def greedy_swap_budgets(loss, unit: int, total: int):
+    """Non-uniform head budgets by greedy swaps (p1 section 4.2; p2 section 4,
+    Fig. 3 and 4): loss[h][j] is head h's sensitivity when it keeps (j+1)
+    units of ``unit`` keys.  Every head starts even (the remainder one unit to
+    each of the lowest heads); then, while a move lowers the summed loss, one
+    unit goes to the head whose loss falls most by gaining it, from the other
+    head whose loss rises least by losing it (ties to the lower head).
+    Returns (budgets in keys, moves)."""
+    L = np.asarray(loss, dtype=np.float64)
+    H, J = L.shape
+    if total % unit:
+        raise ValueError("total must be a multiple of unit")
+    units = total // unit
+    if not (H <= units <= H * J):
+        raise ValueError("total out of range")
+    u = [units // H + (1 if h < units % H else 0) for h in range(H)]
+    moves = 0
+    while True:
+        gains = [(L[h, u[h] - 1] - L[h, u[h]], h) for h in range(H) if u[h] < J]
+        if not gains:
+            break
+        gain, r = max(gains, key=lambda x: (x[0], -x[1]))
+        costs = [(L[h, u[h] - 2] - L[h, u[h] - 1], h) for h in range(H) if h != r and u[h] > 1]
+        if not costs:
+            break
+        cost, d = min(costs, key=lambda x: (x[0], x[1]))
+        if not gain > cost:
+            break
+        u[d] -= 1
+        u[r] += 1
+        moves += 1
+    return [x * unit for x in u], moves
 
 
 # ----------------------------------------------------------------------------

@@ -145,6 +145,18 @@ def digit_variant_head(seed, n: int, T: int, d: int, kind: str) -> Head:
     return Head(Qb, Kb, Vb, np.zeros((1, d)), False)
 
 
+def sensitivity_curves(seed, num_heads: int, steps: int) -> np.ndarray:
+    """Synthetic per-head sensitivity curves for the budget schedule (real ones
+    need a model): loss_h(j) = a_h exp(-(j+1) / s_h), j = 0..steps-1, a
+    decreasing convex curve per head with a log-normal level a_h and a decay
+    length s_h uniform in [1, steps / 2]: some heads need many keys, others few."""
+    rng = np.random.default_rng(seed)
+    a = np.exp(rng.normal(0.0, 1.0, size=num_heads))
+    sc = rng.uniform(1.0, max(1.0, steps / 2), size=num_heads)
+    j = np.arange(1, steps + 1)
+    return a[:, None] * np.exp(-j[None, :] / sc[:, None])
+
+
 def random_beta(seed, T: int, scale: float = 1.0) -> np.ndarray:
     """A float32-representable per-key bias, for re-compaction inputs."""
     rng = np.random.default_rng(seed)

@@ -73,18 +73,24 @@ def head_outputs(res, h: int):
             Cv.float().cpu().numpy().astype(np.float64), sel.cpu().numpy().astype(np.int64))
 
 
-def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, trace=None):
+def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, trace=None, select: str = "omp"):
     """Compares head h of a libamc result (run with trace=True) with the
-    oracle.  Returns a report dict; ``report['ok']`` is the verdict."""
+    oracle.  Returns a report dict; ``report['ok']`` is the verdict.
+    select "highest": AM-Highest (k, R unused); the oracle checks the GPU's
+    key set against its own scores under the same margin rule."""
     if trace is None:
         trace = res.trace()
     picks_order = [int(j) for j in trace["pick"][h]]
-    sizes = O.iteration_sizes(t, k, R)
-    per_it, pos = [], 0
-    for kk, _ in sizes:
-        per_it.append(picks_order[pos: pos + kk])
-        pos += kk
-    ref = oracle.compact(Q, K, V, t, k, R, beta_in=beta_in, replay=per_it, margin_tol=MARGIN_TOL)
+    if select == "highest":
+        ref = oracle.compact(Q, K, V, t, beta_in=beta_in, replay=picks_order, margin_tol=MARGIN_TOL,
+                             select="highest")
+    else:
+        sizes = O.iteration_sizes(t, k, R)
+        per_it, pos = [], 0
+        for kk, _ in sizes:
+            per_it.append(picks_order[pos: pos + kk])
+            pos += kk
+        ref = oracle.compact(Q, K, V, t, k, R, beta_in=beta_in, replay=per_it, margin_tol=MARGIN_TOL)
     Ck, beta, Cv, sel = head_outputs(res, h)
     rep = {"mismatch_iters": [s.it for s in ref.selection.steps if s.mismatch],
            "forced_iters": [s.it for s in ref.selection.steps if s.forced],
@@ -136,7 +142,8 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
         Pu = P[:, U]
         nrm = np.linalg.norm(Pu, axis=0)
         sv = np.linalg.svd(Pu / np.where(nrm > 0, nrm, 1.0), compute_uv=False) if Pu.shape[1] else np.ones(1)
-        rep["union_sv_min"] = float(sv[-1] / sv[0])
+        # more columns than queries: dependent whatever the singular values say
+        rep["union_sv_min"] = float(sv[-1] / sv[0]) if Pu.shape[1] <= Pu.shape[0] else 0.0
         env = None
         if len(w_ref) <= LD_MAX_T:
             w_ld = O.nnls_qr(P, m, w0=w_ref, dtype=np.longdouble)

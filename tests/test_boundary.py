@@ -165,3 +165,23 @@ def test_nnls_entry_validation():
 def test_status_strings():
     for s in range(5):
         assert amc.status_string(s)
+
+
+def test_greedy_swap_budgets_matches_the_oracle():
+    """The library's schedule (host code) equals the oracle's on seeded convex curves."""
+    import oracle
+    import synth
+    import numpy as np
+    for seed, H, J in [(540, 288, 40), (541, 8, 12), (542, 33, 5)]:
+        L = synth.sensitivity_curves(seed, H, J)
+        for units in (H, (H * J) // 3, H * J):
+            got = amc.greedy_swap_budgets(L, 16, units * 16)
+            want = oracle.greedy_swap_budgets(L, 16, units * 16)
+            assert got == (want[0], want[1])
+    L = synth.sensitivity_curves(543, 4, 5)
+    out = (ctypes.c_int64 * 4)()
+    Lc = np.ascontiguousarray(L)
+    assert amc.lib().amc_greedy_swap_budgets(4, 5, Lc.ctypes.data_as(ctypes.c_void_p), 16, 17, out, None) \
+        == amc.AMC_ERR_INVALID_ARG
+    assert amc.lib().amc_greedy_swap_budgets(4, 5, Lc.ctypes.data_as(ctypes.c_void_p), 16, 16 * 21, out, None) \
+        == amc.AMC_ERR_INVALID_ARG

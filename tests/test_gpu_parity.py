@@ -10,6 +10,7 @@ import synth
 from attention_matching_least_amd import amc
 from oracle import amc_oracle as O
 
+import amc_check
 from amc_check import assert_fallback_share, head_outputs, pack_heads, replay_check, to_device
 
 pytestmark = pytest.mark.gpu
@@ -175,6 +176,89 @@ def test_compact_varlen_ragged(k, R):
     tr = res.trace()
     for i, h in enumerate(heads):
         _assert_ok(replay_check(h.Q, h.K, h.V, budgets[i], k, R, res, i, beta_in=betas[i], trace=tr), f"head{i}")
+
+
+@pytest.mark.parametrize("recompute", [False, True])
+def test_highest_selection(recompute):
+    """AM-Highest: the top-t keys by attention summed over the queries, one
+    NNLS refit and the value fit, against the oracle (stored Phi and the
+    recompute sweep; ragged heads, a key bias, budgets up to 600)."""
+    shapes = [(300, 700, 40), (129, 257, 23), (200, 1000, 64), (520, 1100, 300), (1024, 4096, 600)]
+    heads = [synth.make_head([35, i], n, T, 128, True, "bf16") for i, (n, T, _) in enumerate(shapes)]
+    budgets = [t for _, _, t in shapes]
+    betas = [synth.random_beta([36, i], T, 1.0) for i, (_, T, _) in enumerate(shapes)]
+    _say(f"highest recompute={recompute} shapes={shapes}")
+    kw = dict(phi_budget_bytes=0) if recompute else {}
+    Q, K, V, cu_q, cu_k = pack_heads(heads, "bf16")
+    bt = torch.from_numpy(np.concatenate(betas).astype(np.float32)).cuda()
+    res = amc.compact(Q, K, V, budgets, cu_q=cu_q, cu_k=cu_k, beta_in=bt, select="highest", trace=True, **kw)
+    torch.cuda.synchronize()
+    hs = res.head_status.cpu().numpy()
+    _say(f"head status {hs}")
+    assert np.all(hs & (amc.HS_NNLS_CAP | amc.HS_NONFINITE) == 0), hs
+    tr = res.trace()
+    assert all(len(tr["relres"][i]) == 1 for i in range(len(heads)))
+    reps = []
+    for i, h in enumerate(heads):
+        assert list(tr["pick"][i]) == sorted(tr["pick"][i])
+        rep = replay_check(h.Q, h.K, h.V, budgets[i], 1, 1, res, i, beta_in=betas[i], trace=tr, select="highest")
+        reps.append(rep)
+        _assert_ok(rep, f"head{i}")
+    assert_fallback_share(reps)
+
+
+def test_chunked_compaction():
+    """KV-based chunked compaction: every chunk replayed against the oracle
+    as a head of its own, and each head's concatenation (keys in order, exact
+    rows) with the errors of the oracle's own chunked compaction."""
+    shapes = [(300, 1000, 60), (200, 700, 45), (150, 290, 30)]
+    chunk = 300
+    heads = [synth.make_head([37, i], n, T, 128, True, "bf16") for i, (n, T, _) in enumerate(shapes)]
+    budgets = [t for _, _, t in shapes]
+    betas = [synth.random_beta([38, i], T, 1.0) for i, (_, T, _) in enumerate(shapes)]
+    _say(f"chunked compaction chunk={chunk} shapes={shapes}")
+    Q, K, V, cu_q, cu_k = pack_heads(heads, "bf16")
+    bt = torch.from_numpy(np.concatenate(betas).astype(np.float32)).cuda()
+    res = amc.compact_chunked(Q, K, V, budgets, chunk, cu_q=cu_q, cu_k=cu_k, beta_in=bt, select="batched", topk=4,
+                              refit_every=2, trace=True)
+    torch.cuda.synchronize()
+    tr = res.result.trace()
+    reps = []
+    for i, h in enumerate(heads):
+        for c, (k0, k1, tc) in enumerate(res.split[i]):
+            ch = res.chunk_head(i, c)
+            rep = replay_check(h.Q, h.K[k0:k1], h.V[k0:k1], tc, 4, 2, res.result, ch, beta_in=betas[i][k0:k1],
+                               trace=tr)
+            reps.append(rep)
+            _assert_ok(rep, f"head{i} chunk{c} [{k0},{k1}) t={tc}")
+        Ck, beta, Cv, sel = head_outputs(res, i)
+        assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < h.K.shape[0]
+        assert np.array_equal(Ck, np.asarray(h.K, dtype=np.float64)[sel])
+        ref = oracle.compact_chunked(h.Q, h.K, h.V, budgets[i], chunk, 4, 2, beta_in=betas[i])
+        e_gpu = oracle.errors(h.Q, h.K, h.V, Ck, beta, Cv, betas[i])
+        e_ref = oracle.errors(h.Q, h.K, h.V, ref.Ck, ref.beta, ref.Cv, betas[i])
+        _say(f"head{i} concatenated: e_gpu {e_gpu} e_ref {e_ref}")
+        assert abs(e_gpu[0] - e_ref[0]) <= 1e-3 and abs(e_gpu[1] - e_ref[1]) <= 1e-3
+    assert_fallback_share(reps)
+
+
+@pytest.mark.xfail(strict=True, reason="the Gram-form NNLS (budgets above 640) settles on a neighbouring active set: "
+                   "beta off by about 6 at a residual within 3e-10 of the minimum; beta is determined to 8e-4 "
+                   "by the float64 data (cond(Phi_F D^-1) 7e4), so this is a solver departure, not a tie")
+def test_gram_path_beta_above_640_keys():
+    """The limit of the Gram-form refit: one AM-Highest head of 700 keys from
+    4096 (1024 queries), held to the beta rule."""
+    h = synth.make_head([35, 4], 1024, 4096, 128, True, "bf16")
+    beta = synth.random_beta([36, 4], 4096, 1.0)
+    Q, K, V, cu_q, cu_k = pack_heads([h], "bf16")
+    bt = torch.from_numpy(beta.astype(np.float32)).cuda()
+    res = amc.compact(Q, K, V, [700], cu_q=cu_q, cu_k=cu_k, beta_in=bt, select="highest", trace=True)
+    torch.cuda.synchronize()
+    assert int(res.head_status[0]) & amc.HS_NNLS_QR == 0  # the Gram form ran
+    rep = replay_check(h.Q, h.K, h.V, 700, 1, 1, res, 0, beta_in=beta, select="highest")
+    amc_check.REPORTS.remove(rep)  # a recorded limitation, not parity evidence: out of the session summary
+    _say(f"700-key Gram head: {rep}")
+    assert rep["ok"] and not rep["fallback"]
 
 
 @pytest.mark.parametrize("k,R", [(1, 1), (4, 2)])

@@ -149,6 +149,23 @@ def test_fnnls_matches_lawson_hanson(t):
         assert np.allclose(w_f[big], w_lh[big], rtol=1e-5)
 
 
+def test_fnnls_at_large_budget_well_conditioned():
+    """fnnls at t = 300 on a well-conditioned system (independent Gaussian
+    columns): KKT, and the minimiser of scipy's Lawson-Hanson."""
+    rng = np.random.default_rng(301)
+    n, t = 900, 300
+    A = rng.normal(size=(n, t))
+    y = A @ (np.abs(rng.normal(size=t)) * (rng.random(t) > 0.4)) + 0.3 * rng.normal(size=n)
+    G, b = A.T @ A, A.T @ y
+    w_f = oracle.fnnls(G, b)
+    w_lh = oracle.nnls_lawson_hanson(A, y)
+    assert O.nnls_kkt_violation(G, b, w_f) < 1e-8
+    assert np.linalg.norm(A @ (w_f - w_lh)) <= 1e-9 * np.linalg.norm(y)
+    assert np.array_equal(w_f > 0, w_lh > 0)
+    big = w_lh > 1e-6 * w_lh.max()
+    assert np.allclose(w_f[big], w_lh[big], rtol=1e-8)
+
+
 def test_fnnls_warm_start_same_minimiser():
     rng = np.random.default_rng(7)
     A = _phi_like(rng, 200, 50)
@@ -627,3 +644,189 @@ def test_planted_stale_residual_breaks_brute_force(monkeypatch):
         f = oracle.mass_features(h.Q, h.K, h.V)
         differs += O.omp_select(f.Phi, f.m, 2).S != S
     assert differs > 0
+
+
+# ----------------------------------------------------------------------------
+# AM-Highest (p3 "Method Family and Trade-offs"; p4, highest-attention keys)
+# ----------------------------------------------------------------------------
+def _softmax_scores_by_loops(Q, K, bias, scale):
+    """Each key's attention summed over the queries, one query's softmax at a time."""
+    n, T = Q.shape[0], K.shape[0]
+    score = [0.0] * T
+    for i in range(n):
+        logits = []
+        for j in range(T):
+            dot = 0.0
+            for c in range(Q.shape[1]):
+                dot += float(Q[i, c]) * float(K[j, c])
+            logits.append(scale * dot + (0.0 if bias is None else float(bias[j])))
+        mx = max(logits)
+        ex = [math.exp(v - mx) for v in logits]
+        tot = sum(ex)
+        for j in range(T):
+            score[j] += ex[j] / tot
+    return np.array(score)
+
+
+def test_highest_matches_brute_force_softmax():
+    rng = np.random.default_rng(410)
+    for trial in range(40):
+        n, T, d = int(rng.integers(1, 6)), int(rng.integers(3, 10)), 4
+        t = int(rng.integers(1, T + 1))
+        Q, K = rng.normal(size=(n, d)), rng.normal(size=(T, d)) * 1.5
+        bias = rng.normal(size=T) if trial % 2 else None
+        V = rng.normal(size=(T, 3))
+        ref = _softmax_scores_by_loops(Q, K, bias, 0.5)
+        f = oracle.mass_features(Q, K, V, bias, 0.5)
+        assert np.allclose(oracle.highest_scores(f.Phi, f.m), ref, rtol=1e-12, atol=1e-15)
+        want = sorted(range(T), key=lambda j: (-ref[j], j))[:t]
+        sel = oracle.highest_select(f.Phi, f.m, t)
+        assert sorted(sel.S) == sorted(want)
+        G, b = f.Phi[:, sel.S].T @ f.Phi[:, sel.S], f.Phi[:, sel.S].T @ f.m
+        assert O.nnls_kkt_violation(G, b, sel.w) < 1e-9
+
+
+def test_highest_scores_ignore_per_query_scale():
+    """Dividing row i by its mass makes each query's scale irrelevant: any
+    positive per-query factor (a per-query shift) leaves the scores."""
+    rng = np.random.default_rng(411)
+    Phi = np.exp(rng.normal(size=(30, 50)))
+    m = Phi.sum(axis=1)
+    D = np.exp(rng.normal(size=30) * 5.0)
+    assert np.allclose(oracle.highest_scores(Phi * D[:, None], m * D), oracle.highest_scores(Phi, m), rtol=1e-13)
+
+
+def test_planted_unnormalised_highest_is_caught():
+    """Raw column sums of Phi (no division by the query's mass) rank the keys
+    by the loudest query; the brute-force softmax pin rejects that."""
+    Q = np.array([[4.0, 0.0], [0.0, 0.3], [0.0, 0.3]])
+    K = np.array([[1.0, 0.0], [0.0, 1.0], [0.0, 0.9], [0.2, 0.2]])
+    ref = _softmax_scores_by_loops(Q, K, None, 1.0)
+    f = oracle.mass_features(Q, K, np.zeros((4, 1)), None, 1.0)
+    raw = f.Phi.sum(axis=0)
+    want = sorted(range(4), key=lambda j: (-ref[j], j))[:2]
+    planted = sorted(range(4), key=lambda j: (-raw[j], j))[:2]
+    assert sorted(oracle.highest_select(f.Phi, f.m, 2).S) == sorted(want)
+    assert sorted(planted) != sorted(want)
+
+
+def test_highest_replay_rule():
+    rng = np.random.default_rng(412)
+    Phi = np.exp(rng.normal(size=(40, 30)))
+    m = Phi.sum(axis=1)
+    sel = oracle.highest_select(Phi, m, 8)
+    same = oracle.highest_select(Phi, m, 8, given=list(reversed(sel.S)))
+    assert not same.steps[0].mismatch
+    c = oracle.highest_scores(Phi, m)
+    order = np.argsort(-c, kind="stable")
+    swapped = [int(j) for j in order[:7]] + [int(order[-1])]  # the worst key instead of the 8th
+    bad = oracle.highest_select(Phi, m, 8, given=swapped)
+    assert bad.steps[0].mismatch
+
+
+def test_nnls_exact_on_a_system_scipy_leaves_short():
+    """Two queries, three keys (rank 2): scipy's Lawson-Hanson stops at a
+    residual of 0.03336 with a nonzero gradient on a free variable; the
+    minimiser (0.03185) is what nnls_exact returns."""
+    rng = np.random.default_rng(410)
+    for trial in range(17):
+        n, T, d = int(rng.integers(1, 6)), int(rng.integers(3, 10)), 4
+        t = int(rng.integers(1, T + 1))
+        Q, K = rng.normal(size=(n, d)), rng.normal(size=(T, d)) * 1.5
+        bias = rng.normal(size=T) if trial % 2 else None
+        V = rng.normal(size=(T, 3))
+    assert (n, T, t) == (2, 6, 3)
+    f = oracle.mass_features(Q, K, V, bias, 0.5)
+    A = f.Phi[:, oracle.highest_select(f.Phi, f.m, t).S]
+    w_sp = oracle.nnls_lawson_hanson(A, f.m)
+    w = oracle.nnls_exact(A, f.m)
+    assert O.nnls_kkt_violation(A.T @ A, A.T @ f.m, w_sp) > 1e-4
+    assert O.nnls_kkt_violation(A.T @ A, A.T @ f.m, w) < 1e-12
+    assert np.linalg.norm(A @ w - f.m) < np.linalg.norm(A @ w_sp - f.m) - 1e-3
+
+
+# ----------------------------------------------------------------------------
+# KV-based chunked compaction (p2 section 3; p1 section 4.3)
+# ----------------------------------------------------------------------------
+def test_chunk_budgets_split():
+    for T, t, L in [(1000, 100, 300), (60000, 6000, 8192), (10, 10, 3), (257, 23, 64), (7, 4, 2)]:
+        split = oracle.chunk_budgets(T, t, L)
+        assert split[0][0] == 0 and split[-1][1] == T
+        assert all(a[1] == b[0] for a, b in zip(split, split[1:]))
+        assert sum(tc for _, _, tc in split) == t
+        for k0, k1, tc in split:
+            assert 1 <= tc <= k1 - k0
+            assert abs(tc - t * (k1 - k0) / T) < 1.0 + 1e-9 or tc == 1
+    # largest remainders: 3 chunks of 3, 3, 1 keys sharing 5 -> quotas 2.14, 2.14, 0.71
+    assert [tc for _, _, tc in oracle.chunk_budgets(7, 5, 3)] == [2, 2, 1]
+    with pytest.raises(ValueError):
+        oracle.chunk_budgets(7, 3, 2)  # four chunks, three keys
+
+
+def test_chunked_full_budget_is_identity():
+    """Every chunk at full budget reproduces the block exactly, so the
+    concatenation does: offsets and order are right."""
+    rng = np.random.default_rng(520)
+    Q, K, V = rng.normal(size=(12, 8)), rng.normal(size=(20, 8)), rng.normal(size=(20, 5))
+    bias = rng.normal(size=20)
+    ch = oracle.compact_chunked(Q, K, V, 20, 7, beta_in=bias)
+    assert np.array_equal(ch.sel_idx, np.arange(20))
+    e_mass, e_out = oracle.errors(Q, K, V, ch.Ck, ch.beta, ch.Cv, bias)
+    assert e_mass < 1e-12 and e_out < 1e-12
+
+
+def test_chunked_concatenation_follows_the_mixing_identity():
+    """Attention over the concatenated compacted chunks equals the chunks'
+    own attention outputs combined by their masses."""
+    rng = np.random.default_rng(521)
+    Q, K, V = rng.normal(size=(30, 8)), rng.normal(size=(90, 8)) * 1.3, rng.normal(size=(90, 4))
+    ch = oracle.compact_chunked(Q, K, V, 24, 30, k=2, R=2)
+    O_cat, logM_cat = oracle.attention(Q, ch.Ck, ch.Cv, ch.beta)
+    outs, logms = [], []
+    for p in ch.chunks:
+        o, lm = oracle.attention(Q, p.Ck, p.Cv, p.beta)
+        outs.append(o)
+        logms.append(lm)
+    mx = np.max(np.stack(logms), axis=0)
+    wts = [np.exp(lm - mx) for lm in logms]
+    O_mix = sum(w[:, None] * o for w, o in zip(wts, outs)) / sum(wts)[:, None]
+    assert np.allclose(O_cat, O_mix, rtol=1e-12, atol=1e-12)
+    assert np.allclose(logM_cat, mx + np.log(sum(wts)), rtol=1e-12, atol=1e-12)
+
+
+# ----------------------------------------------------------------------------
+# greedy-swap budget schedule (p1 section 4.2; p2 section 4)
+# ----------------------------------------------------------------------------
+def _best_allocation(L, units):
+    H, J = L.shape
+    best, arg = None, None
+    for alloc in itertools.product(range(1, J + 1), repeat=H):
+        if sum(alloc) != units:
+            continue
+        v = sum(L[h, a - 1] for h, a in enumerate(alloc))
+        if best is None or v < best - 1e-15:
+            best, arg = v, alloc
+    return best, arg
+
+
+def test_greedy_swap_reaches_brute_force_optimum_on_convex_curves():
+    rng = np.random.default_rng(530)
+    for trial in range(60):
+        H, J = int(rng.integers(2, 5)), int(rng.integers(2, 6))
+        units = int(rng.integers(H, H * J + 1))
+        L = synth.sensitivity_curves([531, trial], H, J)
+        b, _ = oracle.greedy_swap_budgets(L, 8, units * 8)
+        assert sum(b) == units * 8 and all(8 <= x <= 8 * J for x in b)
+        got = sum(L[h, b[h] // 8 - 1] for h in range(H))
+        best, _ = _best_allocation(L, units)
+        assert got <= best + 1e-12
+
+
+def test_greedy_swap_even_and_flat_cases():
+    L = np.tile(np.exp(-np.arange(1, 7) / 2.0), (4, 1))
+    b, moves = oracle.greedy_swap_budgets(L, 10, 4 * 30)
+    assert b == [30, 30, 30, 30] and moves == 0
+    L2 = L.copy()
+    L2[2] = 1.0  # a head insensitive to its budget gives all but one unit away
+    b2, _ = oracle.greedy_swap_budgets(L2, 10, 4 * 30)
+    assert b2[2] == 10 and sum(b2) == 120
