@@ -668,6 +668,73 @@ __device__ __forceinline__ void lh_backsub(const double *B, const double *c, con
   }
 }
 
+// The Givens chain of a leaving free column k (see lh_solve's leave): the
+// free columns k+1..f-1 move down one place, each restored by a rotation of
+// rows q, q+1 that zeroes the subdiagonal entry of the column arriving at q.
+// Rotation q needs that column's row q after rotation q-1, so the chain is
+// serial; every lane carries the current row q of the targets it owns (the
+// moved columns, the zero columns, c and, when kept, the leaving column in
+// its new zero slot), and only the rotation itself waits on the previous one.
+// Targets, by index tg: [0, nm) the moved columns (old position k+1+tg), then
+// the nz zero columns, c, and the new zero slot (when ntar = nm + nz + 2).
+// Offsets are from B; `last` is the step at which a moved column is the
+// pivot (INT_MAX: never; -1: no target).
+template <int KS>
+__device__ __forceinline__ void lh_chain(double *B, int64_t cap, int p, int k, int f, int nm, int nz, int ntar) {
+  const int lane = threadIdx.x;
+  int so[KS], dof[KS], last[KS];
+  double carry[KS], bn[KS];
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2) {
+    const int tg = lane + 64 * s2;
+    if (tg < nm) {
+      so[s2] = poff(k + 1 + tg);
+      dof[s2] = poff(k + tg);
+      last[s2] = k + tg;
+    } else if (tg < ntar) {
+      const int m = tg - nm;  // zero column m, then c (m = nz), then the new zero slot (m = nz + 1)
+      so[s2] = int(cap - int64_t(p) * (m == nz ? 1 : (m < nz ? m + 2 : nz + 2)));
+      dof[s2] = so[s2];
+      last[s2] = INT_MAX;
+    } else {
+      so[s2] = 0;
+      dof[s2] = 0;
+      last[s2] = -1;
+    }
+    carry[s2] = last[s2] >= 0 ? B[so[s2] + k] : 0.0;
+    bn[s2] = last[s2] > k ? B[so[s2] + k + 1] : 0.0;
+  }
+  for (int q = k; q < f - 1; ++q) {
+    const int tp = q - k;  // the pivot: the moved column arriving at q
+    double mine = carry[0];
+#pragma unroll
+    for (int s2 = 1; s2 < KS; ++s2)
+      if (s2 == (tp >> 6)) mine = carry[s2];
+    const double x = read_lane(mine, tp & 63);
+    const double y = B[poff(q + 1) + q + 1];  // its diagonal, not yet rotated
+    const double rr = sqrt(fma(x, x, y * y));
+    const double inv = rr > 0.0 ? 1.0 / rr : 0.0;
+    const double cs = rr > 0.0 ? x * inv : 1.0, sn = y * inv;
+#pragma unroll
+    for (int s2 = 0; s2 < KS; ++s2) {
+      const int l = last[s2];
+      if (l < q) continue;  // done, or no target (same for the whole slot's loop bounds)
+      if (l == q) {
+        B[dof[s2] + q] = rr;
+        B[dof[s2] + q + 1] = 0.0;
+        continue;
+      }
+      const double b0 = bn[s2];
+      bn[s2] = (l > q + 1 && q + 2 < p) ? B[so[s2] + q + 2] : 0.0;
+      B[dof[s2] + q] = fma(cs, carry[s2], sn * b0);
+      carry[s2] = fma(cs, b0, -sn * carry[s2]);
+    }
+  }
+#pragma unroll
+  for (int s2 = 0; s2 < KS; ++s2)
+    if (last[s2] == INT_MAX) B[dof[s2] + f - 1] = carry[s2];
+}
+
 // Per-slot state of the Lawson-Hanson steps (LDS).
 struct LhSlots {
   double *u;     // scaled iterate, by slot
@@ -763,48 +830,48 @@ __device__ __forceinline__ bool lh_solve(double *B, int64_t cap, const HeadDesc 
   const int cap_it = 3 * p + 30;
   int iters = 0, status = 0;
   bool overflow = false;
-  // removes free column k (to the zero columns if keep); the later free
-  // columns shift down, each restored by a rotation of rows q, q+1
+  // removes free column k (to a new zero column if keep); the later free
+  // columns shift down, each restored by a rotation (lh_chain)
   auto leave = [&](int k, bool keep) {
-    double *c = P.c();
-    for (int r = lane; r < p; r += NQ) z[r] = r <= k ? P.fc(k)[r] : 0.0;
-    const int slot = perm[k];
-    __syncthreads();
-    for (int q = k; q < f - 1; ++q) {
-      double *dst = P.fc(q);
-      const double *src = P.fc(q + 1);
-      for (int r = lane; r <= q + 1; r += NQ) dst[r] = src[r];
-      if (lane == 0) perm[q] = perm[q + 1];
-      __syncthreads();
-      const double x = dst[q], y = dst[q + 1];
-      if (y != 0.0) {  // same for every lane
-        const double rr = hypot(x, y);
-        const double cs = x / rr, sn = y / rr;
-        const int nlater = f - 2 - q;
-        const int ntar = nlater + nz + 2;
-        for (int j = lane; j < ntar; j += NQ) {
-          double *yv = j < nlater ? P.fc(q + 2 + j) : (j < nlater + nz ? P.zc(j - nlater) : (j == nlater + nz ? c : z));
-          const double a0 = yv[q], b0 = yv[q + 1];
-          yv[q] = fma(cs, a0, sn * b0);
-          yv[q + 1] = fma(cs, b0, -sn * a0);
-        }
-        if (lane == 0) {
-          dst[q] = rr;
-          dst[q + 1] = 0.0;
-        }
-      } else if (lane == 0) {
-        dst[q + 1] = 0.0;
-      }
-      __syncthreads();
+    if (keep && !P.fits(f - 1, nz + 1)) {
+      overflow = true;
+      return;
     }
+    const int slot = perm[k];
+    const int nm = f - 1 - k;
+    if (keep) {
+      double *zk = P.zc(nz);
+      const double *ck = P.fc(k);
+      for (int r = lane; r < p; r += NQ) zk[r] = r <= k ? ck[r] : 0.0;
+    }
+    __syncthreads();
+    if (lane == 0)
+      for (int q = k; q < f - 1; ++q) perm[q] = perm[q + 1];
+    // rows above k move unchanged, in increasing order (a column's new place
+    // is the old place of the one before it)
+    for (int j = k + 1; j < f; ++j) {
+      const double *src = P.fc(j);
+      double *dst = P.fc(j - 1);
+      for (int r = lane; r < k; r += NQ) dst[r] = src[r];
+    }
+    __syncthreads();
+    const int ntar = nm + nz + 1 + (keep ? 1 : 0);
+    switch ((ntar + 63) >> 6) {
+      case 1: lh_chain<1>(B, P.cap, p, k, f, nm, nz, ntar); break;
+      case 2: lh_chain<2>(B, P.cap, p, k, f, nm, nz, ntar); break;
+      case 3: lh_chain<3>(B, P.cap, p, k, f, nm, nz, ntar); break;
+      case 4: lh_chain<4>(B, P.cap, p, k, f, nm, nz, ntar); break;
+      case 5: lh_chain<5>(B, P.cap, p, k, f, nm, nz, ntar); break;
+      case 6: lh_chain<6>(B, P.cap, p, k, f, nm, nz, ntar); break;
+      case 7: lh_chain<7>(B, P.cap, p, k, f, nm, nz, ntar); break;
+      case 8: lh_chain<8>(B, P.cap, p, k, f, nm, nz, ntar); break;
+      case 9: lh_chain<9>(B, P.cap, p, k, f, nm, nz, ntar); break;
+      case 10: lh_chain<10>(B, P.cap, p, k, f, nm, nz, ntar); break;
+      default: lh_chain<11>(B, P.cap, p, k, f, nm, nz, ntar); break;
+    }
+    __syncthreads();
     --f;
     if (keep) {
-      if (!P.fits(f, nz + 1)) {
-        overflow = true;
-        return;
-      }
-      double *zk = P.zc(nz);
-      for (int r = lane; r < p; r += NQ) zk[r] = z[r];
       if (lane == 0) zslot[nz] = slot;
       ++nz;
     }

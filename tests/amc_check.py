@@ -19,9 +19,10 @@ minimisers form a face and both weight vectors lie on it), and (ii) the same
 NNLS solved again in extended precision (long double, warm-started from the
 oracle's float64 minimiser) must not move beta past the tolerance.  Only
 where one of these fails are the GPU's weights held to the minimum value
-instead: their NNLS residual within 1e-6 (relative) of the oracle's.  Such
-heads are counted; a test fails when more than FALLBACK_SHARE of its heads
-need it.
+instead: their NNLS residual within 1e-6 (relative) of the oracle's, and its
+errors to those of the oracle's own value fit on the GPU's weights (the value
+fit depends on the point of the face).  Such heads are counted; a test fails
+when more than FALLBACK_SHARE of its heads need it.
 
 Replayed picks: the oracle's scores carry a float64 rounding bound (see
 oracle.omp_select, tie_ulps); a replayed pick is a mismatch only where a key
@@ -131,6 +132,7 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
     rep["e_out_diff"] = abs(e_gpu[1] - e_ref[1])
     rep["fallback"] = False
     rep["beta_envelope"] = None
+    rep["reference"] = (ref.Ck, ref.beta, ref.Cv)  # the compaction the GPU's errors are compared with
     weights_ok = rep["beta_maxdiff"] <= BETA_TOL and rep["one_sided_ok"]
     if not weights_ok:
         # Is beta determined by the float64 data?  Not when the columns of
@@ -155,6 +157,15 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
         if rep["union_sv_min"] < NULL_SV or (env is not None and env > BETA_TOL):
             rep["fallback"] = True
             weights_ok = rep["resid_excess"] <= RESID_REL
+            # the minimisers form a face and the value fit depends on which
+            # point of it the weights are: the oracle's own value fit, taken on
+            # the GPU's weights, is the reference for the GPU's errors
+            Cv_face = O.ols_values(P, w_gpu64, ref.features.Y)
+            e_face = oracle.errors(Q, K, V, Ck, beta, Cv_face, beta_in)
+            rep["e_face"] = e_face
+            rep["reference"] = (Ck, beta, Cv_face)
+            rep["e_mass_diff"] = abs(e_gpu[0] - e_face[0])
+            rep["e_out_diff"] = abs(e_gpu[1] - e_face[1])
     rep["ok"] = (not rep["mismatch_iters"] and rep["same_set"] and rep["ck_exact"] and weights_ok and
                  rep["e_mass_diff"] <= ERR_TOL and rep["e_out_diff"] <= ERR_TOL and rep["relres_ok"])
     rep["t"] = int(t)

@@ -225,18 +225,24 @@ def test_chunked_compaction():
     tr = res.result.trace()
     reps = []
     for i, h in enumerate(heads):
+        refs = []
         for c, (k0, k1, tc) in enumerate(res.split[i]):
             ch = res.chunk_head(i, c)
             rep = replay_check(h.Q, h.K[k0:k1], h.V[k0:k1], tc, 4, 2, res.result, ch, beta_in=betas[i][k0:k1],
                                trace=tr)
             reps.append(rep)
+            refs.append(rep["reference"])
             _assert_ok(rep, f"head{i} chunk{c} [{k0},{k1}) t={tc}")
         Ck, beta, Cv, sel = head_outputs(res, i)
         assert np.all(np.diff(sel) > 0) and sel[0] >= 0 and sel[-1] < h.K.shape[0]
         assert np.array_equal(Ck, np.asarray(h.K, dtype=np.float64)[sel])
-        ref = oracle.compact_chunked(h.Q, h.K, h.V, budgets[i], chunk, 4, 2, beta_in=betas[i])
+        # the concatenation of the chunks' references (the oracle's compaction of
+        # each chunk, or its value fit on the GPU's weights where they are not unique)
+        assert [t for _, _, t in res.split[i]] == [t for _, _, t in oracle.chunk_budgets(h.K.shape[0], budgets[i],
+                                                                                          chunk)]
         e_gpu = oracle.errors(h.Q, h.K, h.V, Ck, beta, Cv, betas[i])
-        e_ref = oracle.errors(h.Q, h.K, h.V, ref.Ck, ref.beta, ref.Cv, betas[i])
+        e_ref = oracle.errors(h.Q, h.K, h.V, np.concatenate([r[0] for r in refs]),
+                              np.concatenate([r[1] for r in refs]), np.concatenate([r[2] for r in refs]), betas[i])
         _say(f"head{i} concatenated: e_gpu {e_gpu} e_ref {e_ref}")
         assert abs(e_gpu[0] - e_ref[0]) <= 1e-3 and abs(e_gpu[1] - e_ref[1]) <= 1e-3
     assert_fallback_share(reps)
