@@ -825,39 +825,46 @@ typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef double f64x2 __attribute__((ext_vector_type(2)));
 
-// 2^(j/32) for j = 0..31, each rounded to the nearest float64.
-__constant__ double kExp2Tab32[32] = {
-    1.0, 1.0218971486541166, 1.0442737824274138, 1.0671404006768237,
-    1.0905077326652577, 1.1143867425958924, 1.1387886347566916, 1.1637248587775775,
-    1.189207115002721, 1.215247359980469, 1.241857812073484, 1.2690509571917332,
-    1.2968395546510096, 1.3252366431597413, 1.3542555469368927, 1.383909881963832,
-    1.4142135623730951, 1.4451808069770467, 1.4768261459394993, 1.5091644275934228,
-    1.5422108254079407, 1.5759808451078865, 1.6104903319492543, 1.645755478153965,
-    1.681792830507429, 1.718619298122478, 1.7562521603732995, 1.7947090750031072,
-    1.8340080864093424, 1.8741676341103, 1.9152065613971474, 1.9571441241754002};
+// 2^(j/64) for j = 0..63, each rounded to the nearest float64.
+__constant__ double kExp2Tab64[64] = {
+    1.0, 1.0108892860517005, 1.0218971486541166, 1.0330248790212284,
+    1.0442737824274138, 1.0556451783605572, 1.0671404006768237, 1.0787607977571199,
+    1.0905077326652577, 1.102382583307841, 1.1143867425958924, 1.1265216186082418,
+    1.1387886347566916, 1.1511892299529827, 1.1637248587775775, 1.1763969916502812,
+    1.189207115002721, 1.202156731452703, 1.215247359980469, 1.22848053610687,
+    1.241857812073484, 1.255380757024691, 1.2690509571917332, 1.2828700160787783,
+    1.2968395546510096, 1.3109612115247644, 1.3252366431597413, 1.339667524053303,
+    1.3542555469368927, 1.3690024229745905, 1.383909881963832, 1.3989796725383112,
+    1.4142135623730951, 1.42961333839197, 1.4451808069770467, 1.460917794180647,
+    1.4768261459394993, 1.4929077282912648, 1.5091644275934228, 1.5255981507445384,
+    1.5422108254079407, 1.559004400237837, 1.5759808451078865, 1.593142151342267,
+    1.6104903319492543, 1.6280274218573478, 1.645755478153965, 1.6636765803267364,
+    1.681792830507429, 1.7001063537185235, 1.718619298122478, 1.7373338352737062,
+    1.7562521603732995, 1.7753764925265212, 1.7947090750031072, 1.8142521755003989,
+    1.8340080864093424, 1.8539791250833855, 1.8741676341103, 1.8945759815869656,
+    1.9152065613971474, 1.9360617934922943, 1.9571441241754002, 1.978456026387951};
 
-// exp(x) in float64 by the table-driven reduction of P. T. P. Tang (ACM
-// TOMS 15(2), 1989): x = (32 m + j) ln2/32 + r with |r| <= ln2/64 (ln2/32 in
-// two parts, so that r carries no cancellation error), exp(x) = 2^m 2^(j/32)
-// exp(r), and exp(r) - 1 from its Taylor polynomial of degree 6 (truncation
-// below 2^-58 for such r).  Within 1 ulp for x >= -745 (checked against a
-// 50-digit reference); x below that, and -inf, give 0; NaN stays NaN.
-// tab: the 32 values of kExp2Tab32.
-__device__ __forceinline__ double exp_tang(double x, const double *tab) {
-  const double N = __builtin_rint(x * 46.16624130844683);  // 32 / ln2
-  const int k = int(N);
-  double r = __builtin_fma(-N, 0.02166084939249829, x);  // ln2/32, leading part
-  r = __builtin_fma(-N, 7.247021293269686e-19, r);        // ln2/32, trailing part
-  double p = 1.0 / 720.0;
-  p = __builtin_fma(p, r, 1.0 / 120.0);
-  p = __builtin_fma(p, r, 1.0 / 24.0);
-  p = __builtin_fma(p, r, 1.0 / 6.0);
-  p = __builtin_fma(p, r, 0.5);
-  p = __builtin_fma(p, r, 1.0);
-  p *= r;
-  const double t = tab[k & 31];
-  const double e = __builtin_amdgcn_ldexp(__builtin_fma(t, p, t), k >> 5);
-  return x < -745.2 ? 0.0 : e;
+// exp(x) in float64 after the table-driven reduction of P. T. P. Tang (ACM
+// TOMS 15(2), 1989) with 64 table entries: x = (64 m + j) ln2/64 + r with
+// |r| <= ln2/128, exp(x) = 2^m 2^(j/64) exp(r), and exp(r) from its Taylor
+// polynomial of degree 4 (truncation below 4e-14 relative).  N = 64 m + j is
+// rounded by one fused multiply-add with 1.5 2^52, whose low word then holds
+// N; ln2/64 enters in one part, which moves r by at most |N| 2^-60 (below
+// 4e-15 for x >= -40).  x is first raised to -746, so -inf and anything below
+// give 0; a NaN x would give 0 too, so callers never pass one (heads whose
+// bias is NaN or +inf take the float64 kernel).
+// tab: the 64 values of kExp2Tab64.
+__device__ __forceinline__ double exp_t64(double x, const double *tab) {
+  x = __builtin_fmax(x, -746.0);
+  const double kd = __builtin_fma(x, 92.33248261689366, 6755399441055744.0);  // 64/ln2, 1.5 2^52
+  const int k = int(uint32_t(__builtin_bit_cast(uint64_t, kd)));
+  const double N = kd - 6755399441055744.0;
+  const double r = __builtin_fma(N, -0.010830424696249145, x);  // ln2/64
+  double q = __builtin_fma(r, 1.0 / 24.0, 1.0 / 6.0);
+  q = __builtin_fma(q, r, 0.5);
+  q = __builtin_fma(q, r, 1.0);
+  const double t = tab[k & 63];
+  return __builtin_amdgcn_ldexp(__builtin_fma(t * r, q, t), k >> 6);
 }
 
 // ---------------------------------------------------------------------------
@@ -867,8 +874,8 @@ __device__ __forceinline__ double exp_tang(double x, const double *tab) {
 // base-256 digits d_0..d_4 in [-128, 127] with N = sum_s d_s 256^s.  x lies on
 // this grid when its last significand bit is worth at least 2^(E - 37): for a
 // normal bf16, when its exponent is at least E - 30.  A head with an entry
-// off the grid, or a non-finite entry, gets f64_heads[h] = 1 and takes the
-// float64 logit kernel.
+// off the grid, a non-finite entry, or a bias - shift that is NaN or +inf
+// gets f64_heads[h] = 1 and takes the float64 logit kernel.
 // Layouts: a Q row r: digit s of dims 8 j .. 8 j + 7 at qdig[5 D r + D s + 8 j],
 // 4 E + z at qexp[r] (rows numbered as in Q), z the row's low digits that are
 // zero in all its entries, counted up to 2.  K rows run over the head's keys
@@ -979,7 +986,11 @@ __global__ __launch_bounds__(256) void k_digits(const HeadDesc *__restrict__ des
         const int pos = store_pos(kk >> 4, kk & 3, (kk >> 2) & 3);
         uint8_t *tb = ktab + ((Dh.kt_off + key) >> 6) * 1024;
         double bms = -INFINITY;
-        if (key < Dh.T) bms = (beta_in ? double(beta_in[Dh.k_off + key]) : 0.0) - double(s_shift);
+        if (key < Dh.T) {
+          bms = (beta_in ? double(beta_in[Dh.k_off + key]) : 0.0) - double(s_shift);
+          // a NaN or +inf bias (or shift) is the float64 kernel's to report
+          if (!(bms < INFINITY)) bad = 1;
+        }
         reinterpret_cast<double *>(tb)[pos] = bms;
         reinterpret_cast<int32_t *>(tb + 512)[pos] = E;
         atomicMin(&s_zmin[(tid / TPR) >> 4], z);
@@ -1004,18 +1015,32 @@ __global__ __launch_bounds__(256) void k_digits(const HeadDesc *__restrict__ des
 // (k_digits), the logit of query q and key k is
 //   2^(E_q + E_k - 74) sum_c C_c 256^c,  C_c = sum over digit pairs s + t = c
 //   of the int32 dot products of Q digit s and K digit t,
-// each product on v_mfma_i32_16x16x64_i8 (exact: |C_c| < 2^24).  The nine C_c
-// are joined in float64 (one rounding per join), and the power of two, the
-// logit scale, the bias and the shift applied in one fused multiply-add, so
-// the result is the float64 dot product of the bf16 inputs to within a few
-// roundings, as the float64 MFMA gives it.  Per 64-key tile three contiguous
-// asynchronous copies stage the K digit rows (KROW slots per key), the value
-// tile and the key table (bias - shift, -inf past T, so padding keys give 0
-// with no test; row exponents).  MFMA row 4 g + e is fed key g + 4 e of its
-// 16-key block, so the outputs land where the float64 kernel has them.  The
-// exps of a block are software-pipelined against the next block's MFMAs.
-// Heads with f64_heads[h] != 0 return at once (the float64 kernel takes
-// them).
+// each product on v_mfma_i32_16x16x64_i8 (exact: |C_c| < 2^24).
+//
+// Joining the classes.  Digits 0..3 are at most 128 in size and digit 4 at
+// most 64, so with Q digits from 1 up (a wave's zq >= 1) the pairs
+//   P1 = C_3 + 256 C_4,  P2 = C_5 + 256 C_6,  P3 = C_7 + 256 C_8
+// stay below 2^31 (the largest, P1 with zq = 1, below 1.9e9), and the logit
+// in units of class 3 is P1 + 2^16 P2 + 2^32 P3 (+ C_2 / 256 when zq = 1):
+// three or four int32 -> float64 conversions and fused multiply-adds, the
+// first exact and the last rounded once, as the float64 MFMA gives the dot
+// product to within a few roundings.  Waves with zq = 0 (an entry more than
+// 22 binades below its row's largest) join the classes one by one.  K digit
+// 0 is zero in almost every 16-key block (zk >= 1); a block with zk = 0 takes
+// its digit-0 products in a branch, which folds the lowest class (below the
+// join's) into the key's bias term.  The power of two, the logit scale, the
+// bias and the shift enter in one fused multiply-add.
+//
+// Schedule.  Per 64-key tile three contiguous asynchronous copies stage the K
+// digit rows (KROW slots per key), the value tile and the key table (bias -
+// shift, -inf past T, so padding keys give 0 with no test; row exponents; zk
+// per block).  MFMA row 4 g + e is fed key g + 4 e of its 16-key block, so the
+// outputs land where the float64 kernel has them.  The four 16-key blocks run
+// as a two-stage pipeline: the class products of block kb on the matrix units
+// next to the join and exp of block kb - 1 on the vector units (two class
+// accumulator sets), then Phi V of keys 0..31 next to block 3, and of keys
+// 32..63 last.  Heads with f64_heads[h] != 0 return at once (the float64
+// kernel takes them).
 // ---------------------------------------------------------------------------
 template <int D, int STORE>
 __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
@@ -1038,7 +1063,7 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
   __shared__ __attribute__((aligned(16))) uint32_t lk_all[2 * KWORDS];
   __shared__ __attribute__((aligned(16))) uint32_t lv_all[2 * VWORDS];
   __shared__ __attribute__((aligned(16))) uint32_t lt_all[2 * 256];  // key tables
-  __shared__ double s_tab[32];
+  __shared__ double s_tab[64];
   // STORE == 2: each wave's Phi of a tile, [64 keys][16 queries], turned into
   // key rows for 16-byte stores of the two planes
   __shared__ __attribute__((aligned(16))) uint32_t lx_all[STORE == 2 ? P16_WAVES * 1024 : 1];
@@ -1074,26 +1099,21 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off));
     if (tid == 0) s_shift = double(v);
-  } else if (tid < 96) {
-    s_tab[tid - 64] = kExp2Tab32[tid - 64];
+  } else if (tid < 128) {
+    s_tab[tid - 64] = kExp2Tab64[tid - 64];
   }
 
   // B operand: query q, digit s, dims 64 c + 16 g + (0..15) at k-step c
   const int64_t qw = q0 + 16 * wave;
   const int64_t q = qw + c16;
   const bool qvalid = q < Dh.n;
+  const bool wfull = qw + 16 <= Dh.n;  // no padding query in the wave
   const int64_t qrow = Dh.q_off + (qvalid ? q : Dh.n - 1);
-  u32x4 qd[kDigits][NCH];
-#pragma unroll
-  for (int sd = 0; sd < kDigits; ++sd)
-#pragma unroll
-    for (int c = 0; c < NCH; ++c) {
-      qd[sd][c] = *reinterpret_cast<const u32x4 *>(qdig + qrow * (kDigits * D) + sd * D + 64 * c + 16 * g);
-      if (!qvalid) qd[sd][c] = u32x4{0u, 0u, 0u, 0u};
-    }
-  // scale 2^(E_q - 74): times 2^(E_k) per key, an exact power-of-two rescaling
+  const int8_t *qsrc = qdig + qrow * (kDigits * D) + 16 * g;
+  // scale of class 3: 2^(E_q - 74 + 24), times 2^(E_k) per key, an exact
+  // power-of-two rescaling
   const int qx = qexp[qrow];
-  const double qscale = ldexp(scale, (qx >> 2) - 74);
+  const double qs3 = ldexp(scale, (qx >> 2) - 50);
   // low Q digits zero in all 16 queries of the wave (0, 1 or 2: most waves
   // have every entry within 14 binades of its row's largest, two)
   int zq = qvalid ? (qx & 3) : 2;
@@ -1136,10 +1156,46 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
   // MFMA row c16 of a 16-key block is fed key (c16 >> 2) + 4 (c16 & 3)
   const int krow = (c16 >> 2) + 4 * (c16 & 3);
 
-  // ZQ: Q digits below ZQ are zero for the whole wave and skipped; per 16-key
-  // block, K digits below its zk likewise.
-  auto compute = [&](auto zq_c, int tile, const uint32_t *lk, const uint32_t *lv, const uint32_t *lt, bool next,
-                     uint32_t *nk, uint32_t *nv, uint32_t *nt) __attribute__((always_inline)) {
+  // Phi V of the 32 keys 32 c .. 32 c + 31 (blocks 2 c and 2 c + 1): each
+  // float32 Phi as three bf16 parts (high, middle, low: exact), all three
+  // against the bf16 values
+  auto phiv = [&](const float (&x)[4][4], const u32x4 *vl4, int c) __attribute__((always_inline)) {
+    uint32_t w[3][4];
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int e2 = 0; e2 < 2; ++e2) {
+        uint32_t t[3][2];
+#pragma unroll
+        for (int h2 = 0; h2 < 2; ++h2) {
+          const float v = x[2 * c + j][2 * e2 + h2];
+          const float hi = __uint_as_float(__float_as_uint(v) & 0xffff0000u);
+          const float r1 = v - hi;
+          const float mi = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
+          const float lo = r1 - mi;
+          t[0][h2] = __float_as_uint(v);
+          t[1][h2] = __float_as_uint(r1);
+          t[2][h2] = __float_as_uint(lo);
+        }
+        // the high halves of v, r1 and lo are the three parts
+#pragma unroll
+        for (int qq = 0; qq < 3; ++qq) w[qq][2 * j + e2] = __builtin_amdgcn_perm(t[qq][1], t[qq][0], 0x07060302u);
+      }
+#pragma unroll
+    for (int db = 0; db < NU; ++db) {
+      const u32x4 vv = vl4[db * 16 * 9 + 4 * c];
+      const bf16x8 bv = __builtin_bit_cast(bf16x8, vv);
+#pragma unroll
+      for (int qq = 2; qq >= 0; --qq)
+        uacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+            __builtin_bit_cast(bf16x8, u32x4{w[qq][0], w[qq][1], w[qq][2], w[qq][3]}), bv, uacc[db], 0, 0, 0);
+    }
+  };
+
+  // ZQ: Q digits below ZQ are zero for the whole wave and skipped.
+  auto compute = [&](auto zq_c, const u32x4 (&qd)[kDigits][NCH], int tile, const uint32_t *lk, const uint32_t *lv,
+                     const uint32_t *lt, bool next, uint32_t *nk, uint32_t *nv, uint32_t *nt)
+      __attribute__((always_inline)) {
     constexpr int ZQ = decltype(zq_c)::value;
     const int64_t k0 = int64_t(tile) * 64;
     if (next) issue(tile + 1, nk, nv, nt);
@@ -1147,69 +1203,102 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
     const u32x4 *vl4 = reinterpret_cast<const u32x4 *>(lv) + (c16 * 9 + g);
     const double *tbm = reinterpret_cast<const double *>(lt);
     const int32_t *tke = reinterpret_cast<const int32_t *>(lt) + 128;
-    const int32_t *tzk = reinterpret_cast<const int32_t *>(lt) + 192;
-    // Software pipeline over the four 16-key blocks: the exps of block kb - 1
-    // are independent of the MFMAs of block kb, so the two interleave.
+    const i32x4 zk4 = *reinterpret_cast<const i32x4 *>(reinterpret_cast<const int32_t *>(lt) + 192);
     float x[4][4];
-    double arg[4][4];  // exp arguments (scaled logit + bias - shift)
+    i32x4 acc[2][NC];
+    double bms[2][4];
+    int32_t kex[2][4];
 #pragma unroll
     for (int kb = 0; kb <= 4; ++kb) {
-      i32x4 acc[NC];
-      if (kb < 4) {
-#pragma unroll
-        for (int c = 0; c < NC; ++c) acc[c] = i32x4{0, 0, 0, 0};
-        const int zk = __builtin_amdgcn_readfirstlane(tzk[kb]);
-#pragma unroll
-        for (int c = 0; c < NCH; ++c) {
-#pragma unroll
-          for (int t = 0; t < kDigits; ++t) {
-            if (t >= 2 || t >= zk) {
-              const u32x4 kd = kl4[kb * 16 * KROW + t * (D / 16) + 4 * c];
-#pragma unroll
-              for (int sd = ZQ; sd < kDigits; ++sd)
-                acc[sd + t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, kd),
-                                                                    __builtin_bit_cast(i32x4, qd[sd][c]),
-                                                                    acc[sd + t], 0, 0, 0);
-            }
-          }
-        }
-      }
-      if (kb > 0) {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const double p = exp_tang(arg[kb - 1][e], s_tab);
-          msum += p;
-          x[kb - 1][e] = float(p);
-        }
-      }
+      const int cur = kb & 1, prv = cur ^ 1;
       if (kb < 4) {
         const int pos = store_pos(kb, g, 0);
         const f64x2 bm0 = *reinterpret_cast<const f64x2 *>(tbm + pos);
         const f64x2 bm1 = *reinterpret_cast<const f64x2 *>(tbm + pos + 2);
         const i32x4 ke = *reinterpret_cast<const i32x4 *>(tke + pos);
-        const double bms[4] = {bm0[0], bm0[1], bm1[0], bm1[1]};
+        bms[cur][0] = bm0[0];
+        bms[cur][1] = bm0[1];
+        bms[cur][2] = bm1[0];
+        bms[cur][3] = bm1[1];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) kex[cur][e] = ke[e];
+#pragma unroll
+        for (int c = 0; c < NC; ++c) acc[cur][c] = i32x4{0, 0, 0, 0};
+        // class products of K digits 1..4
+#pragma unroll
+        for (int c = 0; c < NCH; ++c) {
+#pragma unroll
+          for (int t = 1; t < kDigits; ++t) {
+            const u32x4 kd = kl4[kb * 16 * KROW + t * (D / 16) + 4 * c];
+#pragma unroll
+            for (int sd = ZQ; sd < kDigits; ++sd)
+              acc[cur][sd + t] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, kd),
+                                                                      __builtin_bit_cast(i32x4, qd[sd][c]),
+                                                                      acc[cur][sd + t], 0, 0, 0);
+          }
+        }
+      }
+      if (kb > 0) {
+        // join and exp of block kb - 1
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          // C_0 + 256 C_1 and C_7 + 256 C_8 stay within int32 (|C_0| <= 2^21,
-          // |C_1| <= 2^22; the top digits are at most 64 in size, so
-          // |C_7| < 2^21.1, |C_8| < 2^19.1); the rest join in float64
-          // (classes below ZQ are zero)
-          double v = ZQ >= 2 ? double(acc[2][e]) : double((ZQ >= 1 ? 0 : acc[0][e]) + (acc[1][e] << 8));
-          double w256 = ZQ >= 2 ? 65536.0 : 256.0;
+          double v;
+          if constexpr (ZQ >= 1) {
+            const int32_t p1 = acc[prv][3][e] + (acc[prv][4][e] << 8);
+            const int32_t p2 = acc[prv][5][e] + (acc[prv][6][e] << 8);
+            const int32_t p3 = acc[prv][7][e] + (acc[prv][8][e] << 8);
+            v = fma(double(p2), 65536.0, double(p1));
+            v = fma(double(p3), 4294967296.0, v);
+            if constexpr (ZQ == 1) v = fma(double(acc[prv][2][e]), 0.00390625, v);
+          } else {
+            v = double(acc[prv][1][e]) * 1.52587890625e-05;  // 2^-16
+            double w = 0.00390625;
 #pragma unroll
-          for (int c = ZQ >= 2 ? 3 : 2; c < NC - 2; ++c) {
-            w256 *= 256.0;
-            v = fma(double(acc[c][e]), w256, v);
+            for (int c = 2; c < NC; ++c) {
+              v = fma(double(acc[prv][c][e]), w, v);
+              w *= 256.0;
+            }
           }
-          v = fma(double(acc[NC - 2][e] + (acc[NC - 1][e] << 8)), w256 * 256.0, v);
-          arg[kb][e] = fma(v, ldexp(qscale, ke[e]), bms[e]);
+          const double p = exp_t64(fma(v, ldexp(qs3, kex[prv][e]), bms[prv][e]), s_tab);
+          msum += p;
+          x[kb - 1][e] = float(p);
+        }
+      }
+      if (kb == 3) phiv(x, vl4, 0);
+      if (kb < 4) {
+        const int zk = __builtin_amdgcn_readfirstlane(zk4[kb]);
+        if (zk == 0) {
+          // K digit 0 is live in this block: its products, the lowest class
+          // (s = ZQ, t = 0) folded into the bias term
+          i32x4 low = {0, 0, 0, 0};
+#pragma unroll
+          for (int c = 0; c < NCH; ++c) {
+            const u32x4 kd = kl4[kb * 16 * KROW + 4 * c];
+            low = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, kd),
+                                                       __builtin_bit_cast(i32x4, qd[ZQ][c]), low, 0, 0, 0);
+#pragma unroll
+            for (int sd = ZQ + 1; sd < kDigits; ++sd)
+              acc[cur][sd] = __builtin_amdgcn_mfma_i32_16x16x64_i8(__builtin_bit_cast(i32x4, kd),
+                                                                  __builtin_bit_cast(i32x4, qd[sd][c]), acc[cur][sd],
+                                                                  0, 0, 0);
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            bms[cur][e] = fma(double(low[e]), ldexp(qs3, kex[cur][e] - 8 * (3 - ZQ)), bms[cur][e]);
         }
       }
     }
+    phiv(x, vl4, 1);
     // the next tile's copies have landed
     __builtin_amdgcn_s_waitcnt(0);
     if constexpr (STORE == 2) {
       if (qw < Dh.ldN) {
+        if (!wfull) {
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x[kb][e] = qvalid ? x[kb][e] : 0.0f;
+        }
         // lane (c16, g) puts its values at [key][c16] of the wave's block; then
         // lane l takes (key, 8 queries) items l and l + 64 and writes the high
         // and the low halves of the 8 values as one 16-byte store each (the
@@ -1218,7 +1307,7 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-          for (int e = 0; e < 4; ++e) lx[(16 * kb + g + 4 * e) * 16 + c16] = __float_as_uint(qvalid ? x[kb][e] : 0.0f);
+          for (int e = 0; e < 4; ++e) lx[(16 * kb + g + 4 * e) * 16 + c16] = __float_as_uint(x[kb][e]);
         uint16_t *hp = phi16 + 2 * Dh.phi_off;
         uint16_t *lp = hp + Dh.ldT * Dh.ldN;
 #pragma unroll
@@ -1236,38 +1325,6 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
         }
       }
     }
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      uint32_t w[3][4];
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-#pragma unroll
-        for (int e2 = 0; e2 < 2; ++e2) {
-          uint32_t t[3][2];
-#pragma unroll
-          for (int h2 = 0; h2 < 2; ++h2) {
-            const float v = x[2 * c + j][2 * e2 + h2];
-            const float hi = __uint_as_float(__float_as_uint(v) & 0xffff0000u);
-            const float r1 = v - hi;
-            const float mi = __uint_as_float(__float_as_uint(r1) & 0xffff0000u);
-            const float lo = r1 - mi;
-            t[0][h2] = __float_as_uint(hi);
-            t[1][h2] = __float_as_uint(mi);
-            t[2][h2] = __float_as_uint(lo);
-          }
-#pragma unroll
-          for (int qq = 0; qq < 3; ++qq) w[qq][2 * j + e2] = (t[qq][0] >> 16) | (t[qq][1] & 0xffff0000u);
-        }
-#pragma unroll
-      for (int db = 0; db < NU; ++db) {
-        const u32x4 vv = vl4[db * 16 * 9 + 4 * c];
-        const bf16x8 bv = __builtin_bit_cast(bf16x8, vv);
-#pragma unroll
-        for (int qq = 2; qq >= 0; --qq)
-          uacc[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-              __builtin_bit_cast(bf16x8, u32x4{w[qq][0], w[qq][1], w[qq][2], w[qq][3]}), bv, uacc[db], 0, 0, 0);
-      }
-    }
   };
 
   issue(0, lk0, lv0, lt0);
@@ -1280,11 +1337,20 @@ __global__ __launch_bounds__(kPhi16Rows * 4) void k_phi8(
   // waves of one block may take different variants; every path meets the
   // same barriers
   auto run = [&](auto zq_c) __attribute__((always_inline)) {
+    constexpr int ZQ = decltype(zq_c)::value;
+    u32x4 qd[kDigits][NCH];
+#pragma unroll
+    for (int sd = 0; sd < kDigits; ++sd)
+#pragma unroll
+      for (int c = 0; c < NCH; ++c) {
+        qd[sd][c] = u32x4{0u, 0u, 0u, 0u};
+        if (sd >= ZQ && qvalid) qd[sd][c] = *reinterpret_cast<const u32x4 *>(qsrc + sd * D + 64 * c);
+      }
     for (int tile = 0; tile < ntiles; tile += 2) {
-      compute(zq_c, tile, lk0, lv0, lt0, tile + 1 < ntiles, lk1, lv1, lt1);
+      compute(zq_c, qd, tile, lk0, lv0, lt0, tile + 1 < ntiles, lk1, lv1, lt1);
       __syncthreads();
       if (tile + 1 >= ntiles) break;
-      compute(zq_c, tile + 1, lk1, lv1, lt1, tile + 2 < ntiles, lk0, lv0, lt0);
+      compute(zq_c, qd, tile + 1, lk1, lv1, lt1, tile + 2 < ntiles, lk0, lv0, lt0);
       __syncthreads();
     }
   };

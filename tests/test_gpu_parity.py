@@ -612,6 +612,24 @@ def test_nonfinite_input_is_flagged_and_isolated():
     _assert_ok(replay_check(heads[0].Q, heads[0].K, heads[0].V, 10, 1, 1, res, 0), "clean head next to a NaN head")
 
 
+@pytest.mark.parametrize("bad", [float("nan"), float("inf")])
+def test_nonfinite_bias_is_flagged_and_isolated(bad):
+    heads = [synth.make_head([81, i], 70, 200, 128, True, "bf16") for i in range(2)]
+    Q, K, V, cu_q, cu_k = pack_heads(heads, "bf16")
+    betas = [synth.random_beta([82, i], 200, 2.0) for i in range(2)]
+    betas[1] = betas[1].copy()
+    betas[1][17] = bad
+    beta = torch.from_numpy(np.concatenate(betas).astype(np.float32)).cuda()
+    shift, _, m, _, hs = amc.mass_features(Q, K, V, cu_q=cu_q, cu_k=cu_k, beta_in=beta, want_phi=False)
+    hs = hs.cpu().numpy()
+    _say(f"bias {bad}: status {hs}")
+    assert hs[1] & amc.HS_NONFINITE
+    assert hs[0] == 0
+    f = oracle.mass_features(heads[0].Q, heads[0].K, heads[0].V, betas[0], shift=float(shift[0]))
+    mm = m.cpu().numpy()[cu_q[0]: cu_q[1]]
+    assert np.max(np.abs(mm - f.m) / f.m) < 1e-12
+
+
 @pytest.mark.slow
 def test_workload1_full_size_sampled():
     w = synth.workload(1)
