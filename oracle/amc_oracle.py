@@ -266,7 +266,7 @@ def nnls_qr(PhiS, m, w0=None, max_outer=None, dtype=np.float64):
         f = len(free)
         T = _qr_r(np.column_stack([A[:, free + zero], y]))
         Tf = np.zeros((t, t + 1), dtype=dtype)
-        Tf[: T.shape[0]] = T
+        Tf[: T.shape[0], : T.shape[1]] = T  # fewer columns once some are left out
         c = Tf[:, f + len(zero)]
         dep = [i for i in range(f) if abs(Tf[i, i]) <= DEP_TOL]
         if dep:  # dependent on the free columns before it: out for good
@@ -308,6 +308,143 @@ def nnls_qr(PhiS, m, w0=None, max_outer=None, dtype=np.float64):
     raise RuntimeError(f"nnls_qr: no KKT point within {max_outer} iterations")
 
 
+def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
+    """nnls_qr's Lawson-Hanson iteration, step for step, with the factor of
+    the columns ordered [free | zero] and y kept from one iteration to the
+    next instead of recomputed (the same algorithm: p1 section 1.6, the NNLS
+    refit; its least-squares steps through an orthogonal factorisation of
+    Phi_S).  O(t^2) per iteration instead of nnls_qr's O(t^3), for budgets in
+    the thousands.
+
+    State: W (t rows; columns in position order, the free block upper
+    triangular, zero columns full height) and c, both Q^T of the reduced
+    system for some orthogonal Q.
+    - A column enters: it moves to position f and one Householder reflection
+      of rows f..t-1 zeroes it below row f (the zero columns and c take it).
+    - A column leaves from free position k: the free columns after it move
+      down one place and a Givens rotation of rows q, q+1 for q = k..f-2
+      restores the triangle (every column from q on and c take them); a
+      column kept for later goes to the zero block, a dependent one is
+      dropped.
+    Norms of the zero columns below row f and their inner products with c
+    there do not depend on Q, so the entering test is nnls_qr's; ties go to
+    the lower key, as there.
+    """
+    from scipy.linalg import solve_triangular
+
+    A0 = np.asarray(PhiS, dtype=np.float64)
+    y0 = np.asarray(m, dtype=np.float64)
+    n, t = A0.shape
+    dg = np.sqrt(np.sum(A0 * A0, axis=0))
+    live = dg > 0
+    dg = np.where(live, dg, 1)
+    R = _qr_r(np.column_stack([A0 / dg, y0]))
+    A = np.zeros((t, t))
+    y = np.zeros(t)
+    k0 = min(R.shape[0], t)
+    A[:k0] = R[:k0, :t]
+    y[:k0] = R[:k0, t]
+    if max_outer is None:
+        max_outer = 3 * t + 30
+    u = np.zeros(t)
+    if w0 is not None:
+        u[: len(w0)] = np.maximum(np.asarray(w0, dtype=np.float64), 0) * dg[: len(w0)]
+    u[~live] = 0
+    free = [a for a in range(t) if u[a] > 0]
+    zero = [a for a in range(t) if live[a] and u[a] == 0]
+    Mf = _qr_r(np.column_stack([A[:, free + zero], y]))
+    W = np.zeros((t, len(free) + len(zero)))
+    c = np.zeros(t)
+    W[: Mf.shape[0]] = Mf[:, :-1]
+    c[: Mf.shape[0]] = Mf[:, -1]
+    cols = free + zero  # key of each column position
+
+    def leave(k, keep):
+        nonlocal W
+        f = len(free)
+        key = cols[k]
+        colk = W[:, k].copy()
+        W = np.delete(W, k, axis=1)
+        del cols[k]
+        del free[k]
+        if keep:
+            W = np.column_stack([W, colk])
+            cols.append(key)
+            zero.append(key)
+        for q in range(k, f - 1):
+            a, b = W[q, q], W[q + 1, q]
+            r = math.hypot(a, b)
+            if r == 0.0:
+                continue
+            cs, sn = a / r, b / r
+            top = W[q, q:].copy()
+            W[q, q:] = cs * top + sn * W[q + 1, q:]
+            W[q + 1, q:] = cs * W[q + 1, q:] - sn * top
+            W[q + 1, q] = 0.0
+            cq = c[q]
+            c[q] = cs * cq + sn * c[q + 1]
+            c[q + 1] = cs * c[q + 1] - sn * cq
+
+    for _ in range(max_outer):
+        f = len(free)
+        d = np.abs(np.diag(W[:f, :f])) if f else np.zeros(0)
+        dep = np.flatnonzero(d <= DEP_TOL)
+        if dep.size:  # dependent on the free columns before it: out for good
+            a = free[int(dep[0])]
+            u[a] = 0
+            leave(int(dep[0]), False)
+            continue
+        z = solve_triangular(W[:f, :f], c[:f]) if f else np.zeros(0)
+        if np.any(z <= 0):
+            # step from the feasible u toward z until the first free variable hits zero
+            neg = np.flatnonzero(z <= 0)
+            uf = u[free]
+            ratios = uf[neg] / (uf[neg] - z[neg])
+            i_min = int(neg[int(np.argmin(ratios))])
+            uf = uf + ratios.min() * (z - uf)
+            uf[i_min] = 0
+            u[free] = np.maximum(uf, 0)
+            for kk in range(f - 1, -1, -1):
+                if not u[free[kk]] > 0:
+                    leave(kk, True)
+            continue
+        u[:] = 0
+        u[free] = z
+        rz = c[f:]
+        nr = float(np.sqrt(np.sum(rz * rz)))
+        nz = len(cols) - f
+        enter = -1
+        if nz and nr > 0:
+            Z = W[f:, f:]
+            den = np.sqrt(np.sum(Z * Z, axis=0))
+            with np.errstate(invalid="ignore", divide="ignore"):
+                cos = np.where(den > DEP_TOL, (rz @ Z) / (den * nr), -np.inf)
+            best = np.max(cos)
+            if best > COS_TOL:
+                keys = np.asarray(cols[f:])
+                enter = f + int(np.flatnonzero(cos == best)[np.argmin(keys[cos == best])])
+        if enter < 0:
+            return (u / dg).astype(np.float64)
+        # the entering column to position f, then one reflection of rows f..t-1
+        key = cols[enter]
+        W[:, [f, enter]] = W[:, [enter, f]]
+        cols[f], cols[enter] = cols[enter], cols[f]
+        zero.remove(key)
+        free.append(key)
+        x = W[f:, f]
+        nrm = float(np.sqrt(np.sum(x * x)))
+        if nrm > 0 and f + 1 < t:
+            alpha = -nrm if x[0] >= 0 else nrm
+            v = x.copy()
+            v[0] -= alpha
+            vtv = float(np.sum(v * v))
+            if vtv > 0:
+                W[f:, f:] -= np.outer(v, (v @ W[f:, f:]) * (2 / vtv))
+                c[f:] -= v * ((v @ c[f:]) * (2 / vtv))
+                W[f + 1:, f] = 0.0
+    raise RuntimeError(f"nnls_lh_update: no KKT point within {max_outer} iterations")
+
+
 def nnls_exact(PhiS, m, w_prev=None):
     """The exact NNLS minimiser of ||Phi_S w - m|| over w >= 0, the bias fit of
     the key-selection step (p1 section 1.6: refit w by NNLS; p2 section 2,
@@ -316,8 +453,10 @@ def nnls_exact(PhiS, m, w_prev=None):
     The pages' GPU solver is projected gradient (p2 Fig. 2); what it converges
     to is this minimiser, which the oracle computes directly: Lawson-Hanson
     (scipy) for up to 256 columns, above that Lawson-Hanson on the
-    triangular factor of [Phi_S m] (nnls_qr), warm-started from the previous
-    refit's weights.  Both work on Phi_S through orthogonal factorisations.
+    triangular factor of [Phi_S m] with the factor updated between
+    iterations (nnls_lh_update, nnls_qr's iteration), warm-started from the
+    previous refit's weights.  Both work on Phi_S through orthogonal
+    factorisations.
     """
     t = PhiS.shape[1]
     if t <= 256:
@@ -333,7 +472,7 @@ def nnls_exact(PhiS, m, w_prev=None):
     if w_prev is not None:
         w0 = np.zeros(t)
         w0[: len(w_prev)] = w_prev
-    return nnls_qr(PhiS, m, w0)
+    return nnls_lh_update(PhiS, m, w0)
 
 
 def nnls_kkt_violation(G, b, w):

@@ -257,6 +257,49 @@ def test_nnls_qr_warm_start_same_minimiser():
     assert np.array_equal(cold > 0, warm > 0)
 
 
+def test_nnls_lh_update_follows_nnls_qr():
+    """The updating form of the Lawson-Hanson iteration against the
+    refactoring one, on systems with dependent columns, fewer rows than
+    columns, zero columns and warm starts: the same minimum (1e-9 of |m|) and,
+    on full-rank systems, the same weights."""
+    rng = np.random.default_rng(44)
+    for trial in range(120):
+        n = int(rng.integers(2, 50))
+        t = int(rng.integers(1, 40))
+        A = np.abs(rng.normal(size=(n, t))) ** rng.uniform(0.5, 3)
+        if trial % 4 == 0 and t > 3:
+            A[:, 2] = 0.5 * (A[:, 0] + A[:, 1])
+        if trial % 9 == 0 and t > 1:
+            A[:, 1] = 0.0
+        m = A @ (np.abs(rng.normal(size=t)) * (rng.random(t) > 0.3)) + np.abs(rng.normal(size=n)) * rng.uniform(0, 1)
+        w_qr = oracle.nnls_qr(A, m)
+        w0 = None if trial % 3 else w_qr * rng.uniform(0.2, 2.0, size=t) * (rng.random(t) > 0.4)
+        w_up = oracle.nnls_lh_update(A, m, w0=w0)
+        assert np.all(w_up >= 0)
+        nm = np.linalg.norm(m)
+        assert abs(_objective(A, m, w_up) - _objective(A, m, w_qr)) <= 1e-9 * nm
+        if n >= t + 5 and trial % 4 and trial % 9:
+            assert np.allclose(w_up, w_qr, rtol=1e-7, atol=1e-9 * w_qr.max(initial=1.0))
+
+
+def test_nnls_lh_update_kkt_at_large_budget():
+    """At t = 1000 of a real head (2048 queries) the updating solver reaches
+    a KKT point of the refit to float64 resolution, and agrees with the
+    refactoring solver's minimum at t = 300 on the same head."""
+    h = synth.make_head([45, 0], 2048, 4096, 128, True, "bf16")
+    f = oracle.mass_features(h.Q, h.K, h.V)
+    order = np.argsort(-O.highest_scores(f.Phi, f.m), kind="stable")
+    P = f.Phi[:, order[:1000]]
+    w = oracle.nnls_lh_update(P, f.m)
+    assert O.nnls_kkt_violation(P.T @ P, P.T @ f.m, w) < 1e-12
+    P3 = f.Phi[:, order[:300]]
+    w3, q3 = oracle.nnls_lh_update(P3, f.m), oracle.nnls_qr(P3, f.m)
+    assert abs(_objective(P3, f.m, w3) / _objective(P3, f.m, q3) - 1) < 1e-9
+    both = (w3 > 0) & (q3 > 0)
+    assert np.array_equal(w3 > 0, q3 > 0)
+    assert np.max(np.abs(np.log(w3[both]) - np.log(q3[both]))) < 1e-6
+
+
 def test_nnls_iteration_caps_raise():
     """An exhausted iteration cap is an error, not a silent return."""
     rng = np.random.default_rng(12)
@@ -266,6 +309,8 @@ def test_nnls_iteration_caps_raise():
         oracle.fnnls(A.T @ A, A.T @ y, max_outer=2)
     with pytest.raises(RuntimeError):
         oracle.nnls_qr(A, y, max_outer=2)
+    with pytest.raises(RuntimeError):
+        oracle.nnls_lh_update(A, y, max_outer=2)
 
 
 def test_planted_coarse_dependence_test_misses_minimiser(monkeypatch):
