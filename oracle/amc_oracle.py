@@ -353,33 +353,41 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
     free = [a for a in range(t) if u[a] > 0]
     zero = [a for a in range(t) if live[a] and u[a] == 0]
     Mf = _qr_r(np.column_stack([A[:, free + zero], y]))
-    W = np.zeros((t, len(free) + len(zero)))
+    ncol = len(free) + len(zero)  # live columns of W (positions 0..ncol-1)
+    W = np.zeros((t, max(ncol, 1)))
     c = np.zeros(t)
-    W[: Mf.shape[0]] = Mf[:, :-1]
+    W[: Mf.shape[0], :ncol] = Mf[:, :-1]
     c[: Mf.shape[0]] = Mf[:, -1]
     cols = free + zero  # key of each column position
 
     def leave(k, keep):
-        nonlocal W
+        # the free columns after k move down one place (the leaving column
+        # to position f - 1, the first zero place, or out when not kept)
+        nonlocal ncol
         f = len(free)
         key = cols[k]
         colk = W[:, k].copy()
-        W = np.delete(W, k, axis=1)
+        W[:, k: f - 1] = W[:, k + 1: f]
+        W[:, f - 1] = colk
         del cols[k]
+        cols.insert(f - 1, key)
         del free[k]
         if keep:
-            W = np.column_stack([W, colk])
-            cols.append(key)
             zero.append(key)
+        else:  # dropped: to the last live place, then out
+            W[:, [f - 1, ncol - 1]] = W[:, [ncol - 1, f - 1]]
+            cols[f - 1], cols[ncol - 1] = cols[ncol - 1], cols[f - 1]
+            cols.pop()
+            ncol -= 1
         for q in range(k, f - 1):
             a, b = W[q, q], W[q + 1, q]
             r = math.hypot(a, b)
             if r == 0.0:
                 continue
             cs, sn = a / r, b / r
-            top = W[q, q:].copy()
-            W[q, q:] = cs * top + sn * W[q + 1, q:]
-            W[q + 1, q:] = cs * W[q + 1, q:] - sn * top
+            top = W[q, q:ncol].copy()
+            W[q, q:ncol] = cs * top + sn * W[q + 1, q:ncol]
+            W[q + 1, q:ncol] = cs * W[q + 1, q:ncol] - sn * top
             W[q + 1, q] = 0.0
             cq = c[q]
             c[q] = cs * cq + sn * c[q + 1]
@@ -394,7 +402,7 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
             u[a] = 0
             leave(int(dep[0]), False)
             continue
-        z = solve_triangular(W[:f, :f], c[:f]) if f else np.zeros(0)
+        z = solve_triangular(W[:f, :f], c[:f], check_finite=False) if f else np.zeros(0)
         if np.any(z <= 0):
             # step from the feasible u toward z until the first free variable hits zero
             neg = np.flatnonzero(z <= 0)
@@ -412,16 +420,16 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
         u[free] = z
         rz = c[f:]
         nr = float(np.sqrt(np.sum(rz * rz)))
-        nz = len(cols) - f
+        nz = ncol - f
         enter = -1
         if nz and nr > 0:
-            Z = W[f:, f:]
-            den = np.sqrt(np.sum(Z * Z, axis=0))
+            Z = W[f:, f:ncol]
+            den = np.sqrt(np.einsum("ij,ij->j", Z, Z))
             with np.errstate(invalid="ignore", divide="ignore"):
                 cos = np.where(den > DEP_TOL, (rz @ Z) / (den * nr), -np.inf)
             best = np.max(cos)
             if best > COS_TOL:
-                keys = np.asarray(cols[f:])
+                keys = np.asarray(cols[f:ncol])
                 enter = f + int(np.flatnonzero(cos == best)[np.argmin(keys[cos == best])])
         if enter < 0:
             return (u / dg).astype(np.float64)
@@ -439,7 +447,8 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
             v[0] -= alpha
             vtv = float(np.sum(v * v))
             if vtv > 0:
-                W[f:, f:] -= np.outer(v, (v @ W[f:, f:]) * (2 / vtv))
+                B = W[f:, f:ncol]
+                B -= np.multiply.outer(v, (v @ B) * (2 / vtv))
                 c[f:] -= v * ((v @ c[f:]) * (2 / vtv))
                 W[f + 1:, f] = 0.0
     raise RuntimeError(f"nnls_lh_update: no KKT point within {max_outer} iterations")

@@ -98,20 +98,122 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
            "min_margin": float(min(s.margin for s in ref.selection.steps))}
     rep["same_set"] = bool(np.array_equal(np.asarray(ref.sel_idx), sel))
     rep["ck_exact"] = bool(np.array_equal(Ck, np.asarray(K, dtype=np.float64)[sel])) if rep["same_set"] else False
+    P = ref.features.Phi[:, np.asarray(ref.sel_idx)]
+    # the GPU's float64 weights (trace, selection order) in ascending key order
+    order = np.argsort(np.asarray(trace["pick"][h]), kind="stable")
+    w_gpu64 = np.asarray(trace["weight"][h], dtype=np.float64)[order]
+    relres_gpu = float(trace["relres"][h][-1]) if "relres" in trace and len(trace["relres"][h]) else None
+    _judge_weights(rep, Q, K, V, P, ref.features.m, ref.features.Y, ref.w, (ref.Ck, ref.beta, ref.Cv), sel, Ck,
+                   beta, Cv, w_gpu64, relres_gpu, beta_in)
+    rep["ok"] = (not rep["mismatch_iters"] and rep["same_set"] and rep["ck_exact"] and rep["weights_ok"] and
+                 rep["e_mass_diff"] <= ERR_TOL and rep["e_out_diff"] <= ERR_TOL and rep["relres_ok"])
+    rep["t"] = int(t)
+    REPORTS.append(rep)
+    return rep
+
+
+def spot_replay(Q, K, V, t: int, k: int, R: int, res, h: int, cycles, beta_in=None, trace=None, final=True):
+    """Spot replay of one large head at chosen refits (a full replay solves an
+    exact NNLS at every refit, which large budgets cannot afford).  For each
+    refit c in `cycles` (1-based, the refit after iteration c R or after the
+    last one), the oracle takes the GPU's keys through that refit, solves the
+    exact NNLS on them (oracle.nnls_exact, cold), scores every other key by
+    Phi^T r and replays the iterations up to the next refit, all on that
+    residual, under the replay rule (a mismatch needs a key left out to score
+    above a key taken by more than 1e-6 of the top score and by more than the
+    two keys' float64 bounds).  Beside it: the relative residual of the GPU's
+    own refit c (its trace) and the minimum's.  final: after the last refit,
+    the weights and errors on the GPU's key set as in replay_check.  Returns
+    a report; report['ok'] is the verdict."""
+    if trace is None:
+        trace = res.trace()
+    picks = [int(j) for j in trace["pick"][h]]
+    feats = O.mass_features(Q, K, V, beta_in)
+    Phi, m = feats.Phi, feats.m
+    T = Phi.shape[1]
+    nm = float(np.linalg.norm(m))
+    eb = O.score_tie_ulps(Q, K, t, beta_in) * np.finfo(np.float64).eps
+    b_all = np.abs(Phi).T @ np.abs(m)
+    sizes = O.iteration_sizes(t, k, R)
+    refit_at, pos = [], 0
+    for i, (kk, refit) in enumerate(sizes):
+        pos += kk
+        if refit:
+            refit_at.append((pos, i + 1))  # keys through the refit, index of the next iteration
+    relres_tr = trace["relres"][h] if "relres" in trace else []
+    rep = {"t": int(t), "cycles": {}, "mismatch_iters": [], "forced_iters": []}
+    for c in cycles:
+        p, it = refit_at[c - 1]
+        PS = Phi[:, picks[:p]]
+        w = O.nnls_exact(PS, m)
+        r = m - PS @ w
+        cyc = {"keys": p, "relres_min": float(np.linalg.norm(r)) / nm}
+        if c - 1 < len(relres_tr):
+            cyc["relres_gpu"] = float(relres_tr[c - 1])
+        sc = Phi.T @ r
+        selected = np.zeros(T, dtype=bool)
+        selected[picks[:p]] = True
+        pos = p
+        while it < len(sizes):
+            kk, refit = sizes[it]
+            it += 1
+            given = picks[pos: pos + kk]
+            cs = np.where(selected, -np.inf, sc)
+            order = np.lexsort((np.arange(T), -cs))
+            top = float(cs[order[0]])
+            if set(given) != set(int(j) for j in order[:kk]):
+                out = ~selected
+                out[given] = False
+                c_out, b_out = cs[out], b_all[out]
+                thr = MARGIN_TOL * abs(top)
+                resolved = any(np.any((c_out - cs[g] > thr) & (c_out - cs[g] > eb * (b_out + b_all[g])))
+                               for g in given)
+                (rep["mismatch_iters"] if resolved else rep["forced_iters"]).append(it)
+            selected[given] = True
+            pos += kk
+            if refit:
+                break
+        rep["cycles"][c] = cyc
+    rep["weights_ok"], rep["relres_ok"] = True, True
+    rep["e_mass_diff"] = rep["e_out_diff"] = 0.0
+    if final:
+        Ck, beta, Cv, sel = head_outputs(res, h)
+        rep["same_set"] = bool(np.array_equal(np.sort(np.asarray(picks)), sel))
+        P = Phi[:, sel]
+        w_ref = O.nnls_exact(P, m)
+        beta_ref = O.log_weights(w_ref)
+        if beta_in is not None:
+            beta_ref = beta_ref + np.asarray(beta_in, dtype=np.float64)[sel]
+        ref_out = (np.asarray(K, dtype=np.float64)[sel], beta_ref, O.ols_values(P, w_ref, feats.Y))
+        order = np.argsort(np.asarray(picks), kind="stable")
+        w_gpu64 = np.asarray(trace["weight"][h], dtype=np.float64)[order]
+        relres_gpu = float(relres_tr[-1]) if len(relres_tr) else None
+        _judge_weights(rep, Q, K, V, P, m, feats.Y, w_ref, ref_out, sel, Ck, beta, Cv, w_gpu64, relres_gpu, beta_in)
+        rep["ck_exact"] = bool(np.array_equal(Ck, ref_out[0]))
+        REPORTS.append(rep)
+    rep["ok"] = (not rep["mismatch_iters"] and rep["weights_ok"] and rep["relres_ok"] and
+                 rep["e_mass_diff"] <= ERR_TOL and rep["e_out_diff"] <= ERR_TOL and
+                 rep.get("same_set", True) and rep.get("ck_exact", True))
+    return rep
+
+
+def _judge_weights(rep, Q, K, V, P, m, Y, w_ref, ref_out, sel, Ck, beta, Cv, w_gpu64, relres_gpu, beta_in):
+    """The weight and error part of the replay (see the module docstring) for
+    the GPU's key set `sel` (ascending), its outputs (Ck, beta, Cv), its
+    float64 weights w_gpu64 (ascending key order) and the relative residual
+    its trace reports after the last refit, against the oracle's exact
+    minimiser w_ref on the same keys (P = Phi[:, sel]) and the oracle's
+    outputs ref_out = (Ck, beta, Cv).  Fills rep; rep['weights_ok'] is the
+    weight verdict."""
     # weights: the GPU's beta carries beta_in + log w
     bi = np.zeros(len(sel)) if beta_in is None else np.asarray(beta_in, dtype=np.float64)[sel]
     with np.errstate(invalid="ignore"):
         w_gpu = np.where(np.isfinite(beta), np.exp(beta - bi), 0.0)
-    w_ref = ref.w
     act_g, act_r = w_gpu > 0, w_ref > 0
     both = act_g & act_r
-    rep["beta_maxdiff"] = float(np.max(np.abs(beta[both] - ref.beta[both]))) if np.any(both) else 0.0
+    ref_beta = ref_out[1]
+    rep["beta_maxdiff"] = float(np.max(np.abs(beta[both] - ref_beta[both]))) if np.any(both) else 0.0
     rep["one_sided_ok"] = _one_sided_ok(w_gpu, w_ref)
-    P = ref.features.Phi[:, np.asarray(ref.sel_idx)]
-    m = ref.features.m
-    # the GPU's float64 weights (trace, selection order) in ascending key order
-    order = np.argsort(np.asarray(trace["pick"][h]), kind="stable")
-    w_gpu64 = np.asarray(trace["weight"][h], dtype=np.float64)[order]
     res_g = float(np.linalg.norm(m - P @ w_gpu64))
     res_r = float(np.linalg.norm(m - P @ w_ref))
     rep["resid_excess"] = (res_g - res_r) / max(res_r, 1e-300)
@@ -120,19 +222,18 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
     # own weights (float64 residuals on both sides; cancellation leaves about
     # 1e-16 / relres of relative difference)
     rep["relres_ok"] = True
-    if "relres" in trace and len(trace["relres"][h]):
-        rg = float(trace["relres"][h][-1])
+    if relres_gpu is not None:
         want = res_g / float(np.linalg.norm(m))
-        rep["relres_gpu"] = rg
-        rep["relres_ok"] = abs(rg - want) <= 1e-6 * want + 1e-13
+        rep["relres_gpu"] = relres_gpu
+        rep["relres_ok"] = abs(relres_gpu - want) <= 1e-6 * want + 1e-13
     e_gpu = oracle.errors(Q, K, V, Ck, beta, Cv, beta_in)
-    e_ref = oracle.errors(Q, K, V, ref.Ck, ref.beta, ref.Cv, beta_in)
+    e_ref = oracle.errors(Q, K, V, ref_out[0], ref_beta, ref_out[2], beta_in)
     rep["e_gpu"], rep["e_ref"] = e_gpu, e_ref
     rep["e_mass_diff"] = abs(e_gpu[0] - e_ref[0])
     rep["e_out_diff"] = abs(e_gpu[1] - e_ref[1])
     rep["fallback"] = False
     rep["beta_envelope"] = None
-    rep["reference"] = (ref.Ck, ref.beta, ref.Cv)  # the compaction the GPU's errors are compared with
+    rep["reference"] = ref_out  # the compaction the GPU's errors are compared with
     weights_ok = rep["beta_maxdiff"] <= BETA_TOL and rep["one_sided_ok"]
     if not weights_ok:
         # Is beta determined by the float64 data?  Not when the columns of
@@ -160,17 +261,13 @@ def replay_check(Q, K, V, t: int, k: int, R: int, res, h: int, beta_in=None, tra
             # the minimisers form a face and the value fit depends on which
             # point of it the weights are: the oracle's own value fit, taken on
             # the GPU's weights, is the reference for the GPU's errors
-            Cv_face = O.ols_values(P, w_gpu64, ref.features.Y)
+            Cv_face = O.ols_values(P, w_gpu64, Y)
             e_face = oracle.errors(Q, K, V, Ck, beta, Cv_face, beta_in)
             rep["e_face"] = e_face
             rep["reference"] = (Ck, beta, Cv_face)
             rep["e_mass_diff"] = abs(e_gpu[0] - e_face[0])
             rep["e_out_diff"] = abs(e_gpu[1] - e_face[1])
-    rep["ok"] = (not rep["mismatch_iters"] and rep["same_set"] and rep["ck_exact"] and weights_ok and
-                 rep["e_mass_diff"] <= ERR_TOL and rep["e_out_diff"] <= ERR_TOL and rep["relres_ok"])
-    rep["t"] = int(t)
-    REPORTS.append(rep)
-    return rep
+    rep["weights_ok"] = bool(weights_ok)
 
 
 def _one_sided_ok(wa, wb):
