@@ -212,6 +212,8 @@ def _qr_r(M):
 COS_TOL = 1e-10
 DEP_TOL = 1e-12
 KKT_ACCEPT = 1e-8  # largest relative KKT violation of scipy's Lawson-Hanson result kept by nnls_exact
+STALL_ENTERS = 64  # nnls_lh_update: entering steps over which ...
+STALL_REL = 1e-15  # ... the residual must fall by more than this fraction of |m| to go on
 
 
 def nnls_qr(PhiS, m, w0=None, max_outer=None, dtype=np.float64):
@@ -308,7 +310,7 @@ def nnls_qr(PhiS, m, w0=None, max_outer=None, dtype=np.float64):
     raise RuntimeError(f"nnls_qr: no KKT point within {max_outer} iterations")
 
 
-def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
+def nnls_lh_update(PhiS, m, w0=None, max_outer=None, dtype=np.float64):
     """nnls_qr's Lawson-Hanson iteration, step for step, with the factor of
     the columns ordered [free | zero] and y kept from one iteration to the
     next instead of recomputed (the same algorithm: p1 section 1.6, the NNLS
@@ -328,37 +330,57 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
       dropped.
     Norms of the zero columns below row f and their inner products with c
     there do not depend on Q, so the entering test is nnls_qr's; ties go to
-    the lower key, as there.
+    the lower key, as there.  Near a degenerate minimiser float64 can keep
+    swapping columns at the rounding level (each entering column's cosine
+    near 1e-6, the residual moving in its twelfth digit, far below the
+    resolution eps |m| of a float64 residual): once STALL_ENTERS entering
+    steps have lowered the residual by less than STALL_REL |m|, the iterate
+    is the minimiser to float64 resolution and the iteration stops there.
+    ``dtype``: arithmetic of the solve (numpy.longdouble for an
+    extended-precision cross-check; STALL_REL then scales with its epsilon).
     """
     from scipy.linalg import solve_triangular
 
-    A0 = np.asarray(PhiS, dtype=np.float64)
-    y0 = np.asarray(m, dtype=np.float64)
+    A0 = np.asarray(PhiS, dtype=dtype)
+    y0 = np.asarray(m, dtype=dtype)
+    wide = np.dtype(dtype) != np.float64
+    stall = STALL_REL * float(np.finfo(dtype).eps / np.finfo(np.float64).eps)
+
+    def back_sub(Tm, b):
+        if not wide:
+            return solve_triangular(Tm, b, check_finite=False)
+        z = np.zeros(len(b), dtype=dtype)
+        for i in range(len(b) - 1, -1, -1):
+            z[i] = (b[i] - Tm[i, i + 1:] @ z[i + 1:]) / Tm[i, i]
+        return z
+
     n, t = A0.shape
     dg = np.sqrt(np.sum(A0 * A0, axis=0))
     live = dg > 0
     dg = np.where(live, dg, 1)
     R = _qr_r(np.column_stack([A0 / dg, y0]))
-    A = np.zeros((t, t))
-    y = np.zeros(t)
+    A = np.zeros((t, t), dtype=dtype)
+    y = np.zeros(t, dtype=dtype)
     k0 = min(R.shape[0], t)
     A[:k0] = R[:k0, :t]
     y[:k0] = R[:k0, t]
     if max_outer is None:
         max_outer = 3 * t + 30
-    u = np.zeros(t)
+    u = np.zeros(t, dtype=dtype)
     if w0 is not None:
-        u[: len(w0)] = np.maximum(np.asarray(w0, dtype=np.float64), 0) * dg[: len(w0)]
+        u[: len(w0)] = np.maximum(np.asarray(w0, dtype=dtype), 0) * dg[: len(w0)]
     u[~live] = 0
     free = [a for a in range(t) if u[a] > 0]
     zero = [a for a in range(t) if live[a] and u[a] == 0]
     Mf = _qr_r(np.column_stack([A[:, free + zero], y]))
     ncol = len(free) + len(zero)  # live columns of W (positions 0..ncol-1)
-    W = np.zeros((t, max(ncol, 1)))
-    c = np.zeros(t)
+    W = np.zeros((t, max(ncol, 1)), dtype=dtype)
+    c = np.zeros(t, dtype=dtype)
     W[: Mf.shape[0], :ncol] = Mf[:, :-1]
     c[: Mf.shape[0]] = Mf[:, -1]
     cols = free + zero  # key of each column position
+    hist = []  # residual norm at each feasible solve
+    ym = np.sqrt(np.sum(y0 * y0))
 
     def leave(k, keep):
         # the free columns after k move down one place (the leaving column
@@ -381,7 +403,7 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
             ncol -= 1
         for q in range(k, f - 1):
             a, b = W[q, q], W[q + 1, q]
-            r = math.hypot(a, b)
+            r = np.hypot(a, b)
             if r == 0.0:
                 continue
             cs, sn = a / r, b / r
@@ -402,7 +424,7 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
             u[a] = 0
             leave(int(dep[0]), False)
             continue
-        z = solve_triangular(W[:f, :f], c[:f], check_finite=False) if f else np.zeros(0)
+        z = back_sub(W[:f, :f], c[:f]) if f else np.zeros(0, dtype=dtype)
         if np.any(z <= 0):
             # step from the feasible u toward z until the first free variable hits zero
             neg = np.flatnonzero(z <= 0)
@@ -419,8 +441,11 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
         u[:] = 0
         u[free] = z
         rz = c[f:]
-        nr = float(np.sqrt(np.sum(rz * rz)))
+        nr = np.sqrt(np.sum(rz * rz))
         nz = ncol - f
+        hist.append(nr)
+        if len(hist) > STALL_ENTERS and hist[-1 - STALL_ENTERS] - nr <= stall * ym:
+            return (u / dg).astype(np.float64)
         enter = -1
         if nz and nr > 0:
             Z = W[f:, f:ncol]
@@ -440,12 +465,12 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None):
         zero.remove(key)
         free.append(key)
         x = W[f:, f]
-        nrm = float(np.sqrt(np.sum(x * x)))
+        nrm = np.sqrt(np.sum(x * x))
         if nrm > 0 and f + 1 < t:
             alpha = -nrm if x[0] >= 0 else nrm
             v = x.copy()
             v[0] -= alpha
-            vtv = float(np.sum(v * v))
+            vtv = np.sum(v * v)
             if vtv > 0:
                 B = W[f:, f:ncol]
                 B -= np.multiply.outer(v, (v @ B) * (2 / vtv))

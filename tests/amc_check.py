@@ -17,7 +17,9 @@ they are: (i) the columns of the two supports together must have full
 numerical rank (relative smallest singular value above NULL_SV; below it the
 minimisers form a face and both weight vectors lie on it), and (ii) the same
 NNLS solved again in extended precision (long double, warm-started from the
-oracle's float64 minimiser) must not move beta past the tolerance.  Only
+oracle's float64 minimiser; above LD_MAX_T keys, which that solve cannot
+afford, the same NNLS in float64 on data moved by its own rounding, a
+relative 2^-52 per entry) must not move beta past the tolerance.  Only
 where one of these fails are the GPU's weights held to the minimum value
 instead: their NNLS residual within 1e-6 (relative) of the oracle's, and its
 errors to those of the oracle's own value fit on the GPU's weights (the value
@@ -44,7 +46,7 @@ ERR_TOL = 1e-3
 WEIGHT_REL = 1e-6
 RESID_REL = 1e-6
 FALLBACK_SHARE = 0.25  # largest share of a test's heads held to the minimum value only
-LD_MAX_T = 512  # largest budget the extended-precision envelope is computed for
+LD_MAX_T = 512  # largest budget the extended-precision envelope is computed for (then: rounding-level data)
 NULL_SV = 1e-10  # relative singular value below which columns count as dependent
 
 REPORTS = []  # every replay report of the session (summarised at its end by conftest)
@@ -247,13 +249,20 @@ def _judge_weights(rep, Q, K, V, P, m, Y, w_ref, ref_out, sel, Ck, beta, Cv, w_g
         sv = np.linalg.svd(Pu / np.where(nrm > 0, nrm, 1.0), compute_uv=False) if Pu.shape[1] else np.ones(1)
         # more columns than queries: dependent whatever the singular values say
         rep["union_sv_min"] = float(sv[-1] / sv[0]) if Pu.shape[1] <= Pu.shape[0] else 0.0
-        env = None
         if len(w_ref) <= LD_MAX_T:
             w_ld = O.nnls_qr(P, m, w0=w_ref, dtype=np.longdouble)
-            both_o = (w_ref > 0) & (w_ld > 0)
-            env = float(np.max(np.abs(np.log(w_ref[both_o]) - np.log(w_ld[both_o])))) if np.any(both_o) else 0.0
-            if not _one_sided_ok(w_ld, w_ref):
-                env = float("inf")
+        else:
+            # past the size an extended-precision solve affords: the same
+            # NNLS on data moved by its float64 rounding (each entry of Phi_S
+            # and m by a relative 2^-52, seeded), warm-started at the minimiser
+            rng = np.random.default_rng(len(w_ref))
+            eps = np.finfo(np.float64).eps
+            w_ld = O.nnls_exact(P * (1 + eps * rng.uniform(-1, 1, P.shape)), m * (1 + eps * rng.uniform(-1, 1, m.shape)),
+                                w_prev=w_ref)
+        both_o = (w_ref > 0) & (w_ld > 0)
+        env = float(np.max(np.abs(np.log(w_ref[both_o]) - np.log(w_ld[both_o])))) if np.any(both_o) else 0.0
+        if not _one_sided_ok(w_ld, w_ref):
+            env = float("inf")
         rep["beta_envelope"] = env
         if rep["union_sv_min"] < NULL_SV or (env is not None and env > BETA_TOL):
             rep["fallback"] = True

@@ -284,14 +284,16 @@ def test_nnls_lh_update_follows_nnls_qr():
 
 def test_nnls_lh_update_kkt_at_large_budget():
     """At t = 1000 of a real head (2048 queries) the updating solver reaches
-    a KKT point of the refit to float64 resolution, and agrees with the
-    refactoring solver's minimum at t = 300 on the same head."""
+    a KKT point of the refit (violation below 1e-10, a hundredth of what
+    nnls_exact accepts from scipy; the stall stop ends it once 64 entering
+    steps gain less than 1e-15 of |m|), and agrees with the refactoring
+    solver's minimum at t = 300 on the same head."""
     h = synth.make_head([45, 0], 2048, 4096, 128, True, "bf16")
     f = oracle.mass_features(h.Q, h.K, h.V)
     order = np.argsort(-O.highest_scores(f.Phi, f.m), kind="stable")
     P = f.Phi[:, order[:1000]]
     w = oracle.nnls_lh_update(P, f.m)
-    assert O.nnls_kkt_violation(P.T @ P, P.T @ f.m, w) < 1e-12
+    assert O.nnls_kkt_violation(P.T @ P, P.T @ f.m, w) < 1e-10
     P3 = f.Phi[:, order[:300]]
     w3, q3 = oracle.nnls_lh_update(P3, f.m), oracle.nnls_qr(P3, f.m)
     assert abs(_objective(P3, f.m, w3) / _objective(P3, f.m, q3) - 1) < 1e-9
