@@ -333,9 +333,11 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None, dtype=np.float64):
     the lower key, as there.  Near a degenerate minimiser float64 can keep
     swapping columns at the rounding level (each entering column's cosine
     near 1e-6, the residual moving in its twelfth digit, far below the
-    resolution eps |m| of a float64 residual): once STALL_ENTERS entering
-    steps have lowered the residual by less than STALL_REL |m|, the iterate
-    is the minimiser to float64 resolution and the iteration stops there.
+    resolution eps |m| of a float64 residual) until the iteration cap: there,
+    when the last STALL_ENTERS entering steps lowered the residual by less
+    than STALL_REL |m|, the iterate is the minimiser to float64 resolution
+    and is returned (otherwise the cap is an error).  Every other run ends
+    where nnls_qr's does.
     ``dtype``: arithmetic of the solve (numpy.longdouble for an
     extended-precision cross-check; STALL_REL then scales with its epsilon).
     """
@@ -444,8 +446,6 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None, dtype=np.float64):
         nr = np.sqrt(np.sum(rz * rz))
         nz = ncol - f
         hist.append(nr)
-        if len(hist) > STALL_ENTERS and hist[-1 - STALL_ENTERS] - nr <= stall * ym:
-            return (u / dg).astype(np.float64)
         enter = -1
         if nz and nr > 0:
             Z = W[f:, f:ncol]
@@ -476,6 +476,8 @@ def nnls_lh_update(PhiS, m, w0=None, max_outer=None, dtype=np.float64):
                 B -= np.multiply.outer(v, (v @ B) * (2 / vtv))
                 c[f:] -= v * ((v @ c[f:]) * (2 / vtv))
                 W[f + 1:, f] = 0.0
+    if len(hist) > STALL_ENTERS and hist[-1 - STALL_ENTERS] - hist[-1] <= stall * ym:
+        return (u / dg).astype(np.float64)  # swapping at the rounding level (see above)
     raise RuntimeError(f"nnls_lh_update: no KKT point within {max_outer} iterations")
 
 
