@@ -50,6 +50,7 @@ def test_varlen_2048_key_head():
     _say(f"varlen head {h}: t=2048 T={w.T} n={w.n}")
     res = _compact([head], [2048], w.topk, w.refit_every)
     rep = spot_replay(head.Q, head.K, head.V, 2048, w.topk, w.refit_every, res, 0, [1, 64, 128, 192])
+    amc_check.REPORTS.remove(rep)  # a recorded limitation, not parity evidence: out of the session summary
     _report(f"varlen head {h}", rep)
     assert rep["ok"], rep
 
