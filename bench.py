@@ -388,6 +388,9 @@ def main():
                     help="NNLS refits through the orthogonal factorisation: every head it takes, heads the "
                          "Gram solver flags, none")
     ap.add_argument("--no-highest", action="store_true", help="leave out the AM-Highest line")
+    ap.add_argument("--recompute", action="store_true",
+                    help="workloads 1, 2, 4: Phi recomputed in every sweep instead of stored (the mode the 60k-token "
+                         "stack takes past its Phi budget), timed on the same inputs; no kernel pass or roofline")
     ap.add_argument("--no-timer", action="store_true", help="skip the kernel pass (per-kernel events, roofline)")
     ap.add_argument("--head-groups", type=int, default=0,
                     help="head groups (streams) of the timed steps; 0: the library's choice")
@@ -453,8 +456,12 @@ def main():
     select = "omp" if (w.topk == 1 and w.refit_every == 1) else "batched"
     kw = dict(cu_q=cu_q, cu_k=cu_k, select=select, topk=w.topk, refit_every=w.refit_every,
               exact_refit=args.exact_refit)
+    if args.recompute:
+        kw["phi_budget_bytes"] = 0
+        args.no_timer = True
     ws_bytes = amc.compact_workspace_bytes(cu_q, cu_k, w.budgets, w.d, tdt, select=select, topk=w.topk,
-                                           refit_every=w.refit_every, exact_refit=args.exact_refit)
+                                           refit_every=w.refit_every, exact_refit=args.exact_refit,
+                                           phi_budget_bytes=kw.get("phi_budget_bytes"))
     workspace = torch.empty(ws_bytes + 256, dtype=torch.uint8, device=dev)
     timer = None if args.no_timer else amc.Timer()
 
@@ -585,7 +592,8 @@ def main():
         "config": {"workload": w.name, "heads": H, "T": w.T, "n": w.n, "d": w.d,
                    "budget": w.budgets[0] if len(set(w.budgets)) == 1 else
                    f"{min(w.budgets)}..{max(w.budgets)} (sum {sum(w.budgets)})",
-                   "topk": w.topk, "refit_every": w.refit_every, "parallelism": "none (one GPU)"},
+                   "topk": w.topk, "refit_every": w.refit_every, "parallelism": "none (one GPU)",
+                   "phi": "recomputed in every sweep" if args.recompute else "stored (two 16-bit planes)"},
         "roofline": roofline,
         "roofline_next": roofline_other,
         "cpu_baseline": cpu,
