@@ -23,7 +23,7 @@ AMC_F32, AMC_BF16 = 0, 1
 AMC_SEL_OMP, AMC_SEL_OMP_BATCHED, AMC_SEL_HIGHEST = 0, 1, 2
 AMC_FLAG_TRACE = 1
 HS_CHOL_JITTER, HS_NNLS_CAP, HS_NONFINITE, HS_NNLS_SINGULAR, HS_NNLS_QR = 1, 2, 4, 8, 16
-EXACT_REFIT = {"auto": 0, "gated": 1, "never": 2}
+EXACT_REFIT = {"auto": 3, "cold": 0, "gated": 1, "never": 2}
 
 KERNEL_CLASSES = ["init", "shift", "phi", "sweep", "merge", "panel", "gram", "nnls", "resid",
                   "ols_normal", "ols_solve", "pack", "sweep_exact", "rescore", "prune", "digits", "phi_f64"]

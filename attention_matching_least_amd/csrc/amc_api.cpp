@@ -113,7 +113,7 @@ static amc_status check_options(const amc_options *o) {
   if (o->nnls_max_iters < 0 || o->nnls_polish < 0 || o->nnls_polish > 8) return AMC_ERR_INVALID_ARG;
   if (o->head_groups < 0 || o->head_groups > 16) return AMC_ERR_INVALID_ARG;
   if (o->head_groups > 8) return AMC_ERR_UNSUPPORTED;
-  if (o->exact_refit < 0 || o->exact_refit > 2) return AMC_ERR_INVALID_ARG;
+  if (o->exact_refit < 0 || o->exact_refit > 3) return AMC_ERR_INVALID_ARG;
   if (o->digits_in_panel != 0 && o->digits_in_panel != 1) return AMC_ERR_INVALID_ARG;
   if (!(o->nnls_tol >= 0.0) || !std::isfinite(o->nnls_tol)) return AMC_ERR_INVALID_ARG;
   if (o->cv_dtype != AMC_F32 && o->cv_dtype != AMC_BF16) return AMC_ERR_INVALID_ARG;
@@ -475,7 +475,7 @@ void amc_default_options(amc_options *o) {
   o->phi_budget_bytes = 64ull << 30;
   o->cv_dtype = AMC_F32;
   o->head_groups = 0;
-  o->exact_refit = 0;
+  o->exact_refit = 3;
   o->digits_in_panel = 1;
   o->flags = 0;
   o->timer = nullptr;
@@ -662,9 +662,11 @@ static amc_status compact_impl(const amc_problem *p, const amc_options *o, const
   if (b.tr_swept && !pl.store_phi) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.tr_swept, pl.sum_cycles, 0, stream));
   if (b.tr_swept8) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.tr_swept8, pl.sum_cycles, 0, stream));
   if (b.q8_bad) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.q8_bad, dm.H, 0, stream));
-  // exact refit: 2 sends every eligible head there from its first refit; 0
-  // leaves it to the Gram solver until that flags the head
-  if (b.qr_flag) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.qr_flag, dm.H, o->exact_refit == 0 ? 2 : 0, stream));
+  // exact refit: 2 sends every eligible head there from its first refit
+  // (with bit 8, the Gram solver runs first and gives each refit its warm
+  // start); 0 leaves it to the Gram solver until that flags the head
+  const int qr_init = o->exact_refit == 0 ? 2 : o->exact_refit == 3 ? 2 | 8 : 0;
+  if (b.qr_flag) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.qr_flag, dm.H, qr_init, stream));
   if (b.qr_built) AMC_LAUNCH(AMC_K_INIT, launch_fill_i32(b.qr_built, dm.H, 0, stream));
 
   // The heads run in groups, each on a stream of its own (the caller's for the

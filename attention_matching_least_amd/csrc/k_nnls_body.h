@@ -1414,7 +1414,11 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
   if ((D.t > kNnlsLdsT) != kGlobal) return;
   // heads whose refits went to the orthogonal-factorisation path stay there
   const bool qr_ok = qr_flag && D.qr_off >= 0;
-  if (qr_ok && qr_flag[h] >= 2) return;
+  const int qf = qr_ok ? qr_flag[h] : 0;
+  // qr_flag bit 8: the exact refit follows every refit of this head and starts
+  // from this refit's weights (which serve only as its warm start)
+  const bool warm_only = (qf & 8) != 0;
+  if (qf >= 2 && !warm_only) return;
   int64_t S0;
   int Kc;
   if (polish) {
@@ -1492,7 +1496,7 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
   // every later one of the head go to the orthogonal-factorisation path, which
   // reports its own status.
   bool gate = false;
-  if (qr_ok && tol > 0.0) {
+  if (qr_ok && !warm_only && tol > 0.0) {
     gate = (sh_status & int(AMC_HS_NNLS_CAP | AMC_HS_NNLS_SINGULAR)) != 0;
     if (!gate && S0 > 0 && rpart) {
       double rr = 0.0, mm = 0.0;
@@ -1507,7 +1511,7 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
     nn_np[h] = np;
     if (tr_iters && !polish) tr_iters[D.cyc_off + cycle] = iters;
     if (gate) qr_flag[h] = 1;
-    else if (sh_status && head_status) atomicOr(head_status + h, sh_status);
+    else if (sh_status && head_status && !warm_only) atomicOr(head_status + h, sh_status);
   }
   if (tr_weight)
     for (int a = tid; a < p; a += NT) tr_weight[D.t_off + a] = S.u[a] / S.dg[a];

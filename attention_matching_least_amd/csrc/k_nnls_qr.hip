@@ -253,21 +253,40 @@ template <int RPT, int CW>
 __device__ __forceinline__ void apply_block(double (&X)[RPT][CW], const double *V, const double *Tc, int n,
                                             int c0, int len, AppendLds &L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-#pragma unroll 1
-  for (int l = 0; l < len; ++l) {
-    const double *vr = V + int64_t(c0 + l) * n;
-    double acc[CW];
+  // the reflection vectors come in groups of kVg, every load of a group
+  // issued before its products (one memory latency per group, not per vector)
+  constexpr int kVg = 4;
+  double vb[kVg][RPT];
+  auto load_group = [&](int l0) {
 #pragma unroll
-    for (int k = 0; k < CW; ++k) acc[k] = 0.0;
+    for (int u = 0; u < kVg; ++u) {
+      const int l = l0 + u < len ? l0 + u : l0;  // a vector past len reads an existing row, unused
+      const double *vr = V + int64_t(c0 + l) * n;
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const int i = tid + r * NA;
-      const double v = i < n ? vr[i] : 0.0;
-#pragma unroll
-      for (int k = 0; k < CW; ++k) acc[k] = fma(v, X[r][k], acc[k]);
+      for (int r = 0; r < RPT; ++r) {
+        const int i = tid + r * NA;
+        vb[u][r] = i < n ? vr[i] : 0.0;
+      }
     }
-    const double s = wave_sum_scatter<CW>(acc);
-    if ((lane & (64 / CW - 1)) == 0) L.wpart[wave][l][lane / (64 / CW)] = s;
+  };
+#pragma unroll 1
+  for (int l0 = 0; l0 < len; l0 += kVg) {
+    load_group(l0);
+#pragma unroll
+    for (int u = 0; u < kVg; ++u) {
+      const int l = l0 + u;
+      if (l >= len) break;  // same for every thread
+      double acc[CW];
+#pragma unroll
+      for (int k = 0; k < CW; ++k) acc[k] = 0.0;
+#pragma unroll
+      for (int r = 0; r < RPT; ++r) {
+#pragma unroll
+        for (int k = 0; k < CW; ++k) acc[k] = fma(vb[u][r], X[r][k], acc[k]);
+      }
+      const double s = wave_sum_scatter<CW>(acc);
+      if ((lane & (64 / CW - 1)) == 0) L.wpart[wave][l][lane / (64 / CW)] = s;
+    }
   }
   __syncthreads();
   if (tid < len * CW) {
@@ -285,14 +304,17 @@ __device__ __forceinline__ void apply_block(double (&X)[RPT][CW], const double *
   }
   __syncthreads();
 #pragma unroll 1
-  for (int l = 0; l < len; ++l) {
-    const double *vr = V + int64_t(c0 + l) * n;
+  for (int l0 = 0; l0 < len; l0 += kVg) {
+    load_group(l0);
 #pragma unroll
-    for (int r = 0; r < RPT; ++r) {
-      const int i = tid + r * NA;
-      const double v = i < n ? vr[i] : 0.0;
+    for (int u = 0; u < kVg; ++u) {
+      const int l = l0 + u;
+      if (l >= len) break;  // same for every thread
 #pragma unroll
-      for (int k = 0; k < CW; ++k) X[r][k] = fma(-v, L.Zl[l][k], X[r][k]);
+      for (int r = 0; r < RPT; ++r) {
+#pragma unroll
+        for (int k = 0; k < CW; ++k) X[r][k] = fma(-vb[u][r], L.Zl[l][k], X[r][k]);
+      }
     }
   }
 }
@@ -1082,8 +1104,9 @@ __global__ __launch_bounds__(NQ) void k_nnls_qr(const HeadDesc *__restrict__ des
   L.perm = reinterpret_cast<int *>(lds + 4 * p);
   L.zslot = L.perm + p;
   // warm start: the weights of the previous refit; a head flagged by the Gram
-  // solver at this refit also has its weights for the new keys
-  const int nwarm = (flag & 3) == 1 ? p : int(S0);
+  // solver at this refit, or whose every refit the Gram solver runs first
+  // (flag bit 8), also has its weights for the new keys
+  const int nwarm = ((flag & 3) == 1 || (flag & 8)) ? p : int(S0);
   const double *Gh = G + D.tt_off;
   LhResult R;
   if (!lh_solve<true>(lds + 5 * p, int64_t(lds_words) - 5 * p, D, St, Gh, w, p, nwarm, L, R)) {
@@ -1099,7 +1122,7 @@ __global__ __launch_bounds__(NQ) void k_nnls_qr(const HeadDesc *__restrict__ des
   // the value fit leaves the normal equations when the free columns are
   // nearly dependent: smallest pivot of the free block below 1e-6
   if (lane == 0) {
-    qr_flag[h] = 2 | (((flag & 4) || (polish && R.pmin < kOlsPivot)) ? 4 : 0);
+    qr_flag[h] = 2 | (flag & 8) | (((flag & 4) || (polish && R.pmin < kOlsPivot)) ? 4 : 0);
     if (tr_iters && !polish) tr_iters[D.cyc_off + cycle] = R.iters;
     if (head_status) atomicOr(head_status + h, R.status | int(AMC_HS_NNLS_QR));
   }

@@ -384,9 +384,10 @@ def main():
     ap.add_argument("--no-long", action="store_true",
                     help="leave out the 60k-token stack's key-selection seconds (run by default with workload 2)")
     ap.add_argument("--workers", type=int, default=min(16, len(os.sched_getaffinity(0))))
-    ap.add_argument("--exact-refit", default="auto", choices=["auto", "gated", "never"],
-                    help="NNLS refits through the orthogonal factorisation: every head it takes, heads the "
-                         "Gram solver flags, none")
+    ap.add_argument("--exact-refit", default="auto", choices=["auto", "cold", "gated", "never"],
+                    help="NNLS refits through the orthogonal factorisation: every head it takes, warm-started by "
+                         "the Gram solver; every head it takes, warm-started by the previous refit; heads the "
+                         "Gram solver flags; none")
     ap.add_argument("--no-highest", action="store_true", help="leave out the AM-Highest line")
     ap.add_argument("--recompute", action="store_true",
                     help="workloads 1, 2, 4: Phi recomputed in every sweep instead of stored (the mode the 60k-token "

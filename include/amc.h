@@ -157,7 +157,11 @@ typedef struct {
                            * fitted (zhichai.net deep-dive, section 1.6; xinfinite.net
                            * article, section 2, steps 2 and 3).  Heads with budget up to
                            * 640 and at most 8192 queries only; the others keep the Gram form.
-                           * 0 (default): every such head, from its first refit;
+                           * 3 (default): every such head, from its first refit, each refit
+                           * warm-started from the Gram solver's weights for the same keys
+                           * (run first; the same minimiser, reached in fewer active-set
+                           * steps); 0: every such head, from its first refit, warm-started
+                           * from the previous refit's weights only;
                            * 1: a head moves there, for the rest of the call, at the first
                            * refit whose last relative mass residual is below 1e-6 or whose
                            * Gram solve met a singular candidate or the iteration cap (faster

@@ -104,7 +104,7 @@ def test_invalid_options_are_rejected():
     for g in (9, 16):  # inside the range, not run by this build
         o = amc.make_options(head_groups=g)
         assert L.amc_workspace_size(ctypes.byref(p), ctypes.byref(o), ctypes.byref(out)) == amc.AMC_ERR_UNSUPPORTED
-    for fld, bad in (("exact_refit", 3), ("exact_refit", -1), ("digits_in_panel", 2)):
+    for fld, bad in (("exact_refit", 4), ("exact_refit", -1), ("digits_in_panel", 2), ("nnls_polish", 9)):
         o = amc.make_options()
         setattr(o, fld, bad)
         assert L.amc_workspace_size(ctypes.byref(p), ctypes.byref(o), ctypes.byref(out)) == amc.AMC_ERR_INVALID_ARG

@@ -441,6 +441,34 @@ def test_compact_recompute_sweep(dtype, d, k, R):
     assert_fallback_share(reps)
 
 
+@pytest.mark.parametrize("k,R,d", [(1, 1, 128), (4, 2, 128), (1, 1, 64)])
+def test_exact_refit_cold_start(k, R, d):
+    """exact_refit 'cold': the orthogonal-factorisation refit starts from the
+    previous refit's weights alone (by default the Gram solver runs first at
+    every refit and gives it a warm start).  The minimiser is the same, so the
+    bar is the default path's: ragged heads with a key bias, budgets to t/n =
+    0.78 (where the Gram form alone settles short of the minimum), and at
+    d = 64 the nearly collinear selection of the recompute test (cond(Phi_S)
+    1e8)."""
+    shapes = [(300, 700, 40), (129, 257, 23), (200, 1000, 64), (512, 1024, 400)]
+    heads = [synth.make_head([34, i], n, T, d, True, "bf16") for i, (n, T, _) in enumerate(shapes)]
+    budgets = [t for _, _, t in shapes]
+    betas = [synth.random_beta([35, i], T, 1.0) for i, (_, T, _) in enumerate(shapes)]
+    _say(f"cold-started exact refit k={k} R={R} d={d}")
+    res = _run(heads, budgets, "bf16", k, R, beta_in=betas, exact_refit="cold")
+    hs = res.head_status.cpu().numpy()
+    _say(f"head status {hs}")
+    assert np.all(hs & ~amc.HS_NNLS_QR == 0), hs
+    assert np.all(hs & amc.HS_NNLS_QR), hs
+    tr = res.trace()
+    reps = []
+    for i, h in enumerate(heads):
+        rep = replay_check(h.Q, h.K, h.V, budgets[i], k, R, res, i, beta_in=betas[i], trace=tr)
+        _assert_ok(rep, f"head{i}")
+        reps.append(rep)
+    assert_fallback_share(reps)
+
+
 _DIGIT_SHAPES = [(512, 1024, 400), (384, 768, 360)]
 
 
