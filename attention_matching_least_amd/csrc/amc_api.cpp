@@ -199,6 +199,8 @@ static amc_status make_plan(const amc_problem *p, const amc_options *o, bool fea
     dm.max_T = std::max(dm.max_T, D.T);
     dm.max_t = std::max(dm.max_t, D.t);
     dm.min_t = h == 0 ? D.t : std::min(dm.min_t, D.t);
+    dm.n_lo = h == 0 ? D.n : std::min(dm.n_lo, D.n);
+    dm.n_hi = std::max(dm.n_hi, D.n);
     dm.max_sblk = std::max(dm.max_sblk, D.n_sblk);
     dm.max_cblk = std::max(dm.max_cblk, D.n_cblk);
     pl.max_cycles = std::max(pl.max_cycles, cycles);
@@ -717,7 +719,13 @@ static amc_status compact_impl(const amc_problem *p, const amc_options *o, const
     Dims dg = dm;
     dg.H = h1 - h0;
     int64_t cycles = 0;
-    for (int h = h0; h < h1; ++h) cycles = std::max(cycles, ceil_div(pl.desc[size_t(h)].t, pl.kR));
+    dg.n_lo = pl.desc[size_t(h0)].n;
+    dg.n_hi = 0;
+    for (int h = h0; h < h1; ++h) {
+      cycles = std::max(cycles, ceil_div(pl.desc[size_t(h)].t, pl.kR));
+      dg.n_lo = std::min(dg.n_lo, pl.desc[size_t(h)].n);
+      dg.n_hi = std::max(dg.n_hi, pl.desc[size_t(h)].n);
+    }
     result = [&]() -> amc_status {
       hipStream_t stream = gs[size_t(g)];
       // the shift, value tiles and digit rows of a group run beside the

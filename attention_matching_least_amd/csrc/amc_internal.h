@@ -165,6 +165,8 @@ struct Dims {
   int in_bf16;         // 1: Q/K/V are bfloat16, 0: float32
   double scale;
   int64_t max_n, max_T, max_t, min_t;
+  int64_t n_lo, n_hi;  // fewest and most queries of the heads a launch covers (the exact refit
+                       // launches one kernel per class of n)
   int64_t max_sblk, max_cblk, max_qblk;
   int band_cap;        // largest band the rescoring takes (<= kBandCap)
   int64_t qb128;       // 128-query blocks of the longest head (column sums per key)

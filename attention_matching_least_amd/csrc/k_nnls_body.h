@@ -1454,7 +1454,7 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
       static_for<0, 8>([&](auto U) {
         constexpr int u = decltype(U)::value;
         const int e = e0 + u * NT + tid;
-        v[u] = e < ne ? Lg[e] : 0.0;
+        v[u] = Lg[e < ne ? e : ne - 1];  // unconditional load; the store below is guarded
       });
       static_for<0, 8>([&](auto U) {
         constexpr int u = decltype(U)::value;

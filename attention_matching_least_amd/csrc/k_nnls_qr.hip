@@ -253,40 +253,21 @@ template <int RPT, int CW>
 __device__ __forceinline__ void apply_block(double (&X)[RPT][CW], const double *V, const double *Tc, int n,
                                             int c0, int len, AppendLds &L) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // the reflection vectors come in groups of kVg, every load of a group
-  // issued before its products (one memory latency per group, not per vector)
-  constexpr int kVg = 4;
-  double vb[kVg][RPT];
-  auto load_group = [&](int l0) {
-#pragma unroll
-    for (int u = 0; u < kVg; ++u) {
-      const int l = l0 + u < len ? l0 + u : l0;  // a vector past len reads an existing row, unused
-      const double *vr = V + int64_t(c0 + l) * n;
-#pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-        const int i = tid + r * NA;
-        vb[u][r] = i < n ? vr[i] : 0.0;
-      }
-    }
-  };
 #pragma unroll 1
-  for (int l0 = 0; l0 < len; l0 += kVg) {
-    load_group(l0);
+  for (int l = 0; l < len; ++l) {
+    const double *vr = V + int64_t(c0 + l) * n;
+    double acc[CW];
 #pragma unroll
-    for (int u = 0; u < kVg; ++u) {
-      const int l = l0 + u;
-      if (l >= len) break;  // same for every thread
-      double acc[CW];
+    for (int k = 0; k < CW; ++k) acc[k] = 0.0;
 #pragma unroll
-      for (int k = 0; k < CW; ++k) acc[k] = 0.0;
+    for (int r = 0; r < RPT; ++r) {
+      const int i = tid + r * NA;
+      const double v = i < n ? vr[i] : 0.0;
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-#pragma unroll
-        for (int k = 0; k < CW; ++k) acc[k] = fma(vb[u][r], X[r][k], acc[k]);
-      }
-      const double s = wave_sum_scatter<CW>(acc);
-      if ((lane & (64 / CW - 1)) == 0) L.wpart[wave][l][lane / (64 / CW)] = s;
+      for (int k = 0; k < CW; ++k) acc[k] = fma(v, X[r][k], acc[k]);
     }
+    const double s = wave_sum_scatter<CW>(acc);
+    if ((lane & (64 / CW - 1)) == 0) L.wpart[wave][l][lane / (64 / CW)] = s;
   }
   __syncthreads();
   if (tid < len * CW) {
@@ -304,17 +285,14 @@ __device__ __forceinline__ void apply_block(double (&X)[RPT][CW], const double *
   }
   __syncthreads();
 #pragma unroll 1
-  for (int l0 = 0; l0 < len; l0 += kVg) {
-    load_group(l0);
+  for (int l = 0; l < len; ++l) {
+    const double *vr = V + int64_t(c0 + l) * n;
 #pragma unroll
-    for (int u = 0; u < kVg; ++u) {
-      const int l = l0 + u;
-      if (l >= len) break;  // same for every thread
+    for (int r = 0; r < RPT; ++r) {
+      const int i = tid + r * NA;
+      const double v = i < n ? vr[i] : 0.0;
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) {
-#pragma unroll
-        for (int k = 0; k < CW; ++k) X[r][k] = fma(-vb[u][r], L.Zl[l][k], X[r][k]);
-      }
+      for (int k = 0; k < CW; ++k) X[r][k] = fma(-v, L.Zl[l][k], X[r][k]);
     }
   }
 }
@@ -799,15 +777,16 @@ __device__ __forceinline__ bool lh_solve(double *B, int64_t cap, const HeadDesc 
   // the triangle in slot order (Rb's first p columns, same packing) and c
   {
     const int total = poff(p);
-    for (int e0 = 0; e0 < total; e0 += 4 * NQ) {
-      double v[4];
+    // sixteen loads in flight per lane (one wave copies the whole triangle)
+    for (int e0 = 0; e0 < total; e0 += 16 * NQ) {
+      double v[16];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 16; ++j) {
         const int e = e0 + j * NQ + lane;
-        v[j] = e < total ? St.Rb[e] : 0.0;
+        v[j] = St.Rb[e < total ? e : total - 1];  // unconditional load; the store below is guarded
       }
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < 16; ++j) {
         const int e = e0 + j * NQ + lane;
         if (e < total) B[e] = v[j];
       }
@@ -1215,17 +1194,20 @@ __global__ __launch_bounds__(NT) void k_ols_qr(const HeadDesc *__restrict__ desc
 
 hipError_t launch_nnls_qr(const Dims &dm, const Buffers &b, int cycle, int kR, int polish, hipStream_t s) {
   if (!b.qr_flag) return hipSuccess;
-  // one launch per row-count class present among the heads
-  const int64_t maxn = dm.max_n < kQrMaxN ? dm.max_n : kQrMaxN;
-  hipLaunchKernelGGL((k_qr_append<2, 8>), dim3(unsigned(dm.H)), dim3(NA), 0, s, b.desc, b.panel, b.m, b.G, cycle, kR,
-                     polish, b.qr_flag, b.qr_built, b.qrbuf);
-  if (maxn > 2 * NA)
+  // one launch per row-count class present among the launch's heads: class
+  // RPT takes n in (NA RPT / 2, NA RPT] (the first class from n = 1)
+  const int64_t lo = dm.n_lo, hi = dm.n_hi < kQrMaxN ? dm.n_hi : kQrMaxN;
+  auto has = [&](int64_t a, int64_t b_) { return lo <= b_ && hi > a; };
+  if (has(0, 2 * NA))
+    hipLaunchKernelGGL((k_qr_append<2, 8>), dim3(unsigned(dm.H)), dim3(NA), 0, s, b.desc, b.panel, b.m, b.G, cycle,
+                       kR, polish, b.qr_flag, b.qr_built, b.qrbuf);
+  if (has(2 * NA, 4 * NA))
     hipLaunchKernelGGL((k_qr_append<4, 8>), dim3(unsigned(dm.H)), dim3(NA), 0, s, b.desc, b.panel, b.m, b.G, cycle,
                        kR, polish, b.qr_flag, b.qr_built, b.qrbuf);
-  if (maxn > 4 * NA)
+  if (has(4 * NA, 8 * NA))
     hipLaunchKernelGGL((k_qr_append<8, 8>), dim3(unsigned(dm.H)), dim3(NA), 0, s, b.desc, b.panel, b.m, b.G, cycle,
                        kR, polish, b.qr_flag, b.qr_built, b.qrbuf);
-  if (maxn > 8 * NA)
+  if (has(8 * NA, 16 * NA))
     hipLaunchKernelGGL((k_qr_append<16, 4>), dim3(unsigned(dm.H)), dim3(NA), 0, s, b.desc, b.panel, b.m, b.G, cycle,
                        kR, polish, b.qr_flag, b.qr_built, b.qrbuf);
   hipError_t e = hipGetLastError();

@@ -238,7 +238,7 @@ def bench_online(args):
                    "keep_newest": w.keep_newest, "ratio": w.ratio, "topk": w.topk,
                    "refit_every": w.refit_every},
         "kernels_ms": {k: round(v["total_ms"] / args.steps, 1) for k, v in kernels.items()},
-        "head_status_nonzero": int(np.count_nonzero(status)),
+        "head_status_nonzero": int(np.count_nonzero(status & ~amc.HS_NNLS_QR)),
         "input_generation_s": round(gen_s, 1),
     }), flush=True)
 
@@ -333,7 +333,7 @@ def run_long(args, flat, H: int, timer=None):
         "calls": len(allparts),
         "extrapolated_from_heads": H if H < w.num_heads else None,
         "full_call_s_measured": round(call_s, 3),
-        "head_status_nonzero": int(np.count_nonzero(status)),
+        "head_status_nonzero": int(np.count_nonzero(status & ~amc.HS_NNLS_QR)),
         "heads_exact_refit": int(np.count_nonzero(status & 16)),
     }
     if timer:
@@ -600,7 +600,7 @@ def main():
         "cpu_baseline": cpu,
         "kernel_pass": kernel_pass,
         "kernels_ms": {k: round(v["total_ms"] / args.steps, 3) for k, v in (kernels or {}).items()},
-        "head_status_nonzero": int(np.count_nonzero(status)),
+        "head_status_nonzero": int(np.count_nonzero(status & ~amc.HS_NNLS_QR)),
         "heads_exact_refit": int(np.count_nonzero(status & 16)),
         "input_generation_s": round(gen_s, 1),
         "long_context": long_ctx,
