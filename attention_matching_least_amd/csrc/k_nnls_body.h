@@ -1323,9 +1323,26 @@ __device__ __forceinline__ void nnls_core(const St &S, const double *G, int64_t 
 // entries of w) and the accurate gradient gA (nullable: formed from G and
 // b), and marks the starting free set.  Returns the KKT tolerance, 0 when
 // there is nothing to fit.
+// Entering tolerances relative to max |b| in unit-diagonal form (when the
+// caller gives none).  The refits that steer the selection take the textbook
+// worst case of the gradient's rounding, 10 eps p.  The final refit, whose
+// weights are the output, and the stand-alone solver take half an ulp of the
+// largest |b|: any gradient the float64 data resolve.  Once the mass is fitted
+// to a small residual the true gradients of keys that the minimiser still
+// needs fall below 10 eps p (a 2048-key head ended with beta off by 0.11, a
+// 700-key one by 6); a variable entered on a gradient at rounding level whose
+// solution is not positive leaves again and is set aside for the rest of the
+// fit.  Heads above kNnlsFineMaxT keys keep the coarse test in the polish too:
+// with the fine one a single 6000-key head's polish ran past three minutes
+// (each active-set step there walks a factor of up to 6000 rows in global
+// memory), and the fine test in every refit would cost more still.
+__device__ __forceinline__ double nnls_tol_coarse(int p) { return 10.0 * DBL_EPSILON * double(p); }
+constexpr double kNnlsTolFine = 0.5 * DBL_EPSILON;
+constexpr int64_t kNnlsFineMaxT = 2048;
+
 __device__ __forceinline__ double nnls_setup(const St &S, const double *G, int64_t ld, int p, const double *b,
                                              const double *gA, const double *w, int nwarm, const NnlsParams &prm,
-                                             Red *red) {
+                                             double auto_tol, Red *red) {
   const int tid = threadIdx.x;
   double bl = 0.0;
   for (int a = tid; a < p; a += NT) {
@@ -1358,7 +1375,7 @@ __device__ __forceinline__ double nnls_setup(const St &S, const double *G, int64
   double bmax;
   (void)block_argmax(bl, 0, red, &bmax);
   if (!(bmax > 0.0) || !isfinite(bmax)) return 0.0;
-  return (prm.tol > 0.0 ? prm.tol : 10.0 * DBL_EPSILON * double(p)) * bmax;
+  return (prm.tol > 0.0 ? prm.tol : auto_tol) * bmax;
 }
 
 // Projected-gradient warm-up (step 1/L, L a Gershgorin bound of Gs).
@@ -1471,6 +1488,7 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
   }
   __syncthreads();
   const double tol = nnls_setup(S, G + D.tt_off, D.t, p, bvec + D.t_off, gA + D.t_off, w + D.t_off, int(S0), prm,
+                                (polish && D.t <= kNnlsFineMaxT) ? kNnlsTolFine : nnls_tol_coarse(p),
                                 &red);
   int iters = 0;
   if (tol > 0.0) {
@@ -1544,7 +1562,7 @@ __global__ __launch_bounds__(NT) void k_nnls_batched(NnlsChunk ch, int base, con
     bk.ctl[3] = NB;
   }
   __syncthreads();
-  const double tol = nnls_setup(S, Gi, p, p, g + t0, nullptr, w + t0, warm ? p : 0, prm, &red);
+  const double tol = nnls_setup(S, Gi, p, p, g + t0, nullptr, w + t0, warm ? p : 0, prm, kNnlsTolFine, &red);
   int it = 0;
   if (tol > 0.0) {
     if (prm.pg_iters > 0) pg_warmup(S, Gi, p, p, prm.pg_iters, &red);

@@ -477,9 +477,11 @@ def main():
     status = res.head_status.cpu().numpy()
     ms_per_step = 1000.0 * elapsed / args.steps
     value = H * args.steps / elapsed
+    print(f"{w.name}: {args.steps} timed steps, {ms_per_step:.1f} ms per step", file=sys.stderr, flush=True)
 
     roofline = None
     roofline_other = None
+    roofline_fit = None
     kernels = None
     kernel_pass = None
     if timer:
@@ -491,6 +493,7 @@ def main():
             kres = amc.compact(Q, K, V, w.budgets, workspace=workspace, head_groups=1, timer=timer, trace=True,
                                **kw)
         torch.cuda.synchronize()
+        print("kernel pass done", file=sys.stderr, flush=True)
         kernel_pass = {"head_groups": 1, "steps": args.steps,
                        "ms_per_step": round(1000.0 * (time.perf_counter() - t1) / args.steps, 3)}
         kernels = timer.summary()
@@ -542,6 +545,38 @@ def main():
             roofline = found[0][1]
         if len(found) > 1:
             roofline_other = found[1][1]
+        # the float64 matrix-core contractions of the fit side, by the method's flops
+        # (each head alike; a padded tile counts only its rows and columns in use):
+        # the Gram update of cycle c is [panel rows S0 + Kc, m] x [Kc new keys, r]
+        # over the n queries (the polish refit: the panel rows by r); the value fit's
+        # normal equations N = A^T A (one triangle) and A^T Y
+        # (the Gram update reads the panel rows, m, r and the new keys' rows once per
+        # cycle: its bytes against the HBM roof too)
+        fit_flops, gram_bytes = {}, 0.0
+        for b in w.budgets:
+            gram = 0.0
+            for c in range(-(-b // kr)):
+                s0 = c * kr
+                kc = min(kr, b - s0)
+                gram += 2.0 * w.n * (s0 + kc + 1) * (kc + 1)
+                gram_bytes += 8.0 * w.n * (s0 + 2 * kc + 2)
+            gram += 2.0 * w.n * b
+            gram_bytes += 8.0 * w.n * (b + 1)
+            fit_flops["gram"] = fit_flops.get("gram", 0.0) + gram
+            fit_flops["ols_normal"] = fit_flops.get("ols_normal", 0.0) + 2.0 * w.n * (b * (b + 1) / 2 + b * w.d)
+        roofline_fit = {}
+        for cls, kname in (("gram", "k_gram"), ("ols_normal", "k_ols_normal")):
+            kk = kernels.get(cls)
+            if kk and kk["total_ms"] > 0:
+                tf = fit_flops[cls] * args.steps / (kk["total_ms"] * 1e-3) / 1e12
+                roofline_fit[kname] = {"bound": "mfma", "achieved": round(tf, 2), "peak": F64_MFMA_PEAK_TFS,
+                                       "unit": "TFLOP/s", "frac": round(tf / F64_MFMA_PEAK_TFS, 4),
+                                       "flops_per_step": fit_flops[cls], "avg_launch_ms": round(kk["avg_ms"], 4),
+                                       "launches": kk["launches"]}
+                if cls == "gram":
+                    gbs = gram_bytes * args.steps / (kk["total_ms"] * 1e-3) / 1e9
+                    roofline_fit[kname].update({"bytes_per_step": gram_bytes, "hbm_gbs": round(gbs, 1),
+                                                "hbm_frac": round(gbs / HBM_PEAK_GBS, 4)})
 
     highest = None
     if not args.no_highest:
@@ -560,12 +595,15 @@ def main():
         torch.cuda.synchronize()
         hsec = time.perf_counter() - th
         hstat = hres.head_status.cpu().numpy()
+        print(f"AM-Highest: {1000.0 * hsec / args.steps:.1f} ms per step", file=sys.stderr, flush=True)
         highest = {"select": "AM-Highest", "value": round(H * args.steps / hsec, 2), "unit": "heads/s",
                    "ms_per_step": round(1000.0 * hsec / args.steps, 3),
                    "heads_exact_refit": int(np.count_nonzero(hstat & 16))}
         del hres
 
     cpu = cpu_baseline(args.workload, args.cpu_sample) if args.cpu_sample > 0 else None
+    if cpu:
+        print(f"CPU oracle: {cpu['value']:.3f} heads/s", file=sys.stderr, flush=True)
     long_ctx = None
     if long_flat is not None:
         # the headline's buffers go before the 60k-token stack takes the card
@@ -597,6 +635,7 @@ def main():
                    "phi": "recomputed in every sweep" if args.recompute else "stored (two 16-bit planes)"},
         "roofline": roofline,
         "roofline_next": roofline_other,
+        "roofline_fit": roofline_fit,
         "cpu_baseline": cpu,
         "kernel_pass": kernel_pass,
         "kernels_ms": {k: round(v["total_ms"] / args.steps, 3) for k, v in (kernels or {}).items()},
