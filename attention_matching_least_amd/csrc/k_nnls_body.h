@@ -1487,15 +1487,18 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
     for (int k = tid; k < int(D.t); k += NT) S.slot[k] = np_in > 0 ? sg[k] : k;
   }
   __syncthreads();
+  const bool fine = polish && D.t <= kNnlsFineMaxT && !(prm.tol > 0.0);
   const double tol = nnls_setup(S, G + D.tt_off, D.t, p, bvec + D.t_off, gA + D.t_off, w + D.t_off, int(S0), prm,
-                                (polish && D.t <= kNnlsFineMaxT) ? kNnlsTolFine : nnls_tol_coarse(p),
-                                &red);
+                                fine ? kNnlsTolFine : nnls_tol_coarse(p), &red);
   int iters = 0;
   if (tol > 0.0) {
     const int cap = prm.max_iters > 0 ? prm.max_iters : 3 * p + 30;
     nnls_core(S, G + D.tt_off, D.t, p, tol, cap, false, &red, &sh_status, &iters);
   }
   __syncthreads();
+  // the fine test probes candidates whose gradients are at rounding level; a
+  // dependent one among them is set aside by design, not a numeric event
+  const int st = fine ? (sh_status & ~int(AMC_HS_NNLS_SINGULAR)) : sh_status;
   for (int a = tid; a < p; a += NT) w[D.t_off + a] = S.u[a] / S.dg[a];
   const int np = bk.np;
   if (!kGlobal) {
@@ -1515,7 +1518,7 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
   // reports its own status.
   bool gate = false;
   if (qr_ok && !warm_only && tol > 0.0) {
-    gate = (sh_status & int(AMC_HS_NNLS_CAP | AMC_HS_NNLS_SINGULAR)) != 0;
+    gate = (st & int(AMC_HS_NNLS_CAP | AMC_HS_NNLS_SINGULAR)) != 0;
     if (!gate && S0 > 0 && rpart) {
       double rr = 0.0, mm = 0.0;
       for (int k = 0; k < nrb; ++k) {
@@ -1529,7 +1532,7 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
     nn_np[h] = np;
     if (tr_iters && !polish) tr_iters[D.cyc_off + cycle] = iters;
     if (gate) qr_flag[h] = 1;
-    else if (sh_status && head_status && !warm_only) atomicOr(head_status + h, sh_status);
+    else if (st && head_status && !warm_only) atomicOr(head_status + h, st);
   }
   if (tr_weight)
     for (int a = tid; a < p; a += NT) tr_weight[D.t_off + a] = S.u[a] / S.dg[a];

@@ -152,6 +152,13 @@ def read_traffic(kernel: str):
     return None
 
 
+def status_bits(status: np.ndarray) -> dict:
+    """Heads per head-status bit (the exact-refit marker included)."""
+    names = ("chol_jitter", "nnls_cap", "nonfinite", "nnls_singular", "nnls_qr")
+    return {nm: int(np.count_nonzero(status & (1 << i))) for i, nm in enumerate(names)
+            if np.any(status & (1 << i))}
+
+
 def cpu_baseline(idx: int, sample_heads: int):
     import oracle
 
@@ -239,6 +246,7 @@ def bench_online(args):
                    "refit_every": w.refit_every},
         "kernels_ms": {k: round(v["total_ms"] / args.steps, 1) for k, v in kernels.items()},
         "head_status_nonzero": int(np.count_nonzero(status & ~amc.HS_NNLS_QR)),
+        "head_status_bits": status_bits(status),
         "input_generation_s": round(gen_s, 1),
     }), flush=True)
 
@@ -334,6 +342,7 @@ def run_long(args, flat, H: int, timer=None):
         "extrapolated_from_heads": H if H < w.num_heads else None,
         "full_call_s_measured": round(call_s, 3),
         "head_status_nonzero": int(np.count_nonzero(status & ~amc.HS_NNLS_QR)),
+        "head_status_bits": status_bits(status),
         "heads_exact_refit": int(np.count_nonzero(status & 16)),
     }
     if timer:
@@ -640,6 +649,7 @@ def main():
         "kernel_pass": kernel_pass,
         "kernels_ms": {k: round(v["total_ms"] / args.steps, 3) for k, v in (kernels or {}).items()},
         "head_status_nonzero": int(np.count_nonzero(status & ~amc.HS_NNLS_QR)),
+        "head_status_bits": status_bits(status),
         "heads_exact_refit": int(np.count_nonzero(status & 16)),
         "input_generation_s": round(gen_s, 1),
         "long_context": long_ctx,
