@@ -238,6 +238,7 @@ __device__ __forceinline__ void block_sums(double (&v)[NV], double *red) {
 }
 
 struct AppendLds {
+  double mt[kQrMaxN];  // the rotated mass H^T m of the head (each thread keeps its own rows)
   double red[RED_RES + 32];
   double wpart[NAW][kQrChunk][kQrChunk];
   double Wl[kQrChunk][kQrChunk];
@@ -312,11 +313,13 @@ __device__ void qr_append_head(const HeadDesc &D, const QrState &S, const double
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int t = int(D.t);
   const int n = int(D.n);
-  double mtr[RPT];
+  // the rotated mass stays in LDS (a thread reads and writes only its own
+  // rows), keeping registers for the columns
+  double *mtr = L.mt;
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     const int i = tid + r * NA;
-    mtr[r] = i < n ? (from == 0 ? m[i] : S.mt[i]) : 0.0;
+    if (i < n) mtr[i] = from == 0 ? m[i] : S.mt[i];
   }
 #pragma unroll 1
   for (int cidx = from / CW; cidx * CW < p; ++cidx) {
@@ -459,7 +462,10 @@ __device__ void qr_append_head(const HeadDesc &D, const QrState &S, const double
 #pragma unroll
       for (int k = 0; k < CW; ++k) dv[k] = 0.0;
 #pragma unroll
-      for (int r = 0; r < RPT; ++r) dv[0] = fma(xc[r], mtr[r], dv[0]);
+      for (int r = 0; r < RPT; ++r) {
+        const int i = tid + r * NA;
+        dv[0] = fma(xc[r], i < n ? mtr[i] : 0.0, dv[0]);
+      }
 #pragma unroll
       for (int j = 0; j < CW - 1; ++j) {
         if (j >= kc) continue;  // same for every thread
@@ -475,8 +481,11 @@ __device__ void qr_append_head(const HeadDesc &D, const QrState &S, const double
       for (int r = 0; r < RPT; ++r) {
         const int i = tid + r * NA;
         if (i < n) va[i] = xc[r];
-        mtr[r] = fma(-tau * dv[0], xc[r], mtr[r]);
-        if (i == a) S.cb[a] = mtr[r];
+        if (i < n) {
+          const double mv = fma(-tau * dv[0], xc[r], mtr[i]);
+          mtr[i] = mv;
+          if (i == a) S.cb[a] = mv;
+        }
       }
       if (tid == 0 && a >= n) S.cb[a] = 0.0;
       // T_c column kc: tau on the diagonal, -tau T_c[l][0..kc) e above it
@@ -494,7 +503,7 @@ __device__ void qr_append_head(const HeadDesc &D, const QrState &S, const double
 #pragma unroll
   for (int r = 0; r < RPT; ++r) {
     const int i = tid + r * NA;
-    if (i < n) S.mt[i] = mtr[r];
+    if (i < n) S.mt[i] = mtr[i];
   }
   (void)lane;
   (void)wave;

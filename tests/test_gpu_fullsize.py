@@ -19,10 +19,10 @@ def _say(msg):
     print(msg, flush=True)
 
 
-def _compact(heads, budgets, k, R, beta_in=None):
+def _compact(heads, budgets, k, R, beta_in=None, **kw):
     Q, K, V, cu_q, cu_k = pack_heads(heads, "bf16")
     res = amc.compact(Q, K, V, budgets, cu_q=cu_q, cu_k=cu_k, beta_in=beta_in, select="batched", topk=k,
-                      refit_every=R, trace=True)
+                      refit_every=R, trace=True, **kw)
     torch.cuda.synchronize()
     hs = res.head_status.cpu().numpy()
     assert np.all(hs & (amc.HS_NNLS_CAP | amc.HS_NONFINITE) == 0), hs
@@ -94,4 +94,20 @@ def test_long_context_head(long_context_run, h):
     rep = spot_replay(head.Q, head.K, head.V, w.budgets[h], w.topk, w.refit_every, res, h, [1, 12],
                       final=False)
     _report(f"60k-token head {h}", rep)
+    assert rep["ok"], rep
+
+
+def test_long_context_head_fine_entering_test():
+    """The first head of the 60k-token stack with the Gram solver's entering
+    test given as 1e-14 of max |b| in every refit (amc_options.nnls_tol; at
+    most 400 active-set steps per refit) instead of the default 10 eps t: its
+    picks follow the oracle's at refits 12 and 24, where the default's part
+    from the oracle's after refit 12.  The finer test costs about four times
+    the default's time per head."""
+    w = synth.workload(3)
+    head = w.heads([0])[0]
+    _say(f"60k-token head 0, entering test 1e-14: t={w.budgets[0]}")
+    res = _compact([head], w.budgets[:1], w.topk, w.refit_every, nnls_tol=1e-14, nnls_max_iters=400)
+    rep = spot_replay(head.Q, head.K, head.V, w.budgets[0], w.topk, w.refit_every, res, 0, [12, 24], final=False)
+    _report("60k-token head 0, entering test 1e-14", rep)
     assert rep["ok"], rep
