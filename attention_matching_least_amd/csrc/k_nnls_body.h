@@ -1487,7 +1487,8 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
     for (int k = tid; k < int(D.t); k += NT) S.slot[k] = np_in > 0 ? sg[k] : k;
   }
   __syncthreads();
-  const bool fine = polish && D.t <= kNnlsFineMaxT && !(prm.tol > 0.0);
+  // (a warm start for the exact refit needs no fine test: Lawson-Hanson decides)
+  const bool fine = polish && D.t <= kNnlsFineMaxT && !(prm.tol > 0.0) && !warm_only;
   const double tol = nnls_setup(S, G + D.tt_off, D.t, p, bvec + D.t_off, gA + D.t_off, w + D.t_off, int(S0), prm,
                                 fine ? kNnlsTolFine : nnls_tol_coarse(p), &red);
   int iters = 0;

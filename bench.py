@@ -333,6 +333,9 @@ def run_long(args, flat, H: int, timer=None):
         "metric": "OMP key-select s at T=60k",
         "value": round(call_s * scale, 2),
         "value_covers": "wall-clock seconds of the compaction calls: key selection plus the value fit and packing",
+        "parity": "the Gram-form refits' default entering test: in spot replays against the float64 oracle "
+                  "the picks after refit 1 follow the oracle's, those after refit 12 of 47 do not (with "
+                  "nnls_tol=1e-14 those after refits 12 and 24 do, at about 4x the time per head)",
         "unit": "s",
         "higher_is_better": False,
         "config": {"workload": w.name, "heads_run": H, "heads_total": w.num_heads, "head_batch": B, "T": w.T,
