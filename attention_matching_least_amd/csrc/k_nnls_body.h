@@ -1324,10 +1324,11 @@ __device__ __forceinline__ void nnls_core(const St &S, const double *G, int64_t 
 // b), and marks the starting free set.  Returns the KKT tolerance, 0 when
 // there is nothing to fit.
 // Entering tolerances relative to max |b| in unit-diagonal form (when the
-// caller gives none).  The refits that steer the selection take the textbook
-// worst case of the gradient's rounding, 10 eps p.  The final refit, whose
-// weights are the output, and the stand-alone solver take half an ulp of the
-// largest |b|: any gradient the float64 data resolve.  Once the mass is fitted
+// caller gives none).  The refits that steer the selection on the Gram form
+// take the textbook worst case of the gradient's rounding, 10 eps p.  The
+// final refit, whose weights are the output, the refits that warm-start the
+// exact refit, and the stand-alone solver take half an ulp of the largest
+// |b|: any gradient the float64 data resolve.  Once the mass is fitted
 // to a small residual the true gradients of keys that the minimiser still
 // needs fall below 10 eps p (a 2048-key head ended with beta off by 0.11, a
 // 700-key one by 6); a variable entered on a gradient at rounding level whose
@@ -1487,8 +1488,12 @@ __global__ __launch_bounds__(NT) void k_nnls_cycle(const HeadDesc *__restrict__ 
     for (int k = tid; k < int(D.t); k += NT) S.slot[k] = np_in > 0 ? sg[k] : k;
   }
   __syncthreads();
-  // (a warm start for the exact refit needs no fine test: Lawson-Hanson decides)
-  const bool fine = polish && D.t <= kNnlsFineMaxT && !(prm.tol > 0.0) && !warm_only;
+  // The fine test also serves every refit of a head whose Gram solve is the
+  // exact refit's warm start (budgets up to 640: small factors, cheap steps): a
+  // start at the minimiser leaves Lawson-Hanson a single verifying step (on the
+  // 288-head stack at most 2 steps in any refit, against up to 38 from a start
+  // the coarse test leaves).
+  const bool fine = !(prm.tol > 0.0) && (warm_only || (polish && D.t <= kNnlsFineMaxT));
   const double tol = nnls_setup(S, G + D.tt_off, D.t, p, bvec + D.t_off, gA + D.t_off, w + D.t_off, int(S0), prm,
                                 fine ? kNnlsTolFine : nnls_tol_coarse(p), &red);
   int iters = 0;

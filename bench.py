@@ -400,6 +400,8 @@ def main():
                     help="NNLS refits through the orthogonal factorisation: every head it takes, warm-started by "
                          "the Gram solver; every head it takes, warm-started by the previous refit; heads the "
                          "Gram solver flags; none")
+    ap.add_argument("--nnls-tol", type=float, default=0.0,
+                    help="the Gram solver's entering test relative to max |b| in every refit (0: the library's)")
     ap.add_argument("--no-highest", action="store_true", help="leave out the AM-Highest line")
     ap.add_argument("--recompute", action="store_true",
                     help="workloads 1, 2, 4: Phi recomputed in every sweep instead of stored (the mode the 60k-token "
@@ -468,7 +470,7 @@ def main():
     cu_k = [w.T * h for h in range(H + 1)]
     select = "omp" if (w.topk == 1 and w.refit_every == 1) else "batched"
     kw = dict(cu_q=cu_q, cu_k=cu_k, select=select, topk=w.topk, refit_every=w.refit_every,
-              exact_refit=args.exact_refit)
+              exact_refit=args.exact_refit, nnls_tol=args.nnls_tol)
     if args.recompute:
         kw["phi_budget_bytes"] = 0
         args.no_timer = True

@@ -131,10 +131,11 @@ typedef struct {
   int32_t nnls_max_iters; /* active-set iteration cap per refit (0 = 3 * budget + 30) */
   int32_t nnls_polish;    /* refinement refits after the last key (default 1) */
   double nnls_tol;        /* KKT entering tolerance of the Gram solver, relative to max |b| in
-                           * unit-diagonal form (0 = automatic: 10 eps t in the refits of the
-                           * selection; eps / 2, any gradient the float64 data resolve, in
-                           * the polish refits after the last key of budgets up to 2048 and
-                           * in amc_nnls) */
+                           * unit-diagonal form (0 = automatic: 10 eps t in the Gram-form
+                           * refits of the selection; eps / 2, any gradient the float64 data
+                           * resolve, in the polish refits after the last key of budgets up
+                           * to 2048, in every refit that warm-starts the exact refit, and in
+                           * amc_nnls) */
   uint64_t phi_budget_bytes; /* Phi is stored when sum_h n_h ceil8(T_h) * 4 <= this, as two
                               * 16-bit planes (the high and low halves of its float32
                               * values): a sweep reads the high plane, bounds every score,
