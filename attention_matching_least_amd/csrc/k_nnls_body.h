@@ -1319,10 +1319,6 @@ __device__ __forceinline__ void nnls_core(const St &S, const double *G, int64_t 
   *iters_out = iters;
 }
 
-// Sets up u, g, dg, flag for a < p from G, b, the warm start (first nwarm
-// entries of w) and the accurate gradient gA (nullable: formed from G and
-// b), and marks the starting free set.  Returns the KKT tolerance, 0 when
-// there is nothing to fit.
 // Entering tolerances relative to max |b| in unit-diagonal form (when the
 // caller gives none).  The refits that steer the selection on the Gram form
 // take the textbook worst case of the gradient's rounding, 10 eps p.  The
@@ -1341,6 +1337,10 @@ __device__ __forceinline__ double nnls_tol_coarse(int p) { return 10.0 * DBL_EPS
 constexpr double kNnlsTolFine = 0.5 * DBL_EPSILON;
 constexpr int64_t kNnlsFineMaxT = 2048;
 
+// Sets up u, g, dg, flag for a < p from G, b, the warm start (first nwarm
+// entries of w) and the accurate gradient gA (nullable: formed from G and
+// b), and marks the starting free set.  Returns the KKT tolerance, 0 when
+// there is nothing to fit (auto_tol: the entering test when prm gives none).
 __device__ __forceinline__ double nnls_setup(const St &S, const double *G, int64_t ld, int p, const double *b,
                                              const double *gA, const double *w, int nwarm, const NnlsParams &prm,
                                              double auto_tol, Red *red) {
